@@ -1,0 +1,639 @@
+/*
+ * mx_oracle.c -- CPU oracle for block-scaled quantisation of bf16 tensors
+ * (MXFP8: E8M0 scale per 32 elements + E4M3 elements; NVFP4: fp32 tensor
+ * scale + E4M3 scale per 16 elements + E2M1 elements).
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the checker, not the product: only
+ * the test suite, the smoke check and the benchmark's CPU-baseline leg load
+ * it.  It shares no code, header, table or constant with the HIP library and
+ * includes nothing from it.
+ *
+ * Style: every value is decoded from its bit pattern with the format's own
+ * definition, held exactly in a double, and every encoder searches for the
+ * nearest representable value of the target format.  No bit tricks, no
+ * blocking, no fusion.  Where the method fixes fp32 arithmetic (the fused
+ * activations and the NVFP4 scale chain) the step is written as an explicit
+ * fp32 operation; "fl32(a op b)" below is computed as (float)((double)a op b),
+ * which is the correctly rounded fp32 result because a double carries more
+ * than 2*24+2 bits (double rounding is innocuous for + - * /).
+ *
+ * Sources.  The pages ("[Common] Fix pointer arithmatic to generate correct
+ * LDS/STS instructions", TransformerEngine PR 3291; "Multiply with inverse
+ * scale in loop inside of dividing to improve perf", torchao PR 12) name the
+ * MXFP8 / NVFP4 cast kernels and their fusions (tables "MXFP8 generic quantize
+ * kernel", "MXFP8 gated (swiglu / geglu) kernel", "NVFP4 2D quantize-transpose
+ * kernel") but never define the arithmetic.  The rules below are the readings
+ * recorded in the design notes:
+ *   R1  E8M0 shared exponent = floor(log2(amax)) - 8 (8 = exponent of the
+ *       largest E4M3 binade), biased by 127 and clamped to [0, 254].
+ *   R2  element = E4M3(x / 2^(byte-127)), round to nearest, ties to the even
+ *       code, magnitudes above 448 saturate to 448, sign kept (-0 -> 0x80).
+ *   R3  a block holding Inf or NaN gets scale 0xFF and elements 0x7F.
+ *   R4  column-wise output is the row-wise output of the transpose.
+ *   R5  fused pre-ops are evaluated in fp32 by the sequences in this file and
+ *       rounded once to bf16 (RNE); that bf16 tensor is what gets quantised
+ *       and what dbias sums.
+ *   R6  NVFP4 per the chain in nvfp4_block().
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fopenmp -shared
+ * -fPIC (see build.py).  OpenMP only splits independent rows / columns /
+ * blocks, never a reduction, so results do not depend on the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_OK 0
+#define ORC_ERR_SHAPE 3
+#define ORC_ERR_ENUM 2
+#define ORC_ERR_NOMEM 9
+
+/* ------------------------------------------------------------------------ */
+/* bfloat16: 1 sign bit, 8 exponent bits (bias 127), 7 mantissa bits.        */
+/* ------------------------------------------------------------------------ */
+
+double orc_bf16_value(uint16_t b)
+{
+    int s = b >> 15, e = (b >> 7) & 0xFF, m = b & 0x7F;
+    double mag;
+    if (e == 0xFF)
+        mag = m ? NAN : INFINITY;
+    else if (e == 0)
+        mag = ldexp((double)m, -133);           /* (m/128) * 2^-126 */
+    else
+        mag = ldexp(128.0 + m, e - 134);        /* (1 + m/128) * 2^(e-127) */
+    return s ? -mag : mag;
+}
+
+/* Nearest bf16 to v, ties to the even significand, overflow to Inf. */
+uint16_t orc_bf16_round(double v)
+{
+    if (isnan(v))
+        return 0x7FC0;
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (isinf(a))
+        return sign | 0x7F80;
+    if (a == 0.0)
+        return sign;
+    int ex;
+    frexp(a, &ex);                   /* a = f * 2^ex, f in [0.5, 1) */
+    int e = ex - 1;                  /* floor(log2 a) */
+    if (e < -126)
+        e = -126;                    /* subnormals share the last binade's spacing */
+    double q = ldexp(1.0, e - 7);    /* bf16 spacing in this binade */
+    double n = nearbyint(a / q);     /* default rounding mode: nearest, ties even */
+    double r = n * q;
+    if (r >= 0x1p128)
+        return sign | 0x7F80;
+    if (r < 0x1p-126)
+        return sign | (uint16_t)(r / 0x1p-133);
+    frexp(r, &ex);
+    e = ex - 1;
+    int m = (int)(r / ldexp(1.0, e - 7)) - 128;
+    return sign | (uint16_t)((e + 127) << 7) | (uint16_t)m;
+}
+
+/* ------------------------------------------------------------------------ */
+/* E4M3 ("fn" variant): bias 7, no Inf, 0x7F / 0xFF are NaN, max 448.         */
+/* ------------------------------------------------------------------------ */
+
+double orc_e4m3_value(uint8_t c)
+{
+    int s = c >> 7, e = (c >> 3) & 0xF, m = c & 7;
+    double mag;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        mag = ldexp((double)m, -9);             /* (m/8) * 2^-6 */
+    else
+        mag = ldexp(8.0 + m, e - 10);           /* (1 + m/8) * 2^(e-7) */
+    return s ? -mag : mag;
+}
+
+static double E4M3_MAG[127];   /* magnitudes of codes 0x00..0x7E, increasing */
+static double E2M1_MAG[8];     /* magnitudes of codes 0x0..0x7, increasing */
+
+double orc_e2m1_value(uint8_t c)
+{
+    int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+    double mag = (e == 0) ? 0.5 * m                       /* subnormal: m/2 */
+                          : ldexp(1.0 + 0.5 * m, e - 1);  /* (1 + m/2) * 2^(e-1) */
+    return s ? -mag : mag;
+}
+
+static void init_tables(void)
+{
+    static int done = 0;
+    if (done)
+        return;
+    for (int c = 0; c < 127; c++)
+        E4M3_MAG[c] = orc_e4m3_value((uint8_t)c);
+    for (int c = 0; c < 8; c++)
+        E2M1_MAG[c] = orc_e2m1_value((uint8_t)c);
+    done = 1;
+}
+
+void orc_init(void) { init_tables(); }
+
+/* Nearest of the magnitudes mag[0..n-1] (increasing) to a >= 0, a < mag[n-1];
+ * on a tie the even code wins. */
+static int nearest_code(const double *mag, int n, double a)
+{
+    int lo = 0, hi = n - 1;       /* mag[lo] <= a < mag[hi] */
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (mag[mid] <= a)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    double dlo = a - mag[lo], dhi = mag[hi] - a;
+    if (dlo < dhi)
+        return lo;
+    if (dhi < dlo)
+        return hi;
+    return (lo & 1) ? hi : lo;
+}
+
+/* R2: round to nearest E4M3, ties to even code, saturate at 448, keep sign. */
+uint8_t orc_e4m3_encode(double v)
+{
+    init_tables();
+    if (isnan(v))
+        return 0x7F;
+    uint8_t sign = signbit(v) ? 0x80 : 0;
+    double a = fabs(v);
+    if (a >= 448.0)
+        return sign | 0x7E;
+    return sign | (uint8_t)nearest_code(E4M3_MAG, 127, a);
+}
+
+/* E2M1: magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}; nearest, ties to even code,
+ * saturate at 6 (Inf included), sign in bit 3, NaN -> +0. */
+uint8_t orc_e2m1_encode(double v)
+{
+    init_tables();
+    if (isnan(v))
+        return 0x0;
+    uint8_t sign = signbit(v) ? 0x8 : 0;
+    double a = fabs(v);
+    if (a >= 6.0)
+        return sign | 0x7;
+    return sign | (uint8_t)nearest_code(E2M1_MAG, 8, a);
+}
+
+/* ------------------------------------------------------------------------ */
+/* E8M0 shared scale (R1).                                                   */
+/* ------------------------------------------------------------------------ */
+
+double orc_e8m0_value(uint8_t b)
+{
+    return b == 0xFF ? NAN : ldexp(1.0, (int)b - 127);
+}
+
+uint8_t orc_e8m0_byte(double amax)
+{
+    if (isnan(amax) || isinf(amax))
+        return 0xFF;
+    if (amax == 0.0)
+        return 0;
+    int ex;
+    frexp(amax, &ex);                  /* floor(log2 amax) = ex - 1 */
+    int b = (ex - 1) - 8 + 127;        /* E4M3's largest binade is 2^8 */
+    if (b < 0)
+        b = 0;
+    if (b > 254)
+        b = 254;
+    return (uint8_t)b;
+}
+
+/* One MX block: n values (exact doubles) -> n E4M3 codes (q[i*qstride]) and
+ * the E8M0 byte.  The scale is applied as a true division by 2^(byte-127);
+ * that is exact here, so it equals multiplying by the power-of-two inverse
+ * (the point of "Multiply with inverse scale in loop inside of dividing",
+ * body bullets). */
+void orc_mx_block(const double *v, int n, uint8_t *q, int64_t qstride, uint8_t *s)
+{
+    double amax = 0.0;
+    int nonfinite = 0;
+    for (int i = 0; i < n; i++) {
+        if (!isfinite(v[i]))
+            nonfinite = 1;
+        else if (fabs(v[i]) > amax)
+            amax = fabs(v[i]);
+    }
+    if (nonfinite) {                               /* R3 */
+        *s = 0xFF;
+        for (int i = 0; i < n; i++)
+            q[i * qstride] = 0x7F;
+        return;
+    }
+    uint8_t b = orc_e8m0_byte(amax);
+    double X = orc_e8m0_value(b);
+    for (int i = 0; i < n; i++)
+        q[i * qstride] = orc_e4m3_encode(v[i] / X);
+    *s = b;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Fused pre-op arithmetic (R5).  Every line is one IEEE fp32 operation;     */
+/* fmaf is the fused multiply-add with a single rounding.                    */
+/* ------------------------------------------------------------------------ */
+
+/* e^a in fp32: Cody & Waite argument reduction a = n*ln2 + r with ln2 split
+ * as 355/512 + (ln2 - 355/512), then the degree-7 Taylor polynomial of e^r
+ * (|r| <= ln2/2) evaluated by Horner with fmaf, then scaling by 2^n as two
+ * exact power-of-two factors so that subnormal results round once. */
+float orc_exp32(float a)
+{
+    const float LOG2E = 1.44269504088896340736f;       /* 1/ln 2 */
+    const float LN2_HI = 0.693359375f;                 /* 355/512, exact */
+    const float LN2_LO = -2.12194440054690583e-4f;     /* ln 2 - 355/512 */
+    const float C2 = 1.0f / 2.0f, C3 = (float)(1.0 / 6.0), C4 = (float)(1.0 / 24.0),
+                C5 = (float)(1.0 / 120.0), C6 = (float)(1.0 / 720.0),
+                C7 = (float)(1.0 / 5040.0);
+    if (a != a)
+        return a;
+    if (a > 88.72283172607421875f)      /* e^a would round to +Inf */
+        return INFINITY;
+    if (a < -104.0f)                    /* e^a below half the least subnormal */
+        return 0.0f;
+    float n = rintf(a * LOG2E);
+    float r = fmaf(n, -LN2_HI, a);
+    r = fmaf(n, -LN2_LO, r);
+    float p = C7;
+    p = fmaf(p, r, C6);
+    p = fmaf(p, r, C5);
+    p = fmaf(p, r, C4);
+    p = fmaf(p, r, C3);
+    p = fmaf(p, r, C2);
+    p = fmaf(p, r, 1.0f);
+    p = fmaf(p, r, 1.0f);
+    int ni = (int)n;                    /* in [-150, 128] */
+    int n1 = ni / 2, n2 = ni - n1;      /* each in [-75, 64]: 2^n1, 2^n2 are normal */
+    return (p * ldexpf(1.0f, n1)) * ldexpf(1.0f, n2);
+}
+
+/* Logistic sigma(z) = 1/(1+e^-z) and its complement 1 - sigma(z), both built
+ * from e = e^-|z| <= 1 so that nothing overflows and neither is computed by
+ * cancellation:  for z >= 0: sigma = 1/(1+e), 1-sigma = e/(1+e); for z < 0
+ * the two swap. */
+static void sigmoid_pair(float z, float *s, float *sc)
+{
+    float e = orc_exp32(-fabsf(z));
+    float d = 1.0f + e;
+    float r = 1.0f / d;
+    float er = e * r;
+    if (z >= 0.0f) {
+        *s = r;
+        *sc = er;
+    } else {
+        *s = er;
+        *sc = r;
+    }
+}
+
+static const float GELU_K0 = 0.797884560802865355879892119868763737f;  /* sqrt(2/pi) */
+static const float GELU_K1 = 0.044715f;
+static const float GELU_K3 = 0.134145f;                                 /* 3 * 0.044715 */
+static const float GELU_2K0 = 1.59576912160573071175978423973752747f;  /* 2*sqrt(2/pi) */
+
+/* tanh-form GELU: 0.5*x*(1 + tanh(u)), u = sqrt(2/pi)*(x + 0.044715 x^3),
+ * evaluated through the identity 0.5*(1 + tanh(u)) = sigma(2u). */
+float orc_gelu32(float x)
+{
+    float x2 = x * x;
+    float x3 = x2 * x;
+    float inner = fmaf(GELU_K1, x3, x);
+    float u = GELU_K0 * inner;
+    float s, sc;
+    sigmoid_pair(u + u, &s, &sc);
+    return x * s;
+}
+
+/* d/dx of the GELU above: sigma(2u) + x * sigma(2u)(1 - sigma(2u)) * 2u'(x),
+ * 2u'(x) = 2*sqrt(2/pi)*(1 + 3*0.044715 x^2).  When sigma(1-sigma) is 0 the
+ * second term is 0 (this also keeps 0 * Inf out for huge |x|). */
+float orc_dgelu32(float x)
+{
+    float x2 = x * x;
+    float x3 = x2 * x;
+    float inner = fmaf(GELU_K1, x3, x);
+    float u = GELU_K0 * inner;
+    float s, sc;
+    sigmoid_pair(u + u, &s, &sc);
+    float ss = s * sc;
+    float du = GELU_2K0 * fmaf(GELU_K3, x2, 1.0f);
+    float t = (ss == 0.0f) ? 0.0f : (x * ss) * du;
+    return s + t;
+}
+
+/* SiLU: g * sigma(g). */
+float orc_silu32(float g)
+{
+    float s, sc;
+    sigmoid_pair(g, &s, &sc);
+    return g * s;
+}
+
+static float f32_of_bf16(uint16_t b) { return (float)orc_bf16_value(b); }
+
+/* The fused elementwise value y (as bf16 bits) for one input element.
+ * pre: 0 none, 1 GELU(x), 2 dGELU(x) * grad. */
+uint16_t orc_preop(int pre, uint16_t x, uint16_t grad)
+{
+    switch (pre) {
+    case 0:
+        return x;
+    case 1:
+        return orc_bf16_round(orc_gelu32(f32_of_bf16(x)));
+    case 2: {
+        float d = orc_dgelu32(f32_of_bf16(x));
+        float y = d * f32_of_bf16(grad);
+        return orc_bf16_round(y);
+    }
+    default:
+        return 0x7FC0;
+    }
+}
+
+/* Gated value for one output element. act: 1 SwiGLU, 2 GeGLU. */
+uint16_t orc_gated(int act, uint16_t gate, uint16_t lin)
+{
+    float g = f32_of_bf16(gate), l = f32_of_bf16(lin);
+    float a;
+    if (act == 1)
+        a = orc_silu32(g);
+    else if (act == 2)
+        a = orc_gelu32(g);
+    else
+        return 0x7FC0;
+    float y = a * l;
+    return orc_bf16_round(y);
+}
+
+/* ------------------------------------------------------------------------ */
+/* MXFP8 over a tensor.                                                      */
+/* ------------------------------------------------------------------------ */
+
+/* Row-wise and column-wise MX quantisation of the bf16 tensor y[M][K].
+ *   rows: q_row[M][K], s_row[M][K/32]   (blocks of 32 along K)
+ *   cols: q_col[K][M], s_col[K][M/32]   (blocks of 32 along M, stored as the
+ *         row-wise output of the transpose, R4) */
+static void mx_tensor(const uint16_t *y, int64_t M, int64_t K, unsigned axis,
+                      uint8_t *q_row, uint8_t *s_row, uint8_t *q_col, uint8_t *s_col)
+{
+    if (axis & 1u) {
+#pragma omp parallel for schedule(static)
+        for (int64_t m = 0; m < M; m++) {
+            double v[32];
+            for (int64_t j = 0; j < K / 32; j++) {
+                for (int i = 0; i < 32; i++)
+                    v[i] = orc_bf16_value(y[m * K + 32 * j + i]);
+                orc_mx_block(v, 32, q_row + m * K + 32 * j, 1, s_row + m * (K / 32) + j);
+            }
+        }
+    }
+    if (axis & 2u) {
+#pragma omp parallel for schedule(static)
+        for (int64_t k = 0; k < K; k++) {
+            double v[32];
+            for (int64_t j = 0; j < M / 32; j++) {
+                for (int i = 0; i < 32; i++)
+                    v[i] = orc_bf16_value(y[(32 * j + i) * K + k]);
+                orc_mx_block(v, 32, q_col + k * M + 32 * j, 1, s_col + k * (M / 32) + j);
+            }
+        }
+    }
+}
+
+/* dbias[k] = sum over m of y[m][k]: summed in double in row order, rounded
+ * once to fp32. */
+static void column_sums(const uint16_t *y, int64_t M, int64_t K, float *dbias)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < K; k++) {
+        double acc = 0.0;
+        for (int64_t m = 0; m < M; m++)
+            acc += orc_bf16_value(y[m * K + k]);
+        dbias[k] = (float)acc;
+    }
+}
+
+/* fusion: low nibble = pre-op (0 none, 1 GELU, 2 dGELU), bit 0x10 = dbias.
+ * y_out (optional, [M][K]) receives the fused bf16 tensor. */
+int orc_mx_quantize(const uint16_t *x, const uint16_t *grad, int64_t M, int64_t K,
+                    unsigned axis, int fusion, uint8_t *q_row, uint8_t *s_row,
+                    uint8_t *q_col, uint8_t *s_col, float *dbias, uint16_t *y_out)
+{
+    int pre = fusion & 0xF;
+    if (M <= 0 || K <= 0 || M % 32 || K % 32)
+        return ORC_ERR_SHAPE;
+    if (pre > 2 || (fusion & ~0x1F) || (axis & ~3u))
+        return ORC_ERR_ENUM;
+    init_tables();
+    const uint16_t *y = x;
+    uint16_t *ybuf = NULL;
+    if (pre != 0) {
+        ybuf = y_out ? y_out : (uint16_t *)malloc((size_t)(M * K) * 2);
+        if (!ybuf)
+            return ORC_ERR_NOMEM;
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < M * K; i++)
+            ybuf[i] = orc_preop(pre, x[i], grad ? grad[i] : 0);
+        y = ybuf;
+    } else if (y_out) {
+        memcpy(y_out, x, (size_t)(M * K) * 2);
+    }
+    mx_tensor(y, M, K, axis, q_row, s_row, q_col, s_col);
+    if ((fusion & 0x10) && dbias)
+        column_sums(y, M, K, dbias);
+    if (ybuf && ybuf != y_out)
+        free(ybuf);
+    return ORC_OK;
+}
+
+/* x[M][2N] = [gate | linear] (gate = columns 0..N-1); y[m][n] = act(gate)*lin. */
+int orc_mx_quantize_gated(const uint16_t *x, int64_t M, int64_t N, unsigned axis, int act,
+                          uint8_t *q_row, uint8_t *s_row, uint8_t *q_col, uint8_t *s_col,
+                          uint16_t *y_out)
+{
+    if (M <= 0 || N <= 0 || M % 32 || N % 32)
+        return ORC_ERR_SHAPE;
+    if ((act != 1 && act != 2) || (axis & ~3u))
+        return ORC_ERR_ENUM;
+    init_tables();
+    uint16_t *y = y_out ? y_out : (uint16_t *)malloc((size_t)(M * N) * 2);
+    if (!y)
+        return ORC_ERR_NOMEM;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t n = 0; n < N; n++)
+            y[m * N + n] = orc_gated(act, x[m * 2 * N + n], x[m * 2 * N + N + n]);
+    mx_tensor(y, M, N, axis, q_row, s_row, q_col, s_col);
+    if (y != y_out)
+        free(y);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* NVFP4 (R6).                                                               */
+/* ------------------------------------------------------------------------ */
+
+/* Largest magnitude of the tensor, as the (exact) fp32 value. */
+float orc_absmax(const uint16_t *x, int64_t n)
+{
+    double a = 0.0;
+    for (int64_t i = 0; i < n; i++) {
+        double v = fabs(orc_bf16_value(x[i]));
+        if (v > a)
+            a = v;
+    }
+    return (float)a;
+}
+
+/* Tensor scale S_g = fl32(A / (448*6)), or 1 when A = 0. */
+float orc_nvfp4_global_scale(float A)
+{
+    if (A == 0.0f)
+        return 1.0f;
+    return (float)((double)A / 2688.0);
+}
+
+/* One NVFP4 block of n values (exact doubles) with tensor scale Sg:
+ *   b    = max |x_i|
+ *   s_q  = fl32(fl32(b / 6) / Sg)           block scale relative to Sg
+ *   byte = E4M3(s_q)                        stored scale (RNE, saturating)
+ *   den  = fl32(decode(byte) * Sg)          the block's effective scale
+ *   inv  = den == 0 ? 0 : fl32(1 / den)     one division per block
+ *   q_i  = E2M1(fl32(x_i * inv))            one multiply per element
+ * Codes are written one per byte into nib[i*stride]; the caller packs. */
+static void nvfp4_block(const double *v, int n, float Sg, uint8_t *nib, int64_t stride,
+                        uint8_t *s)
+{
+    double b = 0.0;
+    for (int i = 0; i < n; i++)
+        if (fabs(v[i]) > b)
+            b = fabs(v[i]);
+    float b6 = (float)(b / 6.0);
+    float sq = (float)((double)b6 / (double)Sg);
+    uint8_t sb = orc_e4m3_encode(sq);
+    float d = (float)orc_e4m3_value(sb);
+    float den = (float)((double)d * (double)Sg);
+    float inv = (den == 0.0f) ? 0.0f : (float)(1.0 / (double)den);
+    for (int i = 0; i < n; i++) {
+        float vs = (float)(v[i] * (double)inv);
+        nib[i * stride] = orc_e2m1_encode(vs);
+    }
+    *s = sb;
+}
+
+/* Row-wise NVFP4 of x[M][K] (blocks of 16 along K) into q_row[M][K/2] (code
+ * of element 2j in the low nibble of byte j, 2j+1 in the high nibble) and
+ * s_row[M][K/16]; and the same for the transpose into q_col[K][M/2],
+ * s_col[K][M/16].  tensor_amax < 0 means "compute it from x". */
+int orc_nvfp4_quantize_transpose(const uint16_t *x, int64_t M, int64_t K, unsigned axis,
+                                 float tensor_amax, uint8_t *q_row, uint8_t *s_row,
+                                 uint8_t *q_col, uint8_t *s_col, float *sg_out)
+{
+    if (M <= 0 || K <= 0 || M % 16 || K % 16)
+        return ORC_ERR_SHAPE;
+    if (axis & ~3u)
+        return ORC_ERR_ENUM;
+    init_tables();
+    float A = tensor_amax >= 0.0f ? tensor_amax : orc_absmax(x, M * K);
+    float Sg = orc_nvfp4_global_scale(A);
+    if (sg_out)
+        *sg_out = Sg;
+    if (axis & 1u) {
+#pragma omp parallel for schedule(static)
+        for (int64_t m = 0; m < M; m++) {
+            double v[16];
+            uint8_t c[16];
+            for (int64_t j = 0; j < K / 16; j++) {
+                for (int i = 0; i < 16; i++)
+                    v[i] = orc_bf16_value(x[m * K + 16 * j + i]);
+                nvfp4_block(v, 16, Sg, c, 1, s_row + m * (K / 16) + j);
+                for (int i = 0; i < 8; i++)
+                    q_row[m * (K / 2) + 8 * j + i] = (uint8_t)(c[2 * i] | (c[2 * i + 1] << 4));
+            }
+        }
+    }
+    if (axis & 2u) {
+#pragma omp parallel for schedule(static)
+        for (int64_t k = 0; k < K; k++) {
+            double v[16];
+            uint8_t c[16];
+            for (int64_t j = 0; j < M / 16; j++) {
+                for (int i = 0; i < 16; i++)
+                    v[i] = orc_bf16_value(x[(16 * j + i) * K + k]);
+                nvfp4_block(v, 16, Sg, c, 1, s_col + k * (M / 16) + j);
+                for (int i = 0; i < 8; i++)
+                    q_col[k * (M / 2) + 8 * j + i] = (uint8_t)(c[2 * i] | (c[2 * i + 1] << 4));
+            }
+        }
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Array helpers for the self-tests (elementwise, no method arithmetic).     */
+/* ------------------------------------------------------------------------ */
+
+void orc_e4m3_encode_array(const double *v, uint8_t *out, int64_t n)
+{
+    init_tables();
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++)
+        out[i] = orc_e4m3_encode(v[i]);
+}
+
+void orc_e2m1_encode_array(const double *v, uint8_t *out, int64_t n)
+{
+    init_tables();
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++)
+        out[i] = orc_e2m1_encode(v[i]);
+}
+
+void orc_bf16_round_array(const double *v, uint16_t *out, int64_t n)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++)
+        out[i] = orc_bf16_round(v[i]);
+}
+
+/* which: 0 exp32, 1 gelu32, 2 dgelu32, 3 silu32 */
+void orc_unary32_array(int which, const float *v, float *out, int64_t n)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++) {
+        float a = v[i];
+        out[i] = which == 0 ? orc_exp32(a) : which == 1 ? orc_gelu32(a)
+               : which == 2 ? orc_dgelu32(a) : orc_silu32(a);
+    }
+}
+
+void orc_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+int orc_get_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,193 @@
+"""Pins for the oracle's fused pre-op arithmetic (CPU only).
+
+The fp32 sequences (own exp, logistic form of tanh-GELU) are a reading: the
+pages name gelu / dgelu / swiglu / geglu fusions (tables "MXFP8 generic
+quantize kernel", "MXFP8 gated (swiglu / geglu) kernel") but fix no
+arithmetic.  They are pinned here against float64 closed forms written the
+textbook way (tanh, 1/(1+exp)), against a finite difference for the
+derivative, and by the compositions the fused casts rely on.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+
+K0_32 = float(np.float32(math.sqrt(2.0 / math.pi)))
+K1_32 = float(np.float32(0.044715))
+
+
+def all_finite_bf16_f32():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]
+    return W.bf16_to_f32(bits)
+
+
+def one_plus_tanh(u):
+    """1 + tanh(u) in float64 without cancellation: for u < 0 use
+    2 e^(2u) / (1 + e^(2u))."""
+    with np.errstate(over="ignore", invalid="ignore"):
+        e = np.exp(2.0 * np.minimum(u, 0.0))
+        return np.where(u >= 0, 1.0 + np.tanh(u), 2.0 * e / (1.0 + e))
+
+
+def one_minus_tanh_sq(u):
+    """1 - tanh(u)^2 = 4 e^(-2|u|) / (1 + e^(-2|u|))^2, cancellation free."""
+    with np.errstate(over="ignore", invalid="ignore"):
+        e = np.exp(-2.0 * np.abs(u))
+        return 4.0 * e / (1.0 + e) ** 2
+
+
+def gelu64(x, k0=math.sqrt(2 / math.pi), k1=0.044715):
+    """tanh-form GELU 0.5 x (1 + tanh(k0 (x + k1 x^3))) in float64."""
+    x = np.asarray(x, np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        u = k0 * (x + k1 * x ** 3)
+        return 0.5 * x * one_plus_tanh(u)
+
+
+def dgelu64(x, k0=math.sqrt(2 / math.pi), k1=0.044715):
+    """Its derivative 0.5 (1 + t) + 0.5 x (1 - t^2) k0 (1 + 3 k1 x^2)."""
+    x = np.asarray(x, np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        u = k0 * (x + k1 * x ** 3)
+        d = 0.5 * one_plus_tanh(u) + 0.5 * x * one_minus_tanh_sq(u) * k0 * (1 + 3 * k1 * x * x)
+    return np.where(np.isfinite(d), d, np.where(x > 0, 1.0, 0.0))
+
+
+def cond_ulps(x):
+    """Error budget in fp32 ulps: a few roundings, plus the amplification of
+    u's rounding (about 3 ulps relative) by e^(2u), i.e. 3 |2u|."""
+    x = np.asarray(x, np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        u = K0_32 * (x + K1_32 * x ** 3)
+    return 8.0 + 3.0 * np.abs(2.0 * u)
+
+
+def silu64(x):
+    x = np.asarray(x, np.float64)
+    with np.errstate(over="ignore"):
+        return x / (1.0 + np.exp(-x))
+
+
+def ulp32(v):
+    a = np.abs(np.asarray(v, np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return 2.0 ** (e - 23)
+
+
+def test_exp32_accuracy_and_range():
+    a = np.linspace(-103.0, 88.72, 2_000_001).astype(np.float32)
+    got = O.unary32("exp", a).astype(np.float64)
+    want = np.exp(a.astype(np.float64))
+    normal = want >= 2.0 ** -126
+    err = np.abs(got - want)[normal] / ulp32(want[normal])
+    assert err.max() <= 2.0, err.max()
+    # subnormal results: within one unit of the least subnormal
+    assert np.all(np.abs(got - want)[~normal] <= 2.0 ** -149)
+    assert O.unary32("exp", [0.0])[0] == 1.0
+    assert np.isfinite(O.unary32("exp", [88.72283172607421875])[0])
+    assert np.isinf(O.unary32("exp", [88.7228393554687])[0])
+    assert O.unary32("exp", [-104.5])[0] == 0.0
+
+
+def test_gelu32_against_tanh_form():
+    x = all_finite_bf16_f32()
+    got = O.unary32("gelu", x).astype(np.float64)
+    want = gelu64(x, K0_32, K1_32)                 # same constants, tanh route
+    fin = np.isfinite(want)
+    assert np.all(np.isfinite(got[fin]))
+    err = np.abs(got - want)[fin]
+    tol = cond_ulps(x[fin]) * ulp32(want[fin]) + 2.0 ** -148
+    assert np.all(err <= tol), (x[fin][err > tol][:5], got[fin][err > tol][:5], want[fin][err > tol][:5])
+    # the fp32 constants cost at most ~1e-5 relative against the exact ones
+    mid = np.abs(x) < 8
+    rel = np.abs(got[mid] - gelu64(x[mid])) / np.maximum(np.abs(gelu64(x[mid])), 1e-30)
+    assert np.all(rel[np.abs(gelu64(x[mid])) > 1e-30] < 1e-5)
+    # bf16-rounded results equal float64's bf16 rounding almost always, never off by more than 1 ulp
+    gb = O.bf16_round_array(got)
+    wb = O.bf16_round_array(want)
+    agree = np.mean(gb == wb)
+    assert agree > 0.9995, agree
+    assert np.all(np.abs(gb.astype(np.int64) - wb.astype(np.int64))[gb != wb] <= 1)
+
+
+def test_dgelu32_against_analytic_derivative():
+    x = all_finite_bf16_f32()
+    got = O.unary32("dgelu", x).astype(np.float64)
+    want = dgelu64(x, K0_32, K1_32)
+    err = np.abs(got - want)
+    # gelu' has a zero near x = -0.75 where its two O(1) terms cancel, so the
+    # budget also allows a few ulps of 1 in absolute terms
+    tol = cond_ulps(x) * ulp32(want) + 16 * 2.0 ** -24
+    assert np.all(err <= tol), (x[err > tol][:5], got[err > tol][:5], want[err > tol][:5])
+    away = np.abs(want) > 0.05
+    assert np.all(err[away] <= cond_ulps(x[away]) * ulp32(want[away]) * 4)
+
+
+def test_dgelu_analytic_form_is_the_derivative_of_gelu():
+    x = np.linspace(-6, 6, 4001)
+    h = 1e-6
+    fd = (gelu64(x + h) - gelu64(x - h)) / (2 * h)
+    assert np.max(np.abs(fd - dgelu64(x))) < 1e-8
+
+
+def test_silu32_against_closed_form():
+    x = all_finite_bf16_f32()
+    got = O.unary32("silu", x).astype(np.float64)
+    want = silu64(x)
+    err = np.abs(got - want)
+    tol = (8.0 + 2.0 * np.abs(x)) * ulp32(want) + 2.0 ** -148
+    assert np.all(err <= tol), (x[err > tol][:5], got[err > tol][:5], want[err > tol][:5])
+
+
+def test_special_values():
+    g = O.unary32("gelu", [0.0, -0.0, 1e30, -1e30, 3.0e38, -3.0e38])
+    assert list(g[:2]) == [0.0, 0.0] and g[2] == np.float32(1e30) and g[4] == np.float32(3e38)
+    assert g[3] == 0.0 and np.signbit(g[3]) and g[5] == 0.0
+    d = O.unary32("dgelu", [0.0, 1e30, -1e30, 3e38])
+    assert list(d) == [0.5, 1.0, 0.0, 1.0]
+    s = O.unary32("silu", [0.0, 1e30, -1e30])
+    assert s[0] == 0.0 and s[1] == np.float32(1e30) and s[2] == 0.0
+
+
+def test_preop_and_gated_compositions():
+    rng = np.random.default_rng(21)
+    xs = W.bf16_bits(rng.standard_normal(2000).astype(np.float32) * 3)
+    one, two = 0x3F80, 0x4000
+    for x in xs[:500]:
+        x = int(x)
+        xf = O.bf16_value(x)
+        g = float(O.unary32("gelu", [xf])[0])
+        assert O.preop(O.FUSE_GELU, x) == O.bf16_round(g)
+        d = float(O.unary32("dgelu", [xf])[0])
+        assert O.preop(O.FUSE_DGELU, x, one) == O.bf16_round(d)
+        assert O.preop(O.FUSE_NONE, x) == x
+        s = float(O.unary32("silu", [xf])[0])
+        # linear = 1 leaves act(gate): gate and linear are not swapped
+        assert O.gated(O.GATED_SWIGLU, x, one) == O.bf16_round(s)
+        assert O.gated(O.GATED_GEGLU, x, one) == O.bf16_round(g)
+        # linear = 2 doubles exactly
+        assert O.bf16_value(O.gated(O.GATED_SWIGLU, x, two)) == 2 * O.bf16_value(O.bf16_round(s))
+        # gate = 0 gives +-0 whatever the linear half
+        assert O.bf16_value(O.gated(O.GATED_SWIGLU, 0, x)) == 0.0
+
+
+def test_fused_tensor_equals_plain_cast_of_fused_values():
+    x, g = W.make("c3_gelu_dbias_8192", 64, 64)
+    for fusion in (O.FUSE_GELU, O.FUSE_DGELU):
+        f = O.mx_quantize(x, grad=g, fusion=fusion, want_y=True)
+        p = O.mx_quantize(f["y"])
+        for k in ("q_row", "s_row", "q_col", "s_col"):
+            assert np.array_equal(f[k], p[k])
+    xg = W.make("c4_gated_8192", 64, 128)
+    for act in (O.GATED_SWIGLU, O.GATED_GEGLU):
+        f = O.mx_quantize_gated(xg, act, want_y=True)
+        p = O.mx_quantize(f["y"])
+        for k in ("q_row", "s_row", "q_col", "s_col"):
+            assert np.array_equal(f[k], p[k])
+        # y[m][n] = act(x[m][n]) * x[m][N + n]
+        m, n = 5, 17
+        assert f["y"][m, n] == O.gated(act, int(xg[m, n]), int(xg[m, 64 + n]))

@@ -1,0 +1,161 @@
+"""Pins for the oracle's NVFP4 quantize-transpose (CPU only).
+
+  * hand-derived blocks with tensor scale 1 (tests/golden/nvfp4_blocks.txt);
+  * an independent implementation of the same scale chain in numpy float32
+    arithmetic (IEEE single operations, not the oracle's double-then-round
+    route) with a brute-force E2M1 encoder, compared on whole tensors;
+  * invariants: dequantisation within half an E2M1 ulp at the block scale,
+    the E4M3 block scale is the nearest to b/6/S_g, transpose, sign symmetry.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def load_golden():
+    rows = []
+    for line in open(os.path.join(GOLDEN, "nvfp4_blocks.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        tag, xin, s, q = [f.strip() for f in line.split("|")]
+        rows.append((tag, [int(h, 16) for h in xin.split(",")], int(s, 16),
+                     [int(h, 16) for h in q.split(",")]))
+    return rows
+
+
+@pytest.mark.parametrize("tag,xin,scale,nibbles", load_golden())
+def test_golden_block(tag, xin, scale, nibbles):
+    x = np.zeros((16, 16), np.uint16)
+    x[0, :len(xin)] = xin
+    out = O.nvfp4_quantize_transpose(x, tensor_amax=2688.0)
+    assert out["sg"] == 1.0
+    assert out["s_row"][0, 0] == scale, tag
+    want = np.zeros(16, np.uint8)
+    want[:len(nibbles)] = nibbles
+    packed = want[0::2] | (want[1::2] << 4)
+    assert list(out["q_row"][0]) == list(packed), tag
+    # the same block as column 0 of the transpose
+    outT = O.nvfp4_quantize_transpose(np.ascontiguousarray(x.T), tensor_amax=2688.0)
+    assert outT["s_col"][0, 0] == scale and list(outT["q_col"][0]) == list(packed)
+
+
+def test_golden_ties_packing_literal():
+    """Byte packing of the first golden block, written out: element 2j low nibble."""
+    tag, xin, scale, nib = load_golden()[0]
+    x = np.zeros((16, 16), np.uint16)
+    x[0] = xin
+    out = O.nvfp4_quantize_transpose(x, tensor_amax=2688.0)
+    assert bytes(out["q_row"][0]).hex() == "6746240 2f880 5624".replace(" ", "")
+
+
+def brute_e2m1(v):
+    a = np.abs(v)
+    d = np.abs(a[..., None] - E2M1)
+    best = d.min(-1, keepdims=True)
+    hit = d == best
+    idx = np.argmax(hit, -1)
+    two = hit.sum(-1) == 2
+    idx = np.where(two & (idx % 2 == 1), idx + 1, idx)
+    idx = np.where(a >= 6, 7, idx)
+    return (idx | np.where(np.signbit(v), 8, 0)).astype(np.uint8)
+
+
+def numpy_nvfp4_rows(bits, A):
+    """Independent row-wise NVFP4 in numpy float32 arithmetic."""
+    x = W.bf16_to_f32(bits)
+    M, K = x.shape
+    f32 = np.float32
+    Sg = f32(1.0) if A == 0 else f32(A) / f32(2688.0)
+    blk = x.reshape(M, K // 16, 16)
+    b = np.abs(blk).max(-1)
+    sq = (b / f32(6.0)) / Sg
+    sbyte = torch.from_numpy(np.minimum(sq, f32(448.0))).to(torch.float8_e4m3fn) \
+        .view(torch.uint8).numpy()
+    d = torch.from_numpy(sbyte).view(torch.float8_e4m3fn).float().numpy()
+    den = d * Sg
+    with np.errstate(divide="ignore"):
+        inv = np.where(den == 0, f32(0.0), f32(1.0) / den).astype(np.float32)
+    v = blk * inv[..., None]
+    codes = brute_e2m1(v.astype(np.float64)).reshape(M, K)
+    return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8), sbyte, Sg
+
+
+@pytest.mark.parametrize("case", ["student_t", "normal", "loguniform", "tiny"])
+def test_tensor_matches_numpy_float32_chain(case):
+    if case == "student_t":
+        x = W.student_t_rows(128, 160, seed=31)
+    elif case == "normal":
+        x = W.normal(64, 96, seed=32)
+    elif case == "loguniform":
+        x = W.loguniform_rows(96, 64, seed=33)
+    else:
+        x = W.normal(32, 64, seed=34, sigma=1e-20)
+    out = O.nvfp4_quantize_transpose(x)
+    A = float(np.abs(W.bf16_to_f32(x)).max())
+    q, s, Sg = numpy_nvfp4_rows(x, A)
+    assert out["sg"] == float(Sg)
+    assert np.array_equal(out["q_row"], q) and np.array_equal(out["s_row"], s)
+    qt, st, _ = numpy_nvfp4_rows(np.ascontiguousarray(x.T), A)
+    assert np.array_equal(out["q_col"], qt) and np.array_equal(out["s_col"], st)
+
+
+def test_global_scale():
+    assert O.nvfp4_global_scale(0.0) == 1.0
+    assert O.nvfp4_global_scale(2688.0) == 1.0
+    rng = np.random.default_rng(35)
+    for A in W.bf16_to_f32(W.bf16_bits(rng.uniform(1e-3, 1e4, 200).astype(np.float32))):
+        assert O.nvfp4_global_scale(float(A)) == float(np.float32(A) / np.float32(2688.0))
+
+
+def e2m1_half_ulp(v):
+    a = np.abs(v)
+    return np.where(a < 2, 0.25, np.where(a < 4, 0.5, 1.0))
+
+
+def test_dequantisation_bound_and_scale_choice():
+    x = W.student_t_rows(256, 256, seed=36)
+    out = O.nvfp4_quantize_transpose(x)
+    xf = W.bf16_to_f32(x).astype(np.float64)
+    Sg = out["sg"]
+    d = torch.from_numpy(out["s_row"]).view(torch.float8_e4m3fn).double().numpy()
+    den = np.repeat(d * Sg, 16, axis=1)
+    codes = np.stack([out["q_row"] & 0xF, out["q_row"] >> 4], -1).reshape(x.shape)
+    val = np.array([O.e2m1_value(c) for c in range(16)])[codes]
+    v = xf / den
+    sat = np.abs(v) > 6 * (1 + 2.0 ** -21)
+    slack = 1 + 2.0 ** -21
+    ok = np.abs(val * den - xf) <= e2m1_half_ulp(v) * den * slack + 1e-300
+    assert np.all(ok[~sat])
+    assert np.all(np.abs(val[sat]) == 6)
+    # the stored block scale is the E4M3 value nearest to (b/6)/S_g (fp32 rounding aside)
+    b = np.abs(xf).reshape(256, 16, 16).max(-1)
+    ideal = b / 6 / Sg
+    near = O.e4m3_encode_array(ideal)
+    assert np.mean(near == out["s_row"]) > 0.999
+
+
+def test_transpose_and_sign_invariants():
+    x = W.student_t_rows(64, 96, seed=37)
+    a = O.nvfp4_quantize_transpose(x)
+    t = O.nvfp4_quantize_transpose(np.ascontiguousarray(x.T))
+    assert np.array_equal(a["q_col"], t["q_row"]) and np.array_equal(a["s_col"], t["s_row"])
+    n = O.nvfp4_quantize_transpose(x ^ np.uint16(0x8000))
+    assert np.array_equal(n["s_row"], a["s_row"])
+    assert np.array_equal(n["q_row"], a["q_row"] ^ 0x88)
+
+
+def test_zero_tensor_and_shape_errors():
+    z = np.zeros((16, 32), np.uint16)
+    out = O.nvfp4_quantize_transpose(z)
+    assert out["sg"] == 1.0 and not out["q_row"].any() and not out["s_row"].any()
+    with pytest.raises(ValueError):
+        O.nvfp4_quantize_transpose(np.zeros((16, 24), np.uint16))

@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-scaled cast hot path on one MI355X.
+
+Default workload: the MXFP8 cast of a 16384 x 16384 bf16 tensor (log-uniform
+row magnitudes), row-wise (dim0) and column-wise (dim1, transposed output) in
+one pass, block size 32 -- one step is one mx_quantize call over the whole
+tensor, inputs resident in HBM.  The metric follows the torchao "Multiply
+with inverse scale" page ("Performance" section): GB/s = algorithmic bytes
+read + written / kernel time, where the bytes are 2 per input element plus,
+per direction, 1 per E4M3 element and 1 per 32-element E8M0 scale.
+
+Prints ONE JSON line.  `--config` times one of the other workloads instead
+(for the design notes); `--copy` runs the plain device copy used to calibrate
+the HBM byte counters.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
+
+KERNEL_SOURCES = ["block_scaled_precision_bf16_amd/csrc/mx_cast.hip",
+                  "block_scaled_precision_bf16_amd/csrc/nvfp4.hip",
+                  "block_scaled_precision_bf16_amd/csrc/device_math.h",
+                  "block_scaled_precision_bf16_amd/csrc/launch.h"]
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic_mx_cast_dim0_dim1_16384.md")
+
+
+def mx_bytes(M, K, directions, extra_inputs=0):
+    """Algorithmic bytes of an MXFP8 cast: 2 B per bf16 input element (per
+    input tensor), 1 B per E4M3 element and 1 B per E8M0 scale (per 32
+    elements) for each output direction."""
+    n = M * K
+    return 2 * n * (1 + extra_inputs) + directions * (n + n // 32)
+
+
+def nvfp4_bytes(M, K, directions):
+    """2 B per bf16 input, 1/2 B per E2M1 element and 1 B per 16-element E4M3
+    scale for each direction (the absmax pre-pass is timed separately)."""
+    n = M * K
+    return 2 * n + directions * (n // 2 + n // 16)
+
+
+CONFIGS = {
+    # name: (workload generator key, shape, kind, bytes)
+    "mxfp8_dim0_dim1_16384": ("c2_dim1_16384", (16384, 16384), "mx", 3),
+    "mxfp8_dim1_16384": ("c2_dim1_16384", (16384, 16384), "mx", 2),
+    "mxfp8_gelu_dbias_8192": ("c3_gelu_dbias_8192", (8192, 8192), "mx_gelu", 3),
+    "mxfp8_dgelu_dbias_8192": ("c3_gelu_dbias_8192", (8192, 8192), "mx_dgelu", 3),
+    "mxfp8_swiglu_8192": ("c4_gated_8192", (8192, 8192), "gated_swiglu", 3),
+    "mxfp8_geglu_8192": ("c4_gated_8192", (8192, 8192), "gated_geglu", 3),
+    "nvfp4_16384": ("c5_nvfp4_16384", (16384, 16384), "nvfp4", 3),
+}
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(HERE, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, or None when
+    the kernel sources changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
+    h = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    if not m or not h or h.group(1) != kernel_source_hash():
+        return None
+    return int(m.group(1))
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="mxfp8_dim0_dim1_16384", choices=sorted(CONFIGS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--copy", action="store_true", help="run the byte-counter calibration copy")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the cast shards by rows with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_scaled_precision_bf16_amd as mx
+    import workloads as W
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    if args.copy:
+        n = 512 * 1024 * 1024
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
+        return
+
+    key, (M, K), kind, dirs = CONFIGS[args.config]
+    print(f"[bench] generating {args.config} inputs {M}x{K}", file=sys.stderr, flush=True)
+    inputs = W.make(key)
+    if kind == "mx_gelu" or kind == "mx_dgelu":
+        x_h, g_h = inputs
+    else:
+        x_h, g_h = inputs, None
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+    x = to_dev(x_h)
+    grad = to_dev(g_h) if g_h is not None else None
+
+    # outputs and workspace allocated once, outside the timed region
+    if kind == "nvfp4":
+        amax = mx.mx_absmax_bf16(x)
+        out = mx.nvfp4_quantize_transpose(x, amax)
+        step = lambda: mx.nvfp4_quantize_transpose(x, amax, out=out)
+        alg_bytes = nvfp4_bytes(M, K, 2)
+        desc = dict(workload=args.config, M=M, K=K, block=16, directions="row+transpose",
+                    format="nvfp4 (e2m1 + e4m3 scales + fp32 tensor scale)")
+    elif kind.startswith("gated"):
+        act = mx.GATED_SWIGLU if kind.endswith("swiglu") else mx.GATED_GEGLU
+        out = mx.mx_quantize_gated(x, act)
+        step = lambda: mx.mx_quantize_gated(x, act, out=out)
+        N = K // 2
+        alg_bytes = 2 * M * K + 2 * (M * N + M * N // 32)
+        desc = dict(workload=args.config, M=M, K=K, N=N, block=32, directions="row+col",
+                    format="mxfp8 e4m3 + e8m0", activation=kind.split("_")[1])
+    else:
+        axis = mx.COLWISE if dirs == 2 else mx.ROWWISE | mx.COLWISE
+        fusion = {"mx": mx.FUSE_NONE, "mx_gelu": mx.FUSE_GELU | mx.FUSE_DBIAS,
+                  "mx_dgelu": mx.FUSE_DGELU | mx.FUSE_DBIAS}[kind]
+        ws = torch.empty(max(16, mx.mx_quantize_workspace_size(M, K, axis, fusion)),
+                         dtype=torch.uint8, device=dev)
+        out = mx.mx_quantize(x, grad, axis=axis, fusion=fusion, workspace=ws)
+        step = lambda: mx.mx_quantize(x, grad, axis=axis, fusion=fusion, out=out, workspace=ws)
+        ndir = 1 if dirs == 2 else 2
+        alg_bytes = mx_bytes(M, K, ndir, extra_inputs=1 if kind == "mx_dgelu" else 0)
+        if fusion & mx.FUSE_DBIAS:
+            alg_bytes += 4 * K
+        desc = dict(workload=args.config, M=M, K=K, block=32,
+                    directions="col" if ndir == 1 else "row+col", format="mxfp8 e4m3 + e8m0",
+                    fusion={"mx": "none", "mx_gelu": "gelu+dbias", "mx_dgelu": "dgelu+dbias"}[kind])
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = sorted(s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends))   # us per launch
+    mean_us = sum(per) / len(per)
+    median_us = per[len(per) // 2]
+    gbs = alg_bytes / (mean_us * 1e3)
+
+    # cold-cache spot check: a 1 GiB fill (larger than the 256 MB MALL) before each call
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(5):
+        flush.fill_(0)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        step()
+        e.record(stream)
+        torch.cuda.synchronize()
+        cold.append(s.elapsed_time(e) * 1e3)
+    del flush
+    cold_us = sorted(cold)[len(cold) // 2]
+
+    traffic = measured_traffic() if args.config == "mxfp8_dim0_dim1_16384" else None
+    result = {
+        "metric": "MXFP8 cast GB/s (bytes rd+wr / kernel us) and % HBM peak at 16384^2 bf16",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": desc,
+        "us_per_launch": {"mean": round(mean_us, 2), "median": round(median_us, 2),
+                          "p10": round(per[len(per) // 10], 2), "p90": round(per[(9 * len(per)) // 10], 2),
+                          "cold_median": round(cold_us, 2)},
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "algorithmic_bytes": alg_bytes,
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "kernel_source_sha256": kernel_source_hash(),
+    }
+
+    if not args.no_cpu:
+        import oracle as O
+        cores = min(16, len(os.sched_getaffinity(0)))
+        O.set_threads(cores)
+        rows = 4096 if M >= 4096 else M
+        xs = np.ascontiguousarray(x_h[:rows])
+        print(f"[bench] oracle CPU baseline on {rows}x{K} rows, {cores} threads",
+              file=sys.stderr, flush=True)
+        t0 = time.perf_counter()
+        if kind == "nvfp4":
+            O.nvfp4_quantize_transpose(xs, tensor_amax=O.absmax(x_h))
+            sb = nvfp4_bytes(rows, K, 2)
+        elif kind.startswith("gated"):
+            O.mx_quantize_gated(xs, mx.GATED_SWIGLU if kind.endswith("swiglu") else mx.GATED_GEGLU)
+            sb = 2 * rows * K + 2 * (rows * (K // 2) + rows * (K // 2) // 32)
+        else:
+            gs = np.ascontiguousarray(g_h[:rows]) if g_h is not None else None
+            O.mx_quantize(xs, grad=gs, axis=axis, fusion=fusion)
+            sb = mx_bytes(rows, K, ndir, extra_inputs=1 if kind == "mx_dgelu" else 0)
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(sb / (dt * 1e9), 3), "unit": "GB/s",
+                                  "cores": cores, "kind": "oracle",
+                                  "sample": f"first {rows} of {M} rows ({rows}x{K}), same recipe and seed",
+                                  "seconds": round(dt, 3), "cpu": cpu_model()}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,264 @@
+// api.cpp -- the extern "C" entry points of libmxcast (declared and
+// documented in include/mxcast.h): argument validation on the host, then one
+// or two kernel launches on the caller's stream.  Validation is pure host
+// code that runs before any HIP call, so a rejected call touches neither the
+// device nor the runtime.
+
+#include "mxcast.h"
+
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Span {
+    const void *p;
+    uint64_t n;   // bytes
+};
+
+bool overlap(const Span &a, const Span &b)
+{
+    if (!a.p || !b.p || a.n == 0 || b.n == 0)
+        return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+// Every output must be disjoint from every input and from every other output.
+bool any_alias(const Span *in, int nin, const Span *out, int nout)
+{
+    for (int i = 0; i < nout; i++) {
+        for (int j = 0; j < nin; j++)
+            if (overlap(out[i], in[j]))
+                return true;
+        for (int j = i + 1; j < nout; j++)
+            if (overlap(out[i], out[j]))
+                return true;
+    }
+    return false;
+}
+
+bool shape_ok(int64_t M, int64_t K, int64_t block)
+{
+    return M > 0 && K > 0 && M % block == 0 && K % block == 0 && M <= kMaxDim && K <= kMaxDim &&
+           M * K <= kMaxElems;
+}
+
+int tiles(int64_t n, int64_t t) { return (int)((n + t - 1) / t); }
+
+size_t dbias_workspace(int64_t M, int64_t K)
+{
+    return (size_t)tiles(M, mxk::kTileM) * (size_t)K * sizeof(float);
+}
+
+mx_status from_hip(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int mx_abi_version(void) { return MXCAST_ABI_VERSION; }
+
+const char *mx_status_str(int s)
+{
+    switch (s) {
+    case MX_OK: return "MX_OK";
+    case MX_ERR_NULL: return "MX_ERR_NULL: a required pointer is NULL";
+    case MX_ERR_ENUM: return "MX_ERR_ENUM: unknown axis mask, fusion or activation";
+    case MX_ERR_SHAPE: return "MX_ERR_SHAPE: size not a positive multiple of the block size, or too large";
+    case MX_ERR_ALIGN: return "MX_ERR_ALIGN: pointer not 16-byte aligned";
+    case MX_ERR_WORKSPACE: return "MX_ERR_WORKSPACE: workspace missing or too small";
+    case MX_ERR_ALIAS: return "MX_ERR_ALIAS: an output overlaps an input or another output";
+    case MX_ERR_HIP: return "MX_ERR_HIP: kernel launch failed";
+    case MX_ERR_UNSUPPORTED: return "MX_ERR_UNSUPPORTED";
+    default: return "unknown mx_status";
+    }
+}
+
+size_t mx_quantize_workspace_size(int64_t M, int64_t K, unsigned axis_mask, int fusion)
+{
+    if (!(fusion & MX_FUSE_DBIAS) || !shape_ok(M, K, 32) || axis_mask == 0 || (axis_mask & ~3u))
+        return 0;
+    return dbias_workspace(M, K);
+}
+
+mx_status mx_quantize(const void *x, const void *grad, int64_t M, int64_t K, unsigned axis_mask,
+                      int fusion, uint8_t *q_row, uint8_t *s_row, uint8_t *q_col, uint8_t *s_col,
+                      float *dbias, void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    const int pre = fusion & 0xF;
+    const bool want_dbias = (fusion & MX_FUSE_DBIAS) != 0;
+    if (axis_mask == 0 || (axis_mask & ~3u) || (fusion & ~0x1F) || pre > MX_FUSE_DGELU)
+        return MX_ERR_ENUM;
+    const bool row = axis_mask & MX_ROWWISE, col = axis_mask & MX_COLWISE;
+    if (!x || (pre == MX_FUSE_DGELU && !grad) || (row && (!q_row || !s_row)) ||
+        (col && (!q_col || !s_col)) || (want_dbias && !dbias))
+        return MX_ERR_NULL;
+    if (!shape_ok(M, K, 32))
+        return MX_ERR_SHAPE;
+    if (!aligned(x, 16) || (pre == MX_FUSE_DGELU && !aligned(grad, 16)) ||
+        (row && (!aligned(q_row, 16) || !aligned(s_row, 16))) ||
+        (col && (!aligned(q_col, 16) || !aligned(s_col, 16))) ||
+        (want_dbias && (!aligned(dbias, 4) || (workspace && !aligned(workspace, 16)))))
+        return MX_ERR_ALIGN;
+    const size_t need = want_dbias ? dbias_workspace(M, K) : 0;
+    if (want_dbias && (!workspace || workspace_bytes < need))
+        return MX_ERR_WORKSPACE;
+    const uint64_t n = (uint64_t)(M * K);
+    const Span in[2] = {{x, 2 * n}, {pre == MX_FUSE_DGELU ? grad : nullptr, 2 * n}};
+    const Span out[6] = {{row ? q_row : nullptr, n}, {row ? s_row : nullptr, n / 32},
+                         {col ? q_col : nullptr, n}, {col ? s_col : nullptr, n / 32},
+                         {want_dbias ? dbias : nullptr, 4 * (uint64_t)K},
+                         {want_dbias ? workspace : nullptr, need}};
+    if (any_alias(in, 2, out, 6))
+        return MX_ERR_ALIAS;
+
+    mxk::MxArgs a;
+    a.x = static_cast<const uint16_t *>(x);
+    a.aux = static_cast<const uint16_t *>(grad);
+    a.M = M;
+    a.K = K;
+    a.ldx = K;
+    a.lin_off = 0;
+    a.q_row = q_row;
+    a.s_row = s_row;
+    a.q_col = q_col;
+    a.s_col = s_col;
+    a.partials = want_dbias ? static_cast<float *>(workspace) : nullptr;
+    a.tiles_k = tiles(K, mxk::kTileK);
+    a.tiles_m = tiles(M, mxk::kTileM);
+    mx_status st = from_hip(mxk::launch_mx_cast(pre, axis_mask, want_dbias, a, stream));
+    if (st != MX_OK || !want_dbias)
+        return st;
+    return from_hip(mxk::launch_dbias_reduce(a.partials, a.tiles_m, K, dbias, stream));
+}
+
+mx_status mx_quantize_gated(const void *x, int64_t M, int64_t N, unsigned axis_mask, int act,
+                            uint8_t *q_row, uint8_t *s_row, uint8_t *q_col, uint8_t *s_col,
+                            hipStream_t stream)
+{
+    if (axis_mask == 0 || (axis_mask & ~3u) || (act != MX_GATED_SWIGLU && act != MX_GATED_GEGLU))
+        return MX_ERR_ENUM;
+    const bool row = axis_mask & MX_ROWWISE, col = axis_mask & MX_COLWISE;
+    if (!x || (row && (!q_row || !s_row)) || (col && (!q_col || !s_col)))
+        return MX_ERR_NULL;
+    if (!shape_ok(M, N, 32) || !shape_ok(M, 2 * N, 32))
+        return MX_ERR_SHAPE;
+    if (!aligned(x, 16) || (row && (!aligned(q_row, 16) || !aligned(s_row, 16))) ||
+        (col && (!aligned(q_col, 16) || !aligned(s_col, 16))))
+        return MX_ERR_ALIGN;
+    const uint64_t n = (uint64_t)(M * N);
+    const Span in[1] = {{x, 4 * n}};
+    const Span out[4] = {{row ? q_row : nullptr, n}, {row ? s_row : nullptr, n / 32},
+                         {col ? q_col : nullptr, n}, {col ? s_col : nullptr, n / 32}};
+    if (any_alias(in, 1, out, 4))
+        return MX_ERR_ALIAS;
+
+    mxk::MxArgs a;
+    a.x = static_cast<const uint16_t *>(x);
+    a.aux = nullptr;
+    a.M = M;
+    a.K = N;
+    a.ldx = 2 * N;
+    a.lin_off = N;
+    a.q_row = q_row;
+    a.s_row = s_row;
+    a.q_col = q_col;
+    a.s_col = s_col;
+    a.partials = nullptr;
+    a.tiles_k = tiles(N, mxk::kTileK);
+    a.tiles_m = tiles(M, mxk::kTileM);
+    const int op = act == MX_GATED_SWIGLU ? mxk::OP_SWIGLU : mxk::OP_GEGLU;
+    return from_hip(mxk::launch_mx_cast(op, axis_mask, false, a, stream));
+}
+
+mx_status mx_fused_values(const void *x, const void *grad, int64_t M, int64_t K, int op, void *y,
+                          hipStream_t stream)
+{
+    int kop;
+    switch (op) {
+    case MX_FUSE_GELU: kop = mxk::OP_GELU; break;
+    case MX_FUSE_DGELU: kop = mxk::OP_DGELU; break;
+    case MX_OP_GATED | MX_GATED_SWIGLU: kop = mxk::OP_SWIGLU; break;
+    case MX_OP_GATED | MX_GATED_GEGLU: kop = mxk::OP_GEGLU; break;
+    default: return MX_ERR_ENUM;
+    }
+    const bool gated = (op & MX_OP_GATED) != 0;
+    if (!x || !y || (kop == mxk::OP_DGELU && !grad))
+        return MX_ERR_NULL;
+    if (!shape_ok(M, K, 32) || (gated && !shape_ok(M, 2 * K, 32)))
+        return MX_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(y, 16) || (kop == mxk::OP_DGELU && !aligned(grad, 16)))
+        return MX_ERR_ALIGN;
+    const uint64_t n = (uint64_t)(M * K);
+    const Span in[2] = {{x, gated ? 4 * n : 2 * n}, {kop == mxk::OP_DGELU ? grad : nullptr, 2 * n}};
+    const Span out[1] = {{y, 2 * n}};
+    if (any_alias(in, 2, out, 1))
+        return MX_ERR_ALIAS;
+    return from_hip(mxk::launch_fused_values(kop, static_cast<const uint16_t *>(x),
+                                             static_cast<const uint16_t *>(grad), M, K,
+                                             static_cast<uint16_t *>(y), stream));
+}
+
+mx_status mx_absmax_bf16(const void *x, int64_t n, float *amax, hipStream_t stream)
+{
+    if (!x || !amax)
+        return MX_ERR_NULL;
+    if (n <= 0 || n > kMaxElems)
+        return MX_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(amax, 4))
+        return MX_ERR_ALIGN;
+    const Span in[1] = {{x, 2 * (uint64_t)n}};
+    const Span out[1] = {{amax, 4}};
+    if (any_alias(in, 1, out, 1))
+        return MX_ERR_ALIAS;
+    return from_hip(mxk::launch_absmax(static_cast<const uint16_t *>(x), n, amax, stream));
+}
+
+mx_status nvfp4_quantize_transpose(const void *x, int64_t M, int64_t K, const float *amax,
+                                   unsigned axis_mask, uint8_t *q_row, uint8_t *s_row,
+                                   uint8_t *q_col, uint8_t *s_col, float *global_scale_out,
+                                   hipStream_t stream)
+{
+    if (axis_mask == 0 || (axis_mask & ~3u))
+        return MX_ERR_ENUM;
+    const bool row = axis_mask & MX_ROWWISE, col = axis_mask & MX_COLWISE;
+    if (!x || !amax || (row && (!q_row || !s_row)) || (col && (!q_col || !s_col)))
+        return MX_ERR_NULL;
+    if (!shape_ok(M, K, 16))
+        return MX_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(amax, 4) ||
+        (row && (!aligned(q_row, 16) || !aligned(s_row, 16))) ||
+        (col && (!aligned(q_col, 16) || !aligned(s_col, 16))) ||
+        (global_scale_out && !aligned(global_scale_out, 4)))
+        return MX_ERR_ALIGN;
+    const uint64_t n = (uint64_t)(M * K);
+    const Span in[2] = {{x, 2 * n}, {amax, 4}};
+    const Span out[5] = {{row ? q_row : nullptr, n / 2}, {row ? s_row : nullptr, n / 16},
+                         {col ? q_col : nullptr, n / 2}, {col ? s_col : nullptr, n / 16},
+                         {global_scale_out, 4}};
+    if (any_alias(in, 2, out, 5))
+        return MX_ERR_ALIAS;
+
+    mxk::Nv4Args a;
+    a.x = static_cast<const uint16_t *>(x);
+    a.M = M;
+    a.K = K;
+    a.amax = amax;
+    a.q_row = q_row;
+    a.s_row = s_row;
+    a.q_col = q_col;
+    a.s_col = s_col;
+    a.sg_out = global_scale_out;
+    a.tiles_k = tiles(K, mxk::kTileK);
+    a.tiles_m = tiles(M, mxk::kTileM);
+    return from_hip(mxk::launch_nvfp4(axis_mask, a, stream));
+}
+
+}  // extern "C"

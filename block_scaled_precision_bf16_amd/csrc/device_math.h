@@ -1,0 +1,241 @@
+// device_math.h -- per-element and per-block arithmetic of the cast kernels
+// (gfx950).  Everything here is exact integer work or a fixed sequence of
+// IEEE fp32 operations, so results are reproducible bit for bit.  The whole
+// library is compiled with -ffp-contract=off: every a*b+c below is two
+// roundings unless written as __builtin_fmaf.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace mxk {
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float f32_bits(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t bits_f32(float f) { return __float_as_uint(f); }
+
+// bf16 halves of a packed word, widened exactly to fp32.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return f32_bits(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return f32_bits(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN -> canonical quiet NaN.
+__device__ __forceinline__ uint32_t bf16_rne(float f)
+{
+    uint32_t u = bits_f32(f);
+    uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? 0x7FC0u : r;
+}
+
+// Lane-wise max of the two 15-bit magnitudes packed in a word of bf16 pairs.
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b)
+{
+    u16x2 va = __builtin_bit_cast(u16x2, a), vb = __builtin_bit_cast(u16x2, b);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(va, vb));
+}
+
+// ---------------------------------------------------------------------------
+// MXFP8 scale: E8M0 byte from the largest |bf16| of a block, given as its
+// 15-bit magnitude pattern.  For a finite amax the exponent field E equals
+// floor(log2 amax) + 127 (normal) or 0 (subnormal, where the clamp applies),
+// so byte = max(E - 8, 0): 8 is the exponent of E4M3's largest binade.
+// Inf / NaN (pattern >= 0x7F80) -> 0xFF.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e8m0_from_mag(uint32_t mag)
+{
+    int e = (int)(mag >> 7) - 8;
+    uint32_t b = e > 0 ? (uint32_t)e : 0u;
+    return mag >= 0x7F80u ? 0xFFu : b;
+}
+
+// 2^(127 - byte) as an fp32 (a normal number for every byte <= 253): the
+// exact inverse of the block scale, so each element costs one multiply
+// ("Multiply with inverse scale in loop inside of dividing", body bullets).
+__device__ __forceinline__ float e8m0_inverse(uint32_t byte)
+{
+    return f32_bits(((254u - byte) & 0xFFu) << 23);
+}
+
+// ---------------------------------------------------------------------------
+// fp32 -> E4M3 ("fn": bias 7, max 448, no Inf), round to nearest with ties to
+// the even code, saturating, sign kept.  Normal range: round the 23-bit
+// significand to 3 bits at bit 20 and rebias the exponent (127 -> 7);
+// subnormal range (< 2^-6, spacing 2^-9): the code is |v| * 2^9 rounded to an
+// integer (0..8, where 8 is the smallest normal).  NaN is never passed in.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float v)
+{
+    uint32_t u = bits_f32(v);
+    uint32_t sign = (u >> 24) & 0x80u;
+    uint32_t a = u & 0x7FFFFFFFu;
+    uint32_t nrm = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
+    uint32_t sub = (uint32_t)__builtin_rintf(f32_bits(a) * 512.0f);
+    uint32_t code = a < 0x3C800000u ? sub : nrm;
+    code = a >= 0x43E00000u ? 0x7Eu : code;
+    return sign | code;
+}
+
+// E4M3 code (no NaN) -> its exact fp32 value.
+__device__ __forceinline__ float e4m3_value(uint32_t c)
+{
+    uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+    float mag = e ? f32_bits(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+    return (c & 0x80u) ? -mag : mag;
+}
+
+// fp32 -> E2M1 nibble: magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}, nearest with
+// ties to the even code, saturating at 6 (Inf too), sign in bit 3, NaN -> 0.
+// Each comparison is one decision boundary; ">" at a tie whose lower code is
+// even, ">=" where the upper code is even.
+__device__ __forceinline__ uint32_t e2m1_rne_sat(float v)
+{
+    uint32_t u = bits_f32(v);
+    uint32_t a = u & 0x7FFFFFFFu;
+    float x = f32_bits(a);
+    uint32_t c = (uint32_t)(x > 0.25f) + (uint32_t)(x >= 0.75f) + (uint32_t)(x > 1.25f) +
+                 (uint32_t)(x >= 1.75f) + (uint32_t)(x > 2.5f) + (uint32_t)(x >= 3.5f) +
+                 (uint32_t)(x > 5.0f);
+    c |= (u >> 28) & 8u;
+    return a > 0x7F800000u ? 0u : c;
+}
+
+// ---------------------------------------------------------------------------
+// Fused pre-op arithmetic.  Each statement is one IEEE fp32 operation.
+// ---------------------------------------------------------------------------
+
+// e^a: Cody & Waite reduction a = n ln2 + r (ln2 = 355/512 + remainder), the
+// degree-7 Taylor polynomial of e^r by Horner with fused multiply-adds, and
+// scaling by 2^n as two exact power-of-two factors (one final rounding, also
+// for subnormal results).
+__device__ __forceinline__ float exp32(float a)
+{
+    const float LOG2E = 1.44269504088896340736f;
+    const float LN2_A = 0.693359375f;                 // 355/512
+    const float LN2_B = -2.12194440054690583e-4f;     // ln2 - 355/512
+    if (a != a)
+        return a;
+    if (a > 88.72283172607421875f)
+        return __builtin_inff();
+    if (a < -104.0f)
+        return 0.0f;
+    float n = __builtin_rintf(a * LOG2E);
+    float r = __builtin_fmaf(n, -LN2_A, a);
+    r = __builtin_fmaf(n, -LN2_B, r);
+    float p = (float)(1.0 / 5040.0);
+    p = __builtin_fmaf(p, r, (float)(1.0 / 720.0));
+    p = __builtin_fmaf(p, r, (float)(1.0 / 120.0));
+    p = __builtin_fmaf(p, r, (float)(1.0 / 24.0));
+    p = __builtin_fmaf(p, r, (float)(1.0 / 6.0));
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    int ni = (int)n;
+    int n1 = ni / 2, n2 = ni - n1;
+    return (p * f32_bits((uint32_t)(n1 + 127) << 23)) * f32_bits((uint32_t)(n2 + 127) << 23);
+}
+
+// sigma(z) = 1/(1+e^-z) and 1 - sigma(z) from e = e^-|z| (no overflow, no
+// cancellation): z >= 0 gives (1/(1+e), e/(1+e)), z < 0 the swapped pair.
+__device__ __forceinline__ void sigmoid_pair(float z, float &s, float &sc)
+{
+    float e = exp32(-__builtin_fabsf(z));
+    float d = 1.0f + e;
+    float r = 1.0f / d;
+    float er = e * r;
+    s = z >= 0.0f ? r : er;
+    sc = z >= 0.0f ? er : r;
+}
+
+constexpr float K_SQRT_2_OVER_PI = 0.797884560802865355879892119868763737f;
+constexpr float K_CUBIC = 0.044715f;
+constexpr float K_CUBIC3 = 0.134145f;
+constexpr float K_2SQRT_2_OVER_PI = 1.59576912160573071175978423973752747f;
+
+// tanh-form GELU: x * sigma(2u), u = sqrt(2/pi)(x + 0.044715 x^3); this equals
+// 0.5 x (1 + tanh u).
+__device__ __forceinline__ float gelu32(float x)
+{
+    float x2 = x * x;
+    float x3 = x2 * x;
+    float inner = __builtin_fmaf(K_CUBIC, x3, x);
+    float u = K_SQRT_2_OVER_PI * inner;
+    float s, sc;
+    sigmoid_pair(u + u, s, sc);
+    return x * s;
+}
+
+// d/dx of gelu32's function: sigma + x sigma (1 - sigma) 2u'(x), with
+// 2u'(x) = 2 sqrt(2/pi) (1 + 3 * 0.044715 x^2); the second term is 0 when
+// sigma(1 - sigma) is 0.
+__device__ __forceinline__ float dgelu32(float x)
+{
+    float x2 = x * x;
+    float x3 = x2 * x;
+    float inner = __builtin_fmaf(K_CUBIC, x3, x);
+    float u = K_SQRT_2_OVER_PI * inner;
+    float s, sc;
+    sigmoid_pair(u + u, s, sc);
+    float ss = s * sc;
+    float du = K_2SQRT_2_OVER_PI * __builtin_fmaf(K_CUBIC3, x2, 1.0f);
+    float t = ss == 0.0f ? 0.0f : (x * ss) * du;
+    return s + t;
+}
+
+__device__ __forceinline__ float silu32(float g)
+{
+    float s, sc;
+    sigmoid_pair(g, s, sc);
+    return g * s;
+}
+
+// y (bf16 bits) for one element.  a = x (or gate), b = grad (or linear).
+template <int OP>
+__device__ __forceinline__ uint32_t fused_value(float a, float b)
+{
+    if constexpr (OP == OP_GELU)
+        return bf16_rne(gelu32(a));
+    else if constexpr (OP == OP_DGELU)
+        return bf16_rne(dgelu32(a) * b);
+    else if constexpr (OP == OP_SWIGLU)
+        return bf16_rne(silu32(a) * b);
+    else
+        return bf16_rne(gelu32(a) * b);
+}
+
+// Apply the pre-op to a packed pair of bf16 (and its partner pair).
+template <int OP>
+__device__ __forceinline__ uint32_t fused_pair(uint32_t a, uint32_t b)
+{
+    uint32_t lo = fused_value<OP>(bf16_lo(a), bf16_lo(b));
+    uint32_t hi = fused_value<OP>(bf16_hi(a), bf16_hi(b));
+    return lo | (hi << 16);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane max within aligned groups of 2 / 4 lanes (DPP quad permutes,
+// no LDS traffic).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t max_xor1(uint32_t v)
+{
+    uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false); // [1,0,3,2]
+    return v > o ? v : o;
+}
+__device__ __forceinline__ uint32_t max_xor2(uint32_t v)
+{
+    uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false); // [2,3,0,1]
+    return v > o ? v : o;
+}
+
+// Hardware dispatches workgroup i to XCD (i mod 8).  Give each XCD a
+// contiguous range of logical tiles so that neighbouring tiles (which share
+// scale-tensor cache lines) are written through the same L2.
+__device__ __forceinline__ int xcd_tile(int bid, int nblocks)
+{
+    int per = nblocks >> 3, rem = nblocks & 7;
+    int xcd = bid & 7, slot = bid >> 3;
+    return xcd * per + (xcd < rem ? xcd : rem) + slot;
+}
+
+}  // namespace mxk

@@ -1,0 +1,54 @@
+// launch.h -- internal interface between the host API (api.cpp) and the
+// kernel translation units.  Not installed; the public ABI is mxcast.h.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace mxk {
+
+// Elementwise pre-op of a cast kernel.
+enum Op : int { OP_PLAIN = 0, OP_GELU = 1, OP_DGELU = 2, OP_SWIGLU = 3, OP_GEGLU = 4 };
+
+// Workgroup tile of the cast kernels.  A lane owns 16 rows x 8 columns; the
+// two halves of a wave (lanes 0-31, 32-63) own rows 0-15 and 16-31 of the
+// same 256 columns, so a wave covers 32 rows (one MXFP8 column block) and a
+// workgroup of 4 waves covers 128 rows x 256 columns.
+constexpr int kRowsPerLane = 16;
+constexpr int kColsPerLane = 8;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTileM = 2 * kRowsPerLane * kWaves;  // 128
+constexpr int kTileK = kColsPerLane * 32;          // 256
+
+struct MxArgs {
+    const uint16_t *x;     // input (gated: [M][2N] with the linear half at lin_off)
+    const uint16_t *aux;   // grad for dGELU, else unused
+    int64_t M, K;          // rows and columns of the quantised tensor
+    int64_t ldx;           // row stride of x in elements
+    int64_t lin_off;       // gated: column offset of the linear half
+    uint8_t *q_row, *s_row, *q_col, *s_col;
+    float *partials;       // dbias: [tiles_m][K] fp32 column partial sums
+    int tiles_k, tiles_m;
+};
+
+struct Nv4Args {
+    const uint16_t *x;
+    int64_t M, K;
+    const float *amax;
+    uint8_t *q_row, *s_row, *q_col, *s_col;
+    float *sg_out;
+    int tiles_k, tiles_m;
+};
+
+// op: 0 plain, 1 GELU, 2 dGELU, 3 SwiGLU, 4 GeGLU.
+hipError_t launch_mx_cast(int op, unsigned axis, bool dbias, const MxArgs &a, hipStream_t s);
+hipError_t launch_dbias_reduce(const float *partials, int tiles_m, int64_t K, float *dbias,
+                               hipStream_t s);
+// op as above (1..4); gated ops read x[M][2K].
+hipError_t launch_fused_values(int op, const uint16_t *x, const uint16_t *aux, int64_t M,
+                               int64_t K, uint16_t *y, hipStream_t s);
+hipError_t launch_absmax(const uint16_t *x, int64_t n, float *amax, hipStream_t s);
+hipError_t launch_nvfp4(unsigned axis, const Nv4Args &a, hipStream_t s);
+
+}  // namespace mxk

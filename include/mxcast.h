@@ -1,0 +1,174 @@
+/*
+ * mxcast.h -- C ABI of libmxcast: block-scaled quantisation of bf16 tensors
+ * on MI355X (gfx950).
+ *
+ * The operations are the cast kernels that the pages measure:
+ *   - MXFP8 cast, row-wise, column-wise (into the transposed layout) or both
+ *     in one pass, optionally fused with a GELU / dGELU pre-op and a dbias
+ *     column sum ("[Common] Fix pointer arithmatic to generate correct
+ *     LDS/STS instructions", TransformerEngine PR 3291: tables "MXFP8 generic
+ *     quantize kernel" and "MXFP8 specialized cast-only kernel
+ *     (bidimensional)"; torchao PR 12 "Multiply with inverse scale in loop
+ *     inside of dividing to improve perf": the dim1 cast and its inverse-scale
+ *     multiply);
+ *   - gated MXFP8 cast of act(gate) * linear with SwiGLU or GeGLU (PR 3291,
+ *     table "MXFP8 gated (swiglu / geglu) kernel");
+ *   - NVFP4 quantize-transpose with 16-element blocks (PR 3291, the NVFP4
+ *     quantize-transpose kernels under "Important Files Changed" and
+ *     "Patched but not measurable").
+ *
+ * Numerics (the pages name these formats but do not define their
+ * arithmetic; these are the readings the library implements bit-exactly):
+ *   MXFP8 block of 32: amax = max|y|; scale byte (E8M0) = floor(log2 amax) - 8
+ *     + 127 clamped to [0, 254]; element = E4M3(y * 2^(127 - byte)), round
+ *     to nearest, ties to even code, saturating at +-448, sign kept.  A block
+ *     holding Inf/NaN gets scale 0xFF and elements 0x7F.
+ *   Fused pre-ops: evaluated in fp32 (tanh-form GELU through
+ *     0.5(1+tanh u) = 1/(1+e^-2u), the library's own exp), rounded once to
+ *     bf16; that bf16 tensor y is what is quantised and what dbias sums.
+ *   NVFP4: S_g = fl32(amax / 2688) (1 if amax = 0); per block of 16:
+ *     s = E4M3(fl32(fl32(b/6)/S_g)), inv = fl32(1/fl32(decode(s)*S_g)) (0 if
+ *     the product is 0), element = E2M1(fl32(x*inv)), nearest, ties to even,
+ *     saturating at +-6.
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library never allocates, frees or synchronises.  Work is enqueued on
+ *     `stream` (NULL = the default stream) and completes asynchronously.
+ *   - bf16 tensors are raw 16-bit patterns; E4M3, E8M0 and packed E2M1 are
+ *     raw bytes.  Every tensor is row-major and contiguous.
+ *   - Column-wise outputs are transposed: for x[M][K], q_col is [K][M] and
+ *     s_col is [K][M/32] (MXFP8) or q_col [K][M/2], s_col [K][M/16] (NVFP4).
+ *   - Every pointer must be 16-byte aligned (dbias: 4-byte).
+ *   - Arguments are validated on the host before anything is enqueued; on a
+ *     validation error nothing is written and a non-zero status returns.
+ *     Launch failures return MX_ERR_HIP.  Device faults surface at the
+ *     caller's next synchronisation.
+ *   - Calls hold no state and are safe from several host threads.
+ */
+#ifndef MXCAST_H
+#define MXCAST_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MXCAST_ABI_VERSION 1
+
+typedef enum mx_status {
+    MX_OK = 0,
+    MX_ERR_NULL = 1,        /* a required pointer is NULL                     */
+    MX_ERR_ENUM = 2,        /* unknown axis mask, fusion or activation        */
+    MX_ERR_SHAPE = 3,       /* non-positive size, or not a multiple of the    */
+                            /* block size (32 MXFP8, 16 NVFP4), or too large  */
+    MX_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned               */
+    MX_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required     */
+    MX_ERR_ALIAS = 6,       /* an output overlaps an input or another output  */
+    MX_ERR_HIP = 7,         /* the HIP runtime reported a launch error        */
+    MX_ERR_UNSUPPORTED = 8  /* valid request this build does not implement    */
+} mx_status;
+
+/* axis_mask bits */
+#define MX_ROWWISE 1u       /* blocks along K: q_row[M][K], s_row[M][K/32]    */
+#define MX_COLWISE 2u       /* blocks along M, transposed outputs             */
+
+/* fusion: a pre-op in the low bits, optionally OR-ed with MX_FUSE_DBIAS */
+#define MX_FUSE_NONE 0
+#define MX_FUSE_GELU 1      /* y = GELU(x)                                    */
+#define MX_FUSE_DGELU 2     /* y = GELU'(x) * grad                            */
+#define MX_FUSE_DBIAS 0x10  /* also write dbias[k] = sum_m y[m][k] (fp32)     */
+
+/* gated activation */
+#define MX_GATED_SWIGLU 1   /* y = silu(gate) * linear                        */
+#define MX_GATED_GEGLU 2    /* y = gelu(gate) * linear                        */
+
+/*
+ * MXFP8 cast of x[M][K] (bf16), block size 32.
+ *   x        device, bf16 [M][K]
+ *   grad     device, bf16 [M][K]; required for MX_FUSE_DGELU, else ignored
+ *   M, K     rows, columns; positive multiples of 32, each <= 2^30, M*K <= 2^40
+ *   axis_mask  MX_ROWWISE, MX_COLWISE or both (one pass over x)
+ *   fusion   MX_FUSE_NONE | GELU | DGELU, optionally | MX_FUSE_DBIAS
+ *   q_row, s_row  E4M3 [M][K] and E8M0 [M][K/32]; required iff MX_ROWWISE
+ *   q_col, s_col  E4M3 [K][M] and E8M0 [K][M/32]; required iff MX_COLWISE
+ *   dbias    fp32 [K]; required iff MX_FUSE_DBIAS
+ *   workspace, workspace_bytes  device scratch of at least
+ *            mx_quantize_workspace_size() bytes (0 unless MX_FUSE_DBIAS);
+ *            its contents on entry are ignored and on exit are undefined
+ *   stream   HIP stream
+ * With MX_FUSE_DBIAS a second, small kernel reduces per-tile column partial
+ * sums (fp32, fixed order) into dbias, so results are run-to-run identical.
+ */
+mx_status mx_quantize(const void *x, const void *grad, int64_t M, int64_t K,
+                      unsigned axis_mask, int fusion,
+                      uint8_t *q_row, uint8_t *s_row, uint8_t *q_col, uint8_t *s_col,
+                      float *dbias, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* Bytes of workspace mx_quantize needs for these arguments (0 without dbias;
+ * 0 also for invalid arguments). */
+size_t mx_quantize_workspace_size(int64_t M, int64_t K, unsigned axis_mask, int fusion);
+
+/*
+ * Gated MXFP8 cast.  x is bf16 [M][2N] holding [gate | linear] (gate =
+ * columns 0..N-1); the quantised tensor is y[M][N] = act(gate) * linear,
+ * block size 32, M and N positive multiples of 32.
+ *   q_row, s_row  E4M3 [M][N], E8M0 [M][N/32]   (iff MX_ROWWISE)
+ *   q_col, s_col  E4M3 [N][M], E8M0 [N][M/32]   (iff MX_COLWISE)
+ */
+mx_status mx_quantize_gated(const void *x, int64_t M, int64_t N, unsigned axis_mask, int act,
+                            uint8_t *q_row, uint8_t *s_row, uint8_t *q_col, uint8_t *s_col,
+                            hipStream_t stream);
+
+/*
+ * The fused elementwise values alone, as bf16: y = pre-op(x[, grad]) for
+ * op = MX_FUSE_GELU / MX_FUSE_DGELU (x, grad and y are [M][K]), or the gated
+ * value for op = 0x100 | MX_GATED_SWIGLU / MX_GATED_GEGLU (x is [M][2K],
+ * y is [M][K]).  This is the exact tensor the fused casts quantise; it is
+ * exposed so that the pre-op arithmetic can be checked on its own.  M and K
+ * are positive multiples of 32.
+ */
+#define MX_OP_GATED 0x100
+mx_status mx_fused_values(const void *x, const void *grad, int64_t M, int64_t K, int op,
+                          void *y, hipStream_t stream);
+
+/*
+ * Tensor absmax for NVFP4: *amax = max |x_i| over n bf16 elements, as fp32
+ * (exact).  amax is a device pointer to one float; it is first cleared and
+ * then combined with integer atomic max, so the result does not depend on
+ * scheduling.  n > 0, n <= 2^40, x 16-byte aligned.
+ */
+mx_status mx_absmax_bf16(const void *x, int64_t n, float *amax, hipStream_t stream);
+
+/*
+ * NVFP4 quantize-transpose of x[M][K] (bf16), block size 16, M and K positive
+ * multiples of 16.
+ *   amax     device, one fp32: the tensor absmax the global scale is built
+ *            from (e.g. from mx_absmax_bf16 on the same stream)
+ *   q_row, s_row  packed E2M1 [M][K/2] (element 2j in the low nibble of byte
+ *            j), E4M3 [M][K/16]                     (iff MX_ROWWISE)
+ *   q_col, s_col  the same for the transpose: [K][M/2], [K][M/16]
+ *                                                   (iff MX_COLWISE)
+ *   global_scale_out  device, one fp32 receiving S_g; may be NULL
+ */
+mx_status nvfp4_quantize_transpose(const void *x, int64_t M, int64_t K, const float *amax,
+                                   unsigned axis_mask,
+                                   uint8_t *q_row, uint8_t *s_row, uint8_t *q_col, uint8_t *s_col,
+                                   float *global_scale_out, hipStream_t stream);
+
+/* Static string naming a status code. */
+const char *mx_status_str(int status);
+
+/* MXCAST_ABI_VERSION of the built library. */
+int mx_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXCAST_H */

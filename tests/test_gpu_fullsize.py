@@ -1,0 +1,86 @@
+"""The five workloads at full size, in the launch configuration the benchmark
+times, compared with the oracle on every output element (the oracle runs
+these sizes in seconds with OpenMP over rows / columns).
+
+  16384^2 log-uniform rows: dim1 only, and dim0 + dim1 in one pass
+  8192^2 N(0, 2): GELU + dbias, and dGELU(x) * grad + dbias
+  8192 x 8192 [gate | linear]: SwiGLU and GeGLU, both directions
+  16384^2 Student-t with 1% of rows x100: NVFP4 quantize-transpose
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_precision_bf16_amd as mx
+import oracle as O
+import workloads as W
+from gpu_util import assert_dbias_close, mx_outputs_equal, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def threads():
+    O.set_threads(min(16, len(os.sched_getaffinity(0))))
+
+
+@pytest.fixture(scope="module")
+def loguniform16k():
+    return W.make("c2_dim1_16384")
+
+
+def test_c2_dim1_16384(loguniform16k):
+    x = loguniform16k
+    g = mx.mx_quantize(to_dev(x), axis=mx.COLWISE)
+    torch.cuda.synchronize()
+    o = O.mx_quantize(x, axis=mx.COLWISE)
+    mx_outputs_equal(g, o, "C2 dim1")
+
+
+def test_metric_dim0_dim1_16384(loguniform16k):
+    x = loguniform16k
+    g = mx.mx_quantize(to_dev(x), axis=mx.ROWWISE | mx.COLWISE)
+    torch.cuda.synchronize()
+    o = O.mx_quantize(x)
+    mx_outputs_equal(g, o, "dim0+dim1 16384")
+
+
+@pytest.mark.parametrize("pre", [mx.FUSE_GELU, mx.FUSE_DGELU])
+def test_c3_fused_dbias_8192(pre):
+    x, grad = W.make("c3_gelu_dbias_8192")
+    f = pre | mx.FUSE_DBIAS
+    g = mx.mx_quantize(to_dev(x), to_dev(grad), fusion=f)
+    torch.cuda.synchronize()
+    o = O.mx_quantize(x, grad=grad, fusion=f, want_y=True)
+    mx_outputs_equal(g, o, f"C3 pre-op {pre}")
+    ycols = np.abs(W.bf16_to_f32(o["y"]).astype(np.float64)).sum(axis=0)
+    assert_dbias_close(g["dbias"], o["dbias"], ycols)
+
+
+@pytest.mark.parametrize("act", [mx.GATED_SWIGLU, mx.GATED_GEGLU])
+def test_c4_gated_8192(act):
+    x = W.make("c4_gated_8192")
+    g = mx.mx_quantize_gated(to_dev(x), act)
+    torch.cuda.synchronize()
+    o = O.mx_quantize_gated(x, act)
+    mx_outputs_equal(g, o, f"C4 act {act}")
+
+
+def test_c5_nvfp4_16384():
+    x = W.make("c5_nvfp4_16384")
+    xd = to_dev(x)
+    amax = mx.mx_absmax_bf16(xd)
+    g = mx.nvfp4_quantize_transpose(xd, amax)
+    torch.cuda.synchronize()
+    o = O.nvfp4_quantize_transpose(x)
+    assert g["sg"].item() == o["sg"]
+    mx_outputs_equal(g, o, "C5 nvfp4")
+
+
+def test_c1_special_256x512():
+    x = W.special_256x512()
+    g = mx.mx_quantize(to_dev(x))
+    torch.cuda.synchronize()
+    mx_outputs_equal(g, O.mx_quantize(x), "C1")

@@ -1,0 +1,139 @@
+"""GPU parity of the plain MXFP8 cast (mx_quantize, no pre-op) against the CPU
+oracle, element by element: E4M3 bytes and E8M0 scales must be bit-identical.
+
+Shapes span several workgroup tiles (128 rows x 256 columns) and ragged tile
+tails; the special 256x512 tensor carries the degenerate blocks (all zero,
+amax exactly 2^3, ~1e-30, ~+-3e38); an exhaustive tensor drives every
+(bf16 element, scale byte) pair a block can produce through both directions.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_precision_bf16_amd as mx
+import oracle as O
+import workloads as W
+from gpu_util import assert_same, mx_outputs_equal, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_both(x, axis=3):
+    g = mx.mx_quantize(to_dev(x), axis=axis)
+    torch.cuda.synchronize()
+    return g, O.mx_quantize(x, axis=axis)
+
+
+def test_special_256x512_both_axes():
+    x = W.special_256x512()
+    g, o = run_both(x)
+    mx_outputs_equal(g, o, "special")
+    # the degenerate blocks are where they were put
+    assert np.all(o["s_row"][0:32, 0] == 0) and np.all(o["s_row"][32:64, 1] == 122)
+
+
+@pytest.mark.parametrize("axis", [1, 2, 3])
+@pytest.mark.parametrize("M,K", [(32, 32), (64, 96), (96, 288), (128, 256), (160, 800),
+                                 (288, 544), (416, 1056)])
+def test_random_shapes(M, K, axis):
+    x = W.loguniform_rows(M, K, seed=1000 + M + K)
+    g, o = run_both(x, axis)
+    mx_outputs_equal(g, o, f"{M}x{K} axis {axis}")
+    if axis == 1:
+        assert g["q_col"] is None
+
+
+def exhaustive_pairs_tensor(width=2048):
+    """Blocks of [setter, 31 elements]: for each scale byte b the setter is the
+    largest bf16 with exponent field b+8 (so the block's byte is exactly b) and
+    the elements run over every bf16 with exponent field <= b+8, both signs."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    fin = bits[(bits & 0x7F80) != 0x7F80]
+    ef = (fin >> 7) & 0xFF
+    blocks = []
+    for b in range(0, 247):
+        vals = fin[ef <= b + 8]
+        pad = (-len(vals)) % 31
+        vals = np.concatenate([vals, np.zeros(pad, np.uint16)]).reshape(-1, 31)
+        setter = np.full((vals.shape[0], 1), ((b + 8) << 7) | 0x7F, np.uint16)
+        blocks.append(np.concatenate([setter, vals], axis=1))
+    blk = np.concatenate(blocks)
+    per_row = width // 32
+    pad = (-blk.shape[0]) % per_row
+    blk = np.concatenate([blk, np.zeros((pad, 32), np.uint16)])
+    x = blk.reshape(-1, width)
+    rows = (-x.shape[0]) % 32
+    return np.concatenate([x, np.zeros((rows, width), np.uint16)])
+
+
+def test_exhaustive_element_scale_pairs_rowwise():
+    x = exhaustive_pairs_tensor()
+    g, o = run_both(x, axis=1)
+    mx_outputs_equal(g, o, "exhaustive rows")
+    assert set(np.unique(o["s_row"])) >= set(range(247))
+
+
+def test_exhaustive_element_scale_pairs_colwise():
+    x = np.ascontiguousarray(exhaustive_pairs_tensor().T)
+    g, o = run_both(x, axis=2)
+    mx_outputs_equal(g, o, "exhaustive cols")
+
+
+def test_nonfinite_blocks():
+    x = W.normal(64, 256, seed=5)
+    x[3, 40] = 0x7F80      # +Inf
+    x[40, 200] = 0xFFC1    # NaN
+    x[10, 7] = 0xFF80      # -Inf
+    g, o = run_both(x)
+    mx_outputs_equal(g, o, "nonfinite")
+    assert o["s_row"][3, 1] == 0xFF and o["s_col"][200, 1] == 0xFF
+
+
+def test_subnormal_and_zero_inputs():
+    rng = np.random.default_rng(6)
+    x = rng.integers(0, 0x80, (64, 512)).astype(np.uint16)          # bf16 subnormals
+    x |= (rng.random((64, 512)) < 0.5).astype(np.uint16) << 15
+    x[:32, :32] = 0
+    x[32:64, 32:64] = 0x8000                                          # -0
+    g, o = run_both(x)
+    mx_outputs_equal(g, o, "subnormal")
+
+
+def test_sign_and_scale_invariants_on_gpu():
+    x = W.normal(128, 512, seed=7, sigma=4.0)
+    a = mx.mx_quantize(to_dev(x))
+    n = mx.mx_quantize(to_dev(x ^ np.uint16(0x8000)))
+    torch.cuda.synchronize()
+    assert torch.equal(a["s_row"], n["s_row"]) and torch.equal(a["s_col"], n["s_col"])
+    assert torch.equal(a["q_row"] ^ 0x80, n["q_row"]) and torch.equal(a["q_col"] ^ 0x80, n["q_col"])
+
+
+def test_deterministic_and_guard_bands():
+    x = W.loguniform_rows(256, 768, seed=8)
+    M, K = x.shape
+    xd = to_dev(x)
+    guard = 4096
+    bufs = {}
+    outs = {}
+    for name, n in dict(q_row=M * K, s_row=M * K // 32, q_col=M * K, s_col=M * K // 32).items():
+        b = torch.full((n + 2 * guard,), 0x5A, dtype=torch.uint8, device="cuda")
+        bufs[name] = b
+        shape = {"q_row": (M, K), "s_row": (M, K // 32), "q_col": (K, M), "s_col": (K, M // 32)}[name]
+        outs[name] = b[guard:guard + n].view(shape)
+    r1 = mx.mx_quantize(xd, out=outs)
+    snap = {k: v.clone() for k, v in r1.items() if v is not None}
+    mx.mx_quantize(xd, out=outs)
+    torch.cuda.synchronize()
+    for k, v in snap.items():
+        assert torch.equal(v, outs[k]), k
+    for name, b in bufs.items():
+        assert torch.all(b[:guard] == 0x5A) and torch.all(b[-guard:] == 0x5A), name
+    o = O.mx_quantize(x)
+    mx_outputs_equal(outs, o, "guarded")
+
+
+def test_error_raises_through_binding():
+    xd = to_dev(np.zeros((48, 64), np.uint16))
+    with pytest.raises(mx.MxError) as e:
+        mx.mx_quantize(xd)
+    assert e.value.status == mx.MX_ERR_SHAPE

@@ -1,0 +1,77 @@
+"""GPU parity of NVFP4 quantize-transpose and the tensor absmax: packed E2M1
+bytes, E4M3 block scales and the fp32 global scale bit-exact against the
+oracle, on shapes with ragged tiles (M a multiple of 16 but not 32 included),
+the hand-worked blocks, and degenerate tensors (all zero, tiny magnitudes
+that drive block scales subnormal or to zero)."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_precision_bf16_amd as mx
+import oracle as O
+import workloads as W
+from gpu_util import assert_same, mx_outputs_equal, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_both(x, axis=3, tensor_amax=None):
+    xd = to_dev(x)
+    if tensor_amax is None:
+        amax = mx.mx_absmax_bf16(xd)
+    else:
+        amax = torch.tensor([tensor_amax], dtype=torch.float32, device="cuda")
+    g = mx.nvfp4_quantize_transpose(xd, amax, axis=axis)
+    torch.cuda.synchronize()
+    o = O.nvfp4_quantize_transpose(x, axis=axis, tensor_amax=tensor_amax)
+    assert g["sg"].item() == o["sg"]
+    return g, o
+
+
+@pytest.mark.parametrize("axis", [1, 2, 3])
+@pytest.mark.parametrize("M,K", [(16, 16), (48, 80), (128, 256), (144, 528), (400, 784)])
+def test_random_shapes(M, K, axis):
+    x = W.student_t_rows(M, K, seed=2000 + M + K)
+    g, o = run_both(x, axis)
+    mx_outputs_equal(g, o, f"nvfp4 {M}x{K} axis {axis}")
+
+
+def test_absmax_matches_oracle():
+    for shape, seed in (((64, 64), 1), ((1000, 24), 2), ((3, 5), 3), ((16384, 160), 4)):
+        x = W.student_t_rows(*shape, seed=seed)
+        a = mx.mx_absmax_bf16(to_dev(x))
+        torch.cuda.synchronize()
+        assert a.item() == O.absmax(x)
+
+
+def test_golden_blocks():
+    here = os.path.dirname(__file__)
+    x = np.zeros((16, 16), np.uint16)
+    for i, line in enumerate(l for l in open(os.path.join(here, "golden", "nvfp4_blocks.txt"))
+                             if l.strip() and not l.startswith("#")):
+        vals = [int(h, 16) for h in line.split("|")[1].split(",")]
+        x[i, :len(vals)] = vals
+    g, o = run_both(x, tensor_amax=2688.0)
+    mx_outputs_equal(g, o, "golden")
+
+
+@pytest.mark.parametrize("sigma", [0.0, 1e-20, 1e-36, 1e30])
+def test_degenerate_magnitudes(sigma):
+    x = W.normal(64, 96, seed=43, sigma=sigma if sigma else 1.0)
+    if sigma == 0.0:
+        x[:] = 0
+        x[5, 5] = 0x8000
+    g, o = run_both(x)
+    mx_outputs_equal(g, o, f"nvfp4 sigma {sigma}")
+
+
+def test_tiny_global_scale_overflowing_inverse():
+    """A tensor amax below 2^-120 makes S_g so small that some block
+    multipliers overflow to Inf (x*Inf saturates, 0*Inf encodes as +0)."""
+    x = W.normal(32, 64, seed=44, sigma=1e-37)
+    x[0, :16] = 0
+    x[1, 0] = 0x8000
+    g, o = run_both(x)
+    mx_outputs_equal(g, o, "tiny S_g")

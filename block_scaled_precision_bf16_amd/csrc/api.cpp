@@ -52,9 +52,25 @@ bool shape_ok(int64_t M, int64_t K, int64_t block)
 
 int tiles(int64_t n, int64_t t) { return (int)((n + t - 1) / t); }
 
+// Walks along M of the cast kernels for an M x K tensor.
+int walks_m(int64_t M, int64_t K)
+{
+    const int tm = tiles(M, mxk::kTileM), tk = tiles(K, mxk::kTileK);
+    const int g = mxk::pick_group(tm, tk);
+    return (tm + g - 1) / g;
+}
+
 size_t dbias_workspace(int64_t M, int64_t K)
 {
-    return (size_t)tiles(M, mxk::kTileM) * (size_t)K * sizeof(float);
+    return (size_t)walks_m(M, K) * (size_t)K * sizeof(float);
+}
+
+void set_walk(mxk::MxArgs &a)
+{
+    a.tiles_k = tiles(a.K, mxk::kTileK);
+    a.tiles_m = tiles(a.M, mxk::kTileM);
+    a.group = mxk::pick_group(a.tiles_m, a.tiles_k);
+    a.groups_m = (a.tiles_m + a.group - 1) / a.group;
 }
 
 mx_status from_hip(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
@@ -131,12 +147,11 @@ mx_status mx_quantize(const void *x, const void *grad, int64_t M, int64_t K, uns
     a.q_col = q_col;
     a.s_col = s_col;
     a.partials = want_dbias ? static_cast<float *>(workspace) : nullptr;
-    a.tiles_k = tiles(K, mxk::kTileK);
-    a.tiles_m = tiles(M, mxk::kTileM);
+    set_walk(a);
     mx_status st = from_hip(mxk::launch_mx_cast(pre, axis_mask, want_dbias, a, stream));
     if (st != MX_OK || !want_dbias)
         return st;
-    return from_hip(mxk::launch_dbias_reduce(a.partials, a.tiles_m, K, dbias, stream));
+    return from_hip(mxk::launch_dbias_reduce(a.partials, a.groups_m, K, dbias, stream));
 }
 
 mx_status mx_quantize_gated(const void *x, int64_t M, int64_t N, unsigned axis_mask, int act,
@@ -172,8 +187,7 @@ mx_status mx_quantize_gated(const void *x, int64_t M, int64_t N, unsigned axis_m
     a.q_col = q_col;
     a.s_col = s_col;
     a.partials = nullptr;
-    a.tiles_k = tiles(N, mxk::kTileK);
-    a.tiles_m = tiles(M, mxk::kTileM);
+    set_walk(a);
     const int op = act == MX_GATED_SWIGLU ? mxk::OP_SWIGLU : mxk::OP_GEGLU;
     return from_hip(mxk::launch_mx_cast(op, axis_mask, false, a, stream));
 }

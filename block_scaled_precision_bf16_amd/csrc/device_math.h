@@ -21,12 +21,16 @@ __device__ __forceinline__ uint32_t bits_f32(float f) { return __float_as_uint(f
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return f32_bits(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return f32_bits(w & 0xFFFF0000u); }
 
-// fp32 -> bf16 bits, round to nearest even; NaN -> canonical quiet NaN.
-__device__ __forceinline__ uint32_t bf16_rne(float f)
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> a packed pair of bf16 bits (lo in bits 0-15), round to nearest
+// even, by gfx950's v_cvt_pk_bf16_f32 (qualified bit-identical to integer RNE
+// rounding over all 2^32 fp32 inputs; Inf stays Inf).
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi)
 {
-    uint32_t u = bits_f32(f);
-    uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-    return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? 0x7FC0u : r;
+    const bf16x2 r = __builtin_convertvector((f32x2){lo, hi}, bf16x2);
+    return __builtin_bit_cast(uint32_t, r);
 }
 
 // Lane-wise max of the two 15-bit magnitudes packed in a word of bf16 pairs.
@@ -77,6 +81,77 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float v)
     return sign | code;
 }
 
+// Two fp32 -> two E4M3 bytes (round to nearest even, saturating), written into
+// the low (HI = false) or high (HI = true) 16 bits of `old`, first value in the
+// lower byte.  v_cvt_pk_fp8_f32 rounds to nearest even but turns values beyond
+// the format into NaN, so both inputs are first clamped to +-448, which leaves
+// every in-range value (and -0) unchanged.  The pair is bit-identical to
+// e4m3_rne_sat on every finite input a block can produce.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2(float a, float b, uint32_t old)
+{
+    a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+    b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
+}
+
+// Lane-wise min of two packed 16-bit magnitudes.
+__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b)
+{
+    u16x2 va = __builtin_bit_cast(u16x2, a), vb = __builtin_bit_cast(u16x2, b);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(va, vb));
+}
+
+// bf16 pattern of the largest magnitude a block with scale byte b may keep
+// before saturating: 448 * 2^(b - 127) = 1.75 * 2^(b + 8 - 127), i.e. exponent
+// field b + 8 and mantissa 0x60, duplicated into both halves.  Valid for
+// b <= 246, the largest byte a finite bf16 amax produces.
+__device__ __forceinline__ uint32_t sat_limit2(uint32_t b)
+{
+    const uint32_t l = ((b + 8u) << 7) | 0x60u;
+    return l | (l << 16);
+}
+
+// A packed pair of bf16 with each magnitude clamped to the limit (signs kept).
+__device__ __forceinline__ uint32_t clamp_pair(uint32_t w, uint32_t mag, uint32_t lim2)
+{
+    return (pk_min_u16(mag, lim2) & 0x7FFF7FFFu) | (w & 0x80008000u);
+}
+
+// A packed pair of bf16 -> two E4M3 bytes in the low (HI = false) or high
+// 16 bits of `old`, first element in the lower byte.  The pair must already be
+// clamped with sat_limit2(b); v_cvt_scalef32_pk_fp8_bf16 then divides each
+// element by 2^(b - 127) -- the scale operand carries the E8M0 byte in its
+// exponent field -- and rounds to nearest even, which is exactly the block
+// rule (the division by a power of two is exact, so it equals multiplying by
+// the inverse).  The clamp is what makes it saturate: on its own the
+// instruction turns values beyond 448 into NaN.  Qualified bit-identical to
+// e4m3_rne_sat(x * 2^(127 - b)) over every reachable (element, byte) pair, in
+// both halves of the pair.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_scaled(uint32_t pair, float scale, uint32_t old)
+{
+    typedef short s16x2 __attribute__((ext_vector_type(2)));
+    const s16x2 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(__builtin_bit_cast(s16x2, old),
+                                                              __builtin_bit_cast(bf16x2, pair),
+                                                              scale, HI);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// The scale operand of the scaled converts: the E8M0 byte in the exponent field.
+__device__ __forceinline__ float e8m0_operand(uint32_t b) { return f32_bits(b << 23); }
+
+// Two fp32 -> two E2M1 nibbles in byte SEL of `old` (first value in the low
+// nibble), by v_cvt_scalef32_pk_fp4_f32 with scale 1: round to nearest even,
+// saturating at 6, Inf -> 6; bit-identical to e2m1_rne_sat on every non-NaN
+// input.  (A NaN input -- only 0 * Inf -- gives 6 here, so callers route blocks
+// whose multiplier is Inf through e2m1_rne_sat.)
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1x2(float a, float b, uint32_t old)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+}
+
 // E4M3 code (no NaN) -> its exact fp32 value.
 __device__ __forceinline__ float e4m3_value(uint32_t c)
 {
@@ -114,14 +189,13 @@ __device__ __forceinline__ float exp32(float a)
     const float LOG2E = 1.44269504088896340736f;
     const float LN2_A = 0.693359375f;                 // 355/512
     const float LN2_B = -2.12194440054690583e-4f;     // ln2 - 355/512
-    if (a != a)
-        return a;
-    if (a > 88.72283172607421875f)
-        return __builtin_inff();
-    if (a < -104.0f)
-        return 0.0f;
-    float n = __builtin_rintf(a * LOG2E);
-    float r = __builtin_fmaf(n, -LN2_A, a);
+    const float HI = 88.72283172607421875f;           // above: e^a rounds to +Inf
+    const float LO = -104.0f;                         // below: e^a rounds to 0
+    // straight-line: evaluate at the clamped argument, then select the
+    // out-of-range results (identical to returning early for them)
+    const float c = __builtin_amdgcn_fmed3f(a, LO, HI);
+    const float n = __builtin_rintf(c * LOG2E);
+    float r = __builtin_fmaf(n, -LN2_A, c);
     r = __builtin_fmaf(n, -LN2_B, r);
     float p = (float)(1.0 / 5040.0);
     p = __builtin_fmaf(p, r, (float)(1.0 / 720.0));
@@ -131,9 +205,12 @@ __device__ __forceinline__ float exp32(float a)
     p = __builtin_fmaf(p, r, 0.5f);
     p = __builtin_fmaf(p, r, 1.0f);
     p = __builtin_fmaf(p, r, 1.0f);
-    int ni = (int)n;
-    int n1 = ni / 2, n2 = ni - n1;
-    return (p * f32_bits((uint32_t)(n1 + 127) << 23)) * f32_bits((uint32_t)(n2 + 127) << 23);
+    const int ni = (int)n;                            // in [-150, 128]
+    const int n1 = ni / 2, n2 = ni - n1;              // each in [-75, 64]
+    float e = (p * f32_bits((uint32_t)(n1 + 127) << 23)) * f32_bits((uint32_t)(n2 + 127) << 23);
+    e = a > HI ? __builtin_inff() : e;
+    e = a < LO ? 0.0f : e;
+    return a != a ? a : e;
 }
 
 // sigma(z) = 1/(1+e^-z) and 1 - sigma(z) from e = e^-|z| (no overflow, no
@@ -190,27 +267,28 @@ __device__ __forceinline__ float silu32(float g)
     return g * s;
 }
 
-// y (bf16 bits) for one element.  a = x (or gate), b = grad (or linear).
+// y (fp32, before the bf16 rounding) for one element.  a = x (or gate),
+// b = grad (or linear).
 template <int OP>
-__device__ __forceinline__ uint32_t fused_value(float a, float b)
+__device__ __forceinline__ float fused_value(float a, float b)
 {
     if constexpr (OP == OP_GELU)
-        return bf16_rne(gelu32(a));
+        return gelu32(a);
     else if constexpr (OP == OP_DGELU)
-        return bf16_rne(dgelu32(a) * b);
+        return dgelu32(a) * b;
     else if constexpr (OP == OP_SWIGLU)
-        return bf16_rne(silu32(a) * b);
+        return silu32(a) * b;
     else
-        return bf16_rne(gelu32(a) * b);
+        return gelu32(a) * b;
 }
 
-// Apply the pre-op to a packed pair of bf16 (and its partner pair).
+// Apply the pre-op to a packed pair of bf16 (with its partner pair) and round
+// the two results to bf16.
 template <int OP>
 __device__ __forceinline__ uint32_t fused_pair(uint32_t a, uint32_t b)
 {
-    uint32_t lo = fused_value<OP>(bf16_lo(a), bf16_lo(b));
-    uint32_t hi = fused_value<OP>(bf16_hi(a), bf16_hi(b));
-    return lo | (hi << 16);
+    return bf16x2_rne(fused_value<OP>(bf16_lo(a), bf16_lo(b)),
+                      fused_value<OP>(bf16_hi(a), bf16_hi(b)));
 }
 
 // ---------------------------------------------------------------------------

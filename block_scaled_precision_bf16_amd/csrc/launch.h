@@ -20,6 +20,20 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTileM = 2 * kRowsPerLane * kWaves;  // 128
 constexpr int kTileK = kColsPerLane * 32;          // 256
+// A cast workgroup walks down up to kMaxGroup sub-tiles of a 256-column strip.
+constexpr int kMaxGroup = 16;
+// Workgroups the host aims to launch at least (two per MI355X compute unit).
+constexpr int kTargetWorkgroups = 512;
+
+// Sub-tiles per workgroup for a tiles_m x tiles_k grid of sub-tiles: the
+// deepest power of two <= kMaxGroup that still yields kTargetWorkgroups.
+inline int pick_group(int tiles_m, int tiles_k)
+{
+    int g = kMaxGroup;
+    while (g > 1 && (int64_t)((tiles_m + g - 1) / g) * tiles_k < kTargetWorkgroups)
+        g >>= 1;
+    return g;
+}
 
 struct MxArgs {
     const uint16_t *x;     // input (gated: [M][2N] with the linear half at lin_off)
@@ -28,8 +42,9 @@ struct MxArgs {
     int64_t ldx;           // row stride of x in elements
     int64_t lin_off;       // gated: column offset of the linear half
     uint8_t *q_row, *s_row, *q_col, *s_col;
-    float *partials;       // dbias: [tiles_m][K] fp32 column partial sums
-    int tiles_k, tiles_m;
+    float *partials;       // dbias: [groups_m][K] fp32 column partial sums
+    int tiles_k, tiles_m;  // 128 x 256 sub-tiles along K and M
+    int group, groups_m;   // sub-tiles per workgroup walk, walks along M
 };
 
 struct Nv4Args {
@@ -43,7 +58,7 @@ struct Nv4Args {
 
 // op: 0 plain, 1 GELU, 2 dGELU, 3 SwiGLU, 4 GeGLU.
 hipError_t launch_mx_cast(int op, unsigned axis, bool dbias, const MxArgs &a, hipStream_t s);
-hipError_t launch_dbias_reduce(const float *partials, int tiles_m, int64_t K, float *dbias,
+hipError_t launch_dbias_reduce(const float *partials, int segments, int64_t K, float *dbias,
                                hipStream_t s);
 // op as above (1..4); gated ops read x[M][2K].
 hipError_t launch_fused_values(int op, const uint16_t *x, const uint16_t *aux, int64_t M,

@@ -11,7 +11,8 @@
 // block of 16 spans two lanes, combined with one DPP permute.
 //
 // Per block the scale chain costs three IEEE fp32 divisions (b/6, /S_g and
-// the reciprocal); each element then costs one multiply and an E2M1 encode.
+// the reciprocal); each element then costs one multiply and half of a packed
+// hardware E2M1 convert.
 
 #include "device_math.h"
 #include "launch.h"
@@ -31,16 +32,44 @@ __device__ __forceinline__ void nv_block(uint32_t mag, float sg, uint32_t &sbyte
 }
 
 // Eight bf16 (four words) times inv -> eight E2M1 nibbles, element i in bits
-// 4i..4i+3 (so element 2j is the low nibble of byte j).
+// 4i..4i+3 (so element 2j is the low nibble of byte j).  A block whose
+// multiplier overflowed to Inf (tensor scale below ~2^-120) takes the software
+// encoder, which maps 0 * Inf to +0.
 __device__ __forceinline__ uint32_t encode8_fp4(const uint32_t (&w)[4], float inv)
 {
-    uint32_t o = 0;
+    if (__builtin_isinf(inv)) {
+        uint32_t o = 0;
 #pragma unroll
-    for (int d = 0; d < 4; d++) {
-        o |= e2m1_rne_sat(bf16_lo(w[d]) * inv) << (8 * d);
-        o |= e2m1_rne_sat(bf16_hi(w[d]) * inv) << (8 * d + 4);
+        for (int d = 0; d < 4; d++) {
+            o |= e2m1_rne_sat(bf16_lo(w[d]) * inv) << (8 * d);
+            o |= e2m1_rne_sat(bf16_hi(w[d]) * inv) << (8 * d + 4);
+        }
+        return o;
     }
-    return o;
+    uint32_t o = e2m1x2<0>(bf16_lo(w[0]) * inv, bf16_hi(w[0]) * inv, 0u);
+    o = e2m1x2<1>(bf16_lo(w[1]) * inv, bf16_hi(w[1]) * inv, o);
+    o = e2m1x2<2>(bf16_lo(w[2]) * inv, bf16_hi(w[2]) * inv, o);
+    return e2m1x2<3>(bf16_lo(w[3]) * inv, bf16_hi(w[3]) * inv, o);
+}
+
+// Rows 8q..8q+7 of one column (half HI of word d) times inv -> eight nibbles,
+// row 8q+i in bits 4i..4i+3.
+template <int HI>
+__device__ __forceinline__ uint32_t encode8_fp4_col(const uint32_t (&w)[kRowsPerLane][4], int q,
+                                                    int d, float inv)
+{
+    auto v = [&](int i) { return (HI ? bf16_hi(w[8 * q + i][d]) : bf16_lo(w[8 * q + i][d])) * inv; };
+    if (__builtin_isinf(inv)) {
+        uint32_t o = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            o |= e2m1_rne_sat(v(i)) << (4 * i);
+        return o;
+    }
+    uint32_t o = e2m1x2<0>(v(0), v(1), 0u);
+    o = e2m1x2<1>(v(2), v(3), o);
+    o = e2m1x2<2>(v(4), v(5), o);
+    return e2m1x2<3>(v(6), v(7), o);
 }
 
 template <bool ROW, bool COL>
@@ -106,15 +135,8 @@ __global__ __launch_bounds__(kThreads) void nvfp4_kernel(Nv4Args a)
             nv_block(mag, sg, sb, inv);
             uint32_t o[2];
 #pragma unroll
-            for (int q = 0; q < 2; q++) {
-                uint32_t v = 0;
-#pragma unroll
-                for (int i = 0; i < 8; i++) {
-                    const uint32_t wd = w[8 * q + i][d];
-                    v |= e2m1_rne_sat((hi ? bf16_hi(wd) : bf16_lo(wd)) * inv) << (4 * i);
-                }
-                o[q] = v;
-            }
+            for (int q = 0; q < 2; q++)
+                o[q] = hi ? encode8_fp4_col<1>(w, q, d, inv) : encode8_fp4_col<0>(w, q, d, inv);
             *reinterpret_cast<uint2 *>(a.q_col + (k + c) * (a.M >> 1) + (m0 >> 1)) =
                 make_uint2(o[0], o[1]);
             a.s_col[(k + c) * (a.M >> 4) + (m0 >> 4)] = (uint8_t)sb;

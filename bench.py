@@ -29,7 +29,8 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
 KERNEL_SOURCES = ["block_scaled_precision_bf16_amd/csrc/mx_cast.hip",
                   "block_scaled_precision_bf16_amd/csrc/nvfp4.hip",
                   "block_scaled_precision_bf16_amd/csrc/device_math.h",
-                  "block_scaled_precision_bf16_amd/csrc/launch.h"]
+                  "block_scaled_precision_bf16_amd/csrc/launch.h",
+                  "block_scaled_precision_bf16_amd/csrc/bufio.h"]
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic_mx_cast_dim0_dim1_16384.md")
 
 

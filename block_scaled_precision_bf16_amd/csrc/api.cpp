@@ -12,7 +12,10 @@
 
 namespace {
 
-constexpr int64_t kMaxDim = int64_t(1) << 30;
+// Largest row count and row length (in elements, for a gated input the full
+// [gate | linear] row): the kernels address a 128-row sub-tile, and a strip
+// of 256 transposed rows, with 32-bit byte offsets from its first element.
+constexpr int64_t kMaxDim = int64_t(1) << 23;
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }

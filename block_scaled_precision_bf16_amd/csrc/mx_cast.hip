@@ -6,27 +6,31 @@
 // (bidimensional)", "MXFP8 gated (swiglu / geglu) kernel") and the torchao
 // dim1 cast of PR 12, designed here for CDNA4.
 //
-// Layout of the work: a workgroup (4 waves) owns a 128-row x 256-column
-// tile.  A lane owns 16 consecutive rows x 8 consecutive columns, loaded as
-// 16 128-bit loads; lanes 0-31 of a wave hold rows 0-15 and lanes 32-63 rows
-// 16-31 of the same 256 columns, so each wave load instruction reads two
-// 512-byte row segments (fully coalesced) and a wave covers exactly one
-// 32-row column block.  The column-wise (dim1) amax of a column is the max of
-// two lanes' in-register maxima (one exchange between lane l and l^32), and
-// each lane then converts and stores its own 16 bytes of the transposed row,
-// so the dim1 path needs no transpose through LDS.  The row-wise amax spans 4
-// lanes (4 x 8 = 32 columns), reduced with two DPP quad permutes.  Row
-// outputs leave as 8-byte stores (256 contiguous bytes per half-wave);
-// column outputs as 16-byte stores, the 8 lane-halves of a workgroup
-// completing each 128-byte line of the transposed tensor.  LDS is used only
-// for the dbias cross-wave sum, as a statically declared array (its address
-// never passes through an integer: the fix the PR 3291 page is about).
+// Layout of the work: a workgroup (4 waves) converts a 128-row x 256-column
+// sub-tile at a time and walks down a 256-column strip.  A lane owns 16
+// consecutive rows x 8 consecutive columns, loaded as 16 128-bit loads;
+// lanes 0-31 of a wave hold rows 0-15 and lanes 32-63 rows 16-31 of the same
+// 256 columns, so each wave load instruction reads two 512-byte row segments
+// and a wave covers exactly one 32-row column block.  The row-wise amax spans
+// 4 lanes (4 x 8 = 32 columns), reduced with two DPP quad permutes; row
+// outputs leave as 8-byte stores (256 contiguous bytes per half-wave).  The
+// column-wise amax of a column is the max of two lanes' in-register maxima
+// (one exchange between lane l and l^32); each lane converts its own 16
+// bytes of each transposed row into an LDS staging tile, from which the
+// workgroup writes whole 128-byte lines of the transposed tensor.  Row and
+// column scales are staged in LDS as well and leave as 8-byte and 16-byte
+// pieces.  The LDS arrays are statically declared, so their addresses never
+// pass through an integer (the fix the PR 3291 page is about).
 //
 // Every element costs a packed integer clamp and half of a packed scaled
 // convert that applies the block's power-of-two scale exactly (the torchao
 // PR 12 page: divisions per element made the dim1 cast compute bound; here
-// there is not even a multiply per element).
+// there is not even a multiply per element).  All global memory access goes
+// through buffer resources with out-of-range offsets for masked lanes (see
+// bufio.h), so the load of the next sub-tile stays in flight while the
+// current one is converted.
 
+#include "bufio.h"
 #include "device_math.h"
 #include "launch.h"
 
@@ -36,6 +40,22 @@ __device__ __forceinline__ float half_value(uint32_t w, int hi)
 {
     return hi ? bf16_hi(w) : bf16_lo(w);
 }
+
+// Cache policy of each stream, chosen by measurement on the 16384 x 16384
+// cast: the input is read once, so its loads are non-temporal.  With both
+// outputs the transposed tile (lines and scales) is written non-temporal as
+// well and the row-wise elements with the SC1 bit; the row scales keep the
+// default policy (non-temporal row scales, 8-byte pieces of lines that other
+// workgroups complete, cost ~15%).  With one output only the loads are
+// non-temporal.  The policies change timing only, never results.
+template <bool ROW, bool COL>
+struct Policy {
+    static constexpr int x = kNT;                        // input loads
+    static constexpr int q_row = ROW && COL ? kSC1 : 0;  // row-wise stores
+    static constexpr int s_row = 0;
+    static constexpr int q_col = ROW && COL ? kNT : 0;   // transposed stores
+    static constexpr int s_col = ROW && COL ? kNT : 0;
+};
 
 // Row r's 8 elements (4 words w, magnitudes mag) with scale byte b -> 8 E4M3
 // bytes.
@@ -77,21 +97,59 @@ __device__ __forceinline__ uint4 encode16_col(const uint32_t (&w)[kRowsPerLane][
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-template <int OP>
-__device__ __forceinline__ void load_rows(const MxArgs &a, const uint16_t *px,
-                                          const uint16_t *pg, uint32_t (&w)[kRowsPerLane][4])
+// Per-lane coordinates inside a sub-tile.
+struct LaneAt {
+    int wave, half, cl;
+    int row;        // first of the lane's 16 rows inside the sub-tile
+};
+
+__device__ __forceinline__ LaneAt lane_at()
 {
+    LaneAt l;
+    l.wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int lane = (int)threadIdx.x & 63;
+    l.half = lane >> 5;
+    l.cl = lane & 31;
+    l.row = l.wave * (2 * kRowsPerLane) + l.half * kRowsPerLane;
+    return l;
+}
+
+// The lane's rows exist (M is a multiple of 32, so a wave is wholly inside or
+// outside) and its 8 columns exist (K is a multiple of 32, so a column group
+// of 8, a 4-lane row block and an l / l^32 pair are wholly inside or outside).
+__device__ __forceinline__ bool lane_live(const MxArgs &a, const LaneAt &l, int tm, int tk)
+{
+    return (int64_t)tm * kTileM + l.wave * 32 < a.M && (int64_t)tk * kTileK + l.cl * kColsPerLane < a.K;
+}
+
+// This lane's 16 rows x 8 columns of sub-tile (tm, tk), after the pre-op.  A
+// sub-tile outside the tensor (tm >= tiles_m) reads as zeros without memory
+// traffic, which the plain cast uses for the prefetch past a walk's end.
+template <int OP, int XA>
+__device__ __forceinline__ void load_tile(const MxArgs &a, const LaneAt &l, int tm, int tk,
+                                          uint32_t (&w)[kRowsPerLane][4])
+{
+    const int64_t tile = (int64_t)tm * kTileM * a.ldx + (int64_t)tk * kTileK;   // elements
+    const int64_t total = a.M * a.ldx;
+    const rsrc_t rx = make_rsrc(a.x, 2 * tile, 2 * total);
+    const uint32_t rs = (uint32_t)(2 * a.ldx);
+    const uint32_t off = lane_live(a, l, tm, tk)
+                             ? (uint32_t)l.row * rs + (uint32_t)(2 * kColsPerLane * l.cl)
+                             : kDead;
+    rsrc_t rb = rx;
+    if constexpr (OP == OP_DGELU)
+        rb = make_rsrc(a.aux, 2 * tile, 2 * total);
+    else if constexpr (OP == OP_SWIGLU || OP == OP_GEGLU)
+        rb = make_rsrc(a.x, 2 * (tile + a.lin_off), 2 * total);
 #pragma unroll
     for (int r = 0; r < kRowsPerLane; r++) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(px);
+        const uint4 v = buf_load16<XA>(rx, off + r * rs);
         if constexpr (OP == OP_PLAIN) {
             w[r][0] = v.x; w[r][1] = v.y; w[r][2] = v.z; w[r][3] = v.w;
         } else {
             uint4 b = v;   // GELU has no second operand
-            if constexpr (OP == OP_DGELU)
-                b = *reinterpret_cast<const uint4 *>(pg);
-            else if constexpr (OP == OP_SWIGLU || OP == OP_GEGLU)
-                b = *reinterpret_cast<const uint4 *>(px + a.lin_off);
+            if constexpr (OP != OP_GELU)
+                b = buf_load16<XA>(rb, off + r * rs);
             w[r][0] = fused_pair<OP>(v.x, b.x);
             w[r][1] = fused_pair<OP>(v.y, b.y);
             w[r][2] = fused_pair<OP>(v.z, b.z);
@@ -100,8 +158,6 @@ __device__ __forceinline__ void load_rows(const MxArgs &a, const uint16_t *px,
             // multiplies the live temporaries
             __builtin_amdgcn_sched_barrier(0);
         }
-        px += a.ldx;
-        pg += a.ldx;
     }
 }
 
@@ -109,10 +165,16 @@ __device__ __forceinline__ void load_rows(const MxArgs &a, const uint16_t *px,
 // scale, convert, store.  Column maxima are accumulated on the way.
 template <bool ROW, bool COL>
 __device__ __forceinline__ void row_pass(const MxArgs &a, const uint32_t (&w)[kRowsPerLane][4],
-                                         int64_t m0, int64_t k, int lane, uint8_t *srow,
+                                         const LaneAt &l, int tm, int tk, bool live, uint8_t *srow,
                                          uint32_t (&cmax)[4])
 {
-    uint8_t *qr = a.q_row + m0 * a.K + k;
+    rsrc_t rq;
+    uint32_t off = kDead;
+    if constexpr (ROW) {
+        rq = make_rsrc(a.q_row, (int64_t)tm * kTileM * a.K + (int64_t)tk * kTileK, a.M * a.K);
+        if (live)
+            off = (uint32_t)(l.row * a.K) + (uint32_t)(kColsPerLane * l.cl);
+    }
 #pragma unroll
     for (int r = 0; r < kRowsPerLane; r++) {
         uint32_t m[4];
@@ -132,10 +194,9 @@ __device__ __forceinline__ void row_pass(const MxArgs &a, const uint32_t (&w)[kR
             uint2 o = encode8_row(w[r], m, sb);
             if (sb == 0xFFu)
                 o.x = o.y = 0x7F7F7F7Fu;
-            *reinterpret_cast<uint2 *>(qr) = o;
-            if ((lane & 3) == 0)
+            buf_store8<Policy<ROW, COL>::q_row>(rq, off + (uint32_t)(r * a.K), o);
+            if ((l.cl & 3) == 0)
                 srow[r * (kTileK / 32)] = (uint8_t)sb;
-            qr += a.K;
         }
     }
 }
@@ -181,120 +242,100 @@ __device__ __forceinline__ void col_pass(ColStage &st, const uint32_t (&w)[kRows
 // Write the staged transposed tile of sub-tile tm: thread t writes 16-byte
 // chunk t % 8 of q_col rows t / 8 + 32 i (i = 0..7), so each wave store
 // instruction covers 8 whole 128-byte lines.
+template <int AUX>
 __device__ __forceinline__ void col_flush_q(const MxArgs &a, const ColStage &st, int tm, int tk)
 {
     const int t = (int)threadIdx.x;
     const int jr = t & 7;
     const int64_t mt = (int64_t)tm * kTileM;
     const int64_t k0 = (int64_t)tk * kTileK;
+    const rsrc_t rc = make_rsrc(a.q_col, k0 * a.M + mt, a.K * a.M);
     const bool chunk_live = mt + 16 * jr < a.M;   // M is a multiple of 32
 #pragma unroll
     for (int i = 0; i < kTileK / 32; i++) {
         const int kr = (t >> 3) + 32 * i;
-        if (chunk_live && k0 + kr < a.K)
-            *reinterpret_cast<uint4 *>(a.q_col + (k0 + kr) * a.M + mt + 16 * jr) =
-                st.q[kr][stage_chunk(kr, jr)];
+        const uint32_t off = chunk_live && k0 + kr < a.K ? (uint32_t)(kr * a.M) + 16 * jr : kDead;
+        buf_store16<AUX>(rc, off, st.q[kr][stage_chunk(kr, jr)]);
     }
 }
 
 // Write the strip segment's column scales: thread t owns column k0 + t and
 // writes its 4 n scale bytes (n sub-tiles) as 16-byte stores when the row of
 // s_col allows it (a whole 64-byte chunk for a 16-deep walk), else bytewise.
+template <int AUX>
 __device__ __forceinline__ void col_flush_s(const MxArgs &a, const ColStage &st, int rg, int tk,
                                             int n)
 {
     const int t = (int)threadIdx.x;
     const int64_t k0 = (int64_t)tk * kTileK;
-    if (k0 + t >= a.K)
-        return;
     const int64_t nblk = a.M >> 5;                        // scales per column
     const int64_t first = (int64_t)rg * a.group * 4;      // this segment's first block
     const int64_t left = nblk - first;
     const int count = (int)(left < 4 * n ? left : 4 * n);
-    uint8_t *dst = a.s_col + (k0 + t) * nblk + first;
+    const rsrc_t rs = make_rsrc(a.s_col, k0 * nblk + first, a.K * nblk);
+    const uint32_t off = k0 + t < a.K ? (uint32_t)(t * nblk) : kDead;
     if (((nblk | first) & 15) == 0 && (count & 15) == 0) {
         for (int i = 0; i < count; i += 16)
-            *reinterpret_cast<uint4 *>(dst + i) = *reinterpret_cast<const uint4 *>(&st.s[t][i]);
+            buf_store16<AUX>(rs, off + i, *reinterpret_cast<const uint4 *>(&st.s[t][i]));
     } else {
         for (int i = 0; i < count; i++)
-            dst[i] = st.s[t][i];
+            buf_store1<AUX>(rs, off + i, st.s[t][i]);
     }
 }
 
 // Row scales of a sub-tile, staged as [128 rows][8 blocks] bytes: thread
 // t < 128 writes row t's 8 scale bytes with one 8-byte store (instead of 8
 // one-byte stores from 8 lanes).
+template <int AUX>
 __device__ __forceinline__ void srow_flush(const MxArgs &a, const uint8_t (&srow)[kTileM][kTileK / 32],
                                            int tm, int tk)
 {
     const int t = (int)threadIdx.x;
     const int64_t row = (int64_t)tm * kTileM + t;
-    if (t >= kTileM || row >= a.M)
-        return;
     const int64_t k0 = (int64_t)tk * kTileK;
-    uint8_t *dst = a.s_row + row * (a.K >> 5) + (k0 >> 5);
-    const int64_t blocks = (a.K - k0) >> 5;   // scale bytes of this tile inside K
+    const int64_t nb = a.K >> 5;                          // scale bytes per row
+    const rsrc_t rs = make_rsrc(a.s_row, (int64_t)tm * kTileM * nb + (k0 >> 5), a.M * nb);
+    const uint32_t off = t < kTileM && row < a.M ? (uint32_t)(t * nb) : kDead;
+    const uint8_t *src = srow[t & (kTileM - 1)];
     if ((a.K & 255) == 0) {
-        *reinterpret_cast<uint2 *>(dst) = *reinterpret_cast<const uint2 *>(srow[t]);
+        buf_store8<AUX>(rs, off, *reinterpret_cast<const uint2 *>(src));
     } else {
+        const int64_t blocks = nb - (k0 >> 5);            // scale bytes of this tile inside K
 #pragma unroll
         for (int b = 0; b < kTileK / 32; b++)
-            if (b < blocks)
-                dst[b] = srow[t][b];
-    }
-}
-
-// Raw bf16 words of this lane's 16 rows of sub-tile tm (no pre-op).
-__device__ __forceinline__ void load_plain(const MxArgs &a, int64_t m0, int64_t k,
-                                           uint32_t (&w)[kRowsPerLane][4])
-{
-    const uint16_t *px = a.x + m0 * a.ldx + k;
-#pragma unroll
-    for (int r = 0; r < kRowsPerLane; r++) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(px);
-        w[r][0] = v.x; w[r][1] = v.y; w[r][2] = v.z; w[r][3] = v.w;
-        px += a.ldx;
+            buf_store1<AUX>(rs, b < blocks ? off + b : kDead, src[b]);
     }
 }
 
 // One sub-tile of the walk: row pass (direct row stores, row scales to LDS),
-// column pass into LDS, then the staged output leaves as whole lines.
+// column pass into LDS, then the staged output leaves as whole lines.  Lanes
+// outside the tensor hold zeros and their stores are out of range.
 template <bool ROW, bool COL, bool DBIAS>
-__device__ __forceinline__ void tile_step(const MxArgs &a, const uint32_t (&w)[kRowsPerLane][4],
+__device__ __forceinline__ void tile_step(const MxArgs &a, const LaneAt &l,
+                                          const uint32_t (&w)[kRowsPerLane][4],
                                           uint8_t (&srow)[kTileM][kTileK / 32], ColStage *st,
                                           int tm, int tk, int g, float (&dsum)[kColsPerLane])
 {
-    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    const int lane = (int)threadIdx.x & 63;
-    const int half = lane >> 5, cl = lane & 31;
-    const int64_t mb = (int64_t)tm * kTileM + wave * (2 * kRowsPerLane);
-    const int64_t m0 = mb + half * kRowsPerLane;
-    const int64_t k = (int64_t)tk * kTileK + cl * kColsPerLane;
-    // M is a multiple of 32, so a wave is wholly inside or outside; a column
-    // group of 8 is wholly inside or outside K, and so are the 4-lane row
-    // blocks and the l / l^32 pairs that exchange data.
-    const bool live = mb < a.M && k < a.K;
-    if (live) {
-        uint32_t cmax[4] = {0u, 0u, 0u, 0u};
-        row_pass<ROW, COL>(a, w, m0, k, lane, &srow[wave * 32 + half * 16][cl >> 2], cmax);
-        if constexpr (COL)
-            col_pass(*st, w, wave, half, cl, g, cmax);
-        if constexpr (DBIAS) {
+    const bool live = lane_live(a, l, tm, tk);
+    uint32_t cmax[4] = {0u, 0u, 0u, 0u};
+    row_pass<ROW, COL>(a, w, l, tm, tk, live, &srow[l.row][l.cl >> 2], cmax);
+    if constexpr (COL)
+        col_pass(*st, w, l.wave, l.half, l.cl, g, cmax);
+    if constexpr (DBIAS) {
 #pragma unroll
-            for (int c = 0; c < kColsPerLane; c++) {
-                float acc = dsum[c];
+        for (int c = 0; c < kColsPerLane; c++) {
+            float acc = dsum[c];
 #pragma unroll
-                for (int r = 0; r < kRowsPerLane; r++)
-                    acc += half_value(w[r][c >> 1], c & 1);
-                dsum[c] = acc;
-            }
+            for (int r = 0; r < kRowsPerLane; r++)
+                acc += half_value(w[r][c >> 1], c & 1);
+            dsum[c] = acc;
         }
     }
     __syncthreads();
     if constexpr (COL)
-        col_flush_q(a, *st, tm, tk);
+        col_flush_q<Policy<ROW, COL>::q_col>(a, *st, tm, tk);
     if constexpr (ROW)
-        srow_flush(a, srow, tm, tk);
+        srow_flush<Policy<ROW, COL>::s_row>(a, srow, tm, tk);
     __syncthreads();   // the staging buffers are reused by the next sub-tile
 }
 
@@ -310,11 +351,7 @@ __global__ __launch_bounds__(kThreads) void mx_cast_kernel(MxArgs a)
     const int tk = job - rg * a.tiles_k;
     const int tm0 = rg * a.group;
     const int n = (a.tiles_m - tm0) < a.group ? (a.tiles_m - tm0) : a.group;
-    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    const int lane = (int)threadIdx.x & 63;
-    const int half = lane >> 5, cl = lane & 31;
-    const int64_t k = (int64_t)tk * kTileK + cl * kColsPerLane;
-    const int64_t row_off = wave * (2 * kRowsPerLane) + half * kRowsPerLane;
+    const LaneAt l = lane_at();
 
     __shared__ __align__(16) uint8_t srow[kTileM][kTileK / 32];
     ColStage *st = nullptr;
@@ -323,45 +360,46 @@ __global__ __launch_bounds__(kThreads) void mx_cast_kernel(MxArgs a)
         st = &stage;
     }
     float dsum[kColsPerLane] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    auto live = [&](int g) { return (int64_t)(tm0 + g) * kTileM + wave * 32 < a.M && k < a.K; };
 
     if constexpr (OP == OP_PLAIN) {
-        // software pipeline over two register sets
+        // Software pipeline over two register sets.  Every pass through the
+        // loop body issues the same memory instructions (the load past the
+        // walk's end reads a sub-tile outside the tensor, which costs no
+        // traffic), so the loads of the next sub-tile are never waited for
+        // early; the scheduling barriers keep each prefetch where it is
+        // issued instead of next to its first use.
         uint32_t wa[kRowsPerLane][4], wb[kRowsPerLane][4];
-        if (n > 0 && live(0))
-            load_plain(a, (int64_t)tm0 * kTileM + row_off, k, wa);
-        for (int g = 0; g < n; g += 2) {
-            if (g + 1 < n && live(g + 1))
-                load_plain(a, (int64_t)(tm0 + g + 1) * kTileM + row_off, k, wb);
-            tile_step<ROW, COL, DBIAS>(a, wa, srow, st, tm0 + g, tk, g, dsum);
-            if (g + 1 < n) {
-                if (g + 2 < n && live(g + 2))
-                    load_plain(a, (int64_t)(tm0 + g + 2) * kTileM + row_off, k, wa);
-                tile_step<ROW, COL, DBIAS>(a, wb, srow, st, tm0 + g + 1, tk, g + 1, dsum);
-            }
+        const int past = a.tiles_m;   // a sub-tile row outside the tensor
+        load_tile<OP, Policy<ROW, COL>::x>(a, l, tm0, tk, wa);
+        int g = 0;
+        for (; g + 1 < n; g += 2) {
+            load_tile<OP, Policy<ROW, COL>::x>(a, l, tm0 + g + 1, tk, wb);
+            __builtin_amdgcn_sched_barrier(0);
+            tile_step<ROW, COL, DBIAS>(a, l, wa, srow, st, tm0 + g, tk, g, dsum);
+            load_tile<OP, Policy<ROW, COL>::x>(a, l, g + 2 < n ? tm0 + g + 2 : past, tk, wa);
+            __builtin_amdgcn_sched_barrier(0);
+            tile_step<ROW, COL, DBIAS>(a, l, wb, srow, st, tm0 + g + 1, tk, g + 1, dsum);
         }
+        if (g < n)
+            tile_step<ROW, COL, DBIAS>(a, l, wa, srow, st, tm0 + g, tk, g, dsum);
     } else {
         uint32_t w[kRowsPerLane][4];
         for (int g = 0; g < n; g++) {
-            if (live(g)) {
-                const int64_t m0 = (int64_t)(tm0 + g) * kTileM + row_off;
-                const uint16_t *px = a.x + m0 * a.ldx + k;
-                load_rows<OP>(a, px, OP == OP_DGELU ? a.aux + m0 * a.ldx + k : px, w);
-            }
-            tile_step<ROW, COL, DBIAS>(a, w, srow, st, tm0 + g, tk, g, dsum);
+            load_tile<OP, Policy<ROW, COL>::x>(a, l, tm0 + g, tk, w);
+            tile_step<ROW, COL, DBIAS>(a, l, w, srow, st, tm0 + g, tk, g, dsum);
         }
     }
     if constexpr (COL)
-        col_flush_s(a, *st, rg, tk, n);
+        col_flush_s<Policy<ROW, COL>::s_col>(a, *st, rg, tk, n);
 
     if constexpr (DBIAS) {
         // per-lane sums (rows in order, sub-tiles in order), then the 8
         // lane-halves of the workgroup in order: one fp32 partial per
         // (strip segment, column)
         __shared__ float4 red[2 * kWaves][kTileK / 4];
-        const int slot = 2 * wave + half;
-        red[slot][cl * 2] = make_float4(dsum[0], dsum[1], dsum[2], dsum[3]);
-        red[slot][cl * 2 + 1] = make_float4(dsum[4], dsum[5], dsum[6], dsum[7]);
+        const int slot = 2 * l.wave + l.half;
+        red[slot][l.cl * 2] = make_float4(dsum[0], dsum[1], dsum[2], dsum[3]);
+        red[slot][l.cl * 2 + 1] = make_float4(dsum[4], dsum[5], dsum[6], dsum[7]);
         __syncthreads();
         const int t = (int)threadIdx.x;   // one column of the strip per thread
         const int64_t kc = (int64_t)tk * kTileK + t;

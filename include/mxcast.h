@@ -91,7 +91,7 @@ typedef enum mx_status {
  * MXFP8 cast of x[M][K] (bf16), block size 32.
  *   x        device, bf16 [M][K]
  *   grad     device, bf16 [M][K]; required for MX_FUSE_DGELU, else ignored
- *   M, K     rows, columns; positive multiples of 32, each <= 2^30, M*K <= 2^40
+ *   M, K     rows, columns; positive multiples of 32, each <= 2^23, M*K <= 2^40
  *   axis_mask  MX_ROWWISE, MX_COLWISE or both (one pass over x)
  *   fusion   MX_FUSE_NONE | GELU | DGELU, optionally | MX_FUSE_DBIAS
  *   q_row, s_row  E4M3 [M][K] and E8M0 [M][K/32]; required iff MX_ROWWISE
@@ -117,7 +117,7 @@ size_t mx_quantize_workspace_size(int64_t M, int64_t K, unsigned axis_mask, int 
 /*
  * Gated MXFP8 cast.  x is bf16 [M][2N] holding [gate | linear] (gate =
  * columns 0..N-1); the quantised tensor is y[M][N] = act(gate) * linear,
- * block size 32, M and N positive multiples of 32.
+ * block size 32, M and N positive multiples of 32, M <= 2^23, 2N <= 2^23.
  *   q_row, s_row  E4M3 [M][N], E8M0 [M][N/32]   (iff MX_ROWWISE)
  *   q_col, s_col  E4M3 [N][M], E8M0 [N][M/32]   (iff MX_COLWISE)
  */
@@ -131,7 +131,7 @@ mx_status mx_quantize_gated(const void *x, int64_t M, int64_t N, unsigned axis_m
  * value for op = 0x100 | MX_GATED_SWIGLU / MX_GATED_GEGLU (x is [M][2K],
  * y is [M][K]).  This is the exact tensor the fused casts quantise; it is
  * exposed so that the pre-op arithmetic can be checked on its own.  M and K
- * are positive multiples of 32.
+ * are positive multiples of 32, each <= 2^23 (2K <= 2^23 for gated ops).
  */
 #define MX_OP_GATED 0x100
 mx_status mx_fused_values(const void *x, const void *grad, int64_t M, int64_t K, int op,
@@ -147,7 +147,7 @@ mx_status mx_absmax_bf16(const void *x, int64_t n, float *amax, hipStream_t stre
 
 /*
  * NVFP4 quantize-transpose of x[M][K] (bf16), block size 16, M and K positive
- * multiples of 16.
+ * multiples of 16, each <= 2^23, M*K <= 2^40.
  *   amax     device, one fp32: the tensor absmax the global scale is built
  *            from (e.g. from mx_absmax_bf16 on the same stream)
  *   q_row, s_row  packed E2M1 [M][K/2] (element 2j in the low nibble of byte

@@ -120,6 +120,8 @@ NULL = ctypes.c_void_p(0)
     (dict(M=-32), mx.MX_ERR_SHAPE),
     (dict(M=1 << 31), mx.MX_ERR_SHAPE),
     (dict(M=1 << 26, K=1 << 26), mx.MX_ERR_SHAPE),
+    (dict(M=(1 << 23) + 32), mx.MX_ERR_SHAPE),
+    (dict(K=(1 << 23) + 32), mx.MX_ERR_SHAPE),
     (dict(fusion=mx.FUSE_DBIAS, ws=NULL), mx.MX_ERR_WORKSPACE),
     (dict(fusion=mx.FUSE_DBIAS, ws_bytes=16), mx.MX_ERR_WORKSPACE),
 ])

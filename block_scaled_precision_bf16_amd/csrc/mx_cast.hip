@@ -259,9 +259,11 @@ __device__ __forceinline__ void col_flush_q(const MxArgs &a, const ColStage &st,
     }
 }
 
-// Write the strip segment's column scales: thread t owns column k0 + t and
-// writes its 4 n scale bytes (n sub-tiles) as 16-byte stores when the row of
-// s_col allows it (a whole 64-byte chunk for a 16-deep walk), else bytewise.
+// Write the strip segment's column scales (4 n bytes per column for n
+// sub-tiles).  When the rows of s_col allow 16-byte stores, the c = 4n / 16
+// chunks of a column go to c neighbouring threads, so one store instruction
+// touches 64 / c lines rather than 64 (scattered partial-line stores are what
+// cost here); otherwise thread t writes column k0 + t bytewise.
 template <int AUX>
 __device__ __forceinline__ void col_flush_s(const MxArgs &a, const ColStage &st, int rg, int tk,
                                             int n)
@@ -273,11 +275,16 @@ __device__ __forceinline__ void col_flush_s(const MxArgs &a, const ColStage &st,
     const int64_t left = nblk - first;
     const int count = (int)(left < 4 * n ? left : 4 * n);
     const rsrc_t rs = make_rsrc(a.s_col, k0 * nblk + first, a.K * nblk);
-    const uint32_t off = k0 + t < a.K ? (uint32_t)(t * nblk) : kDead;
     if (((nblk | first) & 15) == 0 && (count & 15) == 0) {
-        for (int i = 0; i < count; i += 16)
-            buf_store16<AUX>(rs, off + i, *reinterpret_cast<const uint4 *>(&st.s[t][i]));
+        const int chunks = count >> 4;                    // 16-byte chunks per column
+        for (int i = 0; i < chunks; i++) {
+            const int idx = t + kThreads * i;             // (column, chunk) pair
+            const int c = idx / chunks, q = idx - c * chunks;
+            const uint32_t off = k0 + c < a.K ? (uint32_t)(c * nblk) + 16 * q : kDead;
+            buf_store16<AUX>(rs, off, *reinterpret_cast<const uint4 *>(&st.s[c][16 * q]));
+        }
     } else {
+        const uint32_t off = k0 + t < a.K ? (uint32_t)(t * nblk) : kDead;
         for (int i = 0; i < count; i++)
             buf_store1<AUX>(rs, off + i, st.s[t][i]);
     }

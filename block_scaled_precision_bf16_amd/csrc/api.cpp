@@ -275,6 +275,8 @@ mx_status nvfp4_quantize_transpose(const void *x, int64_t M, int64_t K, const fl
     a.sg_out = global_scale_out;
     a.tiles_k = tiles(K, mxk::kTileK);
     a.tiles_m = tiles(M, mxk::kTileM);
+    a.group = mxk::pick_group(a.tiles_m, a.tiles_k);
+    a.groups_m = (a.tiles_m + a.group - 1) / a.group;
     return from_hip(mxk::launch_nvfp4(axis_mask, a, stream));
 }
 

@@ -53,7 +53,8 @@ struct Nv4Args {
     const float *amax;
     uint8_t *q_row, *s_row, *q_col, *s_col;
     float *sg_out;
-    int tiles_k, tiles_m;
+    int tiles_k, tiles_m;  // 128 x 256 sub-tiles along K and M
+    int group, groups_m;   // sub-tiles per workgroup walk, walks along M
 };
 
 // op: 0 plain, 1 GELU, 2 dGELU, 3 SwiGLU, 4 GeGLU.

@@ -6,142 +6,392 @@
 // row-wise output and along M for the transposed output.
 //
 // Same work layout as the MXFP8 cast: a lane owns 16 rows x 8 columns of a
-// 128 x 256 workgroup tile, which makes each lane's 16 rows exactly one
-// column block of the transposed output (no cross-lane work for dim1); a row
-// block of 16 spans two lanes, combined with one DPP permute.
+// 128 x 256 sub-tile, which makes each lane's 16 rows exactly one column
+// block of the transposed output (no cross-lane work for dim1); a row block
+// of 16 spans two lanes, combined with one DPP permute.  A workgroup walks
+// down a 256-column strip with the next sub-tile's loads in flight; the
+// transposed nibbles of two sub-tiles are staged in LDS and leave as whole
+// 128-byte lines, the column scales of the whole walk at its end, the row
+// scales of each sub-tile as 16-byte pieces.  All global access goes through
+// buffer resources (bufio.h).
 //
 // Per block the scale chain costs three IEEE fp32 divisions (b/6, /S_g and
 // the reciprocal); each element then costs one multiply and half of a packed
 // hardware E2M1 convert.
 
+#include "bufio.h"
 #include "device_math.h"
 #include "launch.h"
 
 namespace mxk {
 
-// Block scale byte and the element multiplier of one NVFP4 block whose
-// largest magnitude has bf16 pattern `mag`.
-__device__ __forceinline__ void nv_block(uint32_t mag, float sg, uint32_t &sbyte, float &inv)
+// fl32(b / 6) for b >= 0 holding a bf16 value (at most 8 significant bits):
+// q0 = b * RN(1/6), the residual b - 6 q0 (exact in the FMA, since q0 is
+// within an ulp of b / 6), and one correction step.  Equal to the IEEE
+// division for every finite non-negative bf16 (checked exhaustively with
+// exact arithmetic by the CPU tests), at a third of its cost.
+__device__ __forceinline__ float div6_bf16(float b)
 {
-    const float b = f32_bits(mag << 16);
-    const float b6 = b / 6.0f;
-    const float sq = b6 / sg;
-    sbyte = e4m3_rne_sat(sq);
-    const float den = e4m3_value(sbyte) * sg;
-    inv = den == 0.0f ? 0.0f : 1.0f / den;
+    const float c = 0x1.555556p-3f;   // RN(1/6)
+    const float q0 = b * c;
+    const float r = __builtin_fmaf(-6.0f, q0, b);
+    return __builtin_fmaf(r, c, q0);
+}
+
+// Scale byte of one NVFP4 block whose largest magnitude has bf16 pattern
+// mag: E4M3(fl32(fl32(b / 6) / S_g)); the division by S_g is IEEE, the E4M3
+// rounding the saturating hardware convert (inputs are finite here).
+__device__ __forceinline__ uint32_t nv_scale(uint32_t mag, float sg)
+{
+    const float sq = div6_bf16(f32_bits(mag << 16)) / sg;
+    return e4m3x2<false>(sq, 0.0f, 0u) & 0xFFu;
+}
+
+// Element multiplier of scale byte s: fl32(1 / fl32(dec(s) * S_g)), 0 when
+// the product is 0.  It depends on s alone within a tensor, so a workgroup
+// tabulates the 127 finite codes once.
+__device__ __forceinline__ float nv_inverse(uint32_t s, float sg)
+{
+    const float den = e4m3_value(s) * sg;
+    return den == 0.0f ? 0.0f : 1.0f / den;
+}
+
+// 0xF when bf16 h is +-0 or NaN (its product with an infinite multiplier is
+// NaN), else 0.
+__device__ __forceinline__ uint32_t zero_or_nan_nibble(uint32_t h)
+{
+    const uint32_t a = h & 0x7FFFu;
+    return (a == 0u || a > 0x7F80u) ? 0xFu : 0u;
 }
 
 // Eight bf16 (four words) times inv -> eight E2M1 nibbles, element i in bits
-// 4i..4i+3 (so element 2j is the low nibble of byte j).  A block whose
-// multiplier overflowed to Inf (tensor scale below ~2^-120) takes the software
-// encoder, which maps 0 * Inf to +0.
+// 4i..4i+3 (so element 2j is the low nibble of byte j).  The hardware
+// convert matches the software encoder on every non-NaN product; a NaN
+// product (0 * Inf or NaN * Inf, possible only when the multiplier
+// overflowed to Inf, tensor scale below ~2^-120) encodes as 0 there, so such
+// nibbles are cleared afterwards.
 __device__ __forceinline__ uint32_t encode8_fp4(const uint32_t (&w)[4], float inv)
 {
-    if (__builtin_isinf(inv)) {
-        uint32_t o = 0;
-#pragma unroll
-        for (int d = 0; d < 4; d++) {
-            o |= e2m1_rne_sat(bf16_lo(w[d]) * inv) << (8 * d);
-            o |= e2m1_rne_sat(bf16_hi(w[d]) * inv) << (8 * d + 4);
-        }
-        return o;
-    }
     uint32_t o = e2m1x2<0>(bf16_lo(w[0]) * inv, bf16_hi(w[0]) * inv, 0u);
     o = e2m1x2<1>(bf16_lo(w[1]) * inv, bf16_hi(w[1]) * inv, o);
     o = e2m1x2<2>(bf16_lo(w[2]) * inv, bf16_hi(w[2]) * inv, o);
-    return e2m1x2<3>(bf16_lo(w[3]) * inv, bf16_hi(w[3]) * inv, o);
+    o = e2m1x2<3>(bf16_lo(w[3]) * inv, bf16_hi(w[3]) * inv, o);
+    if (__builtin_isinf(inv)) {
+        uint32_t clear = 0;
+#pragma unroll
+        for (int d = 0; d < 4; d++)
+            clear |= (zero_or_nan_nibble(w[d]) << (8 * d)) | (zero_or_nan_nibble(w[d] >> 16) << (8 * d + 4));
+        o &= ~clear;
+    }
+    return o;
 }
 
 // Rows 8q..8q+7 of one column (half HI of word d) times inv -> eight nibbles,
-// row 8q+i in bits 4i..4i+3.
+// row 8q+i in bits 4i..4i+3 (NaN products cleared as above).
 template <int HI>
 __device__ __forceinline__ uint32_t encode8_fp4_col(const uint32_t (&w)[kRowsPerLane][4], int q,
                                                     int d, float inv)
 {
+    auto h = [&](int i) { return HI ? w[8 * q + i][d] >> 16 : w[8 * q + i][d]; };
     auto v = [&](int i) { return (HI ? bf16_hi(w[8 * q + i][d]) : bf16_lo(w[8 * q + i][d])) * inv; };
-    if (__builtin_isinf(inv)) {
-        uint32_t o = 0;
-#pragma unroll
-        for (int i = 0; i < 8; i++)
-            o |= e2m1_rne_sat(v(i)) << (4 * i);
-        return o;
-    }
     uint32_t o = e2m1x2<0>(v(0), v(1), 0u);
     o = e2m1x2<1>(v(2), v(3), o);
     o = e2m1x2<2>(v(4), v(5), o);
-    return e2m1x2<3>(v(6), v(7), o);
+    o = e2m1x2<3>(v(6), v(7), o);
+    if (__builtin_isinf(inv)) {
+        uint32_t clear = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            clear |= zero_or_nan_nibble(h(i)) << (4 * i);
+        o &= ~clear;
+    }
+    return o;
 }
 
+// Cache policy of each stream (as for the MXFP8 cast): non-temporal input;
+// with both outputs, non-temporal transposed output.
 template <bool ROW, bool COL>
-__global__ __launch_bounds__(kThreads) void nvfp4_kernel(Nv4Args a)
+struct NvPolicy {
+    static constexpr int x = kNT;
+    static constexpr int q_row = 0, s_row = 0;
+    static constexpr int q_col = ROW && COL ? kNT : 0;
+    static constexpr int s_col = ROW && COL ? kNT : 0;
+};
+
+// Lane coordinates: the lane's 16 rows start at `row` inside the sub-tile.
+struct NvLane {
+    int wave, half, cl, row;
+};
+
+__device__ __forceinline__ NvLane nv_lane()
 {
-    const int tile = xcd_tile((int)blockIdx.x, (int)gridDim.x);
-    const int tm = tile / a.tiles_k;
-    const int tk = tile - tm * a.tiles_k;
-    const int wave = (int)threadIdx.x >> 6, lane = (int)threadIdx.x & 63;
-    const int half = lane >> 5, cl = lane & 31;
-    const int64_t m0 = (int64_t)tm * kTileM + wave * (2 * kRowsPerLane) + half * kRowsPerLane;
-    const int64_t k = (int64_t)tk * kTileK + cl * kColsPerLane;
+    NvLane l;
+    l.wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int lane = (int)threadIdx.x & 63;
+    l.half = lane >> 5;
+    l.cl = lane & 31;
+    l.row = l.wave * (2 * kRowsPerLane) + l.half * kRowsPerLane;
+    return l;
+}
+
+// M and K are multiples of 16: a lane's 16 rows, and the two lanes of a row
+// block, exist or not together.
+__device__ __forceinline__ bool nv_live(const Nv4Args &a, const NvLane &l, int tm, int tk)
+{
+    return (int64_t)tm * kTileM + l.row < a.M && (int64_t)tk * kTileK + l.cl * kColsPerLane < a.K;
+}
+
+// LDS staging.  q: the transposed E2M1 output of two consecutive sub-tiles
+// (256 rows = 128 bytes per transposed row), as 8 chunks of 16 bytes per
+// transposed row, chunk j at position j ^ ((kl >> 3) & 7) (the flush reads a
+// row's 8 chunks with 8 threads without bank conflicts).  Sub-tile p of the
+// pair fills chunks 4p..4p+3; the lane of rows 16h..16h+15 of the sub-tile
+// writes bytes 8(h & 1) of chunk 4p + h / 2.  s: the 8 column-block scales
+// per sub-tile of the whole walk.  srow: the 16 row-block scales per row of
+// the current sub-tile.
+struct NvStage {
+    uint8_t q[kTileK][128];                      // 32 KB
+    uint8_t s[kTileK][8 * kMaxGroup];            // 32 KB
+    uint8_t srow[kTileM][kTileK / 16];           // 2 KB
+    float inv[128];                              // multiplier of each scale byte
+};
+
+__device__ __forceinline__ int nv_chunk(int kl, int j) { return j ^ ((kl >> 3) & 7); }
+
+template <int XA>
+__device__ __forceinline__ void nv_load(const Nv4Args &a, const NvLane &l, int tm, int tk,
+                                        uint32_t (&w)[kRowsPerLane][4])
+{
+    const int64_t tile = (int64_t)tm * kTileM * a.K + (int64_t)tk * kTileK;
+    const rsrc_t rx = make_rsrc(a.x, 2 * tile, 2 * a.M * a.K);
+    const uint32_t rs = (uint32_t)(2 * a.K);
+    const uint32_t off = nv_live(a, l, tm, tk)
+                             ? (uint32_t)l.row * rs + (uint32_t)(2 * kColsPerLane * l.cl)
+                             : kDead;
+#pragma unroll
+    for (int r = 0; r < kRowsPerLane; r++) {
+        const uint4 v = buf_load16<XA>(rx, off + r * rs);
+        w[r][0] = v.x; w[r][1] = v.y; w[r][2] = v.z; w[r][3] = v.w;
+    }
+}
+
+// Transposed output of the staged pair (chunks 0..4 * parts - 1 of each
+// transposed row; parts = 1 when the walk ends on the first sub-tile of a
+// pair).  tm: the pair's first sub-tile.  HALF: M is not a multiple of 32,
+// so a 16-byte chunk may hold 16 rows inside M and 16 outside; then each
+// chunk leaves as two 8-byte halves.
+template <int AUX, bool HALF>
+__device__ __forceinline__ void nv_flush_q(const Nv4Args &a, const NvStage &st, int tm, int tk,
+                                           int parts)
+{
+    const int t = (int)threadIdx.x;
+    const int jr = t & 7;
+    const int64_t m0 = (int64_t)tm * kTileM;
+    const int64_t k0 = (int64_t)tk * kTileK;
+    const int64_t ld = a.M >> 1;                               // bytes per transposed row
+    const rsrc_t rc = make_rsrc(a.q_col, k0 * ld + (m0 >> 1), a.K * ld);
+    const int64_t row0 = m0 + 32 * jr;                         // first row of chunk jr
+    const bool in_pair = jr < 4 * parts;
+#pragma unroll
+    for (int i = 0; i < kTileK / 32; i++) {
+        const int kr = (t >> 3) + 32 * i;
+        const bool col_ok = in_pair && k0 + kr < a.K;
+        const uint4 v = *reinterpret_cast<const uint4 *>(&st.q[kr][16 * nv_chunk(kr, jr)]);
+        const uint32_t off = (uint32_t)(kr * ld) + 16 * jr;
+        if constexpr (!HALF) {
+            buf_store16<AUX>(rc, col_ok && row0 < a.M ? off : kDead, v);
+        } else {
+            buf_store8<AUX>(rc, col_ok && row0 < a.M ? off : kDead, make_uint2(v.x, v.y));
+            buf_store8<AUX>(rc, col_ok && row0 + 16 < a.M ? off + 8 : kDead, make_uint2(v.z, v.w));
+        }
+    }
+}
+
+// Column-block scales of the walk: 8 n bytes per column for n sub-tiles,
+// 16-byte chunks from neighbouring threads when s_col's rows allow it.
+template <int AUX>
+__device__ __forceinline__ void nv_flush_s(const Nv4Args &a, const NvStage &st, int tm0, int tk,
+                                           int n)
+{
+    const int t = (int)threadIdx.x;
+    const int64_t k0 = (int64_t)tk * kTileK;
+    const int64_t nblk = a.M >> 4;                             // scales per column
+    const int64_t first = (int64_t)tm0 * (kTileM / 16);
+    const int64_t left = nblk - first;
+    const int count = (int)(left < 8 * n ? left : 8 * n);
+    const rsrc_t rs = make_rsrc(a.s_col, k0 * nblk + first, a.K * nblk);
+    if (((nblk | first) & 15) == 0 && (count & 15) == 0) {
+        const int chunks = count >> 4;
+        for (int i = 0; i < chunks; i++) {
+            const int idx = t + kThreads * i;
+            const int c = idx / chunks, q = idx - c * chunks;
+            const uint32_t off = k0 + c < a.K ? (uint32_t)(c * nblk) + 16 * q : kDead;
+            buf_store16<AUX>(rs, off, *reinterpret_cast<const uint4 *>(&st.s[c][16 * q]));
+        }
+    } else {
+        const uint32_t off = k0 + t < a.K ? (uint32_t)(t * nblk) : kDead;
+        for (int i = 0; i < count; i++)
+            buf_store1<AUX>(rs, off + i, st.s[t][i]);
+    }
+}
+
+// Row-block scales of sub-tile tm: thread t < 128 writes row t's 16 bytes.
+template <int AUX>
+__device__ __forceinline__ void nv_flush_srow(const Nv4Args &a, const NvStage &st, int tm, int tk)
+{
+    const int t = (int)threadIdx.x;
+    const int64_t row = (int64_t)tm * kTileM + t;
+    const int64_t k0 = (int64_t)tk * kTileK;
+    const int64_t nb = a.K >> 4;
+    const rsrc_t rs = make_rsrc(a.s_row, (int64_t)tm * kTileM * nb + (k0 >> 4), a.M * nb);
+    const uint32_t off = t < kTileM && row < a.M ? (uint32_t)(t * nb) : kDead;
+    const uint8_t *src = st.srow[t & (kTileM - 1)];
+    if ((a.K & 255) == 0) {
+        buf_store16<AUX>(rs, off, *reinterpret_cast<const uint4 *>(src));
+    } else {
+        const int64_t blocks = nb - (k0 >> 4);
+#pragma unroll
+        for (int b = 0; b < kTileK / 16; b++)
+            buf_store1<AUX>(rs, b < blocks ? off + b : kDead, src[b]);
+    }
+}
+
+// One sub-tile (g-th of the walk): row blocks (direct stores, scales to
+// LDS), column blocks into the staging pair; FLUSH 0: keep staging, 1: the
+// walk ends on the first sub-tile of a pair, 2: the pair is complete.
+template <bool ROW, bool COL, bool HALF, int FLUSH>
+__device__ __forceinline__ void nv_step(const Nv4Args &a, const NvLane &l,
+                                        const uint32_t (&w)[kRowsPerLane][4], NvStage &st,
+                                        float sg, int tm, int tk, int g)
+{
+    using P = NvPolicy<ROW, COL>;
+    const bool live = nv_live(a, l, tm, tk);
+    uint32_t cmax[4] = {0u, 0u, 0u, 0u};
+    rsrc_t rq;
+    uint32_t qoff = kDead;
+    if constexpr (ROW) {
+        const int64_t ld = a.K >> 1;
+        rq = make_rsrc(a.q_row, (int64_t)tm * kTileM * ld + (int64_t)tk * (kTileK / 2), a.M * ld);
+        if (live)
+            qoff = (uint32_t)(l.row * ld) + 4 * l.cl;
+    }
+    // Rows go in pairs: both lanes of a row block know the block maxima of
+    // rows r and r + 1; the even lane derives the scale of row r, the odd
+    // lane that of row r + 1, and they swap results.
+#pragma unroll
+    for (int r = 0; r < kRowsPerLane; r += 2) {
+        uint32_t mag2[2];
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            uint32_t m[4];
+#pragma unroll
+            for (int d = 0; d < 4; d++) {
+                m[d] = w[r + h][d] & 0x7FFF7FFFu;
+                if constexpr (COL)
+                    cmax[d] = pk_max_u16(cmax[d], m[d]);
+            }
+            const uint32_t t = pk_max_u16(pk_max_u16(m[0], m[1]), pk_max_u16(m[2], m[3]));
+            const uint32_t lo = t & 0xFFFFu, hi = t >> 16;
+            mag2[h] = max_xor1(lo > hi ? lo : hi);
+        }
+        if constexpr (ROW) {
+            const bool odd = l.cl & 1;
+            const uint32_t mine = nv_scale(odd ? mag2[1] : mag2[0], sg);
+            const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)mine, 0xB1, 0xF, 0xF, false);
+            const uint32_t sb0 = odd ? other : mine, sb1 = odd ? mine : other;
+            buf_store4<P::q_row>(rq, qoff + (uint32_t)(r * (a.K >> 1)),
+                                 encode8_fp4(w[r], st.inv[sb0]));
+            buf_store4<P::q_row>(rq, qoff + (uint32_t)((r + 1) * (a.K >> 1)),
+                                 encode8_fp4(w[r + 1], st.inv[sb1]));
+            if (!odd) {
+                st.srow[l.row + r][l.cl >> 1] = (uint8_t)sb0;
+                st.srow[l.row + r + 1][l.cl >> 1] = (uint8_t)sb1;
+            }
+        }
+        // one row pair at a time: left alone, the scheduler interleaves the
+        // scale divisions of all rows and runs out of registers
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (COL) {
+        // The row pass expanded every element to fp32; without this empty,
+        // register-only barrier the compiler keeps those 128 values alive for
+        // reuse here instead of re-deriving them from the 64 packed words.
+        uint32_t wc[kRowsPerLane][4];
+#pragma unroll
+        for (int r = 0; r < kRowsPerLane; r++)
+#pragma unroll
+            for (int d = 0; d < 4; d++) {
+                wc[r][d] = w[r][d];
+                if constexpr (ROW)
+                    asm volatile("" : "+v"(wc[r][d]));
+            }
+        const int p = g & 1;
+        const int jr = 4 * p + l.wave;                       // logical 16-byte chunk
+#pragma unroll
+        for (int c = 0; c < kColsPerLane; c++) {
+            const int d = c >> 1, hi = c & 1;
+            const uint32_t mag = hi ? (cmax[d] >> 16) : (cmax[d] & 0xFFFFu);
+            const uint32_t sb = nv_scale(mag, sg);
+            const float inv = st.inv[sb];
+            uint32_t o[2];
+#pragma unroll
+            for (int q = 0; q < 2; q++)
+                o[q] = hi ? encode8_fp4_col<1>(wc, q, d, inv) : encode8_fp4_col<0>(wc, q, d, inv);
+            const int kl = l.cl * kColsPerLane + c;
+            *reinterpret_cast<uint2 *>(&st.q[kl][16 * nv_chunk(kl, jr) + 8 * l.half]) =
+                make_uint2(o[0], o[1]);
+            st.s[kl][8 * g + 2 * l.wave + l.half] = (uint8_t)sb;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    __syncthreads();
+    if constexpr (ROW)
+        nv_flush_srow<P::s_row>(a, st, tm, tk);
+    if constexpr (COL && FLUSH != 0)
+        nv_flush_q<P::q_col, HALF>(a, st, FLUSH == 2 ? tm - 1 : tm, tk, FLUSH);
+    __syncthreads();
+}
+
+// A workgroup walks a 256-column strip down `group` sub-tiles of 128 rows,
+// with the next sub-tile's loads in flight while one is converted (as in the
+// MXFP8 cast); the transposed output leaves every second sub-tile as whole
+// 128-byte lines.
+template <bool ROW, bool COL, bool HALF>
+__global__ __launch_bounds__(kThreads, 2) void nvfp4_kernel(Nv4Args a)
+{
+    using P = NvPolicy<ROW, COL>;
+    const int job = xcd_tile((int)blockIdx.x, (int)gridDim.x);
+    const int rg = job / a.tiles_k;
+    const int tk = job - rg * a.tiles_k;
+    const int tm0 = rg * a.group;
+    const int n = (a.tiles_m - tm0) < a.group ? (a.tiles_m - tm0) : a.group;
+    const NvLane l = nv_lane();
 
     const float A = *a.amax;
     const float sg = A == 0.0f ? 1.0f : A / 2688.0f;
     if (a.sg_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
         *a.sg_out = sg;
-    // M and K are multiples of 16: a lane's 16 rows, and the two lanes of a
-    // row block, are valid or invalid together.
-    if (m0 >= a.M || k >= a.K)
-        return;
 
-    uint32_t w[kRowsPerLane][4];
-#pragma unroll
-    for (int r = 0; r < kRowsPerLane; r++) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(a.x + (m0 + r) * a.K + k);
-        w[r][0] = v.x; w[r][1] = v.y; w[r][2] = v.z; w[r][3] = v.w;
+    __shared__ NvStage st;
+    if (threadIdx.x < 128)
+        st.inv[threadIdx.x] = nv_inverse(threadIdx.x, sg);
+    __syncthreads();
+    uint32_t wa[kRowsPerLane][4], wb[kRowsPerLane][4];
+    const int past = a.tiles_m;   // a sub-tile row outside the tensor: reads as zeros
+    nv_load<P::x>(a, l, tm0, tk, wa);
+    int g = 0;
+    for (; g + 1 < n; g += 2) {
+        nv_load<P::x>(a, l, tm0 + g + 1, tk, wb);
+        __builtin_amdgcn_sched_barrier(0);
+        nv_step<ROW, COL, HALF, 0>(a, l, wa, st, sg, tm0 + g, tk, g);
+        nv_load<P::x>(a, l, g + 2 < n ? tm0 + g + 2 : past, tk, wa);
+        __builtin_amdgcn_sched_barrier(0);
+        nv_step<ROW, COL, HALF, 2>(a, l, wb, st, sg, tm0 + g + 1, tk, g + 1);
     }
-
-    uint32_t cmax[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int r = 0; r < kRowsPerLane; r++) {
-        uint32_t m[4];
-#pragma unroll
-        for (int d = 0; d < 4; d++) {
-            m[d] = w[r][d] & 0x7FFF7FFFu;
-            if constexpr (COL)
-                cmax[d] = pk_max_u16(cmax[d], m[d]);
-        }
-        if constexpr (ROW) {
-            const uint32_t t = pk_max_u16(pk_max_u16(m[0], m[1]), pk_max_u16(m[2], m[3]));
-            const uint32_t lo = t & 0xFFFFu, hi = t >> 16;
-            uint32_t mag = lo > hi ? lo : hi;
-            mag = max_xor1(mag);
-            uint32_t sb;
-            float inv;
-            nv_block(mag, sg, sb, inv);
-            const int64_t row = m0 + r;
-            *reinterpret_cast<uint32_t *>(a.q_row + row * (a.K >> 1) + (k >> 1)) =
-                encode8_fp4(w[r], inv);
-            if ((lane & 1) == 0)
-                a.s_row[row * (a.K >> 4) + (k >> 4)] = (uint8_t)sb;
-        }
-    }
-
-    if constexpr (COL) {
-#pragma unroll
-        for (int c = 0; c < kColsPerLane; c++) {
-            const int d = c >> 1, hi = c & 1;
-            const uint32_t mag = hi ? (cmax[d] >> 16) : (cmax[d] & 0xFFFFu);
-            uint32_t sb;
-            float inv;
-            nv_block(mag, sg, sb, inv);
-            uint32_t o[2];
-#pragma unroll
-            for (int q = 0; q < 2; q++)
-                o[q] = hi ? encode8_fp4_col<1>(w, q, d, inv) : encode8_fp4_col<0>(w, q, d, inv);
-            *reinterpret_cast<uint2 *>(a.q_col + (k + c) * (a.M >> 1) + (m0 >> 1)) =
-                make_uint2(o[0], o[1]);
-            a.s_col[(k + c) * (a.M >> 4) + (m0 >> 4)] = (uint8_t)sb;
-        }
-    }
+    if (g < n)
+        nv_step<ROW, COL, HALF, 1>(a, l, wa, st, sg, tm0 + g, tk, g);
+    if constexpr (COL)
+        nv_flush_s<P::s_col>(a, st, tm0, tk, n);
 }
 
 // ---------------------------------------------------------------------------
@@ -153,14 +403,28 @@ __global__ void absmax_clear_kernel(uint32_t *amax_bits) { *amax_bits = 0u; }
 __global__ __launch_bounds__(256) void absmax_kernel(const uint16_t *x, int64_t n,
                                                      uint32_t *amax_bits)
 {
+    const u32x4_t *xv = reinterpret_cast<const u32x4_t *>(x);
     const int64_t nvec = n >> 3;
     const int64_t stride = (int64_t)gridDim.x * 256;
+    auto fold = [](uint32_t m, u32x4_t v) {
+        return pk_max_u16(m, pk_max_u16(pk_max_u16(v[0] & 0x7FFF7FFFu, v[1] & 0x7FFF7FFFu),
+                                        pk_max_u16(v[2] & 0x7FFF7FFFu, v[3] & 0x7FFF7FFFu)));
+    };
     uint32_t m = 0;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nvec; i += stride) {
-        const uint4 v = reinterpret_cast<const uint4 *>(x)[i];
-        m = pk_max_u16(m, pk_max_u16(pk_max_u16(v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu),
-                                     pk_max_u16(v.z & 0x7FFF7FFFu, v.w & 0x7FFF7FFFu)));
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    // four independent 16-byte loads in flight per thread; the input is read
+    // once, so the loads are non-temporal
+    for (; i + 3 * stride < nvec; i += 4 * stride) {
+        u32x4_t v[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            v[j] = __builtin_nontemporal_load(xv + i + j * stride);
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            m = fold(m, v[j]);
     }
+    for (; i < nvec; i += stride)
+        m = fold(m, __builtin_nontemporal_load(xv + i));
     if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
         const uint32_t t = x[(nvec << 3) + threadIdx.x] & 0x7FFFu;
         m = pk_max_u16(m, t);
@@ -184,8 +448,8 @@ hipError_t launch_absmax(const uint16_t *x, int64_t n, float *amax, hipStream_t 
     if (e != hipSuccess)
         return e;
     int64_t blocks = ((n >> 3) + 255) / 256;
-    if (blocks > 4096)
-        blocks = 4096;
+    if (blocks > 2048)
+        blocks = 2048;
     if (blocks < 1)
         blocks = 1;
     hipLaunchKernelGGL(absmax_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, n, bits);
@@ -195,8 +459,11 @@ hipError_t launch_absmax(const uint16_t *x, int64_t n, float *amax, hipStream_t 
 template <bool ROW, bool COL>
 static hipError_t launch_nv(const Nv4Args &a, hipStream_t s)
 {
-    hipLaunchKernelGGL((nvfp4_kernel<ROW, COL>), dim3(a.tiles_m * a.tiles_k), dim3(kThreads), 0,
-                       s, a);
+    const dim3 grid((unsigned)(a.groups_m * a.tiles_k));
+    if (COL && (a.M & 31) != 0)
+        hipLaunchKernelGGL((nvfp4_kernel<ROW, COL, true>), grid, dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((nvfp4_kernel<ROW, COL, false>), grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -48,13 +48,14 @@ __device__ __forceinline__ float half_value(uint32_t w, int hi)
 // default policy (non-temporal row scales, 8-byte pieces of lines that other
 // workgroups complete, cost ~15%).  With one output only the loads are
 // non-temporal.  The policies change timing only, never results.
-template <bool ROW, bool COL>
+template <int OP, bool ROW, bool COL>
 struct Policy {
-    static constexpr int x = kNT;                        // input loads
-    static constexpr int q_row = ROW && COL ? kSC1 : 0;  // row-wise stores
+    static constexpr bool plain = OP == OP_PLAIN, both = plain && ROW && COL;
+    static constexpr int x = plain ? kNT : 0;            // input loads
+    static constexpr int q_row = both ? kSC1 : 0;        // row-wise stores
     static constexpr int s_row = 0;
-    static constexpr int q_col = ROW && COL ? kNT : 0;   // transposed stores
-    static constexpr int s_col = ROW && COL ? kNT : 0;
+    static constexpr int q_col = both ? kNT : 0;         // transposed stores
+    static constexpr int s_col = both ? kNT : 0;
 };
 
 // Row r's 8 elements (4 words w, magnitudes mag) with scale byte b -> 8 E4M3
@@ -163,7 +164,7 @@ __device__ __forceinline__ void load_tile(const MxArgs &a, const LaneAt &l, int 
 
 // Row-wise blocks of this lane's 16 rows: amax over 4 lanes x 8 columns,
 // scale, convert, store.  Column maxima are accumulated on the way.
-template <bool ROW, bool COL>
+template <int OP, bool ROW, bool COL>
 __device__ __forceinline__ void row_pass(const MxArgs &a, const uint32_t (&w)[kRowsPerLane][4],
                                          const LaneAt &l, int tm, int tk, bool live, uint8_t *srow,
                                          uint32_t (&cmax)[4])
@@ -194,7 +195,7 @@ __device__ __forceinline__ void row_pass(const MxArgs &a, const uint32_t (&w)[kR
             uint2 o = encode8_row(w[r], m, sb);
             if (sb == 0xFFu)
                 o.x = o.y = 0x7F7F7F7Fu;
-            buf_store8<Policy<ROW, COL>::q_row>(rq, off + (uint32_t)(r * a.K), o);
+            buf_store8<Policy<OP, ROW, COL>::q_row>(rq, off + (uint32_t)(r * a.K), o);
             if ((l.cl & 3) == 0)
                 srow[r * (kTileK / 32)] = (uint8_t)sb;
         }
@@ -259,35 +260,54 @@ __device__ __forceinline__ void col_flush_q(const MxArgs &a, const ColStage &st,
     }
 }
 
-// Write the strip segment's column scales (4 n bytes per column for n
-// sub-tiles).  When the rows of s_col allow 16-byte stores, the c = 4n / 16
-// chunks of a column go to c neighbouring threads, so one store instruction
-// touches 64 / c lines rather than 64 (scattered partial-line stores are what
-// cost here); otherwise thread t writes column k0 + t bytewise.
+// Column scales of a strip segment in CH-byte pieces: the count / CH pieces
+// of a column go to neighbouring threads, so one store instruction touches
+// 64 CH / count lines rather than 64 (scattered partial-line stores are what
+// cost here).
+template <int AUX, int CH>
+__device__ __forceinline__ void col_flush_s_ch(const MxArgs &a, const ColStage &st, rsrc_t rs,
+                                               int64_t k0, int64_t nblk, int count)
+{
+    const int t = (int)threadIdx.x;
+    const int pieces = count / CH;                        // per column
+    for (int i = 0; i < pieces; i++) {
+        const int idx = t + kThreads * i;                 // (column, piece) pair
+        const int c = idx / pieces, q = idx - c * pieces;
+        const uint32_t off = k0 + c < a.K ? (uint32_t)(c * nblk) + CH * q : kDead;
+        const uint8_t *src = &st.s[c][CH * q];
+        if constexpr (CH == 16)
+            buf_store16<AUX>(rs, off, *reinterpret_cast<const uint4 *>(src));
+        else if constexpr (CH == 8)
+            buf_store8<AUX>(rs, off, *reinterpret_cast<const uint2 *>(src));
+        else if constexpr (CH == 4)
+            buf_store4<AUX>(rs, off, *reinterpret_cast<const uint32_t *>(src));
+        else
+            buf_store1<AUX>(rs, off, *src);
+    }
+}
+
+// Write the strip segment's column scales: 4 n bytes per column for a walk
+// of n sub-tiles, in the widest pieces (16, 8, 4 or 1 bytes) that the row
+// length of s_col, the segment's start and its length allow.
 template <int AUX>
 __device__ __forceinline__ void col_flush_s(const MxArgs &a, const ColStage &st, int rg, int tk,
                                             int n)
 {
-    const int t = (int)threadIdx.x;
     const int64_t k0 = (int64_t)tk * kTileK;
     const int64_t nblk = a.M >> 5;                        // scales per column
     const int64_t first = (int64_t)rg * a.group * 4;      // this segment's first block
     const int64_t left = nblk - first;
     const int count = (int)(left < 4 * n ? left : 4 * n);
     const rsrc_t rs = make_rsrc(a.s_col, k0 * nblk + first, a.K * nblk);
-    if (((nblk | first) & 15) == 0 && (count & 15) == 0) {
-        const int chunks = count >> 4;                    // 16-byte chunks per column
-        for (int i = 0; i < chunks; i++) {
-            const int idx = t + kThreads * i;             // (column, chunk) pair
-            const int c = idx / chunks, q = idx - c * chunks;
-            const uint32_t off = k0 + c < a.K ? (uint32_t)(c * nblk) + 16 * q : kDead;
-            buf_store16<AUX>(rs, off, *reinterpret_cast<const uint4 *>(&st.s[c][16 * q]));
-        }
-    } else {
-        const uint32_t off = k0 + t < a.K ? (uint32_t)(t * nblk) : kDead;
-        for (int i = 0; i < count; i++)
-            buf_store1<AUX>(rs, off + i, st.s[t][i]);
-    }
+    const int64_t align = nblk | first | count;
+    if ((align & 15) == 0)
+        col_flush_s_ch<AUX, 16>(a, st, rs, k0, nblk, count);
+    else if ((align & 7) == 0)
+        col_flush_s_ch<AUX, 8>(a, st, rs, k0, nblk, count);
+    else if ((align & 3) == 0)
+        col_flush_s_ch<AUX, 4>(a, st, rs, k0, nblk, count);
+    else
+        col_flush_s_ch<AUX, 1>(a, st, rs, k0, nblk, count);
 }
 
 // Row scales of a sub-tile, staged as [128 rows][8 blocks] bytes: thread
@@ -317,7 +337,7 @@ __device__ __forceinline__ void srow_flush(const MxArgs &a, const uint8_t (&srow
 // One sub-tile of the walk: row pass (direct row stores, row scales to LDS),
 // column pass into LDS, then the staged output leaves as whole lines.  Lanes
 // outside the tensor hold zeros and their stores are out of range.
-template <bool ROW, bool COL, bool DBIAS>
+template <int OP, bool ROW, bool COL, bool DBIAS>
 __device__ __forceinline__ void tile_step(const MxArgs &a, const LaneAt &l,
                                           const uint32_t (&w)[kRowsPerLane][4],
                                           uint8_t (&srow)[kTileM][kTileK / 32], ColStage *st,
@@ -325,7 +345,7 @@ __device__ __forceinline__ void tile_step(const MxArgs &a, const LaneAt &l,
 {
     const bool live = lane_live(a, l, tm, tk);
     uint32_t cmax[4] = {0u, 0u, 0u, 0u};
-    row_pass<ROW, COL>(a, w, l, tm, tk, live, &srow[l.row][l.cl >> 2], cmax);
+    row_pass<OP, ROW, COL>(a, w, l, tm, tk, live, &srow[l.row][l.cl >> 2], cmax);
     if constexpr (COL)
         col_pass(*st, w, l.wave, l.half, l.cl, g, cmax);
     if constexpr (DBIAS) {
@@ -340,9 +360,9 @@ __device__ __forceinline__ void tile_step(const MxArgs &a, const LaneAt &l,
     }
     __syncthreads();
     if constexpr (COL)
-        col_flush_q<Policy<ROW, COL>::q_col>(a, *st, tm, tk);
+        col_flush_q<Policy<OP, ROW, COL>::q_col>(a, *st, tm, tk);
     if constexpr (ROW)
-        srow_flush<Policy<ROW, COL>::s_row>(a, srow, tm, tk);
+        srow_flush<Policy<OP, ROW, COL>::s_row>(a, srow, tm, tk);
     __syncthreads();   // the staging buffers are reused by the next sub-tile
 }
 
@@ -377,27 +397,27 @@ __global__ __launch_bounds__(kThreads) void mx_cast_kernel(MxArgs a)
         // issued instead of next to its first use.
         uint32_t wa[kRowsPerLane][4], wb[kRowsPerLane][4];
         const int past = a.tiles_m;   // a sub-tile row outside the tensor
-        load_tile<OP, Policy<ROW, COL>::x>(a, l, tm0, tk, wa);
+        load_tile<OP, Policy<OP, ROW, COL>::x>(a, l, tm0, tk, wa);
         int g = 0;
         for (; g + 1 < n; g += 2) {
-            load_tile<OP, Policy<ROW, COL>::x>(a, l, tm0 + g + 1, tk, wb);
+            load_tile<OP, Policy<OP, ROW, COL>::x>(a, l, tm0 + g + 1, tk, wb);
             __builtin_amdgcn_sched_barrier(0);
-            tile_step<ROW, COL, DBIAS>(a, l, wa, srow, st, tm0 + g, tk, g, dsum);
-            load_tile<OP, Policy<ROW, COL>::x>(a, l, g + 2 < n ? tm0 + g + 2 : past, tk, wa);
+            tile_step<OP, ROW, COL, DBIAS>(a, l, wa, srow, st, tm0 + g, tk, g, dsum);
+            load_tile<OP, Policy<OP, ROW, COL>::x>(a, l, g + 2 < n ? tm0 + g + 2 : past, tk, wa);
             __builtin_amdgcn_sched_barrier(0);
-            tile_step<ROW, COL, DBIAS>(a, l, wb, srow, st, tm0 + g + 1, tk, g + 1, dsum);
+            tile_step<OP, ROW, COL, DBIAS>(a, l, wb, srow, st, tm0 + g + 1, tk, g + 1, dsum);
         }
         if (g < n)
-            tile_step<ROW, COL, DBIAS>(a, l, wa, srow, st, tm0 + g, tk, g, dsum);
+            tile_step<OP, ROW, COL, DBIAS>(a, l, wa, srow, st, tm0 + g, tk, g, dsum);
     } else {
         uint32_t w[kRowsPerLane][4];
         for (int g = 0; g < n; g++) {
-            load_tile<OP, Policy<ROW, COL>::x>(a, l, tm0 + g, tk, w);
-            tile_step<ROW, COL, DBIAS>(a, l, w, srow, st, tm0 + g, tk, g, dsum);
+            load_tile<OP, Policy<OP, ROW, COL>::x>(a, l, tm0 + g, tk, w);
+            tile_step<OP, ROW, COL, DBIAS>(a, l, w, srow, st, tm0 + g, tk, g, dsum);
         }
     }
     if constexpr (COL)
-        col_flush_s<Policy<ROW, COL>::s_col>(a, *st, rg, tk, n);
+        col_flush_s<Policy<OP, ROW, COL>::s_col>(a, *st, rg, tk, n);
 
     if constexpr (DBIAS) {
         // per-lane sums (rows in order, sub-tiles in order), then the 8

@@ -23,7 +23,7 @@ _f32p = ctypes.POINTER(ctypes.c_float)
 _f64p = ctypes.POINTER(ctypes.c_double)
 _i64 = ctypes.c_int64
 
-FUSE_NONE, FUSE_GELU, FUSE_DGELU, FUSE_DBIAS = 0, 1, 2, 0x10
+FUSE_NONE, FUSE_GELU, FUSE_DGELU, FUSE_DSILU, FUSE_DBIAS = 0, 1, 2, 3, 0x10
 GATED_SWIGLU, GATED_GEGLU = 1, 2
 ROWWISE, COLWISE = 1, 2
 
@@ -54,7 +54,7 @@ def lib():
         L.orc_mx_block.argtypes = [_f64p, ctypes.c_int, _u8p, _i64, _u8p]
         L.orc_exp32.restype = ctypes.c_float
         L.orc_exp32.argtypes = [ctypes.c_float]
-        for f in ("orc_gelu32", "orc_dgelu32", "orc_silu32"):
+        for f in ("orc_gelu32", "orc_dgelu32", "orc_silu32", "orc_dsilu32"):
             getattr(L, f).restype = ctypes.c_float
             getattr(L, f).argtypes = [ctypes.c_float]
         L.orc_preop.restype = ctypes.c_uint16
@@ -64,6 +64,12 @@ def lib():
         L.orc_mx_quantize.restype = ctypes.c_int
         L.orc_mx_quantize.argtypes = [_u16p, _u16p, _i64, _i64, ctypes.c_uint, ctypes.c_int,
                                       _u8p, _u8p, _u8p, _u8p, _f32p, _u16p]
+        L.orc_gated_bwd.restype = ctypes.c_int
+        L.orc_gated_bwd.argtypes = [ctypes.c_int, ctypes.c_uint16, ctypes.c_uint16,
+                                    ctypes.c_uint16, _u16p, _u16p]
+        L.orc_mx_quantize_dgated.restype = ctypes.c_int
+        L.orc_mx_quantize_dgated.argtypes = [_u16p, _u16p, _i64, _i64, ctypes.c_uint,
+                                             ctypes.c_int, _u8p, _u8p, _u8p, _u8p, _u16p]
         L.orc_mx_quantize_gated.restype = ctypes.c_int
         L.orc_mx_quantize_gated.argtypes = [_u16p, _i64, _i64, ctypes.c_uint, ctypes.c_int,
                                             _u8p, _u8p, _u8p, _u8p, _u16p]
@@ -176,7 +182,7 @@ def mx_block(values):
 
 # --- fused pre-op arithmetic (fp32 sequences) ---------------------------------
 
-_UNARY = {"exp": 0, "gelu": 1, "dgelu": 2, "silu": 3}
+_UNARY = {"exp": 0, "gelu": 1, "dgelu": 2, "silu": 3, "dsilu": 4}
 
 
 def unary32(which: str, v) -> np.ndarray:
@@ -192,6 +198,15 @@ def preop(pre: int, x: int, grad: int = 0) -> int:
 
 def gated(act: int, gate: int, lin: int) -> int:
     return lib().orc_gated(act, gate, lin)
+
+
+def gated_bwd(act: int, gate: int, lin: int, grad: int):
+    """(d_gate, d_lin) bf16 bits of the gated backward for one element pair."""
+    dg, dl = ctypes.c_uint16(), ctypes.c_uint16()
+    rc = lib().orc_gated_bwd(act, gate, lin, grad, ctypes.byref(dg), ctypes.byref(dl))
+    if rc != 0:
+        raise ValueError(f"oracle gated_bwd failed with code {rc}")
+    return dg.value, dl.value
 
 
 # --- tensor entry points --------------------------------------------------------
@@ -232,6 +247,27 @@ def mx_quantize_gated(x, act, axis=ROWWISE | COLWISE, want_y=False):
                                      _p(y, _u16p))
     if rc != 0:
         raise ValueError(f"oracle mx_quantize_gated failed with code {rc}")
+    return dict(q_row=q_row, s_row=s_row, q_col=q_col, s_col=s_col, y=y)
+
+
+def mx_quantize_dgated(grad, x, act, axis=ROWWISE | COLWISE, want_y=False):
+    """Gated backward MXFP8 cast: grad[M][N], x[M][2N] = [gate | linear]; the
+    quantised tensor is dx[M][2N] = [d_gate | d_lin]."""
+    grad = _c(grad, np.uint16)
+    x = _c(x, np.uint16)
+    M, N2 = x.shape
+    N = N2 // 2
+    assert grad.shape == (M, N)
+    q_row = np.zeros((M, N2), np.uint8) if axis & ROWWISE else None
+    s_row = np.zeros((M, N2 // 32), np.uint8) if axis & ROWWISE else None
+    q_col = np.zeros((N2, M), np.uint8) if axis & COLWISE else None
+    s_col = np.zeros((N2, M // 32), np.uint8) if axis & COLWISE else None
+    y = np.zeros((M, N2), np.uint16) if want_y else None
+    rc = lib().orc_mx_quantize_dgated(_p(grad, _u16p), _p(x, _u16p), M, N, axis, act,
+                                      _p(q_row, _u8p), _p(s_row, _u8p), _p(q_col, _u8p),
+                                      _p(s_col, _u8p), _p(y, _u16p))
+    if rc != 0:
+        raise ValueError(f"oracle mx_quantize_dgated failed with code {rc}")
     return dict(q_row=q_row, s_row=s_row, q_col=q_col, s_col=s_col, y=y)
 
 

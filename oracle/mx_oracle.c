@@ -32,7 +32,10 @@
  *   R4  column-wise output is the row-wise output of the transpose.
  *   R5  fused pre-ops are evaluated in fp32 by the sequences in this file and
  *       rounded once to bf16 (RNE); that bf16 tensor is what gets quantised
- *       and what dbias sums.
+ *       and what dbias sums.  The backward ones (dSiLU, dSwiGLU, dGeGLU, named
+ *       in the "MXFP8 generic quantize kernel" and gated tables) use the
+ *       derivative of the same forward sequences, in the order written in
+ *       orc_preop() and orc_gated_bwd().
  *   R6  NVFP4 per the chain in nvfp4_block().
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fopenmp -shared
@@ -341,13 +344,29 @@ float orc_silu32(float g)
     return g * s;
 }
 
+/* d/dg of the SiLU above: sigma(g) + g * sigma(g)(1 - sigma(g)); the second
+ * term is 0 when sigma(1 - sigma) is 0 (as for dGELU). */
+float orc_dsilu32(float g)
+{
+    float s, sc;
+    sigmoid_pair(g, &s, &sc);
+    float ss = s * sc;
+    float t = (ss == 0.0f) ? 0.0f : g * ss;
+    return s + t;
+}
+
 static float f32_of_bf16(uint16_t b) { return (float)orc_bf16_value(b); }
 
 /* The fused elementwise value y (as bf16 bits) for one input element.
- * pre: 0 none, 1 GELU(x), 2 dGELU(x) * grad. */
+ * pre: 0 none, 1 GELU(x), 2 dGELU(x) * grad, 3 dSiLU(x) * grad. */
 uint16_t orc_preop(int pre, uint16_t x, uint16_t grad)
 {
     switch (pre) {
+    case 3: {
+        float d = orc_dsilu32(f32_of_bf16(x));
+        float y = d * f32_of_bf16(grad);
+        return orc_bf16_round(y);
+    }
     case 0:
         return x;
     case 1:
@@ -375,6 +394,32 @@ uint16_t orc_gated(int act, uint16_t gate, uint16_t lin)
         return 0x7FC0;
     float y = a * l;
     return orc_bf16_round(y);
+}
+
+/* Gated backward for one element pair: with a = act(gate), da = act'(gate)
+ * (act 1 SiLU, 2 GELU), the gradients of the two input halves are
+ *   d_gate = fl32(fl32(da * grad) * linear),   d_lin = fl32(a * grad),
+ * each rounded once to bf16. */
+int orc_gated_bwd(int act, uint16_t gate, uint16_t lin, uint16_t grad, uint16_t *d_gate,
+                  uint16_t *d_lin)
+{
+    float g = f32_of_bf16(gate), l = f32_of_bf16(lin), dy = f32_of_bf16(grad);
+    float a, da;
+    if (act == 1) {
+        a = orc_silu32(g);
+        da = orc_dsilu32(g);
+    } else if (act == 2) {
+        a = orc_gelu32(g);
+        da = orc_dgelu32(g);
+    } else {
+        return ORC_ERR_ENUM;
+    }
+    float t = da * dy;
+    float yg = t * l;
+    float yl = a * dy;
+    *d_gate = orc_bf16_round(yg);
+    *d_lin = orc_bf16_round(yl);
+    return ORC_OK;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -425,7 +470,7 @@ static void column_sums(const uint16_t *y, int64_t M, int64_t K, float *dbias)
     }
 }
 
-/* fusion: low nibble = pre-op (0 none, 1 GELU, 2 dGELU), bit 0x10 = dbias.
+/* fusion: low nibble = pre-op (0 none, 1 GELU, 2 dGELU, 3 dSiLU), bit 0x10 = dbias.
  * y_out (optional, [M][K]) receives the fused bf16 tensor. */
 int orc_mx_quantize(const uint16_t *x, const uint16_t *grad, int64_t M, int64_t K,
                     unsigned axis, int fusion, uint8_t *q_row, uint8_t *s_row,
@@ -434,7 +479,7 @@ int orc_mx_quantize(const uint16_t *x, const uint16_t *grad, int64_t M, int64_t 
     int pre = fusion & 0xF;
     if (M <= 0 || K <= 0 || M % 32 || K % 32)
         return ORC_ERR_SHAPE;
-    if (pre > 2 || (fusion & ~0x1F) || (axis & ~3u))
+    if (pre > 3 || (fusion & ~0x1F) || (axis & ~3u))
         return ORC_ERR_ENUM;
     init_tables();
     const uint16_t *y = x;
@@ -476,6 +521,31 @@ int orc_mx_quantize_gated(const uint16_t *x, int64_t M, int64_t N, unsigned axis
         for (int64_t n = 0; n < N; n++)
             y[m * N + n] = orc_gated(act, x[m * 2 * N + n], x[m * 2 * N + N + n]);
     mx_tensor(y, M, N, axis, q_row, s_row, q_col, s_col);
+    if (y != y_out)
+        free(y);
+    return ORC_OK;
+}
+
+/* Gated backward cast: grad[M][N], x[M][2N] = [gate | linear]; the tensor
+ * quantised is dx[M][2N] = [d_gate | d_lin] (orc_gated_bwd per element). */
+int orc_mx_quantize_dgated(const uint16_t *grad, const uint16_t *x, int64_t M, int64_t N,
+                           unsigned axis, int act, uint8_t *q_row, uint8_t *s_row,
+                           uint8_t *q_col, uint8_t *s_col, uint16_t *y_out)
+{
+    if (M <= 0 || N <= 0 || M % 32 || N % 32)
+        return ORC_ERR_SHAPE;
+    if ((act != 1 && act != 2) || (axis & ~3u))
+        return ORC_ERR_ENUM;
+    init_tables();
+    uint16_t *y = y_out ? y_out : (uint16_t *)malloc((size_t)(M * 2 * N) * 2);
+    if (!y)
+        return ORC_ERR_NOMEM;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t n = 0; n < N; n++)
+            orc_gated_bwd(act, x[m * 2 * N + n], x[m * 2 * N + N + n], grad[m * N + n],
+                          &y[m * 2 * N + n], &y[m * 2 * N + N + n]);
+    mx_tensor(y, M, 2 * N, axis, q_row, s_row, q_col, s_col);
     if (y != y_out)
         free(y);
     return ORC_OK;
@@ -608,14 +678,14 @@ void orc_bf16_round_array(const double *v, uint16_t *out, int64_t n)
         out[i] = orc_bf16_round(v[i]);
 }
 
-/* which: 0 exp32, 1 gelu32, 2 dgelu32, 3 silu32 */
+/* which: 0 exp32, 1 gelu32, 2 dgelu32, 3 silu32, 4 dsilu32 */
 void orc_unary32_array(int which, const float *v, float *out, int64_t n)
 {
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; i++) {
         float a = v[i];
         out[i] = which == 0 ? orc_exp32(a) : which == 1 ? orc_gelu32(a)
-               : which == 2 ? orc_dgelu32(a) : orc_silu32(a);
+               : which == 2 ? orc_dgelu32(a) : which == 3 ? orc_silu32(a) : orc_dsilu32(a);
     }
 }
 

@@ -191,3 +191,83 @@ def test_fused_tensor_equals_plain_cast_of_fused_values():
         # y[m][n] = act(x[m][n]) * x[m][N + n]
         m, n = 5, 17
         assert f["y"][m, n] == O.gated(act, int(xg[m, n]), int(xg[m, 64 + n]))
+
+
+def dsilu64(x):
+    """d/dx x sigma(x) = sigma(x) (1 + x (1 - sigma(x))), with sigma and
+    1 - sigma from e^-|x| (no overflow, no cancellation)."""
+    x = np.asarray(x, np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        e = np.exp(-np.abs(x))
+        s = np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+        sc = np.where(x >= 0, e / (1.0 + e), 1.0 / (1.0 + e))
+        d = s * (1.0 + x * sc)
+    return np.where(np.isfinite(d), d, np.where(x > 0, 1.0, 0.0))
+
+
+def test_dsilu_closed_form_is_the_derivative_of_silu():
+    x = np.linspace(-12, 12, 4801)
+    h = 1e-6
+    fd = (silu64(x + h) - silu64(x - h)) / (2 * h)
+    assert np.max(np.abs(fd - dsilu64(x))) < 1e-8
+
+
+def test_dsilu32_against_closed_form():
+    x = all_finite_bf16_f32()
+    got = O.unary32("dsilu", x).astype(np.float64)
+    want = dsilu64(x)
+    err = np.abs(got - want)
+    # silu' has a zero near x = -1.28 where sigma and x sigma (1 - sigma)
+    # cancel, hence the absolute term (a few ulps of 1)
+    tol = (8.0 + 2.0 * np.abs(x)) * ulp32(want) + 16 * 2.0 ** -24
+    assert np.all(err <= tol), (x[err > tol][:5], got[err > tol][:5], want[err > tol][:5])
+    away = np.abs(want) > 0.05
+    with np.errstate(over="ignore"):
+        assert np.all(err[away] <= (8.0 + 2.0 * np.abs(x[away])) * ulp32(want[away]) * 4)
+    d = O.unary32("dsilu", [0.0, 1e30, -1e30, 3e38])
+    assert list(d) == [0.5, 1.0, 0.0, 1.0]
+
+
+def test_dsilu_preop_and_gated_backward_compositions():
+    rng = np.random.default_rng(22)
+    v = W.bf16_bits(rng.standard_normal(1500).astype(np.float32) * 3)
+    one = 0x3F80
+    for i in range(500):
+        gate, lin, dy = int(v[i]), int(v[500 + i]), int(v[1000 + i])
+        gf, lf = O.bf16_value(gate), O.bf16_value(lin)
+        ds = float(O.unary32("dsilu", [gf])[0])
+        dg = float(O.unary32("dgelu", [gf])[0])
+        # single-input dSiLU: grad = 1 leaves dsilu(x)
+        assert O.preop(O.FUSE_DSILU, gate, one) == O.bf16_round(ds)
+        for act, da, pre in ((O.GATED_SWIGLU, ds, O.FUSE_DSILU), (O.GATED_GEGLU, dg, O.FUSE_DGELU)):
+            d_gate, d_lin = O.gated_bwd(act, gate, lin, dy)
+            # d_lin = act(gate) * grad is the forward gated value with linear := grad
+            assert d_lin == O.gated(act, gate, dy)
+            # linear = 1: d_gate = act'(gate) * grad, the single-input backward
+            assert O.gated_bwd(act, gate, one, dy)[0] == O.preop(pre, gate, dy)
+            # grad = 1: d_gate = fl32(act'(gate) * linear), one fp32 rounding
+            want = np.float32(np.float32(da) * np.float32(lf))
+            assert O.gated_bwd(act, gate, lin, one)[0] == O.bf16_round(float(want))
+            # gate = 0: act(0) = 0, so d_lin = +-0
+            assert O.bf16_value(O.gated_bwd(act, 0, lin, dy)[1]) == 0.0
+
+
+def test_backward_tensors_equal_plain_cast_of_their_values():
+    x, g = W.make("c3_gelu_dbias_8192", 64, 64)
+    f = O.mx_quantize(x, grad=g, fusion=O.FUSE_DSILU | O.FUSE_DBIAS, want_y=True)
+    p = O.mx_quantize(f["y"])
+    for k in ("q_row", "s_row", "q_col", "s_col"):
+        assert np.array_equal(f[k], p[k])
+    assert f["y"][3, 7] == O.preop(O.FUSE_DSILU, int(x[3, 7]), int(g[3, 7]))
+    xg = W.make("c4_gated_8192", 64, 128)
+    dy = W.normal(64, 64, seed=9)
+    for act in (O.GATED_SWIGLU, O.GATED_GEGLU):
+        f = O.mx_quantize_dgated(dy, xg, act, want_y=True)
+        p = O.mx_quantize(f["y"])
+        for k in ("q_row", "s_row", "q_col", "s_col"):
+            assert np.array_equal(f[k], p[k])
+        assert f["q_row"].shape == (64, 128) and f["s_col"].shape == (128, 2)
+        # dx[m][n] = d_gate, dx[m][N + n] = d_lin of element pair n
+        m, n = 5, 17
+        d_gate, d_lin = O.gated_bwd(act, int(xg[m, n]), int(xg[m, 64 + n]), int(dy[m, n]))
+        assert f["y"][m, n] == d_gate and f["y"][m, 64 + n] == d_lin

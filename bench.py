@@ -58,6 +58,9 @@ CONFIGS = {
     "mxfp8_swiglu_8192": ("c4_gated_8192", (8192, 8192), "gated_swiglu", 3),
     "mxfp8_geglu_8192": ("c4_gated_8192", (8192, 8192), "gated_geglu", 3),
     "nvfp4_16384": ("c5_nvfp4_16384", (16384, 16384), "nvfp4", 3),
+    "mxfp8_dsilu_dbias_8192": ("f1_dsilu_dbias_8192", (8192, 8192), "mx_dsilu", 3),
+    "mxfp8_dswiglu_8192": ("f1_dgated_8192", (8192, 4096), "dgated_swiglu", 3),
+    "mxfp8_dgeglu_8192": ("f1_dgated_8192", (8192, 4096), "dgated_geglu", 3),
 }
 
 
@@ -129,8 +132,10 @@ def main():
     key, (M, K), kind, dirs = CONFIGS[args.config]
     print(f"[bench] generating {args.config} inputs {M}x{K}", file=sys.stderr, flush=True)
     inputs = W.make(key)
-    if kind == "mx_gelu" or kind == "mx_dgelu":
+    if kind in ("mx_gelu", "mx_dgelu", "mx_dsilu"):
         x_h, g_h = inputs
+    elif kind.startswith("dgated"):
+        g_h, x_h = inputs
     else:
         x_h, g_h = inputs, None
     to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
@@ -145,6 +150,15 @@ def main():
         alg_bytes = nvfp4_bytes(M, K, 2)
         desc = dict(workload=args.config, M=M, K=K, block=16, directions="row+transpose",
                     format="nvfp4 (e2m1 + e4m3 scales + fp32 tensor scale)")
+    elif kind.startswith("dgated"):
+        act = mx.GATED_SWIGLU if kind.endswith("swiglu") else mx.GATED_GEGLU
+        out = mx.mx_quantize_dgated(grad, x, act)
+        step = lambda: mx.mx_quantize_dgated(grad, x, act, out=out)
+        N = K
+        alg_bytes = 2 * M * N + 4 * M * N + 2 * (2 * M * N + 2 * M * N // 32)
+        desc = dict(workload=args.config, M=M, N=N, block=32, directions="row+col",
+                    format="mxfp8 e4m3 + e8m0", activation="d" + kind.split("_")[1],
+                    output="[d_gate | d_linear] M x 2N")
     elif kind.startswith("gated"):
         act = mx.GATED_SWIGLU if kind.endswith("swiglu") else mx.GATED_GEGLU
         out = mx.mx_quantize_gated(x, act)
@@ -156,18 +170,20 @@ def main():
     else:
         axis = mx.COLWISE if dirs == 2 else mx.ROWWISE | mx.COLWISE
         fusion = {"mx": mx.FUSE_NONE, "mx_gelu": mx.FUSE_GELU | mx.FUSE_DBIAS,
-                  "mx_dgelu": mx.FUSE_DGELU | mx.FUSE_DBIAS}[kind]
+                  "mx_dgelu": mx.FUSE_DGELU | mx.FUSE_DBIAS,
+                  "mx_dsilu": mx.FUSE_DSILU | mx.FUSE_DBIAS}[kind]
         ws = torch.empty(max(16, mx.mx_quantize_workspace_size(M, K, axis, fusion)),
                          dtype=torch.uint8, device=dev)
         out = mx.mx_quantize(x, grad, axis=axis, fusion=fusion, workspace=ws)
         step = lambda: mx.mx_quantize(x, grad, axis=axis, fusion=fusion, out=out, workspace=ws)
         ndir = 1 if dirs == 2 else 2
-        alg_bytes = mx_bytes(M, K, ndir, extra_inputs=1 if kind == "mx_dgelu" else 0)
+        alg_bytes = mx_bytes(M, K, ndir, extra_inputs=1 if kind in ("mx_dgelu", "mx_dsilu") else 0)
         if fusion & mx.FUSE_DBIAS:
             alg_bytes += 4 * K
         desc = dict(workload=args.config, M=M, K=K, block=32,
                     directions="col" if ndir == 1 else "row+col", format="mxfp8 e4m3 + e8m0",
-                    fusion={"mx": "none", "mx_gelu": "gelu+dbias", "mx_dgelu": "dgelu+dbias"}[kind])
+                    fusion={"mx": "none", "mx_gelu": "gelu+dbias", "mx_dgelu": "dgelu+dbias",
+                            "mx_dsilu": "dsilu+dbias"}[kind])
 
     stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):
@@ -242,13 +258,17 @@ def main():
         if kind == "nvfp4":
             O.nvfp4_quantize_transpose(xs, tensor_amax=O.absmax(x_h))
             sb = nvfp4_bytes(rows, K, 2)
+        elif kind.startswith("dgated"):
+            O.mx_quantize_dgated(np.ascontiguousarray(g_h[:rows]), xs,
+                                 mx.GATED_SWIGLU if kind.endswith("swiglu") else mx.GATED_GEGLU)
+            sb = 6 * rows * K + 2 * (2 * rows * K + 2 * rows * K // 32)
         elif kind.startswith("gated"):
             O.mx_quantize_gated(xs, mx.GATED_SWIGLU if kind.endswith("swiglu") else mx.GATED_GEGLU)
             sb = 2 * rows * K + 2 * (rows * (K // 2) + rows * (K // 2) // 32)
         else:
             gs = np.ascontiguousarray(g_h[:rows]) if g_h is not None else None
             O.mx_quantize(xs, grad=gs, axis=axis, fusion=fusion)
-            sb = mx_bytes(rows, K, ndir, extra_inputs=1 if kind == "mx_dgelu" else 0)
+            sb = mx_bytes(rows, K, ndir, extra_inputs=1 if kind in ("mx_dgelu", "mx_dsilu") else 0)
         dt = time.perf_counter() - t0
         cpu_s = time.process_time() - c0
         result["cpu_baseline"] = {"value": round(sb / (dt * 1e9), 3), "unit": "GB/s",

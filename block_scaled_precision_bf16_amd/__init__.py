@@ -23,13 +23,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmxcast.so")
 
 ROWWISE, COLWISE = 1, 2
-FUSE_NONE, FUSE_GELU, FUSE_DGELU, FUSE_DBIAS = 0, 1, 2, 0x10
+FUSE_NONE, FUSE_GELU, FUSE_DGELU, FUSE_DSILU, FUSE_DBIAS = 0, 1, 2, 3, 0x10
 GATED_SWIGLU, GATED_GEGLU = 1, 2
-OP_GATED = 0x100
+OP_GATED, OP_DGATED = 0x100, 0x200
 (MX_OK, MX_ERR_NULL, MX_ERR_ENUM, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_WORKSPACE,
  MX_ERR_ALIAS, MX_ERR_HIP, MX_ERR_UNSUPPORTED) = range(9)
 
-EXPORTS = ("mx_quantize", "mx_quantize_workspace_size", "mx_quantize_gated", "mx_fused_values",
+EXPORTS = ("mx_quantize", "mx_quantize_workspace_size", "mx_quantize_gated",
+           "mx_quantize_dgated", "mx_fused_values",
            "mx_absmax_bf16", "nvfp4_quantize_transpose", "mx_status_str", "mx_abi_version")
 
 
@@ -60,6 +61,9 @@ def lib():
         L.mx_quantize_gated.restype = ctypes.c_int
         L.mx_quantize_gated.argtypes = [_vp, _i64, _i64, ctypes.c_uint, ctypes.c_int,
                                         _vp, _vp, _vp, _vp, _vp]
+        L.mx_quantize_dgated.restype = ctypes.c_int
+        L.mx_quantize_dgated.argtypes = [_vp, _vp, _i64, _i64, ctypes.c_uint, ctypes.c_int,
+                                         _vp, _vp, _vp, _vp, _vp]
         L.mx_fused_values.restype = ctypes.c_int
         L.mx_fused_values.argtypes = [_vp, _vp, _i64, _i64, ctypes.c_int, _vp, _vp]
         L.mx_absmax_bf16.restype = ctypes.c_int
@@ -122,7 +126,7 @@ def mx_quantize(x, grad=None, axis=ROWWISE | COLWISE, fusion=FUSE_NONE, out=None
     (None where not requested).  `out` may hold preallocated outputs and
     `workspace` a preallocated uint8 buffer (needed only with FUSE_DBIAS)."""
     x = _bf16_bits(x)
-    grad = _bf16_bits(grad) if (fusion & 0xF) == FUSE_DGELU else None
+    grad = _bf16_bits(grad) if (fusion & 0xF) in (FUSE_DGELU, FUSE_DSILU) else None
     M, K = x.shape
     dev = x.device
     o = dict(out or {})
@@ -168,15 +172,40 @@ def mx_quantize_gated(x, act, axis=ROWWISE | COLWISE, out=None, stream=None):
     return {k: o.get(k) for k in ("q_row", "s_row", "q_col", "s_col")}
 
 
-def mx_fused_values(x, grad=None, op=FUSE_GELU, out=None, stream=None):
-    """The bf16 values the fused casts quantise (returned as int16 bits)."""
+def mx_quantize_dgated(grad, x, act, axis=ROWWISE | COLWISE, out=None, stream=None):
+    """Gated backward MXFP8 cast: grad[M][N], x[M][2N] = [gate | linear] ->
+    quantised dx[M][2N] = [d_gate | d_linear]."""
+    grad = _bf16_bits(grad)
     x = _bf16_bits(x)
-    gated = bool(op & OP_GATED)
+    M, N2 = x.shape
+    N = N2 // 2
+    dev = x.device
+    o = dict(out or {})
+    if axis & ROWWISE:
+        o.setdefault("q_row", _u8((M, N2), dev))
+        o.setdefault("s_row", _u8((M, N2 // 32), dev))
+    if axis & COLWISE:
+        o.setdefault("q_col", _u8((N2, M), dev))
+        o.setdefault("s_col", _u8((N2, M // 32), dev))
+    st = lib().mx_quantize_dgated(_ptr(grad), _ptr(x), M, N, axis, act, _ptr(o.get("q_row")),
+                                  _ptr(o.get("s_row")), _ptr(o.get("q_col")),
+                                  _ptr(o.get("s_col")), _stream(dev, stream))
+    _check(st, "mx_quantize_dgated")
+    return {k: o.get(k) for k in ("q_row", "s_row", "q_col", "s_col")}
+
+
+def mx_fused_values(x, grad=None, op=FUSE_GELU, out=None, stream=None):
+    """The bf16 values the fused casts quantise (returned as int16 bits).
+    Gated ops (OP_GATED | act) take x[M][2K] and give [M][K]; gated backward
+    ops (OP_DGATED | act) take x[M][2K] and grad[M][K] and give [M][2K]."""
+    x = _bf16_bits(x)
+    gated = bool(op & (OP_GATED | OP_DGATED))
     M, W = x.shape
     K = W // 2 if gated else W
     dev = x.device
-    y = out if out is not None else torch.empty((M, K), dtype=torch.int16, device=dev)
-    g = _bf16_bits(grad) if op == FUSE_DGELU else None
+    shape = (M, 2 * K) if op & OP_DGATED else (M, K)
+    y = out if out is not None else torch.empty(shape, dtype=torch.int16, device=dev)
+    g = _bf16_bits(grad) if (op in (FUSE_DGELU, FUSE_DSILU) or op & OP_DGATED) else None
     st = lib().mx_fused_values(_ptr(x), _ptr(g), M, K, op, _ptr(y), _stream(dev, stream))
     _check(st, "mx_fused_values")
     return y

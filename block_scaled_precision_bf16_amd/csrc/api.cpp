@@ -113,15 +113,16 @@ mx_status mx_quantize(const void *x, const void *grad, int64_t M, int64_t K, uns
 {
     const int pre = fusion & 0xF;
     const bool want_dbias = (fusion & MX_FUSE_DBIAS) != 0;
-    if (axis_mask == 0 || (axis_mask & ~3u) || (fusion & ~0x1F) || pre > MX_FUSE_DGELU)
+    if (axis_mask == 0 || (axis_mask & ~3u) || (fusion & ~0x1F) || pre > MX_FUSE_DSILU)
         return MX_ERR_ENUM;
+    const bool has_grad = pre == MX_FUSE_DGELU || pre == MX_FUSE_DSILU;
     const bool row = axis_mask & MX_ROWWISE, col = axis_mask & MX_COLWISE;
-    if (!x || (pre == MX_FUSE_DGELU && !grad) || (row && (!q_row || !s_row)) ||
+    if (!x || (has_grad && !grad) || (row && (!q_row || !s_row)) ||
         (col && (!q_col || !s_col)) || (want_dbias && !dbias))
         return MX_ERR_NULL;
     if (!shape_ok(M, K, 32))
         return MX_ERR_SHAPE;
-    if (!aligned(x, 16) || (pre == MX_FUSE_DGELU && !aligned(grad, 16)) ||
+    if (!aligned(x, 16) || (has_grad && !aligned(grad, 16)) ||
         (row && (!aligned(q_row, 16) || !aligned(s_row, 16))) ||
         (col && (!aligned(q_col, 16) || !aligned(s_col, 16))) ||
         (want_dbias && (!aligned(dbias, 4) || (workspace && !aligned(workspace, 16)))))
@@ -130,7 +131,7 @@ mx_status mx_quantize(const void *x, const void *grad, int64_t M, int64_t K, uns
     if (want_dbias && (!workspace || workspace_bytes < need))
         return MX_ERR_WORKSPACE;
     const uint64_t n = (uint64_t)(M * K);
-    const Span in[2] = {{x, 2 * n}, {pre == MX_FUSE_DGELU ? grad : nullptr, 2 * n}};
+    const Span in[2] = {{x, 2 * n}, {has_grad ? grad : nullptr, 2 * n}};
     const Span out[6] = {{row ? q_row : nullptr, n}, {row ? s_row : nullptr, n / 32},
                          {col ? q_col : nullptr, n}, {col ? s_col : nullptr, n / 32},
                          {want_dbias ? dbias : nullptr, 4 * (uint64_t)K},
@@ -140,10 +141,11 @@ mx_status mx_quantize(const void *x, const void *grad, int64_t M, int64_t K, uns
 
     mxk::MxArgs a;
     a.x = static_cast<const uint16_t *>(x);
-    a.aux = static_cast<const uint16_t *>(grad);
+    a.aux = has_grad ? static_cast<const uint16_t *>(grad) : nullptr;
     a.M = M;
     a.K = K;
     a.ldx = K;
+    a.ldg = K;
     a.lin_off = 0;
     a.q_row = q_row;
     a.s_row = s_row;
@@ -151,7 +153,9 @@ mx_status mx_quantize(const void *x, const void *grad, int64_t M, int64_t K, uns
     a.s_col = s_col;
     a.partials = want_dbias ? static_cast<float *>(workspace) : nullptr;
     set_walk(a);
-    mx_status st = from_hip(mxk::launch_mx_cast(pre, axis_mask, want_dbias, a, stream));
+    const int op = pre == MX_FUSE_GELU ? mxk::OP_GELU : pre == MX_FUSE_DGELU ? mxk::OP_DGELU
+                 : pre == MX_FUSE_DSILU ? mxk::OP_DSILU : mxk::OP_PLAIN;
+    mx_status st = from_hip(mxk::launch_mx_cast(op, axis_mask, want_dbias, a, stream));
     if (st != MX_OK || !want_dbias)
         return st;
     return from_hip(mxk::launch_dbias_reduce(a.partials, a.groups_m, K, dbias, stream));
@@ -184,6 +188,7 @@ mx_status mx_quantize_gated(const void *x, int64_t M, int64_t N, unsigned axis_m
     a.M = M;
     a.K = N;
     a.ldx = 2 * N;
+    a.ldg = 0;
     a.lin_off = N;
     a.q_row = q_row;
     a.s_row = s_row;
@@ -192,6 +197,46 @@ mx_status mx_quantize_gated(const void *x, int64_t M, int64_t N, unsigned axis_m
     a.partials = nullptr;
     set_walk(a);
     const int op = act == MX_GATED_SWIGLU ? mxk::OP_SWIGLU : mxk::OP_GEGLU;
+    return from_hip(mxk::launch_mx_cast(op, axis_mask, false, a, stream));
+}
+
+mx_status mx_quantize_dgated(const void *grad, const void *x, int64_t M, int64_t N,
+                             unsigned axis_mask, int act, uint8_t *q_row, uint8_t *s_row,
+                             uint8_t *q_col, uint8_t *s_col, hipStream_t stream)
+{
+    if (axis_mask == 0 || (axis_mask & ~3u) || (act != MX_GATED_SWIGLU && act != MX_GATED_GEGLU))
+        return MX_ERR_ENUM;
+    const bool row = axis_mask & MX_ROWWISE, col = axis_mask & MX_COLWISE;
+    if (!grad || !x || (row && (!q_row || !s_row)) || (col && (!q_col || !s_col)))
+        return MX_ERR_NULL;
+    if (!shape_ok(M, N, 32) || !shape_ok(M, 2 * N, 32))
+        return MX_ERR_SHAPE;
+    if (!aligned(grad, 16) || !aligned(x, 16) ||
+        (row && (!aligned(q_row, 16) || !aligned(s_row, 16))) ||
+        (col && (!aligned(q_col, 16) || !aligned(s_col, 16))))
+        return MX_ERR_ALIGN;
+    const uint64_t n = (uint64_t)(M * N);
+    const Span in[2] = {{grad, 2 * n}, {x, 4 * n}};
+    const Span out[4] = {{row ? q_row : nullptr, 2 * n}, {row ? s_row : nullptr, n / 16},
+                         {col ? q_col : nullptr, 2 * n}, {col ? s_col : nullptr, n / 16}};
+    if (any_alias(in, 2, out, 4))
+        return MX_ERR_ALIAS;
+
+    mxk::MxArgs a;
+    a.x = static_cast<const uint16_t *>(x);
+    a.aux = static_cast<const uint16_t *>(grad);
+    a.M = M;
+    a.K = 2 * N;
+    a.ldx = 2 * N;
+    a.ldg = N;
+    a.lin_off = N;
+    a.q_row = q_row;
+    a.s_row = s_row;
+    a.q_col = q_col;
+    a.s_col = s_col;
+    a.partials = nullptr;
+    set_walk(a);
+    const int op = act == MX_GATED_SWIGLU ? mxk::OP_DSWIGLU : mxk::OP_DGEGLU;
     return from_hip(mxk::launch_mx_cast(op, axis_mask, false, a, stream));
 }
 
@@ -204,18 +249,23 @@ mx_status mx_fused_values(const void *x, const void *grad, int64_t M, int64_t K,
     case MX_FUSE_DGELU: kop = mxk::OP_DGELU; break;
     case MX_OP_GATED | MX_GATED_SWIGLU: kop = mxk::OP_SWIGLU; break;
     case MX_OP_GATED | MX_GATED_GEGLU: kop = mxk::OP_GEGLU; break;
+    case MX_FUSE_DSILU: kop = mxk::OP_DSILU; break;
+    case MX_OP_DGATED | MX_GATED_SWIGLU: kop = mxk::OP_DSWIGLU; break;
+    case MX_OP_DGATED | MX_GATED_GEGLU: kop = mxk::OP_DGEGLU; break;
     default: return MX_ERR_ENUM;
     }
-    const bool gated = (op & MX_OP_GATED) != 0;
-    if (!x || !y || (kop == mxk::OP_DGELU && !grad))
+    const bool gated = (op & (MX_OP_GATED | MX_OP_DGATED)) != 0;
+    const bool dgated = (op & MX_OP_DGATED) != 0;
+    const bool has_grad = kop == mxk::OP_DGELU || kop == mxk::OP_DSILU || dgated;
+    if (!x || !y || (has_grad && !grad))
         return MX_ERR_NULL;
     if (!shape_ok(M, K, 32) || (gated && !shape_ok(M, 2 * K, 32)))
         return MX_ERR_SHAPE;
-    if (!aligned(x, 16) || !aligned(y, 16) || (kop == mxk::OP_DGELU && !aligned(grad, 16)))
+    if (!aligned(x, 16) || !aligned(y, 16) || (has_grad && !aligned(grad, 16)))
         return MX_ERR_ALIGN;
     const uint64_t n = (uint64_t)(M * K);
-    const Span in[2] = {{x, gated ? 4 * n : 2 * n}, {kop == mxk::OP_DGELU ? grad : nullptr, 2 * n}};
-    const Span out[1] = {{y, 2 * n}};
+    const Span in[2] = {{x, gated ? 4 * n : 2 * n}, {has_grad ? grad : nullptr, 2 * n}};
+    const Span out[1] = {{y, dgated ? 4 * n : 2 * n}};
     if (any_alias(in, 2, out, 1))
         return MX_ERR_ALIAS;
     return from_hip(mxk::launch_fused_values(kop, static_cast<const uint16_t *>(x),

@@ -267,6 +267,48 @@ __device__ __forceinline__ float silu32(float g)
     return g * s;
 }
 
+// d/dg of silu32's function: sigma + g sigma (1 - sigma); the second term is
+// 0 when sigma(1 - sigma) is 0.
+__device__ __forceinline__ float dsilu32(float g)
+{
+    float s, sc;
+    sigmoid_pair(g, s, sc);
+    float ss = s * sc;
+    float t = ss == 0.0f ? 0.0f : g * ss;
+    return s + t;
+}
+
+// Gated backward of one element pair: with a = act(gate), da = act'(gate)
+// (SiLU for OP_DSWIGLU, GELU for OP_DGEGLU; one shared logistic evaluation,
+// the same values as silu32/dsilu32 or gelu32/dgelu32), d_gate =
+// (da * grad) * linear and d_linear = a * grad.
+template <int OP>
+__device__ __forceinline__ float dgated_value(float gate, float grad, float lin, bool gate_half)
+{
+    float s, sc, a, da;
+    if constexpr (OP == OP_DSWIGLU) {
+        sigmoid_pair(gate, s, sc);
+        a = gate * s;
+        float ss = s * sc;
+        da = s + (ss == 0.0f ? 0.0f : gate * ss);
+    } else {
+        float x2 = gate * gate;
+        float x3 = x2 * gate;
+        float inner = __builtin_fmaf(K_CUBIC, x3, gate);
+        float u = K_SQRT_2_OVER_PI * inner;
+        sigmoid_pair(u + u, s, sc);
+        a = gate * s;
+        float ss = s * sc;
+        float du = K_2SQRT_2_OVER_PI * __builtin_fmaf(K_CUBIC3, x2, 1.0f);
+        da = s + (ss == 0.0f ? 0.0f : (gate * ss) * du);
+    }
+    if (gate_half) {
+        float t = da * grad;
+        return t * lin;
+    }
+    return a * grad;
+}
+
 // y (fp32, before the bf16 rounding) for one element.  a = x (or gate),
 // b = grad (or linear).
 template <int OP>
@@ -278,6 +320,8 @@ __device__ __forceinline__ float fused_value(float a, float b)
         return dgelu32(a) * b;
     else if constexpr (OP == OP_SWIGLU)
         return silu32(a) * b;
+    else if constexpr (OP == OP_DSILU)
+        return dsilu32(a) * b;
     else
         return gelu32(a) * b;
 }
@@ -289,6 +333,14 @@ __device__ __forceinline__ uint32_t fused_pair(uint32_t a, uint32_t b)
 {
     return bf16x2_rne(fused_value<OP>(bf16_lo(a), bf16_lo(b)),
                       fused_value<OP>(bf16_hi(a), bf16_hi(b)));
+}
+
+// Gated backward of packed pairs (gate, grad, linear words), rounded to bf16.
+template <int OP>
+__device__ __forceinline__ uint32_t dgated_pair(uint32_t g, uint32_t dy, uint32_t l, bool gate_half)
+{
+    return bf16x2_rne(dgated_value<OP>(bf16_lo(g), bf16_lo(dy), bf16_lo(l), gate_half),
+                      dgated_value<OP>(bf16_hi(g), bf16_hi(dy), bf16_hi(l), gate_half));
 }
 
 // ---------------------------------------------------------------------------

@@ -8,7 +8,11 @@
 namespace mxk {
 
 // Elementwise pre-op of a cast kernel.
-enum Op : int { OP_PLAIN = 0, OP_GELU = 1, OP_DGELU = 2, OP_SWIGLU = 3, OP_GEGLU = 4 };
+enum Op : int {
+    OP_PLAIN = 0, OP_GELU = 1, OP_DGELU = 2, OP_SWIGLU = 3, OP_GEGLU = 4,
+    OP_DSILU = 5,                    // dsilu(x) * grad
+    OP_DSWIGLU = 6, OP_DGEGLU = 7    // gated backward: [d_gate | d_linear]
+};
 
 // Workgroup tile of the cast kernels.  A lane owns 16 rows x 8 columns; the
 // two halves of a wave (lanes 0-31, 32-63) own rows 0-15 and 16-31 of the
@@ -41,6 +45,7 @@ struct MxArgs {
     int64_t M, K;          // rows and columns of the quantised tensor
     int64_t ldx;           // row stride of x in elements
     int64_t lin_off;       // gated: column offset of the linear half
+    int64_t ldg;           // row stride of aux (grad) in elements
     uint8_t *q_row, *s_row, *q_col, *s_col;
     float *partials;       // dbias: [groups_m][K] fp32 column partial sums
     int tiles_k, tiles_m;  // 128 x 256 sub-tiles along K and M
@@ -61,7 +66,8 @@ struct Nv4Args {
 hipError_t launch_mx_cast(int op, unsigned axis, bool dbias, const MxArgs &a, hipStream_t s);
 hipError_t launch_dbias_reduce(const float *partials, int segments, int64_t K, float *dbias,
                                hipStream_t s);
-// op as above (1..4); gated ops read x[M][2K].
+// op as above (1..7); gated ops read x[M][2K]; the gated backward ops read
+// grad aux[M][K] and write y[M][2K].
 hipError_t launch_fused_values(int op, const uint16_t *x, const uint16_t *aux, int64_t M,
                                int64_t K, uint16_t *y, hipStream_t s);
 hipError_t launch_absmax(const uint16_t *x, int64_t n, float *amax, hipStream_t s);

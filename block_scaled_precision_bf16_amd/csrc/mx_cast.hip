@@ -130,18 +130,50 @@ template <int OP, int XA>
 __device__ __forceinline__ void load_tile(const MxArgs &a, const LaneAt &l, int tm, int tk,
                                           uint32_t (&w)[kRowsPerLane][4])
 {
+    const bool live = lane_live(a, l, tm, tk);
+    if constexpr (OP == OP_DSWIGLU || OP == OP_DGEGLU) {
+        // output column k of [d_gate | d_linear] (each half N = lin_off wide)
+        // reads gate and grad at column n = k mod N, and, in the gate half,
+        // linear at N + n; a lane's 8 columns lie in one half (N % 32 == 0)
+        const int64_t N = a.lin_off;
+        const int64_t k = (int64_t)tk * kTileK + kColsPerLane * l.cl;
+        const bool gate_half = k < N;
+        const uint32_t n = (uint32_t)(gate_half ? k : k - N);
+        const int64_t m0 = (int64_t)tm * kTileM;
+        const rsrc_t rx = make_rsrc(a.x, 2 * m0 * a.ldx, 2 * a.M * a.ldx);
+        const rsrc_t rg = make_rsrc(a.aux, 2 * m0 * a.ldg, 2 * a.M * a.ldg);
+        const uint32_t sx = (uint32_t)(2 * a.ldx), sg = (uint32_t)(2 * a.ldg);
+        const uint32_t ox = live ? (uint32_t)l.row * sx + 2 * n : kDead;
+        const uint32_t og = live ? (uint32_t)l.row * sg + 2 * n : kDead;
+        const uint32_t ol = live && gate_half ? ox + (uint32_t)(2 * N) : kDead;
+#pragma unroll
+        for (int r = 0; r < kRowsPerLane; r++) {
+            const uint4 g = buf_load16<XA>(rx, ox + r * sx);
+            const uint4 dy = buf_load16<XA>(rg, og + r * sg);
+            const uint4 li = buf_load16<XA>(rx, ol + r * sx);
+            w[r][0] = dgated_pair<OP>(g.x, dy.x, li.x, gate_half);
+            w[r][1] = dgated_pair<OP>(g.y, dy.y, li.y, gate_half);
+            w[r][2] = dgated_pair<OP>(g.z, dy.z, li.z, gate_half);
+            w[r][3] = dgated_pair<OP>(g.w, dy.w, li.w, gate_half);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        return;
+    }
     const int64_t tile = (int64_t)tm * kTileM * a.ldx + (int64_t)tk * kTileK;   // elements
     const int64_t total = a.M * a.ldx;
     const rsrc_t rx = make_rsrc(a.x, 2 * tile, 2 * total);
     const uint32_t rs = (uint32_t)(2 * a.ldx);
-    const uint32_t off = lane_live(a, l, tm, tk)
-                             ? (uint32_t)l.row * rs + (uint32_t)(2 * kColsPerLane * l.cl)
-                             : kDead;
+    const uint32_t off = live ? (uint32_t)l.row * rs + (uint32_t)(2 * kColsPerLane * l.cl) : kDead;
     rsrc_t rb = rx;
-    if constexpr (OP == OP_DGELU)
-        rb = make_rsrc(a.aux, 2 * tile, 2 * total);
-    else if constexpr (OP == OP_SWIGLU || OP == OP_GEGLU)
+    uint32_t rbs = rs, boff = off;
+    if constexpr (OP == OP_DGELU || OP == OP_DSILU) {
+        const int64_t gtile = (int64_t)tm * kTileM * a.ldg + (int64_t)tk * kTileK;
+        rb = make_rsrc(a.aux, 2 * gtile, 2 * a.M * a.ldg);
+        rbs = (uint32_t)(2 * a.ldg);
+        boff = live ? (uint32_t)l.row * rbs + (uint32_t)(2 * kColsPerLane * l.cl) : kDead;
+    } else if constexpr (OP == OP_SWIGLU || OP == OP_GEGLU) {
         rb = make_rsrc(a.x, 2 * (tile + a.lin_off), 2 * total);
+    }
 #pragma unroll
     for (int r = 0; r < kRowsPerLane; r++) {
         const uint4 v = buf_load16<XA>(rx, off + r * rs);
@@ -150,7 +182,7 @@ __device__ __forceinline__ void load_tile(const MxArgs &a, const LaneAt &l, int 
         } else {
             uint4 b = v;   // GELU has no second operand
             if constexpr (OP != OP_GELU)
-                b = buf_load16<XA>(rb, off + r * rs);
+                b = buf_load16<XA>(rb, boff + r * rbs);
             w[r][0] = fused_pair<OP>(v.x, b.x);
             w[r][1] = fused_pair<OP>(v.y, b.y);
             w[r][2] = fused_pair<OP>(v.z, b.z);
@@ -455,25 +487,40 @@ __global__ __launch_bounds__(256) void dbias_reduce_kernel(const float *partials
 }
 
 // y = fused value of each element; 8 elements per thread.  Gated ops read
-// the row [gate | linear] of width 2K.
+// the row [gate | linear] of width 2K; the gated backward ops read that row
+// and grad[M][K] and write the row [d_gate | d_linear] of y[M][2K].
 template <int OP>
 __global__ __launch_bounds__(256) void fused_values_kernel(const uint16_t *x, const uint16_t *aux,
                                                            int64_t M, int64_t K, uint16_t *y)
 {
+    constexpr bool dgated = OP == OP_DSWIGLU || OP == OP_DGEGLU;
+    const int64_t W = dgated ? 2 * K : K;                  // width of y
     const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
-    if (i >= M * K)
+    if (i >= M * W)
         return;
-    const int64_t row = i / K, col = i - row * K;
-    const bool gated = OP == OP_SWIGLU || OP == OP_GEGLU;
-    const uint16_t *pa = gated ? x + row * 2 * K + col : x + i;
-    const uint16_t *pb = gated ? pa + K : aux + i;
-    const uint4 va = *reinterpret_cast<const uint4 *>(pa);
-    const uint4 vb = *reinterpret_cast<const uint4 *>(pb);
+    const int64_t row = i / W, col = i - row * W;
     uint4 o;
-    o.x = fused_pair<OP>(va.x, vb.x);
-    o.y = fused_pair<OP>(va.y, vb.y);
-    o.z = fused_pair<OP>(va.z, vb.z);
-    o.w = fused_pair<OP>(va.w, vb.w);
+    if constexpr (dgated) {
+        const bool gate_half = col < K;
+        const int64_t n = gate_half ? col : col - K;
+        const uint4 g = *reinterpret_cast<const uint4 *>(x + row * 2 * K + n);
+        const uint4 dy = *reinterpret_cast<const uint4 *>(aux + row * K + n);
+        const uint4 li = *reinterpret_cast<const uint4 *>(x + row * 2 * K + K + n);
+        o.x = dgated_pair<OP>(g.x, dy.x, li.x, gate_half);
+        o.y = dgated_pair<OP>(g.y, dy.y, li.y, gate_half);
+        o.z = dgated_pair<OP>(g.z, dy.z, li.z, gate_half);
+        o.w = dgated_pair<OP>(g.w, dy.w, li.w, gate_half);
+    } else {
+        const bool gated = OP == OP_SWIGLU || OP == OP_GEGLU;
+        const uint16_t *pa = gated ? x + row * 2 * K + col : x + i;
+        const uint16_t *pb = gated ? pa + K : aux + i;
+        const uint4 va = *reinterpret_cast<const uint4 *>(pa);
+        const uint4 vb = *reinterpret_cast<const uint4 *>(pb);
+        o.x = fused_pair<OP>(va.x, vb.x);
+        o.y = fused_pair<OP>(va.y, vb.y);
+        o.z = fused_pair<OP>(va.z, vb.z);
+        o.w = fused_pair<OP>(va.w, vb.w);
+    }
     *reinterpret_cast<uint4 *>(y + i) = o;
 }
 
@@ -510,6 +557,12 @@ hipError_t launch_mx_cast(int op, unsigned axis, bool dbias, const MxArgs &a, hi
         return launch_axis<OP_SWIGLU, false>(axis, a, s);
     case OP_GEGLU:
         return launch_axis<OP_GEGLU, false>(axis, a, s);
+    case OP_DSILU:
+        return dbias ? launch_axis<OP_DSILU, true>(axis, a, s) : launch_axis<OP_DSILU, false>(axis, a, s);
+    case OP_DSWIGLU:
+        return launch_axis<OP_DSWIGLU, false>(axis, a, s);
+    case OP_DGEGLU:
+        return launch_axis<OP_DGEGLU, false>(axis, a, s);
     default:
         return hipErrorInvalidValue;
     }
@@ -527,7 +580,7 @@ hipError_t launch_dbias_reduce(const float *partials, int segments, int64_t K, f
 hipError_t launch_fused_values(int op, const uint16_t *x, const uint16_t *aux, int64_t M,
                                int64_t K, uint16_t *y, hipStream_t s)
 {
-    const int64_t threads = M * K / 8;
+    const int64_t threads = M * K * (op == OP_DSWIGLU || op == OP_DGEGLU ? 2 : 1) / 8;
     const dim3 grid((unsigned)((threads + 255) / 256));
     switch (op) {
     case OP_GELU:
@@ -541,6 +594,15 @@ hipError_t launch_fused_values(int op, const uint16_t *x, const uint16_t *aux, i
         break;
     case OP_GEGLU:
         hipLaunchKernelGGL(fused_values_kernel<OP_GEGLU>, grid, dim3(256), 0, s, x, x, M, K, y);
+        break;
+    case OP_DSILU:
+        hipLaunchKernelGGL(fused_values_kernel<OP_DSILU>, grid, dim3(256), 0, s, x, aux, M, K, y);
+        break;
+    case OP_DSWIGLU:
+        hipLaunchKernelGGL(fused_values_kernel<OP_DSWIGLU>, grid, dim3(256), 0, s, x, aux, M, K, y);
+        break;
+    case OP_DGEGLU:
+        hipLaunchKernelGGL(fused_values_kernel<OP_DGEGLU>, grid, dim3(256), 0, s, x, aux, M, K, y);
         break;
     default:
         return hipErrorInvalidValue;

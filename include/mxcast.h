@@ -12,7 +12,9 @@
  *     inside of dividing to improve perf": the dim1 cast and its inverse-scale
  *     multiply);
  *   - gated MXFP8 cast of act(gate) * linear with SwiGLU or GeGLU (PR 3291,
- *     table "MXFP8 gated (swiglu / geglu) kernel");
+ *     table "MXFP8 gated (swiglu / geglu) kernel"), and the backward casts
+ *     the same tables name: dSiLU (generic kernel) and dSwiGLU / dGeGLU
+ *     (gated kernel);
  *   - NVFP4 quantize-transpose with 16-element blocks (PR 3291, the NVFP4
  *     quantize-transpose kernels under "Important Files Changed" and
  *     "Patched but not measurable").
@@ -58,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MXCAST_ABI_VERSION 1
+#define MXCAST_ABI_VERSION 2
 
 typedef enum mx_status {
     MX_OK = 0,
@@ -81,6 +83,7 @@ typedef enum mx_status {
 #define MX_FUSE_NONE 0
 #define MX_FUSE_GELU 1      /* y = GELU(x)                                    */
 #define MX_FUSE_DGELU 2     /* y = GELU'(x) * grad                            */
+#define MX_FUSE_DSILU 3     /* y = SiLU'(x) * grad                            */
 #define MX_FUSE_DBIAS 0x10  /* also write dbias[k] = sum_m y[m][k] (fp32)     */
 
 /* gated activation */
@@ -90,10 +93,11 @@ typedef enum mx_status {
 /*
  * MXFP8 cast of x[M][K] (bf16), block size 32.
  *   x        device, bf16 [M][K]
- *   grad     device, bf16 [M][K]; required for MX_FUSE_DGELU, else ignored
+ *   grad     device, bf16 [M][K]; required for MX_FUSE_DGELU / DSILU, else
+ *            ignored
  *   M, K     rows, columns; positive multiples of 32, each <= 2^23, M*K <= 2^40
  *   axis_mask  MX_ROWWISE, MX_COLWISE or both (one pass over x)
- *   fusion   MX_FUSE_NONE | GELU | DGELU, optionally | MX_FUSE_DBIAS
+ *   fusion   MX_FUSE_NONE | GELU | DGELU | DSILU, optionally | MX_FUSE_DBIAS
  *   q_row, s_row  E4M3 [M][K] and E8M0 [M][K/32]; required iff MX_ROWWISE
  *   q_col, s_col  E4M3 [K][M] and E8M0 [K][M/32]; required iff MX_COLWISE
  *   dbias    fp32 [K]; required iff MX_FUSE_DBIAS
@@ -126,14 +130,33 @@ mx_status mx_quantize_gated(const void *x, int64_t M, int64_t N, unsigned axis_m
                             hipStream_t stream);
 
 /*
+ * Gated backward MXFP8 cast (the dswiglu / dgeglu rows of the gated table).
+ * grad is bf16 [M][N] (the gradient of act(gate) * linear), x the forward
+ * input bf16 [M][2N] = [gate | linear].  With a = act(gate), a' = act'(gate)
+ * (act = SiLU for MX_GATED_SWIGLU, GELU for MX_GATED_GEGLU), the quantised
+ * tensor is dx[M][2N] = [d_gate | d_linear]:
+ *   d_gate   = fl32(fl32(a' * grad) * linear),   d_linear = fl32(a * grad),
+ * each rounded once to bf16; block size 32 along 2N (row-wise) and M.
+ * M, N positive multiples of 32, M <= 2^23, 2N <= 2^23.
+ *   q_row, s_row  E4M3 [M][2N], E8M0 [M][2N/32]   (iff MX_ROWWISE)
+ *   q_col, s_col  E4M3 [2N][M], E8M0 [2N][M/32]   (iff MX_COLWISE)
+ * Errors as for mx_quantize_gated.
+ */
+mx_status mx_quantize_dgated(const void *grad, const void *x, int64_t M, int64_t N,
+                             unsigned axis_mask, int act, uint8_t *q_row, uint8_t *s_row,
+                             uint8_t *q_col, uint8_t *s_col, hipStream_t stream);
+
+/*
  * The fused elementwise values alone, as bf16: y = pre-op(x[, grad]) for
- * op = MX_FUSE_GELU / MX_FUSE_DGELU (x, grad and y are [M][K]), or the gated
- * value for op = 0x100 | MX_GATED_SWIGLU / MX_GATED_GEGLU (x is [M][2K],
- * y is [M][K]).  This is the exact tensor the fused casts quantise; it is
+ * op = MX_FUSE_GELU / MX_FUSE_DGELU / MX_FUSE_DSILU (x, grad and y are
+ * [M][K]), the gated value for op = 0x100 | MX_GATED_SWIGLU / MX_GATED_GEGLU
+ * (x is [M][2K], y is [M][K]), or the gated backward for op = 0x200 |
+ * MX_GATED_SWIGLU / MX_GATED_GEGLU (x is [M][2K], grad [M][K], y [M][2K]).  This is the exact tensor the fused casts quantise; it is
  * exposed so that the pre-op arithmetic can be checked on its own.  M and K
  * are positive multiples of 32, each <= 2^23 (2K <= 2^23 for gated ops).
  */
 #define MX_OP_GATED 0x100
+#define MX_OP_DGATED 0x200
 mx_status mx_fused_values(const void *x, const void *grad, int64_t M, int64_t K, int op,
                           void *y, hipStream_t stream);
 

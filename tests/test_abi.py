@@ -35,8 +35,13 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, name), name
 
 
+def header_abi_version():
+    text = open(os.path.join(ROOT, "include", "mxcast.h")).read()
+    return int(re.search(r"#define MXCAST_ABI_VERSION (\d+)", text).group(1))
+
+
 def test_version_and_status_strings():
-    assert mx.mx_abi_version() == 1
+    assert mx.mx_abi_version() == header_abi_version() == 2
     for code in range(9):
         assert mx.mx_status_str(code).startswith("MX_")
     assert "unknown" in mx.mx_status_str(99)
@@ -108,8 +113,10 @@ NULL = ctypes.c_void_p(0)
 @pytest.mark.parametrize("kw,code", [
     (dict(axis=0), mx.MX_ERR_ENUM),
     (dict(axis=4), mx.MX_ERR_ENUM),
-    (dict(fusion=3), mx.MX_ERR_ENUM),
+    (dict(fusion=5), mx.MX_ERR_ENUM),
     (dict(fusion=0x20), mx.MX_ERR_ENUM),
+    (dict(fusion=4), mx.MX_ERR_ENUM),
+    (dict(fusion=mx.FUSE_DSILU, grad=NULL), mx.MX_ERR_NULL),
     (dict(x=NULL), mx.MX_ERR_NULL),
     (dict(fusion=mx.FUSE_DGELU, grad=NULL), mx.MX_ERR_NULL),
     (dict(axis=1, s_row=NULL), mx.MX_ERR_NULL),
@@ -167,6 +174,28 @@ def test_gated_and_fused_values_reject():
     assert f(K=40) == mx.MX_ERR_SHAPE
     assert f(y=b.p("q_row", 2)) == mx.MX_ERR_ALIGN
     assert f(y=b.p("x", 16)) == mx.MX_ERR_ALIAS
+    assert b.untouched()
+
+
+def test_dgated_and_backward_values_reject():
+    b = Bufs(64, 128)        # x [64][128] = [gate | linear], grad in "g", outputs [64][128]
+    L = mx.lib()
+    d = lambda **kw: L.mx_quantize_dgated(kw.get("g", b.p("g")), kw.get("x", b.p("x")),
+                                          kw.get("M", 64), kw.get("N", 64), kw.get("axis", 3),
+                                          kw.get("act", 1), kw.get("q_row", b.p("q_row")),
+                                          kw.get("s_row", b.p("s_row")), kw.get("q_col", b.p("q_col")),
+                                          kw.get("s_col", b.p("s_col")), None)
+    assert d(act=0) == mx.MX_ERR_ENUM and d(act=3) == mx.MX_ERR_ENUM and d(axis=4) == mx.MX_ERR_ENUM
+    assert d(g=NULL) == mx.MX_ERR_NULL and d(x=NULL) == mx.MX_ERR_NULL
+    assert d(axis=1, s_row=NULL) == mx.MX_ERR_NULL
+    assert d(N=48) == mx.MX_ERR_SHAPE and d(M=0) == mx.MX_ERR_SHAPE
+    assert d(g=b.p("g", 2)) == mx.MX_ERR_ALIGN and d(s_col=b.p("s_col", 8)) == mx.MX_ERR_ALIGN
+    assert d(q_col=b.p("g", 16)) == mx.MX_ERR_ALIAS and d(q_row=b.p("x", 64)) == mx.MX_ERR_ALIAS
+    f = lambda **kw: L.mx_fused_values(kw.get("x", b.p("x")), kw.get("g", b.p("g")), 64, 64,
+                                       kw.get("op", mx.FUSE_DSILU), kw.get("y", b.p("q_row")), None)
+    assert f(op=mx.OP_DGATED | 3) == mx.MX_ERR_ENUM and f(op=mx.OP_DGATED) == mx.MX_ERR_ENUM
+    assert f(g=NULL) == mx.MX_ERR_NULL and f(op=mx.OP_DGATED | 1, g=NULL) == mx.MX_ERR_NULL
+    assert f(y=b.p("x", 32)) == mx.MX_ERR_ALIAS
     assert b.untouched()
 
 

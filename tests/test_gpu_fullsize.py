@@ -6,6 +6,9 @@ these sizes in seconds with OpenMP over rows / columns).
   8192^2 N(0, 2): GELU + dbias, and dGELU(x) * grad + dbias
   8192 x 8192 [gate | linear]: SwiGLU and GeGLU, both directions
   16384^2 Student-t with 1% of rows x100: NVFP4 quantize-transpose
+and the backward casts at the same sizes as their forward ones:
+  8192^2 N(0, 2) with grad N(0, 1): dSiLU(x) * grad + dbias
+  grad 8192 x 4096 with [gate | linear] 8192 x 8192: dSwiGLU and dGeGLU
 """
 import os
 
@@ -77,6 +80,26 @@ def test_c5_nvfp4_16384():
     o = O.nvfp4_quantize_transpose(x)
     assert g["sg"].item() == o["sg"]
     mx_outputs_equal(g, o, "C5 nvfp4")
+
+
+def test_dsilu_dbias_8192():
+    x, grad = W.make("f1_dsilu_dbias_8192")
+    f = mx.FUSE_DSILU | mx.FUSE_DBIAS
+    g = mx.mx_quantize(to_dev(x), to_dev(grad), fusion=f)
+    torch.cuda.synchronize()
+    o = O.mx_quantize(x, grad=grad, fusion=f, want_y=True)
+    mx_outputs_equal(g, o, "dSiLU + dbias")
+    ycols = np.abs(W.bf16_to_f32(o["y"]).astype(np.float64)).sum(axis=0)
+    assert_dbias_close(g["dbias"], o["dbias"], ycols)
+
+
+@pytest.mark.parametrize("act", [mx.GATED_SWIGLU, mx.GATED_GEGLU])
+def test_gated_backward_8192(act):
+    grad, x = W.make("f1_dgated_8192")
+    g = mx.mx_quantize_dgated(to_dev(grad), to_dev(x), act)
+    torch.cuda.synchronize()
+    o = O.mx_quantize_dgated(grad, x, act)
+    mx_outputs_equal(g, o, f"gated backward act {act}")
 
 
 def test_c1_special_256x512():

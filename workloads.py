@@ -120,4 +120,13 @@ def make(name: str, M: int = None, K: int = None):
         return normal(M or 8192, K or 8192, seed=4)
     if name == "c5_nvfp4_16384":
         return student_t_rows(M or 16384, K or 16384, seed=5)
+    if name == "f1_dsilu_dbias_8192":
+        # the backward of the fused cast: forward input ~N(0, 2), grad ~N(0, 1)
+        M, K = M or 8192, K or 8192
+        return normal(M, K, seed=6, sigma=float(np.sqrt(2.0))), normal(M, K, seed=66)
+    if name == "f1_dgated_8192":
+        # gated backward: grad [M][N] ~N(0, 1) and the forward input
+        # [gate | linear] [M][2N] ~N(0, 1); here K names N
+        M, N = M or 8192, K or 4096
+        return normal(M, N, seed=7), normal(M, 2 * N, seed=77)
     raise KeyError(name)

@@ -55,24 +55,32 @@ bool shape_ok(int64_t M, int64_t K, int64_t block)
 
 int tiles(int64_t n, int64_t t) { return (int)((n + t - 1) / t); }
 
-// Walks along M of the cast kernels for an M x K tensor.
-int walks_m(int64_t M, int64_t K)
+// Kernel op of an mx_quantize pre-op.
+int cast_op(int pre)
+{
+    return pre == MX_FUSE_GELU ? mxk::OP_GELU : pre == MX_FUSE_DGELU ? mxk::OP_DGELU
+         : pre == MX_FUSE_DSILU ? mxk::OP_DSILU : mxk::OP_PLAIN;
+}
+
+// Walks along M of the cast kernel `op` (with or without dbias) for an
+// M x K tensor.
+int walks_m(int64_t M, int64_t K, int op, bool dbias)
 {
     const int tm = tiles(M, mxk::kTileM), tk = tiles(K, mxk::kTileK);
-    const int g = mxk::pick_group(tm, tk);
+    const int g = mxk::pick_group(tm, tk, mxk::target_workgroups(op, dbias));
     return (tm + g - 1) / g;
 }
 
-size_t dbias_workspace(int64_t M, int64_t K)
+size_t dbias_workspace(int64_t M, int64_t K, int op)
 {
-    return (size_t)walks_m(M, K) * (size_t)K * sizeof(float);
+    return (size_t)walks_m(M, K, op, true) * (size_t)K * sizeof(float);
 }
 
-void set_walk(mxk::MxArgs &a)
+void set_walk(mxk::MxArgs &a, int op, bool dbias)
 {
     a.tiles_k = tiles(a.K, mxk::kTileK);
     a.tiles_m = tiles(a.M, mxk::kTileM);
-    a.group = mxk::pick_group(a.tiles_m, a.tiles_k);
+    a.group = mxk::pick_group(a.tiles_m, a.tiles_k, mxk::target_workgroups(op, dbias));
     a.groups_m = (a.tiles_m + a.group - 1) / a.group;
 }
 
@@ -102,9 +110,10 @@ const char *mx_status_str(int s)
 
 size_t mx_quantize_workspace_size(int64_t M, int64_t K, unsigned axis_mask, int fusion)
 {
-    if (!(fusion & MX_FUSE_DBIAS) || !shape_ok(M, K, 32) || axis_mask == 0 || (axis_mask & ~3u))
+    if (!(fusion & MX_FUSE_DBIAS) || !shape_ok(M, K, 32) || axis_mask == 0 || (axis_mask & ~3u) ||
+        (fusion & ~0x1F) || (fusion & 0xF) > MX_FUSE_DSILU)
         return 0;
-    return dbias_workspace(M, K);
+    return dbias_workspace(M, K, cast_op(fusion & 0xF));
 }
 
 mx_status mx_quantize(const void *x, const void *grad, int64_t M, int64_t K, unsigned axis_mask,
@@ -127,7 +136,8 @@ mx_status mx_quantize(const void *x, const void *grad, int64_t M, int64_t K, uns
         (col && (!aligned(q_col, 16) || !aligned(s_col, 16))) ||
         (want_dbias && (!aligned(dbias, 4) || (workspace && !aligned(workspace, 16)))))
         return MX_ERR_ALIGN;
-    const size_t need = want_dbias ? dbias_workspace(M, K) : 0;
+    const int op = cast_op(pre);
+    const size_t need = want_dbias ? dbias_workspace(M, K, op) : 0;
     if (want_dbias && (!workspace || workspace_bytes < need))
         return MX_ERR_WORKSPACE;
     const uint64_t n = (uint64_t)(M * K);
@@ -152,9 +162,7 @@ mx_status mx_quantize(const void *x, const void *grad, int64_t M, int64_t K, uns
     a.q_col = q_col;
     a.s_col = s_col;
     a.partials = want_dbias ? static_cast<float *>(workspace) : nullptr;
-    set_walk(a);
-    const int op = pre == MX_FUSE_GELU ? mxk::OP_GELU : pre == MX_FUSE_DGELU ? mxk::OP_DGELU
-                 : pre == MX_FUSE_DSILU ? mxk::OP_DSILU : mxk::OP_PLAIN;
+    set_walk(a, op, want_dbias);
     mx_status st = from_hip(mxk::launch_mx_cast(op, axis_mask, want_dbias, a, stream));
     if (st != MX_OK || !want_dbias)
         return st;
@@ -195,8 +203,8 @@ mx_status mx_quantize_gated(const void *x, int64_t M, int64_t N, unsigned axis_m
     a.q_col = q_col;
     a.s_col = s_col;
     a.partials = nullptr;
-    set_walk(a);
     const int op = act == MX_GATED_SWIGLU ? mxk::OP_SWIGLU : mxk::OP_GEGLU;
+    set_walk(a, op, false);
     return from_hip(mxk::launch_mx_cast(op, axis_mask, false, a, stream));
 }
 
@@ -235,8 +243,8 @@ mx_status mx_quantize_dgated(const void *grad, const void *x, int64_t M, int64_t
     a.q_col = q_col;
     a.s_col = s_col;
     a.partials = nullptr;
-    set_walk(a);
     const int op = act == MX_GATED_SWIGLU ? mxk::OP_DSWIGLU : mxk::OP_DGEGLU;
+    set_walk(a, op, false);
     return from_hip(mxk::launch_mx_cast(op, axis_mask, false, a, stream));
 }
 
@@ -325,7 +333,7 @@ mx_status nvfp4_quantize_transpose(const void *x, int64_t M, int64_t K, const fl
     a.sg_out = global_scale_out;
     a.tiles_k = tiles(K, mxk::kTileK);
     a.tiles_m = tiles(M, mxk::kTileM);
-    a.group = mxk::pick_group(a.tiles_m, a.tiles_k);
+    a.group = mxk::pick_group(a.tiles_m, a.tiles_k, mxk::kTargetWorkgroups);
     a.groups_m = (a.tiles_m + a.group - 1) / a.group;
     return from_hip(mxk::launch_nvfp4(axis_mask, a, stream));
 }

@@ -26,15 +26,25 @@ constexpr int kTileM = 2 * kRowsPerLane * kWaves;  // 128
 constexpr int kTileK = kColsPerLane * 32;          // 256
 // A cast workgroup walks down up to kMaxGroup sub-tiles of a 256-column strip.
 constexpr int kMaxGroup = 16;
-// Workgroups the host aims to launch at least (two per MI355X compute unit).
+// Workgroups the host aims to launch at least: two per MI355X compute unit
+// for the plain cast (bound by memory, two resident per CU) and for the casts
+// with dbias; four for the other fused casts (bound by their arithmetic,
+// three resident per CU; more workgroups than slots keep every CU busy to
+// the end).  Chosen by measurement on the 8192^2 and 16384^2 workloads.
 constexpr int kTargetWorkgroups = 512;
+constexpr int kTargetWorkgroupsFused = 1024;
+
+inline int target_workgroups(int op, bool dbias)
+{
+    return op == OP_PLAIN || dbias ? kTargetWorkgroups : kTargetWorkgroupsFused;
+}
 
 // Sub-tiles per workgroup for a tiles_m x tiles_k grid of sub-tiles: the
-// deepest power of two <= kMaxGroup that still yields kTargetWorkgroups.
-inline int pick_group(int tiles_m, int tiles_k)
+// deepest power of two <= kMaxGroup that still yields `target` workgroups.
+inline int pick_group(int tiles_m, int tiles_k, int target)
 {
     int g = kMaxGroup;
-    while (g > 1 && (int64_t)((tiles_m + g - 1) / g) * tiles_k < kTargetWorkgroups)
+    while (g > 1 && (int64_t)((tiles_m + g - 1) / g) * tiles_k < target)
         g >>= 1;
     return g;
 }

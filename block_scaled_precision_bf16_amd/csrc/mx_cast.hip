@@ -402,8 +402,19 @@ __device__ __forceinline__ void tile_step(const MxArgs &a, const LaneAt &l,
 // Walking keeps the strip's column scales together (so they leave as whole
 // 64-byte chunks rather than 4-byte pieces) and, for the plain cast, lets the
 // next sub-tile's loads overlap the current sub-tile's conversion.
+// Workgroups per CU the compiler budgets registers for: the fused casts
+// without dbias are bound by their arithmetic and gain from a third
+// workgroup (at most 168 VGPRs); the plain cast keeps its double register set
+// for the prefetch, and the dbias sums and the gated backward need their
+// registers (capping them spills and measured slower).
+template <int OP, bool DBIAS>
+constexpr int min_blocks()
+{
+    return OP == OP_PLAIN || OP == OP_DSWIGLU || OP == OP_DGEGLU || DBIAS ? 1 : 3;
+}
+
 template <int OP, bool ROW, bool COL, bool DBIAS>
-__global__ __launch_bounds__(kThreads) void mx_cast_kernel(MxArgs a)
+__global__ __launch_bounds__(kThreads, (min_blocks<OP, DBIAS>())) void mx_cast_kernel(MxArgs a)
 {
     const int job = xcd_tile((int)blockIdx.x, (int)gridDim.x);
     const int rg = job / a.tiles_k;
@@ -455,7 +466,16 @@ __global__ __launch_bounds__(kThreads) void mx_cast_kernel(MxArgs a)
         // per-lane sums (rows in order, sub-tiles in order), then the 8
         // lane-halves of the workgroup in order: one fp32 partial per
         // (strip segment, column)
-        __shared__ float4 red[2 * kWaves][kTileK / 4];
+        // the cross-wave sums reuse the transposed-output stage when there is
+        // one (its q part is no longer read), which keeps the LDS of a
+        // workgroup small enough for three per CU
+        float4 (*red)[kTileK / 4];
+        if constexpr (COL) {
+            red = reinterpret_cast<float4 (*)[kTileK / 4]>(&st->q[0][0]);
+        } else {
+            __shared__ float4 red_own[2 * kWaves][kTileK / 4];
+            red = red_own;
+        }
         const int slot = 2 * l.wave + l.half;
         red[slot][l.cl * 2] = make_float4(dsum[0], dsum[1], dsum[2], dsum[3]);
         red[slot][l.cl * 2 + 1] = make_float4(dsum[4], dsum[5], dsum[6], dsum[7]);

@@ -47,25 +47,32 @@ def test_version_and_status_strings():
     assert "unknown" in mx.mx_status_str(99)
 
 
-def walks(M, K):
+def walks(M, K, target=512):
     """Workgroup walks along M: sub-tiles are 128 x 256; a walk takes the deepest
-    power of two <= 16 sub-tiles that still leaves >= 512 workgroups."""
+    power of two <= 16 sub-tiles that still leaves >= target workgroups (512
+    for the plain cast and casts with dbias, 1024 for the other fused casts)."""
     tm, tk = -(-M // 128), -(-K // 256)
     g = 16
-    while g > 1 and -(-tm // g) * tk < 512:
+    while g > 1 and -(-tm // g) * tk < target:
         g //= 2
     return -(-tm // g)
 
 
 def test_workspace_size():
-    assert mx.mx_quantize_workspace_size(8192, 8192, 3, mx.FUSE_NONE) == 0
+    ws = mx.mx_quantize_workspace_size
+    assert ws(8192, 8192, 3, mx.FUSE_NONE) == 0
     assert walks(8192, 8192) == 16 and walks(16384, 16384) == 8 and walks(96, 32) == 1
-    assert mx.mx_quantize_workspace_size(8192, 8192, 3, mx.FUSE_DBIAS) == 16 * 8192 * 4
-    assert mx.mx_quantize_workspace_size(200 * 32, 96, 3, mx.FUSE_GELU | mx.FUSE_DBIAS) == 50 * 96 * 4
+    assert walks(8192, 8192, 1024) == 32
+    assert ws(8192, 8192, 3, mx.FUSE_DBIAS) == 16 * 8192 * 4
+    assert ws(8192, 8192, 3, mx.FUSE_GELU | mx.FUSE_DBIAS) == 16 * 8192 * 4
+    assert ws(200 * 32, 96, 3, mx.FUSE_GELU | mx.FUSE_DBIAS) == 50 * 96 * 4
     for M, K in ((32, 32), (4096, 14336), (16384, 5120), (8192, 28672)):
-        assert mx.mx_quantize_workspace_size(M, K, 3, mx.FUSE_DBIAS) == walks(M, K) * K * 4
-    assert mx.mx_quantize_workspace_size(48, 64, 3, mx.FUSE_DBIAS) == 0      # invalid shape
-    assert mx.mx_quantize_workspace_size(64, 64, 0, mx.FUSE_DBIAS) == 0      # invalid axis
+        assert ws(M, K, 3, mx.FUSE_DBIAS) == walks(M, K) * K * 4
+        for pre in (mx.FUSE_GELU, mx.FUSE_DGELU, mx.FUSE_DSILU):
+            assert ws(M, K, 3, pre | mx.FUSE_DBIAS) == walks(M, K) * K * 4
+    assert ws(48, 64, 3, mx.FUSE_DBIAS) == 0      # invalid shape
+    assert ws(64, 64, 0, mx.FUSE_DBIAS) == 0      # invalid axis
+    assert ws(64, 64, 3, 0x14) == 0               # invalid pre-op
 
 
 class Bufs:

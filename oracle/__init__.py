@@ -73,6 +73,10 @@ def lib():
         L.orc_mx_quantize_gated.restype = ctypes.c_int
         L.orc_mx_quantize_gated.argtypes = [_u16p, _i64, _i64, ctypes.c_uint, ctypes.c_int,
                                             _u8p, _u8p, _u8p, _u8p, _u16p]
+        L.orc_nvfp4_quantize_transpose_2d.restype = ctypes.c_int
+        L.orc_nvfp4_quantize_transpose_2d.argtypes = [_u16p, _i64, _i64, ctypes.c_uint,
+                                                      ctypes.c_float, _u8p, _u8p, _u8p, _u8p,
+                                                      _f32p]
         L.orc_absmax.restype = ctypes.c_float
         L.orc_absmax.argtypes = [_u16p, _i64]
         L.orc_nvfp4_global_scale.restype = ctypes.c_float
@@ -280,8 +284,9 @@ def nvfp4_global_scale(A: float) -> float:
     return lib().orc_nvfp4_global_scale(A)
 
 
-def nvfp4_quantize_transpose(x, axis=ROWWISE | COLWISE, tensor_amax=None):
-    """NVFP4 of x[M][K] and of its transpose. tensor_amax overrides max|x|."""
+def nvfp4_quantize_transpose(x, axis=ROWWISE | COLWISE, tensor_amax=None, two_d=False):
+    """NVFP4 of x[M][K] and of its transpose. tensor_amax overrides max|x|.
+    two_d: one scale per 16 x 16 block (written per row / per column)."""
     x = _c(x, np.uint16)
     M, K = x.shape
     q_row = np.zeros((M, K // 2), np.uint8) if axis & ROWWISE else None
@@ -290,9 +295,9 @@ def nvfp4_quantize_transpose(x, axis=ROWWISE | COLWISE, tensor_amax=None):
     s_col = np.zeros((K, M // 16), np.uint8) if axis & COLWISE else None
     sg = np.zeros(1, np.float32)
     A = -1.0 if tensor_amax is None else float(tensor_amax)
-    rc = lib().orc_nvfp4_quantize_transpose(_p(x, _u16p), M, K, axis, A, _p(q_row, _u8p),
-                                            _p(s_row, _u8p), _p(q_col, _u8p),
-                                            _p(s_col, _u8p), _p(sg, _f32p))
+    fn = lib().orc_nvfp4_quantize_transpose_2d if two_d else lib().orc_nvfp4_quantize_transpose
+    rc = fn(_p(x, _u16p), M, K, axis, A, _p(q_row, _u8p), _p(s_row, _u8p), _p(q_col, _u8p),
+            _p(s_col, _u8p), _p(sg, _f32p))
     if rc != 0:
         raise ValueError(f"oracle nvfp4_quantize_transpose failed with code {rc}")
     return dict(q_row=q_row, s_row=s_row, q_col=q_col, s_col=s_col, sg=float(sg[0]))

@@ -651,6 +651,58 @@ int orc_nvfp4_quantize_transpose(const uint16_t *x, int64_t M, int64_t K, unsign
     return ORC_OK;
 }
 
+/* NVFP4 with 2D scaling ("nvfp42d" in the quantize-transpose table): one
+ * E4M3 scale per 16 x 16 block of x, by the same chain as the 1D blocks with
+ * b = max |x| over the 256 elements.  Both outputs keep the 1D layouts: the
+ * block's scale is written for each of its 16 rows in s_row[M][K/16] and for
+ * each of its 16 columns in s_col[K][M/16], and every element is coded with
+ * its block's multiplier in q_row and in the transposed q_col. */
+int orc_nvfp4_quantize_transpose_2d(const uint16_t *x, int64_t M, int64_t K, unsigned axis,
+                                    float tensor_amax, uint8_t *q_row, uint8_t *s_row,
+                                    uint8_t *q_col, uint8_t *s_col, float *sg_out)
+{
+    if (M <= 0 || K <= 0 || M % 16 || K % 16)
+        return ORC_ERR_SHAPE;
+    if (axis & ~3u)
+        return ORC_ERR_ENUM;
+    init_tables();
+    float A = tensor_amax >= 0.0f ? tensor_amax : orc_absmax(x, M * K);
+    float Sg = orc_nvfp4_global_scale(A);
+    if (sg_out)
+        *sg_out = Sg;
+#pragma omp parallel for schedule(static)
+    for (int64_t bi = 0; bi < M / 16; bi++) {
+        double v[256];
+        uint8_t c[256];
+        for (int64_t bj = 0; bj < K / 16; bj++) {
+            for (int r = 0; r < 16; r++)
+                for (int q = 0; q < 16; q++)
+                    v[16 * r + q] = orc_bf16_value(x[(16 * bi + r) * K + 16 * bj + q]);
+            uint8_t sb;
+            nvfp4_block(v, 256, Sg, c, 1, &sb);        /* codes in row-major order */
+            for (int r = 0; r < 16; r++) {
+                const int64_t m = 16 * bi + r;
+                if (axis & 1u) {
+                    s_row[m * (K / 16) + bj] = sb;
+                    for (int i = 0; i < 8; i++)
+                        q_row[m * (K / 2) + 8 * bj + i] =
+                            (uint8_t)(c[16 * r + 2 * i] | (c[16 * r + 2 * i + 1] << 4));
+                }
+            }
+            for (int q = 0; q < 16; q++) {
+                const int64_t k = 16 * bj + q;
+                if (axis & 2u) {
+                    s_col[k * (M / 16) + bi] = sb;
+                    for (int i = 0; i < 8; i++)
+                        q_col[k * (M / 2) + 8 * bi + i] =
+                            (uint8_t)(c[16 * (2 * i) + q] | (c[16 * (2 * i + 1) + q] << 4));
+                }
+            }
+        }
+    }
+    return ORC_OK;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Array helpers for the self-tests (elementwise, no method arithmetic).     */
 /* ------------------------------------------------------------------------ */

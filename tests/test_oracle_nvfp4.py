@@ -159,3 +159,50 @@ def test_zero_tensor_and_shape_errors():
     assert out["sg"] == 1.0 and not out["q_row"].any() and not out["s_row"].any()
     with pytest.raises(ValueError):
         O.nvfp4_quantize_transpose(np.zeros((16, 24), np.uint16))
+
+
+# --- NVFP4 with 2D (16 x 16 block) scaling ------------------------------------
+
+def test_2d_transposes_like_the_transpose():
+    """A 16 x 16 block is its own transpose's block: the column-wise outputs of
+    x equal the row-wise outputs of x^T (same tensor scale)."""
+    x = W.student_t_rows(96, 160, seed=61)
+    a = O.nvfp4_quantize_transpose(x, two_d=True)
+    b = O.nvfp4_quantize_transpose(np.ascontiguousarray(x.T), two_d=True)
+    assert a["sg"] == b["sg"]
+    assert np.array_equal(a["q_col"], b["q_row"]) and np.array_equal(a["s_col"], b["s_row"])
+    assert np.array_equal(a["q_row"], b["q_col"]) and np.array_equal(a["s_row"], b["s_col"])
+
+
+def test_2d_scale_is_one_per_block_replicated():
+    x = W.student_t_rows(64, 128, seed=62)
+    a = O.nvfp4_quantize_transpose(x, two_d=True)
+    s = a["s_row"].reshape(4, 16, 8)
+    assert np.all(s == s[:, :1, :])                       # same for the 16 rows of a block
+    assert np.array_equal(a["s_col"][::16, :], a["s_row"][::16, :].T)
+
+
+def test_2d_equals_1d_when_the_rows_of_a_block_are_equal():
+    base = W.student_t_rows(4, 256, seed=63)
+    x = np.repeat(base, 16, axis=0)                       # each 16-row group is one row repeated
+    a = O.nvfp4_quantize_transpose(x, axis=1, two_d=True)
+    b = O.nvfp4_quantize_transpose(x, axis=1)
+    assert np.array_equal(a["q_row"], b["q_row"]) and np.array_equal(a["s_row"], b["s_row"])
+
+
+def test_2d_block_amax_spans_rows():
+    """One element of 6.0 in a block of 0.5s, tensor scale 1 (amax 2688 given):
+    b = 6 gives scale E4M3(1) = 0x38 and multiplier 1 for all 256 elements, so
+    every 0.5 codes as E2M1 0x1 -- in 1D, the rows without the 6.0 would get
+    their own (smaller) scale instead."""
+    x = np.full((16, 16), 0x3F00, np.uint16)              # 0.5
+    x[3, 7] = 0x40C0                                      # 6.0
+    a = O.nvfp4_quantize_transpose(x, tensor_amax=2688.0, two_d=True)
+    assert a["sg"] == 1.0
+    assert np.all(a["s_row"] == 0x38) and np.all(a["s_col"] == 0x38)
+    codes = np.stack([a["q_row"] & 0xF, a["q_row"] >> 4], axis=-1).reshape(16, 16)
+    want = np.full((16, 16), 0x1, np.uint8)
+    want[3, 7] = 0x7
+    assert np.array_equal(codes, want)
+    one_d = O.nvfp4_quantize_transpose(x, tensor_amax=2688.0)
+    assert one_d["s_row"][0, 0] != 0x38                   # row 0 has no 6.0

@@ -58,6 +58,7 @@ CONFIGS = {
     "mxfp8_swiglu_8192": ("c4_gated_8192", (8192, 8192), "gated_swiglu", 3),
     "mxfp8_geglu_8192": ("c4_gated_8192", (8192, 8192), "gated_geglu", 3),
     "nvfp4_16384": ("c5_nvfp4_16384", (16384, 16384), "nvfp4", 3),
+    "nvfp4_2d_16384": ("c5_nvfp4_16384", (16384, 16384), "nvfp4_2d", 3),
     "mxfp8_dsilu_dbias_8192": ("f1_dsilu_dbias_8192", (8192, 8192), "mx_dsilu", 3),
     "mxfp8_dswiglu_8192": ("f1_dgated_8192", (8192, 4096), "dgated_swiglu", 3),
     "mxfp8_dgeglu_8192": ("f1_dgated_8192", (8192, 4096), "dgated_geglu", 3),
@@ -143,12 +144,14 @@ def main():
     grad = to_dev(g_h) if g_h is not None else None
 
     # outputs and workspace allocated once, outside the timed region
-    if kind == "nvfp4":
+    if kind.startswith("nvfp4"):
+        two_d = kind == "nvfp4_2d"
         amax = mx.mx_absmax_bf16(x)
-        out = mx.nvfp4_quantize_transpose(x, amax)
-        step = lambda: mx.nvfp4_quantize_transpose(x, amax, out=out)
+        out = mx.nvfp4_quantize_transpose(x, amax, two_d=two_d)
+        step = lambda: mx.nvfp4_quantize_transpose(x, amax, out=out, two_d=two_d)
         alg_bytes = nvfp4_bytes(M, K, 2)
-        desc = dict(workload=args.config, M=M, K=K, block=16, directions="row+transpose",
+        desc = dict(workload=args.config, M=M, K=K, block="16x16" if two_d else 16,
+                    directions="row+transpose",
                     format="nvfp4 (e2m1 + e4m3 scales + fp32 tensor scale)")
     elif kind.startswith("dgated"):
         act = mx.GATED_SWIGLU if kind.endswith("swiglu") else mx.GATED_GEGLU
@@ -255,8 +258,8 @@ def main():
               file=sys.stderr, flush=True)
         c0 = time.process_time()
         t0 = time.perf_counter()
-        if kind == "nvfp4":
-            O.nvfp4_quantize_transpose(xs, tensor_amax=O.absmax(x_h))
+        if kind.startswith("nvfp4"):
+            O.nvfp4_quantize_transpose(xs, tensor_amax=O.absmax(x_h), two_d=kind == "nvfp4_2d")
             sb = nvfp4_bytes(rows, K, 2)
         elif kind.startswith("dgated"):
             O.mx_quantize_dgated(np.ascontiguousarray(g_h[:rows]), xs,

@@ -31,7 +31,8 @@ OP_GATED, OP_DGATED = 0x100, 0x200
 
 EXPORTS = ("mx_quantize", "mx_quantize_workspace_size", "mx_quantize_gated",
            "mx_quantize_dgated", "mx_fused_values",
-           "mx_absmax_bf16", "nvfp4_quantize_transpose", "mx_status_str", "mx_abi_version")
+           "mx_absmax_bf16", "nvfp4_quantize_transpose", "nvfp4_quantize_transpose_2d",
+           "mx_status_str", "mx_abi_version")
 
 
 class MxError(RuntimeError):
@@ -71,6 +72,8 @@ def lib():
         L.nvfp4_quantize_transpose.restype = ctypes.c_int
         L.nvfp4_quantize_transpose.argtypes = [_vp, _i64, _i64, _vp, ctypes.c_uint,
                                                _vp, _vp, _vp, _vp, _vp, _vp]
+        L.nvfp4_quantize_transpose_2d.restype = ctypes.c_int
+        L.nvfp4_quantize_transpose_2d.argtypes = L.nvfp4_quantize_transpose.argtypes
         L.mx_status_str.restype = ctypes.c_char_p
         L.mx_status_str.argtypes = [ctypes.c_int]
         L.mx_abi_version.restype = ctypes.c_int
@@ -220,10 +223,11 @@ def mx_absmax_bf16(x, out=None, stream=None):
     return amax
 
 
-def nvfp4_quantize_transpose(x, amax=None, axis=ROWWISE | COLWISE, out=None, stream=None):
+def nvfp4_quantize_transpose(x, amax=None, axis=ROWWISE | COLWISE, out=None, stream=None,
+                             two_d=False):
     """NVFP4 of x[M][K] and its transpose.  amax: one-element float32 device
-    tensor (computed with mx_absmax_bf16 when None).  Returns {q_row, s_row,
-    q_col, s_col, sg}."""
+    tensor (computed with mx_absmax_bf16 when None).  two_d: one scale per
+    16 x 16 block.  Returns {q_row, s_row, q_col, s_col, sg}."""
     x = _bf16_bits(x)
     M, K = x.shape
     dev = x.device
@@ -237,9 +241,8 @@ def nvfp4_quantize_transpose(x, amax=None, axis=ROWWISE | COLWISE, out=None, str
         o.setdefault("q_col", _u8((K, M // 2), dev))
         o.setdefault("s_col", _u8((K, M // 16), dev))
     o.setdefault("sg", torch.empty(1, dtype=torch.float32, device=dev))
-    st = lib().nvfp4_quantize_transpose(_ptr(x), M, K, _ptr(amax), axis, _ptr(o.get("q_row")),
-                                        _ptr(o.get("s_row")), _ptr(o.get("q_col")),
-                                        _ptr(o.get("s_col")), _ptr(o["sg"]),
-                                        _stream(dev, stream))
-    _check(st, "nvfp4_quantize_transpose")
+    fn = lib().nvfp4_quantize_transpose_2d if two_d else lib().nvfp4_quantize_transpose
+    st = fn(_ptr(x), M, K, _ptr(amax), axis, _ptr(o.get("q_row")), _ptr(o.get("s_row")),
+            _ptr(o.get("q_col")), _ptr(o.get("s_col")), _ptr(o["sg"]), _stream(dev, stream))
+    _check(st, "nvfp4_quantize_transpose_2d" if two_d else "nvfp4_quantize_transpose")
     return {k: o.get(k) for k in ("q_row", "s_row", "q_col", "s_col", "sg")}

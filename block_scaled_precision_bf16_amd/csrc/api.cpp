@@ -88,6 +88,48 @@ mx_status from_hip(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; 
 
 }  // namespace
 
+// NVFP4 quantize-transpose with 1D (two_d = false) or 16 x 16 block scaling.
+static mx_status nvfp4_impl(bool two_d, const void *x, int64_t M, int64_t K, const float *amax,
+                            unsigned axis_mask, uint8_t *q_row, uint8_t *s_row, uint8_t *q_col,
+                            uint8_t *s_col, float *global_scale_out, hipStream_t stream)
+{
+    if (axis_mask == 0 || (axis_mask & ~3u))
+        return MX_ERR_ENUM;
+    const bool row = axis_mask & MX_ROWWISE, col = axis_mask & MX_COLWISE;
+    if (!x || !amax || (row && (!q_row || !s_row)) || (col && (!q_col || !s_col)))
+        return MX_ERR_NULL;
+    if (!shape_ok(M, K, 16))
+        return MX_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(amax, 4) ||
+        (row && (!aligned(q_row, 16) || !aligned(s_row, 16))) ||
+        (col && (!aligned(q_col, 16) || !aligned(s_col, 16))) ||
+        (global_scale_out && !aligned(global_scale_out, 4)))
+        return MX_ERR_ALIGN;
+    const uint64_t n = (uint64_t)(M * K);
+    const Span in[2] = {{x, 2 * n}, {amax, 4}};
+    const Span out[5] = {{row ? q_row : nullptr, n / 2}, {row ? s_row : nullptr, n / 16},
+                         {col ? q_col : nullptr, n / 2}, {col ? s_col : nullptr, n / 16},
+                         {global_scale_out, 4}};
+    if (any_alias(in, 2, out, 5))
+        return MX_ERR_ALIAS;
+
+    mxk::Nv4Args a;
+    a.x = static_cast<const uint16_t *>(x);
+    a.M = M;
+    a.K = K;
+    a.amax = amax;
+    a.q_row = q_row;
+    a.s_row = s_row;
+    a.q_col = q_col;
+    a.s_col = s_col;
+    a.sg_out = global_scale_out;
+    a.tiles_k = tiles(K, mxk::kTileK);
+    a.tiles_m = tiles(M, mxk::kTileM);
+    a.group = mxk::pick_group(a.tiles_m, a.tiles_k, mxk::kTargetWorkgroups);
+    a.groups_m = (a.tiles_m + a.group - 1) / a.group;
+    return from_hip(mxk::launch_nvfp4(axis_mask, two_d, a, stream));
+}
+
 extern "C" {
 
 int mx_abi_version(void) { return MXCAST_ABI_VERSION; }
@@ -301,41 +343,17 @@ mx_status nvfp4_quantize_transpose(const void *x, int64_t M, int64_t K, const fl
                                    uint8_t *q_col, uint8_t *s_col, float *global_scale_out,
                                    hipStream_t stream)
 {
-    if (axis_mask == 0 || (axis_mask & ~3u))
-        return MX_ERR_ENUM;
-    const bool row = axis_mask & MX_ROWWISE, col = axis_mask & MX_COLWISE;
-    if (!x || !amax || (row && (!q_row || !s_row)) || (col && (!q_col || !s_col)))
-        return MX_ERR_NULL;
-    if (!shape_ok(M, K, 16))
-        return MX_ERR_SHAPE;
-    if (!aligned(x, 16) || !aligned(amax, 4) ||
-        (row && (!aligned(q_row, 16) || !aligned(s_row, 16))) ||
-        (col && (!aligned(q_col, 16) || !aligned(s_col, 16))) ||
-        (global_scale_out && !aligned(global_scale_out, 4)))
-        return MX_ERR_ALIGN;
-    const uint64_t n = (uint64_t)(M * K);
-    const Span in[2] = {{x, 2 * n}, {amax, 4}};
-    const Span out[5] = {{row ? q_row : nullptr, n / 2}, {row ? s_row : nullptr, n / 16},
-                         {col ? q_col : nullptr, n / 2}, {col ? s_col : nullptr, n / 16},
-                         {global_scale_out, 4}};
-    if (any_alias(in, 2, out, 5))
-        return MX_ERR_ALIAS;
+    return nvfp4_impl(false, x, M, K, amax, axis_mask, q_row, s_row, q_col, s_col,
+                      global_scale_out, stream);
+}
 
-    mxk::Nv4Args a;
-    a.x = static_cast<const uint16_t *>(x);
-    a.M = M;
-    a.K = K;
-    a.amax = amax;
-    a.q_row = q_row;
-    a.s_row = s_row;
-    a.q_col = q_col;
-    a.s_col = s_col;
-    a.sg_out = global_scale_out;
-    a.tiles_k = tiles(K, mxk::kTileK);
-    a.tiles_m = tiles(M, mxk::kTileM);
-    a.group = mxk::pick_group(a.tiles_m, a.tiles_k, mxk::kTargetWorkgroups);
-    a.groups_m = (a.tiles_m + a.group - 1) / a.group;
-    return from_hip(mxk::launch_nvfp4(axis_mask, a, stream));
+mx_status nvfp4_quantize_transpose_2d(const void *x, int64_t M, int64_t K, const float *amax,
+                                      unsigned axis_mask, uint8_t *q_row, uint8_t *s_row,
+                                      uint8_t *q_col, uint8_t *s_col, float *global_scale_out,
+                                      hipStream_t stream)
+{
+    return nvfp4_impl(true, x, M, K, amax, axis_mask, q_row, s_row, q_col, s_col,
+                      global_scale_out, stream);
 }
 
 }  // extern "C"

@@ -81,6 +81,7 @@ hipError_t launch_dbias_reduce(const float *partials, int segments, int64_t K, f
 hipError_t launch_fused_values(int op, const uint16_t *x, const uint16_t *aux, int64_t M,
                                int64_t K, uint16_t *y, hipStream_t s);
 hipError_t launch_absmax(const uint16_t *x, int64_t n, float *amax, hipStream_t s);
-hipError_t launch_nvfp4(unsigned axis, const Nv4Args &a, hipStream_t s);
+// two_d: one scale per 16 x 16 block instead of per 16 elements of a row.
+hipError_t launch_nvfp4(unsigned axis, bool two_d, const Nv4Args &a, hipStream_t s);
 
 }  // namespace mxk

@@ -259,7 +259,61 @@ __device__ __forceinline__ void nv_flush_srow(const Nv4Args &a, const NvStage &s
 // One sub-tile (g-th of the walk): row blocks (direct stores, scales to
 // LDS), column blocks into the staging pair; FLUSH 0: keep staging, 1: the
 // walk ends on the first sub-tile of a pair, 2: the pair is complete.
-template <bool ROW, bool COL, bool HALF, int FLUSH>
+// 2D scaling: the lane's 16 rows x 8 columns and its pair lane's form one
+// 16 x 16 block; one scale and multiplier serve all its elements, in both
+// outputs.
+template <bool ROW, bool COL>
+__device__ __forceinline__ void nv_step_2d(const Nv4Args &a, const NvLane &l,
+                                           const uint32_t (&w)[kRowsPerLane][4], NvStage &st,
+                                           float sg, rsrc_t rq, uint32_t qoff, int g)
+{
+    using P = NvPolicy<ROW, COL>;
+    uint32_t t = 0;
+#pragma unroll
+    for (int r = 0; r < kRowsPerLane; r++)
+#pragma unroll
+        for (int d = 0; d < 4; d++)
+            t = pk_max_u16(t, w[r][d] & 0x7FFF7FFFu);
+    const uint32_t lo = t & 0xFFFFu, hi = t >> 16;
+    const uint32_t sb = nv_scale(max_xor1(lo > hi ? lo : hi), sg);
+    const float inv = st.inv[sb];
+    if constexpr (ROW) {
+#pragma unroll
+        for (int r = 0; r < kRowsPerLane; r++) {
+            buf_store4<P::q_row>(rq, qoff + (uint32_t)(r * (a.K >> 1)), encode8_fp4(w[r], inv));
+            if ((l.cl & 1) == 0)
+                st.srow[l.row + r][l.cl >> 1] = (uint8_t)sb;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    if constexpr (COL) {
+        // re-derive the fp32 values from the packed words (see nv_step)
+        uint32_t wc[kRowsPerLane][4];
+#pragma unroll
+        for (int r = 0; r < kRowsPerLane; r++)
+#pragma unroll
+            for (int d = 0; d < 4; d++) {
+                wc[r][d] = w[r][d];
+                if constexpr (ROW)
+                    asm volatile("" : "+v"(wc[r][d]));
+            }
+        const int jr = 4 * (g & 1) + l.wave;
+#pragma unroll
+        for (int c = 0; c < kColsPerLane; c++) {
+            const int d = c >> 1;
+            uint32_t o[2];
+#pragma unroll
+            for (int q = 0; q < 2; q++)
+                o[q] = (c & 1) ? encode8_fp4_col<1>(wc, q, d, inv) : encode8_fp4_col<0>(wc, q, d, inv);
+            const int kl = l.cl * kColsPerLane + c;
+            *reinterpret_cast<uint2 *>(&st.q[kl][16 * nv_chunk(kl, jr) + 8 * l.half]) =
+                make_uint2(o[0], o[1]);
+            st.s[kl][8 * g + 2 * l.wave + l.half] = (uint8_t)sb;
+        }
+    }
+}
+
+template <bool ROW, bool COL, bool HALF, bool TWO_D, int FLUSH>
 __device__ __forceinline__ void nv_step(const Nv4Args &a, const NvLane &l,
                                         const uint32_t (&w)[kRowsPerLane][4], NvStage &st,
                                         float sg, int tm, int tk, int g)
@@ -275,6 +329,9 @@ __device__ __forceinline__ void nv_step(const Nv4Args &a, const NvLane &l,
         if (live)
             qoff = (uint32_t)(l.row * ld) + 4 * l.cl;
     }
+    if constexpr (TWO_D) {
+        nv_step_2d<ROW, COL>(a, l, w, st, sg, rq, qoff, g);
+    } else {
     // Rows go in pairs: both lanes of a row block know the block maxima of
     // rows r and r + 1; the even lane derives the scale of row r, the odd
     // lane that of row r + 1, and they swap results.
@@ -344,6 +401,7 @@ __device__ __forceinline__ void nv_step(const Nv4Args &a, const NvLane &l,
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    }
     __syncthreads();
     if constexpr (ROW)
         nv_flush_srow<P::s_row>(a, st, tm, tk);
@@ -356,7 +414,7 @@ __device__ __forceinline__ void nv_step(const Nv4Args &a, const NvLane &l,
 // with the next sub-tile's loads in flight while one is converted (as in the
 // MXFP8 cast); the transposed output leaves every second sub-tile as whole
 // 128-byte lines.
-template <bool ROW, bool COL, bool HALF>
+template <bool ROW, bool COL, bool HALF, bool TWO_D>
 __global__ __launch_bounds__(kThreads, 2) void nvfp4_kernel(Nv4Args a)
 {
     using P = NvPolicy<ROW, COL>;
@@ -383,13 +441,13 @@ __global__ __launch_bounds__(kThreads, 2) void nvfp4_kernel(Nv4Args a)
     for (; g + 1 < n; g += 2) {
         nv_load<P::x>(a, l, tm0 + g + 1, tk, wb);
         __builtin_amdgcn_sched_barrier(0);
-        nv_step<ROW, COL, HALF, 0>(a, l, wa, st, sg, tm0 + g, tk, g);
+        nv_step<ROW, COL, HALF, TWO_D, 0>(a, l, wa, st, sg, tm0 + g, tk, g);
         nv_load<P::x>(a, l, g + 2 < n ? tm0 + g + 2 : past, tk, wa);
         __builtin_amdgcn_sched_barrier(0);
-        nv_step<ROW, COL, HALF, 2>(a, l, wb, st, sg, tm0 + g + 1, tk, g + 1);
+        nv_step<ROW, COL, HALF, TWO_D, 2>(a, l, wb, st, sg, tm0 + g + 1, tk, g + 1);
     }
     if (g < n)
-        nv_step<ROW, COL, HALF, 1>(a, l, wa, st, sg, tm0 + g, tk, g);
+        nv_step<ROW, COL, HALF, TWO_D, 1>(a, l, wa, st, sg, tm0 + g, tk, g);
     if constexpr (COL)
         nv_flush_s<P::s_col>(a, st, tm0, tk, n);
 }
@@ -456,25 +514,31 @@ hipError_t launch_absmax(const uint16_t *x, int64_t n, float *amax, hipStream_t 
     return hipGetLastError();
 }
 
-template <bool ROW, bool COL>
+template <bool ROW, bool COL, bool TWO_D>
 static hipError_t launch_nv(const Nv4Args &a, hipStream_t s)
 {
     const dim3 grid((unsigned)(a.groups_m * a.tiles_k));
     if (COL && (a.M & 31) != 0)
-        hipLaunchKernelGGL((nvfp4_kernel<ROW, COL, true>), grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((nvfp4_kernel<ROW, COL, true, TWO_D>), grid, dim3(kThreads), 0, s, a);
     else
-        hipLaunchKernelGGL((nvfp4_kernel<ROW, COL, false>), grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((nvfp4_kernel<ROW, COL, false, TWO_D>), grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_nvfp4(unsigned axis, const Nv4Args &a, hipStream_t s)
+template <bool TWO_D>
+static hipError_t launch_nv_axis(unsigned axis, const Nv4Args &a, hipStream_t s)
 {
     switch (axis) {
-    case 1u: return launch_nv<true, false>(a, s);
-    case 2u: return launch_nv<false, true>(a, s);
-    case 3u: return launch_nv<true, true>(a, s);
+    case 1u: return launch_nv<true, false, TWO_D>(a, s);
+    case 2u: return launch_nv<false, true, TWO_D>(a, s);
+    case 3u: return launch_nv<true, true, TWO_D>(a, s);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_nvfp4(unsigned axis, bool two_d, const Nv4Args &a, hipStream_t s)
+{
+    return two_d ? launch_nv_axis<true>(axis, a, s) : launch_nv_axis<false>(axis, a, s);
 }
 
 }  // namespace mxk

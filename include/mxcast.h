@@ -184,6 +184,20 @@ mx_status nvfp4_quantize_transpose(const void *x, int64_t M, int64_t K, const fl
                                    uint8_t *q_row, uint8_t *s_row, uint8_t *q_col, uint8_t *s_col,
                                    float *global_scale_out, hipStream_t stream);
 
+/*
+ * NVFP4 quantize-transpose with 2D scaling (the "nvfp42d" rows of the
+ * quantize-transpose table): one E4M3 scale per 16 x 16 block of x, from the
+ * block's amax over its 256 elements by the same chain as above; every
+ * element is coded with its block's multiplier.  Arguments, layouts and
+ * errors exactly as for nvfp4_quantize_transpose: the block's scale is
+ * written for each of its 16 rows in s_row and for each of its 16 columns in
+ * s_col, so a consumer of the 1D layouts reads 2D-scaled data unchanged.
+ */
+mx_status nvfp4_quantize_transpose_2d(const void *x, int64_t M, int64_t K, const float *amax,
+                                      unsigned axis_mask,
+                                      uint8_t *q_row, uint8_t *s_row, uint8_t *q_col,
+                                      uint8_t *s_col, float *global_scale_out, hipStream_t stream);
+
 /* Static string naming a status code. */
 const char *mx_status_str(int status);
 

@@ -71,15 +71,16 @@ def test_c4_gated_8192(act):
     mx_outputs_equal(g, o, f"C4 act {act}")
 
 
-def test_c5_nvfp4_16384():
+@pytest.mark.parametrize("two_d", [False, True])
+def test_c5_nvfp4_16384(two_d):
     x = W.make("c5_nvfp4_16384")
     xd = to_dev(x)
     amax = mx.mx_absmax_bf16(xd)
-    g = mx.nvfp4_quantize_transpose(xd, amax)
+    g = mx.nvfp4_quantize_transpose(xd, amax, two_d=two_d)
     torch.cuda.synchronize()
-    o = O.nvfp4_quantize_transpose(x)
+    o = O.nvfp4_quantize_transpose(x, two_d=two_d)
     assert g["sg"].item() == o["sg"]
-    mx_outputs_equal(g, o, "C5 nvfp4")
+    mx_outputs_equal(g, o, f"C5 nvfp4 two_d={two_d}")
 
 
 def test_dsilu_dbias_8192():

@@ -17,15 +17,15 @@ from gpu_util import assert_same, mx_outputs_equal, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def run_both(x, axis=3, tensor_amax=None):
+def run_both(x, axis=3, tensor_amax=None, two_d=False):
     xd = to_dev(x)
     if tensor_amax is None:
         amax = mx.mx_absmax_bf16(xd)
     else:
         amax = torch.tensor([tensor_amax], dtype=torch.float32, device="cuda")
-    g = mx.nvfp4_quantize_transpose(xd, amax, axis=axis)
+    g = mx.nvfp4_quantize_transpose(xd, amax, axis=axis, two_d=two_d)
     torch.cuda.synchronize()
-    o = O.nvfp4_quantize_transpose(x, axis=axis, tensor_amax=tensor_amax)
+    o = O.nvfp4_quantize_transpose(x, axis=axis, tensor_amax=tensor_amax, two_d=two_d)
     assert g["sg"].item() == o["sg"]
     return g, o
 
@@ -88,3 +88,29 @@ def test_every_row_scale_code():
     g, o = run_both(W.bf16_bits(x.astype(np.float32)))
     assert set(np.unique(o["s_row"]).tolist()) == set(range(127))
     mx_outputs_equal(g, o, "nvfp4 scale sweep")
+
+
+# --- 2D (16 x 16 block) scaling ------------------------------------------------
+
+@pytest.mark.parametrize("axis", [1, 2, 3])
+@pytest.mark.parametrize("M,K", [(16, 16), (48, 80), (128, 256), (144, 528), (400, 784)])
+def test_2d_random_shapes(M, K, axis):
+    x = W.student_t_rows(M, K, seed=2100 + M + K)
+    g, o = run_both(x, axis, two_d=True)
+    mx_outputs_equal(g, o, f"nvfp4 2d {M}x{K} axis {axis}")
+
+
+def test_2d_every_scale_code_and_tiny_global_scale():
+    rng = np.random.default_rng(46)
+    M, K = 256, 2048
+    t = np.linspace(0, 1, (M // 16) * (K // 16)).reshape(M // 16, K // 16)
+    scale = np.repeat(np.repeat(2.0 ** (-19 * t), 16, axis=0), 16, axis=1)
+    x = W.bf16_bits((rng.standard_normal((M, K)) * scale).astype(np.float32))
+    g, o = run_both(x, two_d=True)
+    assert set(np.unique(o["s_row"]).tolist()) == set(range(127))
+    mx_outputs_equal(g, o, "nvfp4 2d scale sweep")
+    x = W.normal(32, 64, seed=47, sigma=1e-37)
+    x[0:16, 0:16] = 0
+    x[1, 20] = 0x8000
+    g, o = run_both(x, two_d=True)
+    mx_outputs_equal(g, o, "nvfp4 2d tiny S_g")

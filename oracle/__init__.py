@@ -26,6 +26,7 @@ _i64 = ctypes.c_int64
 FUSE_NONE, FUSE_GELU, FUSE_DGELU, FUSE_DSILU, FUSE_DBIAS = 0, 1, 2, 3, 0x10
 GATED_SWIGLU, GATED_GEGLU = 1, 2
 ROWWISE, COLWISE = 1, 2
+ELEM_E5M2, SCALE_ROUND_UP = 4, 8     # variant flags OR-ed into axis (MXFP8 only)
 
 
 def lib():
@@ -48,6 +49,16 @@ def lib():
         L.orc_e2m1_encode.argtypes = [ctypes.c_double]
         L.orc_e8m0_byte.restype = ctypes.c_uint8
         L.orc_e8m0_byte.argtypes = [ctypes.c_double]
+        L.orc_e8m0_byte_mode.restype = ctypes.c_uint8
+        L.orc_e8m0_byte_mode.argtypes = [ctypes.c_double, ctypes.c_uint]
+        L.orc_e5m2_value.restype = ctypes.c_double
+        L.orc_e5m2_value.argtypes = [ctypes.c_uint8]
+        L.orc_e5m2_encode.restype = ctypes.c_uint8
+        L.orc_e5m2_encode.argtypes = [ctypes.c_double]
+        L.orc_mx_block_mode.restype = None
+        L.orc_mx_block_mode.argtypes = [_f64p, ctypes.c_int, _u8p, _i64, _u8p, ctypes.c_uint]
+        L.orc_e5m2_encode_array.restype = None
+        L.orc_e5m2_encode_array.argtypes = [_f64p, _u8p, _i64]
         L.orc_e8m0_value.restype = ctypes.c_double
         L.orc_e8m0_value.argtypes = [ctypes.c_uint8]
         L.orc_mx_block.restype = None
@@ -150,6 +161,26 @@ def e8m0_byte(amax: float) -> int:
     return lib().orc_e8m0_byte(amax)
 
 
+def e8m0_byte_mode(amax: float, mode: int) -> int:
+    """E8M0 byte under the variant flags (ELEM_E5M2, SCALE_ROUND_UP)."""
+    return lib().orc_e8m0_byte_mode(amax, mode)
+
+
+def e5m2_value(c: int) -> float:
+    return lib().orc_e5m2_value(c)
+
+
+def e5m2_encode(v: float) -> int:
+    return lib().orc_e5m2_encode(v)
+
+
+def e5m2_encode_array(v) -> np.ndarray:
+    v = _c(np.asarray(v, dtype=np.float64), np.float64)
+    out = np.empty(v.shape, np.uint8)
+    lib().orc_e5m2_encode_array(_p(v, _f64p), _p(out, _u8p), v.size)
+    return out
+
+
 def e8m0_value(b: int) -> float:
     return lib().orc_e8m0_value(b)
 
@@ -175,12 +206,16 @@ def bf16_round_array(v) -> np.ndarray:
     return out
 
 
-def mx_block(values):
-    """One MX block: exact values -> (E4M3 codes, E8M0 byte)."""
+def mx_block(values, mode=0):
+    """One MX block: exact values -> (element codes, E8M0 byte); mode holds the
+    variant flags (ELEM_E5M2, SCALE_ROUND_UP), 0 = E4M3 with the floor rule."""
     v = _c(np.asarray(values, dtype=np.float64), np.float64)
     q = np.empty(v.size, np.uint8)
     s = np.empty(1, np.uint8)
-    lib().orc_mx_block(_p(v, _f64p), v.size, _p(q, _u8p), 1, _p(s, _u8p))
+    if mode:
+        lib().orc_mx_block_mode(_p(v, _f64p), v.size, _p(q, _u8p), 1, _p(s, _u8p), mode)
+    else:
+        lib().orc_mx_block(_p(v, _f64p), v.size, _p(q, _u8p), 1, _p(s, _u8p))
     return q, int(s[0])
 
 

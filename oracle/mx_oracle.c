@@ -37,6 +37,11 @@
  *       derivative of the same forward sequences, in the order written in
  *       orc_preop() and orc_gated_bwd().
  *   R6  NVFP4 per the chain in nvfp4_block().
+ *   R7  format variants (flags beside the axis bits): E5M2 elements (bias 15,
+ *       max 57344, emax 15) in place of E4M3, and the round-up scale rule,
+ *       byte = ceil(log2(amax / max_elem)) + 127: the smallest power of two
+ *       that brings amax inside the element range, so nothing saturates.
+ *       The floor rule of R1 reads emax = 15 for E5M2.
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fopenmp -shared
  * -fPIC (see build.py).  OpenMP only splits independent rows / columns /
@@ -120,6 +125,8 @@ double orc_e4m3_value(uint8_t c)
 
 static double E4M3_MAG[127];   /* magnitudes of codes 0x00..0x7E, increasing */
 static double E2M1_MAG[8];     /* magnitudes of codes 0x0..0x7, increasing */
+static double E5M2_MAG[124];
+double orc_e5m2_value(uint8_t c);
 
 double orc_e2m1_value(uint8_t c)
 {
@@ -138,6 +145,8 @@ static void init_tables(void)
         E4M3_MAG[c] = orc_e4m3_value((uint8_t)c);
     for (int c = 0; c < 8; c++)
         E2M1_MAG[c] = orc_e2m1_value((uint8_t)c);
+    for (int c = 0; c < 124; c++)
+        E5M2_MAG[c] = orc_e5m2_value((uint8_t)c);
     done = 1;
 }
 
@@ -191,6 +200,39 @@ uint8_t orc_e2m1_encode(double v)
 }
 
 /* ------------------------------------------------------------------------ */
+/* E5M2: bias 15, 0x7C = Inf, 0x7D..0x7F NaN, max finite 57344 (0x7B).        */
+/* ------------------------------------------------------------------------ */
+
+double orc_e5m2_value(uint8_t c)
+{
+    int s = c >> 7, e = (c >> 2) & 0x1F, m = c & 3;
+    double mag;
+    if (e == 31)
+        mag = m ? NAN : INFINITY;
+    else if (e == 0)
+        mag = ldexp((double)m, -16);            /* (m/4) * 2^-14 */
+    else
+        mag = ldexp(4.0 + m, e - 17);           /* (1 + m/4) * 2^(e-15) */
+    return s ? -mag : mag;
+}
+
+/* E5M2_MAG: magnitudes of codes 0x00..0x7B, increasing. */
+
+/* Nearest E5M2, ties to even code, saturating at 57344 (Inf included: the
+ * saturating conversion never makes Inf), sign kept, NaN -> 0x7F. */
+uint8_t orc_e5m2_encode(double v)
+{
+    init_tables();
+    if (isnan(v))
+        return 0x7F;
+    uint8_t sign = signbit(v) ? 0x80 : 0;
+    double a = fabs(v);
+    if (a >= 57344.0)
+        return sign | 0x7B;
+    return sign | (uint8_t)nearest_code(E5M2_MAG, 124, a);
+}
+
+/* ------------------------------------------------------------------------ */
 /* E8M0 shared scale (R1).                                                   */
 /* ------------------------------------------------------------------------ */
 
@@ -215,12 +257,51 @@ uint8_t orc_e8m0_byte(double amax)
     return (uint8_t)b;
 }
 
-/* One MX block: n values (exact doubles) -> n E4M3 codes (q[i*qstride]) and
- * the E8M0 byte.  The scale is applied as a true division by 2^(byte-127);
- * that is exact here, so it equals multiplying by the power-of-two inverse
- * (the point of "Multiply with inverse scale in loop inside of dividing",
- * body bullets). */
-void orc_mx_block(const double *v, int n, uint8_t *q, int64_t qstride, uint8_t *s)
+/* Element formats of an MX block (R7): exponent of the largest binade and
+ * the largest finite magnitude. */
+#define ORC_E5M2 4u        /* flag: E5M2 elements */
+#define ORC_ROUND_UP 8u    /* flag: round-up scale rule */
+
+static int fmt_emax(unsigned mode) { return (mode & ORC_E5M2) ? 15 : 8; }
+static double fmt_max(unsigned mode) { return (mode & ORC_E5M2) ? 57344.0 : 448.0; }
+
+/* E8M0 byte of a block under either rule (R1 / R7).
+ *   floor:    floor(log2 amax) - emax
+ *   round up: the smallest integer t with amax <= max_elem * 2^t,
+ *             i.e. ceil(log2(amax / max_elem)), found by counting up from a
+ *             value known to be too small (every comparison is exact).
+ * Biased by 127 and clamped to [0, 254]; amax = 0 -> 0; Inf / NaN -> 0xFF. */
+uint8_t orc_e8m0_byte_mode(double amax, unsigned mode)
+{
+    if (isnan(amax) || isinf(amax))
+        return 0xFF;
+    if (amax == 0.0)
+        return 0;
+    int ex;
+    frexp(amax, &ex);                  /* floor(log2 amax) = ex - 1 */
+    int t;
+    if (mode & ORC_ROUND_UP) {
+        t = (ex - 1) - fmt_emax(mode) - 1;     /* max * 2^t < 2^(ex-1) <= amax */
+        while (amax > ldexp(fmt_max(mode), t))
+            t++;
+    } else {
+        t = (ex - 1) - fmt_emax(mode);
+    }
+    int b = t + 127;
+    if (b < 0)
+        b = 0;
+    if (b > 254)
+        b = 254;
+    return (uint8_t)b;
+}
+
+/* One MX block: n values (exact doubles) -> n element codes (q[i*qstride])
+ * and the E8M0 byte; mode selects the element format and the scale rule (R7).
+ * The scale is applied as a true division by 2^(byte-127); that is exact
+ * here, so it equals multiplying by the power-of-two inverse (the point of
+ * "Multiply with inverse scale in loop inside of dividing", body bullets). */
+void orc_mx_block_mode(const double *v, int n, uint8_t *q, int64_t qstride, uint8_t *s,
+                       unsigned mode)
 {
     double amax = 0.0;
     int nonfinite = 0;
@@ -236,11 +317,18 @@ void orc_mx_block(const double *v, int n, uint8_t *q, int64_t qstride, uint8_t *
             q[i * qstride] = 0x7F;
         return;
     }
-    uint8_t b = orc_e8m0_byte(amax);
+    uint8_t b = orc_e8m0_byte_mode(amax, mode);
     double X = orc_e8m0_value(b);
     for (int i = 0; i < n; i++)
-        q[i * qstride] = orc_e4m3_encode(v[i] / X);
+        q[i * qstride] = (mode & ORC_E5M2) ? orc_e5m2_encode(v[i] / X)
+                                           : orc_e4m3_encode(v[i] / X);
     *s = b;
+}
+
+/* The default block: E4M3 elements, floor rule (R1, R2). */
+void orc_mx_block(const double *v, int n, uint8_t *q, int64_t qstride, uint8_t *s)
+{
+    orc_mx_block_mode(v, n, q, qstride, s, 0u);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -429,7 +517,8 @@ int orc_gated_bwd(int act, uint16_t gate, uint16_t lin, uint16_t grad, uint16_t 
 /* Row-wise and column-wise MX quantisation of the bf16 tensor y[M][K].
  *   rows: q_row[M][K], s_row[M][K/32]   (blocks of 32 along K)
  *   cols: q_col[K][M], s_col[K][M/32]   (blocks of 32 along M, stored as the
- *         row-wise output of the transpose, R4) */
+ *         row-wise output of the transpose, R4)
+ * axis bits 0, 1 select the outputs; ORC_E5M2 / ORC_ROUND_UP the variant. */
 static void mx_tensor(const uint16_t *y, int64_t M, int64_t K, unsigned axis,
                       uint8_t *q_row, uint8_t *s_row, uint8_t *q_col, uint8_t *s_col)
 {
@@ -440,7 +529,8 @@ static void mx_tensor(const uint16_t *y, int64_t M, int64_t K, unsigned axis,
             for (int64_t j = 0; j < K / 32; j++) {
                 for (int i = 0; i < 32; i++)
                     v[i] = orc_bf16_value(y[m * K + 32 * j + i]);
-                orc_mx_block(v, 32, q_row + m * K + 32 * j, 1, s_row + m * (K / 32) + j);
+                orc_mx_block_mode(v, 32, q_row + m * K + 32 * j, 1, s_row + m * (K / 32) + j,
+                                  axis);
             }
         }
     }
@@ -451,7 +541,8 @@ static void mx_tensor(const uint16_t *y, int64_t M, int64_t K, unsigned axis,
             for (int64_t j = 0; j < M / 32; j++) {
                 for (int i = 0; i < 32; i++)
                     v[i] = orc_bf16_value(y[(32 * j + i) * K + k]);
-                orc_mx_block(v, 32, q_col + k * M + 32 * j, 1, s_col + k * (M / 32) + j);
+                orc_mx_block_mode(v, 32, q_col + k * M + 32 * j, 1, s_col + k * (M / 32) + j,
+                                  axis);
             }
         }
     }
@@ -470,7 +561,8 @@ static void column_sums(const uint16_t *y, int64_t M, int64_t K, float *dbias)
     }
 }
 
-/* fusion: low nibble = pre-op (0 none, 1 GELU, 2 dGELU, 3 dSiLU), bit 0x10 = dbias.
+/* axis: bit 0 rows, bit 1 columns, ORC_E5M2 / ORC_ROUND_UP variants (R7).
+ * fusion: low nibble = pre-op (0 none, 1 GELU, 2 dGELU, 3 dSiLU), bit 0x10 = dbias.
  * y_out (optional, [M][K]) receives the fused bf16 tensor. */
 int orc_mx_quantize(const uint16_t *x, const uint16_t *grad, int64_t M, int64_t K,
                     unsigned axis, int fusion, uint8_t *q_row, uint8_t *s_row,
@@ -479,7 +571,7 @@ int orc_mx_quantize(const uint16_t *x, const uint16_t *grad, int64_t M, int64_t 
     int pre = fusion & 0xF;
     if (M <= 0 || K <= 0 || M % 32 || K % 32)
         return ORC_ERR_SHAPE;
-    if (pre > 3 || (fusion & ~0x1F) || (axis & ~3u))
+    if (pre > 3 || (fusion & ~0x1F) || (axis & ~15u))
         return ORC_ERR_ENUM;
     init_tables();
     const uint16_t *y = x;
@@ -510,7 +602,7 @@ int orc_mx_quantize_gated(const uint16_t *x, int64_t M, int64_t N, unsigned axis
 {
     if (M <= 0 || N <= 0 || M % 32 || N % 32)
         return ORC_ERR_SHAPE;
-    if ((act != 1 && act != 2) || (axis & ~3u))
+    if ((act != 1 && act != 2) || (axis & ~15u))
         return ORC_ERR_ENUM;
     init_tables();
     uint16_t *y = y_out ? y_out : (uint16_t *)malloc((size_t)(M * N) * 2);
@@ -534,7 +626,7 @@ int orc_mx_quantize_dgated(const uint16_t *grad, const uint16_t *x, int64_t M, i
 {
     if (M <= 0 || N <= 0 || M % 32 || N % 32)
         return ORC_ERR_SHAPE;
-    if ((act != 1 && act != 2) || (axis & ~3u))
+    if ((act != 1 && act != 2) || (axis & ~15u))
         return ORC_ERR_ENUM;
     init_tables();
     uint16_t *y = y_out ? y_out : (uint16_t *)malloc((size_t)(M * 2 * N) * 2);
@@ -713,6 +805,14 @@ void orc_e4m3_encode_array(const double *v, uint8_t *out, int64_t n)
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; i++)
         out[i] = orc_e4m3_encode(v[i]);
+}
+
+void orc_e5m2_encode_array(const double *v, uint8_t *out, int64_t n)
+{
+    init_tables();
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++)
+        out[i] = orc_e5m2_encode(v[i]);
 }
 
 void orc_e2m1_encode_array(const double *v, uint8_t *out, int64_t n)

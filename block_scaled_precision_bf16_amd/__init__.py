@@ -11,6 +11,8 @@ The same names as the C ABI:
     mx_status_str, mx_abi_version
 take torch tensors (bf16 inputs, or int16/uint16 holding bf16 bits, on a ROCm
 device) and return dicts of uint8 / float32 torch tensors on the same device.
+The MXFP8 casts take the format flags ELEM_E5M2 / SCALE_ROUND_UP OR-ed into
+`axis`, as the C ABI does.
 `lib()` returns the raw ctypes library for callers that pass pointers
 themselves.
 """
@@ -23,6 +25,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmxcast.so")
 
 ROWWISE, COLWISE = 1, 2
+ELEM_E5M2, SCALE_ROUND_UP = 4, 8     # MXFP8 format flags, OR-ed into axis
 FUSE_NONE, FUSE_GELU, FUSE_DGELU, FUSE_DSILU, FUSE_DBIAS = 0, 1, 2, 3, 0x10
 GATED_SWIGLU, GATED_GEGLU = 1, 2
 OP_GATED, OP_DGATED = 0x100, 0x200

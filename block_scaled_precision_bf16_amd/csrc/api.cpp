@@ -89,6 +89,17 @@ mx_status from_hip(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; 
 }  // namespace
 
 // NVFP4 quantize-transpose with 1D (two_d = false) or 16 x 16 block scaling.
+// The MXFP8 entry points' axis_mask: at least one of the two axis bits, plus
+// optionally the format flags (E5M2 elements, round-up scale rule).
+static const unsigned kFmtBits = MX_ELEM_E5M2 | MX_SCALE_ROUND_UP;
+static_assert(MX_ELEM_E5M2 == (unsigned)mxk::kFmtE5M2 && MX_SCALE_ROUND_UP == (unsigned)mxk::kFmtRoundUp,
+              "format flags are passed to the kernels unchanged");
+
+static bool mx_mode_ok(unsigned axis_mask)
+{
+    return (axis_mask & 3u) != 0 && (axis_mask & ~(3u | kFmtBits)) == 0;
+}
+
 static mx_status nvfp4_impl(bool two_d, const void *x, int64_t M, int64_t K, const float *amax,
                             unsigned axis_mask, uint8_t *q_row, uint8_t *s_row, uint8_t *q_col,
                             uint8_t *s_col, float *global_scale_out, hipStream_t stream)
@@ -152,7 +163,7 @@ const char *mx_status_str(int s)
 
 size_t mx_quantize_workspace_size(int64_t M, int64_t K, unsigned axis_mask, int fusion)
 {
-    if (!(fusion & MX_FUSE_DBIAS) || !shape_ok(M, K, 32) || axis_mask == 0 || (axis_mask & ~3u) ||
+    if (!(fusion & MX_FUSE_DBIAS) || !shape_ok(M, K, 32) || !mx_mode_ok(axis_mask) ||
         (fusion & ~0x1F) || (fusion & 0xF) > MX_FUSE_DSILU)
         return 0;
     return dbias_workspace(M, K, cast_op(fusion & 0xF));
@@ -164,7 +175,7 @@ mx_status mx_quantize(const void *x, const void *grad, int64_t M, int64_t K, uns
 {
     const int pre = fusion & 0xF;
     const bool want_dbias = (fusion & MX_FUSE_DBIAS) != 0;
-    if (axis_mask == 0 || (axis_mask & ~3u) || (fusion & ~0x1F) || pre > MX_FUSE_DSILU)
+    if (!mx_mode_ok(axis_mask) || (fusion & ~0x1F) || pre > MX_FUSE_DSILU)
         return MX_ERR_ENUM;
     const bool has_grad = pre == MX_FUSE_DGELU || pre == MX_FUSE_DSILU;
     const bool row = axis_mask & MX_ROWWISE, col = axis_mask & MX_COLWISE;
@@ -205,7 +216,8 @@ mx_status mx_quantize(const void *x, const void *grad, int64_t M, int64_t K, uns
     a.s_col = s_col;
     a.partials = want_dbias ? static_cast<float *>(workspace) : nullptr;
     set_walk(a, op, want_dbias);
-    mx_status st = from_hip(mxk::launch_mx_cast(op, axis_mask, want_dbias, a, stream));
+    mx_status st = from_hip(mxk::launch_mx_cast(op, axis_mask & 3u, axis_mask & kFmtBits,
+                                                want_dbias, a, stream));
     if (st != MX_OK || !want_dbias)
         return st;
     return from_hip(mxk::launch_dbias_reduce(a.partials, a.groups_m, K, dbias, stream));
@@ -215,7 +227,7 @@ mx_status mx_quantize_gated(const void *x, int64_t M, int64_t N, unsigned axis_m
                             uint8_t *q_row, uint8_t *s_row, uint8_t *q_col, uint8_t *s_col,
                             hipStream_t stream)
 {
-    if (axis_mask == 0 || (axis_mask & ~3u) || (act != MX_GATED_SWIGLU && act != MX_GATED_GEGLU))
+    if (!mx_mode_ok(axis_mask) || (act != MX_GATED_SWIGLU && act != MX_GATED_GEGLU))
         return MX_ERR_ENUM;
     const bool row = axis_mask & MX_ROWWISE, col = axis_mask & MX_COLWISE;
     if (!x || (row && (!q_row || !s_row)) || (col && (!q_col || !s_col)))
@@ -247,14 +259,15 @@ mx_status mx_quantize_gated(const void *x, int64_t M, int64_t N, unsigned axis_m
     a.partials = nullptr;
     const int op = act == MX_GATED_SWIGLU ? mxk::OP_SWIGLU : mxk::OP_GEGLU;
     set_walk(a, op, false);
-    return from_hip(mxk::launch_mx_cast(op, axis_mask, false, a, stream));
+    return from_hip(
+        mxk::launch_mx_cast(op, axis_mask & 3u, axis_mask & kFmtBits, false, a, stream));
 }
 
 mx_status mx_quantize_dgated(const void *grad, const void *x, int64_t M, int64_t N,
                              unsigned axis_mask, int act, uint8_t *q_row, uint8_t *s_row,
                              uint8_t *q_col, uint8_t *s_col, hipStream_t stream)
 {
-    if (axis_mask == 0 || (axis_mask & ~3u) || (act != MX_GATED_SWIGLU && act != MX_GATED_GEGLU))
+    if (!mx_mode_ok(axis_mask) || (act != MX_GATED_SWIGLU && act != MX_GATED_GEGLU))
         return MX_ERR_ENUM;
     const bool row = axis_mask & MX_ROWWISE, col = axis_mask & MX_COLWISE;
     if (!grad || !x || (row && (!q_row || !s_row)) || (col && (!q_col || !s_col)))
@@ -287,7 +300,8 @@ mx_status mx_quantize_dgated(const void *grad, const void *x, int64_t M, int64_t
     a.partials = nullptr;
     const int op = act == MX_GATED_SWIGLU ? mxk::OP_DSWIGLU : mxk::OP_DGEGLU;
     set_walk(a, op, false);
-    return from_hip(mxk::launch_mx_cast(op, axis_mask, false, a, stream));
+    return from_hip(
+        mxk::launch_mx_cast(op, axis_mask & 3u, axis_mask & kFmtBits, false, a, stream));
 }
 
 mx_status mx_fused_values(const void *x, const void *grad, int64_t M, int64_t K, int op, void *y,

@@ -40,19 +40,32 @@ __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b)
     return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(va, vb));
 }
 
+// Exponent of the element format's largest binade (format flags: launch.h).
+template <int FMT>
+constexpr uint32_t fmt_emax() { return (FMT & kFmtE5M2) ? 15u : 8u; }
+
 // ---------------------------------------------------------------------------
-// MXFP8 scale: E8M0 byte from the largest |bf16| of a block, given as its
+// MX scale: E8M0 byte from the largest |bf16| of a block, given as its
 // 15-bit magnitude pattern.  For a finite amax the exponent field E equals
-// floor(log2 amax) + 127 (normal) or 0 (subnormal, where the clamp applies),
-// so byte = max(E - 8, 0): 8 is the exponent of E4M3's largest binade.
+// floor(log2 amax) + 127 (normal) or 0 (subnormal, where the clamp applies).
+//   floor rule:    byte = max(E - emax, 0)
+//   round-up rule: byte = max(E - emax + (mantissa > 0x60), 0), since
+//                  ceil(log2(amax / (1.75 * 2^emax))) = E - 127 - emax exactly
+//                  when the 7-bit mantissa is at most 0x60 (1 + 96/128 = 1.75)
+//                  and one more otherwise.
 // Inf / NaN (pattern >= 0x7F80) -> 0xFF.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t e8m0_from_mag(uint32_t mag)
+template <int FMT>
+__device__ __forceinline__ uint32_t scale_byte(uint32_t mag)
 {
-    int e = (int)(mag >> 7) - 8;
+    int e = (int)(mag >> 7) - (int)fmt_emax<FMT>();
+    if constexpr ((FMT & kFmtRoundUp) != 0)
+        e += (mag & 0x7Fu) > 0x60u ? 1 : 0;
     uint32_t b = e > 0 ? (uint32_t)e : 0u;
     return mag >= 0x7F80u ? 0xFFu : b;
 }
+
+__device__ __forceinline__ uint32_t e8m0_from_mag(uint32_t mag) { return scale_byte<0>(mag); }
 
 // 2^(127 - byte) as an fp32 (a normal number for every byte <= 253): the
 // exact inverse of the block scale, so each element costs one multiply
@@ -103,12 +116,14 @@ __device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b)
 }
 
 // bf16 pattern of the largest magnitude a block with scale byte b may keep
-// before saturating: 448 * 2^(b - 127) = 1.75 * 2^(b + 8 - 127), i.e. exponent
-// field b + 8 and mantissa 0x60, duplicated into both halves.  Valid for
-// b <= 246, the largest byte a finite bf16 amax produces.
+// before saturating: max * 2^(b - 127) = 1.75 * 2^(b + emax - 127), i.e.
+// exponent field b + emax and mantissa 0x60, duplicated into both halves.
+// Valid for b <= 254 - emax, the largest byte the floor rule gives a finite
+// bf16 amax.  (Under the round-up rule nothing exceeds the limit.)
+template <int FMT = 0>
 __device__ __forceinline__ uint32_t sat_limit2(uint32_t b)
 {
-    const uint32_t l = ((b + 8u) << 7) | 0x60u;
+    const uint32_t l = ((b + fmt_emax<FMT>()) << 7) | 0x60u;
     return l | (l << 16);
 }
 
@@ -136,6 +151,34 @@ __device__ __forceinline__ uint32_t e4m3x2_scaled(uint32_t pair, float scale, ui
                                                               __builtin_bit_cast(bf16x2, pair),
                                                               scale, HI);
     return __builtin_bit_cast(uint32_t, r);
+}
+
+// The same for E5M2 elements (v_cvt_scalef32_pk_bf8_bf16: round to nearest
+// even, subnormals kept; the caller clamps to 57344 * 2^(b - 127) first under
+// the floor rule).  Checked against the nearest-E5M2 rule over every reachable
+// (element, byte) pair by the exhaustive parity tensors.
+template <bool HI>
+__device__ __forceinline__ uint32_t e5m2x2_scaled(uint32_t pair, float scale, uint32_t old)
+{
+    typedef short s16x2 __attribute__((ext_vector_type(2)));
+    const s16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(__builtin_bit_cast(s16x2, old),
+                                                              __builtin_bit_cast(bf16x2, pair),
+                                                              scale, HI);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// Element conversion of a packed bf16 pair (magnitudes mag) in the block
+// format FMT with scale byte b (operand sc = e8m0_operand(b), limit lim =
+// sat_limit2<FMT>(b)).
+template <int FMT, bool HI>
+__device__ __forceinline__ uint32_t mx_pair(uint32_t w, uint32_t mag, uint32_t lim, float sc,
+                                            uint32_t old)
+{
+    const uint32_t p = (FMT & kFmtRoundUp) ? w : clamp_pair(w, mag, lim);
+    if constexpr ((FMT & kFmtE5M2) != 0)
+        return e5m2x2_scaled<HI>(p, sc, old);
+    else
+        return e4m3x2_scaled<HI>(p, sc, old);
 }
 
 // The scale operand of the scaled converts: the E8M0 byte in the exponent field.

@@ -14,6 +14,12 @@ enum Op : int {
     OP_DSWIGLU = 6, OP_DGEGLU = 7    // gated backward: [d_gate | d_linear]
 };
 
+// MX format variants, as flags (the same bits as the ABI's flags beside the
+// axis bits): kFmtE5M2 selects E5M2 elements (bias 15, max 57344 =
+// 1.75 * 2^15) instead of E4M3 (max 448 = 1.75 * 2^8); kFmtRoundUp selects
+// the round-up E8M0 rule instead of the floor rule.
+constexpr int kFmtE5M2 = 4, kFmtRoundUp = 8;
+
 // Workgroup tile of the cast kernels.  A lane owns 16 rows x 8 columns; the
 // two halves of a wave (lanes 0-31, 32-63) own rows 0-15 and 16-31 of the
 // same 256 columns, so a wave covers 32 rows (one MXFP8 column block) and a
@@ -73,7 +79,8 @@ struct Nv4Args {
 };
 
 // op: 0 plain, 1 GELU, 2 dGELU, 3 SwiGLU, 4 GeGLU.
-hipError_t launch_mx_cast(int op, unsigned axis, bool dbias, const MxArgs &a, hipStream_t s);
+hipError_t launch_mx_cast(int op, unsigned axis, unsigned fmt, bool dbias, const MxArgs &a,
+                          hipStream_t s);
 hipError_t launch_dbias_reduce(const float *partials, int segments, int64_t K, float *dbias,
                                hipStream_t s);
 // op as above (1..7); gated ops read x[M][2K]; the gated backward ops read

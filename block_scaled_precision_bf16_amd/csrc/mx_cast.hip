@@ -1,497 +1,11 @@
-// mx_cast.hip -- MXFP8 cast kernels for gfx950: row-wise (dim0), column-wise
-// (dim1, transposed output) or both in one pass over the bf16 input,
-// optionally with a fused GELU / dGELU / SwiGLU / GeGLU pre-op and a dbias
-// column sum.  These are the kernels the TransformerEngine PR 3291 page
-// times ("MXFP8 generic quantize kernel", "MXFP8 specialized cast-only kernel
-// (bidimensional)", "MXFP8 gated (swiglu / geglu) kernel") and the torchao
-// dim1 cast of PR 12, designed here for CDNA4.
-//
-// Layout of the work: a workgroup (4 waves) converts a 128-row x 256-column
-// sub-tile at a time and walks down a 256-column strip.  A lane owns 16
-// consecutive rows x 8 consecutive columns, loaded as 16 128-bit loads;
-// lanes 0-31 of a wave hold rows 0-15 and lanes 32-63 rows 16-31 of the same
-// 256 columns, so each wave load instruction reads two 512-byte row segments
-// and a wave covers exactly one 32-row column block.  The row-wise amax spans
-// 4 lanes (4 x 8 = 32 columns), reduced with two DPP quad permutes; row
-// outputs leave as 8-byte stores (256 contiguous bytes per half-wave).  The
-// column-wise amax of a column is the max of two lanes' in-register maxima
-// (one exchange between lane l and l^32); each lane converts its own 16
-// bytes of each transposed row into an LDS staging tile, from which the
-// workgroup writes whole 128-byte lines of the transposed tensor.  Row and
-// column scales are staged in LDS as well and leave as 8-byte and 16-byte
-// pieces.  The LDS arrays are statically declared, so their addresses never
-// pass through an integer (the fix the PR 3291 page is about).
-//
-// Every element costs a packed integer clamp and half of a packed scaled
-// convert that applies the block's power-of-two scale exactly (the torchao
-// PR 12 page: divisions per element made the dim1 cast compute bound; here
-// there is not even a multiply per element).  All global memory access goes
-// through buffer resources with out-of-range offsets for masked lanes (see
-// bufio.h), so the load of the next sub-tile stays in flight while the
-// current one is converted.
+// mx_cast.hip -- the helper kernels of the MXFP8 casts (the dbias reduction
+// over strip segments and the fused-value kernel that exposes each pre-op's
+// bf16 result) and the dispatch of the cast kernel to its format's
+// instantiation.
 
-#include "bufio.h"
-#include "device_math.h"
-#include "launch.h"
+#include "mx_cast.h"
 
 namespace mxk {
-
-__device__ __forceinline__ float half_value(uint32_t w, int hi)
-{
-    return hi ? bf16_hi(w) : bf16_lo(w);
-}
-
-// Cache policy of each stream, chosen by measurement on the 16384 x 16384
-// cast: the input is read once, so its loads are non-temporal.  With both
-// outputs the transposed tile (lines and scales) is written non-temporal as
-// well and the row-wise elements with the SC1 bit; the row scales keep the
-// default policy (non-temporal row scales, 8-byte pieces of lines that other
-// workgroups complete, cost ~15%).  With one output only the loads are
-// non-temporal.  The policies change timing only, never results.
-template <int OP, bool ROW, bool COL>
-struct Policy {
-    static constexpr bool plain = OP == OP_PLAIN, both = plain && ROW && COL;
-    static constexpr int x = plain ? kNT : 0;            // input loads
-    static constexpr int q_row = both ? kSC1 : 0;        // row-wise stores
-    static constexpr int s_row = 0;
-    static constexpr int q_col = both ? kNT : 0;         // transposed stores
-    static constexpr int s_col = both ? kNT : 0;
-};
-
-// Row r's 8 elements (4 words w, magnitudes mag) with scale byte b -> 8 E4M3
-// bytes.
-__device__ __forceinline__ uint2 encode8_row(const uint32_t (&w)[4], const uint32_t (&mag)[4],
-                                             uint32_t b)
-{
-    const uint32_t lim = sat_limit2(b);
-    const float sc = e8m0_operand(b);
-    uint2 o;
-    o.x = e4m3x2_scaled<false>(clamp_pair(w[0], mag[0], lim), sc, 0u);
-    o.x = e4m3x2_scaled<true>(clamp_pair(w[1], mag[1], lim), sc, o.x);
-    o.y = e4m3x2_scaled<false>(clamp_pair(w[2], mag[2], lim), sc, 0u);
-    o.y = e4m3x2_scaled<true>(clamp_pair(w[3], mag[3], lim), sc, o.y);
-    return o;
-}
-
-// Rows 2i and 2i+1 of one column (half HI of word d) as a packed bf16 pair.
-template <int HI>
-__device__ __forceinline__ uint32_t col_pair(const uint32_t (&w)[kRowsPerLane][4], int i, int d)
-{
-    return __builtin_amdgcn_perm(w[2 * i + 1][d], w[2 * i][d], HI ? 0x07060302u : 0x05040100u);
-}
-
-// One column's 16 rows (half HI of word d) with scale byte b -> 16 E4M3 bytes,
-// row 0 in the lowest byte.
-template <int HI>
-__device__ __forceinline__ uint4 encode16_col(const uint32_t (&w)[kRowsPerLane][4], int d,
-                                              uint32_t b)
-{
-    const uint32_t lim = sat_limit2(b);
-    const float sc = e8m0_operand(b);
-    uint32_t o[4];
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const uint32_t p0 = col_pair<HI>(w, 2 * j, d), p1 = col_pair<HI>(w, 2 * j + 1, d);
-        const uint32_t t = e4m3x2_scaled<false>(clamp_pair(p0, p0 & 0x7FFF7FFFu, lim), sc, 0u);
-        o[j] = e4m3x2_scaled<true>(clamp_pair(p1, p1 & 0x7FFF7FFFu, lim), sc, t);
-    }
-    return make_uint4(o[0], o[1], o[2], o[3]);
-}
-
-// Per-lane coordinates inside a sub-tile.
-struct LaneAt {
-    int wave, half, cl;
-    int row;        // first of the lane's 16 rows inside the sub-tile
-};
-
-__device__ __forceinline__ LaneAt lane_at()
-{
-    LaneAt l;
-    l.wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    const int lane = (int)threadIdx.x & 63;
-    l.half = lane >> 5;
-    l.cl = lane & 31;
-    l.row = l.wave * (2 * kRowsPerLane) + l.half * kRowsPerLane;
-    return l;
-}
-
-// The lane's rows exist (M is a multiple of 32, so a wave is wholly inside or
-// outside) and its 8 columns exist (K is a multiple of 32, so a column group
-// of 8, a 4-lane row block and an l / l^32 pair are wholly inside or outside).
-__device__ __forceinline__ bool lane_live(const MxArgs &a, const LaneAt &l, int tm, int tk)
-{
-    return (int64_t)tm * kTileM + l.wave * 32 < a.M && (int64_t)tk * kTileK + l.cl * kColsPerLane < a.K;
-}
-
-// This lane's 16 rows x 8 columns of sub-tile (tm, tk), after the pre-op.  A
-// sub-tile outside the tensor (tm >= tiles_m) reads as zeros without memory
-// traffic, which the plain cast uses for the prefetch past a walk's end.
-template <int OP, int XA>
-__device__ __forceinline__ void load_tile(const MxArgs &a, const LaneAt &l, int tm, int tk,
-                                          uint32_t (&w)[kRowsPerLane][4])
-{
-    const bool live = lane_live(a, l, tm, tk);
-    if constexpr (OP == OP_DSWIGLU || OP == OP_DGEGLU) {
-        // output column k of [d_gate | d_linear] (each half N = lin_off wide)
-        // reads gate and grad at column n = k mod N, and, in the gate half,
-        // linear at N + n; a lane's 8 columns lie in one half (N % 32 == 0)
-        const int64_t N = a.lin_off;
-        const int64_t k = (int64_t)tk * kTileK + kColsPerLane * l.cl;
-        const bool gate_half = k < N;
-        const uint32_t n = (uint32_t)(gate_half ? k : k - N);
-        const int64_t m0 = (int64_t)tm * kTileM;
-        const rsrc_t rx = make_rsrc(a.x, 2 * m0 * a.ldx, 2 * a.M * a.ldx);
-        const rsrc_t rg = make_rsrc(a.aux, 2 * m0 * a.ldg, 2 * a.M * a.ldg);
-        const uint32_t sx = (uint32_t)(2 * a.ldx), sg = (uint32_t)(2 * a.ldg);
-        const uint32_t ox = live ? (uint32_t)l.row * sx + 2 * n : kDead;
-        const uint32_t og = live ? (uint32_t)l.row * sg + 2 * n : kDead;
-        const uint32_t ol = live && gate_half ? ox + (uint32_t)(2 * N) : kDead;
-#pragma unroll
-        for (int r = 0; r < kRowsPerLane; r++) {
-            const uint4 g = buf_load16<XA>(rx, ox + r * sx);
-            const uint4 dy = buf_load16<XA>(rg, og + r * sg);
-            const uint4 li = buf_load16<XA>(rx, ol + r * sx);
-            w[r][0] = dgated_pair<OP>(g.x, dy.x, li.x, gate_half);
-            w[r][1] = dgated_pair<OP>(g.y, dy.y, li.y, gate_half);
-            w[r][2] = dgated_pair<OP>(g.z, dy.z, li.z, gate_half);
-            w[r][3] = dgated_pair<OP>(g.w, dy.w, li.w, gate_half);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        return;
-    }
-    const int64_t tile = (int64_t)tm * kTileM * a.ldx + (int64_t)tk * kTileK;   // elements
-    const int64_t total = a.M * a.ldx;
-    const rsrc_t rx = make_rsrc(a.x, 2 * tile, 2 * total);
-    const uint32_t rs = (uint32_t)(2 * a.ldx);
-    const uint32_t off = live ? (uint32_t)l.row * rs + (uint32_t)(2 * kColsPerLane * l.cl) : kDead;
-    rsrc_t rb = rx;
-    uint32_t rbs = rs, boff = off;
-    if constexpr (OP == OP_DGELU || OP == OP_DSILU) {
-        const int64_t gtile = (int64_t)tm * kTileM * a.ldg + (int64_t)tk * kTileK;
-        rb = make_rsrc(a.aux, 2 * gtile, 2 * a.M * a.ldg);
-        rbs = (uint32_t)(2 * a.ldg);
-        boff = live ? (uint32_t)l.row * rbs + (uint32_t)(2 * kColsPerLane * l.cl) : kDead;
-    } else if constexpr (OP == OP_SWIGLU || OP == OP_GEGLU) {
-        rb = make_rsrc(a.x, 2 * (tile + a.lin_off), 2 * total);
-    }
-#pragma unroll
-    for (int r = 0; r < kRowsPerLane; r++) {
-        const uint4 v = buf_load16<XA>(rx, off + r * rs);
-        if constexpr (OP == OP_PLAIN) {
-            w[r][0] = v.x; w[r][1] = v.y; w[r][2] = v.z; w[r][3] = v.w;
-        } else {
-            uint4 b = v;   // GELU has no second operand
-            if constexpr (OP != OP_GELU)
-                b = buf_load16<XA>(rb, boff + r * rbs);
-            w[r][0] = fused_pair<OP>(v.x, b.x);
-            w[r][1] = fused_pair<OP>(v.y, b.y);
-            w[r][2] = fused_pair<OP>(v.z, b.z);
-            w[r][3] = fused_pair<OP>(v.w, b.w);
-            // one row's activation math at a time: interleaving rows only
-            // multiplies the live temporaries
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-}
-
-// Row-wise blocks of this lane's 16 rows: amax over 4 lanes x 8 columns,
-// scale, convert, store.  Column maxima are accumulated on the way.
-template <int OP, bool ROW, bool COL>
-__device__ __forceinline__ void row_pass(const MxArgs &a, const uint32_t (&w)[kRowsPerLane][4],
-                                         const LaneAt &l, int tm, int tk, bool live, uint8_t *srow,
-                                         uint32_t (&cmax)[4])
-{
-    rsrc_t rq;
-    uint32_t off = kDead;
-    if constexpr (ROW) {
-        rq = make_rsrc(a.q_row, (int64_t)tm * kTileM * a.K + (int64_t)tk * kTileK, a.M * a.K);
-        if (live)
-            off = (uint32_t)(l.row * a.K) + (uint32_t)(kColsPerLane * l.cl);
-    }
-#pragma unroll
-    for (int r = 0; r < kRowsPerLane; r++) {
-        uint32_t m[4];
-#pragma unroll
-        for (int d = 0; d < 4; d++) {
-            m[d] = w[r][d] & 0x7FFF7FFFu;
-            if constexpr (COL)
-                cmax[d] = pk_max_u16(cmax[d], m[d]);
-        }
-        if constexpr (ROW) {
-            const uint32_t t = pk_max_u16(pk_max_u16(m[0], m[1]), pk_max_u16(m[2], m[3]));
-            const uint32_t lo = t & 0xFFFFu, hi = t >> 16;
-            uint32_t mag = lo > hi ? lo : hi;
-            mag = max_xor1(mag);
-            mag = max_xor2(mag);
-            const uint32_t sb = e8m0_from_mag(mag);
-            uint2 o = encode8_row(w[r], m, sb);
-            if (sb == 0xFFu)
-                o.x = o.y = 0x7F7F7F7Fu;
-            buf_store8<Policy<OP, ROW, COL>::q_row>(rq, off + (uint32_t)(r * a.K), o);
-            if ((l.cl & 3) == 0)
-                srow[r * (kTileK / 32)] = (uint8_t)sb;
-        }
-    }
-}
-
-// LDS staging of the column-wise output.  q: one sub-tile's transposed E4M3
-// tile, q_col rows k0..k0+255, 128 bytes each (sub-tile rows m..m+127), as 8
-// chunks of 16 bytes; chunk j of row kl is stored at chunk position
-// j ^ ((kl >> 3) & 7): the 32 lanes of a half-wave write rows 8 apart (one
-// per lane), the 8 threads that read a row back read its 8 chunks, and both
-// patterns then cover all banks.  s: the column-block scales of the whole
-// strip segment the workgroup walks (4 per sub-tile), written out once.
-struct ColStage {
-    uint4 q[kTileK][kTileM / 16];            // 32 KB
-    uint8_t s[kTileK][4 * kMaxGroup];        // 16 KB
-};
-
-__device__ __forceinline__ int stage_chunk(int kl, int j) { return j ^ ((kl >> 3) & 7); }
-
-// Column-wise blocks of sub-tile g: the 32 rows of a column block are this
-// lane's 16 and those of lane l ^ 32; each lane converts its own 16 bytes of
-// each column and puts them into the staging tile.
-__device__ __forceinline__ void col_pass(ColStage &st, const uint32_t (&w)[kRowsPerLane][4],
-                                         int wave, int half, int cl, int g, uint32_t (&cmax)[4])
-{
-#pragma unroll
-    for (int d = 0; d < 4; d++)
-        cmax[d] = pk_max_u16(cmax[d], (uint32_t)__shfl_xor((int)cmax[d], 32, 64));
-#pragma unroll
-    for (int c = 0; c < kColsPerLane; c++) {
-        const int d = c >> 1, hi = c & 1;
-        const uint32_t mag = hi ? (cmax[d] >> 16) : (cmax[d] & 0xFFFFu);
-        const uint32_t sb = e8m0_from_mag(mag);
-        uint4 o = hi ? encode16_col<1>(w, d, sb) : encode16_col<0>(w, d, sb);
-        if (sb == 0xFFu)
-            o = make_uint4(0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu);
-        const int kl = cl * kColsPerLane + c;
-        st.q[kl][stage_chunk(kl, 2 * wave + half)] = o;
-        if (half == 0)
-            st.s[kl][4 * g + wave] = (uint8_t)sb;
-    }
-}
-
-// Write the staged transposed tile of sub-tile tm: thread t writes 16-byte
-// chunk t % 8 of q_col rows t / 8 + 32 i (i = 0..7), so each wave store
-// instruction covers 8 whole 128-byte lines.
-template <int AUX>
-__device__ __forceinline__ void col_flush_q(const MxArgs &a, const ColStage &st, int tm, int tk)
-{
-    const int t = (int)threadIdx.x;
-    const int jr = t & 7;
-    const int64_t mt = (int64_t)tm * kTileM;
-    const int64_t k0 = (int64_t)tk * kTileK;
-    const rsrc_t rc = make_rsrc(a.q_col, k0 * a.M + mt, a.K * a.M);
-    const bool chunk_live = mt + 16 * jr < a.M;   // M is a multiple of 32
-#pragma unroll
-    for (int i = 0; i < kTileK / 32; i++) {
-        const int kr = (t >> 3) + 32 * i;
-        const uint32_t off = chunk_live && k0 + kr < a.K ? (uint32_t)(kr * a.M) + 16 * jr : kDead;
-        buf_store16<AUX>(rc, off, st.q[kr][stage_chunk(kr, jr)]);
-    }
-}
-
-// Column scales of a strip segment in CH-byte pieces: the count / CH pieces
-// of a column go to neighbouring threads, so one store instruction touches
-// 64 CH / count lines rather than 64 (scattered partial-line stores are what
-// cost here).
-template <int AUX, int CH>
-__device__ __forceinline__ void col_flush_s_ch(const MxArgs &a, const ColStage &st, rsrc_t rs,
-                                               int64_t k0, int64_t nblk, int count)
-{
-    const int t = (int)threadIdx.x;
-    const int pieces = count / CH;                        // per column
-    for (int i = 0; i < pieces; i++) {
-        const int idx = t + kThreads * i;                 // (column, piece) pair
-        const int c = idx / pieces, q = idx - c * pieces;
-        const uint32_t off = k0 + c < a.K ? (uint32_t)(c * nblk) + CH * q : kDead;
-        const uint8_t *src = &st.s[c][CH * q];
-        if constexpr (CH == 16)
-            buf_store16<AUX>(rs, off, *reinterpret_cast<const uint4 *>(src));
-        else if constexpr (CH == 8)
-            buf_store8<AUX>(rs, off, *reinterpret_cast<const uint2 *>(src));
-        else if constexpr (CH == 4)
-            buf_store4<AUX>(rs, off, *reinterpret_cast<const uint32_t *>(src));
-        else
-            buf_store1<AUX>(rs, off, *src);
-    }
-}
-
-// Write the strip segment's column scales: 4 n bytes per column for a walk
-// of n sub-tiles, in the widest pieces (16, 8, 4 or 1 bytes) that the row
-// length of s_col, the segment's start and its length allow.
-template <int AUX>
-__device__ __forceinline__ void col_flush_s(const MxArgs &a, const ColStage &st, int rg, int tk,
-                                            int n)
-{
-    const int64_t k0 = (int64_t)tk * kTileK;
-    const int64_t nblk = a.M >> 5;                        // scales per column
-    const int64_t first = (int64_t)rg * a.group * 4;      // this segment's first block
-    const int64_t left = nblk - first;
-    const int count = (int)(left < 4 * n ? left : 4 * n);
-    const rsrc_t rs = make_rsrc(a.s_col, k0 * nblk + first, a.K * nblk);
-    const int64_t align = nblk | first | count;
-    if ((align & 15) == 0)
-        col_flush_s_ch<AUX, 16>(a, st, rs, k0, nblk, count);
-    else if ((align & 7) == 0)
-        col_flush_s_ch<AUX, 8>(a, st, rs, k0, nblk, count);
-    else if ((align & 3) == 0)
-        col_flush_s_ch<AUX, 4>(a, st, rs, k0, nblk, count);
-    else
-        col_flush_s_ch<AUX, 1>(a, st, rs, k0, nblk, count);
-}
-
-// Row scales of a sub-tile, staged as [128 rows][8 blocks] bytes: thread
-// t < 128 writes row t's 8 scale bytes with one 8-byte store (instead of 8
-// one-byte stores from 8 lanes).
-template <int AUX>
-__device__ __forceinline__ void srow_flush(const MxArgs &a, const uint8_t (&srow)[kTileM][kTileK / 32],
-                                           int tm, int tk)
-{
-    const int t = (int)threadIdx.x;
-    const int64_t row = (int64_t)tm * kTileM + t;
-    const int64_t k0 = (int64_t)tk * kTileK;
-    const int64_t nb = a.K >> 5;                          // scale bytes per row
-    const rsrc_t rs = make_rsrc(a.s_row, (int64_t)tm * kTileM * nb + (k0 >> 5), a.M * nb);
-    const uint32_t off = t < kTileM && row < a.M ? (uint32_t)(t * nb) : kDead;
-    const uint8_t *src = srow[t & (kTileM - 1)];
-    if ((a.K & 255) == 0) {
-        buf_store8<AUX>(rs, off, *reinterpret_cast<const uint2 *>(src));
-    } else {
-        const int64_t blocks = nb - (k0 >> 5);            // scale bytes of this tile inside K
-#pragma unroll
-        for (int b = 0; b < kTileK / 32; b++)
-            buf_store1<AUX>(rs, b < blocks ? off + b : kDead, src[b]);
-    }
-}
-
-// One sub-tile of the walk: row pass (direct row stores, row scales to LDS),
-// column pass into LDS, then the staged output leaves as whole lines.  Lanes
-// outside the tensor hold zeros and their stores are out of range.
-template <int OP, bool ROW, bool COL, bool DBIAS>
-__device__ __forceinline__ void tile_step(const MxArgs &a, const LaneAt &l,
-                                          const uint32_t (&w)[kRowsPerLane][4],
-                                          uint8_t (&srow)[kTileM][kTileK / 32], ColStage *st,
-                                          int tm, int tk, int g, float (&dsum)[kColsPerLane])
-{
-    const bool live = lane_live(a, l, tm, tk);
-    uint32_t cmax[4] = {0u, 0u, 0u, 0u};
-    row_pass<OP, ROW, COL>(a, w, l, tm, tk, live, &srow[l.row][l.cl >> 2], cmax);
-    if constexpr (COL)
-        col_pass(*st, w, l.wave, l.half, l.cl, g, cmax);
-    if constexpr (DBIAS) {
-#pragma unroll
-        for (int c = 0; c < kColsPerLane; c++) {
-            float acc = dsum[c];
-#pragma unroll
-            for (int r = 0; r < kRowsPerLane; r++)
-                acc += half_value(w[r][c >> 1], c & 1);
-            dsum[c] = acc;
-        }
-    }
-    __syncthreads();
-    if constexpr (COL)
-        col_flush_q<Policy<OP, ROW, COL>::q_col>(a, *st, tm, tk);
-    if constexpr (ROW)
-        srow_flush<Policy<OP, ROW, COL>::s_row>(a, srow, tm, tk);
-    __syncthreads();   // the staging buffers are reused by the next sub-tile
-}
-
-// A workgroup walks a strip of 256 columns down `group` sub-tiles of 128 rows.
-// Walking keeps the strip's column scales together (so they leave as whole
-// 64-byte chunks rather than 4-byte pieces) and, for the plain cast, lets the
-// next sub-tile's loads overlap the current sub-tile's conversion.
-// Workgroups per CU the compiler budgets registers for: the fused casts
-// without dbias are bound by their arithmetic and gain from a third
-// workgroup (at most 168 VGPRs); the plain cast keeps its double register set
-// for the prefetch, and the dbias sums and the gated backward need their
-// registers (capping them spills and measured slower).
-template <int OP, bool DBIAS>
-constexpr int min_blocks()
-{
-    return OP == OP_PLAIN || OP == OP_DSWIGLU || OP == OP_DGEGLU || DBIAS ? 1 : 3;
-}
-
-template <int OP, bool ROW, bool COL, bool DBIAS>
-__global__ __launch_bounds__(kThreads, (min_blocks<OP, DBIAS>())) void mx_cast_kernel(MxArgs a)
-{
-    const int job = xcd_tile((int)blockIdx.x, (int)gridDim.x);
-    const int rg = job / a.tiles_k;
-    const int tk = job - rg * a.tiles_k;
-    const int tm0 = rg * a.group;
-    const int n = (a.tiles_m - tm0) < a.group ? (a.tiles_m - tm0) : a.group;
-    const LaneAt l = lane_at();
-
-    __shared__ __align__(16) uint8_t srow[kTileM][kTileK / 32];
-    ColStage *st = nullptr;
-    if constexpr (COL) {
-        __shared__ ColStage stage;
-        st = &stage;
-    }
-    float dsum[kColsPerLane] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-
-    if constexpr (OP == OP_PLAIN) {
-        // Software pipeline over two register sets.  Every pass through the
-        // loop body issues the same memory instructions (the load past the
-        // walk's end reads a sub-tile outside the tensor, which costs no
-        // traffic), so the loads of the next sub-tile are never waited for
-        // early; the scheduling barriers keep each prefetch where it is
-        // issued instead of next to its first use.
-        uint32_t wa[kRowsPerLane][4], wb[kRowsPerLane][4];
-        const int past = a.tiles_m;   // a sub-tile row outside the tensor
-        load_tile<OP, Policy<OP, ROW, COL>::x>(a, l, tm0, tk, wa);
-        int g = 0;
-        for (; g + 1 < n; g += 2) {
-            load_tile<OP, Policy<OP, ROW, COL>::x>(a, l, tm0 + g + 1, tk, wb);
-            __builtin_amdgcn_sched_barrier(0);
-            tile_step<OP, ROW, COL, DBIAS>(a, l, wa, srow, st, tm0 + g, tk, g, dsum);
-            load_tile<OP, Policy<OP, ROW, COL>::x>(a, l, g + 2 < n ? tm0 + g + 2 : past, tk, wa);
-            __builtin_amdgcn_sched_barrier(0);
-            tile_step<OP, ROW, COL, DBIAS>(a, l, wb, srow, st, tm0 + g + 1, tk, g + 1, dsum);
-        }
-        if (g < n)
-            tile_step<OP, ROW, COL, DBIAS>(a, l, wa, srow, st, tm0 + g, tk, g, dsum);
-    } else {
-        uint32_t w[kRowsPerLane][4];
-        for (int g = 0; g < n; g++) {
-            load_tile<OP, Policy<OP, ROW, COL>::x>(a, l, tm0 + g, tk, w);
-            tile_step<OP, ROW, COL, DBIAS>(a, l, w, srow, st, tm0 + g, tk, g, dsum);
-        }
-    }
-    if constexpr (COL)
-        col_flush_s<Policy<OP, ROW, COL>::s_col>(a, *st, rg, tk, n);
-
-    if constexpr (DBIAS) {
-        // per-lane sums (rows in order, sub-tiles in order), then the 8
-        // lane-halves of the workgroup in order: one fp32 partial per
-        // (strip segment, column)
-        // the cross-wave sums reuse the transposed-output stage when there is
-        // one (its q part is no longer read), which keeps the LDS of a
-        // workgroup small enough for three per CU
-        float4 (*red)[kTileK / 4];
-        if constexpr (COL) {
-            red = reinterpret_cast<float4 (*)[kTileK / 4]>(&st->q[0][0]);
-        } else {
-            __shared__ float4 red_own[2 * kWaves][kTileK / 4];
-            red = red_own;
-        }
-        const int slot = 2 * l.wave + l.half;
-        red[slot][l.cl * 2] = make_float4(dsum[0], dsum[1], dsum[2], dsum[3]);
-        red[slot][l.cl * 2 + 1] = make_float4(dsum[4], dsum[5], dsum[6], dsum[7]);
-        __syncthreads();
-        const int t = (int)threadIdx.x;   // one column of the strip per thread
-        const int64_t kc = (int64_t)tk * kTileK + t;
-        if (kc < a.K) {
-            const float *flat = reinterpret_cast<const float *>(red);
-            float acc = flat[t];
-#pragma unroll
-            for (int v = 1; v < 2 * kWaves; v++)
-                acc += flat[v * kTileK + t];
-            a.partials[(int64_t)rg * a.K + kc] = acc;
-        }
-    }
-}
 
 // dbias[k] = sum over strip segments t (in order) of partials[t][k].
 __global__ __launch_bounds__(256) void dbias_reduce_kernel(const float *partials, int segments,
@@ -544,47 +58,15 @@ __global__ __launch_bounds__(256) void fused_values_kernel(const uint16_t *x, co
     *reinterpret_cast<uint4 *>(y + i) = o;
 }
 
-template <int OP, bool ROW, bool COL, bool DBIAS>
-static hipError_t launch_one(const MxArgs &a, hipStream_t s)
+hipError_t launch_mx_cast(int op, unsigned axis, unsigned fmt, bool dbias, const MxArgs &a,
+                          hipStream_t s)
 {
-    const int blocks = a.groups_m * a.tiles_k;
-    hipLaunchKernelGGL((mx_cast_kernel<OP, ROW, COL, DBIAS>), dim3(blocks), dim3(kThreads), 0,
-                       s, a);
-    return hipGetLastError();
-}
-
-template <int OP, bool DBIAS>
-static hipError_t launch_axis(unsigned axis, const MxArgs &a, hipStream_t s)
-{
-    switch (axis) {
-    case 1u: return launch_one<OP, true, false, DBIAS>(a, s);
-    case 2u: return launch_one<OP, false, true, DBIAS>(a, s);
-    case 3u: return launch_one<OP, true, true, DBIAS>(a, s);
+    switch (fmt) {
+    case 0u: return launch_mx_cast_fmt<0>(op, axis, dbias, a, s);
+    case kFmtE5M2: return launch_mx_cast_fmt<kFmtE5M2>(op, axis, dbias, a, s);
+    case kFmtRoundUp: return launch_mx_cast_fmt<kFmtRoundUp>(op, axis, dbias, a, s);
+    case kFmtE5M2 | kFmtRoundUp: return launch_mx_cast_fmt<kFmtE5M2 | kFmtRoundUp>(op, axis, dbias, a, s);
     default: return hipErrorInvalidValue;
-    }
-}
-
-hipError_t launch_mx_cast(int op, unsigned axis, bool dbias, const MxArgs &a, hipStream_t s)
-{
-    switch (op) {
-    case OP_PLAIN:
-        return dbias ? launch_axis<OP_PLAIN, true>(axis, a, s) : launch_axis<OP_PLAIN, false>(axis, a, s);
-    case OP_GELU:
-        return dbias ? launch_axis<OP_GELU, true>(axis, a, s) : launch_axis<OP_GELU, false>(axis, a, s);
-    case OP_DGELU:
-        return dbias ? launch_axis<OP_DGELU, true>(axis, a, s) : launch_axis<OP_DGELU, false>(axis, a, s);
-    case OP_SWIGLU:
-        return launch_axis<OP_SWIGLU, false>(axis, a, s);
-    case OP_GEGLU:
-        return launch_axis<OP_GEGLU, false>(axis, a, s);
-    case OP_DSILU:
-        return dbias ? launch_axis<OP_DSILU, true>(axis, a, s) : launch_axis<OP_DSILU, false>(axis, a, s);
-    case OP_DSWIGLU:
-        return launch_axis<OP_DSWIGLU, false>(axis, a, s);
-    case OP_DGEGLU:
-        return launch_axis<OP_DGEGLU, false>(axis, a, s);
-    default:
-        return hipErrorInvalidValue;
     }
 }
 

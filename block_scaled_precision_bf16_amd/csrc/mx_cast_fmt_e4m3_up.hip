@@ -1,0 +1,6 @@
+// mx_cast_fmt_e4m3_up.hip -- the MXFP8 cast kernel instantiated for E4M3 elements, round-up scale rule.
+#include "mx_cast.h"
+
+namespace mxk {
+template hipError_t launch_mx_cast_fmt<kFmtRoundUp>(int, unsigned, bool, const MxArgs &, hipStream_t);
+}  // namespace mxk

@@ -1,0 +1,6 @@
+// mx_cast_fmt_e5m2.hip -- the MXFP8 cast kernel instantiated for E5M2 elements, floor scale rule.
+#include "mx_cast.h"
+
+namespace mxk {
+template hipError_t launch_mx_cast_fmt<kFmtE5M2>(int, unsigned, bool, const MxArgs &, hipStream_t);
+}  // namespace mxk

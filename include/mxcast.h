@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MXCAST_ABI_VERSION 2
+#define MXCAST_ABI_VERSION 3
 
 typedef enum mx_status {
     MX_OK = 0,
@@ -79,6 +79,25 @@ typedef enum mx_status {
 #define MX_ROWWISE 1u       /* blocks along K: q_row[M][K], s_row[M][K/32]    */
 #define MX_COLWISE 2u       /* blocks along M, transposed outputs             */
 
+/*
+ * Format flags, OR-ed into the axis_mask of the three MXFP8 casts
+ * (mx_quantize, mx_quantize_gated, mx_quantize_dgated; not NVFP4).  The
+ * pages name the MXFP8 cast without fixing its element format or scale rule
+ * (TransformerEngine PR 3291, table "MXFP8 generic quantize kernel"); the
+ * default is E4M3 elements with the floor rule, and these select the other
+ * choices of the OCP MX format family:
+ *   MX_ELEM_E5M2       E5M2 elements (bias 15, max 57344, round to nearest
+ *                      even, saturating) instead of E4M3 (max 448); the
+ *                      floor rule becomes byte = floor(log2 amax) - 15 + 127.
+ *   MX_SCALE_ROUND_UP  byte = ceil(log2(amax / max_elem)) + 127, the smallest
+ *                      power-of-two scale under which no element saturates,
+ *                      instead of floor(log2 amax) - emax + 127.
+ * Bytes clamp to [0, 254]; a block holding Inf or NaN gets scale 0xFF and
+ * elements 0x7F under every choice.  Output layouts are unchanged.
+ */
+#define MX_ELEM_E5M2 4u
+#define MX_SCALE_ROUND_UP 8u
+
 /* fusion: a pre-op in the low bits, optionally OR-ed with MX_FUSE_DBIAS */
 #define MX_FUSE_NONE 0
 #define MX_FUSE_GELU 1      /* y = GELU(x)                                    */
@@ -91,12 +110,14 @@ typedef enum mx_status {
 #define MX_GATED_GEGLU 2    /* y = gelu(gate) * linear                        */
 
 /*
- * MXFP8 cast of x[M][K] (bf16), block size 32.
+ * MXFP8 cast of x[M][K] (bf16), block size 32.  Element bytes are E4M3
+ * unless axis_mask holds MX_ELEM_E5M2.
  *   x        device, bf16 [M][K]
  *   grad     device, bf16 [M][K]; required for MX_FUSE_DGELU / DSILU, else
  *            ignored
  *   M, K     rows, columns; positive multiples of 32, each <= 2^23, M*K <= 2^40
- *   axis_mask  MX_ROWWISE, MX_COLWISE or both (one pass over x)
+ *   axis_mask  MX_ROWWISE, MX_COLWISE or both (one pass over x), optionally
+ *            with the format flags MX_ELEM_E5M2 / MX_SCALE_ROUND_UP
  *   fusion   MX_FUSE_NONE | GELU | DGELU | DSILU, optionally | MX_FUSE_DBIAS
  *   q_row, s_row  E4M3 [M][K] and E8M0 [M][K/32]; required iff MX_ROWWISE
  *   q_col, s_col  E4M3 [K][M] and E8M0 [K][M/32]; required iff MX_COLWISE
@@ -122,6 +143,7 @@ size_t mx_quantize_workspace_size(int64_t M, int64_t K, unsigned axis_mask, int 
  * Gated MXFP8 cast.  x is bf16 [M][2N] holding [gate | linear] (gate =
  * columns 0..N-1); the quantised tensor is y[M][N] = act(gate) * linear,
  * block size 32, M and N positive multiples of 32, M <= 2^23, 2N <= 2^23.
+ * axis_mask as for mx_quantize (format flags included).
  *   q_row, s_row  E4M3 [M][N], E8M0 [M][N/32]   (iff MX_ROWWISE)
  *   q_col, s_col  E4M3 [N][M], E8M0 [N][M/32]   (iff MX_COLWISE)
  */
@@ -137,7 +159,8 @@ mx_status mx_quantize_gated(const void *x, int64_t M, int64_t N, unsigned axis_m
  * tensor is dx[M][2N] = [d_gate | d_linear]:
  *   d_gate   = fl32(fl32(a' * grad) * linear),   d_linear = fl32(a * grad),
  * each rounded once to bf16; block size 32 along 2N (row-wise) and M.
- * M, N positive multiples of 32, M <= 2^23, 2N <= 2^23.
+ * M, N positive multiples of 32, M <= 2^23, 2N <= 2^23.  axis_mask as for
+ * mx_quantize (format flags included).
  *   q_row, s_row  E4M3 [M][2N], E8M0 [M][2N/32]   (iff MX_ROWWISE)
  *   q_col, s_col  E4M3 [2N][M], E8M0 [2N][M/32]   (iff MX_COLWISE)
  * Errors as for mx_quantize_gated.

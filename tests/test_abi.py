@@ -41,7 +41,7 @@ def header_abi_version():
 
 
 def test_version_and_status_strings():
-    assert mx.mx_abi_version() == header_abi_version() == 2
+    assert mx.mx_abi_version() == header_abi_version() == 3
     for code in range(9):
         assert mx.mx_status_str(code).startswith("MX_")
     assert "unknown" in mx.mx_status_str(99)
@@ -73,6 +73,8 @@ def test_workspace_size():
     assert ws(48, 64, 3, mx.FUSE_DBIAS) == 0      # invalid shape
     assert ws(64, 64, 0, mx.FUSE_DBIAS) == 0      # invalid axis
     assert ws(64, 64, 3, 0x14) == 0               # invalid pre-op
+    assert ws(8192, 8192, 3 | mx.ELEM_E5M2 | mx.SCALE_ROUND_UP, mx.FUSE_DBIAS) == 16 * 8192 * 4
+    assert ws(64, 64, 0x23, mx.FUSE_DBIAS) == 0   # unknown flag
 
 
 class Bufs:
@@ -119,7 +121,11 @@ NULL = ctypes.c_void_p(0)
 
 @pytest.mark.parametrize("kw,code", [
     (dict(axis=0), mx.MX_ERR_ENUM),
-    (dict(axis=4), mx.MX_ERR_ENUM),
+    (dict(axis=4), mx.MX_ERR_ENUM),            # a format flag without an axis
+    (dict(axis=12), mx.MX_ERR_ENUM),
+    (dict(axis=0x13), mx.MX_ERR_ENUM),
+    (dict(axis=3 | mx.ELEM_E5M2 | mx.SCALE_ROUND_UP, x=NULL), mx.MX_ERR_NULL),  # flags accepted
+    (dict(axis=1 | mx.ELEM_E5M2, M=48), mx.MX_ERR_SHAPE),
     (dict(fusion=5), mx.MX_ERR_ENUM),
     (dict(fusion=0x20), mx.MX_ERR_ENUM),
     (dict(fusion=4), mx.MX_ERR_ENUM),
@@ -167,7 +173,8 @@ def test_gated_and_fused_values_reject():
                                          kw.get("q_col", b.p("q_col")), kw.get("s_col", b.p("s_col")),
                                          None)
     assert g(act=0) == mx.MX_ERR_ENUM and g(act=3) == mx.MX_ERR_ENUM
-    assert g(axis=0) == mx.MX_ERR_ENUM
+    assert g(axis=0) == mx.MX_ERR_ENUM and g(axis=8) == mx.MX_ERR_ENUM and g(axis=0x23) == mx.MX_ERR_ENUM
+    assert g(axis=3 | mx.ELEM_E5M2 | mx.SCALE_ROUND_UP, x=NULL) == mx.MX_ERR_NULL
     assert g(x=NULL) == mx.MX_ERR_NULL
     assert g(N=48) == mx.MX_ERR_SHAPE and g(M=16) == mx.MX_ERR_SHAPE
     assert g(x=b.p("x", 4)) == mx.MX_ERR_ALIGN
@@ -193,6 +200,7 @@ def test_dgated_and_backward_values_reject():
                                           kw.get("s_row", b.p("s_row")), kw.get("q_col", b.p("q_col")),
                                           kw.get("s_col", b.p("s_col")), None)
     assert d(act=0) == mx.MX_ERR_ENUM and d(act=3) == mx.MX_ERR_ENUM and d(axis=4) == mx.MX_ERR_ENUM
+    assert d(axis=0x43) == mx.MX_ERR_ENUM and d(axis=2 | mx.ELEM_E5M2, x=NULL) == mx.MX_ERR_NULL
     assert d(g=NULL) == mx.MX_ERR_NULL and d(x=NULL) == mx.MX_ERR_NULL
     assert d(axis=1, s_row=NULL) == mx.MX_ERR_NULL
     assert d(N=48) == mx.MX_ERR_SHAPE and d(M=0) == mx.MX_ERR_SHAPE
@@ -217,6 +225,8 @@ def test_nvfp4_and_absmax_reject():
                                                 kw.get("s_col", b.p("s_col")),
                                                 kw.get("sg", NULL), None)
     assert n(axis=0) == mx.MX_ERR_ENUM
+    assert n(axis=3 | mx.ELEM_E5M2) == mx.MX_ERR_ENUM      # NVFP4 has no format flags
+    assert n(axis=1 | mx.SCALE_ROUND_UP) == mx.MX_ERR_ENUM
     assert n(amax=NULL) == mx.MX_ERR_NULL and n(x=NULL) == mx.MX_ERR_NULL
     assert n(M=24) == mx.MX_ERR_SHAPE and n(K=8) == mx.MX_ERR_SHAPE
     assert n(s_col=b.p("s_col", 1)) == mx.MX_ERR_ALIGN

@@ -26,7 +26,9 @@ sys.path.insert(0, HERE)
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
 
-KERNEL_SOURCES = ["block_scaled_precision_bf16_amd/csrc/mx_cast.hip",
+KERNEL_SOURCES = ["block_scaled_precision_bf16_amd/csrc/mx_cast.h",
+                  "block_scaled_precision_bf16_amd/csrc/mx_cast_fmt_e4m3.hip",
+                  "block_scaled_precision_bf16_amd/csrc/mx_cast.hip",
                   "block_scaled_precision_bf16_amd/csrc/nvfp4.hip",
                   "block_scaled_precision_bf16_amd/csrc/device_math.h",
                   "block_scaled_precision_bf16_amd/csrc/launch.h",
@@ -62,7 +64,17 @@ CONFIGS = {
     "mxfp8_dsilu_dbias_8192": ("f1_dsilu_dbias_8192", (8192, 8192), "mx_dsilu", 3),
     "mxfp8_dswiglu_8192": ("f1_dgated_8192", (8192, 4096), "dgated_swiglu", 3),
     "mxfp8_dgeglu_8192": ("f1_dgated_8192", (8192, 4096), "dgated_geglu", 3),
+    "mxfp8_e5m2_dim0_dim1_16384": ("c2_dim1_16384", (16384, 16384), "mx", 3),
+    "mxfp8_e4m3_roundup_dim0_dim1_16384": ("c2_dim1_16384", (16384, 16384), "mx", 3),
+    "mxfp8_e5m2_roundup_dim0_dim1_16384": ("c2_dim1_16384", (16384, 16384), "mx", 3),
 }
+
+# MXFP8 format flags OR-ed into the axis mask (E5M2 elements = 4, round-up
+# E8M0 rule = 8), and the format each plain MXFP8 workload names.
+FORMAT_FLAGS = {"mxfp8_e5m2_dim0_dim1_16384": 4, "mxfp8_e4m3_roundup_dim0_dim1_16384": 8,
+                "mxfp8_e5m2_roundup_dim0_dim1_16384": 12}
+FORMAT_NAMES = {0: "mxfp8 e4m3 + e8m0", 4: "mxfp8 e5m2 + e8m0",
+                8: "mxfp8 e4m3 + e8m0 (round-up rule)", 12: "mxfp8 e5m2 + e8m0 (round-up rule)"}
 
 
 def kernel_source_hash():
@@ -171,7 +183,7 @@ def main():
         desc = dict(workload=args.config, M=M, K=K, N=N, block=32, directions="row+col",
                     format="mxfp8 e4m3 + e8m0", activation=kind.split("_")[1])
     else:
-        axis = mx.COLWISE if dirs == 2 else mx.ROWWISE | mx.COLWISE
+        axis = (mx.COLWISE if dirs == 2 else mx.ROWWISE | mx.COLWISE) | FORMAT_FLAGS.get(args.config, 0)
         fusion = {"mx": mx.FUSE_NONE, "mx_gelu": mx.FUSE_GELU | mx.FUSE_DBIAS,
                   "mx_dgelu": mx.FUSE_DGELU | mx.FUSE_DBIAS,
                   "mx_dsilu": mx.FUSE_DSILU | mx.FUSE_DBIAS}[kind]
@@ -184,7 +196,8 @@ def main():
         if fusion & mx.FUSE_DBIAS:
             alg_bytes += 4 * K
         desc = dict(workload=args.config, M=M, K=K, block=32,
-                    directions="col" if ndir == 1 else "row+col", format="mxfp8 e4m3 + e8m0",
+                    directions="col" if ndir == 1 else "row+col",
+                    format=FORMAT_NAMES[FORMAT_FLAGS.get(args.config, 0)],
                     fusion={"mx": "none", "mx_gelu": "gelu+dbias", "mx_dgelu": "dgelu+dbias",
                             "mx_dsilu": "dsilu+dbias"}[kind])
 

@@ -27,6 +27,7 @@ FUSE_NONE, FUSE_GELU, FUSE_DGELU, FUSE_DSILU, FUSE_DBIAS = 0, 1, 2, 3, 0x10
 GATED_SWIGLU, GATED_GEGLU = 1, 2
 ROWWISE, COLWISE = 1, 2
 ELEM_E5M2, SCALE_ROUND_UP = 4, 8     # variant flags OR-ed into axis (MXFP8 only)
+SCALE_TILED = 16                     # GEMM-ready (MFMA tile) scale layout flag
 
 
 def lib():
@@ -59,6 +60,10 @@ def lib():
         L.orc_mx_block_mode.argtypes = [_f64p, ctypes.c_int, _u8p, _i64, _u8p, ctypes.c_uint]
         L.orc_e5m2_encode_array.restype = None
         L.orc_e5m2_encode_array.argtypes = [_f64p, _u8p, _i64]
+        L.orc_tiled_scale_bytes.restype = ctypes.c_int64
+        L.orc_tiled_scale_bytes.argtypes = [_i64, _i64]
+        L.orc_scale_tiles.restype = None
+        L.orc_scale_tiles.argtypes = [_u8p, _i64, _i64, _u8p]
         L.orc_e8m0_value.restype = ctypes.c_double
         L.orc_e8m0_value.argtypes = [ctypes.c_uint8]
         L.orc_mx_block.restype = None
@@ -185,6 +190,26 @@ def e8m0_value(b: int) -> float:
     return lib().orc_e8m0_value(b)
 
 
+def tiled_scale_bytes(R: int, C: int) -> int:
+    return lib().orc_tiled_scale_bytes(R, C)
+
+
+def scale_tiles(s) -> np.ndarray:
+    """Compact scales s[R][C] -> the flat tiled (GEMM-ready) layout."""
+    s = _c(s, np.uint8)
+    R, C = s.shape
+    out = np.empty(tiled_scale_bytes(R, C), np.uint8)
+    lib().orc_scale_tiles(_p(s, _u8p), R, C, _p(out, _u8p))
+    return out
+
+
+def _scales(axis, rows, blocks):
+    """Output buffer for one direction's scales: [rows][blocks], or flat tiled."""
+    if axis & SCALE_TILED:
+        return np.zeros(tiled_scale_bytes(rows, blocks), np.uint8)
+    return np.zeros((rows, blocks), np.uint8)
+
+
 def e4m3_encode_array(v) -> np.ndarray:
     v = _c(np.asarray(v, dtype=np.float64), np.float64)
     out = np.empty(v.shape, np.uint8)
@@ -257,9 +282,9 @@ def mx_quantize(x, grad=None, axis=ROWWISE | COLWISE, fusion=FUSE_NONE, want_y=F
     g = _c(grad, np.uint16) if grad is not None else None
     out = {}
     q_row = np.zeros((M, K), np.uint8) if axis & ROWWISE else None
-    s_row = np.zeros((M, K // 32), np.uint8) if axis & ROWWISE else None
+    s_row = _scales(axis, M, K // 32) if axis & ROWWISE else None
     q_col = np.zeros((K, M), np.uint8) if axis & COLWISE else None
-    s_col = np.zeros((K, M // 32), np.uint8) if axis & COLWISE else None
+    s_col = _scales(axis, K, M // 32) if axis & COLWISE else None
     dbias = np.zeros(K, np.float32) if fusion & FUSE_DBIAS else None
     y = np.zeros((M, K), np.uint16) if want_y else None
     rc = lib().orc_mx_quantize(_p(x, _u16p), _p(g, _u16p), M, K, axis, fusion,
@@ -277,9 +302,9 @@ def mx_quantize_gated(x, act, axis=ROWWISE | COLWISE, want_y=False):
     M, N2 = x.shape
     N = N2 // 2
     q_row = np.zeros((M, N), np.uint8) if axis & ROWWISE else None
-    s_row = np.zeros((M, N // 32), np.uint8) if axis & ROWWISE else None
+    s_row = _scales(axis, M, N // 32) if axis & ROWWISE else None
     q_col = np.zeros((N, M), np.uint8) if axis & COLWISE else None
-    s_col = np.zeros((N, M // 32), np.uint8) if axis & COLWISE else None
+    s_col = _scales(axis, N, M // 32) if axis & COLWISE else None
     y = np.zeros((M, N), np.uint16) if want_y else None
     rc = lib().orc_mx_quantize_gated(_p(x, _u16p), M, N, axis, act, _p(q_row, _u8p),
                                      _p(s_row, _u8p), _p(q_col, _u8p), _p(s_col, _u8p),
@@ -298,9 +323,9 @@ def mx_quantize_dgated(grad, x, act, axis=ROWWISE | COLWISE, want_y=False):
     N = N2 // 2
     assert grad.shape == (M, N)
     q_row = np.zeros((M, N2), np.uint8) if axis & ROWWISE else None
-    s_row = np.zeros((M, N2 // 32), np.uint8) if axis & ROWWISE else None
+    s_row = _scales(axis, M, N2 // 32) if axis & ROWWISE else None
     q_col = np.zeros((N2, M), np.uint8) if axis & COLWISE else None
-    s_col = np.zeros((N2, M // 32), np.uint8) if axis & COLWISE else None
+    s_col = _scales(axis, N2, M // 32) if axis & COLWISE else None
     y = np.zeros((M, N2), np.uint16) if want_y else None
     rc = lib().orc_mx_quantize_dgated(_p(grad, _u16p), _p(x, _u16p), M, N, axis, act,
                                       _p(q_row, _u8p), _p(s_row, _u8p), _p(q_col, _u8p),

@@ -42,6 +42,13 @@
  *       byte = ceil(log2(amax / max_elem)) + 127: the smallest power of two
  *       that brings amax inside the element range, so nothing saturates.
  *       The floor rule of R1 reads emax = 15 for E5M2.
+ *   R8  GEMM-ready scale layout (flag beside the axis bits): the scales of a
+ *       [R][C] scale matrix are regrouped into tiles of 32 rows x 8 blocks,
+ *       one per wave step group of a 32x32x64 block-scaled MFMA: inside a
+ *       tile, the 4-byte word of lane L holds, in byte j, the scale that lane
+ *       uses in the j-th of four consecutive K steps (row L % 32, block
+ *       2j + L / 32).  Tiles are stored block-tile-major; R and C are padded
+ *       to whole tiles with zero bytes.
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fopenmp -shared
  * -fPIC (see build.py).  OpenMP only splits independent rows / columns /
@@ -511,6 +518,39 @@ int orc_gated_bwd(int act, uint16_t gate, uint16_t lin, uint16_t grad, uint16_t 
 }
 
 /* ------------------------------------------------------------------------ */
+/* GEMM-ready scale layout (R8).                                             */
+/* ------------------------------------------------------------------------ */
+
+#define ORC_TILED 16u      /* flag: scales in the MFMA tile layout */
+
+/* Bytes of the tiled form of an R x C scale matrix. */
+int64_t orc_tiled_scale_bytes(int64_t R, int64_t C)
+{
+    return ((R + 31) / 32) * ((C + 7) / 8) * 256;
+}
+
+/* Compact row-major scales s[R][C] -> the tile layout.  A 32x32x64 MFMA step
+ * with block-scaled operands has lane L hold one row (L % 32) and one block of
+ * 32 K elements (the first or second half of the step's 64, by L / 32), and
+ * takes its scale from a byte of a 32-bit register chosen per step.  So the
+ * scales a wave needs for four consecutive steps (8 blocks of 32 rows) form a
+ * 256-byte tile in which lane L's word holds its scale for step j in byte j:
+ * block 2j + L / 32 of row L % 32.  Tile (row tile rt, block tile bt) sits at
+ * (bt * RT + rt) * 256, RT = ceil(R / 32); bytes outside the matrix are 0. */
+void orc_scale_tiles(const uint8_t *s, int64_t R, int64_t C, uint8_t *out)
+{
+    const int64_t RT = (R + 31) / 32;
+    memset(out, 0, (size_t)orc_tiled_scale_bytes(R, C));
+    for (int64_t r = 0; r < R; r++)
+        for (int64_t c = 0; c < C; c++) {
+            const int64_t tile = (c / 8) * RT + r / 32;
+            const int64_t lane = 32 * (c % 2) + r % 32;
+            const int64_t step = (c % 8) / 2;
+            out[tile * 256 + 4 * lane + step] = s[r * C + c];
+        }
+}
+
+/* ------------------------------------------------------------------------ */
 /* MXFP8 over a tensor.                                                      */
 /* ------------------------------------------------------------------------ */
 
@@ -548,6 +588,32 @@ static void mx_tensor(const uint16_t *y, int64_t M, int64_t K, unsigned axis,
     }
 }
 
+/* mx_tensor with the scales in the layout the axis flags ask for: compact
+ * [rows][blocks], or (ORC_TILED) the tile layout of R8. */
+static int mx_tensor_out(const uint16_t *y, int64_t M, int64_t K, unsigned axis,
+                         uint8_t *q_row, uint8_t *s_row, uint8_t *q_col, uint8_t *s_col)
+{
+    if (!(axis & ORC_TILED)) {
+        mx_tensor(y, M, K, axis, q_row, s_row, q_col, s_col);
+        return ORC_OK;
+    }
+    uint8_t *sr = (axis & 1u) ? (uint8_t *)malloc((size_t)(M * (K / 32))) : NULL;
+    uint8_t *sc = (axis & 2u) ? (uint8_t *)malloc((size_t)(K * (M / 32))) : NULL;
+    if (((axis & 1u) && !sr) || ((axis & 2u) && !sc)) {
+        free(sr);
+        free(sc);
+        return ORC_ERR_NOMEM;
+    }
+    mx_tensor(y, M, K, axis, q_row, sr, q_col, sc);
+    if (sr)
+        orc_scale_tiles(sr, M, K / 32, s_row);
+    if (sc)
+        orc_scale_tiles(sc, K, M / 32, s_col);
+    free(sr);
+    free(sc);
+    return ORC_OK;
+}
+
 /* dbias[k] = sum over m of y[m][k]: summed in double in row order, rounded
  * once to fp32. */
 static void column_sums(const uint16_t *y, int64_t M, int64_t K, float *dbias)
@@ -561,7 +627,8 @@ static void column_sums(const uint16_t *y, int64_t M, int64_t K, float *dbias)
     }
 }
 
-/* axis: bit 0 rows, bit 1 columns, ORC_E5M2 / ORC_ROUND_UP variants (R7).
+/* axis: bit 0 rows, bit 1 columns, ORC_E5M2 / ORC_ROUND_UP variants (R7),
+ * ORC_TILED scale layout (R8: s_row / s_col then hold the tiled bytes).
  * fusion: low nibble = pre-op (0 none, 1 GELU, 2 dGELU, 3 dSiLU), bit 0x10 = dbias.
  * y_out (optional, [M][K]) receives the fused bf16 tensor. */
 int orc_mx_quantize(const uint16_t *x, const uint16_t *grad, int64_t M, int64_t K,
@@ -571,7 +638,7 @@ int orc_mx_quantize(const uint16_t *x, const uint16_t *grad, int64_t M, int64_t 
     int pre = fusion & 0xF;
     if (M <= 0 || K <= 0 || M % 32 || K % 32)
         return ORC_ERR_SHAPE;
-    if (pre > 3 || (fusion & ~0x1F) || (axis & ~15u))
+    if (pre > 3 || (fusion & ~0x1F) || (axis & ~31u))
         return ORC_ERR_ENUM;
     init_tables();
     const uint16_t *y = x;
@@ -587,12 +654,12 @@ int orc_mx_quantize(const uint16_t *x, const uint16_t *grad, int64_t M, int64_t 
     } else if (y_out) {
         memcpy(y_out, x, (size_t)(M * K) * 2);
     }
-    mx_tensor(y, M, K, axis, q_row, s_row, q_col, s_col);
-    if ((fusion & 0x10) && dbias)
+    int rc = mx_tensor_out(y, M, K, axis, q_row, s_row, q_col, s_col);
+    if (rc == ORC_OK && (fusion & 0x10) && dbias)
         column_sums(y, M, K, dbias);
     if (ybuf && ybuf != y_out)
         free(ybuf);
-    return ORC_OK;
+    return rc;
 }
 
 /* x[M][2N] = [gate | linear] (gate = columns 0..N-1); y[m][n] = act(gate)*lin. */
@@ -602,7 +669,7 @@ int orc_mx_quantize_gated(const uint16_t *x, int64_t M, int64_t N, unsigned axis
 {
     if (M <= 0 || N <= 0 || M % 32 || N % 32)
         return ORC_ERR_SHAPE;
-    if ((act != 1 && act != 2) || (axis & ~15u))
+    if ((act != 1 && act != 2) || (axis & ~31u))
         return ORC_ERR_ENUM;
     init_tables();
     uint16_t *y = y_out ? y_out : (uint16_t *)malloc((size_t)(M * N) * 2);
@@ -612,10 +679,10 @@ int orc_mx_quantize_gated(const uint16_t *x, int64_t M, int64_t N, unsigned axis
     for (int64_t m = 0; m < M; m++)
         for (int64_t n = 0; n < N; n++)
             y[m * N + n] = orc_gated(act, x[m * 2 * N + n], x[m * 2 * N + N + n]);
-    mx_tensor(y, M, N, axis, q_row, s_row, q_col, s_col);
+    int rc = mx_tensor_out(y, M, N, axis, q_row, s_row, q_col, s_col);
     if (y != y_out)
         free(y);
-    return ORC_OK;
+    return rc;
 }
 
 /* Gated backward cast: grad[M][N], x[M][2N] = [gate | linear]; the tensor
@@ -626,7 +693,7 @@ int orc_mx_quantize_dgated(const uint16_t *grad, const uint16_t *x, int64_t M, i
 {
     if (M <= 0 || N <= 0 || M % 32 || N % 32)
         return ORC_ERR_SHAPE;
-    if ((act != 1 && act != 2) || (axis & ~15u))
+    if ((act != 1 && act != 2) || (axis & ~31u))
         return ORC_ERR_ENUM;
     init_tables();
     uint16_t *y = y_out ? y_out : (uint16_t *)malloc((size_t)(M * 2 * N) * 2);
@@ -637,10 +704,10 @@ int orc_mx_quantize_dgated(const uint16_t *grad, const uint16_t *x, int64_t M, i
         for (int64_t n = 0; n < N; n++)
             orc_gated_bwd(act, x[m * 2 * N + n], x[m * 2 * N + N + n], grad[m * N + n],
                           &y[m * 2 * N + n], &y[m * 2 * N + N + n]);
-    mx_tensor(y, M, 2 * N, axis, q_row, s_row, q_col, s_col);
+    int rc = mx_tensor_out(y, M, 2 * N, axis, q_row, s_row, q_col, s_col);
     if (y != y_out)
         free(y);
-    return ORC_OK;
+    return rc;
 }
 
 /* ------------------------------------------------------------------------ */

@@ -11,8 +11,8 @@ The same names as the C ABI:
     mx_status_str, mx_abi_version
 take torch tensors (bf16 inputs, or int16/uint16 holding bf16 bits, on a ROCm
 device) and return dicts of uint8 / float32 torch tensors on the same device.
-The MXFP8 casts take the format flags ELEM_E5M2 / SCALE_ROUND_UP OR-ed into
-`axis`, as the C ABI does.
+The MXFP8 casts take the format flags ELEM_E5M2 / SCALE_ROUND_UP and the
+layout flag SCALE_TILED OR-ed into `axis`, as the C ABI does.
 `lib()` returns the raw ctypes library for callers that pass pointers
 themselves.
 """
@@ -26,13 +26,14 @@ LIB_PATH = os.path.join(_HERE, "libmxcast.so")
 
 ROWWISE, COLWISE = 1, 2
 ELEM_E5M2, SCALE_ROUND_UP = 4, 8     # MXFP8 format flags, OR-ed into axis
+SCALE_TILED = 16                     # GEMM-ready scale layout flag, OR-ed into axis
 FUSE_NONE, FUSE_GELU, FUSE_DGELU, FUSE_DSILU, FUSE_DBIAS = 0, 1, 2, 3, 0x10
 GATED_SWIGLU, GATED_GEGLU = 1, 2
 OP_GATED, OP_DGATED = 0x100, 0x200
 (MX_OK, MX_ERR_NULL, MX_ERR_ENUM, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_WORKSPACE,
  MX_ERR_ALIAS, MX_ERR_HIP, MX_ERR_UNSUPPORTED) = range(9)
 
-EXPORTS = ("mx_quantize", "mx_quantize_workspace_size", "mx_quantize_gated",
+EXPORTS = ("mx_quantize", "mx_quantize_workspace_size", "mx_scale_size", "mx_quantize_gated",
            "mx_quantize_dgated", "mx_fused_values",
            "mx_absmax_bf16", "nvfp4_quantize_transpose", "nvfp4_quantize_transpose_2d",
            "mx_status_str", "mx_abi_version")
@@ -62,6 +63,8 @@ def lib():
                                   _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.mx_quantize_workspace_size.restype = ctypes.c_size_t
         L.mx_quantize_workspace_size.argtypes = [_i64, _i64, ctypes.c_uint, ctypes.c_int]
+        L.mx_scale_size.restype = ctypes.c_size_t
+        L.mx_scale_size.argtypes = [_i64, _i64, ctypes.c_uint]
         L.mx_quantize_gated.restype = ctypes.c_int
         L.mx_quantize_gated.argtypes = [_vp, _i64, _i64, ctypes.c_uint, ctypes.c_int,
                                         _vp, _vp, _vp, _vp, _vp]
@@ -126,6 +129,17 @@ def mx_quantize_workspace_size(M: int, K: int, axis: int = ROWWISE | COLWISE,
     return lib().mx_quantize_workspace_size(M, K, axis, fusion)
 
 
+def mx_scale_size(rows: int, cols: int, axis: int = ROWWISE | COLWISE) -> int:
+    return lib().mx_scale_size(rows, cols, axis)
+
+
+def _scales(rows, cols, axis, dev):
+    """One direction's scale tensor: [rows][cols/32], or flat in the tile layout."""
+    if axis & SCALE_TILED:
+        return _u8((mx_scale_size(rows, cols, axis),), dev)
+    return _u8((rows, cols // 32), dev)
+
+
 def mx_quantize(x, grad=None, axis=ROWWISE | COLWISE, fusion=FUSE_NONE, out=None,
                 workspace=None, stream=None):
     """MXFP8 cast of x[M][K].  Returns {q_row, s_row, q_col, s_col, dbias}
@@ -138,10 +152,10 @@ def mx_quantize(x, grad=None, axis=ROWWISE | COLWISE, fusion=FUSE_NONE, out=None
     o = dict(out or {})
     if axis & ROWWISE:
         o.setdefault("q_row", _u8((M, K), dev))
-        o.setdefault("s_row", _u8((M, K // 32), dev))
+        o.setdefault("s_row", _scales(M, K, axis, dev))
     if axis & COLWISE:
         o.setdefault("q_col", _u8((K, M), dev))
-        o.setdefault("s_col", _u8((K, M // 32), dev))
+        o.setdefault("s_col", _scales(K, M, axis, dev))
     ws_bytes = 0
     if fusion & FUSE_DBIAS:
         o.setdefault("dbias", torch.empty(K, dtype=torch.float32, device=dev))
@@ -167,10 +181,10 @@ def mx_quantize_gated(x, act, axis=ROWWISE | COLWISE, out=None, stream=None):
     o = dict(out or {})
     if axis & ROWWISE:
         o.setdefault("q_row", _u8((M, N), dev))
-        o.setdefault("s_row", _u8((M, N // 32), dev))
+        o.setdefault("s_row", _scales(M, N, axis, dev))
     if axis & COLWISE:
         o.setdefault("q_col", _u8((N, M), dev))
-        o.setdefault("s_col", _u8((N, M // 32), dev))
+        o.setdefault("s_col", _scales(N, M, axis, dev))
     st = lib().mx_quantize_gated(_ptr(x), M, N, axis, act, _ptr(o.get("q_row")),
                                  _ptr(o.get("s_row")), _ptr(o.get("q_col")),
                                  _ptr(o.get("s_col")), _stream(dev, stream))
@@ -189,10 +203,10 @@ def mx_quantize_dgated(grad, x, act, axis=ROWWISE | COLWISE, out=None, stream=No
     o = dict(out or {})
     if axis & ROWWISE:
         o.setdefault("q_row", _u8((M, N2), dev))
-        o.setdefault("s_row", _u8((M, N2 // 32), dev))
+        o.setdefault("s_row", _scales(M, N2, axis, dev))
     if axis & COLWISE:
         o.setdefault("q_col", _u8((N2, M), dev))
-        o.setdefault("s_col", _u8((N2, M // 32), dev))
+        o.setdefault("s_col", _scales(N2, M, axis, dev))
     st = lib().mx_quantize_dgated(_ptr(grad), _ptr(x), M, N, axis, act, _ptr(o.get("q_row")),
                                   _ptr(o.get("s_row")), _ptr(o.get("q_col")),
                                   _ptr(o.get("s_col")), _stream(dev, stream))

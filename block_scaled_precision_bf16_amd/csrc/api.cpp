@@ -62,26 +62,45 @@ int cast_op(int pre)
          : pre == MX_FUSE_DSILU ? mxk::OP_DSILU : mxk::OP_PLAIN;
 }
 
+// Sub-tiles per walk of the cast kernel `op`: with the GEMM-ready scale
+// layout a walk covers at least two sub-tiles, so that it starts on a
+// column-scale tile boundary (8 blocks = 256 rows) and no two workgroups
+// write one scale tile.
+int walk_group(int tm, int tk, int op, bool dbias, bool tiled)
+{
+    const int g = mxk::pick_group(tm, tk, mxk::target_workgroups(op, dbias));
+    return tiled && g < 2 ? 2 : g;
+}
+
 // Walks along M of the cast kernel `op` (with or without dbias) for an
 // M x K tensor.
-int walks_m(int64_t M, int64_t K, int op, bool dbias)
+int walks_m(int64_t M, int64_t K, int op, bool dbias, bool tiled)
 {
     const int tm = tiles(M, mxk::kTileM), tk = tiles(K, mxk::kTileK);
-    const int g = mxk::pick_group(tm, tk, mxk::target_workgroups(op, dbias));
+    const int g = walk_group(tm, tk, op, dbias, tiled);
     return (tm + g - 1) / g;
 }
 
-size_t dbias_workspace(int64_t M, int64_t K, int op)
+size_t dbias_workspace(int64_t M, int64_t K, int op, bool tiled)
 {
-    return (size_t)walks_m(M, K, op, true) * (size_t)K * sizeof(float);
+    return (size_t)walks_m(M, K, op, true, tiled) * (size_t)K * sizeof(float);
 }
 
 void set_walk(mxk::MxArgs &a, int op, bool dbias)
 {
     a.tiles_k = tiles(a.K, mxk::kTileK);
     a.tiles_m = tiles(a.M, mxk::kTileM);
-    a.group = mxk::pick_group(a.tiles_m, a.tiles_k, mxk::target_workgroups(op, dbias));
+    a.group = walk_group(a.tiles_m, a.tiles_k, op, dbias, a.tiled != 0);
     a.groups_m = (a.tiles_m + a.group - 1) / a.group;
+}
+
+// Bytes of the scales of a quantised [rows][cols] tensor blocked along cols:
+// compact [rows][cols / 32], or whole 32-row x 8-block tiles of 256 bytes.
+uint64_t scale_bytes(int64_t rows, int64_t cols, bool tiled)
+{
+    if (!tiled)
+        return (uint64_t)(rows * (cols / 32));
+    return (uint64_t)(((rows + 31) / 32) * ((cols / 32 + 7) / 8) * 256);
 }
 
 mx_status from_hip(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
@@ -90,14 +109,16 @@ mx_status from_hip(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; 
 
 // NVFP4 quantize-transpose with 1D (two_d = false) or 16 x 16 block scaling.
 // The MXFP8 entry points' axis_mask: at least one of the two axis bits, plus
-// optionally the format flags (E5M2 elements, round-up scale rule).
+// optionally the format flags (E5M2 elements, round-up scale rule) and the
+// GEMM-ready scale layout flag.
 static const unsigned kFmtBits = MX_ELEM_E5M2 | MX_SCALE_ROUND_UP;
+static const unsigned kModeBits = 3u | kFmtBits | MX_SCALE_TILED;
 static_assert(MX_ELEM_E5M2 == (unsigned)mxk::kFmtE5M2 && MX_SCALE_ROUND_UP == (unsigned)mxk::kFmtRoundUp,
               "format flags are passed to the kernels unchanged");
 
 static bool mx_mode_ok(unsigned axis_mask)
 {
-    return (axis_mask & 3u) != 0 && (axis_mask & ~(3u | kFmtBits)) == 0;
+    return (axis_mask & 3u) != 0 && (axis_mask & ~kModeBits) == 0;
 }
 
 static mx_status nvfp4_impl(bool two_d, const void *x, int64_t M, int64_t K, const float *amax,
@@ -166,7 +187,14 @@ size_t mx_quantize_workspace_size(int64_t M, int64_t K, unsigned axis_mask, int 
     if (!(fusion & MX_FUSE_DBIAS) || !shape_ok(M, K, 32) || !mx_mode_ok(axis_mask) ||
         (fusion & ~0x1F) || (fusion & 0xF) > MX_FUSE_DSILU)
         return 0;
-    return dbias_workspace(M, K, cast_op(fusion & 0xF));
+    return dbias_workspace(M, K, cast_op(fusion & 0xF), (axis_mask & MX_SCALE_TILED) != 0);
+}
+
+size_t mx_scale_size(int64_t rows, int64_t cols, unsigned axis_mask)
+{
+    if (!shape_ok(rows, cols, 32) || !mx_mode_ok(axis_mask))
+        return 0;
+    return (size_t)scale_bytes(rows, cols, (axis_mask & MX_SCALE_TILED) != 0);
 }
 
 mx_status mx_quantize(const void *x, const void *grad, int64_t M, int64_t K, unsigned axis_mask,
@@ -190,13 +218,14 @@ mx_status mx_quantize(const void *x, const void *grad, int64_t M, int64_t K, uns
         (want_dbias && (!aligned(dbias, 4) || (workspace && !aligned(workspace, 16)))))
         return MX_ERR_ALIGN;
     const int op = cast_op(pre);
-    const size_t need = want_dbias ? dbias_workspace(M, K, op) : 0;
+    const bool tiled = (axis_mask & MX_SCALE_TILED) != 0;
+    const size_t need = want_dbias ? dbias_workspace(M, K, op, tiled) : 0;
     if (want_dbias && (!workspace || workspace_bytes < need))
         return MX_ERR_WORKSPACE;
     const uint64_t n = (uint64_t)(M * K);
     const Span in[2] = {{x, 2 * n}, {has_grad ? grad : nullptr, 2 * n}};
-    const Span out[6] = {{row ? q_row : nullptr, n}, {row ? s_row : nullptr, n / 32},
-                         {col ? q_col : nullptr, n}, {col ? s_col : nullptr, n / 32},
+    const Span out[6] = {{row ? q_row : nullptr, n}, {row ? s_row : nullptr, scale_bytes(M, K, tiled)},
+                         {col ? q_col : nullptr, n}, {col ? s_col : nullptr, scale_bytes(K, M, tiled)},
                          {want_dbias ? dbias : nullptr, 4 * (uint64_t)K},
                          {want_dbias ? workspace : nullptr, need}};
     if (any_alias(in, 2, out, 6))
@@ -215,6 +244,7 @@ mx_status mx_quantize(const void *x, const void *grad, int64_t M, int64_t K, uns
     a.q_col = q_col;
     a.s_col = s_col;
     a.partials = want_dbias ? static_cast<float *>(workspace) : nullptr;
+    a.tiled = tiled;
     set_walk(a, op, want_dbias);
     mx_status st = from_hip(mxk::launch_mx_cast(op, axis_mask & 3u, axis_mask & kFmtBits,
                                                 want_dbias, a, stream));
@@ -238,9 +268,10 @@ mx_status mx_quantize_gated(const void *x, int64_t M, int64_t N, unsigned axis_m
         (col && (!aligned(q_col, 16) || !aligned(s_col, 16))))
         return MX_ERR_ALIGN;
     const uint64_t n = (uint64_t)(M * N);
+    const bool tiled = (axis_mask & MX_SCALE_TILED) != 0;
     const Span in[1] = {{x, 4 * n}};
-    const Span out[4] = {{row ? q_row : nullptr, n}, {row ? s_row : nullptr, n / 32},
-                         {col ? q_col : nullptr, n}, {col ? s_col : nullptr, n / 32}};
+    const Span out[4] = {{row ? q_row : nullptr, n}, {row ? s_row : nullptr, scale_bytes(M, N, tiled)},
+                         {col ? q_col : nullptr, n}, {col ? s_col : nullptr, scale_bytes(N, M, tiled)}};
     if (any_alias(in, 1, out, 4))
         return MX_ERR_ALIAS;
 
@@ -257,6 +288,7 @@ mx_status mx_quantize_gated(const void *x, int64_t M, int64_t N, unsigned axis_m
     a.q_col = q_col;
     a.s_col = s_col;
     a.partials = nullptr;
+    a.tiled = tiled;
     const int op = act == MX_GATED_SWIGLU ? mxk::OP_SWIGLU : mxk::OP_GEGLU;
     set_walk(a, op, false);
     return from_hip(
@@ -279,9 +311,12 @@ mx_status mx_quantize_dgated(const void *grad, const void *x, int64_t M, int64_t
         (col && (!aligned(q_col, 16) || !aligned(s_col, 16))))
         return MX_ERR_ALIGN;
     const uint64_t n = (uint64_t)(M * N);
+    const bool tiled = (axis_mask & MX_SCALE_TILED) != 0;
     const Span in[2] = {{grad, 2 * n}, {x, 4 * n}};
-    const Span out[4] = {{row ? q_row : nullptr, 2 * n}, {row ? s_row : nullptr, n / 16},
-                         {col ? q_col : nullptr, 2 * n}, {col ? s_col : nullptr, n / 16}};
+    const Span out[4] = {{row ? q_row : nullptr, 2 * n},
+                         {row ? s_row : nullptr, scale_bytes(M, 2 * N, tiled)},
+                         {col ? q_col : nullptr, 2 * n},
+                         {col ? s_col : nullptr, scale_bytes(2 * N, M, tiled)}};
     if (any_alias(in, 2, out, 4))
         return MX_ERR_ALIAS;
 
@@ -298,6 +333,7 @@ mx_status mx_quantize_dgated(const void *grad, const void *x, int64_t M, int64_t
     a.q_col = q_col;
     a.s_col = s_col;
     a.partials = nullptr;
+    a.tiled = tiled;
     const int op = act == MX_GATED_SWIGLU ? mxk::OP_DSWIGLU : mxk::OP_DGEGLU;
     set_walk(a, op, false);
     return from_hip(

@@ -66,6 +66,7 @@ struct MxArgs {
     float *partials;       // dbias: [groups_m][K] fp32 column partial sums
     int tiles_k, tiles_m;  // 128 x 256 sub-tiles along K and M
     int group, groups_m;   // sub-tiles per workgroup walk, walks along M
+    int tiled;             // scales in the GEMM-ready tile layout (walks of >= 2 sub-tiles)
 };
 
 struct Nv4Args {

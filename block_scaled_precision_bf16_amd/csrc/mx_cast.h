@@ -326,6 +326,43 @@ __device__ __forceinline__ void col_flush_s_ch(const MxArgs &a, const ColStage &
     }
 }
 
+// The 4-byte word lane L of a GEMM-ready scale tile holds: bytes j = 0..3 are
+// blocks 2j + L / 32 of the tile's row L % 32, picked from that row's 8 staged
+// block bytes (v.x = blocks 0-3, v.y = blocks 4-7).
+__device__ __forceinline__ uint32_t tile_word(uint2 v, int lane)
+{
+    return __builtin_amdgcn_perm(v.y, v.x, (lane >> 5) ? 0x07050301u : 0x06040200u);
+}
+
+// Column scales of the strip segment in the GEMM-ready tile layout (tiles of
+// 32 transposed rows x 8 blocks, 256 bytes, block-tile-major).  A walk starts
+// on a tile boundary (its length is even), so its 4 n blocks per column fill
+// whole tiles except, for odd n, the upper half of the last one, which holds
+// no block of the tensor and is written as zeros.  The strip's 256
+// transposed rows are 8 row tiles, contiguous for each block tile.
+template <int AUX>
+__device__ __forceinline__ void col_flush_s_tiled(const MxArgs &a, const ColStage &st, int rg,
+                                                  int tk, int n)
+{
+    const int t = (int)threadIdx.x;
+    const int64_t RT = a.K >> 5;                          // row tiles of s_col
+    const int64_t CT = ((a.M >> 5) + 7) >> 3;             // block tiles
+    const int64_t bt0 = (int64_t)rg * (a.group >> 1);     // first block tile of the walk
+    const int64_t rt0 = (int64_t)tk * (kTileK / 32);
+    const int nbt = (4 * n + 7) >> 3;
+    const rsrc_t rs = make_rsrc(a.s_col, (bt0 * RT + rt0) * 256, RT * CT * 256);
+    for (int i = 0; i < 2 * nbt; i++) {
+        const int idx = t + kThreads * i;                 // (block tile, row tile, lane)
+        const int btl = idx >> 9, rtl = (idx >> 6) & 7, lane = idx & 63;
+        uint2 v = *reinterpret_cast<const uint2 *>(&st.s[32 * rtl + (lane & 31)][8 * btl]);
+        if (4 * n - 8 * btl < 8)
+            v.y = 0u;
+        const uint32_t off = rt0 + rtl < RT ? (uint32_t)(((int64_t)btl * RT + rtl) * 256 + 4 * lane)
+                                            : kDead;
+        buf_store4<AUX>(rs, off, tile_word(v, lane));
+    }
+}
+
 // Write the strip segment's column scales: 4 n bytes per column for a walk
 // of n sub-tiles, in the widest pieces (16, 8, 4 or 1 bytes) that the row
 // length of s_col, the segment's start and its length allow.
@@ -333,6 +370,10 @@ template <int AUX>
 __device__ __forceinline__ void col_flush_s(const MxArgs &a, const ColStage &st, int rg, int tk,
                                             int n)
 {
+    if (a.tiled) {
+        col_flush_s_tiled<AUX>(a, st, rg, tk, n);
+        return;
+    }
     const int64_t k0 = (int64_t)tk * kTileK;
     const int64_t nblk = a.M >> 5;                        // scales per column
     const int64_t first = (int64_t)rg * a.group * 4;      // this segment's first block
@@ -358,6 +399,20 @@ __device__ __forceinline__ void srow_flush(const MxArgs &a, const uint8_t (&srow
                                            int tm, int tk)
 {
     const int t = (int)threadIdx.x;
+    if (a.tiled) {
+        // GEMM-ready layout: the sub-tile's 128 rows x 8 blocks are the four
+        // 256-byte tiles (block tile tk, row tiles 4 tm .. 4 tm + 3), which
+        // lie next to each other; thread t writes word t (tile t / 64, lane
+        // t % 64).  M is a multiple of 32, so a tile is wholly in or out.
+        const int64_t RT = a.M >> 5;
+        const int64_t bytes = RT * (((a.K >> 5) + 7) >> 3) * 256;
+        const rsrc_t rs = make_rsrc(a.s_row, ((int64_t)tk * RT + 4 * (int64_t)tm) * 256, bytes);
+        const int w = t >> 6, lane = t & 63;
+        const uint2 v = *reinterpret_cast<const uint2 *>(srow[32 * w + (lane & 31)]);
+        const bool live = (int64_t)tm * kTileM + 32 * w < a.M;
+        buf_store4<AUX>(rs, live ? (uint32_t)(4 * t) : kDead, tile_word(v, lane));
+        return;
+    }
     const int64_t row = (int64_t)tm * kTileM + t;
     const int64_t k0 = (int64_t)tk * kTileK;
     const int64_t nb = a.K >> 5;                          // scale bytes per row

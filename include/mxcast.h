@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MXCAST_ABI_VERSION 3
+#define MXCAST_ABI_VERSION 4
 
 typedef enum mx_status {
     MX_OK = 0,
@@ -98,6 +98,26 @@ typedef enum mx_status {
 #define MX_ELEM_E5M2 4u
 #define MX_SCALE_ROUND_UP 8u
 
+/*
+ * MX_SCALE_TILED, OR-ed into the axis_mask of the MXFP8 casts: the scale
+ * tensors are written in a GEMM-ready layout instead of compact row-major.
+ * The pages only hint at consumer-ready scale shapes (the "fix scale shapes"
+ * step of the torchao PR 12 stack); the layout is the one a gfx950
+ * block-scaled 32x32x64 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4) reads: lane
+ * L of a wave holds one row (L % 32) and one 32-element K block (half L / 32
+ * of the step's 64), and takes its E8M0 scale from a byte of a 32-bit
+ * register chosen per step.  For a scale matrix S[R][C] (s_row: R = M rows,
+ * C = K/32 blocks; s_col: R = K transposed rows, C = M/32 blocks):
+ *   tile (rt, bt) = rows 32 rt .. 32 rt + 31, blocks 8 bt .. 8 bt + 7,
+ *                   256 bytes at byte offset (bt * ceil(R/32) + rt) * 256;
+ *   inside it, the 4-byte word of lane L holds in byte j (j = 0..3) the scale
+ *                   of row 32 rt + L % 32, block 8 bt + 2j + L / 32, i.e. the
+ *                   scale lane L uses in the j-th of four consecutive steps.
+ * Blocks past C in the last block tile are 0.  Size: ceil(R/32) * ceil(C/8)
+ * * 256 bytes (mx_scale_size).  Element tensors are unchanged.
+ */
+#define MX_SCALE_TILED 16u
+
 /* fusion: a pre-op in the low bits, optionally OR-ed with MX_FUSE_DBIAS */
 #define MX_FUSE_NONE 0
 #define MX_FUSE_GELU 1      /* y = GELU(x)                                    */
@@ -117,7 +137,9 @@ typedef enum mx_status {
  *            ignored
  *   M, K     rows, columns; positive multiples of 32, each <= 2^23, M*K <= 2^40
  *   axis_mask  MX_ROWWISE, MX_COLWISE or both (one pass over x), optionally
- *            with the format flags MX_ELEM_E5M2 / MX_SCALE_ROUND_UP
+ *            with the format flags MX_ELEM_E5M2 / MX_SCALE_ROUND_UP and the
+ *            layout flag MX_SCALE_TILED (scale tensors then have
+ *            mx_scale_size() bytes in the tile layout)
  *   fusion   MX_FUSE_NONE | GELU | DGELU | DSILU, optionally | MX_FUSE_DBIAS
  *   q_row, s_row  E4M3 [M][K] and E8M0 [M][K/32]; required iff MX_ROWWISE
  *   q_col, s_col  E4M3 [K][M] and E8M0 [K][M/32]; required iff MX_COLWISE
@@ -138,6 +160,16 @@ mx_status mx_quantize(const void *x, const void *grad, int64_t M, int64_t K,
 /* Bytes of workspace mx_quantize needs for these arguments (0 without dbias;
  * 0 also for invalid arguments). */
 size_t mx_quantize_workspace_size(int64_t M, int64_t K, unsigned axis_mask, int fusion);
+
+/*
+ * Bytes of one scale tensor of an MXFP8 cast: the scales of a quantised
+ * [rows][cols] tensor blocked along cols (s_row: rows = M, cols = K; s_col:
+ * rows = K, cols = M; for the gated casts the quantised tensor's own sizes).
+ * rows * cols / 32 for the compact layout, ceil(rows/32) * ceil(cols/256) *
+ * 256 with MX_SCALE_TILED in axis_mask.  0 for sizes that are not positive
+ * multiples of 32 or an invalid axis_mask.
+ */
+size_t mx_scale_size(int64_t rows, int64_t cols, unsigned axis_mask);
 
 /*
  * Gated MXFP8 cast.  x is bf16 [M][2N] holding [gate | linear] (gate =

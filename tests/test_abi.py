@@ -41,7 +41,7 @@ def header_abi_version():
 
 
 def test_version_and_status_strings():
-    assert mx.mx_abi_version() == header_abi_version() == 3
+    assert mx.mx_abi_version() == header_abi_version() == 4
     for code in range(9):
         assert mx.mx_status_str(code).startswith("MX_")
     assert "unknown" in mx.mx_status_str(99)
@@ -75,6 +75,29 @@ def test_workspace_size():
     assert ws(64, 64, 3, 0x14) == 0               # invalid pre-op
     assert ws(8192, 8192, 3 | mx.ELEM_E5M2 | mx.SCALE_ROUND_UP, mx.FUSE_DBIAS) == 16 * 8192 * 4
     assert ws(64, 64, 0x23, mx.FUSE_DBIAS) == 0   # unknown flag
+    # the tile layout makes every walk at least two sub-tiles long
+    assert walks(1024, 4096) == 8
+    assert ws(1024, 4096, 3, mx.FUSE_DBIAS) == 8 * 4096 * 4
+    assert ws(1024, 4096, 3 | mx.SCALE_TILED, mx.FUSE_DBIAS) == 4 * 4096 * 4
+    assert ws(8192, 8192, 3 | mx.SCALE_TILED, mx.FUSE_DBIAS) == 16 * 8192 * 4
+
+
+def test_scale_size():
+    sz = mx.mx_scale_size
+    assert sz(16384, 16384, 3) == 16384 * 512
+    assert sz(16384, 16384, 3 | mx.SCALE_TILED) == 16384 * 512       # whole tiles
+    assert sz(64, 96, 1) == 64 * 3
+    assert sz(64, 96, 1 | mx.SCALE_TILED) == 2 * 1 * 256              # 3 blocks pad to 8
+    assert sz(96, 800, 2 | mx.SCALE_TILED) == 3 * 4 * 256             # 25 blocks -> 4 tiles
+    assert sz(48, 64, 3) == 0 and sz(64, 64, 0) == 0 and sz(64, 64, 0x43) == 0
+
+
+def test_tiled_scales_alias_check_uses_tiled_size():
+    b = Bufs(64, 96)
+    # compact s_row is 64 * 3 = 192 bytes; tiled it is 512, so an s_col that
+    # starts 256 bytes after s_row overlaps it (rejected before any launch)
+    assert q(b, axis=3 | mx.SCALE_TILED, s_col=b.p("s_row", 256)) == mx.MX_ERR_ALIAS
+    assert b.untouched()
 
 
 class Bufs:
@@ -123,7 +146,9 @@ NULL = ctypes.c_void_p(0)
     (dict(axis=0), mx.MX_ERR_ENUM),
     (dict(axis=4), mx.MX_ERR_ENUM),            # a format flag without an axis
     (dict(axis=12), mx.MX_ERR_ENUM),
-    (dict(axis=0x13), mx.MX_ERR_ENUM),
+    (dict(axis=0x23), mx.MX_ERR_ENUM),
+    (dict(axis=0x10), mx.MX_ERR_ENUM),
+    (dict(axis=3 | mx.SCALE_TILED, x=NULL), mx.MX_ERR_NULL),
     (dict(axis=3 | mx.ELEM_E5M2 | mx.SCALE_ROUND_UP, x=NULL), mx.MX_ERR_NULL),  # flags accepted
     (dict(axis=1 | mx.ELEM_E5M2, M=48), mx.MX_ERR_SHAPE),
     (dict(fusion=5), mx.MX_ERR_ENUM),

@@ -67,14 +67,17 @@ CONFIGS = {
     "mxfp8_e5m2_dim0_dim1_16384": ("c2_dim1_16384", (16384, 16384), "mx", 3),
     "mxfp8_e4m3_roundup_dim0_dim1_16384": ("c2_dim1_16384", (16384, 16384), "mx", 3),
     "mxfp8_e5m2_roundup_dim0_dim1_16384": ("c2_dim1_16384", (16384, 16384), "mx", 3),
+    "mxfp8_tiled_dim0_dim1_16384": ("c2_dim1_16384", (16384, 16384), "mx", 3),
 }
 
-# MXFP8 format flags OR-ed into the axis mask (E5M2 elements = 4, round-up
-# E8M0 rule = 8), and the format each plain MXFP8 workload names.
+# MXFP8 flags OR-ed into the axis mask (E5M2 elements = 4, round-up E8M0
+# rule = 8, GEMM-ready tiled scales = 16), and the format each plain MXFP8
+# workload names.
 FORMAT_FLAGS = {"mxfp8_e5m2_dim0_dim1_16384": 4, "mxfp8_e4m3_roundup_dim0_dim1_16384": 8,
-                "mxfp8_e5m2_roundup_dim0_dim1_16384": 12}
+                "mxfp8_e5m2_roundup_dim0_dim1_16384": 12, "mxfp8_tiled_dim0_dim1_16384": 16}
 FORMAT_NAMES = {0: "mxfp8 e4m3 + e8m0", 4: "mxfp8 e5m2 + e8m0",
-                8: "mxfp8 e4m3 + e8m0 (round-up rule)", 12: "mxfp8 e5m2 + e8m0 (round-up rule)"}
+                8: "mxfp8 e4m3 + e8m0 (round-up rule)", 12: "mxfp8 e5m2 + e8m0 (round-up rule)",
+                16: "mxfp8 e4m3 + e8m0 in MFMA scale tiles"}
 
 
 def kernel_source_hash():

@@ -282,9 +282,9 @@ def mx_quantize(x, grad=None, axis=ROWWISE | COLWISE, fusion=FUSE_NONE, want_y=F
     g = _c(grad, np.uint16) if grad is not None else None
     out = {}
     q_row = np.zeros((M, K), np.uint8) if axis & ROWWISE else None
-    s_row = _scales(axis, M, K // 32) if axis & ROWWISE else None
+    s_row = _scales(axis, M, -(-K // 32)) if axis & ROWWISE else None
     q_col = np.zeros((K, M), np.uint8) if axis & COLWISE else None
-    s_col = _scales(axis, K, M // 32) if axis & COLWISE else None
+    s_col = _scales(axis, K, -(-M // 32)) if axis & COLWISE else None
     dbias = np.zeros(K, np.float32) if fusion & FUSE_DBIAS else None
     y = np.zeros((M, K), np.uint16) if want_y else None
     rc = lib().orc_mx_quantize(_p(x, _u16p), _p(g, _u16p), M, K, axis, fusion,
@@ -302,9 +302,9 @@ def mx_quantize_gated(x, act, axis=ROWWISE | COLWISE, want_y=False):
     M, N2 = x.shape
     N = N2 // 2
     q_row = np.zeros((M, N), np.uint8) if axis & ROWWISE else None
-    s_row = _scales(axis, M, N // 32) if axis & ROWWISE else None
+    s_row = _scales(axis, M, -(-N // 32)) if axis & ROWWISE else None
     q_col = np.zeros((N, M), np.uint8) if axis & COLWISE else None
-    s_col = _scales(axis, N, M // 32) if axis & COLWISE else None
+    s_col = _scales(axis, N, -(-M // 32)) if axis & COLWISE else None
     y = np.zeros((M, N), np.uint16) if want_y else None
     rc = lib().orc_mx_quantize_gated(_p(x, _u16p), M, N, axis, act, _p(q_row, _u8p),
                                      _p(s_row, _u8p), _p(q_col, _u8p), _p(s_col, _u8p),
@@ -323,9 +323,9 @@ def mx_quantize_dgated(grad, x, act, axis=ROWWISE | COLWISE, want_y=False):
     N = N2 // 2
     assert grad.shape == (M, N)
     q_row = np.zeros((M, N2), np.uint8) if axis & ROWWISE else None
-    s_row = _scales(axis, M, N2 // 32) if axis & ROWWISE else None
+    s_row = _scales(axis, M, -(-N2 // 32)) if axis & ROWWISE else None
     q_col = np.zeros((N2, M), np.uint8) if axis & COLWISE else None
-    s_col = _scales(axis, N2, M // 32) if axis & COLWISE else None
+    s_col = _scales(axis, N2, -(-M // 32)) if axis & COLWISE else None
     y = np.zeros((M, N2), np.uint16) if want_y else None
     rc = lib().orc_mx_quantize_dgated(_p(grad, _u16p), _p(x, _u16p), M, N, axis, act,
                                       _p(q_row, _u8p), _p(s_row, _u8p), _p(q_col, _u8p),

@@ -49,6 +49,10 @@
  *       uses in the j-th of four consecutive K steps (row L % 32, block
  *       2j + L / 32).  Tiles are stored block-tile-major; R and C are padded
  *       to whole tiles with zero bytes.
+ *   R9  a line whose length is not a multiple of 32 ends in a partial block:
+ *       its scale and codes come from its own elements alone (the same as
+ *       padding the line with zeros, which never change an amax and encode
+ *       to zero).
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fopenmp -shared
  * -fPIC (see build.py).  OpenMP only splits independent rows / columns /
@@ -554,35 +558,43 @@ void orc_scale_tiles(const uint8_t *s, int64_t R, int64_t C, uint8_t *out)
 /* MXFP8 over a tensor.                                                      */
 /* ------------------------------------------------------------------------ */
 
+/* Blocks of 32 along a line of n elements; the last one is partial when 32
+ * does not divide n (R9). */
+static int64_t nblocks(int64_t n) { return (n + 31) / 32; }
+
 /* Row-wise and column-wise MX quantisation of the bf16 tensor y[M][K].
- *   rows: q_row[M][K], s_row[M][K/32]   (blocks of 32 along K)
- *   cols: q_col[K][M], s_col[K][M/32]   (blocks of 32 along M, stored as the
- *         row-wise output of the transpose, R4)
+ *   rows: q_row[M][K], s_row[M][ceil(K/32)]   (blocks of 32 along K)
+ *   cols: q_col[K][M], s_col[K][ceil(M/32)]   (blocks of 32 along M, stored
+ *         as the row-wise output of the transpose, R4)
+ * A block at the end of a line that has fewer than 32 elements is quantised
+ * from those elements alone (R9).
  * axis bits 0, 1 select the outputs; ORC_E5M2 / ORC_ROUND_UP the variant. */
 static void mx_tensor(const uint16_t *y, int64_t M, int64_t K, unsigned axis,
                       uint8_t *q_row, uint8_t *s_row, uint8_t *q_col, uint8_t *s_col)
 {
     if (axis & 1u) {
+        const int64_t nb = nblocks(K);
 #pragma omp parallel for schedule(static)
         for (int64_t m = 0; m < M; m++) {
             double v[32];
-            for (int64_t j = 0; j < K / 32; j++) {
-                for (int i = 0; i < 32; i++)
+            for (int64_t j = 0; j < nb; j++) {
+                const int n = (int)(K - 32 * j < 32 ? K - 32 * j : 32);
+                for (int i = 0; i < n; i++)
                     v[i] = orc_bf16_value(y[m * K + 32 * j + i]);
-                orc_mx_block_mode(v, 32, q_row + m * K + 32 * j, 1, s_row + m * (K / 32) + j,
-                                  axis);
+                orc_mx_block_mode(v, n, q_row + m * K + 32 * j, 1, s_row + m * nb + j, axis);
             }
         }
     }
     if (axis & 2u) {
+        const int64_t nb = nblocks(M);
 #pragma omp parallel for schedule(static)
         for (int64_t k = 0; k < K; k++) {
             double v[32];
-            for (int64_t j = 0; j < M / 32; j++) {
-                for (int i = 0; i < 32; i++)
+            for (int64_t j = 0; j < nb; j++) {
+                const int n = (int)(M - 32 * j < 32 ? M - 32 * j : 32);
+                for (int i = 0; i < n; i++)
                     v[i] = orc_bf16_value(y[(32 * j + i) * K + k]);
-                orc_mx_block_mode(v, 32, q_col + k * M + 32 * j, 1, s_col + k * (M / 32) + j,
-                                  axis);
+                orc_mx_block_mode(v, n, q_col + k * M + 32 * j, 1, s_col + k * nb + j, axis);
             }
         }
     }
@@ -597,8 +609,8 @@ static int mx_tensor_out(const uint16_t *y, int64_t M, int64_t K, unsigned axis,
         mx_tensor(y, M, K, axis, q_row, s_row, q_col, s_col);
         return ORC_OK;
     }
-    uint8_t *sr = (axis & 1u) ? (uint8_t *)malloc((size_t)(M * (K / 32))) : NULL;
-    uint8_t *sc = (axis & 2u) ? (uint8_t *)malloc((size_t)(K * (M / 32))) : NULL;
+    uint8_t *sr = (axis & 1u) ? (uint8_t *)malloc((size_t)(M * nblocks(K))) : NULL;
+    uint8_t *sc = (axis & 2u) ? (uint8_t *)malloc((size_t)(K * nblocks(M))) : NULL;
     if (((axis & 1u) && !sr) || ((axis & 2u) && !sc)) {
         free(sr);
         free(sc);
@@ -606,9 +618,9 @@ static int mx_tensor_out(const uint16_t *y, int64_t M, int64_t K, unsigned axis,
     }
     mx_tensor(y, M, K, axis, q_row, sr, q_col, sc);
     if (sr)
-        orc_scale_tiles(sr, M, K / 32, s_row);
+        orc_scale_tiles(sr, M, nblocks(K), s_row);
     if (sc)
-        orc_scale_tiles(sc, K, M / 32, s_col);
+        orc_scale_tiles(sc, K, nblocks(M), s_col);
     free(sr);
     free(sc);
     return ORC_OK;
@@ -636,7 +648,7 @@ int orc_mx_quantize(const uint16_t *x, const uint16_t *grad, int64_t M, int64_t 
                     uint8_t *q_col, uint8_t *s_col, float *dbias, uint16_t *y_out)
 {
     int pre = fusion & 0xF;
-    if (M <= 0 || K <= 0 || M % 32 || K % 32)
+    if (M <= 0 || K <= 0)
         return ORC_ERR_SHAPE;
     if (pre > 3 || (fusion & ~0x1F) || (axis & ~31u))
         return ORC_ERR_ENUM;
@@ -667,7 +679,7 @@ int orc_mx_quantize_gated(const uint16_t *x, int64_t M, int64_t N, unsigned axis
                           uint8_t *q_row, uint8_t *s_row, uint8_t *q_col, uint8_t *s_col,
                           uint16_t *y_out)
 {
-    if (M <= 0 || N <= 0 || M % 32 || N % 32)
+    if (M <= 0 || N <= 0)
         return ORC_ERR_SHAPE;
     if ((act != 1 && act != 2) || (axis & ~31u))
         return ORC_ERR_ENUM;
@@ -691,7 +703,7 @@ int orc_mx_quantize_dgated(const uint16_t *grad, const uint16_t *x, int64_t M, i
                            unsigned axis, int act, uint8_t *q_row, uint8_t *s_row,
                            uint8_t *q_col, uint8_t *s_col, uint16_t *y_out)
 {
-    if (M <= 0 || N <= 0 || M % 32 || N % 32)
+    if (M <= 0 || N <= 0)
         return ORC_ERR_SHAPE;
     if ((act != 1 && act != 2) || (axis & ~31u))
         return ORC_ERR_ENUM;

@@ -134,10 +134,11 @@ def mx_scale_size(rows: int, cols: int, axis: int = ROWWISE | COLWISE) -> int:
 
 
 def _scales(rows, cols, axis, dev):
-    """One direction's scale tensor: [rows][cols/32], or flat in the tile layout."""
+    """One direction's scale tensor: [rows][ceil(cols/32)], or flat in the tile
+    layout."""
     if axis & SCALE_TILED:
         return _u8((mx_scale_size(rows, cols, axis),), dev)
-    return _u8((rows, cols // 32), dev)
+    return _u8((rows, -(-cols // 32)), dev)
 
 
 def mx_quantize(x, grad=None, axis=ROWWISE | COLWISE, fusion=FUSE_NONE, out=None,

@@ -95,12 +95,24 @@ void set_walk(mxk::MxArgs &a, int op, bool dbias)
 }
 
 // Bytes of the scales of a quantised [rows][cols] tensor blocked along cols:
-// compact [rows][cols / 32], or whole 32-row x 8-block tiles of 256 bytes.
+// compact [rows][ceil(cols / 32)], or whole 32-row x 8-block tiles of 256
+// bytes.
 uint64_t scale_bytes(int64_t rows, int64_t cols, bool tiled)
 {
+    const int64_t blocks = (cols + 31) / 32;
     if (!tiled)
-        return (uint64_t)(rows * (cols / 32));
-    return (uint64_t)(((rows + 31) / 32) * ((cols / 32 + 7) / 8) * 256);
+        return (uint64_t)(rows * blocks);
+    return (uint64_t)(((rows + 31) / 32) * ((blocks + 7) / 8) * 256);
+}
+
+// Sizes of an MXFP8 cast: every row of every input and output starts on a
+// 16-byte boundary (K a multiple of 8 for the bf16 input and 8-byte row
+// stores, M a multiple of 16 for the 16-byte stores of the transposed
+// output); blocks at the right and bottom edges may be partial.
+bool mx_shape_ok(int64_t M, int64_t K)
+{
+    return M > 0 && K > 0 && M % 16 == 0 && K % 8 == 0 && M <= kMaxDim && K <= kMaxDim &&
+           M * K <= kMaxElems;
 }
 
 mx_status from_hip(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
@@ -184,7 +196,7 @@ const char *mx_status_str(int s)
 
 size_t mx_quantize_workspace_size(int64_t M, int64_t K, unsigned axis_mask, int fusion)
 {
-    if (!(fusion & MX_FUSE_DBIAS) || !shape_ok(M, K, 32) || !mx_mode_ok(axis_mask) ||
+    if (!(fusion & MX_FUSE_DBIAS) || !mx_shape_ok(M, K) || !mx_mode_ok(axis_mask) ||
         (fusion & ~0x1F) || (fusion & 0xF) > MX_FUSE_DSILU)
         return 0;
     return dbias_workspace(M, K, cast_op(fusion & 0xF), (axis_mask & MX_SCALE_TILED) != 0);
@@ -192,7 +204,7 @@ size_t mx_quantize_workspace_size(int64_t M, int64_t K, unsigned axis_mask, int 
 
 size_t mx_scale_size(int64_t rows, int64_t cols, unsigned axis_mask)
 {
-    if (!shape_ok(rows, cols, 32) || !mx_mode_ok(axis_mask))
+    if (rows <= 0 || cols <= 0 || rows > kMaxDim || cols > kMaxDim || !mx_mode_ok(axis_mask))
         return 0;
     return (size_t)scale_bytes(rows, cols, (axis_mask & MX_SCALE_TILED) != 0);
 }
@@ -210,7 +222,7 @@ mx_status mx_quantize(const void *x, const void *grad, int64_t M, int64_t K, uns
     if (!x || (has_grad && !grad) || (row && (!q_row || !s_row)) ||
         (col && (!q_col || !s_col)) || (want_dbias && !dbias))
         return MX_ERR_NULL;
-    if (!shape_ok(M, K, 32))
+    if (!mx_shape_ok(M, K))
         return MX_ERR_SHAPE;
     if (!aligned(x, 16) || (has_grad && !aligned(grad, 16)) ||
         (row && (!aligned(q_row, 16) || !aligned(s_row, 16))) ||
@@ -262,7 +274,7 @@ mx_status mx_quantize_gated(const void *x, int64_t M, int64_t N, unsigned axis_m
     const bool row = axis_mask & MX_ROWWISE, col = axis_mask & MX_COLWISE;
     if (!x || (row && (!q_row || !s_row)) || (col && (!q_col || !s_col)))
         return MX_ERR_NULL;
-    if (!shape_ok(M, N, 32) || !shape_ok(M, 2 * N, 32))
+    if (!mx_shape_ok(M, N) || !mx_shape_ok(M, 2 * N))
         return MX_ERR_SHAPE;
     if (!aligned(x, 16) || (row && (!aligned(q_row, 16) || !aligned(s_row, 16))) ||
         (col && (!aligned(q_col, 16) || !aligned(s_col, 16))))
@@ -304,7 +316,7 @@ mx_status mx_quantize_dgated(const void *grad, const void *x, int64_t M, int64_t
     const bool row = axis_mask & MX_ROWWISE, col = axis_mask & MX_COLWISE;
     if (!grad || !x || (row && (!q_row || !s_row)) || (col && (!q_col || !s_col)))
         return MX_ERR_NULL;
-    if (!shape_ok(M, N, 32) || !shape_ok(M, 2 * N, 32))
+    if (!mx_shape_ok(M, N) || !mx_shape_ok(M, 2 * N))
         return MX_ERR_SHAPE;
     if (!aligned(grad, 16) || !aligned(x, 16) ||
         (row && (!aligned(q_row, 16) || !aligned(s_row, 16))) ||
@@ -359,7 +371,7 @@ mx_status mx_fused_values(const void *x, const void *grad, int64_t M, int64_t K,
     const bool has_grad = kop == mxk::OP_DGELU || kop == mxk::OP_DSILU || dgated;
     if (!x || !y || (has_grad && !grad))
         return MX_ERR_NULL;
-    if (!shape_ok(M, K, 32) || (gated && !shape_ok(M, 2 * K, 32)))
+    if (!mx_shape_ok(M, K) || (gated && !mx_shape_ok(M, 2 * K)))
         return MX_ERR_SHAPE;
     if (!aligned(x, 16) || !aligned(y, 16) || (has_grad && !aligned(grad, 16)))
         return MX_ERR_ALIGN;

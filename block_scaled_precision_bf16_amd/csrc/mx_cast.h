@@ -122,9 +122,12 @@ __device__ __forceinline__ LaneAt lane_at()
     return l;
 }
 
-// The lane's rows exist (M is a multiple of 32, so a wave is wholly inside or
-// outside) and its 8 columns exist (K is a multiple of 32, so a column group
-// of 8, a 4-lane row block and an l / l^32 pair are wholly inside or outside).
+// The lane's wave has rows inside the tensor and its 8 columns exist (K is a
+// multiple of 8, so a column group of 8 is wholly inside or outside).  Rows
+// of a live wave past M (M is a multiple of 16) read as zeros and their
+// stores fall outside the output's descriptor; a partial 32-column or 32-row
+// block at the tensor's edge thus sees zeros for its missing elements, which
+// change neither its amax nor any code.
 __device__ __forceinline__ bool lane_live(const MxArgs &a, const LaneAt &l, int tm, int tk)
 {
     return (int64_t)tm * kTileM + l.wave * 32 < a.M && (int64_t)tk * kTileK + l.cl * kColsPerLane < a.K;
@@ -141,7 +144,7 @@ __device__ __forceinline__ void load_tile(const MxArgs &a, const LaneAt &l, int 
     if constexpr (OP == OP_DSWIGLU || OP == OP_DGEGLU) {
         // output column k of [d_gate | d_linear] (each half N = lin_off wide)
         // reads gate and grad at column n = k mod N, and, in the gate half,
-        // linear at N + n; a lane's 8 columns lie in one half (N % 32 == 0)
+        // linear at N + n; a lane's 8 columns lie in one half (N % 8 == 0)
         const int64_t N = a.lin_off;
         const int64_t k = (int64_t)tk * kTileK + kColsPerLane * l.cl;
         const bool gate_half = k < N;
@@ -291,7 +294,7 @@ __device__ __forceinline__ void col_flush_q(const MxArgs &a, const ColStage &st,
     const int64_t mt = (int64_t)tm * kTileM;
     const int64_t k0 = (int64_t)tk * kTileK;
     const rsrc_t rc = make_rsrc(a.q_col, k0 * a.M + mt, a.K * a.M);
-    const bool chunk_live = mt + 16 * jr < a.M;   // M is a multiple of 32
+    const bool chunk_live = mt + 16 * jr < a.M;   // M is a multiple of 16
 #pragma unroll
     for (int i = 0; i < kTileK / 32; i++) {
         const int kr = (t >> 3) + 32 * i;
@@ -345,8 +348,8 @@ __device__ __forceinline__ void col_flush_s_tiled(const MxArgs &a, const ColStag
                                                   int tk, int n)
 {
     const int t = (int)threadIdx.x;
-    const int64_t RT = a.K >> 5;                          // row tiles of s_col
-    const int64_t CT = ((a.M >> 5) + 7) >> 3;             // block tiles
+    const int64_t RT = (a.K + 31) >> 5;                   // row tiles of s_col
+    const int64_t CT = (((a.M + 31) >> 5) + 7) >> 3;      // block tiles
     const int64_t bt0 = (int64_t)rg * (a.group >> 1);     // first block tile of the walk
     const int64_t rt0 = (int64_t)tk * (kTileK / 32);
     const int nbt = (4 * n + 7) >> 3;
@@ -375,7 +378,7 @@ __device__ __forceinline__ void col_flush_s(const MxArgs &a, const ColStage &st,
         return;
     }
     const int64_t k0 = (int64_t)tk * kTileK;
-    const int64_t nblk = a.M >> 5;                        // scales per column
+    const int64_t nblk = (a.M + 31) >> 5;                 // scales per column
     const int64_t first = (int64_t)rg * a.group * 4;      // this segment's first block
     const int64_t left = nblk - first;
     const int count = (int)(left < 4 * n ? left : 4 * n);
@@ -403,9 +406,9 @@ __device__ __forceinline__ void srow_flush(const MxArgs &a, const uint8_t (&srow
         // GEMM-ready layout: the sub-tile's 128 rows x 8 blocks are the four
         // 256-byte tiles (block tile tk, row tiles 4 tm .. 4 tm + 3), which
         // lie next to each other; thread t writes word t (tile t / 64, lane
-        // t % 64).  M is a multiple of 32, so a tile is wholly in or out.
-        const int64_t RT = a.M >> 5;
-        const int64_t bytes = RT * (((a.K >> 5) + 7) >> 3) * 256;
+        // t % 64).  Rows of a tile past M hold zero scales (padding).
+        const int64_t RT = (a.M + 31) >> 5;
+        const int64_t bytes = RT * ((((a.K + 31) >> 5) + 7) >> 3) * 256;
         const rsrc_t rs = make_rsrc(a.s_row, ((int64_t)tk * RT + 4 * (int64_t)tm) * 256, bytes);
         const int w = t >> 6, lane = t & 63;
         const uint2 v = *reinterpret_cast<const uint2 *>(srow[32 * w + (lane & 31)]);
@@ -415,7 +418,7 @@ __device__ __forceinline__ void srow_flush(const MxArgs &a, const uint8_t (&srow
     }
     const int64_t row = (int64_t)tm * kTileM + t;
     const int64_t k0 = (int64_t)tk * kTileK;
-    const int64_t nb = a.K >> 5;                          // scale bytes per row
+    const int64_t nb = (a.K + 31) >> 5;                   // scale bytes per row
     const rsrc_t rs = make_rsrc(a.s_row, (int64_t)tm * kTileM * nb + (k0 >> 5), a.M * nb);
     const uint32_t off = t < kTileM && row < a.M ? (uint32_t)(t * nb) : kDead;
     const uint8_t *src = srow[t & (kTileM - 1)];

@@ -60,14 +60,15 @@
 extern "C" {
 #endif
 
-#define MXCAST_ABI_VERSION 4
+#define MXCAST_ABI_VERSION 5
 
 typedef enum mx_status {
     MX_OK = 0,
     MX_ERR_NULL = 1,        /* a required pointer is NULL                     */
     MX_ERR_ENUM = 2,        /* unknown axis mask, fusion or activation        */
-    MX_ERR_SHAPE = 3,       /* non-positive size, or not a multiple of the    */
-                            /* block size (32 MXFP8, 16 NVFP4), or too large  */
+    MX_ERR_SHAPE = 3,       /* non-positive size, not a multiple of the size  */
+                            /* step (MXFP8: M of 16, K of 8; NVFP4: both of   */
+                            /* 16), or too large                              */
     MX_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned               */
     MX_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required     */
     MX_ERR_ALIAS = 6,       /* an output overlaps an input or another output  */
@@ -131,18 +132,23 @@ typedef enum mx_status {
 
 /*
  * MXFP8 cast of x[M][K] (bf16), block size 32.  Element bytes are E4M3
- * unless axis_mask holds MX_ELEM_E5M2.
+ * unless axis_mask holds MX_ELEM_E5M2.  When 32 does not divide K (M), the
+ * last block of each row (column) is partial: its scale and codes come from
+ * its own elements, and the scale tensors have ceil(K/32) (ceil(M/32))
+ * blocks per line.
  *   x        device, bf16 [M][K]
  *   grad     device, bf16 [M][K]; required for MX_FUSE_DGELU / DSILU, else
  *            ignored
- *   M, K     rows, columns; positive multiples of 32, each <= 2^23, M*K <= 2^40
+ *   M, K     rows, columns; M a positive multiple of 16, K of 8 (every row of
+ *            every input and output starts 16-byte aligned), each <= 2^23,
+ *            M*K <= 2^40
  *   axis_mask  MX_ROWWISE, MX_COLWISE or both (one pass over x), optionally
  *            with the format flags MX_ELEM_E5M2 / MX_SCALE_ROUND_UP and the
  *            layout flag MX_SCALE_TILED (scale tensors then have
  *            mx_scale_size() bytes in the tile layout)
  *   fusion   MX_FUSE_NONE | GELU | DGELU | DSILU, optionally | MX_FUSE_DBIAS
- *   q_row, s_row  E4M3 [M][K] and E8M0 [M][K/32]; required iff MX_ROWWISE
- *   q_col, s_col  E4M3 [K][M] and E8M0 [K][M/32]; required iff MX_COLWISE
+ *   q_row, s_row  E4M3 [M][K] and E8M0 [M][ceil(K/32)]; required iff MX_ROWWISE
+ *   q_col, s_col  E4M3 [K][M] and E8M0 [K][ceil(M/32)]; required iff MX_COLWISE
  *   dbias    fp32 [K]; required iff MX_FUSE_DBIAS
  *   workspace, workspace_bytes  device scratch of at least
  *            mx_quantize_workspace_size() bytes (0 unless MX_FUSE_DBIAS);
@@ -165,19 +171,20 @@ size_t mx_quantize_workspace_size(int64_t M, int64_t K, unsigned axis_mask, int 
  * Bytes of one scale tensor of an MXFP8 cast: the scales of a quantised
  * [rows][cols] tensor blocked along cols (s_row: rows = M, cols = K; s_col:
  * rows = K, cols = M; for the gated casts the quantised tensor's own sizes).
- * rows * cols / 32 for the compact layout, ceil(rows/32) * ceil(cols/256) *
- * 256 with MX_SCALE_TILED in axis_mask.  0 for sizes that are not positive
- * multiples of 32 or an invalid axis_mask.
+ * rows * ceil(cols/32) for the compact layout, ceil(rows/32) *
+ * ceil(ceil(cols/32)/8) * 256 with MX_SCALE_TILED in axis_mask.  0 for a
+ * non-positive size, a size above 2^23 or an invalid axis_mask.
  */
 size_t mx_scale_size(int64_t rows, int64_t cols, unsigned axis_mask);
 
 /*
  * Gated MXFP8 cast.  x is bf16 [M][2N] holding [gate | linear] (gate =
  * columns 0..N-1); the quantised tensor is y[M][N] = act(gate) * linear,
- * block size 32, M and N positive multiples of 32, M <= 2^23, 2N <= 2^23.
- * axis_mask as for mx_quantize (format flags included).
- *   q_row, s_row  E4M3 [M][N], E8M0 [M][N/32]   (iff MX_ROWWISE)
- *   q_col, s_col  E4M3 [N][M], E8M0 [N][M/32]   (iff MX_COLWISE)
+ * block size 32 (partial at the edges as for mx_quantize), M a positive
+ * multiple of 16, N of 8, M <= 2^23, 2N <= 2^23.  axis_mask as for
+ * mx_quantize (format flags included).
+ *   q_row, s_row  E4M3 [M][N], E8M0 [M][ceil(N/32)]   (iff MX_ROWWISE)
+ *   q_col, s_col  E4M3 [N][M], E8M0 [N][ceil(M/32)]   (iff MX_COLWISE)
  */
 mx_status mx_quantize_gated(const void *x, int64_t M, int64_t N, unsigned axis_mask, int act,
                             uint8_t *q_row, uint8_t *s_row, uint8_t *q_col, uint8_t *s_col,
@@ -191,10 +198,11 @@ mx_status mx_quantize_gated(const void *x, int64_t M, int64_t N, unsigned axis_m
  * tensor is dx[M][2N] = [d_gate | d_linear]:
  *   d_gate   = fl32(fl32(a' * grad) * linear),   d_linear = fl32(a * grad),
  * each rounded once to bf16; block size 32 along 2N (row-wise) and M.
- * M, N positive multiples of 32, M <= 2^23, 2N <= 2^23.  axis_mask as for
- * mx_quantize (format flags included).
- *   q_row, s_row  E4M3 [M][2N], E8M0 [M][2N/32]   (iff MX_ROWWISE)
- *   q_col, s_col  E4M3 [2N][M], E8M0 [2N][M/32]   (iff MX_COLWISE)
+ * M a positive multiple of 16, N of 8, M <= 2^23, 2N <= 2^23 (partial blocks
+ * at the edges as for mx_quantize).  axis_mask as for mx_quantize (format
+ * flags included).
+ *   q_row, s_row  E4M3 [M][2N], E8M0 [M][ceil(2N/32)]   (iff MX_ROWWISE)
+ *   q_col, s_col  E4M3 [2N][M], E8M0 [2N][ceil(M/32)]   (iff MX_COLWISE)
  * Errors as for mx_quantize_gated.
  */
 mx_status mx_quantize_dgated(const void *grad, const void *x, int64_t M, int64_t N,
@@ -206,9 +214,10 @@ mx_status mx_quantize_dgated(const void *grad, const void *x, int64_t M, int64_t
  * op = MX_FUSE_GELU / MX_FUSE_DGELU / MX_FUSE_DSILU (x, grad and y are
  * [M][K]), the gated value for op = 0x100 | MX_GATED_SWIGLU / MX_GATED_GEGLU
  * (x is [M][2K], y is [M][K]), or the gated backward for op = 0x200 |
- * MX_GATED_SWIGLU / MX_GATED_GEGLU (x is [M][2K], grad [M][K], y [M][2K]).  This is the exact tensor the fused casts quantise; it is
- * exposed so that the pre-op arithmetic can be checked on its own.  M and K
- * are positive multiples of 32, each <= 2^23 (2K <= 2^23 for gated ops).
+ * MX_GATED_SWIGLU / MX_GATED_GEGLU (x is [M][2K], grad [M][K], y [M][2K]).
+ * This is the exact tensor the fused casts quantise; it is exposed so that
+ * the pre-op arithmetic can be checked on its own.  M a positive multiple of
+ * 16, K of 8, each <= 2^23 (2K <= 2^23 for gated ops).
  */
 #define MX_OP_GATED 0x100
 #define MX_OP_DGATED 0x200

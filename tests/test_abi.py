@@ -41,7 +41,7 @@ def header_abi_version():
 
 
 def test_version_and_status_strings():
-    assert mx.mx_abi_version() == header_abi_version() == 4
+    assert mx.mx_abi_version() == header_abi_version() == 5
     for code in range(9):
         assert mx.mx_status_str(code).startswith("MX_")
     assert "unknown" in mx.mx_status_str(99)
@@ -70,7 +70,8 @@ def test_workspace_size():
         assert ws(M, K, 3, mx.FUSE_DBIAS) == walks(M, K) * K * 4
         for pre in (mx.FUSE_GELU, mx.FUSE_DGELU, mx.FUSE_DSILU):
             assert ws(M, K, 3, pre | mx.FUSE_DBIAS) == walks(M, K) * K * 4
-    assert ws(48, 64, 3, mx.FUSE_DBIAS) == 0      # invalid shape
+    assert ws(40, 64, 3, mx.FUSE_DBIAS) == 0      # invalid shape
+    assert ws(48, 72, 3, mx.FUSE_DBIAS) == 72 * 4  # partial blocks: one walk
     assert ws(64, 64, 0, mx.FUSE_DBIAS) == 0      # invalid axis
     assert ws(64, 64, 3, 0x14) == 0               # invalid pre-op
     assert ws(8192, 8192, 3 | mx.ELEM_E5M2 | mx.SCALE_ROUND_UP, mx.FUSE_DBIAS) == 16 * 8192 * 4
@@ -89,7 +90,9 @@ def test_scale_size():
     assert sz(64, 96, 1) == 64 * 3
     assert sz(64, 96, 1 | mx.SCALE_TILED) == 2 * 1 * 256              # 3 blocks pad to 8
     assert sz(96, 800, 2 | mx.SCALE_TILED) == 3 * 4 * 256             # 25 blocks -> 4 tiles
-    assert sz(48, 64, 3) == 0 and sz(64, 64, 0) == 0 and sz(64, 64, 0x43) == 0
+    assert sz(0, 64, 3) == 0 and sz(64, 64, 0) == 0 and sz(64, 64, 0x43) == 0
+    assert sz(48, 72, 3) == 48 * 3 and sz(72, 48, 3) == 72 * 2         # partial blocks
+    assert sz(48, 72, 3 | mx.SCALE_TILED) == 2 * 1 * 256
 
 
 def test_tiled_scales_alias_check_uses_tiled_size():
@@ -150,7 +153,7 @@ NULL = ctypes.c_void_p(0)
     (dict(axis=0x10), mx.MX_ERR_ENUM),
     (dict(axis=3 | mx.SCALE_TILED, x=NULL), mx.MX_ERR_NULL),
     (dict(axis=3 | mx.ELEM_E5M2 | mx.SCALE_ROUND_UP, x=NULL), mx.MX_ERR_NULL),  # flags accepted
-    (dict(axis=1 | mx.ELEM_E5M2, M=48), mx.MX_ERR_SHAPE),
+    (dict(axis=1 | mx.ELEM_E5M2, M=40), mx.MX_ERR_SHAPE),
     (dict(fusion=5), mx.MX_ERR_ENUM),
     (dict(fusion=0x20), mx.MX_ERR_ENUM),
     (dict(fusion=4), mx.MX_ERR_ENUM),
@@ -160,7 +163,8 @@ NULL = ctypes.c_void_p(0)
     (dict(axis=1, s_row=NULL), mx.MX_ERR_NULL),
     (dict(axis=2, q_col=NULL), mx.MX_ERR_NULL),
     (dict(fusion=mx.FUSE_DBIAS, dbias=NULL), mx.MX_ERR_NULL),
-    (dict(M=48), mx.MX_ERR_SHAPE),
+    (dict(M=40), mx.MX_ERR_SHAPE),             # M must be a multiple of 16
+    (dict(K=36), mx.MX_ERR_SHAPE),             # K must be a multiple of 8
     (dict(K=0), mx.MX_ERR_SHAPE),
     (dict(M=-32), mx.MX_ERR_SHAPE),
     (dict(M=1 << 31), mx.MX_ERR_SHAPE),
@@ -201,7 +205,7 @@ def test_gated_and_fused_values_reject():
     assert g(axis=0) == mx.MX_ERR_ENUM and g(axis=8) == mx.MX_ERR_ENUM and g(axis=0x23) == mx.MX_ERR_ENUM
     assert g(axis=3 | mx.ELEM_E5M2 | mx.SCALE_ROUND_UP, x=NULL) == mx.MX_ERR_NULL
     assert g(x=NULL) == mx.MX_ERR_NULL
-    assert g(N=48) == mx.MX_ERR_SHAPE and g(M=16) == mx.MX_ERR_SHAPE
+    assert g(N=44) == mx.MX_ERR_SHAPE and g(M=8) == mx.MX_ERR_SHAPE
     assert g(x=b.p("x", 4)) == mx.MX_ERR_ALIGN
     assert g(q_row=b.p("x", 32)) == mx.MX_ERR_ALIAS
     f = lambda **kw: L.mx_fused_values(kw.get("x", b.p("x")), kw.get("g", b.p("g")), kw.get("M", 64),
@@ -210,7 +214,7 @@ def test_gated_and_fused_values_reject():
     assert f(op=0) == mx.MX_ERR_ENUM and f(op=mx.FUSE_DBIAS) == mx.MX_ERR_ENUM
     assert f(op=mx.OP_GATED | 3) == mx.MX_ERR_ENUM
     assert f(y=NULL) == mx.MX_ERR_NULL and f(op=mx.FUSE_DGELU, g=NULL) == mx.MX_ERR_NULL
-    assert f(K=40) == mx.MX_ERR_SHAPE
+    assert f(K=36) == mx.MX_ERR_SHAPE
     assert f(y=b.p("q_row", 2)) == mx.MX_ERR_ALIGN
     assert f(y=b.p("x", 16)) == mx.MX_ERR_ALIAS
     assert b.untouched()
@@ -228,7 +232,7 @@ def test_dgated_and_backward_values_reject():
     assert d(axis=0x43) == mx.MX_ERR_ENUM and d(axis=2 | mx.ELEM_E5M2, x=NULL) == mx.MX_ERR_NULL
     assert d(g=NULL) == mx.MX_ERR_NULL and d(x=NULL) == mx.MX_ERR_NULL
     assert d(axis=1, s_row=NULL) == mx.MX_ERR_NULL
-    assert d(N=48) == mx.MX_ERR_SHAPE and d(M=0) == mx.MX_ERR_SHAPE
+    assert d(N=44) == mx.MX_ERR_SHAPE and d(M=0) == mx.MX_ERR_SHAPE
     assert d(g=b.p("g", 2)) == mx.MX_ERR_ALIGN and d(s_col=b.p("s_col", 8)) == mx.MX_ERR_ALIGN
     assert d(q_col=b.p("g", 16)) == mx.MX_ERR_ALIAS and d(q_row=b.p("x", 64)) == mx.MX_ERR_ALIAS
     f = lambda **kw: L.mx_fused_values(kw.get("x", b.p("x")), kw.get("g", b.p("g")), 64, 64,

@@ -86,6 +86,10 @@ def lib():
         L.orc_mx_quantize_dgated.restype = ctypes.c_int
         L.orc_mx_quantize_dgated.argtypes = [_u16p, _u16p, _i64, _i64, ctypes.c_uint,
                                              ctypes.c_int, _u8p, _u8p, _u8p, _u8p, _u16p]
+        L.orc_mx_quantize_grouped.restype = ctypes.c_int
+        L.orc_mx_quantize_grouped.argtypes = [_u16p, _u16p, _i64, ctypes.POINTER(ctypes.c_int64),
+                                              ctypes.c_int, ctypes.c_uint, ctypes.c_int,
+                                              _u8p, _u8p, _u8p, _u8p, _f32p]
         L.orc_mx_quantize_gated.restype = ctypes.c_int
         L.orc_mx_quantize_gated.argtypes = [_u16p, _i64, _i64, ctypes.c_uint, ctypes.c_int,
                                             _u8p, _u8p, _u8p, _u8p, _u16p]
@@ -294,6 +298,39 @@ def mx_quantize(x, grad=None, axis=ROWWISE | COLWISE, fusion=FUSE_NONE, want_y=F
         raise ValueError(f"oracle mx_quantize failed with code {rc}")
     out.update(q_row=q_row, s_row=s_row, q_col=q_col, s_col=s_col, dbias=dbias, y=y)
     return out
+
+
+def _scale_len(rows, cols, axis):
+    if rows == 0:
+        return 0
+    blocks = -(-cols // 32)
+    return tiled_scale_bytes(rows, blocks) if axis & SCALE_TILED else rows * blocks
+
+
+def mx_quantize_grouped(x, group_rows, grad=None, axis=ROWWISE | COLWISE, fusion=FUSE_NONE):
+    """Grouped MXFP8 cast: x[M][K] stacks len(group_rows) tensors along rows.
+    Returns flat per-group-concatenated s_row / q_col / s_col, q_row[M][K] and
+    dbias[G][K]."""
+    x = _c(x, np.uint16)
+    M, K = x.shape
+    rows = np.ascontiguousarray(group_rows, dtype=np.int64)
+    G = rows.size
+    assert rows.sum() == M
+    g = _c(grad, np.uint16) if grad is not None else None
+    sr = sum(_scale_len(int(m), K, axis) for m in rows)
+    sc = sum(_scale_len(K, int(m), axis) for m in rows)
+    q_row = np.zeros((M, K), np.uint8) if axis & ROWWISE else None
+    s_row = np.zeros(sr, np.uint8) if axis & ROWWISE else None
+    q_col = np.zeros(K * M, np.uint8) if axis & COLWISE else None
+    s_col = np.zeros(sc, np.uint8) if axis & COLWISE else None
+    dbias = np.zeros((G, K), np.float32) if fusion & FUSE_DBIAS else None
+    rc = lib().orc_mx_quantize_grouped(_p(x, _u16p), _p(g, _u16p), K,
+                                       rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), G,
+                                       axis, fusion, _p(q_row, _u8p), _p(s_row, _u8p),
+                                       _p(q_col, _u8p), _p(s_col, _u8p), _p(dbias, _f32p))
+    if rc != 0:
+        raise ValueError(f"oracle mx_quantize_grouped failed with code {rc}")
+    return dict(q_row=q_row, s_row=s_row, q_col=q_col, s_col=s_col, dbias=dbias)
 
 
 def mx_quantize_gated(x, act, axis=ROWWISE | COLWISE, want_y=False):

@@ -49,6 +49,8 @@
  *       uses in the j-th of four consecutive K steps (row L % 32, block
  *       2j + L / 32).  Tiles are stored block-tile-major; R and C are padded
  *       to whole tiles with zero bytes.
+ *   R10 grouped cast: groups stacked along rows, each cast as a tensor of its
+ *       own, outputs concatenated group after group.
  *   R9  a line whose length is not a multiple of 32 ends in a partial block:
  *       its scale and codes come from its own elements alone (the same as
  *       padding the line with zeros, which never change an amax and encode
@@ -720,6 +722,57 @@ int orc_mx_quantize_dgated(const uint16_t *grad, const uint16_t *x, int64_t M, i
     if (y != y_out)
         free(y);
     return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Grouped (per-expert) MXFP8 cast (R10).                                    */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of one scale tensor of a [rows][cols] cast blocked along cols, in the
+ * layout the axis flags ask for. */
+static int64_t scale_bytes(int64_t rows, int64_t cols, unsigned axis)
+{
+    if (rows == 0)
+        return 0;
+    return (axis & ORC_TILED) ? orc_tiled_scale_bytes(rows, nblocks(cols)) : rows * nblocks(cols);
+}
+
+/* G tensors stacked along rows: x[M][K] with group g owning rows
+ * [r_g, r_g + rows[g]), M = sum of rows[g] (a group may be empty).  Each group
+ * is cast exactly as orc_mx_quantize casts a tensor of its own; the outputs
+ * are the groups' outputs one after the other:
+ *   q_row[M][K]; s_row: group g's scales at sum_{h<g} bytes(rows[h], K);
+ *   q_col: group g's [K][rows[g]] at byte K * r_g;
+ *   s_col: group g's scales at sum_{h<g} bytes(K, rows[h]);
+ *   dbias[G][K]: group g's column sums (0 for an empty group). */
+int orc_mx_quantize_grouped(const uint16_t *x, const uint16_t *grad, int64_t K,
+                            const int64_t *rows, int G, unsigned axis, int fusion,
+                            uint8_t *q_row, uint8_t *s_row, uint8_t *q_col, uint8_t *s_col,
+                            float *dbias)
+{
+    if (G <= 0 || K <= 0)
+        return ORC_ERR_SHAPE;
+    int64_t r = 0, sr = 0, sc = 0;
+    for (int g = 0; g < G; g++) {
+        const int64_t m = rows[g];
+        if (m < 0)
+            return ORC_ERR_SHAPE;
+        if (m > 0) {
+            int rc = orc_mx_quantize(x + r * K, grad ? grad + r * K : NULL, m, K, axis, fusion,
+                                     q_row ? q_row + r * K : NULL, s_row ? s_row + sr : NULL,
+                                     q_col ? q_col + K * r : NULL, s_col ? s_col + sc : NULL,
+                                     dbias ? dbias + (int64_t)g * K : NULL, NULL);
+            if (rc != ORC_OK)
+                return rc;
+        } else if (dbias && (fusion & 0x10)) {
+            for (int64_t k = 0; k < K; k++)
+                dbias[(int64_t)g * K + k] = 0.0f;
+        }
+        sr += scale_bytes(m, K, axis);
+        sc += scale_bytes(K, m, axis);
+        r += m;
+    }
+    return ORC_OK;
 }
 
 /* ------------------------------------------------------------------------ */

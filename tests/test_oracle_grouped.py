@@ -1,0 +1,100 @@
+"""Pins for the oracle's grouped (per-expert) MXFP8 cast: groups stacked
+along rows, each cast as a tensor of its own, outputs concatenated.
+
+  * one group is the plain cast;
+  * row-wise outputs equal those of the whole stacked tensor (rows are
+    independent), for any group sizes;
+  * with group boundaries on multiples of 32 rows no column block crosses a
+    boundary, so each group's transposed output is a column slice of the
+    stacked tensor's;
+  * dbias per group equals numpy's float64 column sums of the group's rows;
+  * empty groups take no space and have zero dbias; tiled scales per group.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+
+
+def split(flat, sizes):
+    out, o = [], 0
+    for n in sizes:
+        out.append(flat[o:o + n])
+        o += n
+    assert o == flat.size
+    return out
+
+
+def test_one_group_is_the_plain_cast():
+    x = W.loguniform_rows(96, 200, seed=61)
+    g = O.mx_quantize_grouped(x, [96])
+    p = O.mx_quantize(x)
+    assert np.array_equal(g["q_row"], p["q_row"]) and np.array_equal(g["s_row"], p["s_row"].ravel())
+    assert np.array_equal(g["q_col"], p["q_col"].ravel()) and np.array_equal(g["s_col"], p["s_col"].ravel())
+
+
+@pytest.mark.parametrize("rows", [[32, 64, 16], [48, 0, 80, 16], [16, 16, 16, 16, 16]])
+def test_rowwise_equals_stacked(rows):
+    M, K = sum(rows), 136
+    x = W.loguniform_rows(M, K, seed=62)
+    g = O.mx_quantize_grouped(x, rows, axis=O.ROWWISE)
+    p = O.mx_quantize(x, axis=O.ROWWISE)
+    assert np.array_equal(g["q_row"], p["q_row"]) and np.array_equal(g["s_row"], p["s_row"].ravel())
+
+
+@pytest.mark.parametrize("mode", [0, O.ELEM_E5M2 | O.SCALE_ROUND_UP])
+def test_aligned_groups_are_column_slices(mode):
+    rows = [64, 0, 32, 128, 96]
+    M, K = sum(rows), 72
+    x = W.normal(M, K, seed=63, sigma=3.0)
+    g = O.mx_quantize_grouped(x, rows, axis=3 | mode)
+    p = O.mx_quantize(x, axis=3 | mode)
+    qc = split(g["q_col"], [K * m for m in rows])
+    sc = split(g["s_col"], [K * (m // 32) for m in rows])
+    r0 = 0
+    for m, q, s in zip(rows, qc, sc):
+        assert np.array_equal(q.reshape(K, m), p["q_col"][:, r0:r0 + m])
+        assert np.array_equal(s.reshape(K, m // 32), p["s_col"][:, r0 // 32:(r0 + m) // 32])
+        r0 += m
+
+
+def test_group_dbias_is_numpy_column_sum():
+    rows = [48, 0, 112]
+    M, K = sum(rows), 96
+    x = W.normal(M, K, seed=64, sigma=2.0)
+    g = O.mx_quantize_grouped(x, rows, fusion=O.FUSE_DBIAS)
+    xf = W.bf16_to_f32(x).astype(np.float64)
+    assert np.array_equal(g["dbias"][0], xf[:48].sum(axis=0).astype(np.float32))
+    assert np.all(g["dbias"][1] == 0)
+    assert np.array_equal(g["dbias"][2], xf[48:].sum(axis=0).astype(np.float32))
+
+
+def test_unaligned_groups_have_their_own_partial_blocks():
+    rows = [48, 80]            # the boundary at row 48 is inside a 32-row block
+    M, K = sum(rows), 40
+    x = W.loguniform_rows(M, K, seed=65)
+    g = O.mx_quantize_grouped(x, rows, axis=O.COLWISE)
+    a = O.mx_quantize(np.ascontiguousarray(x[:48]), axis=O.COLWISE)
+    b = O.mx_quantize(np.ascontiguousarray(x[48:]), axis=O.COLWISE)
+    assert np.array_equal(g["q_col"], np.concatenate([a["q_col"].ravel(), b["q_col"].ravel()]))
+    assert np.array_equal(g["s_col"], np.concatenate([a["s_col"].ravel(), b["s_col"].ravel()]))
+    # the group boundary splits what would be one block of the stacked tensor
+    p = O.mx_quantize(x, axis=O.COLWISE)
+    assert p["s_col"].shape[1] == 4 and a["s_col"].shape[1] + b["s_col"].shape[1] == 5
+
+
+def test_tiled_scales_per_group():
+    rows = [64, 0, 96]
+    M, K = sum(rows), 264
+    x = W.loguniform_rows(M, K, seed=66)
+    g = O.mx_quantize_grouped(x, rows, axis=3 | O.SCALE_TILED)
+    srs = split(g["s_row"], [O.tiled_scale_bytes(m, 9) if m else 0 for m in rows])
+    scs = split(g["s_col"], [O.tiled_scale_bytes(K, m // 32) if m else 0 for m in rows])
+    r0 = 0
+    for m, sr, sc in zip(rows, srs, scs):
+        if m:
+            c = O.mx_quantize(np.ascontiguousarray(x[r0:r0 + m]))
+            assert np.array_equal(sr, O.scale_tiles(c["s_row"]))
+            assert np.array_equal(sc, O.scale_tiles(c["s_col"]))
+        r0 += m

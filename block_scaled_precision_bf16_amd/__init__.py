@@ -6,7 +6,8 @@ libmxcast.so; PyTorch provides device memory and the stream.  If the library
 is not built, importing a function raises -- there is no fallback path.
 
 The same names as the C ABI:
-    mx_quantize, mx_quantize_workspace_size, mx_quantize_gated,
+    mx_quantize, mx_quantize_workspace_size, mx_scale_size, mx_quantize_grouped,
+    mx_quantize_grouped_workspace_size, mx_grouped_scale_size, mx_quantize_gated,
     mx_fused_values, mx_absmax_bf16, nvfp4_quantize_transpose,
     mx_status_str, mx_abi_version
 take torch tensors (bf16 inputs, or int16/uint16 holding bf16 bits, on a ROCm
@@ -33,7 +34,8 @@ OP_GATED, OP_DGATED = 0x100, 0x200
 (MX_OK, MX_ERR_NULL, MX_ERR_ENUM, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_WORKSPACE,
  MX_ERR_ALIAS, MX_ERR_HIP, MX_ERR_UNSUPPORTED) = range(9)
 
-EXPORTS = ("mx_quantize", "mx_quantize_workspace_size", "mx_scale_size", "mx_quantize_gated",
+EXPORTS = ("mx_quantize", "mx_quantize_workspace_size", "mx_scale_size", "mx_quantize_grouped",
+           "mx_quantize_grouped_workspace_size", "mx_grouped_scale_size", "mx_quantize_gated",
            "mx_quantize_dgated", "mx_fused_values",
            "mx_absmax_bf16", "nvfp4_quantize_transpose", "nvfp4_quantize_transpose_2d",
            "mx_status_str", "mx_abi_version")
@@ -65,6 +67,15 @@ def lib():
         L.mx_quantize_workspace_size.argtypes = [_i64, _i64, ctypes.c_uint, ctypes.c_int]
         L.mx_scale_size.restype = ctypes.c_size_t
         L.mx_scale_size.argtypes = [_i64, _i64, ctypes.c_uint]
+        L.mx_quantize_grouped.restype = ctypes.c_int
+        L.mx_quantize_grouped.argtypes = [_vp, _vp, _i64, _vp, ctypes.c_int, ctypes.c_uint,
+                                          ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp,
+                                          ctypes.c_size_t, _vp]
+        L.mx_quantize_grouped_workspace_size.restype = ctypes.c_size_t
+        L.mx_quantize_grouped_workspace_size.argtypes = [_i64, _vp, ctypes.c_int, ctypes.c_uint,
+                                                         ctypes.c_int]
+        L.mx_grouped_scale_size.restype = ctypes.c_size_t
+        L.mx_grouped_scale_size.argtypes = [_i64, _vp, ctypes.c_int, ctypes.c_uint, ctypes.c_int]
         L.mx_quantize_gated.restype = ctypes.c_int
         L.mx_quantize_gated.argtypes = [_vp, _i64, _i64, ctypes.c_uint, ctypes.c_int,
                                         _vp, _vp, _vp, _vp, _vp]
@@ -170,6 +181,59 @@ def mx_quantize(x, grad=None, axis=ROWWISE | COLWISE, fusion=FUSE_NONE, out=None
                            _ptr(workspace) if fusion & FUSE_DBIAS else None, ws_bytes,
                            _stream(dev, stream))
     _check(st, "mx_quantize")
+    return {k: o.get(k) for k in ("q_row", "s_row", "q_col", "s_col", "dbias")}
+
+
+def _rows_arg(group_rows):
+    """Host int64 array of group row counts (kept alive by the caller)."""
+    return (ctypes.c_int64 * len(group_rows))(*[int(r) for r in group_rows])
+
+
+def mx_quantize_grouped_workspace_size(K: int, group_rows, axis: int = ROWWISE | COLWISE,
+                                       fusion: int = FUSE_NONE) -> int:
+    rows = _rows_arg(group_rows)
+    return lib().mx_quantize_grouped_workspace_size(K, ctypes.cast(rows, _vp), len(group_rows),
+                                                    axis, fusion)
+
+
+def mx_grouped_scale_size(K: int, group_rows, axis: int, colwise: bool) -> int:
+    rows = _rows_arg(group_rows)
+    return lib().mx_grouped_scale_size(K, ctypes.cast(rows, _vp), len(group_rows), axis,
+                                       int(colwise))
+
+
+def mx_quantize_grouped(x, group_rows, grad=None, axis=ROWWISE | COLWISE, fusion=FUSE_NONE,
+                        out=None, workspace=None, stream=None):
+    """Grouped MXFP8 cast of x[M][K] = len(group_rows) tensors stacked along
+    rows.  Returns q_row [M][K], flat s_row / q_col / s_col holding the groups'
+    outputs one after the other, and dbias [G][K] (None where not requested)."""
+    x = _bf16_bits(x)
+    grad = _bf16_bits(grad) if (fusion & 0xF) in (FUSE_DGELU, FUSE_DSILU) else None
+    M, K = x.shape
+    G = len(group_rows)
+    dev = x.device
+    o = dict(out or {})
+    if axis & ROWWISE:
+        o.setdefault("q_row", _u8((M, K), dev))
+        o.setdefault("s_row", _u8((max(1, mx_grouped_scale_size(K, group_rows, axis, False)),), dev))
+    if axis & COLWISE:
+        o.setdefault("q_col", _u8((M * K,), dev))
+        o.setdefault("s_col", _u8((max(1, mx_grouped_scale_size(K, group_rows, axis, True)),), dev))
+    ws_bytes = 0
+    if fusion & FUSE_DBIAS:
+        o.setdefault("dbias", torch.empty((G, K), dtype=torch.float32, device=dev))
+        ws_bytes = mx_quantize_grouped_workspace_size(K, group_rows, axis, fusion)
+        if workspace is None:
+            workspace = _u8((max(ws_bytes, 16),), dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    rows = _rows_arg(group_rows)
+    st = lib().mx_quantize_grouped(_ptr(x), _ptr(grad), K, ctypes.cast(rows, _vp), G, axis, fusion,
+                                   _ptr(o.get("q_row")), _ptr(o.get("s_row")),
+                                   _ptr(o.get("q_col")), _ptr(o.get("s_col")),
+                                   _ptr(o.get("dbias")),
+                                   _ptr(workspace) if fusion & FUSE_DBIAS else None, ws_bytes,
+                                   _stream(dev, stream))
+    _check(st, "mx_quantize_grouped")
     return {k: o.get(k) for k in ("q_row", "s_row", "q_col", "s_col", "dbias")}
 
 

@@ -117,6 +117,55 @@ bool mx_shape_ok(int64_t M, int64_t K)
 
 mx_status from_hip(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
 
+// Group table of a grouped cast: walks per group (the walk length chosen for
+// the whole stack, at least two sub-tiles with tiled scales), rows, and each
+// group's scale offsets.  False if a group size is invalid.
+bool build_groups(const int64_t *rows, int G, int64_t K, int op, bool dbias, bool tiled,
+                  mxk::GroupTable &gt, int64_t &M, int &group)
+{
+    if (!rows || G < 1 || G > mxk::kMaxGroups)
+        return false;
+    M = 0;
+    for (int g = 0; g < G; g++) {
+        if (rows[g] < 0 || rows[g] % 16 != 0 || rows[g] > kMaxDim)
+            return false;
+        M += rows[g];
+    }
+    if (M <= 0 || M > kMaxDim || !mx_shape_ok(M, K))
+        return false;
+    const int tk = tiles(K, mxk::kTileK);
+    group = walk_group(tiles(M, mxk::kTileM), tk, op, dbias, tiled);
+    gt = mxk::GroupTable{};
+    gt.count = G;
+    int64_t walks = 0, r = 0, sr = 0, sc = 0;
+    for (int g = 0; g < G; g++) {
+        gt.walk0[g] = (int)walks;
+        gt.row0[g] = r;
+        r += rows[g];
+        gt.srow_off[g] = sr;
+        gt.scol_off[g] = sc;
+        walks += (tiles(rows[g], mxk::kTileM) + group - 1) / group;
+        if (rows[g] > 0) {
+            sr += (int64_t)scale_bytes(rows[g], K, tiled);
+            sc += (int64_t)scale_bytes(K, rows[g], tiled);
+        }
+    }
+    gt.walk0[G] = (int)walks;
+    gt.row0[G] = M;
+    return walks > 0;
+}
+
+// Total scale bytes of a grouped cast (the groups' scale tensors one after
+// the other).
+uint64_t grouped_scale_bytes(const int64_t *rows, int G, int64_t K, bool colwise, bool tiled)
+{
+    uint64_t n = 0;
+    for (int g = 0; g < G; g++)
+        if (rows[g] > 0)
+            n += colwise ? scale_bytes(K, rows[g], tiled) : scale_bytes(rows[g], K, tiled);
+    return n;
+}
+
 }  // namespace
 
 // NVFP4 quantize-transpose with 1D (two_d = false) or 16 x 16 block scaling.
@@ -263,6 +312,99 @@ mx_status mx_quantize(const void *x, const void *grad, int64_t M, int64_t K, uns
     if (st != MX_OK || !want_dbias)
         return st;
     return from_hip(mxk::launch_dbias_reduce(a.partials, a.groups_m, K, dbias, stream));
+}
+
+size_t mx_quantize_grouped_workspace_size(int64_t K, const int64_t *group_rows, int G,
+                                          unsigned axis_mask, int fusion)
+{
+    if (!(fusion & MX_FUSE_DBIAS) || !mx_mode_ok(axis_mask) || (fusion & ~0x1F) ||
+        (fusion & 0xF) > MX_FUSE_DSILU)
+        return 0;
+    mxk::GroupTable gt;
+    int64_t M;
+    int group;
+    if (!build_groups(group_rows, G, K, cast_op(fusion & 0xF), true,
+                      (axis_mask & MX_SCALE_TILED) != 0, gt, M, group))
+        return 0;
+    return (size_t)gt.walk0[G] * (size_t)K * sizeof(float);
+}
+
+size_t mx_grouped_scale_size(int64_t K, const int64_t *group_rows, int G, unsigned axis_mask,
+                             int colwise)
+{
+    mxk::GroupTable gt;
+    int64_t M;
+    int group;
+    if (!mx_mode_ok(axis_mask) || !build_groups(group_rows, G, K, mxk::OP_PLAIN, false,
+                                                (axis_mask & MX_SCALE_TILED) != 0, gt, M, group))
+        return 0;
+    return (size_t)grouped_scale_bytes(group_rows, G, K, colwise != 0,
+                                       (axis_mask & MX_SCALE_TILED) != 0);
+}
+
+mx_status mx_quantize_grouped(const void *x, const void *grad, int64_t K, const int64_t *group_rows,
+                              int G, unsigned axis_mask, int fusion, uint8_t *q_row,
+                              uint8_t *s_row, uint8_t *q_col, uint8_t *s_col, float *dbias,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    const int pre = fusion & 0xF;
+    const bool want_dbias = (fusion & MX_FUSE_DBIAS) != 0;
+    if (!mx_mode_ok(axis_mask) || (fusion & ~0x1F) || pre > MX_FUSE_DSILU)
+        return MX_ERR_ENUM;
+    const bool has_grad = pre == MX_FUSE_DGELU || pre == MX_FUSE_DSILU;
+    const bool row = axis_mask & MX_ROWWISE, col = axis_mask & MX_COLWISE;
+    if (!x || !group_rows || (has_grad && !grad) || (row && (!q_row || !s_row)) ||
+        (col && (!q_col || !s_col)) || (want_dbias && !dbias))
+        return MX_ERR_NULL;
+    const int op = cast_op(pre);
+    const bool tiled = (axis_mask & MX_SCALE_TILED) != 0;
+    mxk::GroupTable gt;
+    int64_t M;
+    int group;
+    if (!build_groups(group_rows, G, K, op, want_dbias, tiled, gt, M, group))
+        return MX_ERR_SHAPE;
+    if (!aligned(x, 16) || (has_grad && !aligned(grad, 16)) ||
+        (row && (!aligned(q_row, 16) || !aligned(s_row, 16))) ||
+        (col && (!aligned(q_col, 16) || !aligned(s_col, 16))) ||
+        (want_dbias && (!aligned(dbias, 4) || (workspace && !aligned(workspace, 16)))))
+        return MX_ERR_ALIGN;
+    const size_t need = want_dbias ? (size_t)gt.walk0[G] * (size_t)K * sizeof(float) : 0;
+    if (want_dbias && (!workspace || workspace_bytes < need))
+        return MX_ERR_WORKSPACE;
+    const uint64_t n = (uint64_t)(M * K);
+    const Span in[2] = {{x, 2 * n}, {has_grad ? grad : nullptr, 2 * n}};
+    const Span out[6] = {{row ? q_row : nullptr, n},
+                         {row ? s_row : nullptr, grouped_scale_bytes(group_rows, G, K, false, tiled)},
+                         {col ? q_col : nullptr, n},
+                         {col ? s_col : nullptr, grouped_scale_bytes(group_rows, G, K, true, tiled)},
+                         {want_dbias ? dbias : nullptr, 4 * (uint64_t)K * (uint64_t)G},
+                         {want_dbias ? workspace : nullptr, need}};
+    if (any_alias(in, 2, out, 6))
+        return MX_ERR_ALIAS;
+
+    mxk::MxArgs a;
+    a.x = static_cast<const uint16_t *>(x);
+    a.aux = has_grad ? static_cast<const uint16_t *>(grad) : nullptr;
+    a.M = M;
+    a.K = K;
+    a.ldx = K;
+    a.ldg = K;
+    a.lin_off = 0;
+    a.q_row = q_row;
+    a.s_row = s_row;
+    a.q_col = q_col;
+    a.s_col = s_col;
+    a.partials = want_dbias ? static_cast<float *>(workspace) : nullptr;
+    a.tiled = tiled;
+    a.tiles_k = tiles(K, mxk::kTileK);
+    a.tiles_m = tiles(M, mxk::kTileM);
+    a.group = group;
+    a.groups_m = gt.walk0[G];
+    mx_status st = from_hip(mxk::launch_mx_cast_grouped(op, axis_mask & 3u, axis_mask & kFmtBits,
+                                                        want_dbias, a, gt, stream));
+    if (st != MX_OK || !want_dbias)
+        return st;
+    return from_hip(mxk::launch_dbias_reduce_grouped(a.partials, gt, K, dbias, stream));
 }
 
 mx_status mx_quantize_gated(const void *x, int64_t M, int64_t N, unsigned axis_mask, int act,

@@ -69,6 +69,18 @@ struct MxArgs {
     int tiled;             // scales in the GEMM-ready tile layout (walks of >= 2 sub-tiles)
 };
 
+// Grouped cast: groups stacked along M, each cast as a tensor of its own in
+// one launch.  Walks never cross a group boundary; walk0 numbers them across
+// all groups.
+constexpr int kMaxGroups = 64;
+struct GroupTable {
+    int count;                        // groups
+    int walk0[kMaxGroups + 1];        // first walk of each group; walk0[count] = all walks
+    int64_t row0[kMaxGroups + 1];     // first row of each group; row0[count] = M
+    int64_t srow_off[kMaxGroups];     // byte offset of each group's row scales
+    int64_t scol_off[kMaxGroups];     // byte offset of each group's column scales
+};
+
 struct Nv4Args {
     const uint16_t *x;
     int64_t M, K;
@@ -82,6 +94,12 @@ struct Nv4Args {
 // op: 0 plain, 1 GELU, 2 dGELU, 3 SwiGLU, 4 GeGLU.
 hipError_t launch_mx_cast(int op, unsigned axis, unsigned fmt, bool dbias, const MxArgs &a,
                           hipStream_t s);
+// The same over the groups of gt (one launch); a.M, a.groups_m and the output
+// pointers describe the whole stack.
+hipError_t launch_mx_cast_grouped(int op, unsigned axis, unsigned fmt, bool dbias, const MxArgs &a,
+                                  const GroupTable &gt, hipStream_t s);
+hipError_t launch_dbias_reduce_grouped(const float *partials, const GroupTable &gt, int64_t K,
+                                       float *dbias, hipStream_t s);
 hipError_t launch_dbias_reduce(const float *partials, int segments, int64_t K, float *dbias,
                                hipStream_t s);
 // op as above (1..7); gated ops read x[M][2K]; the gated backward ops read

@@ -383,7 +383,9 @@ __device__ __forceinline__ void col_flush_s(const MxArgs &a, const ColStage &st,
     const int64_t left = nblk - first;
     const int count = (int)(left < 4 * n ? left : 4 * n);
     const rsrc_t rs = make_rsrc(a.s_col, k0 * nblk + first, a.K * nblk);
-    const int64_t align = nblk | first | count;
+    // the piece width also respects the alignment of s_col itself (a group's
+    // column scales may start on any 8-byte boundary)
+    const int64_t align = nblk | first | count | (int64_t)(reinterpret_cast<uintptr_t>(a.s_col) & 15);
     if ((align & 15) == 0)
         col_flush_s_ch<AUX, 16>(a, st, rs, k0, nblk, count);
     else if ((align & 7) == 0)
@@ -479,12 +481,10 @@ constexpr int min_blocks()
     return OP == OP_PLAIN || OP == OP_DSWIGLU || OP == OP_DGEGLU || DBIAS ? 1 : 3;
 }
 
+// Walk rg of strip tk: the whole of a workgroup's work.
 template <int OP, int FMT, bool ROW, bool COL, bool DBIAS>
-__global__ __launch_bounds__(kThreads, (min_blocks<OP, DBIAS>())) void mx_cast_kernel(MxArgs a)
+__device__ __forceinline__ void mx_cast_walk(const MxArgs &a, int rg, int tk)
 {
-    const int job = xcd_tile((int)blockIdx.x, (int)gridDim.x);
-    const int rg = job / a.tiles_k;
-    const int tk = job - rg * a.tiles_k;
     const int tm0 = rg * a.group;
     const int n = (a.tiles_m - tm0) < a.group ? (a.tiles_m - tm0) : a.group;
     const LaneAt l = lane_at();
@@ -560,58 +560,110 @@ __global__ __launch_bounds__(kThreads, (min_blocks<OP, DBIAS>())) void mx_cast_k
 }
 
 template <int OP, int FMT, bool ROW, bool COL, bool DBIAS>
-hipError_t launch_one(const MxArgs &a, hipStream_t s)
+__global__ __launch_bounds__(kThreads, (min_blocks<OP, DBIAS>())) void mx_cast_kernel(MxArgs a)
+{
+    const int job = xcd_tile((int)blockIdx.x, (int)gridDim.x);
+    const int rg = job / a.tiles_k;
+    mx_cast_walk<OP, FMT, ROW, COL, DBIAS>(a, rg, job - rg * a.tiles_k);
+}
+
+// Grouped: walk rg (numbered across all groups) belongs to the group g with
+// walk0[g] <= rg < walk0[g + 1]; that group is cast as a tensor of its own,
+// its inputs and outputs found at the group's offsets.
+template <int OP, int FMT, bool ROW, bool COL, bool DBIAS>
+__global__ __launch_bounds__(kThreads, (min_blocks<OP, DBIAS>())) void mx_cast_grouped_kernel(
+    MxArgs a, GroupTable gt)
+{
+    const int job = xcd_tile((int)blockIdx.x, (int)gridDim.x);
+    const int rg = job / a.tiles_k;
+    const int tk = job - rg * a.tiles_k;
+    int g = 0;
+    while (g + 1 < gt.count && gt.walk0[g + 1] <= rg)
+        g++;
+    const int64_t r0 = gt.row0[g];
+    MxArgs b = a;
+    b.M = gt.row0[g + 1] - r0;
+    b.x = a.x + r0 * a.ldx;
+    b.aux = a.aux ? a.aux + r0 * a.ldg : nullptr;
+    b.q_row = a.q_row ? a.q_row + r0 * a.K : nullptr;
+    b.s_row = a.s_row ? a.s_row + gt.srow_off[g] : nullptr;
+    b.q_col = a.q_col ? a.q_col + a.K * r0 : nullptr;
+    b.s_col = a.s_col ? a.s_col + gt.scol_off[g] : nullptr;
+    b.partials = a.partials ? a.partials + (int64_t)gt.walk0[g] * a.K : nullptr;
+    b.tiles_m = (int)((b.M + kTileM - 1) / kTileM);
+    b.groups_m = gt.walk0[g + 1] - gt.walk0[g];
+    mx_cast_walk<OP, FMT, ROW, COL, DBIAS>(b, rg - gt.walk0[g], tk);
+}
+
+template <int OP, int FMT, bool ROW, bool COL, bool DBIAS, bool GROUPED>
+hipError_t launch_one(const MxArgs &a, const GroupTable *gt, hipStream_t s)
 {
     const int blocks = a.groups_m * a.tiles_k;
-    hipLaunchKernelGGL((mx_cast_kernel<OP, FMT, ROW, COL, DBIAS>), dim3(blocks), dim3(kThreads),
-                       0, s, a);
+    if constexpr (GROUPED)
+        hipLaunchKernelGGL((mx_cast_grouped_kernel<OP, FMT, ROW, COL, DBIAS>), dim3(blocks),
+                           dim3(kThreads), 0, s, a, *gt);
+    else
+        hipLaunchKernelGGL((mx_cast_kernel<OP, FMT, ROW, COL, DBIAS>), dim3(blocks),
+                           dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
-template <int OP, int FMT, bool DBIAS>
-hipError_t launch_axis(unsigned axis, const MxArgs &a, hipStream_t s)
+template <int OP, int FMT, bool DBIAS, bool GROUPED>
+hipError_t launch_axis(unsigned axis, const MxArgs &a, const GroupTable *gt, hipStream_t s)
 {
     switch (axis) {
-    case 1u: return launch_one<OP, FMT, true, false, DBIAS>(a, s);
-    case 2u: return launch_one<OP, FMT, false, true, DBIAS>(a, s);
-    case 3u: return launch_one<OP, FMT, true, true, DBIAS>(a, s);
+    case 1u: return launch_one<OP, FMT, true, false, DBIAS, GROUPED>(a, gt, s);
+    case 2u: return launch_one<OP, FMT, false, true, DBIAS, GROUPED>(a, gt, s);
+    case 3u: return launch_one<OP, FMT, true, true, DBIAS, GROUPED>(a, gt, s);
     default: return hipErrorInvalidValue;
     }
 }
 
-// Every pre-op, output set and dbias choice of one format.
-template <int FMT>
-hipError_t launch_mx_cast_fmt(int op, unsigned axis, bool dbias, const MxArgs &a, hipStream_t s)
+// Every pre-op, output set and dbias choice of one format, plain (gt null)
+// or grouped.
+template <int FMT, bool GROUPED>
+hipError_t launch_mx_cast_fmt(int op, unsigned axis, bool dbias, const MxArgs &a,
+                              const GroupTable *gt, hipStream_t s)
 {
     switch (op) {
     case OP_PLAIN:
-        return dbias ? launch_axis<OP_PLAIN, FMT, true>(axis, a, s) : launch_axis<OP_PLAIN, FMT, false>(axis, a, s);
+        return dbias ? launch_axis<OP_PLAIN, FMT, true, GROUPED>(axis, a, gt, s)
+                     : launch_axis<OP_PLAIN, FMT, false, GROUPED>(axis, a, gt, s);
     case OP_GELU:
-        return dbias ? launch_axis<OP_GELU, FMT, true>(axis, a, s) : launch_axis<OP_GELU, FMT, false>(axis, a, s);
+        return dbias ? launch_axis<OP_GELU, FMT, true, GROUPED>(axis, a, gt, s)
+                     : launch_axis<OP_GELU, FMT, false, GROUPED>(axis, a, gt, s);
     case OP_DGELU:
-        return dbias ? launch_axis<OP_DGELU, FMT, true>(axis, a, s) : launch_axis<OP_DGELU, FMT, false>(axis, a, s);
+        return dbias ? launch_axis<OP_DGELU, FMT, true, GROUPED>(axis, a, gt, s)
+                     : launch_axis<OP_DGELU, FMT, false, GROUPED>(axis, a, gt, s);
     case OP_SWIGLU:
-        return launch_axis<OP_SWIGLU, FMT, false>(axis, a, s);
+        return launch_axis<OP_SWIGLU, FMT, false, GROUPED>(axis, a, gt, s);
     case OP_GEGLU:
-        return launch_axis<OP_GEGLU, FMT, false>(axis, a, s);
+        return launch_axis<OP_GEGLU, FMT, false, GROUPED>(axis, a, gt, s);
     case OP_DSILU:
-        return dbias ? launch_axis<OP_DSILU, FMT, true>(axis, a, s) : launch_axis<OP_DSILU, FMT, false>(axis, a, s);
+        return dbias ? launch_axis<OP_DSILU, FMT, true, GROUPED>(axis, a, gt, s)
+                     : launch_axis<OP_DSILU, FMT, false, GROUPED>(axis, a, gt, s);
     case OP_DSWIGLU:
-        return launch_axis<OP_DSWIGLU, FMT, false>(axis, a, s);
+        return launch_axis<OP_DSWIGLU, FMT, false, GROUPED>(axis, a, gt, s);
     case OP_DGEGLU:
-        return launch_axis<OP_DGEGLU, FMT, false>(axis, a, s);
+        return launch_axis<OP_DGEGLU, FMT, false, GROUPED>(axis, a, gt, s);
     default:
         return hipErrorInvalidValue;
     }
 }
 
-// Instantiated once each, in mx_cast_fmt*.hip.
-extern template hipError_t launch_mx_cast_fmt<0>(int, unsigned, bool, const MxArgs &, hipStream_t);
-extern template hipError_t launch_mx_cast_fmt<kFmtE5M2>(int, unsigned, bool, const MxArgs &,
-                                                        hipStream_t);
-extern template hipError_t launch_mx_cast_fmt<kFmtRoundUp>(int, unsigned, bool, const MxArgs &,
-                                                           hipStream_t);
-extern template hipError_t launch_mx_cast_fmt<kFmtE5M2 | kFmtRoundUp>(int, unsigned, bool,
-                                                                      const MxArgs &, hipStream_t);
+// Instantiated once each, in mx_cast_fmt_*.hip (plain) and mx_cast_grp_*.hip
+// (grouped).
+#define MXK_DECLARE_FMT(F, G)                                                                   \
+    extern template hipError_t launch_mx_cast_fmt<F, G>(int, unsigned, bool, const MxArgs &,   \
+                                                        const GroupTable *, hipStream_t);
+MXK_DECLARE_FMT(0, false)
+MXK_DECLARE_FMT(kFmtE5M2, false)
+MXK_DECLARE_FMT(kFmtRoundUp, false)
+MXK_DECLARE_FMT(kFmtE5M2 | kFmtRoundUp, false)
+MXK_DECLARE_FMT(0, true)
+MXK_DECLARE_FMT(kFmtE5M2, true)
+MXK_DECLARE_FMT(kFmtRoundUp, true)
+MXK_DECLARE_FMT(kFmtE5M2 | kFmtRoundUp, true)
+#undef MXK_DECLARE_FMT
 
 }  // namespace mxk

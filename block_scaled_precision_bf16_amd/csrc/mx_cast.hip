@@ -20,6 +20,22 @@ __global__ __launch_bounds__(256) void dbias_reduce_kernel(const float *partials
     dbias[k] = acc;
 }
 
+// dbias[g][k] = sum over group g's walks (in order) of partials[walk][k];
+// 0 for a group without rows.  Grid: (ceil(K / 256), groups).
+__global__ __launch_bounds__(256) void dbias_reduce_grouped_kernel(const float *partials,
+                                                                   GroupTable gt, int64_t K,
+                                                                   float *dbias)
+{
+    const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int g = (int)blockIdx.y;
+    if (k >= K)
+        return;
+    float acc = 0.0f;
+    for (int t = gt.walk0[g]; t < gt.walk0[g + 1]; t++)
+        acc += partials[(int64_t)t * K + k];
+    dbias[(int64_t)g * K + k] = acc;
+}
+
 // y = fused value of each element; 8 elements per thread.  Gated ops read
 // the row [gate | linear] of width 2K; the gated backward ops read that row
 // and grad[M][K] and write the row [d_gate | d_linear] of y[M][2K].
@@ -58,16 +74,30 @@ __global__ __launch_bounds__(256) void fused_values_kernel(const uint16_t *x, co
     *reinterpret_cast<uint4 *>(y + i) = o;
 }
 
+template <bool GROUPED>
+static hipError_t dispatch_fmt(int op, unsigned axis, unsigned fmt, bool dbias, const MxArgs &a,
+                               const GroupTable *gt, hipStream_t s)
+{
+    switch (fmt) {
+    case 0u: return launch_mx_cast_fmt<0, GROUPED>(op, axis, dbias, a, gt, s);
+    case kFmtE5M2: return launch_mx_cast_fmt<kFmtE5M2, GROUPED>(op, axis, dbias, a, gt, s);
+    case kFmtRoundUp: return launch_mx_cast_fmt<kFmtRoundUp, GROUPED>(op, axis, dbias, a, gt, s);
+    case kFmtE5M2 | kFmtRoundUp:
+        return launch_mx_cast_fmt<kFmtE5M2 | kFmtRoundUp, GROUPED>(op, axis, dbias, a, gt, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_mx_cast(int op, unsigned axis, unsigned fmt, bool dbias, const MxArgs &a,
                           hipStream_t s)
 {
-    switch (fmt) {
-    case 0u: return launch_mx_cast_fmt<0>(op, axis, dbias, a, s);
-    case kFmtE5M2: return launch_mx_cast_fmt<kFmtE5M2>(op, axis, dbias, a, s);
-    case kFmtRoundUp: return launch_mx_cast_fmt<kFmtRoundUp>(op, axis, dbias, a, s);
-    case kFmtE5M2 | kFmtRoundUp: return launch_mx_cast_fmt<kFmtE5M2 | kFmtRoundUp>(op, axis, dbias, a, s);
-    default: return hipErrorInvalidValue;
-    }
+    return dispatch_fmt<false>(op, axis, fmt, dbias, a, nullptr, s);
+}
+
+hipError_t launch_mx_cast_grouped(int op, unsigned axis, unsigned fmt, bool dbias, const MxArgs &a,
+                                  const GroupTable &gt, hipStream_t s)
+{
+    return dispatch_fmt<true>(op, axis, fmt, dbias, a, &gt, s);
 }
 
 hipError_t launch_dbias_reduce(const float *partials, int segments, int64_t K, float *dbias,
@@ -76,6 +106,14 @@ hipError_t launch_dbias_reduce(const float *partials, int segments, int64_t K, f
     const int64_t blocks = (K + 255) / 256;
     hipLaunchKernelGGL(dbias_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, partials,
                        segments, K, dbias);
+    return hipGetLastError();
+}
+
+hipError_t launch_dbias_reduce_grouped(const float *partials, const GroupTable &gt, int64_t K,
+                                       float *dbias, hipStream_t s)
+{
+    const dim3 grid((unsigned)((K + 255) / 256), (unsigned)gt.count);
+    hipLaunchKernelGGL(dbias_reduce_grouped_kernel, grid, dim3(256), 0, s, partials, gt, K, dbias);
     return hipGetLastError();
 }
 

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MXCAST_ABI_VERSION 5
+#define MXCAST_ABI_VERSION 6
 
 typedef enum mx_status {
     MX_OK = 0,
@@ -176,6 +176,47 @@ size_t mx_quantize_workspace_size(int64_t M, int64_t K, unsigned axis_mask, int 
  * non-positive size, a size above 2^23 or an invalid axis_mask.
  */
 size_t mx_scale_size(int64_t rows, int64_t cols, unsigned axis_mask);
+
+/*
+ * Grouped (per-expert) MXFP8 cast: G tensors stacked along rows, cast in one
+ * launch, each exactly as mx_quantize would cast it on its own.  The pages
+ * name a grouped quantize-transpose (TransformerEngine PR 3291, the
+ * group_quantize_transpose_nvfp4 row of its "Important Files Changed"
+ * table) whose non-Hadamard path was not ready; this is that operation for
+ * MXFP8.
+ *   x, grad      device, bf16 [M][K], M = sum of group_rows; group g owns rows
+ *                r_g .. r_g + group_rows[g] - 1, r_g = sum_{h<g} group_rows[h]
+ *   group_rows   HOST array of G row counts, each >= 0 and a multiple of 16
+ *                (an empty group is allowed); 1 <= G <= 64, M > 0
+ *   axis_mask, fusion  as for mx_quantize (format and layout flags included)
+ *   q_row        [M][K]: the groups' row-wise elements (the stacked tensor's)
+ *   s_row        the groups' row scales one after the other, group g's
+ *                mx_scale_size(group_rows[g], K) bytes each (for the compact
+ *                layout this is [M][ceil(K/32)])
+ *   q_col        the groups' transposed elements one after the other: group
+ *                g's [K][group_rows[g]] at byte K * r_g
+ *   s_col        the groups' column scales one after the other, group g's
+ *                mx_scale_size(K, group_rows[g]) bytes each
+ *   dbias        fp32 [G][K], group g's column sums (0 for an empty group)
+ *   workspace    mx_quantize_grouped_workspace_size() bytes with dbias
+ * Errors as for mx_quantize; MX_ERR_SHAPE also for G out of range or a bad
+ * group size.
+ */
+mx_status mx_quantize_grouped(const void *x, const void *grad, int64_t K,
+                              const int64_t *group_rows, int G, unsigned axis_mask, int fusion,
+                              uint8_t *q_row, uint8_t *s_row, uint8_t *q_col, uint8_t *s_col,
+                              float *dbias, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/* Workspace bytes of mx_quantize_grouped (0 without dbias or for invalid
+ * arguments). */
+size_t mx_quantize_grouped_workspace_size(int64_t K, const int64_t *group_rows, int G,
+                                          unsigned axis_mask, int fusion);
+
+/* Total bytes of the row scales (colwise = 0) or column scales (colwise = 1)
+ * of mx_quantize_grouped (0 for invalid arguments). */
+size_t mx_grouped_scale_size(int64_t K, const int64_t *group_rows, int G, unsigned axis_mask,
+                             int colwise);
 
 /*
  * Gated MXFP8 cast.  x is bf16 [M][2N] holding [gate | linear] (gate =

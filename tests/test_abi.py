@@ -41,7 +41,7 @@ def header_abi_version():
 
 
 def test_version_and_status_strings():
-    assert mx.mx_abi_version() == header_abi_version() == 5
+    assert mx.mx_abi_version() == header_abi_version() == 6
     for code in range(9):
         assert mx.mx_status_str(code).startswith("MX_")
     assert "unknown" in mx.mx_status_str(99)
@@ -266,6 +266,50 @@ def test_nvfp4_and_absmax_reject():
     assert a(n=0) == mx.MX_ERR_SHAPE and a(x=NULL) == mx.MX_ERR_NULL
     assert a(x=b.p("x", 2)) == mx.MX_ERR_ALIGN
     assert a(amax=b.p("x", 16)) == mx.MX_ERR_ALIAS
+    assert b.untouched()
+
+
+def test_grouped_sizes():
+    ws, sz = mx.mx_quantize_grouped_workspace_size, mx.mx_grouped_scale_size
+    # walks per group with the walk length of the whole stack (here 1 sub-tile)
+    assert walks(512, 256) == 4
+    assert ws(256, [128, 0, 256, 128], 3, mx.FUSE_DBIAS) == (1 + 0 + 2 + 1) * 256 * 4
+    assert ws(256, [128, 0, 256, 128], 3, mx.FUSE_NONE) == 0
+    # tiled: walks of at least 2 sub-tiles
+    assert ws(256, [128, 0, 256, 128], 3 | mx.SCALE_TILED, mx.FUSE_DBIAS) == 3 * 256 * 4
+    assert sz(96, [48, 0, 80], 3, False) == 128 * 3
+    assert sz(96, [48, 0, 80], 3, True) == 96 * 2 + 96 * 3
+    assert sz(96, [48, 0, 80], 3 | mx.SCALE_TILED, True) == 3 * 1 * 256 + 3 * 1 * 256
+    assert sz(96, [40], 3, False) == 0 and sz(96, [0, 0], 3, False) == 0 and sz(96, [], 3, False) == 0
+
+
+def test_grouped_rejects():
+    b = Bufs(64, 96)
+    L = mx.lib()
+
+    def gq(rows=(32, 0, 32), G=None, **kw):
+        arr = (ctypes.c_int64 * max(1, len(rows)))(*rows)
+        return L.mx_quantize_grouped(kw.get("x", b.p("x")), kw.get("g", b.p("g")), kw.get("K", 96),
+                                     kw.get("rows_p", ctypes.cast(arr, ctypes.c_void_p)),
+                                     len(rows) if G is None else G, kw.get("axis", 3),
+                                     kw.get("fusion", 0), kw.get("q_row", b.p("q_row")),
+                                     kw.get("s_row", b.p("s_row")), kw.get("q_col", b.p("q_col")),
+                                     kw.get("s_col", b.p("s_col")), kw.get("dbias", b.p("dbias")),
+                                     kw.get("ws", b.p("ws")), kw.get("ws_bytes", 4096), None)
+    assert gq(axis=0) == mx.MX_ERR_ENUM and gq(fusion=5) == mx.MX_ERR_ENUM
+    assert gq(x=NULL) == mx.MX_ERR_NULL and gq(rows_p=NULL) == mx.MX_ERR_NULL
+    assert gq(fusion=mx.FUSE_DGELU, g=NULL) == mx.MX_ERR_NULL
+    assert gq(rows=(32, 8)) == mx.MX_ERR_SHAPE          # not a multiple of 16
+    assert gq(rows=(32, -16, 48)) == mx.MX_ERR_SHAPE
+    assert gq(rows=(0, 0)) == mx.MX_ERR_SHAPE            # no rows at all
+    assert gq(rows=(32,), G=0) == mx.MX_ERR_SHAPE
+    assert gq(rows=tuple([16] * 65)) == mx.MX_ERR_SHAPE   # more than 64 groups
+    assert gq(K=36) == mx.MX_ERR_SHAPE
+    assert gq(x=b.p("x", 8)) == mx.MX_ERR_ALIGN
+    assert gq(fusion=mx.FUSE_DBIAS, ws=NULL) == mx.MX_ERR_WORKSPACE
+    assert gq(fusion=mx.FUSE_DBIAS, ws_bytes=16) == mx.MX_ERR_WORKSPACE
+    assert gq(q_col=b.p("x", 16)) == mx.MX_ERR_ALIAS
+    assert gq(fusion=mx.FUSE_DBIAS, dbias=b.p("ws", 0)) == mx.MX_ERR_ALIAS
     assert b.untouched()
 
 

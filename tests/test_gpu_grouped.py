@@ -1,0 +1,88 @@
+"""GPU parity of the grouped (per-expert) MXFP8 cast against the oracle, byte
+for byte: groups of any multiple of 16 rows (empty ones included) stacked
+along M, cast in one launch, outputs concatenated group after group; dbias
+per group within the dbias tolerance.  Covers walks that end at group
+boundaries, groups smaller than a sub-tile, the format and layout flags and
+an MoE-like set of eight experts."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_precision_bf16_amd as mx
+import oracle as O
+import workloads as W
+from gpu_util import assert_dbias_close, mx_outputs_equal, to_dev
+
+pytestmark = pytest.mark.gpu
+
+GROUPS = [([128, 0, 256, 128], 256), ([48, 0, 80, 16], 136), ([16] * 5, 40),
+          ([2048, 16, 0, 1520], 1056), ([32], 32)]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def threads():
+    O.set_threads(min(16, len(os.sched_getaffinity(0))))
+
+
+@pytest.mark.parametrize("flags", [0, mx.SCALE_TILED, mx.ELEM_E5M2 | mx.SCALE_ROUND_UP],
+                         ids=["plain", "tiled", "e5m2-up"])
+@pytest.mark.parametrize("axis", [1, 2, 3])
+@pytest.mark.parametrize("rows,K", GROUPS)
+def test_grouped_plain(rows, K, axis, flags):
+    M = sum(rows)
+    x = W.loguniform_rows(M, K, seed=6000 + M + K)
+    g = mx.mx_quantize_grouped(to_dev(x), rows, axis=axis | flags)
+    torch.cuda.synchronize()
+    o = O.mx_quantize_grouped(x, rows, axis=axis | flags)
+    mx_outputs_equal(g, o, f"grouped {rows} K={K} axis {axis} flags {flags}")
+
+
+@pytest.mark.parametrize("fusion", [mx.FUSE_DBIAS, mx.FUSE_GELU | mx.FUSE_DBIAS,
+                                    mx.FUSE_DSILU | mx.FUSE_DBIAS, mx.FUSE_DGELU])
+def test_grouped_fused(fusion):
+    rows, K = [256, 0, 48, 400], 520
+    M = sum(rows)
+    x, grad = W.make("c3_gelu_dbias_8192", M, K)
+    g = mx.mx_quantize_grouped(to_dev(x), rows, grad=to_dev(grad), fusion=fusion)
+    torch.cuda.synchronize()
+    o = O.mx_quantize_grouped(x, rows, grad=grad, fusion=fusion)
+    mx_outputs_equal(g, o, f"grouped fusion {fusion}")
+    if fusion & mx.FUSE_DBIAS:
+        r0 = 0
+        for gi, m in enumerate(rows):
+            if m == 0:
+                assert torch.all(g["dbias"][gi] == 0)
+                continue
+            y = O.mx_quantize(np.ascontiguousarray(x[r0:r0 + m]),
+                              grad=np.ascontiguousarray(grad[r0:r0 + m]), fusion=fusion,
+                              want_y=True)["y"]
+            ycols = np.abs(W.bf16_to_f32(y).astype(np.float64)).sum(axis=0)
+            assert_dbias_close(g["dbias"][gi], o["dbias"][gi], ycols, f"dbias group {gi}")
+            r0 += m
+
+
+def test_grouped_moe_eight_experts():
+    rows = [1024, 512, 0, 2048, 16, 1520, 768, 256]
+    K = 2048
+    x = W.normal(sum(rows), K, seed=67, sigma=2.0)
+    g = mx.mx_quantize_grouped(to_dev(x), rows, axis=3)
+    torch.cuda.synchronize()
+    mx_outputs_equal(g, O.mx_quantize_grouped(x, rows, axis=3), "moe experts")
+
+
+def test_grouped_equals_per_group_calls_on_gpu():
+    rows, K = [128, 0, 96, 32], 264
+    x = W.loguniform_rows(sum(rows), K, seed=68)
+    xd = to_dev(x)
+    g = mx.mx_quantize_grouped(xd, rows, axis=3)
+    r0, qc, sc = 0, [], []
+    for m in rows:
+        if m:
+            p = mx.mx_quantize(xd[r0:r0 + m].contiguous(), axis=3)
+            qc.append(p["q_col"].reshape(-1))
+            sc.append(p["s_col"].reshape(-1))
+        r0 += m
+    torch.cuda.synchronize()
+    assert torch.equal(g["q_col"], torch.cat(qc)) and torch.equal(g["s_col"], torch.cat(sc))

@@ -97,6 +97,10 @@ def lib():
         L.orc_nvfp4_quantize_transpose_2d.argtypes = [_u16p, _i64, _i64, ctypes.c_uint,
                                                       ctypes.c_float, _u8p, _u8p, _u8p, _u8p,
                                                       _f32p]
+        L.orc_nvfp4_quantize_transpose_grouped.restype = ctypes.c_int
+        L.orc_nvfp4_quantize_transpose_grouped.argtypes = [
+            _u16p, _i64, ctypes.POINTER(ctypes.c_int64), ctypes.c_int, _f32p, ctypes.c_int,
+            ctypes.c_uint, _u8p, _u8p, _u8p, _u8p, _f32p]
         L.orc_absmax.restype = ctypes.c_float
         L.orc_absmax.argtypes = [_u16p, _i64]
         L.orc_nvfp4_global_scale.restype = ctypes.c_float
@@ -398,3 +402,26 @@ def nvfp4_quantize_transpose(x, axis=ROWWISE | COLWISE, tensor_amax=None, two_d=
     if rc != 0:
         raise ValueError(f"oracle nvfp4_quantize_transpose failed with code {rc}")
     return dict(q_row=q_row, s_row=s_row, q_col=q_col, s_col=s_col, sg=float(sg[0]))
+
+
+def nvfp4_quantize_transpose_grouped(x, group_rows, axis=ROWWISE | COLWISE, amax=None, two_d=False):
+    """Grouped NVFP4: x[M][K] stacks len(group_rows) tensors along rows, each
+    with its own tensor amax (amax[g], or its own max |x|) and global scale."""
+    x = _c(x, np.uint16)
+    M, K = x.shape
+    rows = np.ascontiguousarray(group_rows, dtype=np.int64)
+    G = rows.size
+    assert rows.sum() == M
+    q_row = np.zeros((M, K // 2), np.uint8) if axis & ROWWISE else None
+    s_row = np.zeros((M, K // 16), np.uint8) if axis & ROWWISE else None
+    q_col = np.zeros(K * M // 2, np.uint8) if axis & COLWISE else None
+    s_col = np.zeros(K * M // 16, np.uint8) if axis & COLWISE else None
+    sg = np.zeros(G, np.float32)
+    a = None if amax is None else _c(np.asarray(amax, dtype=np.float32), np.float32)
+    rc = lib().orc_nvfp4_quantize_transpose_grouped(
+        _p(x, _u16p), K, rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), G, _p(a, _f32p),
+        int(two_d), axis, _p(q_row, _u8p), _p(s_row, _u8p), _p(q_col, _u8p), _p(s_col, _u8p),
+        _p(sg, _f32p))
+    if rc != 0:
+        raise ValueError(f"oracle nvfp4_quantize_transpose_grouped failed with code {rc}")
+    return dict(q_row=q_row, s_row=s_row, q_col=q_col, s_col=s_col, sg=sg)

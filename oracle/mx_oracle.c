@@ -927,6 +927,41 @@ int orc_nvfp4_quantize_transpose_2d(const uint16_t *x, int64_t M, int64_t K, uns
     return ORC_OK;
 }
 
+/* Grouped NVFP4 (R10): G tensors stacked along rows, each quantised with its
+ * own tensor amax and global scale (amax[g] when amax is given, else the
+ * group's own max |x|), 1D or 2D scaling; outputs concatenated group after
+ * group: q_row[M][K/2] and s_row[M][K/16] as for the stacked rows, q_col /
+ * s_col group g's [K][rows/2] / [K][rows/16] at bytes K*r_g/2 / K*r_g/16,
+ * sg_out[g] (1 for an empty group, which owns no output). */
+int orc_nvfp4_quantize_transpose_grouped(const uint16_t *x, int64_t K, const int64_t *rows, int G,
+                                         const float *amax, int two_d, unsigned axis,
+                                         uint8_t *q_row, uint8_t *s_row, uint8_t *q_col,
+                                         uint8_t *s_col, float *sg_out)
+{
+    if (G <= 0 || K <= 0 || K % 16)
+        return ORC_ERR_SHAPE;
+    int64_t r = 0;
+    for (int g = 0; g < G; g++) {
+        const int64_t m = rows[g];
+        if (m < 0 || m % 16)
+            return ORC_ERR_SHAPE;
+        if (m == 0) {
+            if (sg_out)
+                sg_out[g] = 1.0f;
+            continue;
+        }
+        const float A = amax ? amax[g] : -1.0f;
+        int rc = (two_d ? orc_nvfp4_quantize_transpose_2d : orc_nvfp4_quantize_transpose)(
+            x + r * K, m, K, axis, A, q_row ? q_row + r * K / 2 : NULL,
+            s_row ? s_row + r * K / 16 : NULL, q_col ? q_col + K * r / 2 : NULL,
+            s_col ? s_col + K * r / 16 : NULL, sg_out ? sg_out + g : NULL);
+        if (rc != ORC_OK)
+            return rc;
+        r += m;
+    }
+    return ORC_OK;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Array helpers for the self-tests (elementwise, no method arithmetic).     */
 /* ------------------------------------------------------------------------ */

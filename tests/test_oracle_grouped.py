@@ -98,3 +98,53 @@ def test_tiled_scales_per_group():
             assert np.array_equal(sr, O.scale_tiles(c["s_row"]))
             assert np.array_equal(sc, O.scale_tiles(c["s_col"]))
         r0 += m
+
+
+# --- grouped NVFP4 -------------------------------------------------------------
+
+def test_nvfp4_one_group_is_the_plain_cast():
+    x = W.student_t_rows(96, 160, seed=71)
+    for two_d in (False, True):
+        g = O.nvfp4_quantize_transpose_grouped(x, [96], two_d=two_d)
+        p = O.nvfp4_quantize_transpose(x, two_d=two_d)
+        assert np.array_equal(g["q_row"], p["q_row"]) and np.array_equal(g["s_row"], p["s_row"])
+        assert np.array_equal(g["q_col"], p["q_col"].ravel()) and np.array_equal(g["s_col"], p["s_col"].ravel())
+        assert g["sg"][0] == p["sg"]
+
+
+@pytest.mark.parametrize("two_d", [False, True])
+def test_nvfp4_equal_amax_groups_are_slices_of_the_stacked_cast(two_d):
+    rows = [48, 0, 16, 96]
+    M, K = sum(rows), 80
+    x = W.student_t_rows(M, K, seed=72)
+    # give every group the same largest magnitude, so every S_g is the stack's
+    big = np.uint16(0x4500)          # 2048, larger than any drawn value
+    r0 = 0
+    for m in rows:
+        if m:
+            x[r0, 0] = big
+        r0 += m
+    g = O.nvfp4_quantize_transpose_grouped(x, rows, two_d=two_d)
+    p = O.nvfp4_quantize_transpose(x, two_d=two_d)
+    assert np.all(g["sg"][[0, 2, 3]] == p["sg"]) and g["sg"][1] == 1.0
+    assert np.array_equal(g["q_row"], p["q_row"]) and np.array_equal(g["s_row"], p["s_row"])
+    qc = split(g["q_col"], [K * m // 2 for m in rows])
+    sc = split(g["s_col"], [K * m // 16 for m in rows])
+    r0 = 0
+    for m, q, s in zip(rows, qc, sc):
+        assert np.array_equal(q.reshape(K, m // 2), p["q_col"][:, r0 // 2:(r0 + m) // 2])
+        assert np.array_equal(s.reshape(K, m // 16), p["s_col"][:, r0 // 16:(r0 + m) // 16])
+        r0 += m
+
+
+def test_nvfp4_group_global_scales_follow_group_amax():
+    rows = [32, 64]
+    x = W.student_t_rows(96, 48, seed=73)
+    g = O.nvfp4_quantize_transpose_grouped(x, rows)
+    xf = np.abs(W.bf16_to_f32(x))
+    for gi, (a, b) in enumerate([(0, 32), (32, 96)]):
+        A = np.float32(xf[a:b].max())
+        assert g["sg"][gi] == np.float32(A / np.float32(2688.0))
+    # a given amax array overrides the groups' own
+    g2 = O.nvfp4_quantize_transpose_grouped(x, rows, amax=[1.0, 2.0])
+    assert list(g2["sg"]) == [np.float32(1.0 / 2688.0), np.float32(2.0 / 2688.0)]

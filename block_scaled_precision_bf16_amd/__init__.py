@@ -38,6 +38,7 @@ EXPORTS = ("mx_quantize", "mx_quantize_workspace_size", "mx_scale_size", "mx_qua
            "mx_quantize_grouped_workspace_size", "mx_grouped_scale_size", "mx_quantize_gated",
            "mx_quantize_dgated", "mx_fused_values",
            "mx_absmax_bf16", "nvfp4_quantize_transpose", "nvfp4_quantize_transpose_2d",
+           "mx_absmax_bf16_grouped", "nvfp4_quantize_transpose_grouped",
            "mx_status_str", "mx_abi_version")
 
 
@@ -91,6 +92,12 @@ def lib():
                                                _vp, _vp, _vp, _vp, _vp, _vp]
         L.nvfp4_quantize_transpose_2d.restype = ctypes.c_int
         L.nvfp4_quantize_transpose_2d.argtypes = L.nvfp4_quantize_transpose.argtypes
+        L.mx_absmax_bf16_grouped.restype = ctypes.c_int
+        L.mx_absmax_bf16_grouped.argtypes = [_vp, _i64, _vp, ctypes.c_int, _vp, _vp]
+        L.nvfp4_quantize_transpose_grouped.restype = ctypes.c_int
+        L.nvfp4_quantize_transpose_grouped.argtypes = [_vp, _i64, _vp, ctypes.c_int, _vp,
+                                                       ctypes.c_int, ctypes.c_uint, _vp, _vp,
+                                                       _vp, _vp, _vp, _vp]
         L.mx_status_str.restype = ctypes.c_char_p
         L.mx_status_str.argtypes = [ctypes.c_int]
         L.mx_abi_version.restype = ctypes.c_int
@@ -327,4 +334,45 @@ def nvfp4_quantize_transpose(x, amax=None, axis=ROWWISE | COLWISE, out=None, str
     st = fn(_ptr(x), M, K, _ptr(amax), axis, _ptr(o.get("q_row")), _ptr(o.get("s_row")),
             _ptr(o.get("q_col")), _ptr(o.get("s_col")), _ptr(o["sg"]), _stream(dev, stream))
     _check(st, "nvfp4_quantize_transpose_2d" if two_d else "nvfp4_quantize_transpose")
+    return {k: o.get(k) for k in ("q_row", "s_row", "q_col", "s_col", "sg")}
+
+
+def mx_absmax_bf16_grouped(x, group_rows, out=None, stream=None):
+    """Per-group max |x| (fp32 [G]) of x[M][K] = len(group_rows) stacked tensors."""
+    x = _bf16_bits(x)
+    M, K = x.shape
+    G = len(group_rows)
+    amax = out if out is not None else torch.empty(G, dtype=torch.float32, device=x.device)
+    rows = _rows_arg(group_rows)
+    st = lib().mx_absmax_bf16_grouped(_ptr(x), K, ctypes.cast(rows, _vp), G, _ptr(amax),
+                                      _stream(x.device, stream))
+    _check(st, "mx_absmax_bf16_grouped")
+    return amax
+
+
+def nvfp4_quantize_transpose_grouped(x, group_rows, amax, axis=ROWWISE | COLWISE, two_d=False,
+                                     out=None, stream=None):
+    """Grouped NVFP4 of x[M][K] = len(group_rows) stacked tensors, each with its
+    own tensor amax (device fp32 [G]).  Returns q_row [M][K/2], s_row
+    [M][K/16], flat q_col / s_col (the groups' transposes one after the
+    other) and the groups' global scales sg [G]."""
+    x = _bf16_bits(x)
+    M, K = x.shape
+    G = len(group_rows)
+    dev = x.device
+    o = dict(out or {})
+    if axis & ROWWISE:
+        o.setdefault("q_row", _u8((M, K // 2), dev))
+        o.setdefault("s_row", _u8((M, K // 16), dev))
+    if axis & COLWISE:
+        o.setdefault("q_col", _u8((M * K // 2,), dev))
+        o.setdefault("s_col", _u8((M * K // 16,), dev))
+    o.setdefault("sg", torch.empty(G, dtype=torch.float32, device=dev))
+    rows = _rows_arg(group_rows)
+    st = lib().nvfp4_quantize_transpose_grouped(_ptr(x), K, ctypes.cast(rows, _vp), G, _ptr(amax),
+                                                int(two_d), axis, _ptr(o.get("q_row")),
+                                                _ptr(o.get("s_row")), _ptr(o.get("q_col")),
+                                                _ptr(o.get("s_col")), _ptr(o["sg"]),
+                                                _stream(dev, stream))
+    _check(st, "nvfp4_quantize_transpose_grouped")
     return {k: o.get(k) for k in ("q_row", "s_row", "q_col", "s_col", "sg")}

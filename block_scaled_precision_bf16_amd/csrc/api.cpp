@@ -155,6 +155,39 @@ bool build_groups(const int64_t *rows, int G, int64_t K, int op, bool dbias, boo
     return walks > 0;
 }
 
+// Group table of a grouped NVFP4 cast: group sizes multiples of 16 rows
+// (empty groups allowed), K a multiple of 16; walks per group with the walk
+// length of the whole stack.
+bool build_nv_groups(const int64_t *rows, int G, int64_t K, mxk::GroupTable &gt, int64_t &M,
+                     int &group)
+{
+    if (!rows || G < 1 || G > mxk::kMaxGroups)
+        return false;
+    M = 0;
+    for (int g = 0; g < G; g++) {
+        if (rows[g] < 0 || rows[g] % 16 != 0 || rows[g] > kMaxDim)
+            return false;
+        M += rows[g];
+    }
+    if (M <= 0 || !shape_ok(M, K, 16))
+        return false;
+    group = mxk::pick_group(tiles(M, mxk::kTileM), tiles(K, mxk::kTileK), mxk::kTargetWorkgroups);
+    gt = mxk::GroupTable{};
+    gt.count = G;
+    int64_t walks = 0, r = 0;
+    for (int g = 0; g < G; g++) {
+        gt.walk0[g] = (int)walks;
+        gt.row0[g] = r;
+        gt.srow_off[g] = r * (K / 16);
+        gt.scol_off[g] = K * (r / 16);
+        walks += (tiles(rows[g], mxk::kTileM) + group - 1) / group;
+        r += rows[g];
+    }
+    gt.walk0[G] = (int)walks;
+    gt.row0[G] = M;
+    return true;
+}
+
 // Total scale bytes of a grouped cast (the groups' scale tensors one after
 // the other).
 uint64_t grouped_scale_bytes(const int64_t *rows, int G, int64_t K, bool colwise, bool tiled)
@@ -549,6 +582,72 @@ mx_status nvfp4_quantize_transpose(const void *x, int64_t M, int64_t K, const fl
 {
     return nvfp4_impl(false, x, M, K, amax, axis_mask, q_row, s_row, q_col, s_col,
                       global_scale_out, stream);
+}
+
+mx_status mx_absmax_bf16_grouped(const void *x, int64_t K, const int64_t *group_rows, int G,
+                                 float *amax, hipStream_t stream)
+{
+    if (!x || !amax || !group_rows)
+        return MX_ERR_NULL;
+    mxk::GroupTable gt;
+    int64_t M;
+    int group;
+    if (!build_nv_groups(group_rows, G, K, gt, M, group))
+        return MX_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(amax, 4))
+        return MX_ERR_ALIGN;
+    const Span in[1] = {{x, 2 * (uint64_t)(M * K)}};
+    const Span out[1] = {{amax, 4 * (uint64_t)G}};
+    if (any_alias(in, 1, out, 1))
+        return MX_ERR_ALIAS;
+    return from_hip(mxk::launch_absmax_grouped(static_cast<const uint16_t *>(x), K, gt, amax,
+                                               stream));
+}
+
+mx_status nvfp4_quantize_transpose_grouped(const void *x, int64_t K, const int64_t *group_rows,
+                                           int G, const float *amax, int scaling_2d,
+                                           unsigned axis_mask, uint8_t *q_row, uint8_t *s_row,
+                                           uint8_t *q_col, uint8_t *s_col,
+                                           float *global_scale_out, hipStream_t stream)
+{
+    if (axis_mask == 0 || (axis_mask & ~3u) || (scaling_2d != 0 && scaling_2d != 1))
+        return MX_ERR_ENUM;
+    const bool row = axis_mask & MX_ROWWISE, col = axis_mask & MX_COLWISE;
+    if (!x || !amax || !group_rows || (row && (!q_row || !s_row)) || (col && (!q_col || !s_col)))
+        return MX_ERR_NULL;
+    mxk::GroupTable gt;
+    int64_t M;
+    int group;
+    if (!build_nv_groups(group_rows, G, K, gt, M, group))
+        return MX_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(amax, 4) ||
+        (row && (!aligned(q_row, 16) || !aligned(s_row, 16))) ||
+        (col && (!aligned(q_col, 16) || !aligned(s_col, 16))) ||
+        (global_scale_out && !aligned(global_scale_out, 4)))
+        return MX_ERR_ALIGN;
+    const uint64_t n = (uint64_t)(M * K);
+    const Span in[2] = {{x, 2 * n}, {amax, 4 * (uint64_t)G}};
+    const Span out[5] = {{row ? q_row : nullptr, n / 2}, {row ? s_row : nullptr, n / 16},
+                         {col ? q_col : nullptr, n / 2}, {col ? s_col : nullptr, n / 16},
+                         {global_scale_out, 4 * (uint64_t)G}};
+    if (any_alias(in, 2, out, 5))
+        return MX_ERR_ALIAS;
+
+    mxk::Nv4Args a;
+    a.x = static_cast<const uint16_t *>(x);
+    a.M = M;
+    a.K = K;
+    a.amax = amax;
+    a.q_row = q_row;
+    a.s_row = s_row;
+    a.q_col = q_col;
+    a.s_col = s_col;
+    a.sg_out = global_scale_out;
+    a.tiles_k = tiles(K, mxk::kTileK);
+    a.tiles_m = tiles(M, mxk::kTileM);
+    a.group = group;
+    a.groups_m = gt.walk0[G];
+    return from_hip(mxk::launch_nvfp4_grouped(axis_mask, scaling_2d != 0, a, gt, stream));
 }
 
 mx_status nvfp4_quantize_transpose_2d(const void *x, int64_t M, int64_t K, const float *amax,

@@ -109,5 +109,9 @@ hipError_t launch_fused_values(int op, const uint16_t *x, const uint16_t *aux, i
 hipError_t launch_absmax(const uint16_t *x, int64_t n, float *amax, hipStream_t s);
 // two_d: one scale per 16 x 16 block instead of per 16 elements of a row.
 hipError_t launch_nvfp4(unsigned axis, bool two_d, const Nv4Args &a, hipStream_t s);
+hipError_t launch_nvfp4_grouped(unsigned axis, bool two_d, const Nv4Args &a, const GroupTable &gt,
+                                hipStream_t s);
+hipError_t launch_absmax_grouped(const uint16_t *x, int64_t K, const GroupTable &gt, float *amax,
+                                 hipStream_t s);
 
 }  // namespace mxk

@@ -414,21 +414,18 @@ __device__ __forceinline__ void nv_step(const Nv4Args &a, const NvLane &l,
 // with the next sub-tile's loads in flight while one is converted (as in the
 // MXFP8 cast); the transposed output leaves every second sub-tile as whole
 // 128-byte lines.
+// The global scale of a tensor with amax A: A / (448 * 6), 1 for A = 0.
+__device__ __forceinline__ float nv_global_scale(float A) { return A == 0.0f ? 1.0f : A / 2688.0f; }
+
 template <bool ROW, bool COL, bool HALF, bool TWO_D>
-__global__ __launch_bounds__(kThreads, 2) void nvfp4_kernel(Nv4Args a)
+__device__ __forceinline__ void nv_walk(const Nv4Args &a, int rg, int tk)
 {
     using P = NvPolicy<ROW, COL>;
-    const int job = xcd_tile((int)blockIdx.x, (int)gridDim.x);
-    const int rg = job / a.tiles_k;
-    const int tk = job - rg * a.tiles_k;
     const int tm0 = rg * a.group;
     const int n = (a.tiles_m - tm0) < a.group ? (a.tiles_m - tm0) : a.group;
     const NvLane l = nv_lane();
 
-    const float A = *a.amax;
-    const float sg = A == 0.0f ? 1.0f : A / 2688.0f;
-    if (a.sg_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
-        *a.sg_out = sg;
+    const float sg = nv_global_scale(*a.amax);
 
     __shared__ NvStage st;
     if (threadIdx.x < 128)
@@ -452,24 +449,66 @@ __global__ __launch_bounds__(kThreads, 2) void nvfp4_kernel(Nv4Args a)
         nv_flush_s<P::s_col>(a, st, tm0, tk, n);
 }
 
+template <bool ROW, bool COL, bool HALF, bool TWO_D>
+__global__ __launch_bounds__(kThreads, 2) void nvfp4_kernel(Nv4Args a)
+{
+    const int job = xcd_tile((int)blockIdx.x, (int)gridDim.x);
+    const int rg = job / a.tiles_k;
+    if (a.sg_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
+        *a.sg_out = nv_global_scale(*a.amax);
+    nv_walk<ROW, COL, HALF, TWO_D>(a, rg, job - rg * a.tiles_k);
+}
+
+// Grouped: walk rg (numbered across all groups) belongs to the group g with
+// walk0[g] <= rg < walk0[g + 1], quantised as a tensor of its own with its
+// own amax (amax[g]) and global scale.  Workgroup 0 writes every group's
+// global scale (1 for an empty group).
+template <bool ROW, bool COL, bool HALF, bool TWO_D>
+__global__ __launch_bounds__(kThreads, 2) void nvfp4_grouped_kernel(Nv4Args a, GroupTable gt)
+{
+    const int job = xcd_tile((int)blockIdx.x, (int)gridDim.x);
+    const int rg = job / a.tiles_k;
+    const int tk = job - rg * a.tiles_k;
+    if (a.sg_out != nullptr && blockIdx.x == 0 && (int)threadIdx.x < gt.count) {
+        const int t = (int)threadIdx.x;
+        a.sg_out[t] = gt.row0[t + 1] == gt.row0[t] ? 1.0f : nv_global_scale(a.amax[t]);
+    }
+    int g = 0;
+    while (g + 1 < gt.count && gt.walk0[g + 1] <= rg)
+        g++;
+    const int64_t r0 = gt.row0[g];
+    Nv4Args b = a;
+    b.M = gt.row0[g + 1] - r0;
+    b.x = a.x + r0 * a.K;
+    b.amax = a.amax + g;
+    b.q_row = a.q_row ? a.q_row + r0 * (a.K >> 1) : nullptr;
+    b.s_row = a.s_row ? a.s_row + r0 * (a.K >> 4) : nullptr;
+    b.q_col = a.q_col ? a.q_col + a.K * (r0 >> 1) : nullptr;
+    b.s_col = a.s_col ? a.s_col + a.K * (r0 >> 4) : nullptr;
+    b.tiles_m = (int)((b.M + kTileM - 1) / kTileM);
+    b.groups_m = gt.walk0[g + 1] - gt.walk0[g];
+    nv_walk<ROW, COL, HALF, TWO_D>(b, rg - gt.walk0[g], tk);
+}
+
 // ---------------------------------------------------------------------------
 // Tensor absmax: largest |bf16| as the fp32 bit pattern (ordered like an
 // unsigned integer for non-negative values), combined with atomic max.
 // ---------------------------------------------------------------------------
 __global__ void absmax_clear_kernel(uint32_t *amax_bits) { *amax_bits = 0u; }
 
-__global__ __launch_bounds__(256) void absmax_kernel(const uint16_t *x, int64_t n,
-                                                     uint32_t *amax_bits)
+// Largest 15-bit magnitude this thread sees of x[0, n), thread `first` of
+// `stride` threads, reduced over the wave into lane 0's bits 16-30.
+__device__ __forceinline__ uint32_t absmax_wave(const uint16_t *x, int64_t n, int64_t first,
+                                                int64_t stride, bool tail)
 {
     const u32x4_t *xv = reinterpret_cast<const u32x4_t *>(x);
     const int64_t nvec = n >> 3;
-    const int64_t stride = (int64_t)gridDim.x * 256;
     auto fold = [](uint32_t m, u32x4_t v) {
         return pk_max_u16(m, pk_max_u16(pk_max_u16(v[0] & 0x7FFF7FFFu, v[1] & 0x7FFF7FFFu),
                                         pk_max_u16(v[2] & 0x7FFF7FFFu, v[3] & 0x7FFF7FFFu)));
     };
     uint32_t m = 0;
-    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    int64_t i = first;
     // four independent 16-byte loads in flight per thread; the input is read
     // once, so the loads are non-temporal
     for (; i + 3 * stride < nvec; i += 4 * stride) {
@@ -483,7 +522,7 @@ __global__ __launch_bounds__(256) void absmax_kernel(const uint16_t *x, int64_t 
     }
     for (; i < nvec; i += stride)
         m = fold(m, __builtin_nontemporal_load(xv + i));
-    if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
+    if (tail && threadIdx.x < (n & 7)) {
         const uint32_t t = x[(nvec << 3) + threadIdx.x] & 0x7FFFu;
         m = pk_max_u16(m, t);
     }
@@ -494,8 +533,37 @@ __global__ __launch_bounds__(256) void absmax_kernel(const uint16_t *x, int64_t 
         const uint32_t o = (uint32_t)__shfl_xor((int)mag, off, 64);
         mag = mag > o ? mag : o;
     }
+    return mag << 16;
+}
+
+__global__ __launch_bounds__(256) void absmax_kernel(const uint16_t *x, int64_t n,
+                                                     uint32_t *amax_bits)
+{
+    const uint32_t bits = absmax_wave(x, n, (int64_t)blockIdx.x * 256 + threadIdx.x,
+                                      (int64_t)gridDim.x * 256, blockIdx.x == 0);
     if ((threadIdx.x & 63) == 0)
-        atomicMax(amax_bits, mag << 16);
+        atomicMax(amax_bits, bits);
+}
+
+// Per-group absmax: blockIdx.y is the group, whose rows are x[row0[g] ..
+// row0[g + 1]) of width K (a multiple of 16, so every group starts and ends
+// on whole 16-byte vectors).
+__global__ void absmax_clear_grouped_kernel(uint32_t *amax_bits, int G)
+{
+    if ((int)threadIdx.x < G)
+        amax_bits[threadIdx.x] = 0u;
+}
+
+__global__ __launch_bounds__(256) void absmax_grouped_kernel(const uint16_t *x, int64_t K,
+                                                             GroupTable gt, uint32_t *amax_bits)
+{
+    const int g = (int)blockIdx.y;
+    const int64_t r0 = gt.row0[g];
+    const uint32_t bits = absmax_wave(x + r0 * K, (gt.row0[g + 1] - r0) * K,
+                                      (int64_t)blockIdx.x * 256 + threadIdx.x,
+                                      (int64_t)gridDim.x * 256, false);
+    if ((threadIdx.x & 63) == 0)
+        atomicMax(amax_bits + g, bits);
 }
 
 hipError_t launch_absmax(const uint16_t *x, int64_t n, float *amax, hipStream_t s)
@@ -514,31 +582,73 @@ hipError_t launch_absmax(const uint16_t *x, int64_t n, float *amax, hipStream_t 
     return hipGetLastError();
 }
 
+hipError_t launch_absmax_grouped(const uint16_t *x, int64_t K, const GroupTable &gt, float *amax,
+                                 hipStream_t s)
+{
+    uint32_t *bits = reinterpret_cast<uint32_t *>(amax);
+    hipLaunchKernelGGL(absmax_clear_grouped_kernel, dim3(1), dim3(kMaxGroups), 0, s, bits,
+                       gt.count);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    int64_t most = 0;
+    for (int g = 0; g < gt.count; g++)
+        most = gt.row0[g + 1] - gt.row0[g] > most ? gt.row0[g + 1] - gt.row0[g] : most;
+    int64_t blocks = ((most * K >> 3) + 255) / 256;
+    const int64_t cap = 2048 / gt.count > 16 ? 2048 / gt.count : 16;
+    blocks = blocks > cap ? cap : (blocks < 1 ? 1 : blocks);
+    hipLaunchKernelGGL(absmax_grouped_kernel, dim3((unsigned)blocks, (unsigned)gt.count),
+                       dim3(256), 0, s, x, K, gt, bits);
+    return hipGetLastError();
+}
+
+// HALF: some tensor (or group) has a row count that is not a multiple of 32.
 template <bool ROW, bool COL, bool TWO_D>
-static hipError_t launch_nv(const Nv4Args &a, hipStream_t s)
+static hipError_t launch_nv(const Nv4Args &a, const GroupTable *gt, bool half, hipStream_t s)
 {
     const dim3 grid((unsigned)(a.groups_m * a.tiles_k));
-    if (COL && (a.M & 31) != 0)
+    if (gt) {
+        if (COL && half)
+            hipLaunchKernelGGL((nvfp4_grouped_kernel<ROW, COL, true, TWO_D>), grid, dim3(kThreads),
+                               0, s, a, *gt);
+        else
+            hipLaunchKernelGGL((nvfp4_grouped_kernel<ROW, COL, false, TWO_D>), grid,
+                               dim3(kThreads), 0, s, a, *gt);
+    } else if (COL && half) {
         hipLaunchKernelGGL((nvfp4_kernel<ROW, COL, true, TWO_D>), grid, dim3(kThreads), 0, s, a);
-    else
+    } else {
         hipLaunchKernelGGL((nvfp4_kernel<ROW, COL, false, TWO_D>), grid, dim3(kThreads), 0, s, a);
+    }
     return hipGetLastError();
 }
 
 template <bool TWO_D>
-static hipError_t launch_nv_axis(unsigned axis, const Nv4Args &a, hipStream_t s)
+static hipError_t launch_nv_axis(unsigned axis, const Nv4Args &a, const GroupTable *gt, bool half,
+                                 hipStream_t s)
 {
     switch (axis) {
-    case 1u: return launch_nv<true, false, TWO_D>(a, s);
-    case 2u: return launch_nv<false, true, TWO_D>(a, s);
-    case 3u: return launch_nv<true, true, TWO_D>(a, s);
+    case 1u: return launch_nv<true, false, TWO_D>(a, gt, half, s);
+    case 2u: return launch_nv<false, true, TWO_D>(a, gt, half, s);
+    case 3u: return launch_nv<true, true, TWO_D>(a, gt, half, s);
     default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_nvfp4(unsigned axis, bool two_d, const Nv4Args &a, hipStream_t s)
 {
-    return two_d ? launch_nv_axis<true>(axis, a, s) : launch_nv_axis<false>(axis, a, s);
+    const bool half = (a.M & 31) != 0;
+    return two_d ? launch_nv_axis<true>(axis, a, nullptr, half, s)
+                 : launch_nv_axis<false>(axis, a, nullptr, half, s);
+}
+
+hipError_t launch_nvfp4_grouped(unsigned axis, bool two_d, const Nv4Args &a, const GroupTable &gt,
+                                hipStream_t s)
+{
+    bool half = false;
+    for (int g = 0; g < gt.count; g++)
+        half = half || ((gt.row0[g + 1] - gt.row0[g]) & 31) != 0;
+    return two_d ? launch_nv_axis<true>(axis, a, &gt, half, s)
+                 : launch_nv_axis<false>(axis, a, &gt, half, s);
 }
 
 }  // namespace mxk

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MXCAST_ABI_VERSION 6
+#define MXCAST_ABI_VERSION 7
 
 typedef enum mx_status {
     MX_OK = 0,
@@ -304,6 +304,41 @@ mx_status nvfp4_quantize_transpose_2d(const void *x, int64_t M, int64_t K, const
                                       uint8_t *s_col, float *global_scale_out, hipStream_t stream);
 
 /* Static string naming a status code. */
+/*
+ * Per-group tensor absmax for the grouped NVFP4 cast: amax[g] = max |x| over
+ * the rows of group g (0 for an empty group), as fp32.  x, group_rows, G as
+ * for nvfp4_quantize_transpose_grouped; amax is a device array of G floats.
+ */
+mx_status mx_absmax_bf16_grouped(const void *x, int64_t K, const int64_t *group_rows, int G,
+                                 float *amax, hipStream_t stream);
+
+/*
+ * Grouped NVFP4 quantize-transpose: G tensors stacked along rows (the
+ * operation of the group_quantize_transpose_nvfp4 row of TransformerEngine PR
+ * 3291's "Important Files Changed" table, without the Hadamard transform),
+ * each quantised in one launch exactly as nvfp4_quantize_transpose (or, with
+ * scaling_2d = 1, nvfp4_quantize_transpose_2d) quantises a tensor of its own:
+ * with its own tensor amax and global scale.
+ *   x            device, bf16 [M][K], M = sum of group_rows; group g owns rows
+ *                r_g .. r_g + group_rows[g] - 1
+ *   group_rows   HOST array of G row counts, each >= 0 and a multiple of 16;
+ *                1 <= G <= 64, M > 0; K a positive multiple of 16
+ *   amax         device, fp32 [G]: each group's tensor amax (for example from
+ *                mx_absmax_bf16_grouped)
+ *   q_row, s_row [M][K/2], [M][K/16]: the groups' rows (the stacked layout)
+ *   q_col, s_col group g's [K][rows/2] and [K][rows/16] at bytes K * r_g / 2
+ *                and K * r_g / 16 (the groups one after the other)
+ *   global_scale_out  device fp32 [G] or NULL: each group's global scale
+ *                (1 for an empty group)
+ * Errors as for nvfp4_quantize_transpose; MX_ERR_ENUM also for scaling_2d not
+ * 0 or 1, MX_ERR_SHAPE for G out of range or a bad group size.
+ */
+mx_status nvfp4_quantize_transpose_grouped(const void *x, int64_t K, const int64_t *group_rows,
+                                           int G, const float *amax, int scaling_2d,
+                                           unsigned axis_mask, uint8_t *q_row, uint8_t *s_row,
+                                           uint8_t *q_col, uint8_t *s_col,
+                                           float *global_scale_out, hipStream_t stream);
+
 const char *mx_status_str(int status);
 
 /* MXCAST_ABI_VERSION of the built library. */

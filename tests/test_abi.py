@@ -41,7 +41,7 @@ def header_abi_version():
 
 
 def test_version_and_status_strings():
-    assert mx.mx_abi_version() == header_abi_version() == 6
+    assert mx.mx_abi_version() == header_abi_version() == 7
     for code in range(9):
         assert mx.mx_status_str(code).startswith("MX_")
     assert "unknown" in mx.mx_status_str(99)
@@ -310,6 +310,36 @@ def test_grouped_rejects():
     assert gq(fusion=mx.FUSE_DBIAS, ws_bytes=16) == mx.MX_ERR_WORKSPACE
     assert gq(q_col=b.p("x", 16)) == mx.MX_ERR_ALIAS
     assert gq(fusion=mx.FUSE_DBIAS, dbias=b.p("ws", 0)) == mx.MX_ERR_ALIAS
+    assert b.untouched()
+
+
+def test_grouped_nvfp4_rejects():
+    b = Bufs(64, 96)
+    L = mx.lib()
+
+    def nq(rows=(32, 0, 32), G=None, **kw):
+        arr = (ctypes.c_int64 * max(1, len(rows)))(*rows)
+        return L.nvfp4_quantize_transpose_grouped(
+            kw.get("x", b.p("x")), kw.get("K", 96), kw.get("rows_p", ctypes.cast(arr, ctypes.c_void_p)),
+            len(rows) if G is None else G, kw.get("amax", b.p("amax")), kw.get("two_d", 0),
+            kw.get("axis", 3), kw.get("q_row", b.p("q_row")), kw.get("s_row", b.p("s_row")),
+            kw.get("q_col", b.p("q_col")), kw.get("s_col", b.p("s_col")), kw.get("sg", NULL), None)
+
+    def am(rows=(32, 0, 32), **kw):
+        arr = (ctypes.c_int64 * len(rows))(*rows)
+        return L.mx_absmax_bf16_grouped(kw.get("x", b.p("x")), kw.get("K", 96),
+                                        ctypes.cast(arr, ctypes.c_void_p), len(rows),
+                                        kw.get("amax", b.p("amax")), None)
+    assert nq(axis=0) == mx.MX_ERR_ENUM and nq(axis=3 | mx.ELEM_E5M2) == mx.MX_ERR_ENUM
+    assert nq(two_d=2) == mx.MX_ERR_ENUM
+    assert nq(x=NULL) == mx.MX_ERR_NULL and nq(amax=NULL) == mx.MX_ERR_NULL
+    assert nq(rows_p=NULL) == mx.MX_ERR_NULL
+    assert nq(rows=(32, 8)) == mx.MX_ERR_SHAPE and nq(K=40) == mx.MX_ERR_SHAPE
+    assert nq(rows=(0,)) == mx.MX_ERR_SHAPE and nq(rows=tuple([16] * 65)) == mx.MX_ERR_SHAPE
+    assert nq(s_col=b.p("s_col", 4)) == mx.MX_ERR_ALIGN
+    assert nq(sg=b.p("x", 0)) == mx.MX_ERR_ALIAS
+    assert am(x=NULL) == mx.MX_ERR_NULL and am(rows=(24,)) == mx.MX_ERR_SHAPE
+    assert am(amax=b.p("x", 16)) == mx.MX_ERR_ALIAS
     assert b.untouched()
 
 

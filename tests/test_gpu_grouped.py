@@ -86,3 +86,47 @@ def test_grouped_equals_per_group_calls_on_gpu():
         r0 += m
     torch.cuda.synchronize()
     assert torch.equal(g["q_col"], torch.cat(qc)) and torch.equal(g["s_col"], torch.cat(sc))
+
+
+# --- grouped NVFP4 -------------------------------------------------------------
+
+NV_GROUPS = [([128, 0, 256, 128], 256), ([48, 0, 80, 16], 144), ([16] * 5, 64),
+             ([2048, 16, 0, 1520], 1056)]
+
+
+@pytest.mark.parametrize("two_d", [False, True], ids=["1d", "2d"])
+@pytest.mark.parametrize("axis", [1, 2, 3])
+@pytest.mark.parametrize("rows,K", NV_GROUPS)
+def test_grouped_nvfp4(rows, K, axis, two_d):
+    M = sum(rows)
+    x = W.student_t_rows(M, K, seed=7000 + M + K)
+    xd = to_dev(x)
+    amax = mx.mx_absmax_bf16_grouped(xd, rows)
+    g = mx.nvfp4_quantize_transpose_grouped(xd, rows, amax, axis=axis, two_d=two_d)
+    torch.cuda.synchronize()
+    o = O.nvfp4_quantize_transpose_grouped(x, rows, axis=axis, two_d=two_d)
+    mx_outputs_equal(g, o, f"grouped nvfp4 {rows} K={K} axis {axis} 2d={two_d}")
+    assert np.array_equal(g["sg"].cpu().numpy(), o["sg"])
+
+
+def test_grouped_absmax_matches_numpy():
+    rows, K = [256, 0, 48, 1024, 16], 512
+    x = W.student_t_rows(sum(rows), K, seed=74)
+    a = mx.mx_absmax_bf16_grouped(to_dev(x), rows).cpu().numpy()
+    xf = np.abs(W.bf16_to_f32(x))
+    r0 = 0
+    for gi, m in enumerate(rows):
+        want = xf[r0:r0 + m].max() if m else 0.0
+        assert a[gi] == np.float32(want), gi
+        r0 += m
+
+
+def test_grouped_nvfp4_moe_eight_experts():
+    rows = [1024, 512, 0, 2048, 16, 1520, 768, 256]
+    K = 2048
+    x = W.student_t_rows(sum(rows), K, seed=75)
+    xd = to_dev(x)
+    g = mx.nvfp4_quantize_transpose_grouped(xd, rows, mx.mx_absmax_bf16_grouped(xd, rows))
+    torch.cuda.synchronize()
+    o = O.nvfp4_quantize_transpose_grouped(x, rows)
+    mx_outputs_equal(g, o, "nvfp4 moe experts")

@@ -339,6 +339,7 @@ mx_status mx_quantize(const void *x, const void *grad, int64_t M, int64_t K, uns
     a.s_col = s_col;
     a.partials = want_dbias ? static_cast<float *>(workspace) : nullptr;
     a.tiled = tiled;
+    a.qcol_nt = M * K >= mxk::kQcolNtBytes && M % 128 == 0;
     set_walk(a, op, want_dbias);
     mx_status st = from_hip(mxk::launch_mx_cast(op, axis_mask & 3u, axis_mask & kFmtBits,
                                                 want_dbias, a, stream));
@@ -429,6 +430,7 @@ mx_status mx_quantize_grouped(const void *x, const void *grad, int64_t K, const 
     a.s_col = s_col;
     a.partials = want_dbias ? static_cast<float *>(workspace) : nullptr;
     a.tiled = tiled;
+    a.qcol_nt = 0;   // groups' transposed rows rarely fill whole lines
     a.tiles_k = tiles(K, mxk::kTileK);
     a.tiles_m = tiles(M, mxk::kTileM);
     a.group = group;
@@ -476,6 +478,7 @@ mx_status mx_quantize_gated(const void *x, int64_t M, int64_t N, unsigned axis_m
     a.s_col = s_col;
     a.partials = nullptr;
     a.tiled = tiled;
+    a.qcol_nt = 0;
     const int op = act == MX_GATED_SWIGLU ? mxk::OP_SWIGLU : mxk::OP_GEGLU;
     set_walk(a, op, false);
     return from_hip(
@@ -521,6 +524,7 @@ mx_status mx_quantize_dgated(const void *grad, const void *x, int64_t M, int64_t
     a.s_col = s_col;
     a.partials = nullptr;
     a.tiled = tiled;
+    a.qcol_nt = 0;
     const int op = act == MX_GATED_SWIGLU ? mxk::OP_DSWIGLU : mxk::OP_DGEGLU;
     set_walk(a, op, false);
     return from_hip(

@@ -67,7 +67,14 @@ struct MxArgs {
     int tiles_k, tiles_m;  // 128 x 256 sub-tiles along K and M
     int group, groups_m;   // sub-tiles per workgroup walk, walks along M
     int tiled;             // scales in the GEMM-ready tile layout (walks of >= 2 sub-tiles)
+    int qcol_nt;           // plain cast with both outputs: transposed stores non-temporal
 };
+
+// The plain cast's transposed stores are non-temporal only for a transposed
+// output of at least this many bytes with whole 128-byte rows (measured on
+// MI355X: below it, and for rows that share cache lines, the default policy
+// is faster; above it much slower).
+constexpr int64_t kQcolNtBytes = int64_t(1) << 27;
 
 // Grouped cast: groups stacked along M, each cast as a tensor of its own in
 // one launch.  Walks never cross a group boundary; walk0 numbers them across

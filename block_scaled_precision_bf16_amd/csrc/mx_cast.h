@@ -39,6 +39,7 @@
 #include "bufio.h"
 #include "device_math.h"
 #include "launch.h"
+#include "stage_flush.h"
 
 namespace mxk {
 
@@ -303,32 +304,6 @@ __device__ __forceinline__ void col_flush_q(const MxArgs &a, const ColStage &st,
     }
 }
 
-// Column scales of a strip segment in CH-byte pieces: the count / CH pieces
-// of a column go to neighbouring threads, so one store instruction touches
-// 64 CH / count lines rather than 64 (scattered partial-line stores are what
-// cost here).
-template <int AUX, int CH>
-__device__ __forceinline__ void col_flush_s_ch(const MxArgs &a, const ColStage &st, rsrc_t rs,
-                                               int64_t k0, int64_t nblk, int count)
-{
-    const int t = (int)threadIdx.x;
-    const int pieces = count / CH;                        // per column
-    for (int i = 0; i < pieces; i++) {
-        const int idx = t + kThreads * i;                 // (column, piece) pair
-        const int c = idx / pieces, q = idx - c * pieces;
-        const uint32_t off = k0 + c < a.K ? (uint32_t)(c * nblk) + CH * q : kDead;
-        const uint8_t *src = &st.s[c][CH * q];
-        if constexpr (CH == 16)
-            buf_store16<AUX>(rs, off, *reinterpret_cast<const uint4 *>(src));
-        else if constexpr (CH == 8)
-            buf_store8<AUX>(rs, off, *reinterpret_cast<const uint2 *>(src));
-        else if constexpr (CH == 4)
-            buf_store4<AUX>(rs, off, *reinterpret_cast<const uint32_t *>(src));
-        else
-            buf_store1<AUX>(rs, off, *src);
-    }
-}
-
 // The 4-byte word lane L of a GEMM-ready scale tile holds: bytes j = 0..3 are
 // blocks 2j + L / 32 of the tile's row L % 32, picked from that row's 8 staged
 // block bytes (v.x = blocks 0-3, v.y = blocks 4-7).
@@ -367,8 +342,8 @@ __device__ __forceinline__ void col_flush_s_tiled(const MxArgs &a, const ColStag
 }
 
 // Write the strip segment's column scales: 4 n bytes per column for a walk
-// of n sub-tiles, in the widest pieces (16, 8, 4 or 1 bytes) that the row
-// length of s_col, the segment's start and its length allow.
+// of n sub-tiles (the tile layout, or compact rows in the widest pieces the
+// row length of s_col, the segment's start and its length allow).
 template <int AUX>
 __device__ __forceinline__ void col_flush_s(const MxArgs &a, const ColStage &st, int rg, int tk,
                                             int n)
@@ -383,17 +358,7 @@ __device__ __forceinline__ void col_flush_s(const MxArgs &a, const ColStage &st,
     const int64_t left = nblk - first;
     const int count = (int)(left < 4 * n ? left : 4 * n);
     const rsrc_t rs = make_rsrc(a.s_col, k0 * nblk + first, a.K * nblk);
-    // the piece width also respects the alignment of s_col itself (a group's
-    // column scales may start on any 8-byte boundary)
-    const int64_t align = nblk | first | count | (int64_t)(reinterpret_cast<uintptr_t>(a.s_col) & 15);
-    if ((align & 15) == 0)
-        col_flush_s_ch<AUX, 16>(a, st, rs, k0, nblk, count);
-    else if ((align & 7) == 0)
-        col_flush_s_ch<AUX, 8>(a, st, rs, k0, nblk, count);
-    else if ((align & 3) == 0)
-        col_flush_s_ch<AUX, 4>(a, st, rs, k0, nblk, count);
-    else
-        col_flush_s_ch<AUX, 1>(a, st, rs, k0, nblk, count);
+    flush_scale_rows<AUX>(rs, st.s, k0, a.K, nblk, first, count, a.s_col);
 }
 
 // Row scales of a sub-tile, staged as [128 rows][8 blocks] bytes: thread
@@ -459,8 +424,14 @@ __device__ __forceinline__ void tile_step(const MxArgs &a, const LaneAt &l,
         }
     }
     __syncthreads();
-    if constexpr (COL)
-        col_flush_q<Policy<OP, ROW, COL>::q_col>(a, *st, tm, tk);
+    if constexpr (COL) {
+        // the non-temporal transposed stores pay off only for outputs too
+        // large to be absorbed by the caches (the host decides: qcol_nt)
+        if (Policy<OP, ROW, COL>::q_col == kNT && !a.qcol_nt)
+            col_flush_q<0>(a, *st, tm, tk);
+        else
+            col_flush_q<Policy<OP, ROW, COL>::q_col>(a, *st, tm, tk);
+    }
     if constexpr (ROW)
         srow_flush<Policy<OP, ROW, COL>::s_row>(a, srow, tm, tk);
     __syncthreads();   // the staging buffers are reused by the next sub-tile

@@ -22,6 +22,7 @@
 #include "bufio.h"
 #include "device_math.h"
 #include "launch.h"
+#include "stage_flush.h"
 
 namespace mxk {
 
@@ -201,8 +202,11 @@ __device__ __forceinline__ void nv_flush_q(const Nv4Args &a, const NvStage &st, 
         if constexpr (!HALF) {
             buf_store16<AUX>(rc, col_ok && row0 < a.M ? off : kDead, v);
         } else {
-            buf_store8<AUX>(rc, col_ok && row0 < a.M ? off : kDead, make_uint2(v.x, v.y));
-            buf_store8<AUX>(rc, col_ok && row0 + 16 < a.M ? off + 8 : kDead, make_uint2(v.z, v.w));
+            // rows of M / 2 bytes (M not a multiple of 32) do not start on
+            // 16-byte boundaries: 8-byte pieces, completed in L2 with the
+            // neighbouring chunks, so with the default cache policy
+            buf_store8<0>(rc, col_ok && row0 < a.M ? off : kDead, make_uint2(v.x, v.y));
+            buf_store8<0>(rc, col_ok && row0 + 16 < a.M ? off + 8 : kDead, make_uint2(v.z, v.w));
         }
     }
 }
@@ -213,26 +217,13 @@ template <int AUX>
 __device__ __forceinline__ void nv_flush_s(const Nv4Args &a, const NvStage &st, int tm0, int tk,
                                            int n)
 {
-    const int t = (int)threadIdx.x;
     const int64_t k0 = (int64_t)tk * kTileK;
     const int64_t nblk = a.M >> 4;                             // scales per column
     const int64_t first = (int64_t)tm0 * (kTileM / 16);
     const int64_t left = nblk - first;
     const int count = (int)(left < 8 * n ? left : 8 * n);
     const rsrc_t rs = make_rsrc(a.s_col, k0 * nblk + first, a.K * nblk);
-    if (((nblk | first) & 15) == 0 && (count & 15) == 0) {
-        const int chunks = count >> 4;
-        for (int i = 0; i < chunks; i++) {
-            const int idx = t + kThreads * i;
-            const int c = idx / chunks, q = idx - c * chunks;
-            const uint32_t off = k0 + c < a.K ? (uint32_t)(c * nblk) + 16 * q : kDead;
-            buf_store16<AUX>(rs, off, *reinterpret_cast<const uint4 *>(&st.s[c][16 * q]));
-        }
-    } else {
-        const uint32_t off = k0 + t < a.K ? (uint32_t)(t * nblk) : kDead;
-        for (int i = 0; i < count; i++)
-            buf_store1<AUX>(rs, off + i, st.s[t][i]);
-    }
+    flush_scale_rows<AUX>(rs, st.s, k0, a.K, nblk, first, count, a.s_col);
 }
 
 // Row-block scales of sub-tile tm: thread t < 128 writes row t's 16 bytes.

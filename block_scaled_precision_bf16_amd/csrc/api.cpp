@@ -133,8 +133,11 @@ bool build_groups(const int64_t *rows, int G, int64_t K, int op, bool dbias, boo
     }
     if (M <= 0 || M > kMaxDim || !mx_shape_ok(M, K))
         return false;
-    const int tk = tiles(K, mxk::kTileK);
-    group = walk_group(tiles(M, mxk::kTileM), tk, op, dbias, tiled);
+    int tm[mxk::kMaxGroups];
+    for (int g = 0; g < G; g++)
+        tm[g] = tiles(rows[g], mxk::kTileM);
+    const int per_cu = mxk::target_workgroups(op, dbias) == mxk::kTargetWorkgroupsFused ? 3 : 2;
+    group = mxk::pick_group_rounds(tm, G, tiles(K, mxk::kTileK), per_cu, tiled ? 2 : 1);
     gt = mxk::GroupTable{};
     gt.count = G;
     int64_t walks = 0, r = 0, sr = 0, sc = 0;
@@ -171,7 +174,10 @@ bool build_nv_groups(const int64_t *rows, int G, int64_t K, mxk::GroupTable &gt,
     }
     if (M <= 0 || !shape_ok(M, K, 16))
         return false;
-    group = mxk::pick_group(tiles(M, mxk::kTileM), tiles(K, mxk::kTileK), mxk::kTargetWorkgroups);
+    int tm[mxk::kMaxGroups];
+    for (int g = 0; g < G; g++)
+        tm[g] = tiles(rows[g], mxk::kTileM);
+    group = mxk::pick_group_rounds(tm, G, tiles(K, mxk::kTileK), 2, 1);
     gt = mxk::GroupTable{};
     gt.count = G;
     int64_t walks = 0, r = 0;

@@ -55,6 +55,37 @@ inline int pick_group(int tiles_m, int tiles_k, int target)
     return g;
 }
 
+// Sub-tiles per walk for groups of the given sub-tile row counts (the
+// grouped casts): every group's walks end at its last sub-tile, so short
+// groups leave partial walks, and the launch may need a last, nearly empty
+// round of workgroups.  Among the walk lengths that fill at least 3/4 of the
+// resident slots (slots_per_cu x 256 CUs) in the first round, take the one
+// with the fewest estimated sub-tile steps, rounds x (walk + 1) (the 1 is a
+// walk's fixed cost: its first load and its scale flush); ties go to the
+// longer walk.  Reproduces pick_group's choice on the one-group workloads it
+// was tuned on.
+inline int pick_group_rounds(const int *tiles_m, int groups, int tiles_k, int slots_per_cu,
+                             int min_group)
+{
+    const int64_t slots = 256 * (int64_t)slots_per_cu;
+    int best = 0;
+    int64_t best_cost = 0;
+    for (int g = kMaxGroup; g >= min_group; g >>= 1) {
+        int64_t walks = 0;
+        for (int i = 0; i < groups; i++)
+            walks += (tiles_m[i] + g - 1) / g;
+        const int64_t jobs = walks * tiles_k;
+        if (4 * jobs < 3 * slots && g > min_group)
+            continue;
+        const int64_t cost = (jobs + slots - 1) / slots * (g + 1);
+        if (best == 0 || cost < best_cost) {
+            best = g;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
 struct MxArgs {
     const uint16_t *x;     // input (gated: [M][2N] with the linear half at lin_off)
     const uint16_t *aux;   // grad for dGELU, else unused

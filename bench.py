@@ -68,7 +68,12 @@ CONFIGS = {
     "mxfp8_e4m3_roundup_dim0_dim1_16384": ("c2_dim1_16384", (16384, 16384), "mx", 3),
     "mxfp8_e5m2_roundup_dim0_dim1_16384": ("c2_dim1_16384", (16384, 16384), "mx", 3),
     "mxfp8_tiled_dim0_dim1_16384": ("c2_dim1_16384", (16384, 16384), "mx", 3),
+    "mxfp8_grouped_8x_16384x7168": ("f4_grouped_moe", (16384, 7168), "mx_grouped", 3),
+    "nvfp4_grouped_8x_16384x7168": ("f4_grouped_moe", (16384, 7168), "nvfp4_grouped", 3),
 }
+
+# Row counts of the 8 experts in the grouped workloads.
+MOE_GROUPS = dict(groups=8, seed=8)
 
 # MXFP8 flags OR-ed into the axis mask (E5M2 elements = 4, round-up E8M0
 # rule = 8, GEMM-ready tiled scales = 16), and the format each plain MXFP8
@@ -159,7 +164,24 @@ def main():
     grad = to_dev(g_h) if g_h is not None else None
 
     # outputs and workspace allocated once, outside the timed region
-    if kind.startswith("nvfp4"):
+    if kind == "mx_grouped":
+        grp_rows = W.moe_group_rows(M, **MOE_GROUPS)
+        out = mx.mx_quantize_grouped(x, grp_rows)
+        step = lambda: mx.mx_quantize_grouped(x, grp_rows, out=out)
+        nbk = -(-K // 32)
+        alg_bytes = 2 * M * K + (M * K + M * nbk) + (M * K + sum(K * -(-m // 32) for m in grp_rows))
+        desc = dict(workload=args.config, M=M, K=K, groups=grp_rows, block=32,
+                    directions="row+col per group", format="mxfp8 e4m3 + e8m0")
+    elif kind == "nvfp4_grouped":
+        grp_rows = W.moe_group_rows(M, **MOE_GROUPS)
+        amax = mx.mx_absmax_bf16_grouped(x, grp_rows)
+        out = mx.nvfp4_quantize_transpose_grouped(x, grp_rows, amax)
+        step = lambda: mx.nvfp4_quantize_transpose_grouped(x, grp_rows, amax, out=out)
+        alg_bytes = nvfp4_bytes(M, K, 2)
+        desc = dict(workload=args.config, M=M, K=K, groups=grp_rows, block=16,
+                    directions="row+transpose per group",
+                    format="nvfp4 (e2m1 + e4m3 scales + fp32 scale per group)")
+    elif kind.startswith("nvfp4"):
         two_d = kind == "nvfp4_2d"
         amax = mx.mx_absmax_bf16(x)
         out = mx.nvfp4_quantize_transpose(x, amax, two_d=two_d)
@@ -274,7 +296,13 @@ def main():
               file=sys.stderr, flush=True)
         c0 = time.process_time()
         t0 = time.perf_counter()
-        if kind.startswith("nvfp4"):
+        if kind == "mx_grouped":
+            O.mx_quantize_grouped(xs, W.moe_group_rows(M, **MOE_GROUPS))
+            sb = alg_bytes
+        elif kind == "nvfp4_grouped":
+            O.nvfp4_quantize_transpose_grouped(xs, W.moe_group_rows(M, **MOE_GROUPS))
+            sb = alg_bytes
+        elif kind.startswith("nvfp4"):
             O.nvfp4_quantize_transpose(xs, tensor_amax=O.absmax(x_h), two_d=kind == "nvfp4_2d")
             sb = nvfp4_bytes(rows, K, 2)
         elif kind.startswith("dgated"):

@@ -107,6 +107,18 @@ FULL = {
 }
 
 
+def moe_group_rows(total: int, groups: int, seed: int, step: int = 16) -> list:
+    """Uneven per-expert row counts (multiples of `step`) summing to `total`:
+    expert shares drawn from a symmetric Dirichlet(1) (seeded), rounded down to
+    the step, the remainder given to the largest expert.  Sizes only; no
+    quantisation arithmetic."""
+    rng = np.random.default_rng(seed)
+    share = rng.dirichlet(np.ones(groups))
+    rows = [int(r) // step * step for r in share * total]
+    rows[int(np.argmax(rows))] += total - sum(rows)
+    return rows
+
+
 def make(name: str, M: int = None, K: int = None):
     """Inputs of a workload, optionally at a reduced shape with the same recipe."""
     if name == "c1_special":
@@ -129,4 +141,8 @@ def make(name: str, M: int = None, K: int = None):
         # [gate | linear] [M][2N] ~N(0, 1); here K names N
         M, N = M or 8192, K or 4096
         return normal(M, N, seed=7), normal(M, 2 * N, seed=77)
+    if name == "f4_grouped_moe":
+        # 8 experts' tokens stacked along rows, N(0, 1); the row counts come
+        # from moe_group_rows(M, 8, seed=8)
+        return normal(M or 16384, K or 7168, seed=88)
     raise KeyError(name)

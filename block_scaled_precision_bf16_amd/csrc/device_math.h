@@ -248,9 +248,10 @@ __device__ __forceinline__ float exp32(float a)
     p = __builtin_fmaf(p, r, 0.5f);
     p = __builtin_fmaf(p, r, 1.0f);
     p = __builtin_fmaf(p, r, 1.0f);
-    const int ni = (int)n;                            // in [-150, 128]
-    const int n1 = ni / 2, n2 = ni - n1;              // each in [-75, 64]
-    float e = (p * f32_bits((uint32_t)(n1 + 127) << 23)) * f32_bits((uint32_t)(n2 + 127) << 23);
+    // p * 2^n with one rounding (v_ldexp_f32, denormals kept): the same bits
+    // as scaling by 2^(n/2) and then 2^(n - n/2), the first product exact
+    const float e0 = __builtin_amdgcn_ldexpf(p, (int)n);   // n in [-150, 128]
+    float e = e0;
     e = a > HI ? __builtin_inff() : e;
     e = a < LO ? 0.0f : e;
     return a != a ? a : e;

@@ -223,20 +223,20 @@ __device__ __forceinline__ uint32_t e2m1_rne_sat(float v)
 // Fused pre-op arithmetic.  Each statement is one IEEE fp32 operation.
 // ---------------------------------------------------------------------------
 
-// e^a: Cody & Waite reduction a = n ln2 + r (ln2 = 355/512 + remainder), the
-// degree-7 Taylor polynomial of e^r by Horner with fused multiply-adds, and
-// scaling by 2^n as two exact power-of-two factors (one final rounding, also
-// for subnormal results).
-__device__ __forceinline__ float exp32(float a)
+// e^a for a <= 0 (or NaN), the only arguments the activations need: Cody &
+// Waite reduction a = n ln2 + r (ln2 = 355/512 + remainder), the degree-7
+// Taylor polynomial of e^r by Horner with fused multiply-adds, and scaling by
+// 2^n with one final rounding (also for subnormal results).  Arguments are
+// clamped at -104, where the sequence already gives 0 (0.97 * 2^-150 rounds
+// to 0), so every smaller argument gets that same 0 without a select; NaN
+// propagates through the final select.
+__device__ __forceinline__ float exp32_nonpos(float a)
 {
     const float LOG2E = 1.44269504088896340736f;
     const float LN2_A = 0.693359375f;                 // 355/512
     const float LN2_B = -2.12194440054690583e-4f;     // ln2 - 355/512
-    const float HI = 88.72283172607421875f;           // above: e^a rounds to +Inf
-    const float LO = -104.0f;                         // below: e^a rounds to 0
-    // straight-line: evaluate at the clamped argument, then select the
-    // out-of-range results (identical to returning early for them)
-    const float c = __builtin_amdgcn_fmed3f(a, LO, HI);
+    const float LO = -104.0f;
+    const float c = __builtin_fmaxf(a, LO);
     const float n = __builtin_rintf(c * LOG2E);
     float r = __builtin_fmaf(n, -LN2_A, c);
     r = __builtin_fmaf(n, -LN2_B, r);
@@ -250,10 +250,7 @@ __device__ __forceinline__ float exp32(float a)
     p = __builtin_fmaf(p, r, 1.0f);
     // p * 2^n with one rounding (v_ldexp_f32, denormals kept): the same bits
     // as scaling by 2^(n/2) and then 2^(n - n/2), the first product exact
-    const float e0 = __builtin_amdgcn_ldexpf(p, (int)n);   // n in [-150, 128]
-    float e = e0;
-    e = a > HI ? __builtin_inff() : e;
-    e = a < LO ? 0.0f : e;
+    const float e = __builtin_amdgcn_ldexpf(p, (int)n);    // n in [-150, 0]
     return a != a ? a : e;
 }
 
@@ -261,7 +258,7 @@ __device__ __forceinline__ float exp32(float a)
 // cancellation): z >= 0 gives (1/(1+e), e/(1+e)), z < 0 the swapped pair.
 __device__ __forceinline__ void sigmoid_pair(float z, float &s, float &sc)
 {
-    float e = exp32(-__builtin_fabsf(z));
+    float e = exp32_nonpos(-__builtin_fabsf(z));
     float d = 1.0f + e;
     // r = fl32(1 / d) for d in [1, 2]: the hardware reciprocal estimate and one
     // Newton step with FMAs; equal to the IEEE quotient for every float in

@@ -1,7 +1,8 @@
 // mx_cast.h -- the MXFP8 cast kernel for gfx950: row-wise (dim0), column-wise
 // (dim1, transposed output) or both in one pass over the bf16 input,
-// optionally with a fused GELU / dGELU / SwiGLU / GeGLU pre-op and a dbias
-// column sum.  These are the kernels the TransformerEngine PR 3291 page
+// optionally with a fused GELU / dGELU / dSiLU / SwiGLU / GeGLU / dSwiGLU /
+// dGeGLU pre-op and a dbias column sum, for one tensor or for a group of
+// tensors stacked along M.  These are the kernels the TransformerEngine PR 3291 page
 // times ("MXFP8 generic quantize kernel", "MXFP8 specialized cast-only kernel
 // (bidimensional)", "MXFP8 gated (swiglu / geglu) kernel") and the torchao
 // dim1 cast of PR 12, designed here for CDNA4.
@@ -32,8 +33,9 @@
 //
 // The element format and the scale rule (E4M3 or E5M2; floor or round-up
 // E8M0) are a template flag FMT; each of the four formats is instantiated
-// in a translation unit of its own (mx_cast_fmt*.hip), which keeps the
-// build parallel.
+// in a translation unit of its own, plain (mx_cast_fmt_*.hip) and grouped
+// (mx_cast_grp_*.hip), which keeps the build parallel.  The scale layout
+// (compact or GEMM-ready tiles) is a run-time choice of the two flushes.
 #pragma once
 
 #include "bufio.h"

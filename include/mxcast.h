@@ -15,16 +15,22 @@
  *     table "MXFP8 gated (swiglu / geglu) kernel"), and the backward casts
  *     the same tables name: dSiLU (generic kernel) and dSwiGLU / dGeGLU
  *     (gated kernel);
- *   - NVFP4 quantize-transpose with 16-element blocks (PR 3291, the NVFP4
- *     quantize-transpose kernels under "Important Files Changed" and
- *     "Patched but not measurable").
+ *   - NVFP4 quantize-transpose with 16-element or 16 x 16 blocks (PR 3291,
+ *     the NVFP4 quantize-transpose kernels under "Important Files Changed",
+ *     "Patched but not measurable" and table "NVFP4 2D quantize-transpose
+ *     kernel");
+ *   - grouped (per-expert) MXFP8 and NVFP4 casts of tensors stacked along
+ *     rows (PR 3291, the grouped NVFP4 quantize-transpose row);
+ *   - format, layout and shape extensions of the MXFP8 casts: E5M2 elements,
+ *     the round-up scale rule, GEMM-ready scale tiles, partial edge blocks.
  *
  * Numerics (the pages name these formats but do not define their
  * arithmetic; these are the readings the library implements bit-exactly):
  *   MXFP8 block of 32: amax = max|y|; scale byte (E8M0) = floor(log2 amax) - 8
  *     + 127 clamped to [0, 254]; element = E4M3(y * 2^(127 - byte)), round
  *     to nearest, ties to even code, saturating at +-448, sign kept.  A block
- *     holding Inf/NaN gets scale 0xFF and elements 0x7F.
+ *     holding Inf/NaN gets scale 0xFF and elements 0x7F.  (E5M2 and the
+ *     round-up rule: see MX_ELEM_E5M2 / MX_SCALE_ROUND_UP.)
  *   Fused pre-ops: evaluated in fp32 (tanh-form GELU through
  *     0.5(1+tanh u) = 1/(1+e^-2u), the library's own exp), rounded once to
  *     bf16; that bf16 tensor y is what is quantised and what dbias sums.
@@ -40,7 +46,8 @@
  *   - bf16 tensors are raw 16-bit patterns; E4M3, E8M0 and packed E2M1 are
  *     raw bytes.  Every tensor is row-major and contiguous.
  *   - Column-wise outputs are transposed: for x[M][K], q_col is [K][M] and
- *     s_col is [K][M/32] (MXFP8) or q_col [K][M/2], s_col [K][M/16] (NVFP4).
+ *     s_col is [K][ceil(M/32)] (MXFP8, compact scales) or q_col [K][M/2],
+ *     s_col [K][M/16] (NVFP4).
  *   - Every pointer must be 16-byte aligned (dbias: 4-byte).
  *   - Arguments are validated on the host before anything is enqueued; on a
  *     validation error nothing is written and a non-zero status returns.
@@ -77,7 +84,7 @@ typedef enum mx_status {
 } mx_status;
 
 /* axis_mask bits */
-#define MX_ROWWISE 1u       /* blocks along K: q_row[M][K], s_row[M][K/32]    */
+#define MX_ROWWISE 1u       /* blocks along K: q_row[M][K] and its scales    */
 #define MX_COLWISE 2u       /* blocks along M, transposed outputs             */
 
 /*

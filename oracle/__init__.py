@@ -90,6 +90,11 @@ def lib():
         L.orc_mx_quantize_grouped.argtypes = [_u16p, _u16p, _i64, ctypes.POINTER(ctypes.c_int64),
                                               ctypes.c_int, ctypes.c_uint, ctypes.c_int,
                                               _u8p, _u8p, _u8p, _u8p, _f32p]
+        L.orc_mx_quantize_gated_grouped.restype = ctypes.c_int
+        L.orc_mx_quantize_gated_grouped.argtypes = [_u16p, _u16p, _i64,
+                                                    ctypes.POINTER(ctypes.c_int64), ctypes.c_int,
+                                                    ctypes.c_uint, ctypes.c_int, _u8p, _u8p, _u8p,
+                                                    _u8p]
         L.orc_mx_quantize_gated.restype = ctypes.c_int
         L.orc_mx_quantize_gated.argtypes = [_u16p, _i64, _i64, ctypes.c_uint, ctypes.c_int,
                                             _u8p, _u8p, _u8p, _u8p, _u16p]
@@ -335,6 +340,32 @@ def mx_quantize_grouped(x, group_rows, grad=None, axis=ROWWISE | COLWISE, fusion
     if rc != 0:
         raise ValueError(f"oracle mx_quantize_grouped failed with code {rc}")
     return dict(q_row=q_row, s_row=s_row, q_col=q_col, s_col=s_col, dbias=dbias)
+
+
+def mx_quantize_gated_grouped(x, group_rows, act, axis=ROWWISE | COLWISE, grad=None):
+    """Grouped gated cast: x[M][2N] = [gate | linear] stacked by group; with
+    grad ([M][N]) the gated backward.  Flat per-group-concatenated outputs
+    (q_row [M][W], W = N forward or 2N backward)."""
+    x = _c(x, np.uint16)
+    M, N2 = x.shape
+    N = N2 // 2
+    rows = np.ascontiguousarray(group_rows, dtype=np.int64)
+    assert rows.sum() == M
+    g = _c(grad, np.uint16) if grad is not None else None
+    W = N2 if grad is not None else N
+    sr = sum(_scale_len(int(m), W, axis) for m in rows)
+    sc = sum(_scale_len(W, int(m), axis) for m in rows)
+    q_row = np.zeros((M, W), np.uint8) if axis & ROWWISE else None
+    s_row = np.zeros(sr, np.uint8) if axis & ROWWISE else None
+    q_col = np.zeros(W * M, np.uint8) if axis & COLWISE else None
+    s_col = np.zeros(sc, np.uint8) if axis & COLWISE else None
+    rc = lib().orc_mx_quantize_gated_grouped(_p(g, _u16p), _p(x, _u16p), N,
+                                             rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                             rows.size, axis, act, _p(q_row, _u8p), _p(s_row, _u8p),
+                                             _p(q_col, _u8p), _p(s_col, _u8p))
+    if rc != 0:
+        raise ValueError(f"oracle mx_quantize_gated_grouped failed with code {rc}")
+    return dict(q_row=q_row, s_row=s_row, q_col=q_col, s_col=s_col)
 
 
 def mx_quantize_gated(x, act, axis=ROWWISE | COLWISE, want_y=False):

@@ -775,6 +775,41 @@ int orc_mx_quantize_grouped(const uint16_t *x, const uint16_t *grad, int64_t K,
     return ORC_OK;
 }
 
+/* Grouped gated casts (R10): x[M][2N] = [gate | linear] rows stacked by group;
+ * group g's output tensor is that of orc_mx_quantize_gated (forward, grad
+ * NULL: y[rows][N]) or orc_mx_quantize_dgated (backward: grad[M][N] given,
+ * dx[rows][2N]); outputs concatenated group after group as in
+ * orc_mx_quantize_grouped, with W = N (forward) or 2N (backward) the width of
+ * the quantised tensor. */
+int orc_mx_quantize_gated_grouped(const uint16_t *grad, const uint16_t *x, int64_t N,
+                                  const int64_t *rows, int G, unsigned axis, int act,
+                                  uint8_t *q_row, uint8_t *s_row, uint8_t *q_col, uint8_t *s_col)
+{
+    if (G <= 0 || N <= 0)
+        return ORC_ERR_SHAPE;
+    const int64_t W = grad ? 2 * N : N;
+    int64_t r = 0, sr = 0, sc = 0;
+    for (int g = 0; g < G; g++) {
+        const int64_t m = rows[g];
+        if (m < 0)
+            return ORC_ERR_SHAPE;
+        if (m > 0) {
+            uint8_t *qr = q_row ? q_row + r * W : NULL, *srp = s_row ? s_row + sr : NULL;
+            uint8_t *qc = q_col ? q_col + W * r : NULL, *scp = s_col ? s_col + sc : NULL;
+            int rc = grad ? orc_mx_quantize_dgated(grad + r * N, x + r * 2 * N, m, N, axis, act,
+                                                   qr, srp, qc, scp, NULL)
+                          : orc_mx_quantize_gated(x + r * 2 * N, m, N, axis, act, qr, srp, qc,
+                                                  scp, NULL);
+            if (rc != ORC_OK)
+                return rc;
+        }
+        sr += scale_bytes(m, W, axis);
+        sc += scale_bytes(W, m, axis);
+        r += m;
+    }
+    return ORC_OK;
+}
+
 /* ------------------------------------------------------------------------ */
 /* NVFP4 (R6).                                                               */
 /* ------------------------------------------------------------------------ */

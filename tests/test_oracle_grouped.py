@@ -148,3 +148,27 @@ def test_nvfp4_group_global_scales_follow_group_amax():
     # a given amax array overrides the groups' own
     g2 = O.nvfp4_quantize_transpose_grouped(x, rows, amax=[1.0, 2.0])
     assert list(g2["sg"]) == [np.float32(1.0 / 2688.0), np.float32(2.0 / 2688.0)]
+
+
+# --- grouped gated casts ------------------------------------------------------
+
+@pytest.mark.parametrize("backward", [False, True])
+def test_gated_grouped_rowwise_equals_stacked_and_aligned_slices(backward):
+    rows = [64, 0, 32, 96]
+    M, N = sum(rows), 80
+    x = W.normal(M, 2 * N, seed=76)
+    grad = W.normal(M, N, seed=77) if backward else None
+    g = O.mx_quantize_gated_grouped(x, rows, O.GATED_SWIGLU, grad=grad)
+    if backward:
+        p = O.mx_quantize_dgated(grad, x, O.GATED_SWIGLU)
+    else:
+        p = O.mx_quantize_gated(x, O.GATED_SWIGLU)
+    Wd = 2 * N if backward else N
+    assert np.array_equal(g["q_row"], p["q_row"]) and np.array_equal(g["s_row"], p["s_row"].ravel())
+    qc = split(g["q_col"], [Wd * m for m in rows])
+    sc = split(g["s_col"], [Wd * (m // 32) for m in rows])
+    r0 = 0
+    for m, q, s in zip(rows, qc, sc):
+        assert np.array_equal(q.reshape(Wd, m), p["q_col"][:, r0:r0 + m])
+        assert np.array_equal(s.reshape(Wd, m // 32), p["s_col"][:, r0 // 32:(r0 + m) // 32])
+        r0 += m

@@ -36,6 +36,7 @@ OP_GATED, OP_DGATED = 0x100, 0x200
 
 EXPORTS = ("mx_quantize", "mx_quantize_workspace_size", "mx_scale_size", "mx_quantize_grouped",
            "mx_quantize_grouped_workspace_size", "mx_grouped_scale_size", "mx_quantize_gated",
+           "mx_quantize_gated_grouped", "mx_quantize_dgated_grouped",
            "mx_quantize_dgated", "mx_fused_values",
            "mx_absmax_bf16", "nvfp4_quantize_transpose", "nvfp4_quantize_transpose_2d",
            "mx_absmax_bf16_grouped", "nvfp4_quantize_transpose_grouped",
@@ -77,6 +78,12 @@ def lib():
                                                          ctypes.c_int]
         L.mx_grouped_scale_size.restype = ctypes.c_size_t
         L.mx_grouped_scale_size.argtypes = [_i64, _vp, ctypes.c_int, ctypes.c_uint, ctypes.c_int]
+        L.mx_quantize_gated_grouped.restype = ctypes.c_int
+        L.mx_quantize_gated_grouped.argtypes = [_vp, _i64, _vp, ctypes.c_int, ctypes.c_uint,
+                                                ctypes.c_int, _vp, _vp, _vp, _vp, _vp]
+        L.mx_quantize_dgated_grouped.restype = ctypes.c_int
+        L.mx_quantize_dgated_grouped.argtypes = [_vp, _vp, _i64, _vp, ctypes.c_int, ctypes.c_uint,
+                                                 ctypes.c_int, _vp, _vp, _vp, _vp, _vp]
         L.mx_quantize_gated.restype = ctypes.c_int
         L.mx_quantize_gated.argtypes = [_vp, _i64, _i64, ctypes.c_uint, ctypes.c_int,
                                         _vp, _vp, _vp, _vp, _vp]
@@ -376,3 +383,34 @@ def nvfp4_quantize_transpose_grouped(x, group_rows, amax, axis=ROWWISE | COLWISE
                                                 _stream(dev, stream))
     _check(st, "nvfp4_quantize_transpose_grouped")
     return {k: o.get(k) for k in ("q_row", "s_row", "q_col", "s_col", "sg")}
+
+
+def mx_quantize_gated_grouped(x, group_rows, act, grad=None, axis=ROWWISE | COLWISE, out=None,
+                              stream=None):
+    """Grouped gated MXFP8 cast of x[M][2N] = [gate | linear] stacked by group
+    (with grad [M][N]: the gated backward).  q_row [M][W] (W = N, or 2N
+    backward) and flat s_row / q_col / s_col, the groups one after the other."""
+    x = _bf16_bits(x)
+    M, N2 = x.shape
+    N = N2 // 2
+    W = N2 if grad is not None else N
+    G = len(group_rows)
+    dev = x.device
+    o = dict(out or {})
+    if axis & ROWWISE:
+        o.setdefault("q_row", _u8((M, W), dev))
+        o.setdefault("s_row", _u8((max(1, mx_grouped_scale_size(W, group_rows, axis, False)),), dev))
+    if axis & COLWISE:
+        o.setdefault("q_col", _u8((M * W,), dev))
+        o.setdefault("s_col", _u8((max(1, mx_grouped_scale_size(W, group_rows, axis, True)),), dev))
+    rows = _rows_arg(group_rows)
+    ptrs = (_ptr(o.get("q_row")), _ptr(o.get("s_row")), _ptr(o.get("q_col")), _ptr(o.get("s_col")))
+    if grad is None:
+        st = lib().mx_quantize_gated_grouped(_ptr(x), N, ctypes.cast(rows, _vp), G, axis, act,
+                                             *ptrs, _stream(dev, stream))
+    else:
+        grad = _bf16_bits(grad)
+        st = lib().mx_quantize_dgated_grouped(_ptr(grad), _ptr(x), N, ctypes.cast(rows, _vp), G,
+                                              axis, act, *ptrs, _stream(dev, stream))
+    _check(st, "mx_quantize_gated_grouped")
+    return {k: o.get(k) for k in ("q_row", "s_row", "q_col", "s_col")}

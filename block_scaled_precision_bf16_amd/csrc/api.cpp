@@ -262,6 +262,66 @@ static mx_status nvfp4_impl(bool two_d, const void *x, int64_t M, int64_t K, con
     return from_hip(mxk::launch_nvfp4(axis_mask, two_d, a, stream));
 }
 
+// The grouped gated casts: group g owns rows r_g .. r_g + rows[g] - 1 of
+// x[M][2N] (and of grad[M][N] for the backward); the quantised tensor of a
+// group has width W = N (forward) or 2N (backward).
+static mx_status gated_grouped_impl(const void *grad, const void *x, int64_t N,
+                                    const int64_t *group_rows, int G, unsigned axis_mask, int act,
+                                    uint8_t *q_row, uint8_t *s_row, uint8_t *q_col, uint8_t *s_col,
+                                    hipStream_t stream)
+{
+    const bool bwd = grad != nullptr;
+    if (!mx_mode_ok(axis_mask) || (act != MX_GATED_SWIGLU && act != MX_GATED_GEGLU))
+        return MX_ERR_ENUM;
+    const bool row = axis_mask & MX_ROWWISE, col = axis_mask & MX_COLWISE;
+    if (!x || !group_rows || (row && (!q_row || !s_row)) || (col && (!q_col || !s_col)))
+        return MX_ERR_NULL;
+    const int op = bwd ? (act == MX_GATED_SWIGLU ? mxk::OP_DSWIGLU : mxk::OP_DGEGLU)
+                       : (act == MX_GATED_SWIGLU ? mxk::OP_SWIGLU : mxk::OP_GEGLU);
+    const int64_t W = bwd ? 2 * N : N;
+    const bool tiled = (axis_mask & MX_SCALE_TILED) != 0;
+    mxk::GroupTable gt;
+    int64_t M;
+    int group;
+    if (!mx_shape_ok(16, N) || !build_groups(group_rows, G, W, op, false, tiled, gt, M, group) ||
+        !mx_shape_ok(M, 2 * N))
+        return MX_ERR_SHAPE;
+    if (!aligned(x, 16) || (bwd && !aligned(grad, 16)) ||
+        (row && (!aligned(q_row, 16) || !aligned(s_row, 16))) ||
+        (col && (!aligned(q_col, 16) || !aligned(s_col, 16))))
+        return MX_ERR_ALIGN;
+    const uint64_t n = (uint64_t)(M * N);
+    const Span in[2] = {{x, 4 * n}, {bwd ? grad : nullptr, 2 * n}};
+    const Span out[4] = {{row ? q_row : nullptr, (uint64_t)(M * W)},
+                         {row ? s_row : nullptr, grouped_scale_bytes(group_rows, G, W, false, tiled)},
+                         {col ? q_col : nullptr, (uint64_t)(M * W)},
+                         {col ? s_col : nullptr, grouped_scale_bytes(group_rows, G, W, true, tiled)}};
+    if (any_alias(in, 2, out, 4))
+        return MX_ERR_ALIAS;
+
+    mxk::MxArgs a;
+    a.x = static_cast<const uint16_t *>(x);
+    a.aux = bwd ? static_cast<const uint16_t *>(grad) : nullptr;
+    a.M = M;
+    a.K = W;
+    a.ldx = 2 * N;
+    a.ldg = bwd ? N : 0;
+    a.lin_off = N;
+    a.q_row = q_row;
+    a.s_row = s_row;
+    a.q_col = q_col;
+    a.s_col = s_col;
+    a.partials = nullptr;
+    a.tiled = tiled;
+    a.qcol_nt = 0;
+    a.tiles_k = tiles(W, mxk::kTileK);
+    a.tiles_m = tiles(M, mxk::kTileM);
+    a.group = group;
+    a.groups_m = gt.walk0[G];
+    return from_hip(mxk::launch_mx_cast_grouped(op, axis_mask & 3u, axis_mask & kFmtBits, false, a,
+                                                gt, stream));
+}
+
 extern "C" {
 
 int mx_abi_version(void) { return MXCAST_ABI_VERSION; }
@@ -446,6 +506,25 @@ mx_status mx_quantize_grouped(const void *x, const void *grad, int64_t K, const 
     if (st != MX_OK || !want_dbias)
         return st;
     return from_hip(mxk::launch_dbias_reduce_grouped(a.partials, gt, K, dbias, stream));
+}
+
+mx_status mx_quantize_gated_grouped(const void *x, int64_t N, const int64_t *group_rows, int G,
+                                    unsigned axis_mask, int act, uint8_t *q_row, uint8_t *s_row,
+                                    uint8_t *q_col, uint8_t *s_col, hipStream_t stream)
+{
+    return gated_grouped_impl(nullptr, x, N, group_rows, G, axis_mask, act, q_row, s_row, q_col,
+                              s_col, stream);
+}
+
+mx_status mx_quantize_dgated_grouped(const void *grad, const void *x, int64_t N,
+                                     const int64_t *group_rows, int G, unsigned axis_mask, int act,
+                                     uint8_t *q_row, uint8_t *s_row, uint8_t *q_col,
+                                     uint8_t *s_col, hipStream_t stream)
+{
+    if (!grad)
+        return MX_ERR_NULL;
+    return gated_grouped_impl(grad, x, N, group_rows, G, axis_mask, act, q_row, s_row, q_col,
+                              s_col, stream);
 }
 
 mx_status mx_quantize_gated(const void *x, int64_t M, int64_t N, unsigned axis_mask, int act,

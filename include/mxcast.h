@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define MXCAST_ABI_VERSION 7
+#define MXCAST_ABI_VERSION 8
 
 typedef enum mx_status {
     MX_OK = 0,
@@ -256,6 +256,28 @@ mx_status mx_quantize_gated(const void *x, int64_t M, int64_t N, unsigned axis_m
 mx_status mx_quantize_dgated(const void *grad, const void *x, int64_t M, int64_t N,
                              unsigned axis_mask, int act, uint8_t *q_row, uint8_t *s_row,
                              uint8_t *q_col, uint8_t *s_col, hipStream_t stream);
+
+/*
+ * Grouped gated casts (an MoE layer's experts in one launch): x is bf16
+ * [M][2N] = [gate | linear] with the groups' rows stacked as for
+ * mx_quantize_grouped (HOST group_rows, multiples of 16, empty groups
+ * allowed, 1 <= G <= 64); each group is cast exactly as mx_quantize_gated
+ * (forward: quantised tensor [rows][N], W = N) or mx_quantize_dgated
+ * (backward, grad bf16 [M][N]: quantised tensor [rows][2N], W = 2N) casts
+ * it on its own.  q_row is [M][W]; q_col holds group g's [W][rows] at byte
+ * W * r_g; s_row and s_col hold the groups' scale tensors one after the
+ * other, group g's mx_scale_size(rows, W) and mx_scale_size(W, rows) bytes
+ * (mx_grouped_scale_size(W, ...) in total).  axis_mask as for mx_quantize.
+ * Errors as for mx_quantize_gated; MX_ERR_SHAPE also for G out of range or a
+ * bad group size.
+ */
+mx_status mx_quantize_gated_grouped(const void *x, int64_t N, const int64_t *group_rows, int G,
+                                    unsigned axis_mask, int act, uint8_t *q_row, uint8_t *s_row,
+                                    uint8_t *q_col, uint8_t *s_col, hipStream_t stream);
+mx_status mx_quantize_dgated_grouped(const void *grad, const void *x, int64_t N,
+                                     const int64_t *group_rows, int G, unsigned axis_mask, int act,
+                                     uint8_t *q_row, uint8_t *s_row, uint8_t *q_col,
+                                     uint8_t *s_col, hipStream_t stream);
 
 /*
  * The fused elementwise values alone, as bf16: y = pre-op(x[, grad]) for

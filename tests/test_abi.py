@@ -41,7 +41,7 @@ def header_abi_version():
 
 
 def test_version_and_status_strings():
-    assert mx.mx_abi_version() == header_abi_version() == 7
+    assert mx.mx_abi_version() == header_abi_version() == 8
     for code in range(9):
         assert mx.mx_status_str(code).startswith("MX_")
     assert "unknown" in mx.mx_status_str(99)
@@ -310,6 +310,31 @@ def test_grouped_rejects():
     assert gq(fusion=mx.FUSE_DBIAS, ws_bytes=16) == mx.MX_ERR_WORKSPACE
     assert gq(q_col=b.p("x", 16)) == mx.MX_ERR_ALIAS
     assert gq(fusion=mx.FUSE_DBIAS, dbias=b.p("ws", 0)) == mx.MX_ERR_ALIAS
+    assert b.untouched()
+
+
+def test_grouped_gated_rejects():
+    b = Bufs(64, 128)          # x [64][128] = [gate | linear] (N = 64), grad in "g"
+    L = mx.lib()
+
+    def gg(rows=(32, 0, 32), bwd=False, **kw):
+        arr = (ctypes.c_int64 * max(1, len(rows)))(*rows)
+        args = [kw.get("x", b.p("x")), kw.get("N", 64), ctypes.cast(arr, ctypes.c_void_p),
+                kw.get("G", len(rows)), kw.get("axis", 3), kw.get("act", 1),
+                kw.get("q_row", b.p("q_row")), kw.get("s_row", b.p("s_row")),
+                kw.get("q_col", b.p("q_col")), kw.get("s_col", b.p("s_col")), None]
+        if bwd:
+            return L.mx_quantize_dgated_grouped(kw.get("g", b.p("g")), *args)
+        return L.mx_quantize_gated_grouped(*args)
+    for bwd in (False, True):
+        assert gg(bwd=bwd, act=0) == mx.MX_ERR_ENUM and gg(bwd=bwd, axis=0x40 | 3) == mx.MX_ERR_ENUM
+        assert gg(bwd=bwd, x=NULL) == mx.MX_ERR_NULL
+        assert gg(bwd=bwd, rows=(32, 8)) == mx.MX_ERR_SHAPE and gg(bwd=bwd, N=12) == mx.MX_ERR_SHAPE
+        assert gg(bwd=bwd, G=0) == mx.MX_ERR_SHAPE
+        assert gg(bwd=bwd, x=b.p("x", 4)) == mx.MX_ERR_ALIGN
+        assert gg(bwd=bwd, q_row=b.p("x", 16)) == mx.MX_ERR_ALIAS
+    assert gg(bwd=True, g=NULL) == mx.MX_ERR_NULL
+    assert gg(bwd=True, q_col=b.p("g", 32)) == mx.MX_ERR_ALIAS
     assert b.untouched()
 
 

@@ -130,3 +130,20 @@ def test_grouped_nvfp4_moe_eight_experts():
     torch.cuda.synchronize()
     o = O.nvfp4_quantize_transpose_grouped(x, rows)
     mx_outputs_equal(g, o, "nvfp4 moe experts")
+
+
+# --- grouped gated casts --------------------------------------------------------
+
+@pytest.mark.parametrize("flags", [0, mx.SCALE_TILED | mx.ELEM_E5M2], ids=["plain", "tiled-e5m2"])
+@pytest.mark.parametrize("backward", [False, True], ids=["fwd", "bwd"])
+@pytest.mark.parametrize("act", [mx.GATED_SWIGLU, mx.GATED_GEGLU])
+@pytest.mark.parametrize("rows,N", [([128, 0, 256, 48], 160), ([16] * 5, 40), ([512, 16, 0, 336], 264)])
+def test_grouped_gated(rows, N, act, backward, flags):
+    M = sum(rows)
+    x = W.normal(M, 2 * N, seed=8000 + M + N)
+    grad = W.normal(M, N, seed=8001 + M + N) if backward else None
+    g = mx.mx_quantize_gated_grouped(to_dev(x), rows, act, grad=to_dev(grad) if backward else None,
+                                     axis=3 | flags)
+    torch.cuda.synchronize()
+    o = O.mx_quantize_gated_grouped(x, rows, act, axis=3 | flags, grad=grad)
+    mx_outputs_equal(g, o, f"grouped gated {rows} N={N} act {act} bwd {backward} flags {flags}")

@@ -108,3 +108,25 @@ def test_c1_special_256x512():
     g = mx.mx_quantize(to_dev(x))
     torch.cuda.synchronize()
     mx_outputs_equal(g, O.mx_quantize(x), "C1")
+
+
+@pytest.mark.parametrize("M,K", [(1 << 23, 32), (32, 1 << 23), ((1 << 23) - 16, 40)])
+@pytest.mark.parametrize("layout", [0, mx.SCALE_TILED], ids=["compact", "tiled"])
+def test_mxfp8_maximum_dimensions(M, K, layout):
+    """The largest row count and row length the library accepts (2^23): the
+    in-tile byte offsets of the loads reach 127 * 2^24, just below 2^31."""
+    x = W.loguniform_rows(M, K, seed=90)
+    g = mx.mx_quantize(to_dev(x), axis=3 | layout)
+    torch.cuda.synchronize()
+    o = O.mx_quantize(x, axis=3 | layout)
+    mx_outputs_equal(g, o, f"max dims {M}x{K} {layout}")
+
+
+@pytest.mark.parametrize("M,K", [(1 << 23, 16), (16, 1 << 23)])
+def test_nvfp4_maximum_dimensions(M, K):
+    x = W.student_t_rows(M, K, seed=91)
+    xd = to_dev(x)
+    g = mx.nvfp4_quantize_transpose(xd, mx.mx_absmax_bf16(xd))
+    torch.cuda.synchronize()
+    o = O.nvfp4_quantize_transpose(x)
+    mx_outputs_equal(g, o, f"nvfp4 max dims {M}x{K}")

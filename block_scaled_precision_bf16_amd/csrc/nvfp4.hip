@@ -178,12 +178,13 @@ __device__ __forceinline__ void nv_load(const Nv4Args &a, const NvLane &l, int t
 
 // Transposed output of the staged pair (chunks 0..4 * parts - 1 of each
 // transposed row; parts = 1 when the walk ends on the first sub-tile of a
-// pair).  tm: the pair's first sub-tile.  HALF: M is not a multiple of 32,
+// pair).  tm: the pair's first sub-tile.  half: M is not a multiple of 32,
 // so a 16-byte chunk may hold 16 rows inside M and 16 outside; then each
-// chunk leaves as two 8-byte halves.
-template <int AUX, bool HALF>
+// chunk leaves as two 8-byte halves (a run-time choice, so that the groups of
+// a grouped cast each take their own).
+template <int AUX>
 __device__ __forceinline__ void nv_flush_q(const Nv4Args &a, const NvStage &st, int tm, int tk,
-                                           int parts)
+                                           int parts, bool half)
 {
     const int t = (int)threadIdx.x;
     const int jr = t & 7;
@@ -199,7 +200,7 @@ __device__ __forceinline__ void nv_flush_q(const Nv4Args &a, const NvStage &st, 
         const bool col_ok = in_pair && k0 + kr < a.K;
         const uint4 v = *reinterpret_cast<const uint4 *>(&st.q[kr][16 * nv_chunk(kr, jr)]);
         const uint32_t off = (uint32_t)(kr * ld) + 16 * jr;
-        if constexpr (!HALF) {
+        if (!half) {
             buf_store16<AUX>(rc, col_ok && row0 < a.M ? off : kDead, v);
         } else {
             // rows of M / 2 bytes (M not a multiple of 32) do not start on
@@ -304,7 +305,7 @@ __device__ __forceinline__ void nv_step_2d(const Nv4Args &a, const NvLane &l,
     }
 }
 
-template <bool ROW, bool COL, bool HALF, bool TWO_D, int FLUSH>
+template <bool ROW, bool COL, bool TWO_D, int FLUSH>
 __device__ __forceinline__ void nv_step(const Nv4Args &a, const NvLane &l,
                                         const uint32_t (&w)[kRowsPerLane][4], NvStage &st,
                                         float sg, int tm, int tk, int g)
@@ -397,7 +398,7 @@ __device__ __forceinline__ void nv_step(const Nv4Args &a, const NvLane &l,
     if constexpr (ROW)
         nv_flush_srow<P::s_row>(a, st, tm, tk);
     if constexpr (COL && FLUSH != 0)
-        nv_flush_q<P::q_col, HALF>(a, st, FLUSH == 2 ? tm - 1 : tm, tk, FLUSH);
+        nv_flush_q<P::q_col>(a, st, FLUSH == 2 ? tm - 1 : tm, tk, FLUSH, (a.M & 31) != 0);
     __syncthreads();
 }
 
@@ -408,7 +409,7 @@ __device__ __forceinline__ void nv_step(const Nv4Args &a, const NvLane &l,
 // The global scale of a tensor with amax A: A / (448 * 6), 1 for A = 0.
 __device__ __forceinline__ float nv_global_scale(float A) { return A == 0.0f ? 1.0f : A / 2688.0f; }
 
-template <bool ROW, bool COL, bool HALF, bool TWO_D>
+template <bool ROW, bool COL, bool TWO_D>
 __device__ __forceinline__ void nv_walk(const Nv4Args &a, int rg, int tk)
 {
     using P = NvPolicy<ROW, COL>;
@@ -429,32 +430,32 @@ __device__ __forceinline__ void nv_walk(const Nv4Args &a, int rg, int tk)
     for (; g + 1 < n; g += 2) {
         nv_load<P::x>(a, l, tm0 + g + 1, tk, wb);
         __builtin_amdgcn_sched_barrier(0);
-        nv_step<ROW, COL, HALF, TWO_D, 0>(a, l, wa, st, sg, tm0 + g, tk, g);
+        nv_step<ROW, COL, TWO_D, 0>(a, l, wa, st, sg, tm0 + g, tk, g);
         nv_load<P::x>(a, l, g + 2 < n ? tm0 + g + 2 : past, tk, wa);
         __builtin_amdgcn_sched_barrier(0);
-        nv_step<ROW, COL, HALF, TWO_D, 2>(a, l, wb, st, sg, tm0 + g + 1, tk, g + 1);
+        nv_step<ROW, COL, TWO_D, 2>(a, l, wb, st, sg, tm0 + g + 1, tk, g + 1);
     }
     if (g < n)
-        nv_step<ROW, COL, HALF, TWO_D, 1>(a, l, wa, st, sg, tm0 + g, tk, g);
+        nv_step<ROW, COL, TWO_D, 1>(a, l, wa, st, sg, tm0 + g, tk, g);
     if constexpr (COL)
         nv_flush_s<P::s_col>(a, st, tm0, tk, n);
 }
 
-template <bool ROW, bool COL, bool HALF, bool TWO_D>
+template <bool ROW, bool COL, bool TWO_D>
 __global__ __launch_bounds__(kThreads, 2) void nvfp4_kernel(Nv4Args a)
 {
     const int job = xcd_tile((int)blockIdx.x, (int)gridDim.x);
     const int rg = job / a.tiles_k;
     if (a.sg_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
         *a.sg_out = nv_global_scale(*a.amax);
-    nv_walk<ROW, COL, HALF, TWO_D>(a, rg, job - rg * a.tiles_k);
+    nv_walk<ROW, COL, TWO_D>(a, rg, job - rg * a.tiles_k);
 }
 
 // Grouped: walk rg (numbered across all groups) belongs to the group g with
 // walk0[g] <= rg < walk0[g + 1], quantised as a tensor of its own with its
 // own amax (amax[g]) and global scale.  Workgroup 0 writes every group's
 // global scale (1 for an empty group).
-template <bool ROW, bool COL, bool HALF, bool TWO_D>
+template <bool ROW, bool COL, bool TWO_D>
 __global__ __launch_bounds__(kThreads, 2) void nvfp4_grouped_kernel(Nv4Args a, GroupTable gt)
 {
     const int job = xcd_tile((int)blockIdx.x, (int)gridDim.x);
@@ -478,7 +479,7 @@ __global__ __launch_bounds__(kThreads, 2) void nvfp4_grouped_kernel(Nv4Args a, G
     b.s_col = a.s_col ? a.s_col + a.K * (r0 >> 4) : nullptr;
     b.tiles_m = (int)((b.M + kTileM - 1) / kTileM);
     b.groups_m = gt.walk0[g + 1] - gt.walk0[g];
-    nv_walk<ROW, COL, HALF, TWO_D>(b, rg - gt.walk0[g], tk);
+    nv_walk<ROW, COL, TWO_D>(b, rg - gt.walk0[g], tk);
 }
 
 // ---------------------------------------------------------------------------
@@ -593,53 +594,40 @@ hipError_t launch_absmax_grouped(const uint16_t *x, int64_t K, const GroupTable 
     return hipGetLastError();
 }
 
-// HALF: some tensor (or group) has a row count that is not a multiple of 32.
 template <bool ROW, bool COL, bool TWO_D>
-static hipError_t launch_nv(const Nv4Args &a, const GroupTable *gt, bool half, hipStream_t s)
+static hipError_t launch_nv(const Nv4Args &a, const GroupTable *gt, hipStream_t s)
 {
     const dim3 grid((unsigned)(a.groups_m * a.tiles_k));
-    if (gt) {
-        if (COL && half)
-            hipLaunchKernelGGL((nvfp4_grouped_kernel<ROW, COL, true, TWO_D>), grid, dim3(kThreads),
-                               0, s, a, *gt);
-        else
-            hipLaunchKernelGGL((nvfp4_grouped_kernel<ROW, COL, false, TWO_D>), grid,
-                               dim3(kThreads), 0, s, a, *gt);
-    } else if (COL && half) {
-        hipLaunchKernelGGL((nvfp4_kernel<ROW, COL, true, TWO_D>), grid, dim3(kThreads), 0, s, a);
-    } else {
-        hipLaunchKernelGGL((nvfp4_kernel<ROW, COL, false, TWO_D>), grid, dim3(kThreads), 0, s, a);
-    }
+    if (gt)
+        hipLaunchKernelGGL((nvfp4_grouped_kernel<ROW, COL, TWO_D>), grid, dim3(kThreads), 0, s, a,
+                           *gt);
+    else
+        hipLaunchKernelGGL((nvfp4_kernel<ROW, COL, TWO_D>), grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
 template <bool TWO_D>
-static hipError_t launch_nv_axis(unsigned axis, const Nv4Args &a, const GroupTable *gt, bool half,
+static hipError_t launch_nv_axis(unsigned axis, const Nv4Args &a, const GroupTable *gt,
                                  hipStream_t s)
 {
     switch (axis) {
-    case 1u: return launch_nv<true, false, TWO_D>(a, gt, half, s);
-    case 2u: return launch_nv<false, true, TWO_D>(a, gt, half, s);
-    case 3u: return launch_nv<true, true, TWO_D>(a, gt, half, s);
+    case 1u: return launch_nv<true, false, TWO_D>(a, gt, s);
+    case 2u: return launch_nv<false, true, TWO_D>(a, gt, s);
+    case 3u: return launch_nv<true, true, TWO_D>(a, gt, s);
     default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_nvfp4(unsigned axis, bool two_d, const Nv4Args &a, hipStream_t s)
 {
-    const bool half = (a.M & 31) != 0;
-    return two_d ? launch_nv_axis<true>(axis, a, nullptr, half, s)
-                 : launch_nv_axis<false>(axis, a, nullptr, half, s);
+    return two_d ? launch_nv_axis<true>(axis, a, nullptr, s)
+                 : launch_nv_axis<false>(axis, a, nullptr, s);
 }
 
 hipError_t launch_nvfp4_grouped(unsigned axis, bool two_d, const Nv4Args &a, const GroupTable &gt,
                                 hipStream_t s)
 {
-    bool half = false;
-    for (int g = 0; g < gt.count; g++)
-        half = half || ((gt.row0[g + 1] - gt.row0[g]) & 31) != 0;
-    return two_d ? launch_nv_axis<true>(axis, a, &gt, half, s)
-                 : launch_nv_axis<false>(axis, a, &gt, half, s);
+    return two_d ? launch_nv_axis<true>(axis, a, &gt, s) : launch_nv_axis<false>(axis, a, &gt, s);
 }
 
 }  // namespace mxk

@@ -26,13 +26,16 @@ sys.path.insert(0, HERE)
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
 
-KERNEL_SOURCES = ["block_scaled_precision_bf16_amd/csrc/mx_cast.h",
-                  "block_scaled_precision_bf16_amd/csrc/mx_cast_fmt_e4m3.hip",
-                  "block_scaled_precision_bf16_amd/csrc/mx_cast.hip",
-                  "block_scaled_precision_bf16_amd/csrc/nvfp4.hip",
+# What the metric kernel is built from: its translation unit, the headers it
+# includes, and the host code that picks its launch shape.  The stored HBM
+# traffic is valid only while their hash matches the one it was taken with.
+KERNEL_SOURCES = ["block_scaled_precision_bf16_amd/csrc/mx_cast_fmt_e4m3.hip",
+                  "block_scaled_precision_bf16_amd/csrc/mx_cast.h",
+                  "block_scaled_precision_bf16_amd/csrc/stage_flush.h",
                   "block_scaled_precision_bf16_amd/csrc/device_math.h",
                   "block_scaled_precision_bf16_amd/csrc/launch.h",
-                  "block_scaled_precision_bf16_amd/csrc/bufio.h"]
+                  "block_scaled_precision_bf16_amd/csrc/bufio.h",
+                  "block_scaled_precision_bf16_amd/csrc/api.cpp"]
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic_mx_cast_dim0_dim1_16384.md")
 
 

@@ -77,12 +77,13 @@ __device__ __forceinline__ uint32_t encode8_fp4(const uint32_t (&w)[4], float in
     o = e2m1x2<1>(bf16_lo(w[1]) * inv, bf16_hi(w[1]) * inv, o);
     o = e2m1x2<2>(bf16_lo(w[2]) * inv, bf16_hi(w[2]) * inv, o);
     o = e2m1x2<3>(bf16_lo(w[3]) * inv, bf16_hi(w[3]) * inv, o);
-    if (__builtin_isinf(inv)) {
+    const bool inf = __builtin_isinf(inv);
+    if (__builtin_amdgcn_ballot_w64(inf) != 0) {   // uniform: no lane's exec mask changes
         uint32_t clear = 0;
 #pragma unroll
         for (int d = 0; d < 4; d++)
             clear |= (zero_or_nan_nibble(w[d]) << (8 * d)) | (zero_or_nan_nibble(w[d] >> 16) << (8 * d + 4));
-        o &= ~clear;
+        o &= inf ? ~clear : ~0u;
     }
     return o;
 }
@@ -99,12 +100,13 @@ __device__ __forceinline__ uint32_t encode8_fp4_col(const uint32_t (&w)[kRowsPer
     o = e2m1x2<1>(v(2), v(3), o);
     o = e2m1x2<2>(v(4), v(5), o);
     o = e2m1x2<3>(v(6), v(7), o);
-    if (__builtin_isinf(inv)) {
+    const bool inf = __builtin_isinf(inv);
+    if (__builtin_amdgcn_ballot_w64(inf) != 0) {
         uint32_t clear = 0;
 #pragma unroll
         for (int i = 0; i < 8; i++)
             clear |= zero_or_nan_nibble(h(i)) << (4 * i);
-        o &= ~clear;
+        o &= inf ? ~clear : ~0u;
     }
     return o;
 }

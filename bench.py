@@ -73,6 +73,7 @@ CONFIGS = {
     "mxfp8_tiled_dim0_dim1_16384": ("c2_dim1_16384", (16384, 16384), "mx", 3),
     "mxfp8_grouped_8x_16384x7168": ("f4_grouped_moe", (16384, 7168), "mx_grouped", 3),
     "nvfp4_grouped_8x_16384x7168": ("f4_grouped_moe", (16384, 7168), "nvfp4_grouped", 3),
+    "mxfp8_grouped_swiglu_8x_16384x4096": ("f4_grouped_moe", (16384, 4096), "mx_grouped_swiglu", 3),
 }
 
 # Row counts of the 8 experts in the grouped workloads.
@@ -155,7 +156,7 @@ def main():
 
     key, (M, K), kind, dirs = CONFIGS[args.config]
     print(f"[bench] generating {args.config} inputs {M}x{K}", file=sys.stderr, flush=True)
-    inputs = W.make(key)
+    inputs = W.make(key, M, K) if kind == "mx_grouped_swiglu" else W.make(key)
     if kind in ("mx_gelu", "mx_dgelu", "mx_dsilu"):
         x_h, g_h = inputs
     elif kind.startswith("dgated"):
@@ -175,6 +176,17 @@ def main():
         alg_bytes = 2 * M * K + (M * K + M * nbk) + (M * K + sum(K * -(-m // 32) for m in grp_rows))
         desc = dict(workload=args.config, M=M, K=K, groups=grp_rows, block=32,
                     directions="row+col per group", format="mxfp8 e4m3 + e8m0")
+    elif kind == "mx_grouped_swiglu":
+        # an MoE layer's expert FFN input [gate | linear] (N = K / 2 per half)
+        grp_rows = W.moe_group_rows(M, **MOE_GROUPS)
+        out = mx.mx_quantize_gated_grouped(x, grp_rows, mx.GATED_SWIGLU)
+        step = lambda: mx.mx_quantize_gated_grouped(x, grp_rows, mx.GATED_SWIGLU, out=out)
+        N = K // 2
+        nbn = -(-N // 32)
+        alg_bytes = 2 * M * K + (M * N + M * nbn) + (M * N + sum(N * -(-m // 32) for m in grp_rows))
+        desc = dict(workload=args.config, M=M, K=K, N=N, groups=grp_rows, block=32,
+                    directions="row+col per group", format="mxfp8 e4m3 + e8m0",
+                    activation="swiglu")
     elif kind == "nvfp4_grouped":
         grp_rows = W.moe_group_rows(M, **MOE_GROUPS)
         amax = mx.mx_absmax_bf16_grouped(x, grp_rows)
@@ -304,6 +316,9 @@ def main():
             sb = alg_bytes
         elif kind == "nvfp4_grouped":
             O.nvfp4_quantize_transpose_grouped(xs, W.moe_group_rows(M, **MOE_GROUPS))
+            sb = alg_bytes
+        elif kind == "mx_grouped_swiglu":
+            O.mx_quantize_gated_grouped(xs, W.moe_group_rows(M, **MOE_GROUPS), mx.GATED_SWIGLU)
             sb = alg_bytes
         elif kind.startswith("nvfp4"):
             O.nvfp4_quantize_transpose(xs, tensor_amax=O.absmax(x_h), two_d=kind == "nvfp4_2d")

@@ -9,6 +9,9 @@ these sizes in seconds with OpenMP over rows / columns).
 and the backward casts at the same sizes as their forward ones:
   8192^2 N(0, 2) with grad N(0, 1): dSiLU(x) * grad + dbias
   grad 8192 x 4096 with [gate | linear] 8192 x 8192: dSwiGLU and dGeGLU
+and the grouped workloads: eight experts' rows (1104, 3008, 1072, 6560, 1632,
+608, 2256, 144) of 16384 x 7168 N(0, 1) tokens cast as MXFP8 and as NVFP4,
+and of a 16384 x 4096 [gate | linear] input through grouped SwiGLU.
 """
 import os
 
@@ -130,3 +133,35 @@ def test_nvfp4_maximum_dimensions(M, K):
     torch.cuda.synchronize()
     o = O.nvfp4_quantize_transpose(x)
     mx_outputs_equal(g, o, f"nvfp4 max dims {M}x{K}")
+
+
+@pytest.fixture(scope="module")
+def moe_rows():
+    return W.moe_group_rows(16384, groups=8, seed=8)
+
+
+def test_grouped_mxfp8_8x_16384x7168(moe_rows):
+    x = W.make("f4_grouped_moe")
+    g = mx.mx_quantize_grouped(to_dev(x), moe_rows)
+    torch.cuda.synchronize()
+    mx_outputs_equal(g, O.mx_quantize_grouped(x, moe_rows), "grouped mxfp8 8 experts")
+
+
+@pytest.mark.parametrize("two_d", [False, True])
+def test_grouped_nvfp4_8x_16384x7168(moe_rows, two_d):
+    x = W.make("f4_grouped_moe")
+    xd = to_dev(x)
+    amax = mx.mx_absmax_bf16_grouped(xd, moe_rows)
+    g = mx.nvfp4_quantize_transpose_grouped(xd, moe_rows, amax, two_d=two_d)
+    torch.cuda.synchronize()
+    o = O.nvfp4_quantize_transpose_grouped(x, moe_rows, two_d=two_d)
+    mx_outputs_equal(g, o, f"grouped nvfp4 8 experts two_d={two_d}")
+    assert np.array_equal(g["sg"].cpu().numpy(), o["sg"])
+
+
+def test_grouped_swiglu_8x_16384x4096(moe_rows):
+    x = W.make("f4_grouped_moe", 16384, 4096)
+    g = mx.mx_quantize_gated_grouped(to_dev(x), moe_rows, mx.GATED_SWIGLU)
+    torch.cuda.synchronize()
+    o = O.mx_quantize_gated_grouped(x, moe_rows, mx.GATED_SWIGLU)
+    mx_outputs_equal(g, o, "grouped swiglu 8 experts")

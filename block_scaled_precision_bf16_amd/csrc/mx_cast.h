@@ -50,18 +50,20 @@ __device__ __forceinline__ float half_value(uint32_t w, int hi)
     return hi ? bf16_hi(w) : bf16_lo(w);
 }
 
-// Cache policy of each stream, chosen by measurement on the 16384 x 16384
-// cast: the input is read once, so its loads are non-temporal, and the
-// row-wise elements are written with the SC1 bit.  With both outputs the
-// transposed tile (lines and scales) is written non-temporal as well; the
-// row scales keep the default policy (non-temporal row scales, 8-byte pieces
-// of lines that other workgroups complete, cost ~15%).  The transposed output
-// alone keeps the default policy (non-temporal: 26% slower).  The policies
-// change timing only, never results.
+// Cache policy of each stream, chosen by measurement (the 16384 x 16384 plain
+// casts, the 8192 x 8192 fused ones).  The input is read once, so its loads
+// are non-temporal, also for the dGELU and dSiLU casts, which read the grad
+// stream beside it (2-3% faster there; slower for GELU and the gated casts).
+// The row-wise elements of the plain casts are written with the SC1 bit.
+// With both outputs the transposed tile (lines and scales) is written
+// non-temporal as well; the row scales keep the default policy (non-temporal
+// row scales, 8-byte pieces of lines that other workgroups complete, cost
+// ~15%), and so does the transposed output alone (non-temporal: 26% slower).
+// The policies change timing only, never results.
 template <int OP, bool ROW, bool COL>
 struct Policy {
     static constexpr bool plain = OP == OP_PLAIN, both = plain && ROW && COL;
-    static constexpr int x = plain ? kNT : 0;            // input loads
+    static constexpr int x = plain || OP == OP_DGELU || OP == OP_DSILU ? kNT : 0;   // input loads
     static constexpr int q_row = plain ? kSC1 : 0;       // row-wise stores
     static constexpr int s_row = 0;
     static constexpr int q_col = both ? kNT : 0;         // transposed stores

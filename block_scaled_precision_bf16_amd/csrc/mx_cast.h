@@ -52,8 +52,9 @@ __device__ __forceinline__ float half_value(uint32_t w, int hi)
 
 // Cache policy of each stream, chosen by measurement (the 16384 x 16384 plain
 // casts, the 8192 x 8192 fused ones).  The input is read once, so its loads
-// are non-temporal, also for the dGELU and dSiLU casts, which read the grad
-// stream beside it (2-3% faster there; slower for GELU and the gated casts).
+// are non-temporal, also for the dGELU, dSiLU and dSwiGLU casts, which read a
+// grad stream beside it (3-5% faster there; 3-10% slower for GELU, dGeGLU and
+// the forward gated casts).
 // The row-wise elements of the plain casts are written with the SC1 bit.
 // With both outputs the transposed tile (lines and scales) is written
 // non-temporal as well; the row scales keep the default policy (non-temporal
@@ -63,7 +64,8 @@ __device__ __forceinline__ float half_value(uint32_t w, int hi)
 template <int OP, bool ROW, bool COL>
 struct Policy {
     static constexpr bool plain = OP == OP_PLAIN, both = plain && ROW && COL;
-    static constexpr int x = plain || OP == OP_DGELU || OP == OP_DSILU ? kNT : 0;   // input loads
+    static constexpr int x =                              // input (and grad) loads
+        plain || OP == OP_DGELU || OP == OP_DSILU || OP == OP_DSWIGLU ? kNT : 0;
     static constexpr int q_row = plain ? kSC1 : 0;       // row-wise stores
     static constexpr int s_row = 0;
     static constexpr int q_col = both ? kNT : 0;         // transposed stores

@@ -9,9 +9,8 @@ with inverse scale" page ("Performance" section): GB/s = algorithmic bytes
 read + written / kernel time, where the bytes are 2 per input element plus,
 per direction, 1 per E4M3 element and 1 per 32-element E8M0 scale.
 
-Prints ONE JSON line.  `--config` times one of the other workloads instead
-(for the design notes); `--copy` runs the plain device copy used to calibrate
-the HBM byte counters.
+Prints ONE JSON line.  `--config` times one of the other workloads instead;
+`--copy` runs the plain device copy used to calibrate the HBM byte counters.
 """
 import argparse
 import hashlib
@@ -131,8 +130,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the cast shards by rows with no exchange; see the design notes)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(the cast shards by rows with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

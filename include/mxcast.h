@@ -80,7 +80,7 @@ typedef enum mx_status {
     MX_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required     */
     MX_ERR_ALIAS = 6,       /* an output overlaps an input or another output  */
     MX_ERR_HIP = 7,         /* the HIP runtime reported a launch error        */
-    MX_ERR_UNSUPPORTED = 8  /* valid request this build does not implement    */
+    MX_ERR_UNSUPPORTED = 8  /* valid request this version does not implement  */
 } mx_status;
 
 /* axis_mask bits */

@@ -23,7 +23,7 @@
  * MXFP8 / NVFP4 cast kernels and their fusions (tables "MXFP8 generic quantize
  * kernel", "MXFP8 gated (swiglu / geglu) kernel", "NVFP4 2D quantize-transpose
  * kernel") but never define the arithmetic.  The rules below are the readings
- * recorded in the design notes:
+ * this oracle implements:
  *   R1  E8M0 shared exponent = floor(log2(amax)) - 8 (8 = exponent of the
  *       largest E4M3 binade), biased by 127 and clamped to [0, 254].
  *   R2  element = E4M3(x / 2^(byte-127)), round to nearest, ties to the even

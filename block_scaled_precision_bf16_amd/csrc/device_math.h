@@ -274,6 +274,13 @@ constexpr float K_SQRT_2_OVER_PI = 0.797884560802865355879892119868763737f;
 constexpr float K_CUBIC = 0.044715f;
 constexpr float K_CUBIC3 = 0.134145f;
 constexpr float K_2SQRT_2_OVER_PI = 1.59576912160573071175978423973752747f;
+static_assert(K_2SQRT_2_OVER_PI == 2.0f * K_SQRT_2_OVER_PI, "the doubled constant is exact");
+
+// 2u for u = fl32(sqrt(2/pi) * inner), as one multiply: fl32(2 sqrt(2/pi) *
+// inner) equals fl32(u + u) because doubling commutes with rounding, except
+// where u is subnormal -- and there both give sigma = 1 - sigma = 1/2, so the
+// activations below come out bit-identical to the u + u form.
+__device__ __forceinline__ float gelu_2u(float inner) { return K_2SQRT_2_OVER_PI * inner; }
 
 // tanh-form GELU: x * sigma(2u), u = sqrt(2/pi)(x + 0.044715 x^3); this equals
 // 0.5 x (1 + tanh u).
@@ -282,9 +289,8 @@ __device__ __forceinline__ float gelu32(float x)
     float x2 = x * x;
     float x3 = x2 * x;
     float inner = __builtin_fmaf(K_CUBIC, x3, x);
-    float u = K_SQRT_2_OVER_PI * inner;
     float s, sc;
-    sigmoid_pair(u + u, s, sc);
+    sigmoid_pair(gelu_2u(inner), s, sc);
     return x * s;
 }
 
@@ -296,9 +302,8 @@ __device__ __forceinline__ float dgelu32(float x)
     float x2 = x * x;
     float x3 = x2 * x;
     float inner = __builtin_fmaf(K_CUBIC, x3, x);
-    float u = K_SQRT_2_OVER_PI * inner;
     float s, sc;
-    sigmoid_pair(u + u, s, sc);
+    sigmoid_pair(gelu_2u(inner), s, sc);
     float ss = s * sc;
     float du = K_2SQRT_2_OVER_PI * __builtin_fmaf(K_CUBIC3, x2, 1.0f);
     float t = ss == 0.0f ? 0.0f : (x * ss) * du;
@@ -340,8 +345,7 @@ __device__ __forceinline__ float dgated_value(float gate, float grad, float lin,
         float x2 = gate * gate;
         float x3 = x2 * gate;
         float inner = __builtin_fmaf(K_CUBIC, x3, gate);
-        float u = K_SQRT_2_OVER_PI * inner;
-        sigmoid_pair(u + u, s, sc);
+        sigmoid_pair(gelu_2u(inner), s, sc);
         a = gate * s;
         float ss = s * sc;
         float du = K_2SQRT_2_OVER_PI * __builtin_fmaf(K_CUBIC3, x2, 1.0f);

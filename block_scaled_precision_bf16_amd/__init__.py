@@ -145,8 +145,78 @@ def _check(status, where):
         raise MxError(status, where)
 
 
-def _u8(shape, dev):
-    return torch.empty(shape, dtype=torch.uint8, device=dev)
+def _2d(t, name):
+    """A bf16-bits input that must be a contiguous 2-D tensor."""
+    t = _bf16_bits(t)
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    return t
+
+
+def _half_width(W, name):
+    """N of a gated row [gate | linear] of W elements (W must be even)."""
+    if W % 2:
+        raise ValueError(f"{name}: a [gate | linear] row has an even number of columns, got {W}")
+    return W // 2
+
+
+def _want_shape(t, shape, name):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _group_total(group_rows, M):
+    if any(int(r) < 0 for r in group_rows):
+        raise ValueError("group row counts must be non-negative")
+    if sum(int(r) for r in group_rows) != M:
+        raise ValueError(f"group row counts sum to {sum(int(r) for r in group_rows)}, "
+                         f"but the input has {M} rows")
+
+
+def _outputs(o, need, dev):
+    """Allocate the outputs the caller did not pass and check those it did.
+    need maps name -> (shape, dtype).  A passed tensor must be a contiguous
+    tensor of that dtype on the input's device with exactly as many elements
+    as the library writes."""
+    o = dict(o or {})
+    for k, (shape, dtype) in need.items():
+        t = o.get(k)
+        if t is None:
+            o[k] = torch.empty(shape, dtype=dtype, device=dev)
+            continue
+        numel = 1
+        for d in shape:
+            numel *= int(d)
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"out[{k!r}] must be a tensor")
+        if t.dtype != dtype or t.numel() != numel or not t.is_contiguous() or t.device != dev:
+            raise ValueError(f"out[{k!r}] must be a contiguous {dtype} tensor of {numel} elements "
+                             f"on {dev}; got {t.dtype}, {t.numel()} elements on {t.device}"
+                             f"{'' if t.is_contiguous() else ', not contiguous'}")
+    return o
+
+
+def _on_device(dev, *tensors):
+    """Every tensor the library reads or writes lives on one ROCm device (a
+    host pointer handed to a kernel would fault the GPU)."""
+    if dev.type != "cuda":
+        raise ValueError(f"tensors must be on a ROCm (cuda) device, got {dev}")
+    for t in tensors:
+        if t is not None and t.device != dev:
+            raise ValueError(f"all tensors must be on {dev}; got one on {t.device}")
+
+
+def _f32_vec(t, n, name, dev):
+    """A float32 device vector of n elements (amax, global scales)."""
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.numel() != n \
+            or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor of {n} elements")
+    if t.device != dev:
+        raise ValueError(f"{name} must be on {dev}, got {t.device}")
+    return t
+
+
+U8, F32, I16 = torch.uint8, torch.float32, torch.int16
 
 
 def mx_quantize_workspace_size(M: int, K: int, axis: int = ROWWISE | COLWISE,
@@ -158,37 +228,54 @@ def mx_scale_size(rows: int, cols: int, axis: int = ROWWISE | COLWISE) -> int:
     return lib().mx_scale_size(rows, cols, axis)
 
 
-def _scales(rows, cols, axis, dev):
+def _scale_shape(rows, cols, axis):
     """One direction's scale tensor: [rows][ceil(cols/32)], or flat in the tile
     layout."""
     if axis & SCALE_TILED:
-        return _u8((mx_scale_size(rows, cols, axis),), dev)
-    return _u8((rows, -(-cols // 32)), dev)
+        return (max(1, mx_scale_size(rows, cols, axis)),)
+    return (rows, -(-cols // 32))
+
+
+def _mx_need(M, K, axis):
+    """Outputs of an MXFP8 cast of a quantised [M][K] tensor."""
+    need = {}
+    if axis & ROWWISE:
+        need["q_row"] = ((M, K), U8)
+        need["s_row"] = (_scale_shape(M, K, axis), U8)
+    if axis & COLWISE:
+        need["q_col"] = ((K, M), U8)
+        need["s_col"] = (_scale_shape(K, M, axis), U8)
+    return need
+
+
+def _workspace(workspace, need_bytes, dev):
+    if workspace is None:
+        return torch.empty(max(need_bytes, 16), dtype=U8, device=dev)
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_contiguous() \
+            or workspace.device != dev:
+        raise ValueError(f"workspace must be a contiguous tensor on {dev}")
+    return workspace
 
 
 def mx_quantize(x, grad=None, axis=ROWWISE | COLWISE, fusion=FUSE_NONE, out=None,
                 workspace=None, stream=None):
     """MXFP8 cast of x[M][K].  Returns {q_row, s_row, q_col, s_col, dbias}
     (None where not requested).  `out` may hold preallocated outputs and
-    `workspace` a preallocated uint8 buffer (needed only with FUSE_DBIAS)."""
-    x = _bf16_bits(x)
-    grad = _bf16_bits(grad) if (fusion & 0xF) in (FUSE_DGELU, FUSE_DSILU) else None
+    `workspace` a preallocated device buffer (needed only with FUSE_DBIAS)."""
+    x = _2d(x, "x")
     M, K = x.shape
+    grad = _2d(grad, "grad") if (fusion & 0xF) in (FUSE_DGELU, FUSE_DSILU) else None
+    _want_shape(grad, (M, K), "grad")
     dev = x.device
-    o = dict(out or {})
-    if axis & ROWWISE:
-        o.setdefault("q_row", _u8((M, K), dev))
-        o.setdefault("s_row", _scales(M, K, axis, dev))
-    if axis & COLWISE:
-        o.setdefault("q_col", _u8((K, M), dev))
-        o.setdefault("s_col", _scales(K, M, axis, dev))
+    need = _mx_need(M, K, axis)
+    if fusion & FUSE_DBIAS:
+        need["dbias"] = ((K,), F32)
+    o = _outputs(out, need, dev)
     ws_bytes = 0
     if fusion & FUSE_DBIAS:
-        o.setdefault("dbias", torch.empty(K, dtype=torch.float32, device=dev))
-        ws_bytes = mx_quantize_workspace_size(M, K, axis, fusion)
-        if workspace is None:
-            workspace = _u8((max(ws_bytes, 16),), dev)
+        workspace = _workspace(workspace, mx_quantize_workspace_size(M, K, axis, fusion), dev)
         ws_bytes = workspace.numel() * workspace.element_size()
+    _on_device(dev, grad, *o.values(), workspace if fusion & FUSE_DBIAS else None)
     st = lib().mx_quantize(_ptr(x), _ptr(grad), M, K, axis, fusion,
                            _ptr(o.get("q_row")), _ptr(o.get("s_row")), _ptr(o.get("q_col")),
                            _ptr(o.get("s_col")), _ptr(o.get("dbias")),
@@ -216,30 +303,40 @@ def mx_grouped_scale_size(K: int, group_rows, axis: int, colwise: bool) -> int:
                                        int(colwise))
 
 
+def _grouped_need(M, W, group_rows, axis):
+    """Outputs of a grouped MXFP8 cast of quantised [rows][W] groups."""
+    need = {}
+    if axis & ROWWISE:
+        need["q_row"] = ((M, W), U8)
+        need["s_row"] = ((max(1, mx_grouped_scale_size(W, group_rows, axis, False)),), U8)
+    if axis & COLWISE:
+        need["q_col"] = ((M * W,), U8)
+        need["s_col"] = ((max(1, mx_grouped_scale_size(W, group_rows, axis, True)),), U8)
+    return need
+
+
 def mx_quantize_grouped(x, group_rows, grad=None, axis=ROWWISE | COLWISE, fusion=FUSE_NONE,
                         out=None, workspace=None, stream=None):
     """Grouped MXFP8 cast of x[M][K] = len(group_rows) tensors stacked along
     rows.  Returns q_row [M][K], flat s_row / q_col / s_col holding the groups'
     outputs one after the other, and dbias [G][K] (None where not requested)."""
-    x = _bf16_bits(x)
-    grad = _bf16_bits(grad) if (fusion & 0xF) in (FUSE_DGELU, FUSE_DSILU) else None
+    x = _2d(x, "x")
     M, K = x.shape
+    _group_total(group_rows, M)
+    grad = _2d(grad, "grad") if (fusion & 0xF) in (FUSE_DGELU, FUSE_DSILU) else None
+    _want_shape(grad, (M, K), "grad")
     G = len(group_rows)
     dev = x.device
-    o = dict(out or {})
-    if axis & ROWWISE:
-        o.setdefault("q_row", _u8((M, K), dev))
-        o.setdefault("s_row", _u8((max(1, mx_grouped_scale_size(K, group_rows, axis, False)),), dev))
-    if axis & COLWISE:
-        o.setdefault("q_col", _u8((M * K,), dev))
-        o.setdefault("s_col", _u8((max(1, mx_grouped_scale_size(K, group_rows, axis, True)),), dev))
+    need = _grouped_need(M, K, group_rows, axis)
+    if fusion & FUSE_DBIAS:
+        need["dbias"] = ((G, K), F32)
+    o = _outputs(out, need, dev)
     ws_bytes = 0
     if fusion & FUSE_DBIAS:
-        o.setdefault("dbias", torch.empty((G, K), dtype=torch.float32, device=dev))
-        ws_bytes = mx_quantize_grouped_workspace_size(K, group_rows, axis, fusion)
-        if workspace is None:
-            workspace = _u8((max(ws_bytes, 16),), dev)
+        workspace = _workspace(workspace,
+                               mx_quantize_grouped_workspace_size(K, group_rows, axis, fusion), dev)
         ws_bytes = workspace.numel() * workspace.element_size()
+    _on_device(dev, grad, *o.values(), workspace if fusion & FUSE_DBIAS else None)
     rows = _rows_arg(group_rows)
     st = lib().mx_quantize_grouped(_ptr(x), _ptr(grad), K, ctypes.cast(rows, _vp), G, axis, fusion,
                                    _ptr(o.get("q_row")), _ptr(o.get("s_row")),
@@ -253,17 +350,12 @@ def mx_quantize_grouped(x, group_rows, grad=None, axis=ROWWISE | COLWISE, fusion
 
 def mx_quantize_gated(x, act, axis=ROWWISE | COLWISE, out=None, stream=None):
     """Gated MXFP8 cast of x[M][2N] = [gate | linear] -> y[M][N] = act(gate)*linear."""
-    x = _bf16_bits(x)
+    x = _2d(x, "x")
     M, N2 = x.shape
-    N = N2 // 2
+    N = _half_width(N2, "mx_quantize_gated")
     dev = x.device
-    o = dict(out or {})
-    if axis & ROWWISE:
-        o.setdefault("q_row", _u8((M, N), dev))
-        o.setdefault("s_row", _scales(M, N, axis, dev))
-    if axis & COLWISE:
-        o.setdefault("q_col", _u8((N, M), dev))
-        o.setdefault("s_col", _scales(N, M, axis, dev))
+    o = _outputs(out, _mx_need(M, N, axis), dev)
+    _on_device(dev, *o.values())
     st = lib().mx_quantize_gated(_ptr(x), M, N, axis, act, _ptr(o.get("q_row")),
                                  _ptr(o.get("s_row")), _ptr(o.get("q_col")),
                                  _ptr(o.get("s_col")), _stream(dev, stream))
@@ -274,18 +366,14 @@ def mx_quantize_gated(x, act, axis=ROWWISE | COLWISE, out=None, stream=None):
 def mx_quantize_dgated(grad, x, act, axis=ROWWISE | COLWISE, out=None, stream=None):
     """Gated backward MXFP8 cast: grad[M][N], x[M][2N] = [gate | linear] ->
     quantised dx[M][2N] = [d_gate | d_linear]."""
-    grad = _bf16_bits(grad)
-    x = _bf16_bits(x)
+    grad = _2d(grad, "grad")
+    x = _2d(x, "x")
     M, N2 = x.shape
-    N = N2 // 2
+    N = _half_width(N2, "mx_quantize_dgated")
+    _want_shape(grad, (M, N), "grad")
     dev = x.device
-    o = dict(out or {})
-    if axis & ROWWISE:
-        o.setdefault("q_row", _u8((M, N2), dev))
-        o.setdefault("s_row", _scales(M, N2, axis, dev))
-    if axis & COLWISE:
-        o.setdefault("q_col", _u8((N2, M), dev))
-        o.setdefault("s_col", _scales(N2, M, axis, dev))
+    o = _outputs(out, _mx_need(M, N2, axis), dev)
+    _on_device(dev, grad, *o.values())
     st = lib().mx_quantize_dgated(_ptr(grad), _ptr(x), M, N, axis, act, _ptr(o.get("q_row")),
                                   _ptr(o.get("s_row")), _ptr(o.get("q_col")),
                                   _ptr(o.get("s_col")), _stream(dev, stream))
@@ -297,14 +385,16 @@ def mx_fused_values(x, grad=None, op=FUSE_GELU, out=None, stream=None):
     """The bf16 values the fused casts quantise (returned as int16 bits).
     Gated ops (OP_GATED | act) take x[M][2K] and give [M][K]; gated backward
     ops (OP_DGATED | act) take x[M][2K] and grad[M][K] and give [M][2K]."""
-    x = _bf16_bits(x)
+    x = _2d(x, "x")
     gated = bool(op & (OP_GATED | OP_DGATED))
     M, W = x.shape
-    K = W // 2 if gated else W
+    K = _half_width(W, "mx_fused_values") if gated else W
     dev = x.device
     shape = (M, 2 * K) if op & OP_DGATED else (M, K)
-    y = out if out is not None else torch.empty(shape, dtype=torch.int16, device=dev)
-    g = _bf16_bits(grad) if (op in (FUSE_DGELU, FUSE_DSILU) or op & OP_DGATED) else None
+    g = _2d(grad, "grad") if (op in (FUSE_DGELU, FUSE_DSILU) or op & OP_DGATED) else None
+    _want_shape(g, (M, K), "grad")
+    y = _outputs({"y": out}, {"y": (shape, I16)}, dev)["y"]
+    _on_device(dev, g, y)
     st = lib().mx_fused_values(_ptr(x), _ptr(g), M, K, op, _ptr(y), _stream(dev, stream))
     _check(st, "mx_fused_values")
     return y
@@ -313,10 +403,24 @@ def mx_fused_values(x, grad=None, op=FUSE_GELU, out=None, stream=None):
 def mx_absmax_bf16(x, out=None, stream=None):
     """Tensor absmax as a one-element float32 device tensor."""
     x = _bf16_bits(x)
-    amax = out if out is not None else torch.empty(1, dtype=torch.float32, device=x.device)
-    st = lib().mx_absmax_bf16(_ptr(x), x.numel(), _ptr(amax), _stream(x.device, stream))
+    dev = x.device
+    amax = _outputs({"amax": out}, {"amax": ((1,), F32)}, dev)["amax"]
+    _on_device(dev, amax)
+    st = lib().mx_absmax_bf16(_ptr(x), x.numel(), _ptr(amax), _stream(dev, stream))
     _check(st, "mx_absmax_bf16")
     return amax
+
+
+def _nv_need(M, K, axis, n_sg):
+    need = {}
+    if axis & ROWWISE:
+        need["q_row"] = ((M, K // 2), U8)
+        need["s_row"] = ((M, K // 16), U8)
+    if axis & COLWISE:
+        need["q_col"] = ((K, M // 2), U8)
+        need["s_col"] = ((K, M // 16), U8)
+    need["sg"] = ((n_sg,), F32)
+    return need
 
 
 def nvfp4_quantize_transpose(x, amax=None, axis=ROWWISE | COLWISE, out=None, stream=None,
@@ -324,19 +428,15 @@ def nvfp4_quantize_transpose(x, amax=None, axis=ROWWISE | COLWISE, out=None, str
     """NVFP4 of x[M][K] and its transpose.  amax: one-element float32 device
     tensor (computed with mx_absmax_bf16 when None).  two_d: one scale per
     16 x 16 block.  Returns {q_row, s_row, q_col, s_col, sg}."""
-    x = _bf16_bits(x)
+    x = _2d(x, "x")
     M, K = x.shape
     dev = x.device
+    o = _outputs(out, _nv_need(M, K, axis, 1), dev)
+    if amax is not None:
+        _f32_vec(amax, 1, "amax", dev)
+    _on_device(dev, *o.values())
     if amax is None:
         amax = mx_absmax_bf16(x, stream=stream)
-    o = dict(out or {})
-    if axis & ROWWISE:
-        o.setdefault("q_row", _u8((M, K // 2), dev))
-        o.setdefault("s_row", _u8((M, K // 16), dev))
-    if axis & COLWISE:
-        o.setdefault("q_col", _u8((K, M // 2), dev))
-        o.setdefault("s_col", _u8((K, M // 16), dev))
-    o.setdefault("sg", torch.empty(1, dtype=torch.float32, device=dev))
     fn = lib().nvfp4_quantize_transpose_2d if two_d else lib().nvfp4_quantize_transpose
     st = fn(_ptr(x), M, K, _ptr(amax), axis, _ptr(o.get("q_row")), _ptr(o.get("s_row")),
             _ptr(o.get("q_col")), _ptr(o.get("s_col")), _ptr(o["sg"]), _stream(dev, stream))
@@ -346,13 +446,16 @@ def nvfp4_quantize_transpose(x, amax=None, axis=ROWWISE | COLWISE, out=None, str
 
 def mx_absmax_bf16_grouped(x, group_rows, out=None, stream=None):
     """Per-group max |x| (fp32 [G]) of x[M][K] = len(group_rows) stacked tensors."""
-    x = _bf16_bits(x)
+    x = _2d(x, "x")
     M, K = x.shape
+    _group_total(group_rows, M)
     G = len(group_rows)
-    amax = out if out is not None else torch.empty(G, dtype=torch.float32, device=x.device)
+    dev = x.device
+    amax = _outputs({"amax": out}, {"amax": ((G,), F32)}, dev)["amax"]
+    _on_device(dev, amax)
     rows = _rows_arg(group_rows)
     st = lib().mx_absmax_bf16_grouped(_ptr(x), K, ctypes.cast(rows, _vp), G, _ptr(amax),
-                                      _stream(x.device, stream))
+                                      _stream(dev, stream))
     _check(st, "mx_absmax_bf16_grouped")
     return amax
 
@@ -363,18 +466,18 @@ def nvfp4_quantize_transpose_grouped(x, group_rows, amax, axis=ROWWISE | COLWISE
     own tensor amax (device fp32 [G]).  Returns q_row [M][K/2], s_row
     [M][K/16], flat q_col / s_col (the groups' transposes one after the
     other) and the groups' global scales sg [G]."""
-    x = _bf16_bits(x)
+    x = _2d(x, "x")
     M, K = x.shape
+    _group_total(group_rows, M)
     G = len(group_rows)
     dev = x.device
-    o = dict(out or {})
-    if axis & ROWWISE:
-        o.setdefault("q_row", _u8((M, K // 2), dev))
-        o.setdefault("s_row", _u8((M, K // 16), dev))
-    if axis & COLWISE:
-        o.setdefault("q_col", _u8((M * K // 2,), dev))
-        o.setdefault("s_col", _u8((M * K // 16,), dev))
-    o.setdefault("sg", torch.empty(G, dtype=torch.float32, device=dev))
+    need = _nv_need(M, K, axis, G)
+    for k in ("q_col", "s_col"):
+        if k in need:
+            need[k] = ((M * K // (2 if k == "q_col" else 16),), U8)
+    o = _outputs(out, need, dev)
+    _f32_vec(amax, G, "amax", dev)
+    _on_device(dev, *o.values())
     rows = _rows_arg(group_rows)
     st = lib().nvfp4_quantize_transpose_grouped(_ptr(x), K, ctypes.cast(rows, _vp), G, _ptr(amax),
                                                 int(two_d), axis, _ptr(o.get("q_row")),
@@ -390,26 +493,24 @@ def mx_quantize_gated_grouped(x, group_rows, act, grad=None, axis=ROWWISE | COLW
     """Grouped gated MXFP8 cast of x[M][2N] = [gate | linear] stacked by group
     (with grad [M][N]: the gated backward).  q_row [M][W] (W = N, or 2N
     backward) and flat s_row / q_col / s_col, the groups one after the other."""
-    x = _bf16_bits(x)
+    x = _2d(x, "x")
     M, N2 = x.shape
-    N = N2 // 2
+    N = _half_width(N2, "mx_quantize_gated_grouped")
+    _group_total(group_rows, M)
+    if grad is not None:
+        grad = _2d(grad, "grad")
+        _want_shape(grad, (M, N), "grad")
     W = N2 if grad is not None else N
     G = len(group_rows)
     dev = x.device
-    o = dict(out or {})
-    if axis & ROWWISE:
-        o.setdefault("q_row", _u8((M, W), dev))
-        o.setdefault("s_row", _u8((max(1, mx_grouped_scale_size(W, group_rows, axis, False)),), dev))
-    if axis & COLWISE:
-        o.setdefault("q_col", _u8((M * W,), dev))
-        o.setdefault("s_col", _u8((max(1, mx_grouped_scale_size(W, group_rows, axis, True)),), dev))
+    o = _outputs(out, _grouped_need(M, W, group_rows, axis), dev)
+    _on_device(dev, grad, *o.values())
     rows = _rows_arg(group_rows)
     ptrs = (_ptr(o.get("q_row")), _ptr(o.get("s_row")), _ptr(o.get("q_col")), _ptr(o.get("s_col")))
     if grad is None:
         st = lib().mx_quantize_gated_grouped(_ptr(x), N, ctypes.cast(rows, _vp), G, axis, act,
                                              *ptrs, _stream(dev, stream))
     else:
-        grad = _bf16_bits(grad)
         st = lib().mx_quantize_dgated_grouped(_ptr(grad), _ptr(x), N, ctypes.cast(rows, _vp), G,
                                               axis, act, *ptrs, _stream(dev, stream))
     _check(st, "mx_quantize_gated_grouped")

@@ -160,15 +160,20 @@ __device__ __forceinline__ void load_tile(const MxArgs &a, const LaneAt &l, int 
         const int64_t m0 = (int64_t)tm * kTileM;
         const rsrc_t rx = make_rsrc(a.x, 2 * m0 * a.ldx, 2 * a.M * a.ldx);
         const rsrc_t rg = make_rsrc(a.aux, 2 * m0 * a.ldg, 2 * a.M * a.ldg);
+        // the linear half gets a descriptor of its own, based at column N of
+        // the sub-tile's first row, and the gate's offsets: added to the
+        // offset instead, the 2N bytes would take the last row's loads past
+        // 2^31 - 1 (the largest descriptor) at 2N = 2^23
+        const rsrc_t rl = make_rsrc(a.x, 2 * (m0 * a.ldx + N), 2 * a.M * a.ldx);
         const uint32_t sx = (uint32_t)(2 * a.ldx), sg = (uint32_t)(2 * a.ldg);
         const uint32_t ox = live ? (uint32_t)l.row * sx + 2 * n : kDead;
         const uint32_t og = live ? (uint32_t)l.row * sg + 2 * n : kDead;
-        const uint32_t ol = live && gate_half ? ox + (uint32_t)(2 * N) : kDead;
+        const uint32_t ol = live && gate_half ? ox : kDead;
 #pragma unroll
         for (int r = 0; r < kRowsPerLane; r++) {
             const uint4 g = buf_load16<XA>(rx, ox + r * sx);
             const uint4 dy = buf_load16<XA>(rg, og + r * sg);
-            const uint4 li = buf_load16<XA>(rx, ol + r * sx);
+            const uint4 li = buf_load16<XA>(rl, ol + r * sx);
             w[r][0] = dgated_pair<OP>(g.x, dy.x, li.x, gate_half);
             w[r][1] = dgated_pair<OP>(g.y, dy.y, li.y, gate_half);
             w[r][2] = dgated_pair<OP>(g.z, dy.z, li.z, gate_half);

@@ -116,8 +116,11 @@ def test_c1_special_256x512():
 @pytest.mark.parametrize("M,K", [(1 << 23, 32), (32, 1 << 23), ((1 << 23) - 16, 40)])
 @pytest.mark.parametrize("layout", [0, mx.SCALE_TILED], ids=["compact", "tiled"])
 def test_mxfp8_maximum_dimensions(M, K, layout):
-    """The largest row count and row length the library accepts (2^23): the
-    in-tile byte offsets of the loads reach 127 * 2^24, just below 2^31."""
+    """The largest row count (2^23 rows of 32 or 40 columns: the most
+    sub-tiles along M, and a transposed output with rows of 2^23 bytes) and
+    the largest row length (32 rows of 2^23 columns: in-tile load offsets up
+    to 31 * 2^24).  Offsets up to 127 * 2^24, just below 2^31, are reached by
+    the 128-row casts of test_gpu_limits.py."""
     x = W.loguniform_rows(M, K, seed=90)
     g = mx.mx_quantize(to_dev(x), axis=3 | layout)
     torch.cuda.synchronize()

@@ -1,0 +1,379 @@
+"""Host model of the cast kernels' buffer addressing at the sizes the ABI
+accepts (pure CPU; no GPU, no library call).
+
+Every global access of the cast kernels goes through a buffer descriptor
+(`make_rsrc` in csrc/bufio.h): a base shifted by a 64-bit byte offset and a
+size capped at 2^31 - 1, plus a 32-bit per-lane byte offset.  A lane that must
+not touch memory gets the offset 2^31 ("dead"), or its access lies past the
+descriptor's size, and the hardware then drops the access.  That scheme is
+only sound if
+
+  (a) every live access lies wholly inside its descriptor:
+      offset + bytes <= size, and
+  (b) every masked access (a dead lane, a row past M, a column past K) lies
+      wholly outside it: offset >= size, without the 32-bit offset wrapping.
+
+This file restates, site by site, the offset arithmetic of mx_cast.h and
+nvfp4.hip (load_tile, row_pass, col_flush_q, srow_flush, col_flush_s[_tiled],
+flush_scale_rows, nv_load, the NVFP4 row store, nv_flush_q, nv_flush_s,
+nv_flush_srow) and checks (a) and (b) for every lane of the first and last
+sub-tile of the first and last walk, at the largest shapes each entry point
+accepts: rows and row lengths of 2^23, M * K = 2^40, a gated input's full row
+2N = 2^23.  The model follows the kernels' own variable names so that each
+line can be compared with the code by eye.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+ROWS_PER_LANE, COLS_PER_LANE, WAVES = 16, 8, 4
+THREADS = 64 * WAVES
+TILE_M, TILE_K = 128, 256
+MAX_GROUP = 16
+MAX_RECORDS = 0x7FFFFFFF
+DEAD = 0x80000000
+U32 = 1 << 32
+
+
+def pick_group(tiles_m, tiles_k, target=512):
+    g = MAX_GROUP
+    while g > 1 and ((tiles_m + g - 1) // g) * tiles_k < target:
+        g >>= 1
+    return g
+
+
+class Desc:
+    """make_rsrc(base, offset, total): bytes [offset, total) of an allocation,
+    size 0 when offset >= total, at most MAX_RECORDS bytes."""
+
+    def __init__(self, offset, total):
+        left = total - offset
+        self.base = offset if left > 0 else 0
+        self.size = 0 if left <= 0 else min(left, MAX_RECORDS)
+        self.total = total
+
+
+class Checker:
+    def __init__(self):
+        self.bad = []
+
+    def access(self, site, d, off, nbytes, live, addr=None):
+        """off: uint32 per-lane offsets (numpy int64 holding the 32-bit value
+        the kernel computes); live: bool mask of accesses that must happen.
+        addr, when given, is the logical byte address of each access inside
+        its allocation; live accesses must land exactly there."""
+        off = np.asarray(off, dtype=np.int64)
+        live = np.broadcast_to(np.asarray(live, dtype=bool), off.shape)
+        if (off < 0).any() or (off >= U32).any():
+            self.bad.append((site, "32-bit offset out of [0, 2^32)"))
+            return
+        inside = off + nbytes <= d.size
+        outside = off >= d.size
+        if (live & ~inside).any():
+            i = np.argwhere(live & ~inside)[0]
+            self.bad.append((site, f"live access past the descriptor: off {int(off[tuple(i)])} "
+                                   f"+ {nbytes} > size {d.size}"))
+        if (~live & ~outside).any():
+            i = np.argwhere(~live & ~outside)[0]
+            self.bad.append((site, f"masked access inside the descriptor: off {int(off[tuple(i)])}, "
+                                   f"size {d.size}"))
+        if addr is not None:
+            addr = np.broadcast_to(np.asarray(addr, dtype=np.int64), off.shape)
+            wrong = live & (d.base + off != addr)
+            if wrong.any():
+                i = np.argwhere(wrong)[0]
+                self.bad.append((site, f"live access at {int(d.base + off[tuple(i)])}, "
+                                       f"element at {int(addr[tuple(i)])}"))
+            if (live & (addr + nbytes > d.total)).any():
+                self.bad.append((site, "live element past the allocation"))
+
+    def ok(self):
+        assert not self.bad, self.bad[:6]
+
+
+def lanes():
+    """Per thread of a workgroup: wave, half, cl (lane & 31), first row."""
+    t = np.arange(THREADS)
+    wave, lane = t >> 6, t & 63
+    half, cl = lane >> 5, lane & 31
+    row = wave * 2 * ROWS_PER_LANE + half * ROWS_PER_LANE
+    return t, wave, half, cl, row
+
+
+def edge(n):
+    return sorted({0, n - 1})
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 cast kernel (mx_cast.h).  op: "plain", "grad" (dGELU / dSiLU: a second
+# [M][K] input), "gated" (x [M][2N], K = N), "dgated" (grad [M][N], x [M][2N],
+# K = 2N).
+# ---------------------------------------------------------------------------
+def mx_model(M, K, op="plain", tiled=False, ck=None):
+    ck = ck or Checker()
+    if op == "gated":
+        ldx, lin_off, ldg = 2 * K, K, 0
+    elif op == "dgated":
+        ldx, lin_off, ldg = K, K // 2, K // 2
+    else:
+        ldx, lin_off, ldg = K, 0, K
+    tiles_m, tiles_k = -(-M // TILE_M), -(-K // TILE_K)
+    group = pick_group(tiles_m, tiles_k)
+    if tiled and group < 2:
+        group = 2
+    groups_m = -(-tiles_m // group)
+    t, wave, half, cl, row = lanes()
+    r = np.arange(ROWS_PER_LANE)[:, None]
+    strips = edge(tiles_k)
+    if op == "dgated":
+        # also the strips on either side of the gate / linear boundary
+        strips = sorted(set(strips) | {(lin_off - 1) // TILE_K, lin_off // TILE_K} - {tiles_k})
+    for tm, tk in itertools.product(edge(tiles_m) + [tiles_m], strips):
+        # lane_live; tm == tiles_m is the prefetch past a walk's end
+        live = (tm * TILE_M + wave * 32 < M) & (tk * TILE_K + cl * COLS_PER_LANE < K)
+        in_rows = tm * TILE_M + row + r < M            # [16][256]
+        # ---- load_tile
+        if op == "dgated":
+            N = lin_off
+            k = tk * TILE_K + COLS_PER_LANE * cl
+            gate_half = k < N
+            n = np.where(gate_half, k, k - N)
+            m0 = tm * TILE_M
+            rx = Desc(2 * m0 * ldx, 2 * M * ldx)
+            rg = Desc(2 * m0 * ldg, 2 * M * ldg)
+            rl = Desc(2 * (m0 * ldx + N), 2 * M * ldx)
+            sx, sg = 2 * ldx, 2 * ldg
+            ox = np.where(live, row * sx + 2 * n, DEAD)
+            og = np.where(live, row * sg + 2 * n, DEAD)
+            ol = np.where(live & gate_half, ox, DEAD)
+            rowabs = m0 + row + r
+            ck.access("dgated gate", rx, ox + r * sx, 16, live & in_rows,
+                      2 * (rowabs * ldx + n))
+            ck.access("dgated grad", rg, og + r * sg, 16, live & in_rows,
+                      2 * (rowabs * ldg + n))
+            ck.access("dgated linear", rl, ol + r * sx, 16, live & gate_half & in_rows,
+                      2 * (rowabs * ldx + N + n))
+        else:
+            tile = tm * TILE_M * ldx + tk * TILE_K
+            total = M * ldx
+            rx = Desc(2 * tile, 2 * total)
+            rs = 2 * ldx
+            off = np.where(live, row * rs + 2 * COLS_PER_LANE * cl, DEAD)
+            col = tk * TILE_K + COLS_PER_LANE * cl
+            addr = 2 * ((tm * TILE_M + row + r) * ldx + col)
+            ck.access(f"{op} x", rx, off + r * rs, 16, live & in_rows, addr)
+            if op == "grad":
+                gtile = tm * TILE_M * ldg + tk * TILE_K
+                rb = Desc(2 * gtile, 2 * M * ldg)
+                boff = np.where(live, row * 2 * ldg + 2 * COLS_PER_LANE * cl, DEAD)
+                ck.access("grad", rb, boff + r * 2 * ldg, 16, live & in_rows,
+                          2 * ((tm * TILE_M + row + r) * ldg + col))
+            elif op == "gated":
+                rb = Desc(2 * (tile + lin_off), 2 * total)
+                ck.access("gated linear", rb, off + r * rs, 16, live & in_rows,
+                          2 * ((tm * TILE_M + row + r) * ldx + lin_off + col))
+        if tm == tiles_m:
+            continue                                    # the prefetch only loads
+        # ---- row_pass: 8-byte row stores
+        rq = Desc(tm * TILE_M * K + tk * TILE_K, M * K)
+        off = np.where(live, row * K + COLS_PER_LANE * cl, DEAD)
+        ck.access("q_row", rq, off + r * K, 8, live & in_rows,
+                  (tm * TILE_M + row + r) * K + tk * TILE_K + COLS_PER_LANE * cl)
+        # ---- col_flush_q: thread t writes chunk t % 8 of transposed rows t / 8 + 32 i
+        jr = t & 7
+        mt, k0 = tm * TILE_M, tk * TILE_K
+        rc = Desc(k0 * M + mt, K * M)
+        chunk_live = mt + 16 * jr < M
+        kr = (t >> 3)[None, :] + 32 * np.arange(TILE_K // 32)[:, None]
+        ok = chunk_live & (k0 + kr < K)
+        ck.access("q_col", rc, np.where(ok, kr * M + 16 * jr, DEAD), 16, ok,
+                  (k0 + kr) * M + mt + 16 * jr)
+        # ---- srow_flush
+        nb = -(-K // 32)
+        if tiled:
+            RT = -(-M // 32)
+            size = RT * (-(-nb // 8)) * 256
+            rs_ = Desc((tk * RT + 4 * tm) * 256, size)
+            w = t >> 6
+            lv = tm * TILE_M + 32 * w < M
+            ck.access("s_row tiled", rs_, np.where(lv, 4 * t, DEAD), 4, lv)
+        else:
+            rrow = tm * TILE_M + t
+            rs_ = Desc(tm * TILE_M * nb + (k0 >> 5), M * nb)
+            o = np.where((t < TILE_M) & (rrow < M), t * nb, DEAD)
+            if K % 256 == 0:
+                ck.access("s_row", rs_, o, 8, (t < TILE_M) & (rrow < M),
+                          rrow * nb + (k0 >> 5))
+            else:
+                blocks = nb - (k0 >> 5)
+                b = np.arange(TILE_K // 32)[:, None]
+                lv = (b < blocks) & (t < TILE_M) & (rrow < M)
+                ck.access("s_row bytes", rs_, np.where(b < blocks, o + b, DEAD), 1, lv,
+                          rrow * nb + (k0 >> 5) + b)
+    # ---- col_flush_s at the end of the first and last walk of each edge strip
+    nblk = -(-M // 32)
+    for rg, tk in itertools.product(edge(groups_m), edge(tiles_k)):
+        n = min(tiles_m - rg * group, group)
+        k0 = tk * TILE_K
+        if tiled:
+            RT = -(-K // 32)
+            CT = -(-nblk // 8)
+            bt0, rt0 = rg * (group >> 1), tk * (TILE_K // 32)
+            nbt = (4 * n + 7) >> 3
+            rs_ = Desc((bt0 * RT + rt0) * 256, RT * CT * 256)
+            idx = t[None, :] + THREADS * np.arange(2 * nbt)[:, None]
+            btl, rtl, lane = idx >> 9, (idx >> 6) & 7, idx & 63
+            lv = rt0 + rtl < RT
+            ck.access("s_col tiled", rs_, np.where(lv, (btl * RT + rtl) * 256 + 4 * lane, DEAD),
+                      4, lv, ((bt0 + btl) * RT + rt0 + rtl) * 256 + 4 * lane)
+        else:
+            first = rg * group * 4
+            count = min(nblk - first, 4 * n)
+            rs_ = Desc(k0 * nblk + first, K * nblk)
+            scale_rows(ck, "s_col", rs_, k0, K, nblk, first, count)
+    return ck
+
+
+def scale_rows(ck, site, rs, k0, K, pitch, first, count, base_align=0):
+    """flush_scale_rows (stage_flush.h): row c's `count` bytes in pieces of
+    the widest size CH that pitch, first, count and the base allow."""
+    align = pitch | first | count | base_align
+    CH = next(c for c in (16, 8, 4, 2, 1) if align % c == 0)
+    t = np.arange(THREADS)
+    pieces = count // CH
+    if pieces == 0:
+        return
+    idx = t[None, :] + THREADS * np.arange(pieces)[:, None]
+    c, q = idx // pieces, idx % pieces
+    lv = k0 + c < K
+    ck.access(site, rs, np.where(lv, c * pitch + CH * q, DEAD), CH, lv,
+              (k0 + c) * pitch + first + CH * q)
+
+
+# ---------------------------------------------------------------------------
+# NVFP4 kernel (nvfp4.hip)
+# ---------------------------------------------------------------------------
+def nv_model(M, K, ck=None):
+    ck = ck or Checker()
+    tiles_m, tiles_k = -(-M // TILE_M), -(-K // TILE_K)
+    group = pick_group(tiles_m, tiles_k)
+    groups_m = -(-tiles_m // group)
+    t, wave, half, cl, row = lanes()
+    r = np.arange(ROWS_PER_LANE)[:, None]
+    for tm, tk in itertools.product(edge(tiles_m) + [tiles_m], edge(tiles_k)):
+        live = (tm * TILE_M + row < M) & (tk * TILE_K + cl * COLS_PER_LANE < K)
+        tile = tm * TILE_M * K + tk * TILE_K
+        rx = Desc(2 * tile, 2 * M * K)
+        rs = 2 * K
+        off = np.where(live, row * rs + 2 * COLS_PER_LANE * cl, DEAD)
+        ck.access("nv x", rx, off + r * rs, 16, live,
+                  2 * ((tm * TILE_M + row + r) * K + tk * TILE_K + COLS_PER_LANE * cl))
+        if tm == tiles_m:
+            continue
+        ld = K >> 1
+        rq = Desc(tm * TILE_M * ld + tk * (TILE_K // 2), M * ld)
+        qoff = np.where(live, row * ld + 4 * cl, DEAD)
+        ck.access("nv q_row", rq, qoff + r * ld, 4, live,
+                  (tm * TILE_M + row + r) * ld + tk * (TILE_K // 2) + 4 * cl)
+        nb = K >> 4
+        rrow = tm * TILE_M + t
+        k0 = tk * TILE_K
+        rs_ = Desc(tm * TILE_M * nb + (k0 >> 4), M * nb)
+        o = np.where((t < TILE_M) & (rrow < M), t * nb, DEAD)
+        if K % 256 == 0:
+            ck.access("nv s_row", rs_, o, 16, (t < TILE_M) & (rrow < M), rrow * nb + (k0 >> 4))
+        else:
+            blocks = nb - (k0 >> 4)
+            b = np.arange(TILE_K // 16)[:, None]
+            lv = (b < blocks) & (t < TILE_M) & (rrow < M)
+            ck.access("nv s_row bytes", rs_, np.where(b < blocks, o + b, DEAD), 1, lv,
+                      rrow * nb + (k0 >> 4) + b)
+    # nv_flush_q for the pair starting at each edge sub-tile (parts 1 and 2)
+    for tm, tk, parts in itertools.product(edge(tiles_m), edge(tiles_k), (1, 2)):
+        jr = t & 7
+        m0, k0 = tm * TILE_M, tk * TILE_K
+        ld = M >> 1
+        rc = Desc(k0 * ld + (m0 >> 1), K * ld)
+        row0 = m0 + 32 * jr
+        in_pair = jr < 4 * parts
+        kr = (t >> 3)[None, :] + 32 * np.arange(TILE_K // 32)[:, None]
+        col_ok = in_pair & (k0 + kr < K)
+        off = kr * ld + 16 * jr
+        addr = (k0 + kr) * ld + (m0 >> 1) + 16 * jr
+        if M % 32 == 0:
+            lv = col_ok & (row0 < M)
+            ck.access("nv q_col", rc, np.where(lv, off, DEAD), 16, lv, addr)
+        else:
+            lv = col_ok & (row0 < M)
+            ck.access("nv q_col lo", rc, np.where(lv, off, DEAD), 8, lv, addr)
+            lv = col_ok & (row0 + 16 < M)
+            ck.access("nv q_col hi", rc, np.where(lv, off + 8, DEAD), 8, lv, addr + 8)
+    nblk = M >> 4
+    for rg, tk in itertools.product(edge(groups_m), edge(tiles_k)):
+        n = min(tiles_m - rg * group, group)
+        tm0 = rg * group
+        k0 = tk * TILE_K
+        first = tm0 * (TILE_M // 16)
+        count = min(nblk - first, 8 * n)
+        rs_ = Desc(k0 * nblk + first, K * nblk)
+        scale_rows(ck, "nv s_col", rs_, k0, K, nblk, first, count)
+    return ck
+
+
+MAXD = 1 << 23
+
+MX_SHAPES = [(MAXD, 32), (MAXD, 8), (MAXD - 16, 40), (32, MAXD), (16, MAXD), (128, MAXD),
+             (144, MAXD - 8), (1 << 17, MAXD), (MAXD, 1 << 17), (16400, 7176), (16384, 16384)]
+
+
+@pytest.mark.parametrize("tiled", [False, True], ids=["compact", "tiled"])
+@pytest.mark.parametrize("M,K", MX_SHAPES)
+@pytest.mark.parametrize("op", ["plain", "grad"])
+def test_mx_quantize_offsets(M, K, op, tiled):
+    mx_model(M, K, op, tiled).ok()
+
+
+# gated: the quantised tensor is [M][N] with N <= 2^22 (full row 2N <= 2^23);
+# gated backward: [M][2N].
+GATED_N = [(MAXD, 8), (128, 1 << 22), (144, (1 << 22) - 8), (1 << 17, 1 << 22),
+           (16, 1 << 22), (8192, 4096), (16400, 3592)]
+
+
+@pytest.mark.parametrize("tiled", [False, True], ids=["compact", "tiled"])
+@pytest.mark.parametrize("M,N", GATED_N)
+def test_gated_offsets(M, N, tiled):
+    mx_model(M, N, "gated", tiled).ok()
+
+
+@pytest.mark.parametrize("tiled", [False, True], ids=["compact", "tiled"])
+@pytest.mark.parametrize("M,N", GATED_N)
+def test_dgated_offsets(M, N, tiled):
+    mx_model(M, 2 * N, "dgated", tiled).ok()
+
+
+NV_SHAPES = [(MAXD, 16), (16, MAXD), (128, MAXD), (144, MAXD - 16), (1 << 17, MAXD),
+             (MAXD, 1 << 17), (16400, 7168), (16384, 16384)]
+
+
+@pytest.mark.parametrize("M,K", NV_SHAPES)
+def test_nvfp4_offsets(M, K):
+    nv_model(M, K).ok()
+
+
+def test_model_sees_the_linear_half_overrun():
+    """The model is sharp enough to see the fault it was written for: with the
+    linear half's 2N bytes added to the lane offset (instead of to the
+    descriptor's base), the last row's load at 2N = 2^23 ends at 2^31,
+    past the largest descriptor."""
+    M, N = 128, 1 << 22
+    ck = Checker()
+    ldx, K = 2 * N, 2 * N
+    t, wave, half, cl, row = lanes()
+    r = np.arange(ROWS_PER_LANE)[:, None]
+    tk = -(-K // TILE_K) // 2 - 1                     # last strip of the gate half
+    k = tk * TILE_K + COLS_PER_LANE * cl
+    rx = Desc(0, 2 * M * ldx)
+    ox = row * 2 * ldx + 2 * k
+    ck.access("old linear", rx, ox + 2 * N + r * 2 * ldx, 16, np.ones_like(ox + r, dtype=bool))
+    assert ck.bad and "past the descriptor" in ck.bad[0][1]

@@ -25,8 +25,10 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Two fp32 -> a packed pair of bf16 bits (lo in bits 0-15), round to nearest
-// even, by gfx950's v_cvt_pk_bf16_f32 (qualified bit-identical to integer RNE
-// rounding over all 2^32 fp32 inputs; Inf stays Inf).
+// even, by gfx950's v_cvt_pk_bf16_f32: on every one of the 2^32 fp32 inputs,
+// in either half of the pair, the nearest bf16 with ties to even (overflow to
+// Inf; NaN stays NaN), as the device qualification tests check against the
+// oracle's rounding.
 __device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi)
 {
     const bf16x2 r = __builtin_convertvector((f32x2){lo, hi}, bf16x2);
@@ -65,41 +67,13 @@ __device__ __forceinline__ uint32_t scale_byte(uint32_t mag)
     return mag >= 0x7F80u ? 0xFFu : b;
 }
 
-__device__ __forceinline__ uint32_t e8m0_from_mag(uint32_t mag) { return scale_byte<0>(mag); }
-
-// 2^(127 - byte) as an fp32 (a normal number for every byte <= 253): the
-// exact inverse of the block scale, so each element costs one multiply
-// ("Multiply with inverse scale in loop inside of dividing", body bullets).
-__device__ __forceinline__ float e8m0_inverse(uint32_t byte)
-{
-    return f32_bits(((254u - byte) & 0xFFu) << 23);
-}
-
-// ---------------------------------------------------------------------------
-// fp32 -> E4M3 ("fn": bias 7, max 448, no Inf), round to nearest with ties to
-// the even code, saturating, sign kept.  Normal range: round the 23-bit
-// significand to 3 bits at bit 20 and rebias the exponent (127 -> 7);
-// subnormal range (< 2^-6, spacing 2^-9): the code is |v| * 2^9 rounded to an
-// integer (0..8, where 8 is the smallest normal).  NaN is never passed in.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t e4m3_rne_sat(float v)
-{
-    uint32_t u = bits_f32(v);
-    uint32_t sign = (u >> 24) & 0x80u;
-    uint32_t a = u & 0x7FFFFFFFu;
-    uint32_t nrm = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
-    uint32_t sub = (uint32_t)__builtin_rintf(f32_bits(a) * 512.0f);
-    uint32_t code = a < 0x3C800000u ? sub : nrm;
-    code = a >= 0x43E00000u ? 0x7Eu : code;
-    return sign | code;
-}
-
 // Two fp32 -> two E4M3 bytes (round to nearest even, saturating), written into
 // the low (HI = false) or high (HI = true) 16 bits of `old`, first value in the
 // lower byte.  v_cvt_pk_fp8_f32 rounds to nearest even but turns values beyond
 // the format into NaN, so both inputs are first clamped to +-448, which leaves
-// every in-range value (and -0) unchanged.  The pair is bit-identical to
-// e4m3_rne_sat on every finite input a block can produce.
+// every in-range value (and -0) unchanged.  The device qualification tests
+// compare the pair, in both halves and both operand positions, with the
+// oracle's saturating E4M3 rounding on every non-NaN fp32 input.
 template <bool HI>
 __device__ __forceinline__ uint32_t e4m3x2(float a, float b, uint32_t old)
 {
@@ -140,9 +114,10 @@ __device__ __forceinline__ uint32_t clamp_pair(uint32_t w, uint32_t mag, uint32_
 // exponent field -- and rounds to nearest even, which is exactly the block
 // rule (the division by a power of two is exact, so it equals multiplying by
 // the inverse).  The clamp is what makes it saturate: on its own the
-// instruction turns values beyond 448 into NaN.  Qualified bit-identical to
-// e4m3_rne_sat(x * 2^(127 - b)) over every reachable (element, byte) pair, in
-// both halves of the pair.
+// instruction turns values beyond 448 into NaN.  The exhaustive parity tensor
+// of the GPU tests (every finite bf16 element under every scale byte it can
+// meet, in both halves of a pair) checks the result against the oracle's
+// nearest-E4M3 rule bit for bit.
 template <bool HI>
 __device__ __forceinline__ uint32_t e4m3x2_scaled(uint32_t pair, float scale, uint32_t old)
 {
@@ -186,13 +161,28 @@ __device__ __forceinline__ float e8m0_operand(uint32_t b) { return f32_bits(b <<
 
 // Two fp32 -> two E2M1 nibbles in byte SEL of `old` (first value in the low
 // nibble), by v_cvt_scalef32_pk_fp4_f32 with scale 1: round to nearest even,
-// saturating at 6, Inf -> 6; bit-identical to e2m1_rne_sat on every non-NaN
-// input.  (A NaN input -- only 0 * Inf -- gives 6 here, so callers route blocks
-// whose multiplier is Inf through e2m1_rne_sat.)
+// saturating at 6, Inf -> 6.  The device qualification tests compare it, in
+// all four byte positions and both operand positions, with the oracle's E2M1
+// rounding on every non-NaN fp32 input.  (A NaN input -- only 0 * Inf -- is
+// not covered; callers clear the nibbles of such products.)
 template <int SEL>
 __device__ __forceinline__ uint32_t e2m1x2(float a, float b, uint32_t old)
 {
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+}
+
+// fl32(b / 6) for b >= 0 holding a bf16 value (at most 8 significant bits):
+// q0 = b * RN(1/6), the residual b - 6 q0 (exact in the FMA, since q0 is
+// within an ulp of b / 6), and one correction step.  Equal to the IEEE
+// division for every finite non-negative bf16 (shown with exact rational
+// arithmetic by the CPU tests, and compared on the device with the correctly
+// rounded quotient by the qualification tests), at a third of its cost.
+__device__ __forceinline__ float div6_bf16(float b)
+{
+    const float c = 0x1.555556p-3f;   // RN(1/6)
+    const float q0 = b * c;
+    const float r = __builtin_fmaf(-6.0f, q0, b);
+    return __builtin_fmaf(r, c, q0);
 }
 
 // E4M3 code (no NaN) -> its exact fp32 value.
@@ -201,22 +191,6 @@ __device__ __forceinline__ float e4m3_value(uint32_t c)
     uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
     float mag = e ? f32_bits(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
     return (c & 0x80u) ? -mag : mag;
-}
-
-// fp32 -> E2M1 nibble: magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}, nearest with
-// ties to the even code, saturating at 6 (Inf too), sign in bit 3, NaN -> 0.
-// Each comparison is one decision boundary; ">" at a tie whose lower code is
-// even, ">=" where the upper code is even.
-__device__ __forceinline__ uint32_t e2m1_rne_sat(float v)
-{
-    uint32_t u = bits_f32(v);
-    uint32_t a = u & 0x7FFFFFFFu;
-    float x = f32_bits(a);
-    uint32_t c = (uint32_t)(x > 0.25f) + (uint32_t)(x >= 0.75f) + (uint32_t)(x > 1.25f) +
-                 (uint32_t)(x >= 1.75f) + (uint32_t)(x > 2.5f) + (uint32_t)(x >= 3.5f) +
-                 (uint32_t)(x > 5.0f);
-    c |= (u >> 28) & 8u;
-    return a > 0x7F800000u ? 0u : c;
 }
 
 // ---------------------------------------------------------------------------
@@ -254,17 +228,24 @@ __device__ __forceinline__ float exp32_nonpos(float a)
     return a != a ? a : e;
 }
 
+// fl32(1 / d) for d in [1, 2]: the hardware reciprocal estimate and one
+// Newton step with FMAs, at a third of the cost of the IEEE division and equal
+// to it for every one of the 2^23 + 1 floats in [1, 2] (the device
+// qualification tests compare all of them with the correctly rounded
+// quotient).
+__device__ __forceinline__ float rcp_1_2(float d)
+{
+    const float r0 = __builtin_amdgcn_rcpf(d);
+    return __builtin_fmaf(__builtin_fmaf(-d, r0, 1.0f), r0, r0);
+}
+
 // sigma(z) = 1/(1+e^-z) and 1 - sigma(z) from e = e^-|z| (no overflow, no
 // cancellation): z >= 0 gives (1/(1+e), e/(1+e)), z < 0 the swapped pair.
 __device__ __forceinline__ void sigmoid_pair(float z, float &s, float &sc)
 {
     float e = exp32_nonpos(-__builtin_fabsf(z));
     float d = 1.0f + e;
-    // r = fl32(1 / d) for d in [1, 2]: the hardware reciprocal estimate and one
-    // Newton step with FMAs; equal to the IEEE quotient for every float in
-    // [1, 2] (all 2^23 + 1 of them checked on gfx950), at a third of its cost
-    const float r0 = __builtin_amdgcn_rcpf(d);
-    float r = __builtin_fmaf(__builtin_fmaf(-d, r0, 1.0f), r0, r0);
+    float r = rcp_1_2(d);   // d is in [1, 2]
     float er = e * r;
     s = z >= 0.0f ? r : er;
     sc = z >= 0.0f ? er : r;

@@ -26,19 +26,6 @@
 
 namespace mxk {
 
-// fl32(b / 6) for b >= 0 holding a bf16 value (at most 8 significant bits):
-// q0 = b * RN(1/6), the residual b - 6 q0 (exact in the FMA, since q0 is
-// within an ulp of b / 6), and one correction step.  Equal to the IEEE
-// division for every finite non-negative bf16 (checked exhaustively with
-// exact arithmetic by the CPU tests), at a third of its cost.
-__device__ __forceinline__ float div6_bf16(float b)
-{
-    const float c = 0x1.555556p-3f;   // RN(1/6)
-    const float q0 = b * c;
-    const float r = __builtin_fmaf(-6.0f, q0, b);
-    return __builtin_fmaf(r, c, q0);
-}
-
 // Scale byte of one NVFP4 block whose largest magnitude has bf16 pattern
 // mag: E4M3(fl32(fl32(b / 6) / S_g)); the division by S_g is IEEE, the E4M3
 // rounding the saturating hardware convert (inputs are finite here).
@@ -67,9 +54,9 @@ __device__ __forceinline__ uint32_t zero_or_nan_nibble(uint32_t h)
 
 // Eight bf16 (four words) times inv -> eight E2M1 nibbles, element i in bits
 // 4i..4i+3 (so element 2j is the low nibble of byte j).  The hardware
-// convert matches the software encoder on every non-NaN product; a NaN
-// product (0 * Inf or NaN * Inf, possible only when the multiplier
-// overflowed to Inf, tensor scale below ~2^-120) encodes as 0 there, so such
+// convert gives the nearest E2M1 code on every non-NaN product (e2m1x2); a
+// NaN product (0 * Inf or NaN * Inf, possible only when the multiplier
+// overflowed to Inf, tensor scale below ~2^-120) must encode as +0, so such
 // nibbles are cleared afterwards.
 __device__ __forceinline__ uint32_t encode8_fp4(const uint32_t (&w)[4], float inv)
 {

@@ -141,6 +141,26 @@ def _c(a, dtype):
     return a
 
 
+_CHECKS = {"bf16_round": ctypes.POINTER(ctypes.c_uint16), "e2m1": _u8p, "e4m3": _u8p,
+           "exp32": ctypes.POINTER(ctypes.c_uint32)}
+
+
+def check_range(which: str, got: np.ndarray, first: int):
+    """Compare device results for the fp32 patterns first, first + 1, ...
+    with the oracle's rule `which` (bf16_round, e2m1, e4m3, exp32).  got holds
+    one result per input (e2m1: one byte per input pair).  Returns (number of
+    differing inputs, first differing input index or -1)."""
+    fn = getattr(lib(), "orc_check_" + which)
+    fn.restype = ctypes.c_int64
+    fn.argtypes = [_CHECKS[which], ctypes.c_uint64, ctypes.c_int64,
+                   ctypes.POINTER(ctypes.c_int64)]
+    got = np.ascontiguousarray(got)
+    n = got.size * (2 if which == "e2m1" else 1)
+    fb = ctypes.c_int64()
+    bad = fn(got.ctypes.data_as(_CHECKS[which]), first, n, ctypes.byref(fb))
+    return int(bad), int(fb.value)
+
+
 def set_threads(n: int) -> None:
     lib().orc_set_threads(int(n))
 

@@ -60,6 +60,7 @@
  * -fPIC (see build.py).  OpenMP only splits independent rows / columns /
  * blocks, never a reduction, so results do not depend on the thread count.
  */
+#include <limits.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -1041,6 +1042,105 @@ void orc_unary32_array(int which, const float *v, float *out, int64_t n)
         out[i] = which == 0 ? orc_exp32(a) : which == 1 ? orc_gelu32(a)
                : which == 2 ? orc_dgelu32(a) : which == 3 ? orc_silu32(a) : orc_dsilu32(a);
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Bulk comparisons for the device qualification tests.  The GPU runs one of */
+/* the library's per-element routines on every fp32 bit pattern of a range  */
+/* (input i is the pattern first + i); these count the results that differ  */
+/* from the rules above and report the first differing index (-1 if none).  */
+/* The threads only split the range; the count and the minimum index do not  */
+/* depend on how.                                                            */
+/* ------------------------------------------------------------------------ */
+
+static float f32_of_bits(uint32_t u)
+{
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* got[i]: bf16 bits of input i rounded to nearest even (NaN: any NaN). */
+int64_t orc_check_bf16_round(const uint16_t *got, uint64_t first, int64_t n, int64_t *first_bad)
+{
+    int64_t bad = 0, fb = INT64_MAX;
+#pragma omp parallel for schedule(static) reduction(+ : bad) reduction(min : fb)
+    for (int64_t i = 0; i < n; i++) {
+        const float f = f32_of_bits((uint32_t)(first + (uint64_t)i));
+        const uint16_t g = got[i];
+        const int ok = isnan(f) ? ((g & 0x7F80) == 0x7F80 && (g & 0x7F) != 0)
+                                : g == orc_bf16_round((double)f);
+        if (!ok) {
+            bad++;
+            if (i < fb)
+                fb = i;
+        }
+    }
+    *first_bad = bad ? fb : -1;
+    return bad;
+}
+
+/* got[j]: E2M1 codes of inputs 2j (low nibble) and 2j + 1 (high nibble);
+ * NaN inputs are not compared. */
+int64_t orc_check_e2m1(const uint8_t *got, uint64_t first, int64_t n, int64_t *first_bad)
+{
+    init_tables();
+    int64_t bad = 0, fb = INT64_MAX;
+#pragma omp parallel for schedule(static) reduction(+ : bad) reduction(min : fb)
+    for (int64_t i = 0; i < n; i++) {
+        const float f = f32_of_bits((uint32_t)(first + (uint64_t)i));
+        if (isnan(f))
+            continue;
+        const uint8_t g = (uint8_t)((got[i >> 1] >> (4 * (i & 1))) & 0xF);
+        if (g != orc_e2m1_encode((double)f)) {
+            bad++;
+            if (i < fb)
+                fb = i;
+        }
+    }
+    *first_bad = bad ? fb : -1;
+    return bad;
+}
+
+/* got[i]: saturating E4M3 code of input i; NaN inputs are not compared. */
+int64_t orc_check_e4m3(const uint8_t *got, uint64_t first, int64_t n, int64_t *first_bad)
+{
+    init_tables();
+    int64_t bad = 0, fb = INT64_MAX;
+#pragma omp parallel for schedule(static) reduction(+ : bad) reduction(min : fb)
+    for (int64_t i = 0; i < n; i++) {
+        const float f = f32_of_bits((uint32_t)(first + (uint64_t)i));
+        if (isnan(f))
+            continue;
+        if (got[i] != orc_e4m3_encode((double)f)) {
+            bad++;
+            if (i < fb)
+                fb = i;
+        }
+    }
+    *first_bad = bad ? fb : -1;
+    return bad;
+}
+
+/* got[i]: fp32 bits of e^x for input i (NaN: any NaN). */
+int64_t orc_check_exp32(const uint32_t *got, uint64_t first, int64_t n, int64_t *first_bad)
+{
+    int64_t bad = 0, fb = INT64_MAX;
+#pragma omp parallel for schedule(static) reduction(+ : bad) reduction(min : fb)
+    for (int64_t i = 0; i < n; i++) {
+        const float f = f32_of_bits((uint32_t)(first + (uint64_t)i));
+        const float e = orc_exp32(f);
+        uint32_t want;
+        memcpy(&want, &e, 4);
+        const int ok = isnan(f) ? isnan(f32_of_bits(got[i])) : got[i] == want;
+        if (!ok) {
+            bad++;
+            if (i < fb)
+                fb = i;
+        }
+    }
+    *first_bad = bad ? fb : -1;
+    return bad;
 }
 
 void orc_set_threads(int n)

@@ -34,7 +34,7 @@ OP_GATED, OP_DGATED = 0x100, 0x200
 (MX_OK, MX_ERR_NULL, MX_ERR_ENUM, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_WORKSPACE,
  MX_ERR_ALIAS, MX_ERR_HIP, MX_ERR_UNSUPPORTED) = range(9)
 
-EXPORTS = ("mx_quantize", "mx_quantize_workspace_size", "mx_scale_size", "mx_quantize_grouped",
+EXPORTS = ("mx_quantize", "mx_quantize_workspace_size", "mx_quantize_noalloc", "mx_scale_size", "mx_quantize_grouped",
            "mx_quantize_grouped_workspace_size", "mx_grouped_scale_size", "mx_quantize_gated",
            "mx_quantize_gated_grouped", "mx_quantize_dgated_grouped",
            "mx_quantize_dgated", "mx_fused_values",
@@ -65,6 +65,9 @@ def lib():
         L.mx_quantize.restype = ctypes.c_int
         L.mx_quantize.argtypes = [_vp, _vp, _i64, _i64, ctypes.c_uint, ctypes.c_int,
                                   _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.mx_quantize_noalloc.restype = ctypes.c_int
+        L.mx_quantize_noalloc.argtypes = [_vp, _vp, _i64, _i64, ctypes.c_uint, ctypes.c_int,
+                                          _vp, _vp, _vp, _vp, _vp, _vp]
         L.mx_quantize_workspace_size.restype = ctypes.c_size_t
         L.mx_quantize_workspace_size.argtypes = [_i64, _i64, ctypes.c_uint, ctypes.c_int]
         L.mx_scale_size.restype = ctypes.c_size_t
@@ -282,6 +285,36 @@ def mx_quantize(x, grad=None, axis=ROWWISE | COLWISE, fusion=FUSE_NONE, out=None
                            _ptr(workspace) if fusion & FUSE_DBIAS else None, ws_bytes,
                            _stream(dev, stream))
     _check(st, "mx_quantize")
+    return {k: o.get(k) for k in ("q_row", "s_row", "q_col", "s_col", "dbias")}
+
+
+NOALLOC_SCRATCH_BYTES = 4 << 20     # MX_NOALLOC_SCRATCH_BYTES
+
+
+def mx_quantize_noalloc(x, out, grad=None, axis=ROWWISE | COLWISE, fusion=FUSE_NONE,
+                        stream=None):
+    """mx_quantize without any device allocation: `out` must hold every
+    requested output (q_row, s_row, q_col, s_col, and dbias with FUSE_DBIAS)
+    preallocated; dbias partials use the library's static device scratch
+    (calls with FUSE_DBIAS that overlap on one GPU race; see mxcast.h)."""
+    x = _2d(x, "x")
+    M, K = x.shape
+    grad = _2d(grad, "grad") if (fusion & 0xF) in (FUSE_DGELU, FUSE_DSILU) else None
+    _want_shape(grad, (M, K), "grad")
+    dev = x.device
+    need = _mx_need(M, K, axis)
+    if fusion & FUSE_DBIAS:
+        need["dbias"] = ((K,), F32)
+    missing = [k for k in need if (out or {}).get(k) is None]
+    if missing:
+        raise ValueError(f"mx_quantize_noalloc allocates nothing: out must hold {missing}")
+    o = _outputs(out, need, dev)
+    _on_device(dev, grad, *o.values())
+    st = lib().mx_quantize_noalloc(_ptr(x), _ptr(grad), M, K, axis, fusion,
+                                   _ptr(o.get("q_row")), _ptr(o.get("s_row")),
+                                   _ptr(o.get("q_col")), _ptr(o.get("s_col")),
+                                   _ptr(o.get("dbias")), _stream(dev, stream))
+    _check(st, "mx_quantize_noalloc")
     return {k: o.get(k) for k in ("q_row", "s_row", "q_col", "s_col", "dbias")}
 
 

@@ -357,9 +357,16 @@ size_t mx_scale_size(int64_t rows, int64_t cols, unsigned axis_mask)
     return (size_t)scale_bytes(rows, cols, (axis_mask & MX_SCALE_TILED) != 0);
 }
 
-mx_status mx_quantize(const void *x, const void *grad, int64_t M, int64_t K, unsigned axis_mask,
-                      int fusion, uint8_t *q_row, uint8_t *s_row, uint8_t *q_col, uint8_t *s_col,
-                      float *dbias, void *workspace, size_t workspace_bytes, hipStream_t stream)
+static_assert(MX_NOALLOC_SCRATCH_BYTES == mxk::kNoAllocScratchBytes,
+              "the header states the scratch size of the allocation-free cast");
+
+// mx_quantize, and with noalloc its allocation-free variant, whose dbias
+// partials live in the library's static device scratch instead of a
+// caller's workspace.
+static mx_status quantize_impl(const void *x, const void *grad, int64_t M, int64_t K,
+                               unsigned axis_mask, int fusion, uint8_t *q_row, uint8_t *s_row,
+                               uint8_t *q_col, uint8_t *s_col, float *dbias, void *workspace,
+                               size_t workspace_bytes, bool noalloc, hipStream_t stream)
 {
     const int pre = fusion & 0xF;
     const bool want_dbias = (fusion & MX_FUSE_DBIAS) != 0;
@@ -380,16 +387,23 @@ mx_status mx_quantize(const void *x, const void *grad, int64_t M, int64_t K, uns
     const int op = cast_op(pre);
     const bool tiled = (axis_mask & MX_SCALE_TILED) != 0;
     const size_t need = want_dbias ? dbias_workspace(M, K, op, tiled) : 0;
-    if (want_dbias && (!workspace || workspace_bytes < need))
+    if (noalloc ? need > mxk::kNoAllocScratchBytes
+                : want_dbias && (!workspace || workspace_bytes < need))
         return MX_ERR_WORKSPACE;
     const uint64_t n = (uint64_t)(M * K);
     const Span in[2] = {{x, 2 * n}, {has_grad ? grad : nullptr, 2 * n}};
     const Span out[6] = {{row ? q_row : nullptr, n}, {row ? s_row : nullptr, scale_bytes(M, K, tiled)},
                          {col ? q_col : nullptr, n}, {col ? s_col : nullptr, scale_bytes(K, M, tiled)},
                          {want_dbias ? dbias : nullptr, 4 * (uint64_t)K},
-                         {want_dbias ? workspace : nullptr, need}};
+                         {want_dbias && !noalloc ? workspace : nullptr, need}};
     if (any_alias(in, 2, out, 6))
         return MX_ERR_ALIAS;
+    if (want_dbias && noalloc) {
+        float *p = nullptr;
+        if (mxk::noalloc_scratch(stream, &p) != hipSuccess)
+            return MX_ERR_HIP;
+        workspace = p;
+    }
 
     mxk::MxArgs a;
     a.x = static_cast<const uint16_t *>(x);
@@ -412,6 +426,22 @@ mx_status mx_quantize(const void *x, const void *grad, int64_t M, int64_t K, uns
     if (st != MX_OK || !want_dbias)
         return st;
     return from_hip(mxk::launch_dbias_reduce(a.partials, a.groups_m, K, dbias, stream));
+}
+
+mx_status mx_quantize(const void *x, const void *grad, int64_t M, int64_t K, unsigned axis_mask,
+                      int fusion, uint8_t *q_row, uint8_t *s_row, uint8_t *q_col, uint8_t *s_col,
+                      float *dbias, void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return quantize_impl(x, grad, M, K, axis_mask, fusion, q_row, s_row, q_col, s_col, dbias,
+                         workspace, workspace_bytes, false, stream);
+}
+
+mx_status mx_quantize_noalloc(const void *x, const void *grad, int64_t M, int64_t K,
+                              unsigned axis_mask, int fusion, uint8_t *q_row, uint8_t *s_row,
+                              uint8_t *q_col, uint8_t *s_col, float *dbias, hipStream_t stream)
+{
+    return quantize_impl(x, grad, M, K, axis_mask, fusion, q_row, s_row, q_col, s_col, dbias,
+                         nullptr, 0, true, stream);
 }
 
 size_t mx_quantize_grouped_workspace_size(int64_t K, const int64_t *group_rows, int G,

@@ -140,6 +140,12 @@ hipError_t launch_dbias_reduce_grouped(const float *partials, const GroupTable &
                                        float *dbias, hipStream_t s);
 hipError_t launch_dbias_reduce(const float *partials, int segments, int64_t K, float *dbias,
                                hipStream_t s);
+
+// Device scratch of the allocation-free cast (mx_quantize_noalloc): a static
+// device array of this many bytes per GPU, holding the dbias partial sums.
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+// Its address on the device of stream s, looked up once per device.
+hipError_t noalloc_scratch(hipStream_t s, float **ptr);
 // op as above (1..7); gated ops read x[M][2K]; the gated backward ops read
 // grad aux[M][K] and write y[M][2K].
 hipError_t launch_fused_values(int op, const uint16_t *x, const uint16_t *aux, int64_t M,

@@ -5,7 +5,50 @@
 
 #include "mx_cast.h"
 
+#include <mutex>
+
 namespace mxk {
+
+// The dbias partials of mx_quantize_noalloc, for callers that cannot
+// allocate: one copy per GPU, alive until the process ends.  In host code
+// the name stands for a host-side shadow, not the device array, so kernels
+// only ever get the address that noalloc_scratch looks up.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+hipError_t noalloc_scratch(hipStream_t s, float **ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static float *addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipStreamGetDevice(s, &dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        // the lookup runs with the stream's device current
+        int cur = 0;
+        e = hipGetDevice(&cur);
+        if (e != hipSuccess)
+            return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+            return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t back = hipSetDevice(cur);
+            if (e == hipSuccess)
+                e = back;
+        }
+        if (e != hipSuccess)
+            return e;
+        addr[dev] = static_cast<float *>(p);
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 // dbias[k] = sum over strip segments t (in order) of partials[t][k].
 __global__ __launch_bounds__(256) void dbias_reduce_kernel(const float *partials, int segments,

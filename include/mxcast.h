@@ -43,6 +43,8 @@
  *   - All tensor pointers are DEVICE pointers owned by the caller; the
  *     library never allocates, frees or synchronises.  Work is enqueued on
  *     `stream` (NULL = the default stream) and completes asynchronously.
+ *     Scratch memory comes from the caller (a workspace argument), except
+ *     for mx_quantize_noalloc, whose scratch is a static device array.
  *   - bf16 tensors are raw 16-bit patterns; E4M3, E8M0 and packed E2M1 are
  *     raw bytes.  Every tensor is row-major and contiguous.
  *   - Column-wise outputs are transposed: for x[M][K], q_col is [K][M] and
@@ -53,7 +55,8 @@
  *     validation error nothing is written and a non-zero status returns.
  *     Launch failures return MX_ERR_HIP.  Device faults surface at the
  *     caller's next synchronisation.
- *   - Calls hold no state and are safe from several host threads.
+ *   - Calls hold no state and are safe from several host threads (the one
+ *     exception, mx_quantize_noalloc's shared scratch, is described there).
  */
 #ifndef MXCAST_H
 #define MXCAST_H
@@ -67,7 +70,7 @@
 extern "C" {
 #endif
 
-#define MXCAST_ABI_VERSION 8
+#define MXCAST_ABI_VERSION 9
 
 typedef enum mx_status {
     MX_OK = 0,
@@ -173,6 +176,33 @@ mx_status mx_quantize(const void *x, const void *grad, int64_t M, int64_t K,
 /* Bytes of workspace mx_quantize needs for these arguments (0 without dbias;
  * 0 also for invalid arguments). */
 size_t mx_quantize_workspace_size(int64_t M, int64_t K, unsigned axis_mask, int fusion);
+
+/*
+ * mx_quantize for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same cast with the same arguments, minus the workspace: with MX_FUSE_DBIAS
+ * the per-tile column partial sums go to a static device array of the
+ * library, MX_NOALLOC_SCRATCH_BYTES per GPU, which each GPU the library runs
+ * on holds until the process ends.  Outputs are bit-identical to
+ * mx_quantize's (the same kernels and the same fixed summation order).
+ *   - No device memory is allocated or freed, by the library or a library it
+ *     calls.  Without MX_FUSE_DBIAS the scratch is not used at all.
+ *   - A dbias cast whose workspace (mx_quantize_workspace_size) exceeds
+ *     MX_NOALLOC_SCRATCH_BYTES returns MX_ERR_WORKSPACE and writes nothing.
+ *   - Every call on one GPU shares that GPU's scratch, which keeps the last
+ *     call's contents (every byte a call reads it has written first): calls
+ *     with MX_FUSE_DBIAS that overlap on one GPU (on different streams, or
+ *     from several host threads without ordering) race and may give wrong
+ *     dbias values.  Calls ordered on one stream are safe.
+ *   - The first call on each device looks up the scratch address (no
+ *     allocation); the stream's device is made current for that lookup.
+ * Other errors as for mx_quantize.
+ */
+#define MX_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+mx_status mx_quantize_noalloc(const void *x, const void *grad, int64_t M, int64_t K,
+                              unsigned axis_mask, int fusion,
+                              uint8_t *q_row, uint8_t *s_row, uint8_t *q_col, uint8_t *s_col,
+                              float *dbias, hipStream_t stream);
 
 /*
  * Bytes of one scale tensor of an MXFP8 cast: the scales of a quantised

@@ -41,7 +41,7 @@ def header_abi_version():
 
 
 def test_version_and_status_strings():
-    assert mx.mx_abi_version() == header_abi_version() == 8
+    assert mx.mx_abi_version() == header_abi_version() == 9
     for code in range(9):
         assert mx.mx_status_str(code).startswith("MX_")
     assert "unknown" in mx.mx_status_str(99)
@@ -373,3 +373,31 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(mx, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         mx.lib()
+
+
+def test_noalloc_rejects_before_any_launch():
+    """The allocation-free cast validates like mx_quantize (no workspace
+    arguments) and refuses a dbias cast whose partials exceed its static
+    scratch, before touching the runtime."""
+    b = Bufs(64, 96)
+    L = mx.lib()
+
+    def qn(**kw):
+        a = dict(x=b.p("x"), grad=b.p("g"), M=64, K=96, axis=3, fusion=0, q_row=b.p("q_row"),
+                 s_row=b.p("s_row"), q_col=b.p("q_col"), s_col=b.p("s_col"), dbias=b.p("dbias"))
+        a.update(kw)
+        return L.mx_quantize_noalloc(a["x"], a["grad"], a["M"], a["K"], a["axis"], a["fusion"],
+                                     a["q_row"], a["s_row"], a["q_col"], a["s_col"], a["dbias"],
+                                     None)
+
+    assert qn(axis=0) == mx.MX_ERR_ENUM
+    assert qn(x=NULL) == mx.MX_ERR_NULL
+    assert qn(fusion=mx.FUSE_DBIAS, dbias=NULL) == mx.MX_ERR_NULL
+    assert qn(M=40) == mx.MX_ERR_SHAPE
+    assert qn(x=b.p("x", 8)) == mx.MX_ERR_ALIGN
+    assert qn(q_row=b.p("x", 16)) == mx.MX_ERR_ALIAS
+    # 128 x 2^21 with dbias: one walk of 2^21 fp32 partials = 8 MiB > 4 MiB
+    assert mx.mx_quantize_workspace_size(128, 1 << 21, 3, mx.FUSE_GELU | mx.FUSE_DBIAS) == 8 << 20
+    assert qn(M=128, K=1 << 21, fusion=mx.FUSE_GELU | mx.FUSE_DBIAS) == mx.MX_ERR_WORKSPACE
+    assert mx.mx_quantize_workspace_size(128, 1 << 20, 3, mx.FUSE_DBIAS) == mx.NOALLOC_SCRATCH_BYTES
+    assert b.untouched()

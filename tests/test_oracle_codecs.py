@@ -4,6 +4,10 @@ Each codec is checked against something other than the oracle itself: torch's
 own bf16 / float8_e4m3fn conversions (library special cases), brute-force
 nearest-value search over the format's value set, and log2.
 """
+import ctypes
+import os
+import subprocess
+
 import numpy as np
 import pytest
 import torch
@@ -139,6 +143,46 @@ def test_e2m1_encode_brute_force():
     assert O.e2m1_encode(float("inf")) == 7 and O.e2m1_encode(-float("inf")) == 15
     assert O.e2m1_encode(float("nan")) == 0
     assert O.e2m1_encode(-0.0) == 8
+
+
+@pytest.fixture(scope="module")
+def e2m1_sweeper(tmp_path_factory):
+    """The brute-force sweep of tests/pins/e2m1_sweep.c, compiled for this run."""
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "pins", "e2m1_sweep.c")
+    so = str(tmp_path_factory.mktemp("pins") / "e2m1_sweep.so")
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp", "-fPIC",
+                    "-shared", src, "-o", so, "-lm"], check=True)
+    L = ctypes.CDLL(so)
+    L.e2m1_sweep.restype = ctypes.c_int64
+    L.e2m1_sweep.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int64,
+                             ctypes.POINTER(ctypes.c_int64)]
+    return L
+
+
+def test_e2m1_encode_every_fp32(e2m1_sweeper):
+    """The oracle's E2M1 encoder on all 2^32 fp32 bit patterns (NaN aside,
+    pinned above) equals the brute-force nearest of the eight magnitudes."""
+    enc = ctypes.cast(O.lib().orc_e2m1_encode, ctypes.c_void_p)
+    fb = ctypes.c_int64()
+    step = 1 << 30
+    for first in range(0, 1 << 32, step):
+        bad = e2m1_sweeper.e2m1_sweep(enc, first, step, ctypes.byref(fb))
+        assert bad == 0, (bad, hex(first + fb.value))
+
+
+def test_e2m1_sweep_catches_a_wrong_encoder(e2m1_sweeper):
+    """The sweep fails an encoder with one rounding decision moved: ties
+    between 2 and 3 (code 4 | 5) going up instead of to the even code."""
+    fn_t = ctypes.CFUNCTYPE(ctypes.c_uint8, ctypes.c_double)
+
+    def wrong(v):
+        c = O.e2m1_encode(v)
+        return (c + 1) if abs(v) == 2.5 else c
+    cb = fn_t(wrong)
+    fb = ctypes.c_int64()
+    first = 0x40200000                         # 2.5
+    bad = e2m1_sweeper.e2m1_sweep(ctypes.cast(cb, ctypes.c_void_p), first - 4, 8, ctypes.byref(fb))
+    assert bad == 1 and fb.value == 4
 
 
 def test_e8m0_exhaustive_over_bf16_amax():

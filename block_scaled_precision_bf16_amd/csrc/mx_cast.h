@@ -263,10 +263,11 @@ __device__ __forceinline__ void row_pass(const MxArgs &a, const uint32_t (&w)[kR
 // j ^ ((kl >> 3) & 7): the 32 lanes of a half-wave write rows 8 apart (one
 // per lane), the 8 threads that read a row back read its 8 chunks, and both
 // patterns then cover all banks.  s: the column-block scales of the whole
-// strip segment the workgroup walks (4 per sub-tile), written out once.
+// strip segment the workgroup walks (4 per sub-tile), transposed (block-major,
+// stage_flush.h) and written out once.
 struct ColStage {
     uint4 q[kTileK][kTileM / 16];            // 32 KB
-    uint8_t s[kTileK][4 * kMaxGroup];        // 16 KB
+    uint8_t s[4 * kMaxGroup][kTileK];        // 16 KB
 };
 
 __device__ __forceinline__ int stage_chunk(int kl, int j) { return j ^ ((kl >> 3) & 7); }
@@ -281,6 +282,7 @@ __device__ __forceinline__ void col_pass(ColStage &st, const uint32_t (&w)[kRows
 #pragma unroll
     for (int d = 0; d < 4; d++)
         cmax[d] = pk_max_u16(cmax[d], (uint32_t)__shfl_xor((int)cmax[d], 32, 64));
+    uint32_t sbs[kColsPerLane];
 #pragma unroll
     for (int c = 0; c < kColsPerLane; c++) {
         const int d = c >> 1, hi = c & 1;
@@ -291,9 +293,11 @@ __device__ __forceinline__ void col_pass(ColStage &st, const uint32_t (&w)[kRows
             o = make_uint4(0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu);
         const int kl = cl * kColsPerLane + c;
         st.q[kl][stage_chunk(kl, 2 * wave + half)] = o;
-        if (half == 0)
-            st.s[kl][4 * g + wave] = (uint8_t)sb;
+        sbs[c] = sb;
     }
+    // both halves hold the same column scales; one writes them
+    if (half == 0)
+        stage_scales8(st.s, 4 * g + wave, cl, pack8(sbs));
 }
 
 // Write the staged transposed tile of sub-tile tm: thread t writes 16-byte
@@ -344,7 +348,9 @@ __device__ __forceinline__ void col_flush_s_tiled(const MxArgs &a, const ColStag
     for (int i = 0; i < 2 * nbt; i++) {
         const int idx = t + kThreads * i;                 // (block tile, row tile, lane)
         const int btl = idx >> 9, rtl = (idx >> 6) & 7, lane = idx & 63;
-        uint2 v = *reinterpret_cast<const uint2 *>(&st.s[32 * rtl + (lane & 31)][8 * btl]);
+        uint32_t b8[2];
+        staged_bytes<8>(st.s, 8 * btl, 32 * rtl + (lane & 31), b8);
+        uint2 v = make_uint2(b8[0], b8[1]);
         if (4 * n - 8 * btl < 8)
             v.y = 0u;
         const uint32_t off = rt0 + rtl < RT ? (uint32_t)(((int64_t)btl * RT + rtl) * 256 + 4 * lane)

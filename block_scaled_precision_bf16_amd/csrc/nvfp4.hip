@@ -137,11 +137,11 @@ __device__ __forceinline__ bool nv_live(const Nv4Args &a, const NvLane &l, int t
 // row's 8 chunks with 8 threads without bank conflicts).  Sub-tile p of the
 // pair fills chunks 4p..4p+3; the lane of rows 16h..16h+15 of the sub-tile
 // writes bytes 8(h & 1) of chunk 4p + h / 2.  s: the 8 column-block scales
-// per sub-tile of the whole walk.  srow: the 16 row-block scales per row of
-// the current sub-tile.
+// per sub-tile of the whole walk, transposed (block-major, stage_flush.h).
+// srow: the 16 row-block scales per row of the current sub-tile.
 struct NvStage {
     uint8_t q[kTileK][128];                      // 32 KB
-    uint8_t s[kTileK][8 * kMaxGroup];            // 32 KB
+    uint8_t s[8 * kMaxGroup][kTileK];            // 32 KB, block-major (stage_flush.h)
     uint8_t srow[kTileM][kTileK / 16];           // 2 KB
     float inv[128];                              // multiplier of each scale byte
 };
@@ -289,8 +289,10 @@ __device__ __forceinline__ void nv_step_2d(const Nv4Args &a, const NvLane &l,
             const int kl = l.cl * kColsPerLane + c;
             *reinterpret_cast<uint2 *>(&st.q[kl][16 * nv_chunk(kl, jr) + 8 * l.half]) =
                 make_uint2(o[0], o[1]);
-            st.s[kl][8 * g + 2 * l.wave + l.half] = (uint8_t)sb;
         }
+        // the 16 x 16 block's scale, for each of the lane's 8 columns
+        const uint32_t rep = sb * 0x01010101u;
+        stage_scales8(st.s, 8 * g + 2 * l.wave + l.half, l.cl, make_uint2(rep, rep));
     }
 }
 
@@ -365,6 +367,7 @@ __device__ __forceinline__ void nv_step(const Nv4Args &a, const NvLane &l,
             }
         const int p = g & 1;
         const int jr = 4 * p + l.wave;                       // logical 16-byte chunk
+        uint32_t sbs[kColsPerLane];
 #pragma unroll
         for (int c = 0; c < kColsPerLane; c++) {
             const int d = c >> 1, hi = c & 1;
@@ -378,9 +381,10 @@ __device__ __forceinline__ void nv_step(const Nv4Args &a, const NvLane &l,
             const int kl = l.cl * kColsPerLane + c;
             *reinterpret_cast<uint2 *>(&st.q[kl][16 * nv_chunk(kl, jr) + 8 * l.half]) =
                 make_uint2(o[0], o[1]);
-            st.s[kl][8 * g + 2 * l.wave + l.half] = (uint8_t)sb;
+            sbs[c] = sb;
             __builtin_amdgcn_sched_barrier(0);
         }
+        stage_scales8(st.s, 8 * g + 2 * l.wave + l.half, l.cl, pack8(sbs));
     }
     }
     __syncthreads();

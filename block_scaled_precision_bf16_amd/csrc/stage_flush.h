@@ -22,8 +22,44 @@ __device__ __forceinline__ void buf_store2(rsrc_t r, uint32_t off, uint16_t v)
     __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)off, 0, AUX);
 }
 
+// Column-block scales are staged transposed: s[b][pos] holds the scale of
+// block b of the walk (a 32-row block of MXFP8, a 16-row block of NVFP4) of
+// transposed row kl, at byte pos = kl ^ scol_swz(b).  A lane's 8 columns
+// (kl = 8 cl .. 8 cl + 7) are 8 contiguous bytes, so the lane writes its
+// scales of one block with one 8-byte store and a half-wave covers a whole
+// 256-byte row: no two of its lanes share an LDS bank.  The XOR (bits 4-5 of
+// kl, from bits 4-5 of b) spreads the flush's reads of the 16 blocks of one
+// 16-byte piece over distinct banks as well.
+__device__ __forceinline__ int scol_pos(int b, int kl) { return kl ^ (16 * ((b >> 4) & 3)); }
+
+template <int W>
+__device__ __forceinline__ void stage_scales8(uint8_t (&s)[W][kTileK], int b, int cl, uint2 v)
+{
+    *reinterpret_cast<uint2 *>(&s[b][scol_pos(b, 8 * cl)]) = v;
+}
+
+// Eight scale bytes (byte j = value j, j = 0..7) packed for stage_scales8.
+__device__ __forceinline__ uint2 pack8(const uint32_t (&b)[8])
+{
+    return make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
+                      b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
+}
+
+// Bytes b0 .. b0 + N - 1 of staged transposed row kl, byte i = block b0 + i.
+template <int N, int W>
+__device__ __forceinline__ void staged_bytes(const uint8_t (&s)[W][kTileK], int b0, int kl,
+                                             uint32_t (&w)[(N + 3) / 4])
+{
+#pragma unroll
+    for (int i = 0; i < (N + 3) / 4; i++)
+        w[i] = 0;
+#pragma unroll
+    for (int j = 0; j < N; j++)
+        w[j >> 2] |= (uint32_t)s[b0 + j][scol_pos(b0 + j, kl)] << (8 * (j & 3));
+}
+
 template <int AUX, int CH, int W>
-__device__ __forceinline__ void flush_scale_rows_ch(rsrc_t rs, const uint8_t (&s)[kTileK][W],
+__device__ __forceinline__ void flush_scale_rows_ch(rsrc_t rs, const uint8_t (&s)[W][kTileK],
                                                     int64_t k0, int64_t K, int64_t pitch,
                                                     int count)
 {
@@ -33,24 +69,25 @@ __device__ __forceinline__ void flush_scale_rows_ch(rsrc_t rs, const uint8_t (&s
         const int idx = t + kThreads * i;                 // (row, piece) pair
         const int c = idx / pieces, q = idx - c * pieces;
         const uint32_t off = k0 + c < K ? (uint32_t)(c * pitch) + CH * q : kDead;
-        const uint8_t *src = &s[c][CH * q];
+        uint32_t w[(CH + 3) / 4];
+        staged_bytes<CH>(s, CH * q, c, w);
         if constexpr (CH == 16)
-            buf_store16<AUX>(rs, off, *reinterpret_cast<const uint4 *>(src));
+            buf_store16<AUX>(rs, off, make_uint4(w[0], w[1], w[2], w[3]));
         else if constexpr (CH == 8)
-            buf_store8<AUX>(rs, off, *reinterpret_cast<const uint2 *>(src));
+            buf_store8<AUX>(rs, off, make_uint2(w[0], w[1]));
         else if constexpr (CH == 4)
-            buf_store4<AUX>(rs, off, *reinterpret_cast<const uint32_t *>(src));
+            buf_store4<AUX>(rs, off, w[0]);
         else if constexpr (CH == 2)
-            buf_store2<AUX>(rs, off, *reinterpret_cast<const uint16_t *>(src));
+            buf_store2<AUX>(rs, off, (uint16_t)w[0]);
         else
-            buf_store1<AUX>(rs, off, *src);
+            buf_store1<AUX>(rs, off, (uint8_t)w[0]);
     }
 }
 
 // rs covers the scale tensor from byte k0 * pitch + first of `base`; rows at
-// or beyond K are skipped.  count <= W.
+// or beyond K are skipped.  count <= W; s is the transposed stage above.
 template <int AUX, int W>
-__device__ __forceinline__ void flush_scale_rows(rsrc_t rs, const uint8_t (&s)[kTileK][W],
+__device__ __forceinline__ void flush_scale_rows(rsrc_t rs, const uint8_t (&s)[W][kTileK],
                                                  int64_t k0, int64_t K, int64_t pitch,
                                                  int64_t first, int count, const void *base)
 {

@@ -136,7 +136,7 @@ __device__ __forceinline__ bool nv_live(const Nv4Args &a, const NvLane &l, int t
 // transposed row, chunk j at position j ^ ((kl >> 3) & 7) (the flush reads a
 // row's 8 chunks with 8 threads without bank conflicts).  Sub-tile p of the
 // pair fills chunks 4p..4p+3; the lane of rows 16h..16h+15 of the sub-tile
-// writes bytes 8(h & 1) of chunk 4p + h / 2.  s: the 8 column-block scales
+// writes bytes 8 nv_half(kl, h & 1) of chunk 4p + h / 2.  s: the 8 column-block scales
 // per sub-tile of the whole walk, transposed (block-major, stage_flush.h).
 // srow: the 16 row-block scales per row of the current sub-tile.
 struct NvStage {
@@ -147,6 +147,13 @@ struct NvStage {
 };
 
 __device__ __forceinline__ int nv_chunk(int kl, int j) { return j ^ ((kl >> 3) & 7); }
+
+// The 8-byte half of a staged chunk that rows 16h .. 16h + 15 of the wave
+// (h = half) go to: swapped for transposed rows with bit 6 set, so that lanes
+// cl and cl + 8 -- whose rows share a chunk position -- write different halves
+// and any 16 consecutive lanes write 16 different 8-byte slots of a 128-byte
+// span (no LDS bank conflict); the flush swaps them back.
+__device__ __forceinline__ int nv_half(int kl, int half) { return half ^ ((kl >> 6) & 1); }
 
 template <int XA>
 __device__ __forceinline__ void nv_load(const Nv4Args &a, const NvLane &l, int tm, int tk,
@@ -187,7 +194,9 @@ __device__ __forceinline__ void nv_flush_q(const Nv4Args &a, const NvStage &st, 
     for (int i = 0; i < kTileK / 32; i++) {
         const int kr = (t >> 3) + 32 * i;
         const bool col_ok = in_pair && k0 + kr < a.K;
-        const uint4 v = *reinterpret_cast<const uint4 *>(&st.q[kr][16 * nv_chunk(kr, jr)]);
+        uint4 v = *reinterpret_cast<const uint4 *>(&st.q[kr][16 * nv_chunk(kr, jr)]);
+        if (nv_half(kr, 0))
+            v = make_uint4(v.z, v.w, v.x, v.y);
         const uint32_t off = (uint32_t)(kr * ld) + 16 * jr;
         if (!half) {
             buf_store16<AUX>(rc, col_ok && row0 < a.M ? off : kDead, v);
@@ -287,7 +296,7 @@ __device__ __forceinline__ void nv_step_2d(const Nv4Args &a, const NvLane &l,
             for (int q = 0; q < 2; q++)
                 o[q] = (c & 1) ? encode8_fp4_col<1>(wc, q, d, inv) : encode8_fp4_col<0>(wc, q, d, inv);
             const int kl = l.cl * kColsPerLane + c;
-            *reinterpret_cast<uint2 *>(&st.q[kl][16 * nv_chunk(kl, jr) + 8 * l.half]) =
+            *reinterpret_cast<uint2 *>(&st.q[kl][16 * nv_chunk(kl, jr) + 8 * nv_half(kl, l.half)]) =
                 make_uint2(o[0], o[1]);
         }
         // the 16 x 16 block's scale, for each of the lane's 8 columns
@@ -379,7 +388,7 @@ __device__ __forceinline__ void nv_step(const Nv4Args &a, const NvLane &l,
             for (int q = 0; q < 2; q++)
                 o[q] = hi ? encode8_fp4_col<1>(wc, q, d, inv) : encode8_fp4_col<0>(wc, q, d, inv);
             const int kl = l.cl * kColsPerLane + c;
-            *reinterpret_cast<uint2 *>(&st.q[kl][16 * nv_chunk(kl, jr) + 8 * l.half]) =
+            *reinterpret_cast<uint2 *>(&st.q[kl][16 * nv_chunk(kl, jr) + 8 * nv_half(kl, l.half)]) =
                 make_uint2(o[0], o[1]);
             sbs[c] = sb;
             __builtin_amdgcn_sched_barrier(0);
@@ -481,53 +490,85 @@ __global__ __launch_bounds__(kThreads, 2) void nvfp4_grouped_kernel(Nv4Args a, G
 // ---------------------------------------------------------------------------
 __global__ void absmax_clear_kernel(uint32_t *amax_bits) { *amax_bits = 0u; }
 
-// Largest 15-bit magnitude this thread sees of x[0, n), thread `first` of
-// `stride` threads, reduced over the wave into lane 0's bits 16-30.
-__device__ __forceinline__ uint32_t absmax_wave(const uint16_t *x, int64_t n, int64_t first,
-                                                int64_t stride, bool tail)
+// 16-byte vectors of the input through a global-address-space pointer, so the
+// loads are global (not flat) loads; the input is read once, so they are
+// non-temporal.
+typedef const __attribute__((address_space(1))) u32x4_t gvec_t;
+
+__device__ __forceinline__ uint32_t fold_vec(uint32_t m, u32x4_t v)
 {
-    const u32x4_t *xv = reinterpret_cast<const u32x4_t *>(x);
-    const int64_t nvec = n >> 3;
-    auto fold = [](uint32_t m, u32x4_t v) {
-        return pk_max_u16(m, pk_max_u16(pk_max_u16(v[0] & 0x7FFF7FFFu, v[1] & 0x7FFF7FFFu),
-                                        pk_max_u16(v[2] & 0x7FFF7FFFu, v[3] & 0x7FFF7FFFu)));
-    };
+    return pk_max_u16(m, pk_max_u16(pk_max_u16(v[0] & 0x7FFF7FFFu, v[1] & 0x7FFF7FFFu),
+                                    pk_max_u16(v[2] & 0x7FFF7FFFu, v[3] & 0x7FFF7FFFu)));
+}
+
+// Largest 15-bit magnitudes (two packed halves) of this workgroup's chunk of
+// vectors, [b0, b1): each pass reads eight runs of 256 consecutive vectors
+// (4 KiB each, one per wave instruction), eight independent loads in flight
+// per thread.  A workgroup reading a contiguous chunk keeps its accesses in
+// few DRAM pages; measured on the 16384^2 tensor, 512 chunked workgroups read
+// at 6.1 TB/s against 5.1 TB/s for a grid-strided loop.
+__device__ __forceinline__ uint32_t absmax_chunk(const uint16_t *x, int64_t b0, int64_t b1)
+{
+    gvec_t *xv = (gvec_t *)x;
     uint32_t m = 0;
-    int64_t i = first;
-    // four independent 16-byte loads in flight per thread; the input is read
-    // once, so the loads are non-temporal
-    for (; i + 3 * stride < nvec; i += 4 * stride) {
-        u32x4_t v[4];
+    int64_t i = b0 + threadIdx.x;
+    for (; i + 7 * 256 < b1; i += 8 * 256) {
+        u32x4_t v[8];
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-            v[j] = __builtin_nontemporal_load(xv + i + j * stride);
+        for (int j = 0; j < 8; j++)
+            v[j] = __builtin_nontemporal_load(xv + i + j * 256);
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-            m = fold(m, v[j]);
+        for (int j = 0; j < 8; j++)
+            m = fold_vec(m, v[j]);
     }
-    for (; i < nvec; i += stride)
-        m = fold(m, __builtin_nontemporal_load(xv + i));
-    if (tail && threadIdx.x < (n & 7)) {
-        const uint32_t t = x[(nvec << 3) + threadIdx.x] & 0x7FFFu;
-        m = pk_max_u16(m, t);
-    }
-    uint32_t lo = m & 0xFFFFu, hi = m >> 16;
-    uint32_t mag = lo > hi ? lo : hi;
+    for (; i < b1; i += 256)
+        m = fold_vec(m, __builtin_nontemporal_load(xv + i));
+    return m;
+}
+
+// Chunk of workgroup b of nb over nvec vectors.
+__device__ __forceinline__ void chunk_of(int64_t nvec, int b, int nb, int64_t &b0, int64_t &b1)
+{
+    const int64_t per = (nvec + nb - 1) / nb;
+    b0 = (int64_t)b * per;
+    b1 = b0 + per < nvec ? b0 + per : nvec;
+}
+
+// The workgroup's largest magnitude, combined into *dst by one atomic max
+// (of its fp32 bit pattern) from thread 0.
+__device__ __forceinline__ void absmax_commit(uint32_t m, uint32_t *dst)
+{
+    uint32_t mag = (m & 0xFFFFu) > (m >> 16) ? (m & 0xFFFFu) : (m >> 16);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
         const uint32_t o = (uint32_t)__shfl_xor((int)mag, off, 64);
         mag = mag > o ? mag : o;
     }
-    return mag << 16;
+    __shared__ uint32_t red[4];
+    if ((threadIdx.x & 63) == 0)
+        red[threadIdx.x >> 6] = mag;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t w = red[0];
+#pragma unroll
+        for (int i = 1; i < 4; i++)
+            w = w > red[i] ? w : red[i];
+        atomicMax(dst, w << 16);
+    }
 }
+
+constexpr int kAbsmaxBlocks = 512;   // two 256-thread workgroups per CU
 
 __global__ __launch_bounds__(256) void absmax_kernel(const uint16_t *x, int64_t n,
                                                      uint32_t *amax_bits)
 {
-    const uint32_t bits = absmax_wave(x, n, (int64_t)blockIdx.x * 256 + threadIdx.x,
-                                      (int64_t)gridDim.x * 256, blockIdx.x == 0);
-    if ((threadIdx.x & 63) == 0)
-        atomicMax(amax_bits, bits);
+    const int64_t nvec = n >> 3;
+    int64_t b0, b1;
+    chunk_of(nvec, (int)blockIdx.x, (int)gridDim.x, b0, b1);
+    uint32_t m = absmax_chunk(x, b0, b1);
+    if (blockIdx.x == 0 && threadIdx.x < (n & 7))   // the last n % 8 elements
+        m = pk_max_u16(m, x[(nvec << 3) + threadIdx.x] & 0x7FFFu);
+    absmax_commit(m, amax_bits);
 }
 
 // Per-group absmax: blockIdx.y is the group, whose rows are x[row0[g] ..
@@ -539,16 +580,27 @@ __global__ void absmax_clear_grouped_kernel(uint32_t *amax_bits, int G)
         amax_bits[threadIdx.x] = 0u;
 }
 
+// Workgroups of the grouped absmax: group g gets blk0[g + 1] - blk0[g] of
+// them, in proportion to its size, so that every workgroup reads a chunk of
+// about the same length.
+struct AbsmaxPlan {
+    int blk0[kMaxGroups + 1];
+};
+
 __global__ __launch_bounds__(256) void absmax_grouped_kernel(const uint16_t *x, int64_t K,
-                                                             GroupTable gt, uint32_t *amax_bits)
+                                                             GroupTable gt, AbsmaxPlan plan,
+                                                             uint32_t *amax_bits)
 {
-    const int g = (int)blockIdx.y;
+    const int b = (int)blockIdx.x;
+    int g = 0;
+    while (g + 1 < gt.count && plan.blk0[g + 1] <= b)
+        g++;
     const int64_t r0 = gt.row0[g];
-    const uint32_t bits = absmax_wave(x + r0 * K, (gt.row0[g + 1] - r0) * K,
-                                      (int64_t)blockIdx.x * 256 + threadIdx.x,
-                                      (int64_t)gridDim.x * 256, false);
-    if ((threadIdx.x & 63) == 0)
-        atomicMax(amax_bits + g, bits);
+    int64_t b0, b1;
+    chunk_of(((gt.row0[g + 1] - r0) * K) >> 3, b - plan.blk0[g], plan.blk0[g + 1] - plan.blk0[g],
+             b0, b1);
+    const uint32_t m = absmax_chunk(x + r0 * K, b0, b1);
+    absmax_commit(m, amax_bits + g);
 }
 
 hipError_t launch_absmax(const uint16_t *x, int64_t n, float *amax, hipStream_t s)
@@ -558,11 +610,8 @@ hipError_t launch_absmax(const uint16_t *x, int64_t n, float *amax, hipStream_t 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    int64_t blocks = ((n >> 3) + 255) / 256;
-    if (blocks > 2048)
-        blocks = 2048;
-    if (blocks < 1)
-        blocks = 1;
+    int64_t blocks = ((n >> 3) + 2047) / 2048;   // at least 2048 vectors per workgroup
+    blocks = blocks > kAbsmaxBlocks ? kAbsmaxBlocks : (blocks < 1 ? 1 : blocks);
     hipLaunchKernelGGL(absmax_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, n, bits);
     return hipGetLastError();
 }
@@ -576,14 +625,21 @@ hipError_t launch_absmax_grouped(const uint16_t *x, int64_t K, const GroupTable 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    int64_t most = 0;
-    for (int g = 0; g < gt.count; g++)
-        most = gt.row0[g + 1] - gt.row0[g] > most ? gt.row0[g + 1] - gt.row0[g] : most;
-    int64_t blocks = ((most * K >> 3) + 255) / 256;
-    const int64_t cap = 2048 / gt.count > 16 ? 2048 / gt.count : 16;
-    blocks = blocks > cap ? cap : (blocks < 1 ? 1 : blocks);
-    hipLaunchKernelGGL(absmax_grouped_kernel, dim3((unsigned)blocks, (unsigned)gt.count),
-                       dim3(256), 0, s, x, K, gt, bits);
+    // about kAbsmaxBlocks workgroups in all, each group's share in
+    // proportion to its rows (at least one for a group with rows)
+    AbsmaxPlan plan;
+    const int64_t M = gt.row0[gt.count];
+    int total = 0;
+    for (int g = 0; g < gt.count; g++) {
+        plan.blk0[g] = total;
+        const int64_t rows = gt.row0[g + 1] - gt.row0[g];
+        const int64_t want = (rows * kAbsmaxBlocks + M - 1) / M;
+        const int64_t cap = ((rows * K >> 3) + 2047) / 2048;   // >= 2048 vectors each
+        total += rows == 0 ? 0 : (int)(want < 1 ? 1 : (want > cap ? (cap < 1 ? 1 : cap) : want));
+    }
+    plan.blk0[gt.count] = total;
+    hipLaunchKernelGGL(absmax_grouped_kernel, dim3((unsigned)total), dim3(256), 0, s, x, K, gt,
+                       plan, bits);
     return hipGetLastError();
 }
 

@@ -115,9 +115,11 @@ typedef enum mx_status {
  * The pages only hint at consumer-ready scale shapes (the "fix scale shapes"
  * step of the torchao PR 12 stack); the layout is the one a gfx950
  * block-scaled 32x32x64 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4) reads: lane
- * L of a wave holds one row (L % 32) and one 32-element K block (half L / 32
- * of the step's 64), and takes its E8M0 scale from a byte of a 32-bit
- * register chosen per step.  For a scale matrix S[R][C] (s_row: R = M rows,
+ * L of a wave supplies the E8M0 scale of row L % 32 and 32-element K block
+ * L / 32 of each 64-wide step (its operand bytes hold 16 K values of each of
+ * the step's two blocks), from a byte of a 32-bit register that the
+ * instruction's op_sel picks per step; a GPU test feeds the cast's outputs
+ * to that instruction.  For a scale matrix S[R][C] (s_row: R = M rows,
  * C = K/32 blocks; s_col: R = K transposed rows, C = M/32 blocks):
  *   tile (rt, bt) = rows 32 rt .. 32 rt + 31, blocks 8 bt .. 8 bt + 7,
  *                   256 bytes at byte offset (bt * ceil(R/32) + rt) * 256;

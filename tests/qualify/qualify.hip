@@ -106,6 +106,61 @@ __global__ void div6_kernel(uint32_t *out)
     out[i] = __float_as_uint(div6_bf16(__uint_as_float((uint32_t)i << 16)));
 }
 
+// One wave multiplies two block-scaled operands the way a GEMM on gfx950
+// consumes the cast's outputs: C[32][32] = sum over k of A[i][k] * B[k][j] by
+// K / 64 steps of v_mfma_scale_f32_32x32x64_f8f6f4.
+//   qa [32][K]: row-wise elements of a [32][K] tensor (A, blocks along k)
+//   qb [32][K]: column-wise elements of a [K][32] tensor, i.e. B transposed
+//               (row j holds B[.][j], blocks along k)
+//   sa, sb:     their scales in the GEMM-ready tile layout (32 rows, so one
+//               row tile; block tile bt at byte 256 bt)
+// The instruction's operand layout (8-bit formats): lane L, h = L / 32,
+// holds row L % 32, K values 16 h .. 16 h + 15 of each 32-value half of the
+// step's 64 (bytes 0-15: k = 16 h + b; bytes 16-31: k = 32 + 16 h + b - 16);
+// its scale byte scales K block h (k = 32 h .. 32 h + 31) of row L % 32.
+// So lane L's scale word is word L of block tile t / 4, and byte t % 4 of it
+// (the op_sel byte select) is the scale of step t.  FMT: 0 E4M3, 1 E5M2.
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+typedef float v16f_t __attribute__((ext_vector_type(16)));
+
+template <int FMT, int J>
+__device__ __forceinline__ v16f_t mx_step(v8i_t a, v8i_t b, v16f_t c, int wa, int wb)
+{
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT, FMT, J, wa, J, wb);
+}
+
+template <int FMT>
+__global__ void mfma_consumer_kernel(const uint8_t *qa, const uint8_t *sa, const uint8_t *qb,
+                                     const uint8_t *sb, int K, float *C)
+{
+    const int L = (int)threadIdx.x;        // one wave of 64
+    v16f_t c = {};
+    for (int t = 0; t < K / 64; t++) {
+        const int k0 = 64 * t + 16 * (L >> 5);
+        const uint4 a0 = *reinterpret_cast<const uint4 *>(qa + (L & 31) * K + k0);
+        const uint4 a1 = *reinterpret_cast<const uint4 *>(qa + (L & 31) * K + k0 + 32);
+        const uint4 b0 = *reinterpret_cast<const uint4 *>(qb + (L & 31) * K + k0);
+        const uint4 b1 = *reinterpret_cast<const uint4 *>(qb + (L & 31) * K + k0 + 32);
+        const v8i_t a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                         (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+        const v8i_t b = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                         (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+        const int wa = *reinterpret_cast<const int *>(sa + (t >> 2) * 256 + 4 * L);
+        const int wb = *reinterpret_cast<const int *>(sb + (t >> 2) * 256 + 4 * L);
+        switch (t & 3) {
+        case 0: c = mx_step<FMT, 0>(a, b, c, wa, wb); break;
+        case 1: c = mx_step<FMT, 1>(a, b, c, wa, wb); break;
+        case 2: c = mx_step<FMT, 2>(a, b, c, wa, wb); break;
+        default: c = mx_step<FMT, 3>(a, b, c, wa, wb); break;
+        }
+    }
+    // accumulator layout of the 32 x 32 MFMA: lane L, register r holds
+    // C[8 (r / 4) + 4 (L / 32) + r % 4][L % 32]
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+        C[(8 * (r >> 2) + 4 * (L >> 5) + (r & 3)) * 32 + (L & 31)] = c[r];
+}
+
 unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
 
 bool range_ok(uint32_t first, int64_t n)
@@ -171,6 +226,21 @@ int qual_div6(uint32_t *out, hipStream_t s)
     if (!out)
         return 1;
     hipLaunchKernelGGL(div6_kernel, dim3(blocks_for(0x7F80)), dim3(256), 0, s, out);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// qa, qb: device [32][K] element bytes; sa, sb: device tile-layout scales of
+// 256 * K / 256 bytes each; K a positive multiple of 256; C: device [32][32]
+// fp32.  fmt: 0 E4M3, 1 E5M2.  One wave.
+int qual_mfma_consumer(const uint8_t *qa, const uint8_t *sa, const uint8_t *qb,
+                       const uint8_t *sb, int K, int fmt, float *C, hipStream_t s)
+{
+    if (!qa || !sa || !qb || !sb || !C || K <= 0 || K % 256 != 0 || (fmt != 0 && fmt != 1))
+        return 1;
+    if (fmt == 0)
+        hipLaunchKernelGGL(mfma_consumer_kernel<0>, dim3(1), dim3(64), 0, s, qa, sa, qb, sb, K, C);
+    else
+        hipLaunchKernelGGL(mfma_consumer_kernel<1>, dim3(1), dim3(64), 0, s, qa, sa, qb, sb, K, C);
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 

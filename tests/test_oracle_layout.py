@@ -54,9 +54,12 @@ def dequant_rows(q, s):
 
 def mfma_walk_product(qa, ta, qb, tb, M, N, K):
     """C = A B^T the way a 32x32x64 block-scaled MFMA wave reads the tiled
-    scales: for each 32 x 32 output tile and each 64-wide K step, lane L takes
-    row L % 32 of A (and of B) and the 32 K elements of half L / 32 of the step,
-    and the scale in byte (step % 4) of its word in tile (block tile, row tile)."""
+    scales: for each 32 x 32 output tile and each 64-wide K step, lane L's
+    scale -- byte (step % 4) of its word in tile (block tile, row tile) --
+    scales row L % 32 of A (and of B) over K block L / 32 of the step.  (On
+    the hardware the lane's operand bytes hold 16 K values of each of the
+    step's two blocks; which lane carries an element does not change the
+    product, the scale of each (row, block) does.)"""
     a = torch.from_numpy(qa).view(torch.float8_e4m3fn).double().numpy()
     b = torch.from_numpy(qb).view(torch.float8_e4m3fn).double().numpy()
     RA, RB = M // 32, N // 32

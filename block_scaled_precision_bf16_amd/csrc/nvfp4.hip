@@ -326,40 +326,59 @@ __device__ __forceinline__ void nv_step(const Nv4Args &a, const NvLane &l,
     } else {
     // Rows go in pairs: both lanes of a row block know the block maxima of
     // rows r and r + 1; the even lane derives the scale of row r, the odd
-    // lane that of row r + 1, and they swap results.
+    // lane that of row r + 1, and they swap results.  The pairs go in two
+    // batches of four: the four codes first (one division each, one pair at
+    // a time: left alone, the scheduler interleaves the divisions of all rows
+    // and runs out of registers), then their eight multipliers read from LDS
+    // together -- one wait for LDS per batch rather than one per lookup.
+    const bool odd = l.cl & 1;
 #pragma unroll
-    for (int r = 0; r < kRowsPerLane; r += 2) {
-        uint32_t mag2[2];
+    for (int r0 = 0; r0 < kRowsPerLane; r0 += kRowsPerLane / 2) {
+        uint32_t mine[kRowsPerLane / 4];
 #pragma unroll
-        for (int h = 0; h < 2; h++) {
-            uint32_t m[4];
+        for (int r = r0; r < r0 + kRowsPerLane / 2; r += 2) {
+            uint32_t mag2[2];
 #pragma unroll
-            for (int d = 0; d < 4; d++) {
-                m[d] = w[r + h][d] & 0x7FFF7FFFu;
-                if constexpr (COL)
-                    cmax[d] = pk_max_u16(cmax[d], m[d]);
+            for (int h = 0; h < 2; h++) {
+                uint32_t m[4];
+#pragma unroll
+                for (int d = 0; d < 4; d++) {
+                    m[d] = w[r + h][d] & 0x7FFF7FFFu;
+                    if constexpr (COL)
+                        cmax[d] = pk_max_u16(cmax[d], m[d]);
+                }
+                const uint32_t t = pk_max_u16(pk_max_u16(m[0], m[1]), pk_max_u16(m[2], m[3]));
+                const uint32_t lo = t & 0xFFFFu, hi = t >> 16;
+                mag2[h] = max_xor1(lo > hi ? lo : hi);
             }
-            const uint32_t t = pk_max_u16(pk_max_u16(m[0], m[1]), pk_max_u16(m[2], m[3]));
-            const uint32_t lo = t & 0xFFFFu, hi = t >> 16;
-            mag2[h] = max_xor1(lo > hi ? lo : hi);
+            if constexpr (ROW)
+                mine[(r - r0) >> 1] = nv_scale(odd ? mag2[1] : mag2[0], sg);
+            __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (ROW) {
-            const bool odd = l.cl & 1;
-            const uint32_t mine = nv_scale(odd ? mag2[1] : mag2[0], sg);
-            const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)mine, 0xB1, 0xF, 0xF, false);
-            const uint32_t sb0 = odd ? other : mine, sb1 = odd ? mine : other;
-            buf_store4<P::q_row>(rq, qoff + (uint32_t)(r * (a.K >> 1)),
-                                 encode8_fp4(w[r], st.inv[sb0]));
-            buf_store4<P::q_row>(rq, qoff + (uint32_t)((r + 1) * (a.K >> 1)),
-                                 encode8_fp4(w[r + 1], st.inv[sb1]));
-            if (!odd) {
-                st.srow[l.row + r][l.cl >> 1] = (uint8_t)sb0;
-                st.srow[l.row + r + 1][l.cl >> 1] = (uint8_t)sb1;
+            float inv0[kRowsPerLane / 4], inv1[kRowsPerLane / 4];
+#pragma unroll
+            for (int p = 0; p < kRowsPerLane / 4; p++) {
+                const uint32_t other =
+                    (uint32_t)__builtin_amdgcn_mov_dpp((int)mine[p], 0xB1, 0xF, 0xF, false);
+                const uint32_t sb0 = odd ? other : mine[p], sb1 = odd ? mine[p] : other;
+                inv0[p] = st.inv[sb0];
+                inv1[p] = st.inv[sb1];
+                if (!odd) {
+                    st.srow[l.row + r0 + 2 * p][l.cl >> 1] = (uint8_t)sb0;
+                    st.srow[l.row + r0 + 2 * p + 1][l.cl >> 1] = (uint8_t)sb1;
+                }
             }
+#pragma unroll
+            for (int p = 0; p < kRowsPerLane / 4; p++) {
+                const int r = r0 + 2 * p;
+                buf_store4<P::q_row>(rq, qoff + (uint32_t)(r * (a.K >> 1)),
+                                     encode8_fp4(w[r], inv0[p]));
+                buf_store4<P::q_row>(rq, qoff + (uint32_t)((r + 1) * (a.K >> 1)),
+                                     encode8_fp4(w[r + 1], inv1[p]));
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        // one row pair at a time: left alone, the scheduler interleaves the
-        // scale divisions of all rows and runs out of registers
-        __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (COL) {
         // The row pass expanded every element to fp32; without this empty,
@@ -376,22 +395,34 @@ __device__ __forceinline__ void nv_step(const Nv4Args &a, const NvLane &l,
             }
         const int p = g & 1;
         const int jr = 4 * p + l.wave;                       // logical 16-byte chunk
+        // the column codes in two batches of four, each batch's multipliers
+        // read from LDS together
         uint32_t sbs[kColsPerLane];
 #pragma unroll
-        for (int c = 0; c < kColsPerLane; c++) {
-            const int d = c >> 1, hi = c & 1;
-            const uint32_t mag = hi ? (cmax[d] >> 16) : (cmax[d] & 0xFFFFu);
-            const uint32_t sb = nv_scale(mag, sg);
-            const float inv = st.inv[sb];
-            uint32_t o[2];
+        for (int c0 = 0; c0 < kColsPerLane; c0 += kColsPerLane / 2) {
+            float inv[kColsPerLane / 2];
 #pragma unroll
-            for (int q = 0; q < 2; q++)
-                o[q] = hi ? encode8_fp4_col<1>(wc, q, d, inv) : encode8_fp4_col<0>(wc, q, d, inv);
-            const int kl = l.cl * kColsPerLane + c;
-            *reinterpret_cast<uint2 *>(&st.q[kl][16 * nv_chunk(kl, jr) + 8 * nv_half(kl, l.half)]) =
-                make_uint2(o[0], o[1]);
-            sbs[c] = sb;
-            __builtin_amdgcn_sched_barrier(0);
+            for (int c = c0; c < c0 + kColsPerLane / 2; c++) {
+                const int d = c >> 1, hi = c & 1;
+                sbs[c] = nv_scale(hi ? (cmax[d] >> 16) : (cmax[d] & 0xFFFFu), sg);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int c = c0; c < c0 + kColsPerLane / 2; c++)
+                inv[c - c0] = st.inv[sbs[c]];
+#pragma unroll
+            for (int c = c0; c < c0 + kColsPerLane / 2; c++) {
+                const int d = c >> 1, hi = c & 1;
+                const float v = inv[c - c0];
+                uint32_t o[2];
+#pragma unroll
+                for (int q = 0; q < 2; q++)
+                    o[q] = hi ? encode8_fp4_col<1>(wc, q, d, v) : encode8_fp4_col<0>(wc, q, d, v);
+                const int kl = l.cl * kColsPerLane + c;
+                *reinterpret_cast<uint2 *>(
+                    &st.q[kl][16 * nv_chunk(kl, jr) + 8 * nv_half(kl, l.half)]) = make_uint2(o[0], o[1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         stage_scales8(st.s, 8 * g + 2 * l.wave + l.half, l.cl, pack8(sbs));
     }

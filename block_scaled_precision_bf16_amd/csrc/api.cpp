@@ -68,6 +68,12 @@ int cast_op(int pre)
 // write one scale tile.
 int walk_group(int tm, int tk, int op, bool dbias, bool tiled)
 {
+    if (op == mxk::OP_PLAIN && !dbias) {
+        // the plain cast: balanced walks on two resident workgroups per CU
+        int len;
+        mxk::plan_walks(&tm, 1, tk, mxk::kTargetWorkgroups, tiled, &len);
+        return len;
+    }
     const int g = mxk::pick_group(tm, tk, mxk::target_workgroups(op, dbias));
     return tiled && g < 2 ? 2 : g;
 }
@@ -137,8 +143,10 @@ bool build_groups(const int64_t *rows, int G, int64_t K, int op, bool dbias, boo
     for (int g = 0; g < G; g++)
         tm[g] = tiles(rows[g], mxk::kTileM);
     const int per_cu = mxk::target_workgroups(op, dbias) == mxk::kTargetWorkgroupsFused ? 3 : 2;
-    group = mxk::pick_group_rounds(tm, G, tiles(K, mxk::kTileK), per_cu, tiled ? 2 : 1);
     gt = mxk::GroupTable{};
+    group = mxk::pick_group_rounds(tm, G, tiles(K, mxk::kTileK), per_cu, tiled ? 2 : 1);
+    for (int g = 0; g < G; g++)
+        gt.len[g] = group;
     gt.count = G;
     int64_t walks = 0, r = 0, sr = 0, sc = 0;
     for (int g = 0; g < G; g++) {
@@ -147,7 +155,7 @@ bool build_groups(const int64_t *rows, int G, int64_t K, int op, bool dbias, boo
         r += rows[g];
         gt.srow_off[g] = sr;
         gt.scol_off[g] = sc;
-        walks += (tiles(rows[g], mxk::kTileM) + group - 1) / group;
+        walks += (tm[g] + group - 1) / group;
         if (rows[g] > 0) {
             sr += (int64_t)scale_bytes(rows[g], K, tiled);
             sc += (int64_t)scale_bytes(K, rows[g], tiled);
@@ -177,8 +185,10 @@ bool build_nv_groups(const int64_t *rows, int G, int64_t K, mxk::GroupTable &gt,
     int tm[mxk::kMaxGroups];
     for (int g = 0; g < G; g++)
         tm[g] = tiles(rows[g], mxk::kTileM);
-    group = mxk::pick_group_rounds(tm, G, tiles(K, mxk::kTileK), 2, 1);
     gt = mxk::GroupTable{};
+    group = mxk::pick_group_rounds(tm, G, tiles(K, mxk::kTileK), 2, 1);
+    for (int g = 0; g < G; g++)
+        gt.len[g] = group;
     gt.count = G;
     int64_t walks = 0, r = 0;
     for (int g = 0; g < G; g++) {
@@ -186,7 +196,7 @@ bool build_nv_groups(const int64_t *rows, int G, int64_t K, mxk::GroupTable &gt,
         gt.row0[g] = r;
         gt.srow_off[g] = r * (K / 16);
         gt.scol_off[g] = K * (r / 16);
-        walks += (tiles(rows[g], mxk::kTileM) + group - 1) / group;
+        walks += (tm[g] + group - 1) / group;
         r += rows[g];
     }
     gt.walk0[G] = (int)walks;
@@ -257,7 +267,7 @@ static mx_status nvfp4_impl(bool two_d, const void *x, int64_t M, int64_t K, con
     a.sg_out = global_scale_out;
     a.tiles_k = tiles(K, mxk::kTileK);
     a.tiles_m = tiles(M, mxk::kTileM);
-    a.group = mxk::pick_group(a.tiles_m, a.tiles_k, mxk::kTargetWorkgroups);
+    mxk::plan_walks(&a.tiles_m, 1, a.tiles_k, mxk::kTargetWorkgroups, false, &a.group);
     a.groups_m = (a.tiles_m + a.group - 1) / a.group;
     return from_hip(mxk::launch_nvfp4(axis_mask, two_d, a, stream));
 }

@@ -86,6 +86,55 @@ inline int pick_group_rounds(const int *tiles_m, int groups, int tiles_k, int sl
     return best;
 }
 
+// Walk lengths for tensors (groups) of tiles_m[g] sub-tile rows, each cast
+// in walks over all tiles_k strips, on `slots` resident workgroups (used for
+// the plain MXFP8 and NVFP4 casts of one tensor; measured on the grouped
+// workloads, whose short groups gain more from many short walks that the
+// hardware hands out as workgroups finish, pick_group_rounds is better).  A
+// target length L (1 .. kMaxGroup; even with `even`, which the GEMM-ready
+// scale layout needs) gives group g the walks of balanced length
+// len[g] = ceil(t / ceil(t / L)) (t = tiles_m[g]; rounded up to even), so a
+// group's last walk is never much shorter than the rest.  Among the targets,
+// take the one with the fewest estimated steps, rounds x (longest walk + 1)
+// -- rounds of `slots` workgroups, the 1 a walk's fixed cost (its first load
+// and its scale flush) -- ties to the longer walks.  For the metric tensor
+// (one group of 128 sub-tile rows, 64 strips, 512 slots) this is 16, the
+// deepest walk that fills every slot once.
+inline void plan_walks(const int *tiles_m, int groups, int tiles_k, int slots, bool even,
+                       int *len)
+{
+    int best_L = 0, best_long = 0;
+    int64_t best_cost = 0;
+    for (int L = even ? 2 : 1; L <= kMaxGroup; L += even ? 2 : 1) {
+        int64_t walks = 0;
+        int longest = 0;
+        for (int g = 0; g < groups; g++) {
+            const int t = tiles_m[g];
+            if (t == 0)
+                continue;
+            int lg = (t + (t + L - 1) / L - 1) / ((t + L - 1) / L);
+            if (even)
+                lg += lg & 1;
+            walks += (t + lg - 1) / lg;
+            longest = lg > longest ? lg : longest;
+        }
+        const int64_t rounds = (walks * tiles_k + slots - 1) / slots;
+        const int64_t cost = rounds * (longest + 1);
+        if (best_L == 0 || cost < best_cost || (cost == best_cost && longest > best_long)) {
+            best_L = L;
+            best_cost = cost;
+            best_long = longest;
+        }
+    }
+    for (int g = 0; g < groups; g++) {
+        const int t = tiles_m[g];
+        int lg = t == 0 ? 1 : (t + (t + best_L - 1) / best_L - 1) / ((t + best_L - 1) / best_L);
+        if (even)
+            lg += lg & 1;
+        len[g] = lg;
+    }
+}
+
 struct MxArgs {
     const uint16_t *x;     // input (gated: [M][2N] with the linear half at lin_off)
     const uint16_t *aux;   // grad for dGELU, else unused
@@ -114,6 +163,7 @@ constexpr int kMaxGroups = 64;
 struct GroupTable {
     int count;                        // groups
     int walk0[kMaxGroups + 1];        // first walk of each group; walk0[count] = all walks
+    int len[kMaxGroups];              // sub-tiles per walk of each group
     int64_t row0[kMaxGroups + 1];     // first row of each group; row0[count] = M
     int64_t srow_off[kMaxGroups];     // byte offset of each group's row scales
     int64_t scol_off[kMaxGroups];     // byte offset of each group's column scales

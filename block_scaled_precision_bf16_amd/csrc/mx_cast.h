@@ -580,6 +580,7 @@ __global__ __launch_bounds__(kThreads, (min_blocks<OP, DBIAS>())) void mx_cast_g
     b.s_col = a.s_col ? a.s_col + gt.scol_off[g] : nullptr;
     b.partials = a.partials ? a.partials + (int64_t)gt.walk0[g] * a.K : nullptr;
     b.tiles_m = (int)((b.M + kTileM - 1) / kTileM);
+    b.group = gt.len[g];
     b.groups_m = gt.walk0[g + 1] - gt.walk0[g];
     mx_cast_walk<OP, FMT, ROW, COL, DBIAS>(b, rg - gt.walk0[g], tk);
 }

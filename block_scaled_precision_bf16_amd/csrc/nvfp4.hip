@@ -511,6 +511,7 @@ __global__ __launch_bounds__(kThreads, 2) void nvfp4_grouped_kernel(Nv4Args a, G
     b.q_col = a.q_col ? a.q_col + a.K * (r0 >> 1) : nullptr;
     b.s_col = a.s_col ? a.s_col + a.K * (r0 >> 4) : nullptr;
     b.tiles_m = (int)((b.M + kTileM - 1) / kTileM);
+    b.group = gt.len[g];
     b.groups_m = gt.walk0[g + 1] - gt.walk0[g];
     nv_walk<ROW, COL, TWO_D>(b, rg - gt.walk0[g], tk);
 }

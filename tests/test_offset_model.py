@@ -43,6 +43,18 @@ def pick_group(tiles_m, tiles_k, target=512):
     return g
 
 
+def plan_walk(t, tiles_k, slots=512, even=False):
+    """plan_walks (launch.h) for one tensor of t sub-tile rows."""
+    best = None
+    for L in range(2 if even else 1, MAX_GROUP + 1, 2 if even else 1):
+        lg = -(-t // -(-t // L))
+        lg += lg & 1 if even else 0
+        cost = -(-(-(-t // lg) * tiles_k) // slots) * (lg + 1)
+        if best is None or cost < best[0] or (cost == best[0] and lg > best[1]):
+            best = (cost, lg)
+    return best[1]
+
+
 class Desc:
     """make_rsrc(base, offset, total): bytes [offset, total) of an allocation,
     size 0 when offset >= total, at most MAX_RECORDS bytes."""
@@ -119,9 +131,12 @@ def mx_model(M, K, op="plain", tiled=False, ck=None):
     else:
         ldx, lin_off, ldg = K, 0, K
     tiles_m, tiles_k = -(-M // TILE_M), -(-K // TILE_K)
-    group = pick_group(tiles_m, tiles_k)
-    if tiled and group < 2:
-        group = 2
+    if op == "plain":
+        group = plan_walk(tiles_m, tiles_k, even=tiled)
+    else:
+        group = pick_group(tiles_m, tiles_k)
+        if tiled and group < 2:
+            group = 2
     groups_m = -(-tiles_m // group)
     t, wave, half, cl, row = lanes()
     r = np.arange(ROWS_PER_LANE)[:, None]
@@ -257,7 +272,7 @@ def scale_rows(ck, site, rs, k0, K, pitch, first, count, base_align=0):
 def nv_model(M, K, ck=None):
     ck = ck or Checker()
     tiles_m, tiles_k = -(-M // TILE_M), -(-K // TILE_K)
-    group = pick_group(tiles_m, tiles_k)
+    group = plan_walk(tiles_m, tiles_k)
     groups_m = -(-tiles_m // group)
     t, wave, half, cl, row = lanes()
     r = np.arange(ROWS_PER_LANE)[:, None]

@@ -288,13 +288,14 @@ static mx_status gated_grouped_impl(const void *grad, const void *x, int64_t N,
         return MX_ERR_NULL;
     const int op = bwd ? (act == MX_GATED_SWIGLU ? mxk::OP_DSWIGLU : mxk::OP_DGEGLU)
                        : (act == MX_GATED_SWIGLU ? mxk::OP_SWIGLU : mxk::OP_GEGLU);
+    if (!mx_shape_ok(16, N))   // N <= 2^23 before 2N is formed
+        return MX_ERR_SHAPE;
     const int64_t W = bwd ? 2 * N : N;
     const bool tiled = (axis_mask & MX_SCALE_TILED) != 0;
     mxk::GroupTable gt;
     int64_t M;
     int group;
-    if (!mx_shape_ok(16, N) || !build_groups(group_rows, G, W, op, false, tiled, gt, M, group) ||
-        !mx_shape_ok(M, 2 * N))
+    if (!build_groups(group_rows, G, W, op, false, tiled, gt, M, group) || !mx_shape_ok(M, 2 * N))
         return MX_ERR_SHAPE;
     if (!aligned(x, 16) || (bwd && !aligned(grad, 16)) ||
         (row && (!aligned(q_row, 16) || !aligned(s_row, 16))) ||

@@ -1,0 +1,374 @@
+// Host-only run of libmxcast's entry points (csrc/api.cpp) under
+// AddressSanitizer and UBSan, with the kernel launchers replaced by
+// recorders (launch_record.cpp).  Device pointers are distinct fake
+// addresses 4 TiB apart that are never dereferenced: validation only
+// compares and offsets them.
+//
+//   * malformed calls (NULL, enum, shape, alignment, workspace, overlap) at
+//     and beyond the size limits, including sizes whose products overflow
+//     int64: the expected status, and no launch;
+//   * valid calls at the size limits of every entry point: MX_OK, one launch,
+//     and a launch plan the kernels can run (tile counts, walk lengths within
+//     the LDS stage, grids below 2^31 workgroups, group tables that tile the
+//     stacked rows).
+//
+// Exit status 0 when every check holds; the sanitizers abort on the first
+// finding.
+#include <stdint.h>
+#include <stdio.h>
+
+#include "launch_record.h"
+#include "mxcast.h"
+
+using mxk::g_rec;
+
+static int failures = 0, checks = 0;
+
+#define CHECK(cond)                                                               \
+    do {                                                                          \
+        checks++;                                                                 \
+        if (!(cond)) {                                                            \
+            fprintf(stderr, "%s:%d: check failed: %s\n", __FILE__, __LINE__, #cond); \
+            failures++;                                                           \
+        }                                                                         \
+    } while (0)
+
+static const int64_t kDim = int64_t(1) << 23;
+static const int64_t kBig = INT64_MAX;
+
+// Fake device buffer i (4 TiB apart, 256-byte aligned) plus a byte offset.
+template <class T = uint8_t>
+static T *P(int i, uint64_t off = 0)
+{
+    return reinterpret_cast<T *>((uint64_t(i + 1) << 42) + off);
+}
+
+static int launches() { return g_rec.calls + g_rec.reduces; }
+
+// The call returns `want`; it launches something exactly when want is MX_OK.
+#define EXPECT(want, call)                                                          \
+    do {                                                                            \
+        const int before = launches();                                              \
+        const mx_status got = (call);                                               \
+        checks++;                                                                   \
+        if (got != (want)) {                                                        \
+            fprintf(stderr, "%s:%d: %s returned %d, expected %d\n", __FILE__, __LINE__, \
+                    #call, (int)got, (int)(want));                                  \
+            failures++;                                                             \
+        }                                                                           \
+        CHECK(((want) == MX_OK) == (launches() > before));                          \
+    } while (0)
+
+static int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// A single-tensor launch plan of an M x K quantised tensor.
+static void check_plan(int64_t M, int64_t K, int tiles_m, int tiles_k, int group, int groups_m,
+                       bool tiled)
+{
+    CHECK(tiles_m == ceil_div(M, mxk::kTileM));
+    CHECK(tiles_k == ceil_div(K, mxk::kTileK));
+    CHECK(group >= 1 && group <= mxk::kMaxGroup);
+    CHECK(!tiled || group % 2 == 0 || group >= tiles_m);
+    CHECK(groups_m == ceil_div(tiles_m, group));
+    CHECK((int64_t)groups_m * tiles_k <= INT32_MAX);
+}
+
+static void check_mx(int64_t M, int64_t K, bool tiled)
+{
+    const mxk::MxArgs &a = g_rec.mx;
+    CHECK(a.M == M && a.K == K);
+    CHECK((a.tiled != 0) == tiled);
+    check_plan(M, K, a.tiles_m, a.tiles_k, a.group, a.groups_m, tiled);
+}
+
+// A group table over G groups of the given row counts, stacked.
+static void check_groups(const int64_t *rows, int G, int walks_total)
+{
+    const mxk::GroupTable &gt = g_rec.gt;
+    CHECK(gt.count == G);
+    int64_t r = 0;
+    for (int g = 0; g < G; g++) {
+        CHECK(gt.row0[g] == r);
+        CHECK(gt.len[g] >= 1 && gt.len[g] <= mxk::kMaxGroup);
+        CHECK(gt.walk0[g + 1] - gt.walk0[g] == ceil_div(ceil_div(rows[g], mxk::kTileM), gt.len[g]));
+        r += rows[g];
+    }
+    CHECK(gt.row0[G] == r);
+    CHECK(gt.walk0[0] == 0 && gt.walk0[G] == walks_total);
+}
+
+static void mx_quantize_cases()
+{
+    const unsigned both = MX_ROWWISE | MX_COLWISE;
+    uint8_t *qr = P(2), *sr = P(3), *qc = P(4), *sc = P(5);
+    float *db = P<float>(6);
+    void *ws = P(7);
+    // valid: the metric shape, the size limits, every format / layout flag
+    EXPECT(MX_OK, mx_quantize(P(0), nullptr, 16384, 16384, both, 0, qr, sr, qc, sc, nullptr,
+                              nullptr, 0, 0));
+    check_mx(16384, 16384, false);
+    const int64_t shapes[][2] = {{kDim, 1 << 17}, {1 << 17, kDim}, {16, kDim}, {kDim, 8},
+                                 {16, 8}, {kDim, kDim >> 6}, {16400, 7176}};
+    for (auto &s : shapes) {
+        for (unsigned flags : {0u, (unsigned)MX_SCALE_TILED, MX_ELEM_E5M2 | MX_SCALE_ROUND_UP}) {
+            for (int fusion : {0, MX_FUSE_GELU, MX_FUSE_DGELU | MX_FUSE_DBIAS, MX_FUSE_DSILU}) {
+                const size_t need = mx_quantize_workspace_size(s[0], s[1], both | flags, fusion);
+                CHECK(((fusion & MX_FUSE_DBIAS) != 0) == (need > 0));
+                EXPECT(MX_OK, mx_quantize(P(0), P(1), s[0], s[1], both | flags, fusion, qr, sr, qc,
+                                          sc, db, ws, need, 0));
+                check_mx(s[0], s[1], flags & MX_SCALE_TILED);
+                if (need) {
+                    CHECK(g_rec.segments == g_rec.mx.groups_m);
+                    CHECK(need == (size_t)g_rec.mx.groups_m * (size_t)s[1] * 4);
+                    EXPECT(MX_ERR_WORKSPACE, mx_quantize(P(0), P(1), s[0], s[1], both | flags, fusion,
+                                                         qr, sr, qc, sc, db, ws, need - 4, 0));
+                }
+            }
+        }
+        EXPECT(MX_OK, mx_quantize(P(0), nullptr, s[0], s[1], MX_ROWWISE, 0, qr, sr, nullptr,
+                                  nullptr, nullptr, nullptr, 0, 0));
+        EXPECT(MX_OK, mx_quantize(P(0), nullptr, s[0], s[1], MX_COLWISE, 0, nullptr, nullptr, qc,
+                                  sc, nullptr, nullptr, 0, 0));
+    }
+    // shapes
+    const int64_t bad[][2] = {{kDim + 16, 8},  {16, kDim + 8}, {kDim, (1 << 17) + 8},
+                              {0, 8},          {16, 0},        {-16, 8},
+                              {16, -8},        {8, 8},         {16, 4},
+                              {kBig, kBig},    {kBig - 15, 8}, {16, kBig - 7},
+                              {INT64_MIN, 8},  {int64_t(1) << 62, int64_t(1) << 62}};
+    for (auto &s : bad) {
+        EXPECT(MX_ERR_SHAPE, mx_quantize(P(0), nullptr, s[0], s[1], both, 0, qr, sr, qc, sc,
+                                         nullptr, nullptr, 0, 0));
+        CHECK(mx_quantize_workspace_size(s[0], s[1], both, MX_FUSE_DBIAS) == 0);
+        CHECK(mx_scale_size(s[0], s[1], both) == 0 || (s[0] > 0 && s[1] > 0));
+    }
+    CHECK(mx_scale_size(kBig, 1, MX_ROWWISE) == 0 && mx_scale_size(1, kBig, MX_ROWWISE) == 0);
+    CHECK(mx_scale_size(kDim, kDim, MX_ROWWISE | MX_SCALE_TILED) ==
+          (size_t)(kDim / 32) * (size_t)(kDim / 256) * 256);
+    // enums, NULLs, alignment, overlap
+    EXPECT(MX_ERR_ENUM, mx_quantize(P(0), nullptr, 16, 8, 0, 0, qr, sr, qc, sc, nullptr, nullptr, 0, 0));
+    EXPECT(MX_ERR_ENUM, mx_quantize(P(0), nullptr, 16, 8, both | 32u, 0, qr, sr, qc, sc, nullptr,
+                                    nullptr, 0, 0));
+    EXPECT(MX_ERR_ENUM, mx_quantize(P(0), nullptr, 16, 8, both, 4, qr, sr, qc, sc, nullptr, nullptr, 0, 0));
+    EXPECT(MX_ERR_ENUM, mx_quantize(P(0), nullptr, 16, 8, both, 0x20, qr, sr, qc, sc, nullptr,
+                                    nullptr, 0, 0));
+    EXPECT(MX_ERR_ENUM, mx_quantize(P(0), nullptr, 16, 8, both, -1, qr, sr, qc, sc, nullptr, nullptr, 0, 0));
+    EXPECT(MX_ERR_NULL, mx_quantize(nullptr, nullptr, 16, 8, both, 0, qr, sr, qc, sc, nullptr,
+                                    nullptr, 0, 0));
+    EXPECT(MX_ERR_NULL, mx_quantize(P(0), nullptr, 16, 8, both, MX_FUSE_DSILU, qr, sr, qc, sc,
+                                    nullptr, nullptr, 0, 0));
+    EXPECT(MX_ERR_NULL, mx_quantize(P(0), nullptr, 16, 8, both, MX_FUSE_DBIAS, qr, sr, qc, sc,
+                                    nullptr, ws, 1 << 20, 0));
+    EXPECT(MX_ERR_NULL, mx_quantize(P(0), nullptr, 16, 8, both, 0, qr, nullptr, qc, sc, nullptr,
+                                    nullptr, 0, 0));
+    EXPECT(MX_ERR_ALIGN, mx_quantize(P(0, 2), nullptr, 16, 8, both, 0, qr, sr, qc, sc, nullptr,
+                                     nullptr, 0, 0));
+    EXPECT(MX_ERR_ALIGN, mx_quantize(P(0), nullptr, 16, 8, both, 0, qr, sr, qc, P(5, 8), nullptr,
+                                     nullptr, 0, 0));
+    EXPECT(MX_ERR_WORKSPACE, mx_quantize(P(0), nullptr, 16, 8, both, MX_FUSE_DBIAS, qr, sr, qc, sc,
+                                         db, nullptr, 0, 0));
+    // overlap: an output ending one byte into the input, outputs sharing a byte
+    const uint64_t n = uint64_t(kDim) << 17;
+    EXPECT(MX_ERR_ALIAS, mx_quantize(P(0), nullptr, kDim, 1 << 17, both, 0, P(0, 2 * n - 16), sr, qc,
+                                     sc, nullptr, nullptr, 0, 0));
+    EXPECT(MX_OK, mx_quantize(P(0), nullptr, kDim, 1 << 17, both, 0, P(0, 2 * n), sr, qc, sc,
+                              nullptr, nullptr, 0, 0));
+    EXPECT(MX_ERR_ALIAS, mx_quantize(P(0), nullptr, kDim, 1 << 17, both, 0, qr, P(2, n - 16), qc, sc,
+                                     nullptr, nullptr, 0, 0));
+    // the allocation-free variant: small dbias casts run, large ones are refused
+    EXPECT(MX_OK, mx_quantize_noalloc(P(0), nullptr, 16384, 16384, both, MX_FUSE_DBIAS, qr, sr, qc,
+                                      sc, db, 0));
+    CHECK(g_rec.segments * 16384 * 4 <= (int64_t)MX_NOALLOC_SCRATCH_BYTES);
+    EXPECT(MX_ERR_WORKSPACE, mx_quantize_noalloc(P(0), nullptr, 128, kDim, both, MX_FUSE_DBIAS, qr,
+                                                 sr, qc, sc, db, 0));
+    EXPECT(MX_OK, mx_quantize_noalloc(P(0), nullptr, kDim, 1 << 17, both, 0, qr, sr, qc, sc,
+                                      nullptr, 0));
+    EXPECT(MX_ERR_SHAPE, mx_quantize_noalloc(P(0), nullptr, kBig, kBig, both, MX_FUSE_DBIAS, qr, sr,
+                                             qc, sc, db, 0));
+}
+
+static void gated_cases()
+{
+    const unsigned both = MX_ROWWISE | MX_COLWISE;
+    uint8_t *qr = P(2), *sr = P(3), *qc = P(4), *sc = P(5);
+    const int64_t ok[][2] = {{128, kDim / 2}, {kDim, 8}, {16, 8}, {kDim, 1 << 16}, {8192, 4096}};
+    for (auto &s : ok) {
+        for (int act : {MX_GATED_SWIGLU, MX_GATED_GEGLU}) {
+            EXPECT(MX_OK, mx_quantize_gated(P(0), s[0], s[1], both, act, qr, sr, qc, sc, 0));
+            check_mx(s[0], s[1], false);
+            CHECK(g_rec.mx.ldx == 2 * s[1] && g_rec.mx.lin_off == s[1]);
+            EXPECT(MX_OK, mx_quantize_dgated(P(1), P(0), s[0], s[1], both | MX_SCALE_TILED, act, qr,
+                                             sr, qc, sc, 0));
+            check_mx(s[0], 2 * s[1], true);
+            CHECK(g_rec.mx.ldx == 2 * s[1] && g_rec.mx.ldg == s[1] && g_rec.mx.lin_off == s[1]);
+        }
+    }
+    const int64_t bad[][2] = {{128, kDim / 2 + 8}, {kDim + 16, 8}, {16, 4}, {16, kBig},
+                              {kBig, 8},           {16, kBig / 2 + 1}, {16, INT64_MIN},
+                              {16, -8},            {int64_t(1) << 62, int64_t(1) << 62}};
+    for (auto &s : bad) {
+        EXPECT(MX_ERR_SHAPE, mx_quantize_gated(P(0), s[0], s[1], both, MX_GATED_SWIGLU, qr, sr, qc, sc, 0));
+        EXPECT(MX_ERR_SHAPE, mx_quantize_dgated(P(1), P(0), s[0], s[1], both, MX_GATED_GEGLU, qr, sr,
+                                                qc, sc, 0));
+        if (s[1] > 0 && s[1] <= kDim / 2 && s[1] % 8 == 0)
+            continue;   // N itself is valid for the grouped casts below
+        const int64_t rows[2] = {16, 16};
+        EXPECT(MX_ERR_SHAPE, mx_quantize_gated_grouped(P(0), s[1], rows, 2, both, MX_GATED_SWIGLU, qr,
+                                                       sr, qc, sc, 0));
+        EXPECT(MX_ERR_SHAPE, mx_quantize_dgated_grouped(P(1), P(0), s[1], rows, 2, both,
+                                                        MX_GATED_SWIGLU, qr, sr, qc, sc, 0));
+    }
+    EXPECT(MX_ERR_ENUM, mx_quantize_gated(P(0), 16, 8, both, 0, qr, sr, qc, sc, 0));
+    EXPECT(MX_ERR_ENUM, mx_quantize_dgated(P(1), P(0), 16, 8, both, 3, qr, sr, qc, sc, 0));
+    EXPECT(MX_ERR_NULL, mx_quantize_dgated(nullptr, P(0), 16, 8, both, 1, qr, sr, qc, sc, 0));
+    EXPECT(MX_ERR_ALIAS, mx_quantize_dgated(P(1), P(0), 16, 8, both, 1, P(1, 16 * 8 * 2 - 16), sr, qc,
+                                            sc, 0));
+    // fused values alone
+    for (int op : {MX_FUSE_GELU, MX_FUSE_DGELU, MX_FUSE_DSILU, MX_OP_GATED | MX_GATED_SWIGLU,
+                   MX_OP_DGATED | MX_GATED_GEGLU}) {
+        EXPECT(MX_OK, mx_fused_values(P(0), P(1), 16, 8, op, P(2), 0));
+        EXPECT(MX_ERR_SHAPE, mx_fused_values(P(0), P(1), kBig, kBig, op, P(2), 0));
+        EXPECT(MX_ERR_SHAPE, mx_fused_values(P(0), P(1), 16, kBig / 2 + 1, op, P(2), 0));
+    }
+    EXPECT(MX_ERR_ENUM, mx_fused_values(P(0), P(1), 16, 8, 0, P(2), 0));
+    EXPECT(MX_ERR_ENUM, mx_fused_values(P(0), P(1), 16, 8, MX_OP_GATED | 3, P(2), 0));
+}
+
+static void grouped_cases()
+{
+    const unsigned both = MX_ROWWISE | MX_COLWISE;
+    uint8_t *qr = P(2), *sr = P(3), *qc = P(4), *sc = P(5);
+    float *db = P<float>(6);
+    void *ws = P(7);
+    // 64 groups filling 2^23 rows, some empty; the 8-expert MoE shape; one group
+    int64_t full[64];
+    for (int g = 0; g < 64; g++)
+        full[g] = g % 4 == 3 ? 0 : (kDim / 48) & ~int64_t(15);
+    const int64_t moe[8] = {1104, 3008, 1072, 6560, 1632, 608, 2256, 144};
+    const int64_t one[1] = {kDim};
+    struct Case { const int64_t *rows; int G; int64_t K; } cases[] = {
+        {full, 64, 1 << 17}, {moe, 8, 7168}, {one, 1, 1 << 17}, {moe, 8, 8}, {one, 1, 1 << 16},
+        {full, 64, 1 << 16}};
+    for (auto &c : cases) {
+        int64_t M = 0;
+        for (int g = 0; g < c.G; g++)
+            M += c.rows[g];
+        for (unsigned flags : {0u, (unsigned)MX_SCALE_TILED}) {
+            for (int fusion : {0, MX_FUSE_DBIAS, MX_FUSE_DGELU | MX_FUSE_DBIAS}) {
+                const size_t need = mx_quantize_grouped_workspace_size(c.K, c.rows, c.G, both | flags,
+                                                                      fusion);
+                EXPECT(MX_OK, mx_quantize_grouped(P(0), P(1), c.K, c.rows, c.G, both | flags, fusion,
+                                                  qr, sr, qc, sc, db, ws, need, 0));
+                CHECK(g_rec.kind == mxk::kLaunchMxGrouped && g_rec.mx.M == M);
+                check_groups(c.rows, c.G, g_rec.mx.groups_m);
+                CHECK((int64_t)g_rec.mx.groups_m * g_rec.mx.tiles_k <= INT32_MAX);
+                const size_t srow = mx_grouped_scale_size(c.K, c.rows, c.G, both | flags, 0);
+                const size_t scol = mx_grouped_scale_size(c.K, c.rows, c.G, both | flags, 1);
+                int64_t s0 = 0, s1 = 0;
+                for (int g = 0; g < c.G; g++) {
+                    CHECK(g_rec.gt.srow_off[g] == s0 && g_rec.gt.scol_off[g] == s1);
+                    s0 += (int64_t)mx_scale_size(c.rows[g], c.K, both | flags);
+                    s1 += (int64_t)mx_scale_size(c.K, c.rows[g], both | flags);
+                }
+                CHECK((size_t)s0 == srow && (size_t)s1 == scol);
+            }
+        }
+        // gated: x is [M][2N] with N = K (at most 2^40 elements, 2N <= 2^23)
+        const bool gated_ok = 2 * c.K <= kDim && M * 2 * c.K <= (int64_t(1) << 40);
+        EXPECT(gated_ok ? MX_OK : MX_ERR_SHAPE,
+               mx_quantize_gated_grouped(P(0), c.K, c.rows, c.G, both, MX_GATED_SWIGLU, qr, sr, qc,
+                                         sc, 0));
+        if (gated_ok)
+            check_groups(c.rows, c.G, g_rec.mx.groups_m);
+        EXPECT(gated_ok ? MX_OK : MX_ERR_SHAPE,
+               mx_quantize_dgated_grouped(P(1), P(0), c.K, c.rows, c.G, both | MX_SCALE_TILED,
+                                          MX_GATED_GEGLU, qr, sr, qc, sc, 0));
+        if (gated_ok) {
+            CHECK(g_rec.mx.K == 2 * c.K && g_rec.mx.tiled == 1);
+            check_groups(c.rows, c.G, g_rec.mx.groups_m);
+        }
+        if (c.K % 16 == 0) {
+            for (int two_d : {0, 1}) {
+                EXPECT(MX_OK, nvfp4_quantize_transpose_grouped(P(0), c.K, c.rows, c.G, P<float>(1), two_d,
+                                                               both, qr, sr, qc, sc, P<float>(6), 0));
+                check_groups(c.rows, c.G, g_rec.nv.groups_m);
+                CHECK((int64_t)g_rec.nv.groups_m * g_rec.nv.tiles_k <= INT32_MAX);
+            }
+            EXPECT(MX_OK, mx_absmax_bf16_grouped(P(0), c.K, c.rows, c.G, P<float>(1), 0));
+        }
+    }
+    // malformed group lists
+    const int64_t neg[2] = {16, -16}, odd[2] = {16, 8}, huge[2] = {16, kBig}, over[2] = {kDim, 16},
+                  empty[3] = {0, 0, 0}, wrap[3] = {kBig - 15, kBig - 15, 48};
+    struct Bad { const int64_t *rows; int G; } bads[] = {
+        {neg, 2}, {odd, 2}, {huge, 2}, {over, 2}, {empty, 3}, {wrap, 3}, {full, 65}, {full, 0},
+        {full, -1}, {nullptr, 2}};
+    for (auto &b : bads) {
+        const mx_status want = b.rows ? MX_ERR_SHAPE : MX_ERR_NULL;
+        EXPECT(want, mx_quantize_grouped(P(0), nullptr, 256, b.rows, b.G, both, 0, qr, sr, qc, sc,
+                                         nullptr, nullptr, 0, 0));
+        EXPECT(want, mx_quantize_gated_grouped(P(0), 256, b.rows, b.G, both, 1, qr, sr, qc, sc, 0));
+        EXPECT(want, nvfp4_quantize_transpose_grouped(P(0), 256, b.rows, b.G, P<float>(1), 0, both,
+                                                      qr, sr, qc, sc, nullptr, 0));
+        EXPECT(want, mx_absmax_bf16_grouped(P(0), 256, b.rows, b.G, P<float>(1), 0));
+        CHECK(mx_quantize_grouped_workspace_size(256, b.rows, b.G, both, MX_FUSE_DBIAS) == 0);
+        CHECK(mx_grouped_scale_size(256, b.rows, b.G, both, 0) == 0);
+    }
+    for (int64_t K : {kBig, int64_t(0), int64_t(-16), kDim + 16, INT64_MIN}) {
+        EXPECT(MX_ERR_SHAPE, mx_quantize_grouped(P(0), nullptr, K, moe, 8, both, 0, qr, sr, qc, sc,
+                                                 nullptr, nullptr, 0, 0));
+        EXPECT(MX_ERR_SHAPE, nvfp4_quantize_transpose_grouped(P(0), K, moe, 8, P<float>(1), 0, both,
+                                                              qr, sr, qc, sc, nullptr, 0));
+        EXPECT(MX_ERR_SHAPE, mx_absmax_bf16_grouped(P(0), K, moe, 8, P<float>(1), 0));
+        CHECK(mx_grouped_scale_size(K, moe, 8, both, 1) == 0);
+    }
+    EXPECT(MX_ERR_ENUM, nvfp4_quantize_transpose_grouped(P(0), 256, moe, 8, P<float>(1), 2, both, qr,
+                                                         sr, qc, sc, nullptr, 0));
+}
+
+static void nvfp4_cases()
+{
+    const unsigned both = MX_ROWWISE | MX_COLWISE;
+    uint8_t *qr = P(2), *sr = P(3), *qc = P(4), *sc = P(5);
+    const int64_t ok[][2] = {{16384, 16384}, {kDim, 1 << 17}, {16, kDim}, {kDim, 16}, {16400, 7168}};
+    for (auto &s : ok) {
+        for (int two_d : {0, 1}) {
+            EXPECT(MX_OK, (two_d ? nvfp4_quantize_transpose_2d : nvfp4_quantize_transpose)(
+                              P(0), s[0], s[1], P<float>(1), both, qr, sr, qc, sc, P<float>(6), 0));
+            const mxk::Nv4Args &a = g_rec.nv;
+            CHECK(a.M == s[0] && a.K == s[1] && g_rec.two_d == (two_d != 0));
+            check_plan(s[0], s[1], a.tiles_m, a.tiles_k, a.group, a.groups_m, false);
+        }
+        EXPECT(MX_OK, mx_absmax_bf16(P(0), s[0] * s[1], P<float>(1), 0));
+    }
+    const int64_t bad[][2] = {{8, 16}, {16, 8}, {kDim + 16, 16}, {kDim, (1 << 17) + 16}, {kBig, kBig},
+                              {-16, 16}, {16, INT64_MIN}, {int64_t(1) << 62, int64_t(1) << 62}};
+    for (auto &s : bad)
+        for (int two_d : {0, 1})
+            EXPECT(MX_ERR_SHAPE, (two_d ? nvfp4_quantize_transpose_2d : nvfp4_quantize_transpose)(
+                                     P(0), s[0], s[1], P<float>(1), both, qr, sr, qc, sc, nullptr, 0));
+    EXPECT(MX_ERR_ENUM, nvfp4_quantize_transpose(P(0), 16, 16, P<float>(1), 4, qr, sr, qc, sc, nullptr, 0));
+    EXPECT(MX_ERR_NULL, nvfp4_quantize_transpose(P(0), 16, 16, nullptr, both, qr, sr, qc, sc, nullptr, 0));
+    EXPECT(MX_ERR_ALIGN, nvfp4_quantize_transpose(P(0), 16, 16, P<float>(1, 2), both, qr, sr, qc, sc,
+                                                  nullptr, 0));
+    EXPECT(MX_ERR_ALIAS, nvfp4_quantize_transpose(P(0), 16, 16, P<float>(1), both, qr, sr, qc, sc,
+                                                  P<float>(1), 0));
+    for (int64_t n : {int64_t(0), int64_t(-1), kBig, INT64_MIN, (int64_t(1) << 40) + 1})
+        EXPECT(MX_ERR_SHAPE, mx_absmax_bf16(P(0), n, P<float>(1), 0));
+    EXPECT(MX_OK, mx_absmax_bf16(P(0), 7, P<float>(1), 0));   // any count of elements
+    EXPECT(MX_OK, mx_absmax_bf16(P(0), int64_t(1) << 40, P<float>(1), 0));
+    EXPECT(MX_ERR_ALIAS, mx_absmax_bf16(P(0), 1024, P<float>(0, 2044), 0));
+}
+
+int main()
+{
+    CHECK(mx_abi_version() == MXCAST_ABI_VERSION);
+    for (int s : {-1, 0, 1, 8, 9, INT32_MAX, INT32_MIN})
+        CHECK(mx_status_str(s) != nullptr);
+    mx_quantize_cases();
+    gated_cases();
+    grouped_cases();
+    nvfp4_cases();
+    printf("%d checks, %d failed\n", checks, failures);
+    return failures ? 1 : 0;
+}

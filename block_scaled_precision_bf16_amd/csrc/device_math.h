@@ -185,6 +185,39 @@ __device__ __forceinline__ float div6_bf16(float b)
     return __builtin_fmaf(r, c, q0);
 }
 
+// Division by a divisor s > 0 that is fixed for a whole tensor, without the
+// per-call IEEE sequence (two scale steps, a reciprocal estimate, five FMAs
+// and a fix-up).  Prepared once: k = 2^64 for s < 2^-90, else 1; s' = s k
+// (exact) and y = fl32(1 / s') by the IEEE division.  Per call, with q' = q k
+// (exact): q0 = q' y, then twice q_i+1 = q_i + (q' - s' q_i) y, the residual
+// exact in the FMA.  The final step from a quotient within an ulp and a
+// correctly rounded reciprocal gives the correctly rounded quotient
+// (Markstein's theorem) wherever the residuals stay normal: for every q whose
+// quotient q / s is at least 2^-10 (the smallest value the E4M3 scale can
+// take), since s' >= 2^-90 bounds the residuals from below.  The device
+// qualification tests compare it with the IEEE quotient over every divisor
+// mantissa at both ends of the range and every subnormal divisor.
+struct DivBy {
+    float s, y, k;
+};
+
+__device__ __forceinline__ DivBy div_by_prepare(float s)
+{
+    DivBy d;
+    d.k = s < 0x1p-90f ? 0x1p64f : 1.0f;
+    d.s = s * d.k;
+    d.y = 1.0f / d.s;
+    return d;
+}
+
+__device__ __forceinline__ float div_by(float q, const DivBy &d)
+{
+    const float qk = q * d.k;
+    const float q0 = qk * d.y;
+    const float q1 = __builtin_fmaf(__builtin_fmaf(-d.s, q0, qk), d.y, q0);
+    return __builtin_fmaf(__builtin_fmaf(-d.s, q1, qk), d.y, q1);
+}
+
 // E4M3 code (no NaN) -> its exact fp32 value.
 __device__ __forceinline__ float e4m3_value(uint32_t c)
 {

@@ -27,11 +27,13 @@
 namespace mxk {
 
 // Scale byte of one NVFP4 block whose largest magnitude has bf16 pattern
-// mag: E4M3(fl32(fl32(b / 6) / S_g)); the division by S_g is IEEE, the E4M3
-// rounding the saturating hardware convert (inputs are finite here).
-__device__ __forceinline__ uint32_t nv_scale(uint32_t mag, float sg)
+// mag: E4M3(fl32(fl32(b / 6) / S_g)).  The division by S_g gives the IEEE
+// quotient wherever the code can be non-zero (div_by, prepared once per
+// workgroup); the E4M3 rounding is the saturating hardware convert (inputs
+// are finite here).
+__device__ __forceinline__ uint32_t nv_scale(uint32_t mag, const DivBy &sg)
 {
-    const float sq = div6_bf16(f32_bits(mag << 16)) / sg;
+    const float sq = div_by(div6_bf16(f32_bits(mag << 16)), sg);
     return e4m3x2<false>(sq, 0.0f, 0u) & 0xFFu;
 }
 
@@ -255,7 +257,7 @@ __device__ __forceinline__ void nv_flush_srow(const Nv4Args &a, const NvStage &s
 template <bool ROW, bool COL>
 __device__ __forceinline__ void nv_step_2d(const Nv4Args &a, const NvLane &l,
                                            const uint32_t (&w)[kRowsPerLane][4], NvStage &st,
-                                           float sg, rsrc_t rq, uint32_t qoff, int g)
+                                           const DivBy &sg, rsrc_t rq, uint32_t qoff, int g)
 {
     using P = NvPolicy<ROW, COL>;
     uint32_t t = 0;
@@ -308,7 +310,7 @@ __device__ __forceinline__ void nv_step_2d(const Nv4Args &a, const NvLane &l,
 template <bool ROW, bool COL, bool TWO_D, int FLUSH>
 __device__ __forceinline__ void nv_step(const Nv4Args &a, const NvLane &l,
                                         const uint32_t (&w)[kRowsPerLane][4], NvStage &st,
-                                        float sg, int tm, int tk, int g)
+                                        const DivBy &sg, int tm, int tk, int g)
 {
     using P = NvPolicy<ROW, COL>;
     const bool live = nv_live(a, l, tm, tk);
@@ -450,11 +452,12 @@ __device__ __forceinline__ void nv_walk(const Nv4Args &a, int rg, int tk)
     const int n = (a.tiles_m - tm0) < a.group ? (a.tiles_m - tm0) : a.group;
     const NvLane l = nv_lane();
 
-    const float sg = nv_global_scale(*a.amax);
+    const float sgf = nv_global_scale(*a.amax);
+    const DivBy sg = div_by_prepare(sgf);
 
     __shared__ NvStage st;
     if (threadIdx.x < 128)
-        st.inv[threadIdx.x] = nv_inverse(threadIdx.x, sg);
+        st.inv[threadIdx.x] = nv_inverse(threadIdx.x, sgf);
     __syncthreads();
     uint32_t wa[kRowsPerLane][4], wb[kRowsPerLane][4];
     const int past = a.tiles_m;   // a sub-tile row outside the tensor: reads as zeros

@@ -106,6 +106,63 @@ __global__ void div6_kernel(uint32_t *out)
     out[i] = __float_as_uint(div6_bf16(__uint_as_float((uint32_t)i << 16)));
 }
 
+// div_by (division by a tensor-wide divisor) against the IEEE division.
+// Thread i takes the divisor s = fp32 pattern first + i and every dividend
+// the NVFP4 scale chain can give it: q = div6_bf16(b) for b = 0 and for every
+// finite bf16 b whose quotient q / s lies in about [2^-12, 2^12].  Counts
+// (summed over the launch): [0] quotients that differ from the IEEE q / s
+// where that is at least 2^-10, [1] pairs whose E4M3 scale codes differ,
+// [2] pairs tested.
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        v += (uint32_t)__shfl_xor((int)v, off, 64);
+    return v;
+}
+
+__global__ void divby_kernel(uint32_t first, int64_t n, unsigned long long *counts)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t bad_q = 0, bad_code = 0, tested = 0;
+    if (i < n) {
+        const float s = in_bits((uint64_t)first + i);
+        const DivBy d = div_by_prepare(s);
+        // b = 6 q spans [6 s 2^-12, 6 s 2^12]; positive bf16 patterns are
+        // ordered like their values (an overflowing bound clamps to the
+        // largest finite pattern)
+        const uint32_t lo = __float_as_uint(6.0f * s * 0x1p-12f) >> 16;
+        uint32_t hi = (__float_as_uint(6.0f * s * 0x1p12f) >> 16) + 1u;
+        hi = hi > 0x7F7Fu ? 0x7F7Fu : hi;
+        for (uint32_t p = lo == 0u ? 0u : lo - 1u; p <= hi; p++) {
+            const uint32_t bp = p < lo ? 0u : p;   // the first pass takes b = 0
+            const float q = div6_bf16(__uint_as_float(bp << 16));
+            const float fast = div_by(q, d), ieee = q / s;
+            bad_q += (__float_as_uint(fast) != __float_as_uint(ieee) && ieee >= 0x1p-10f) ? 1u : 0u;
+            bad_code += ((e4m3x2<false>(fast, 0.0f, 0u) & 0xFFu) !=
+                         (e4m3x2<false>(ieee, 0.0f, 0u) & 0xFFu)) ? 1u : 0u;
+            tested++;
+        }
+    }
+    bad_q = wave_sum(bad_q);
+    bad_code = wave_sum(bad_code);
+    tested = wave_sum(tested);
+    if ((threadIdx.x & 63) == 0) {
+        atomicAdd(&counts[0], (unsigned long long)bad_q);
+        atomicAdd(&counts[1], (unsigned long long)bad_code);
+        atomicAdd(&counts[2], (unsigned long long)tested);
+    }
+}
+
+// out[i] = div_by(q[i], div_by_prepare(s[i])), for a CPU comparison.
+__global__ void divby_values_kernel(const float *s, const float *q, int64_t n, float *out)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n)
+        return;
+    out[i] = div_by(q[i], div_by_prepare(s[i]));
+}
+
 // One wave multiplies two block-scaled operands the way a GEMM on gfx950
 // consumes the cast's outputs: C[32][32] = sum over k of A[i][k] * B[k][j] by
 // K / 64 steps of v_mfma_scale_f32_32x32x64_f8f6f4.
@@ -226,6 +283,25 @@ int qual_div6(uint32_t *out, hipStream_t s)
     if (!out)
         return 1;
     hipLaunchKernelGGL(div6_kernel, dim3(blocks_for(0x7F80)), dim3(256), 0, s, out);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// Divisors first .. first + n - 1 (patterns of positive finite floats);
+// counts: device, 3 zeroed uint64.
+int qual_divby(uint32_t first, int64_t n, unsigned long long *counts, hipStream_t s)
+{
+    if (!counts || n <= 0 || (uint64_t)first + (uint64_t)n > 0x7F800000ull || first == 0u)
+        return 1;
+    hipLaunchKernelGGL(divby_kernel, dim3(blocks_for(n)), dim3(256), 0, s, first, n, counts);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// s, q, out: device arrays of n floats (s > 0 finite).
+int qual_divby_values(const float *sv, const float *q, int64_t n, float *out, hipStream_t s)
+{
+    if (!sv || !q || !out || n <= 0)
+        return 1;
+    hipLaunchKernelGGL(divby_values_kernel, dim3(blocks_for(n)), dim3(256), 0, s, sv, q, n, out);
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 

@@ -20,6 +20,14 @@ oracle's C checkers compare every result:
                                            correctly rounded 1/d
   div6_bf16    b / 6 by multiply + FMA     every finite non-negative bf16:
                                            the correctly rounded b / 6
+  div_by       q / s from a prepared       every divisor mantissa at six
+               reciprocal and two FMA      exponents (every subnormal divisor,
+               residual steps              both sides of the 2^-90 switch, the
+                                           largest tensor scales), with every
+                                           dividend b / 6 of the NVFP4 scale
+                                           chain: the IEEE quotient wherever
+                                           it is at least 2^-10, and the same
+                                           E4M3 scale code everywhere
 """
 import ctypes
 import os
@@ -50,6 +58,10 @@ def Q():
                       ctypes.c_void_p]
     L.qual_exp.restype = ctypes.c_int
     L.qual_exp.argtypes = [ctypes.c_uint32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    L.qual_divby.restype = ctypes.c_int
+    L.qual_divby.argtypes = [ctypes.c_uint32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    L.qual_divby_values.restype = ctypes.c_int
+    L.qual_divby_values.argtypes = [ctypes.c_void_p] * 2 + [ctypes.c_int64] + [ctypes.c_void_p] * 2
     for name in ("qual_rcp_1_2", "qual_div6"):
         getattr(L, name).restype = ctypes.c_int
         getattr(L, name).argtypes = [ctypes.c_void_p, ctypes.c_void_p]
@@ -116,3 +128,48 @@ def test_div6_on_every_bf16(Q):
     want = (b / np.float32(6.0)).view(np.uint32)          # IEEE fp32 division
     bad = np.flatnonzero(got != want)
     assert bad.size == 0, (bad.size, [hex(int(i)) for i in bad[:4]])
+
+
+# divisor exponent ranges: every subnormal divisor (the rescaled path), the
+# binade above the smallest normal, the two binades around the 2^-90 switch,
+# [1, 2), and the binade of the largest tensor scales (bf16 max / 2688 <
+# 2^117); 2^23 divisors each
+DIVISORS = [(1, (1 << 23) - 1), (1 << 23, 1 << 23), (36 << 23, 1 << 23), (37 << 23, 1 << 23),
+            (127 << 23, 1 << 23), (243 << 23, 1 << 23)]
+
+
+@pytest.mark.parametrize("first,n", DIVISORS, ids=[f"{f:#010x}" for f, _ in DIVISORS])
+def test_division_by_tensor_scale(Q, first, n):
+    counts = torch.zeros(3, dtype=torch.int64, device="cuda")
+    for c0 in range(first, first + n, 1 << 21):       # launches of 2^21 divisors
+        cn = min(1 << 21, first + n - c0)
+        assert Q.qual_divby(c0, cn, ctypes.c_void_p(counts.data_ptr()), stream()) == 0
+    bad_q, bad_code, tested = (int(v) for v in counts.cpu())
+    assert tested > 1000 * n
+    assert bad_q == 0 and bad_code == 0, (bad_q, bad_code, tested)
+
+
+def test_division_by_tensor_scale_against_host():
+    """The same routine on random (divisor, bf16 dividend) pairs across the
+    whole range, compared with numpy's IEEE float32 division on the host."""
+    L = ctypes.CDLL(QLIB)
+    L.qual_divby_values.restype = ctypes.c_int
+    L.qual_divby_values.argtypes = [ctypes.c_void_p] * 2 + [ctypes.c_int64] + [ctypes.c_void_p] * 2
+    rng = np.random.default_rng(41)
+    n = 1 << 22
+    s = rng.integers(1, 0x7B000000, size=n, dtype=np.uint32).view(np.float32)   # up to ~2^119
+    b = (rng.integers(0, 0x7F80, size=n, dtype=np.uint32) << 16).view(np.float32)
+    q = (b / np.float32(6.0)).astype(np.float32)
+    with np.errstate(over="ignore", under="ignore"):
+        want = (q / s).astype(np.float32)
+    sd, qd = torch.from_numpy(s).cuda(), torch.from_numpy(q).cuda()
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    assert L.qual_divby_values(ctypes.c_void_p(sd.data_ptr()), ctypes.c_void_p(qd.data_ptr()), n,
+                               ctypes.c_void_p(out.data_ptr()), stream()) == 0
+    got = out.cpu().numpy()
+    # the chain's quotients: at least 2^-10 (else the scale code is 0) and at
+    # most a few thousand (the block amax never exceeds the tensor amax)
+    dom = (np.abs(want) >= np.float32(2.0 ** -10)) & (np.abs(want) <= np.float32(2.0 ** 20))
+    assert dom.sum() > n // 16
+    differ = (got.view(np.uint32) != want.view(np.uint32)) & dom
+    assert not differ.any(), (s[differ][:4], q[differ][:4], got[differ][:4], want[differ][:4])

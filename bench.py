@@ -109,22 +109,23 @@ def measured_traffic():
     return int(m.group(1))
 
 
-def spin_calibrate(stream):
-    """Clock cycles of torch's spin kernel per microsecond on this GPU."""
+def gpu_us_per_call(fn, stream, calls=4):
+    """Mean GPU time of `calls` back-to-back calls of fn (microseconds)."""
     import torch
-    torch.cuda._sleep(1 << 20)   # first launch loads the kernel
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record(stream)
-    torch.cuda._sleep(1 << 22)
+    for _ in range(calls):
+        fn()
     e.record(stream)
     torch.cuda.synchronize()
-    return (1 << 22) / max(s.elapsed_time(e) * 1e3, 1.0)
+    return max(s.elapsed_time(e) * 1e3 / calls, 1.0)
 
 
-def queue_ahead(cycles_per_us, launches):
-    """Occupy the stream for ~100 us per launch to be queued (at least 2 ms)."""
-    import torch
-    torch.cuda._sleep(int(cycles_per_us * max(2000, 100 * launches)))
+def lead_calls(us_per_call, timed, at_least):
+    """Untimed calls to queue right before `timed` timed calls: at least
+    2.5 ms of GPU work, and 100 us per timed call (more than the host needs
+    to queue one), so the host stays ahead of the GPU throughout."""
+    return max(at_least, int(max(2500.0, 100.0 * timed) / us_per_call) + 1)
 
 
 def cpu_model():
@@ -279,18 +280,19 @@ def main():
                 step()
             prewarm += 8
             torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    step_us = gpu_us_per_call(step, stream)
 
-    # The timed launches are queued behind a short spin kernel, so that the
-    # host is ahead of the GPU and a host-side pause (the binding's argument
-    # checks, the interpreter) never lands between a launch's two events.
-    spin_cycles = spin_calibrate(stream)
+    # The timed launches follow, with no pause, a run of untimed launches of
+    # the same step (the warm-up) long enough for the host to queue all of
+    # them first: the GPU stays busy at its working clocks and no host-side
+    # pause (the binding's argument checks, the interpreter) lands between a
+    # launch's two events.
+    lead = lead_calls(step_us, args.steps, args.warmup)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
-    queue_ahead(spin_cycles, args.steps)
+    for _ in range(lead):
+        step()
     for i in range(args.steps):
         starts[i].record(stream)
         step()
@@ -331,13 +333,13 @@ def main():
         # the absmax pre-pass of the NVFP4 casts: a pure read of the input,
         # timed like the cast (back to back, events per launch)
         name, fn, nbytes = pre_pass
-        for _ in range(5):
-            fn()
         n_pre = max(20, args.steps)
+        pre_lead = lead_calls(gpu_us_per_call(fn, stream, 8), n_pre, 5)
         ps = [torch.cuda.Event(enable_timing=True) for _ in range(n_pre)]
         pe = [torch.cuda.Event(enable_timing=True) for _ in range(n_pre)]
         torch.cuda.synchronize()
-        queue_ahead(spin_cycles, n_pre)
+        for _ in range(pre_lead):
+            fn()
         for i in range(n_pre):
             ps[i].record(stream)
             fn()
@@ -370,9 +372,9 @@ def main():
                           "cold_mean": round(sum(cold) / len(cold), 2) if cold else None,
                           "cold_median": pct(cold, 0.5), "cold_p10": pct(cold, 0.1),
                           "cold_p90": pct(cold, 0.9), "cold_samples": len(cold)},
-        "timing": {"warm": "back-to-back launches queued behind a spin kernel (no host gaps), HIP events per launch on the cast's stream",
+        "timing": {"warm": "back-to-back launches right after untimed launches of the same step that keep the GPU busy while the host queues them, HIP events per launch on the cast's stream",
                    "cold": "1 GiB write then 1 GiB read of other buffers before each sample",
-                   "prewarm_launches": prewarm},
+                   "prewarm_launches": prewarm, "lead_launches": lead},
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "algorithmic_bytes": alg_bytes,
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,

@@ -444,6 +444,49 @@ __device__ __forceinline__ void nv_step(const Nv4Args &a, const NvLane &l,
 // The global scale of a tensor with amax A: A / (448 * 6), 1 for A = 0.
 __device__ __forceinline__ float nv_global_scale(float A) { return A == 0.0f ? 1.0f : A / 2688.0f; }
 
+// A tensor whose amax is not finite (it holds an Inf or a NaN) has no usable
+// global scale: the walk's sub-tiles get scale bytes 0x7F (the E4M3 NaN) and
+// element codes 0, in 8-byte pieces of element rows and single scale bytes,
+// every piece outside the tensor dropped by its descriptor.
+template <bool ROW, bool COL>
+__device__ void nv_fill_nonfinite(const Nv4Args &a, int tm0, int n, int tk)
+{
+    const int t = (int)threadIdx.x;
+    const int64_t k0 = (int64_t)tk * kTileK;
+    const uint2 zero = make_uint2(0u, 0u);
+    for (int g = 0; g < n; g++) {
+        const int64_t m0 = (int64_t)(tm0 + g) * kTileM;
+        if constexpr (ROW) {
+            // 128 rows x (128 element bytes, 16 scale bytes)
+            const int64_t lq = a.K >> 1, ls = a.K >> 4;
+            const rsrc_t rq = make_rsrc(a.q_row, m0 * lq + (k0 >> 1), a.M * lq);
+            const rsrc_t rs = make_rsrc(a.s_row, m0 * ls + (k0 >> 4), a.M * ls);
+            for (int i = t; i < kTileM * 16; i += kThreads) {
+                const int r = i >> 4, p = i & 15;
+                const bool row_ok = m0 + r < a.M;
+                buf_store8<0>(rq, row_ok && (k0 >> 1) + 8 * p < lq ? (uint32_t)(r * lq + 8 * p) : kDead,
+                              zero);
+                buf_store1<0>(rs, row_ok && (k0 >> 4) + p < ls ? (uint32_t)(r * ls + p) : kDead,
+                              (uint8_t)0x7F);
+            }
+        }
+        if constexpr (COL) {
+            // 256 transposed rows x (64 element bytes, 8 scale bytes)
+            const int64_t lq = a.M >> 1, ls = a.M >> 4;
+            const rsrc_t rq = make_rsrc(a.q_col, k0 * lq + (m0 >> 1), a.K * lq);
+            const rsrc_t rs = make_rsrc(a.s_col, k0 * ls + (m0 >> 4), a.K * ls);
+            for (int i = t; i < kTileK * 8; i += kThreads) {
+                const int kr = i >> 3, p = i & 7;
+                const bool row_ok = k0 + kr < a.K;
+                buf_store8<0>(rq, row_ok && (m0 >> 1) + 8 * p < lq ? (uint32_t)(kr * lq + 8 * p) : kDead,
+                              zero);
+                buf_store1<0>(rs, row_ok && (m0 >> 4) + p < ls ? (uint32_t)(kr * ls + p) : kDead,
+                              (uint8_t)0x7F);
+            }
+        }
+    }
+}
+
 template <bool ROW, bool COL, bool TWO_D>
 __device__ __forceinline__ void nv_walk(const Nv4Args &a, int rg, int tk)
 {
@@ -453,6 +496,10 @@ __device__ __forceinline__ void nv_walk(const Nv4Args &a, int rg, int tk)
     const NvLane l = nv_lane();
 
     const float sgf = nv_global_scale(*a.amax);
+    if (!__builtin_isfinite(sgf)) {   // uniform: every thread of the workgroup returns
+        nv_fill_nonfinite<ROW, COL>(a, tm0, n, tk);
+        return;
+    }
     const DivBy sg = div_by_prepare(sgf);
 
     __shared__ NvStage st;

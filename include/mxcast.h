@@ -328,8 +328,9 @@ mx_status mx_fused_values(const void *x, const void *grad, int64_t M, int64_t K,
 
 /*
  * Tensor absmax for NVFP4: *amax = max |x_i| over n bf16 elements, as fp32
- * (exact).  amax is a device pointer to one float; it is first cleared and
- * then combined with integer atomic max, so the result does not depend on
+ * (exact); a NaN when an element is NaN, else +Inf when one is infinite.
+ * amax is a device pointer to one float; it is first cleared and then
+ * combined with integer atomic max, so the result does not depend on
  * scheduling.  n > 0, n <= 2^40, x 16-byte aligned.
  */
 mx_status mx_absmax_bf16(const void *x, int64_t n, float *amax, hipStream_t stream);
@@ -338,7 +339,12 @@ mx_status mx_absmax_bf16(const void *x, int64_t n, float *amax, hipStream_t stre
  * NVFP4 quantize-transpose of x[M][K] (bf16), block size 16, M and K positive
  * multiples of 16, each <= 2^23, M*K <= 2^40.
  *   amax     device, one fp32: the tensor absmax the global scale is built
- *            from (e.g. from mx_absmax_bf16 on the same stream)
+ *            from, as mx_absmax_bf16 computes it (on the same stream).  With
+ *            a NaN or infinite amax (a tensor holding a NaN or an Inf) there
+ *            is no usable global scale: every scale byte is 0x7F (the E4M3
+ *            NaN), every element code 0, and S_g = amax / 2688 stays NaN or
+ *            Inf.  An amax other than the tensor's absmax is outside the
+ *            contract.
  *   q_row, s_row  packed E2M1 [M][K/2] (element 2j in the low nibble of byte
  *            j), E4M3 [M][K/16]                     (iff MX_ROWWISE)
  *   q_col, s_col  the same for the transpose: [K][M/2], [K][M/16]

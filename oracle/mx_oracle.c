@@ -36,7 +36,11 @@
  *       in the "MXFP8 generic quantize kernel" and gated tables) use the
  *       derivative of the same forward sequences, in the order written in
  *       orc_preop() and orc_gated_bwd().
- *   R6  NVFP4 per the chain in nvfp4_block().
+ *   R6  NVFP4 per the chain in nvfp4_block(), with the tensor amax A the
+ *       largest |x| (NaN if an element is NaN, else Inf if one is infinite).
+ *       A tensor whose A is not finite has no usable global scale: its scale
+ *       bytes are 0x7F (the E4M3 NaN), its element codes 0, and S_g =
+ *       fl32(A / 2688) stays Inf or NaN.
  *   R7  format variants (flags beside the axis bits): E5M2 elements (bias 15,
  *       max 57344, emax 15) in place of E4M3, and the round-up scale rule,
  *       byte = ceil(log2(amax / max_elem)) + 127: the smallest power of two
@@ -815,16 +819,36 @@ int orc_mx_quantize_gated_grouped(const uint16_t *grad, const uint16_t *x, int64
 /* NVFP4 (R6).                                                               */
 /* ------------------------------------------------------------------------ */
 
-/* Largest magnitude of the tensor, as the (exact) fp32 value. */
+/* Largest magnitude of the tensor, as the (exact) fp32 value; NaN when an
+ * element is NaN (a NaN has no magnitude to compare), +Inf when one is
+ * infinite and none is NaN. */
 float orc_absmax(const uint16_t *x, int64_t n)
 {
     double a = 0.0;
     for (int64_t i = 0; i < n; i++) {
         double v = fabs(orc_bf16_value(x[i]));
+        if (v != v)
+            return NAN;
         if (v > a)
             a = v;
     }
     return (float)a;
+}
+
+/* A tensor whose amax A is not finite (it holds an Inf or a NaN) has no
+ * usable global scale (S_g = fl32(A / 2688) is Inf or NaN): every scale byte
+ * is 0x7F, the E4M3 NaN, and every element code 0 (R6). */
+static void nvfp4_nonfinite(int64_t M, int64_t K, unsigned axis, uint8_t *q_row, uint8_t *s_row,
+                            uint8_t *q_col, uint8_t *s_col)
+{
+    if (axis & 1u) {
+        memset(q_row, 0, (size_t)(M * K / 2));
+        memset(s_row, 0x7F, (size_t)(M * K / 16));
+    }
+    if (axis & 2u) {
+        memset(q_col, 0, (size_t)(M * K / 2));
+        memset(s_col, 0x7F, (size_t)(M * K / 16));
+    }
 }
 
 /* Tensor scale S_g = fl32(A / (448*6)), or 1 when A = 0. */
@@ -866,7 +890,9 @@ static void nvfp4_block(const double *v, int n, float Sg, uint8_t *nib, int64_t 
 /* Row-wise NVFP4 of x[M][K] (blocks of 16 along K) into q_row[M][K/2] (code
  * of element 2j in the low nibble of byte j, 2j+1 in the high nibble) and
  * s_row[M][K/16]; and the same for the transpose into q_col[K][M/2],
- * s_col[K][M/16].  tensor_amax < 0 means "compute it from x". */
+ * s_col[K][M/16].  tensor_amax < 0 means "compute it from x"; a NaN or
+ * infinite tensor_amax (the amax of a tensor holding a NaN or an Inf) gives
+ * the outputs of nvfp4_nonfinite. */
 int orc_nvfp4_quantize_transpose(const uint16_t *x, int64_t M, int64_t K, unsigned axis,
                                  float tensor_amax, uint8_t *q_row, uint8_t *s_row,
                                  uint8_t *q_col, uint8_t *s_col, float *sg_out)
@@ -876,10 +902,14 @@ int orc_nvfp4_quantize_transpose(const uint16_t *x, int64_t M, int64_t K, unsign
     if (axis & ~3u)
         return ORC_ERR_ENUM;
     init_tables();
-    float A = tensor_amax >= 0.0f ? tensor_amax : orc_absmax(x, M * K);
+    float A = tensor_amax < 0.0f ? orc_absmax(x, M * K) : tensor_amax;
     float Sg = orc_nvfp4_global_scale(A);
     if (sg_out)
         *sg_out = Sg;
+    if (!isfinite(A)) {
+        nvfp4_nonfinite(M, K, axis, q_row, s_row, q_col, s_col);
+        return ORC_OK;
+    }
     if (axis & 1u) {
 #pragma omp parallel for schedule(static)
         for (int64_t m = 0; m < M; m++) {
@@ -926,10 +956,14 @@ int orc_nvfp4_quantize_transpose_2d(const uint16_t *x, int64_t M, int64_t K, uns
     if (axis & ~3u)
         return ORC_ERR_ENUM;
     init_tables();
-    float A = tensor_amax >= 0.0f ? tensor_amax : orc_absmax(x, M * K);
+    float A = tensor_amax < 0.0f ? orc_absmax(x, M * K) : tensor_amax;
     float Sg = orc_nvfp4_global_scale(A);
     if (sg_out)
         *sg_out = Sg;
+    if (!isfinite(A)) {
+        nvfp4_nonfinite(M, K, axis, q_row, s_row, q_col, s_col);
+        return ORC_OK;
+    }
 #pragma omp parallel for schedule(static)
     for (int64_t bi = 0; bi < M / 16; bi++) {
         double v[256];

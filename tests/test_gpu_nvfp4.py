@@ -114,3 +114,47 @@ def test_2d_every_scale_code_and_tiny_global_scale():
     x[1, 20] = 0x8000
     g, o = run_both(x, two_d=True)
     mx_outputs_equal(g, o, "nvfp4 2d tiny S_g")
+
+
+def _nan_or_inf_equal(a, b):
+    return (np.isnan(a) and np.isnan(b)) or a == b
+
+
+@pytest.mark.parametrize("bits", [0x7FC0, 0xFFC1, 0x7F80, 0xFF80])
+@pytest.mark.parametrize("two_d", [False, True])
+@pytest.mark.parametrize("M,K", [(48, 80), (144, 528), (1040, 272)])
+def test_nonfinite_tensor(bits, two_d, M, K):
+    """A tensor holding a NaN or an Inf: the device absmax is NaN / Inf, and
+    the cast writes 0x7F scale bytes and zero codes over every (ragged) tile,
+    as the oracle does; S_g stays NaN / Inf."""
+    x = W.student_t_rows(M, K, seed=2100 + M)
+    x[M // 2 + 1, K - 3] = bits
+    xd = to_dev(x)
+    amax = mx.mx_absmax_bf16(xd)
+    torch.cuda.synchronize()
+    A = amax.item()
+    assert _nan_or_inf_equal(A, O.absmax(x)) and not np.isfinite(A)
+    g = mx.nvfp4_quantize_transpose(xd, amax, two_d=two_d)
+    torch.cuda.synchronize()
+    o = O.nvfp4_quantize_transpose(x, two_d=two_d)
+    assert _nan_or_inf_equal(g["sg"].item(), o["sg"])
+    mx_outputs_equal(g, o, f"nvfp4 non-finite {bits:#06x} {M}x{K} 2d={two_d}")
+
+
+@pytest.mark.parametrize("two_d", [False, True])
+def test_nonfinite_group(two_d):
+    """One group of a grouped cast holds a NaN: that group's outputs are the
+    non-finite fill, the others are cast as usual."""
+    rows = [144, 16, 0, 400, 32]
+    x = W.student_t_rows(sum(rows), 272, seed=2200)
+    x[144 + 3, 100] = 0x7FC0
+    x[160 + 399, 0] = 0xFF80            # an Inf in the fourth group
+    xd = to_dev(x)
+    amax = mx.mx_absmax_bf16_grouped(xd, rows)
+    g = mx.nvfp4_quantize_transpose_grouped(xd, rows, amax, two_d=two_d)
+    torch.cuda.synchronize()
+    o = O.nvfp4_quantize_transpose_grouped(x, rows, two_d=two_d)
+    got_sg = g["sg"].cpu().numpy()
+    assert np.isnan(got_sg[1]) and np.isinf(got_sg[3]) and got_sg[2] == 1.0
+    assert all(_nan_or_inf_equal(a, b) for a, b in zip(got_sg, o["sg"]))
+    mx_outputs_equal(g, o, f"grouped nvfp4 non-finite 2d={two_d}")

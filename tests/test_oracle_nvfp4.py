@@ -206,3 +206,64 @@ def test_2d_block_amax_spans_rows():
     assert np.array_equal(codes, want)
     one_d = O.nvfp4_quantize_transpose(x, tensor_amax=2688.0)
     assert one_d["s_row"][0, 0] != 0x38                   # row 0 has no 6.0
+
+
+def _poisoned(M, K, seed, where, bits):
+    x = W.normal(M, K, seed=seed)
+    for (r, c), b in zip(where, bits):
+        x[r, c] = b
+    return x
+
+
+@pytest.mark.parametrize("bits,kind", [((0x7FC0,), "nan"), ((0xFFC1,), "nan"), ((0x7F80,), "inf"),
+                                       ((0xFF80,), "inf"), ((0xFF80, 0x7FC0), "nan")])
+def test_nonfinite_tensor_amax(bits, kind):
+    """The tensor amax is NaN when an element is NaN, else Inf when one is
+    infinite (a NaN outranks an Inf), as numpy finds them."""
+    x = _poisoned(32, 48, 5, [(5, 7), (30, 1)][:len(bits)], bits)
+    A = O.absmax(x)
+    f = W.bf16_to_f32(x).astype(np.float64)
+    assert np.isnan(A) == np.isnan(f).any()
+    assert (np.isinf(A) and A > 0) == (not np.isnan(f).any() and np.isinf(f).any())
+    assert kind == ("nan" if np.isnan(A) else "inf")
+
+
+@pytest.mark.parametrize("bits", [0x7FC0, 0xFF80])
+@pytest.mark.parametrize("two_d", [False, True])
+def test_nonfinite_tensor_has_nan_scales_and_zero_codes(bits, two_d):
+    """R16: a tensor holding a NaN or an Inf has a non-finite amax A and so no
+    usable global scale: S_g = A/2688 stays NaN or Inf, every scale byte is
+    0x7F (the E4M3 NaN) and every element code 0, in both layouts."""
+    x = _poisoned(48, 80, 6, [(17, 33)], [bits])
+    o = O.nvfp4_quantize_transpose(x, two_d=two_d)
+    assert np.isnan(o["sg"]) if bits == 0x7FC0 else (np.isinf(o["sg"]) and o["sg"] > 0)
+    for k in ("s_row", "s_col"):
+        assert o[k].shape == ((48, 5) if k == "s_row" else (80, 3))
+        assert (o[k] == 0x7F).all(), k
+    for k in ("q_row", "q_col"):
+        assert (o[k] == 0).all(), k
+    # one output direction at a time gives the same bytes
+    r = O.nvfp4_quantize_transpose(x, axis=1, two_d=two_d)
+    assert (r["s_row"] == 0x7F).all() and (r["q_row"] == 0).all()
+    # a given non-finite amax does the same to a finite tensor
+    f = O.nvfp4_quantize_transpose(W.normal(48, 80, seed=6), tensor_amax=float("inf"), two_d=two_d)
+    assert (f["s_row"] == 0x7F).all() and (f["q_col"] == 0).all() and np.isinf(f["sg"])
+
+
+def test_nonfinite_group_leaves_the_other_groups_alone():
+    rows = [32, 16, 0, 48]
+    x = W.normal(96, 64, seed=7)
+    x[40, 3] = 0x7FC0                      # a NaN in group 1 (rows 32..47)
+    o = O.nvfp4_quantize_transpose_grouped(x, rows)
+    assert np.isnan(o["sg"][1]) and o["sg"][2] == 1.0
+    assert np.isfinite(o["sg"][[0, 3]]).all()
+    assert (o["s_row"][32:48] == 0x7F).all() and (o["q_row"][32:48] == 0).all()
+    # group 1's transposed outputs: [64][16/2] at byte 64*32/2, [64][16/16] at 64*32/16
+    assert (o["q_col"][64 * 16:64 * 16 + 64 * 8] == 0).all()
+    assert (o["s_col"][64 * 2:64 * 2 + 64] == 0x7F).all()
+    for g, (r0, m) in enumerate(((0, 32), (48, 48))):
+        own = O.nvfp4_quantize_transpose(x[r0:r0 + m])
+        gi = (0, 3)[g]
+        assert own["sg"] == o["sg"][gi]
+        assert np.array_equal(own["s_row"], o["s_row"][r0:r0 + m])
+        assert np.array_equal(own["q_row"], o["q_row"][r0:r0 + m])

@@ -128,6 +128,20 @@ def lead_calls(us_per_call, timed, at_least):
     return max(at_least, int(max(2500.0, 100.0 * timed) / us_per_call) + 1)
 
 
+def run_environment(dev):
+    """What the numbers were measured on: host, GPU, ROCm / HIP version, and
+    the md5 of the loaded libmxcast.so."""
+    import socket
+    import torch
+    import block_scaled_precision_bf16_amd as mx
+    with open(mx.LIB_PATH, "rb") as f:
+        lib_md5 = hashlib.md5(f.read()).hexdigest()
+    props = torch.cuda.get_device_properties(dev)
+    return {"host": socket.gethostname(), "gpu": torch.cuda.get_device_name(dev),
+            "arch": getattr(props, "gcnArchName", None), "hip": torch.version.hip,
+            "torch": torch.__version__, "libmxcast_md5": lib_md5}
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -380,6 +394,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
         "kernel_source_sha256": kernel_source_hash(),
+        "env": run_environment(dev),
     }
 
     if pre_stats is not None:

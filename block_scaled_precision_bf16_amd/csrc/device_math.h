@@ -236,7 +236,9 @@ __device__ __forceinline__ float e4m3_value(uint32_t c)
 // 2^n with one final rounding (also for subnormal results).  Arguments are
 // clamped at -104, where the sequence already gives 0 (0.97 * 2^-150 rounds
 // to 0), so every smaller argument gets that same 0 without a select; NaN
-// propagates through the final select.
+// propagates through the final select.  KEEP_NAN = false leaves that select
+// out (a NaN argument then gives 0), for callers whose result is NaN anyway.
+template <bool KEEP_NAN = true>
 __device__ __forceinline__ float exp32_nonpos(float a)
 {
     const float LOG2E = 1.44269504088896340736f;
@@ -258,7 +260,9 @@ __device__ __forceinline__ float exp32_nonpos(float a)
     // p * 2^n with one rounding (v_ldexp_f32, denormals kept): the same bits
     // as scaling by 2^(n/2) and then 2^(n - n/2), the first product exact
     const float e = __builtin_amdgcn_ldexpf(p, (int)n);    // n in [-150, 0]
-    return a != a ? a : e;
+    if constexpr (KEEP_NAN)
+        return a != a ? a : e;
+    return e;
 }
 
 // fl32(1 / d) for d in [1, 2]: the hardware reciprocal estimate and one
@@ -284,6 +288,17 @@ __device__ __forceinline__ void sigmoid_pair(float z, float &s, float &sc)
     sc = z >= 0.0f ? er : r;
 }
 
+// sigma(z) alone, for the forward activations x * sigma(.).  The exp's NaN
+// select is left out: z is NaN only when x is, and then sigma comes out 0 and
+// the product x * 0 is NaN as well, so the activation's value is the same for
+// every input (a finite or infinite z takes the identical sequence).
+__device__ __forceinline__ float sigmoid_of(float z)
+{
+    const float e = exp32_nonpos<false>(-__builtin_fabsf(z));
+    const float r = rcp_1_2(1.0f + e);   // 1 + e is in [1, 2]
+    return z >= 0.0f ? r : e * r;
+}
+
 constexpr float K_SQRT_2_OVER_PI = 0.797884560802865355879892119868763737f;
 constexpr float K_CUBIC = 0.044715f;
 constexpr float K_CUBIC3 = 0.134145f;
@@ -303,9 +318,7 @@ __device__ __forceinline__ float gelu32(float x)
     float x2 = x * x;
     float x3 = x2 * x;
     float inner = __builtin_fmaf(K_CUBIC, x3, x);
-    float s, sc;
-    sigmoid_pair(gelu_2u(inner), s, sc);
-    return x * s;
+    return x * sigmoid_of(gelu_2u(inner));
 }
 
 // d/dx of gelu32's function: sigma + x sigma (1 - sigma) 2u'(x), with
@@ -324,12 +337,7 @@ __device__ __forceinline__ float dgelu32(float x)
     return s + t;
 }
 
-__device__ __forceinline__ float silu32(float g)
-{
-    float s, sc;
-    sigmoid_pair(g, s, sc);
-    return g * s;
-}
+__device__ __forceinline__ float silu32(float g) { return g * sigmoid_of(g); }
 
 // d/dg of silu32's function: sigma + g sigma (1 - sigma); the second term is
 // 0 when sigma(1 - sigma) is 0.

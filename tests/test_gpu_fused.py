@@ -96,3 +96,45 @@ def test_dbias_deterministic():
     b = mx.mx_quantize(xd, gd, fusion=f)["dbias"]
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+SPECIALS = [0x7FC0, 0xFFC0, 0x7F81, 0x7F80, 0xFF80, 0x7F7F, 0xFF7F, 0x5F80, 0xDF80, 0x0001, 0x8000]
+
+
+def values_match(got, want):
+    """bf16 patterns equal, NaN payloads aside: NaN exactly where the oracle
+    has NaN, every other pattern identical."""
+    g = got.cpu().numpy().view(np.uint16) if isinstance(got, torch.Tensor) else got
+    g_nan = (g & 0x7F80) == 0x7F80
+    g_nan &= (g & 0x7F) != 0
+    w_nan = ((want & 0x7F80) == 0x7F80) & ((want & 0x7F) != 0)
+    assert np.array_equal(g_nan, w_nan), np.argwhere(g_nan != w_nan)[:4]
+    assert np.array_equal(g[~g_nan], want[~w_nan]), "non-NaN values differ"
+
+
+@pytest.mark.parametrize("op", [mx.FUSE_GELU, mx.OP_GATED | mx.GATED_SWIGLU,
+                                mx.OP_GATED | mx.GATED_GEGLU])
+def test_forward_activations_with_nan_and_inf(op):
+    """NaN, +-Inf, the largest finite values and inputs whose cube overflows
+    (+-2^64), planted among N(0, 1): the cast's bytes equal the oracle's, and
+    the fused values are NaN exactly where the oracle's are and equal
+    elsewhere."""
+    gated = bool(op & mx.OP_GATED)
+    M, K = 64, 512
+    x = W.normal(M, K, seed=45)
+    rng = np.random.default_rng(46)
+    for b in SPECIALS:
+        for _ in range(6):
+            x[rng.integers(M), rng.integers(K)] = b
+    xd = to_dev(x)
+    if gated:
+        g = mx.mx_quantize_gated(xd, op & 0xF)
+        o = O.mx_quantize_gated(x, op & 0xF, want_y=True)
+    else:
+        g = mx.mx_quantize(xd, fusion=op)
+        o = O.mx_quantize(x, fusion=op, want_y=True)
+    torch.cuda.synchronize()
+    mx_outputs_equal(g, o, f"op {op:#x} with NaN / Inf")
+    y = mx.mx_fused_values(xd, op=op)
+    torch.cuda.synchronize()
+    values_match(y, o["y"])

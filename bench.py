@@ -40,10 +40,12 @@ TRAFFIC_FILE = os.path.join(HERE, "profiles", "counters_mxfp8_dim0_dim1_16384.md
 
 def mx_bytes(M, K, directions, extra_inputs=0):
     """Algorithmic bytes of an MXFP8 cast: 2 B per bf16 input element (per
-    input tensor), 1 B per E4M3 element and 1 B per E8M0 scale (per 32
-    elements) for each output direction."""
+    input tensor), 1 B per E4M3 element and 1 B per E8M0 scale (one per block
+    of up to 32 elements of a line) for each output direction (directions 2:
+    row-wise and transposed, 1: transposed only)."""
     n = M * K
-    return 2 * n * (1 + extra_inputs) + directions * (n + n // 32)
+    row, col = n + M * -(-K // 32), n + K * -(-M // 32)
+    return 2 * n * (1 + extra_inputs) + (row + col if directions == 2 else col)
 
 
 def nvfp4_bytes(M, K, directions):
@@ -73,6 +75,8 @@ CONFIGS = {
     "mxfp8_grouped_8x_16384x7168": ("f4_grouped_moe", (16384, 7168), "mx_grouped", 3),
     "nvfp4_grouped_8x_16384x7168": ("f4_grouped_moe", (16384, 7168), "nvfp4_grouped", 3),
     "mxfp8_grouped_swiglu_8x_16384x4096": ("f4_grouped_moe", (16384, 4096), "mx_grouped_swiglu", 3),
+    # the any-shape kernel: rows and row lengths that are not multiples of 16 and 8
+    "mxfp8_dim0_dim1_16383": ("c2_dim1_16384", (16383, 16383), "mx", 3),
 }
 
 # Row counts of the 8 experts in the grouped workloads.
@@ -193,7 +197,7 @@ def main():
     key, (M, K), kind, dirs = CONFIGS[args.config]
     pre_pass = None   # NVFP4: the tensor absmax pass, timed on its own
     print(f"[bench] generating {args.config} inputs {M}x{K}", file=sys.stderr, flush=True)
-    inputs = W.make(key, M, K) if kind == "mx_grouped_swiglu" else W.make(key)
+    inputs = W.make(key, M, K)
     if kind in ("mx_gelu", "mx_dgelu", "mx_dsilu"):
         x_h, g_h = inputs
     elif kind.startswith("dgated"):

@@ -111,39 +111,72 @@ uint64_t scale_bytes(int64_t rows, int64_t cols, bool tiled)
     return (uint64_t)(((rows + 31) / 32) * ((blocks + 7) / 8) * 256);
 }
 
-// Sizes of an MXFP8 cast: every row of every input and output starts on a
-// 16-byte boundary (K a multiple of 8 for the bf16 input and 8-byte row
-// stores, M a multiple of 16 for the 16-byte stores of the transposed
-// output); blocks at the right and bottom edges may be partial.
-bool mx_shape_ok(int64_t M, int64_t K)
+// Sizes of an MXFP8 cast: any positive M and K up to the limits; blocks at
+// the right and bottom edges may be partial.
+bool mx_size_ok(int64_t M, int64_t K)
 {
-    return M > 0 && K > 0 && M % 16 == 0 && K % 8 == 0 && M <= kMaxDim && K <= kMaxDim &&
-           M * K <= kMaxElems;
+    return M > 0 && K > 0 && M <= kMaxDim && K <= kMaxDim && M * K <= kMaxElems;
+}
+
+// Shapes the tiled cast kernel takes: every row of every input and output
+// starts on a 16-byte boundary (K a multiple of 8 for the bf16 input and the
+// 8-byte row stores, M a multiple of 16 for the 16-byte stores of the
+// transposed output).  Every other shape goes to the any-shape kernel.
+bool tiled_shape(int64_t M, int64_t K) { return M % 16 == 0 && K % 8 == 0; }
+
+// Group table of the any-shape kernel for one M x K tensor.
+mxk::GroupTable any_table(int64_t M, int64_t K)
+{
+    mxk::GroupTable gt{};
+    gt.count = 1;
+    gt.len[0] = mxk::any_walk_len(&M, 1, K);
+    gt.walk0[0] = 0;
+    gt.walk0[1] = tiles(tiles(M, mxk::kAnyTileM), gt.len[0]);
+    gt.row0[0] = 0;
+    gt.row0[1] = M;
+    gt.srow_off[0] = gt.scol_off[0] = 0;
+    return gt;
+}
+
+// Bytes of dbias partials for one M x K tensor (either kernel).
+size_t quantize_workspace(int64_t M, int64_t K, int op, bool tiled)
+{
+    if (!tiled_shape(M, K))
+        return (size_t)any_table(M, K).walk0[1] * (size_t)K * sizeof(float);
+    return dbias_workspace(M, K, op, tiled);
 }
 
 mx_status from_hip(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
 
 // Group table of a grouped cast: walks per group (the walk length chosen for
 // the whole stack, at least two sub-tiles with tiled scales), rows, and each
-// group's scale offsets.  False if a group size is invalid.
+// group's scale offsets.  False if a group size is invalid.  any is set when
+// the stack goes to the any-shape kernel: some group's rows are not a
+// multiple of 16, or the row length is not aligned for the tiled kernel
+// (width_aligned false); the walks are then that kernel's.
 bool build_groups(const int64_t *rows, int G, int64_t K, int op, bool dbias, bool tiled,
-                  mxk::GroupTable &gt, int64_t &M, int &group)
+                  bool width_aligned, mxk::GroupTable &gt, int64_t &M, int &group, bool &any)
 {
     if (!rows || G < 1 || G > mxk::kMaxGroups)
         return false;
     M = 0;
+    bool rows16 = true;
     for (int g = 0; g < G; g++) {
-        if (rows[g] < 0 || rows[g] % 16 != 0 || rows[g] > kMaxDim)
+        if (rows[g] < 0 || rows[g] > kMaxDim)
             return false;
+        rows16 = rows16 && rows[g] % 16 == 0;
         M += rows[g];
     }
-    if (M <= 0 || M > kMaxDim || !mx_shape_ok(M, K))
+    if (M <= 0 || M > kMaxDim || !mx_size_ok(M, K))
         return false;
+    any = !(rows16 && width_aligned);
     int tm[mxk::kMaxGroups];
     for (int g = 0; g < G; g++)
-        tm[g] = tiles(rows[g], mxk::kTileM);
+        tm[g] = tiles(rows[g], any ? mxk::kAnyTileM : mxk::kTileM);
     gt = mxk::GroupTable{};
-    if (mxk::target_workgroups(op, dbias) == mxk::kTargetWorkgroupsFused) {
+    if (any) {
+        group = mxk::any_walk_len(rows, G, K);
+    } else if (mxk::target_workgroups(op, dbias) == mxk::kTargetWorkgroupsFused) {
         // the casts bound by their arithmetic (fused pre-ops and gated casts
         // without dbias): walks of one sub-tile (two with the tile layout),
         // many short workgroups that the hardware hands out as others finish,
@@ -239,6 +272,20 @@ static bool mx_mode_ok(unsigned axis_mask)
     return (axis_mask & 3u) != 0 && (axis_mask & ~kModeBits) == 0;
 }
 
+// One tensor (a.M x a.K, everything but the walk set) through the any-shape
+// kernel; sets a.tiles_k, a.tiles_m, a.group and a.groups_m to its plan.
+static mx_status launch_any(int op, unsigned axis_mask, bool dbias, mxk::MxArgs &a,
+                            hipStream_t stream)
+{
+    const mxk::GroupTable gt = any_table(a.M, a.K);
+    a.tiles_k = tiles(a.K, mxk::kAnyTileK);
+    a.tiles_m = tiles(a.M, mxk::kAnyTileM);
+    a.group = gt.len[0];
+    a.groups_m = gt.walk0[1];
+    return from_hip(mxk::launch_mx_cast_any(op, axis_mask & 3u, axis_mask & kFmtBits, dbias, a, gt,
+                                            stream));
+}
+
 static mx_status nvfp4_impl(bool two_d, const void *x, int64_t M, int64_t K, const float *amax,
                             unsigned axis_mask, uint8_t *q_row, uint8_t *s_row, uint8_t *q_col,
                             uint8_t *s_col, float *global_scale_out, hipStream_t stream)
@@ -296,14 +343,16 @@ static mx_status gated_grouped_impl(const void *grad, const void *x, int64_t N,
         return MX_ERR_NULL;
     const int op = bwd ? (act == MX_GATED_SWIGLU ? mxk::OP_DSWIGLU : mxk::OP_DGEGLU)
                        : (act == MX_GATED_SWIGLU ? mxk::OP_SWIGLU : mxk::OP_GEGLU);
-    if (!mx_shape_ok(16, N))   // N <= 2^23 before 2N is formed
+    if (!mx_size_ok(16, N))   // N <= 2^23 before 2N is formed
         return MX_ERR_SHAPE;
     const int64_t W = bwd ? 2 * N : N;
     const bool tiled = (axis_mask & MX_SCALE_TILED) != 0;
     mxk::GroupTable gt;
     int64_t M;
     int group;
-    if (!build_groups(group_rows, G, W, op, false, tiled, gt, M, group) || !mx_shape_ok(M, 2 * N))
+    bool any;
+    if (!build_groups(group_rows, G, W, op, false, tiled, N % 8 == 0, gt, M, group, any) ||
+        !mx_size_ok(M, 2 * N))
         return MX_ERR_SHAPE;
     if (!aligned(x, 16) || (bwd && !aligned(grad, 16)) ||
         (row && (!aligned(q_row, 16) || !aligned(s_row, 16))) ||
@@ -333,10 +382,13 @@ static mx_status gated_grouped_impl(const void *grad, const void *x, int64_t N,
     a.partials = nullptr;
     a.tiled = tiled;
     a.qcol_nt = 0;
-    a.tiles_k = tiles(W, mxk::kTileK);
+    a.tiles_k = tiles(W, any ? mxk::kAnyTileK : mxk::kTileK);
     a.tiles_m = tiles(M, mxk::kTileM);
     a.group = group;
     a.groups_m = gt.walk0[G];
+    if (any)
+        return from_hip(mxk::launch_mx_cast_any(op, axis_mask & 3u, axis_mask & kFmtBits, false, a,
+                                                gt, stream));
     return from_hip(mxk::launch_mx_cast_grouped(op, axis_mask & 3u, axis_mask & kFmtBits, false, a,
                                                 gt, stream));
 }
@@ -351,7 +403,7 @@ const char *mx_status_str(int s)
     case MX_OK: return "MX_OK";
     case MX_ERR_NULL: return "MX_ERR_NULL: a required pointer is NULL";
     case MX_ERR_ENUM: return "MX_ERR_ENUM: unknown axis mask, fusion or activation";
-    case MX_ERR_SHAPE: return "MX_ERR_SHAPE: size not a positive multiple of the block size, or too large";
+    case MX_ERR_SHAPE: return "MX_ERR_SHAPE: size not positive, too large, or (NVFP4) not a multiple of 16";
     case MX_ERR_ALIGN: return "MX_ERR_ALIGN: pointer not 16-byte aligned";
     case MX_ERR_WORKSPACE: return "MX_ERR_WORKSPACE: workspace missing or too small";
     case MX_ERR_ALIAS: return "MX_ERR_ALIAS: an output overlaps an input or another output";
@@ -363,10 +415,10 @@ const char *mx_status_str(int s)
 
 size_t mx_quantize_workspace_size(int64_t M, int64_t K, unsigned axis_mask, int fusion)
 {
-    if (!(fusion & MX_FUSE_DBIAS) || !mx_shape_ok(M, K) || !mx_mode_ok(axis_mask) ||
+    if (!(fusion & MX_FUSE_DBIAS) || !mx_size_ok(M, K) || !mx_mode_ok(axis_mask) ||
         (fusion & ~0x1F) || (fusion & 0xF) > MX_FUSE_DSILU)
         return 0;
-    return dbias_workspace(M, K, cast_op(fusion & 0xF), (axis_mask & MX_SCALE_TILED) != 0);
+    return quantize_workspace(M, K, cast_op(fusion & 0xF), (axis_mask & MX_SCALE_TILED) != 0);
 }
 
 size_t mx_scale_size(int64_t rows, int64_t cols, unsigned axis_mask)
@@ -396,7 +448,7 @@ static mx_status quantize_impl(const void *x, const void *grad, int64_t M, int64
     if (!x || (has_grad && !grad) || (row && (!q_row || !s_row)) ||
         (col && (!q_col || !s_col)) || (want_dbias && !dbias))
         return MX_ERR_NULL;
-    if (!mx_shape_ok(M, K))
+    if (!mx_size_ok(M, K))
         return MX_ERR_SHAPE;
     if (!aligned(x, 16) || (has_grad && !aligned(grad, 16)) ||
         (row && (!aligned(q_row, 16) || !aligned(s_row, 16))) ||
@@ -405,7 +457,7 @@ static mx_status quantize_impl(const void *x, const void *grad, int64_t M, int64
         return MX_ERR_ALIGN;
     const int op = cast_op(pre);
     const bool tiled = (axis_mask & MX_SCALE_TILED) != 0;
-    const size_t need = want_dbias ? dbias_workspace(M, K, op, tiled) : 0;
+    const size_t need = want_dbias ? quantize_workspace(M, K, op, tiled) : 0;
     if (noalloc ? need > mxk::kNoAllocScratchBytes
                 : want_dbias && (!workspace || workspace_bytes < need))
         return MX_ERR_WORKSPACE;
@@ -439,9 +491,14 @@ static mx_status quantize_impl(const void *x, const void *grad, int64_t M, int64
     a.partials = want_dbias ? static_cast<float *>(workspace) : nullptr;
     a.tiled = tiled;
     a.qcol_nt = M * K >= mxk::kQcolNtBytes && M % 128 == 0;
-    set_walk(a, op, want_dbias);
-    mx_status st = from_hip(mxk::launch_mx_cast(op, axis_mask & 3u, axis_mask & kFmtBits,
-                                                want_dbias, a, stream));
+    mx_status st;
+    if (tiled_shape(M, K)) {
+        set_walk(a, op, want_dbias);
+        st = from_hip(mxk::launch_mx_cast(op, axis_mask & 3u, axis_mask & kFmtBits, want_dbias, a,
+                                          stream));
+    } else {
+        st = launch_any(op, axis_mask, want_dbias, a, stream);
+    }
     if (st != MX_OK || !want_dbias)
         return st;
     return from_hip(mxk::launch_dbias_reduce(a.partials, a.groups_m, K, dbias, stream));
@@ -472,8 +529,9 @@ size_t mx_quantize_grouped_workspace_size(int64_t K, const int64_t *group_rows, 
     mxk::GroupTable gt;
     int64_t M;
     int group;
+    bool any;
     if (!build_groups(group_rows, G, K, cast_op(fusion & 0xF), true,
-                      (axis_mask & MX_SCALE_TILED) != 0, gt, M, group))
+                      (axis_mask & MX_SCALE_TILED) != 0, K % 8 == 0, gt, M, group, any))
         return 0;
     return (size_t)gt.walk0[G] * (size_t)K * sizeof(float);
 }
@@ -484,8 +542,10 @@ size_t mx_grouped_scale_size(int64_t K, const int64_t *group_rows, int G, unsign
     mxk::GroupTable gt;
     int64_t M;
     int group;
-    if (!mx_mode_ok(axis_mask) || !build_groups(group_rows, G, K, mxk::OP_PLAIN, false,
-                                                (axis_mask & MX_SCALE_TILED) != 0, gt, M, group))
+    bool any;
+    if (!mx_mode_ok(axis_mask) ||
+        !build_groups(group_rows, G, K, mxk::OP_PLAIN, false, (axis_mask & MX_SCALE_TILED) != 0,
+                      K % 8 == 0, gt, M, group, any))
         return 0;
     return (size_t)grouped_scale_bytes(group_rows, G, K, colwise != 0,
                                        (axis_mask & MX_SCALE_TILED) != 0);
@@ -510,7 +570,8 @@ mx_status mx_quantize_grouped(const void *x, const void *grad, int64_t K, const 
     mxk::GroupTable gt;
     int64_t M;
     int group;
-    if (!build_groups(group_rows, G, K, op, want_dbias, tiled, gt, M, group))
+    bool any;
+    if (!build_groups(group_rows, G, K, op, want_dbias, tiled, K % 8 == 0, gt, M, group, any))
         return MX_ERR_SHAPE;
     if (!aligned(x, 16) || (has_grad && !aligned(grad, 16)) ||
         (row && (!aligned(q_row, 16) || !aligned(s_row, 16))) ||
@@ -546,12 +607,15 @@ mx_status mx_quantize_grouped(const void *x, const void *grad, int64_t K, const 
     a.partials = want_dbias ? static_cast<float *>(workspace) : nullptr;
     a.tiled = tiled;
     a.qcol_nt = 0;   // groups' transposed rows rarely fill whole lines
-    a.tiles_k = tiles(K, mxk::kTileK);
+    a.tiles_k = tiles(K, any ? mxk::kAnyTileK : mxk::kTileK);
     a.tiles_m = tiles(M, mxk::kTileM);
     a.group = group;
     a.groups_m = gt.walk0[G];
-    mx_status st = from_hip(mxk::launch_mx_cast_grouped(op, axis_mask & 3u, axis_mask & kFmtBits,
-                                                        want_dbias, a, gt, stream));
+    mx_status st = from_hip(
+        any ? mxk::launch_mx_cast_any(op, axis_mask & 3u, axis_mask & kFmtBits, want_dbias, a, gt,
+                                      stream)
+            : mxk::launch_mx_cast_grouped(op, axis_mask & 3u, axis_mask & kFmtBits, want_dbias, a,
+                                          gt, stream));
     if (st != MX_OK || !want_dbias)
         return st;
     return from_hip(mxk::launch_dbias_reduce_grouped(a.partials, gt, K, dbias, stream));
@@ -585,7 +649,7 @@ mx_status mx_quantize_gated(const void *x, int64_t M, int64_t N, unsigned axis_m
     const bool row = axis_mask & MX_ROWWISE, col = axis_mask & MX_COLWISE;
     if (!x || (row && (!q_row || !s_row)) || (col && (!q_col || !s_col)))
         return MX_ERR_NULL;
-    if (!mx_shape_ok(M, N) || !mx_shape_ok(M, 2 * N))
+    if (!mx_size_ok(M, N) || !mx_size_ok(M, 2 * N))
         return MX_ERR_SHAPE;
     if (!aligned(x, 16) || (row && (!aligned(q_row, 16) || !aligned(s_row, 16))) ||
         (col && (!aligned(q_col, 16) || !aligned(s_col, 16))))
@@ -614,6 +678,8 @@ mx_status mx_quantize_gated(const void *x, int64_t M, int64_t N, unsigned axis_m
     a.tiled = tiled;
     a.qcol_nt = 0;
     const int op = act == MX_GATED_SWIGLU ? mxk::OP_SWIGLU : mxk::OP_GEGLU;
+    if (!tiled_shape(M, N))
+        return launch_any(op, axis_mask, false, a, stream);
     set_walk(a, op, false);
     return from_hip(
         mxk::launch_mx_cast(op, axis_mask & 3u, axis_mask & kFmtBits, false, a, stream));
@@ -628,7 +694,7 @@ mx_status mx_quantize_dgated(const void *grad, const void *x, int64_t M, int64_t
     const bool row = axis_mask & MX_ROWWISE, col = axis_mask & MX_COLWISE;
     if (!grad || !x || (row && (!q_row || !s_row)) || (col && (!q_col || !s_col)))
         return MX_ERR_NULL;
-    if (!mx_shape_ok(M, N) || !mx_shape_ok(M, 2 * N))
+    if (!mx_size_ok(M, N) || !mx_size_ok(M, 2 * N))
         return MX_ERR_SHAPE;
     if (!aligned(grad, 16) || !aligned(x, 16) ||
         (row && (!aligned(q_row, 16) || !aligned(s_row, 16))) ||
@@ -660,6 +726,8 @@ mx_status mx_quantize_dgated(const void *grad, const void *x, int64_t M, int64_t
     a.tiled = tiled;
     a.qcol_nt = 0;
     const int op = act == MX_GATED_SWIGLU ? mxk::OP_DSWIGLU : mxk::OP_DGEGLU;
+    if (!tiled_shape(M, N))   // the tiled kernel needs both halves 8-column aligned
+        return launch_any(op, axis_mask, false, a, stream);
     set_walk(a, op, false);
     return from_hip(
         mxk::launch_mx_cast(op, axis_mask & 3u, axis_mask & kFmtBits, false, a, stream));
@@ -684,7 +752,7 @@ mx_status mx_fused_values(const void *x, const void *grad, int64_t M, int64_t K,
     const bool has_grad = kop == mxk::OP_DGELU || kop == mxk::OP_DSILU || dgated;
     if (!x || !y || (has_grad && !grad))
         return MX_ERR_NULL;
-    if (!mx_shape_ok(M, K) || (gated && !mx_shape_ok(M, 2 * K)))
+    if (!mx_size_ok(M, K) || (gated && !mx_size_ok(M, 2 * K)))
         return MX_ERR_SHAPE;
     if (!aligned(x, 16) || !aligned(y, 16) || (has_grad && !aligned(grad, 16)))
         return MX_ERR_ALIGN;
@@ -693,9 +761,10 @@ mx_status mx_fused_values(const void *x, const void *grad, int64_t M, int64_t K,
     const Span out[1] = {{y, dgated ? 4 * n : 2 * n}};
     if (any_alias(in, 2, out, 1))
         return MX_ERR_ALIAS;
-    return from_hip(mxk::launch_fused_values(kop, static_cast<const uint16_t *>(x),
-                                             static_cast<const uint16_t *>(grad), M, K,
-                                             static_cast<uint16_t *>(y), stream));
+    // the 8-element kernel needs rows of a multiple of 8 elements
+    return from_hip((K % 8 == 0 ? mxk::launch_fused_values : mxk::launch_fused_values_any)(
+        kop, static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(grad), M, K,
+        static_cast<uint16_t *>(y), stream));
 }
 
 mx_status mx_absmax_bf16(const void *x, int64_t n, float *amax, hipStream_t stream)

@@ -135,6 +135,32 @@ inline void plan_walks(const int *tiles_m, int groups, int tiles_k, int slots, b
     }
 }
 
+// The cast of any shape (mx_cast_any.hip): a workgroup walks down a
+// 128-column strip in steps of 64 rows, up to kAnyMaxWalk steps.
+constexpr int kAnyTileM = 64;
+constexpr int kAnyTileK = 128;
+constexpr int kAnyMaxWalk = 8;
+// Workgroups the any-shape cast aims for: four per compute unit (its LDS
+// allows four resident).
+constexpr int kAnyTargetWorkgroups = 1024;
+
+// Steps per walk of the any-shape cast for groups of the given row counts
+// and row length K: the longest of 8, 4, 2, 1 steps that still gives
+// kAnyTargetWorkgroups workgroups (1 if none does).
+inline int any_walk_len(const int64_t *rows, int groups, int64_t K)
+{
+    const int64_t tk = (K + kAnyTileK - 1) / kAnyTileK;
+    int len = kAnyMaxWalk;
+    for (; len > 1; len >>= 1) {
+        int64_t walks = 0;
+        for (int g = 0; g < groups; g++)
+            walks += ((rows[g] + kAnyTileM - 1) / kAnyTileM + len - 1) / len;
+        if (walks * tk >= kAnyTargetWorkgroups)
+            break;
+    }
+    return len;
+}
+
 struct MxArgs {
     const uint16_t *x;     // input (gated: [M][2N] with the linear half at lin_off)
     const uint16_t *aux;   // grad for dGELU, else unused
@@ -186,6 +212,12 @@ hipError_t launch_mx_cast(int op, unsigned axis, unsigned fmt, bool dbias, const
 // pointers describe the whole stack.
 hipError_t launch_mx_cast_grouped(int op, unsigned axis, unsigned fmt, bool dbias, const MxArgs &a,
                                   const GroupTable &gt, hipStream_t s);
+// The same operations for any shape (mx_cast_any.hip): a.tiles_k =
+// ceil(K / kAnyTileK); gt gives each group's rows, walks (gt.len steps each)
+// and scale offsets (one group for a single tensor); a.partials holds
+// [gt.walk0[gt.count]][K] dbias partial sums.
+hipError_t launch_mx_cast_any(int op, unsigned axis, unsigned fmt, bool dbias, const MxArgs &a,
+                              const GroupTable &gt, hipStream_t s);
 hipError_t launch_dbias_reduce_grouped(const float *partials, const GroupTable &gt, int64_t K,
                                        float *dbias, hipStream_t s);
 hipError_t launch_dbias_reduce(const float *partials, int segments, int64_t K, float *dbias,
@@ -200,6 +232,9 @@ hipError_t noalloc_scratch(hipStream_t s, float **ptr);
 // grad aux[M][K] and write y[M][2K].
 hipError_t launch_fused_values(int op, const uint16_t *x, const uint16_t *aux, int64_t M,
                                int64_t K, uint16_t *y, hipStream_t s);
+// launch_fused_values for any M, K (one element per thread).
+hipError_t launch_fused_values_any(int op, const uint16_t *x, const uint16_t *aux, int64_t M,
+                                   int64_t K, uint16_t *y, hipStream_t s);
 hipError_t launch_absmax(const uint16_t *x, int64_t n, float *amax, hipStream_t s);
 // two_d: one scale per 16 x 16 block instead of per 16 elements of a row.
 hipError_t launch_nvfp4(unsigned axis, bool two_d, const Nv4Args &a, hipStream_t s);

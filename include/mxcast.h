@@ -22,7 +22,8 @@
  *   - grouped (per-expert) MXFP8 and NVFP4 casts of tensors stacked along
  *     rows (PR 3291, the grouped NVFP4 quantize-transpose row);
  *   - format, layout and shape extensions of the MXFP8 casts: E5M2 elements,
- *     the round-up scale rule, GEMM-ready scale tiles, partial edge blocks.
+ *     the round-up scale rule, GEMM-ready scale tiles, any row count and row
+ *     length (partial edge blocks).
  *
  * Numerics (the pages name these formats but do not define their
  * arithmetic; these are the readings the library implements bit-exactly):
@@ -70,15 +71,14 @@
 extern "C" {
 #endif
 
-#define MXCAST_ABI_VERSION 9
+#define MXCAST_ABI_VERSION 10
 
 typedef enum mx_status {
     MX_OK = 0,
     MX_ERR_NULL = 1,        /* a required pointer is NULL                     */
     MX_ERR_ENUM = 2,        /* unknown axis mask, fusion or activation        */
-    MX_ERR_SHAPE = 3,       /* non-positive size, not a multiple of the size  */
-                            /* step (MXFP8: M of 16, K of 8; NVFP4: both of   */
-                            /* 16), or too large                              */
+    MX_ERR_SHAPE = 3,       /* non-positive or too large size, or (NVFP4) a   */
+                            /* size that is not a multiple of 16              */
     MX_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned               */
     MX_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required     */
     MX_ERR_ALIAS = 6,       /* an output overlaps an input or another output  */
@@ -151,9 +151,11 @@ typedef enum mx_status {
  *   x        device, bf16 [M][K]
  *   grad     device, bf16 [M][K]; required for MX_FUSE_DGELU / DSILU, else
  *            ignored
- *   M, K     rows, columns; M a positive multiple of 16, K of 8 (every row of
- *            every input and output starts 16-byte aligned), each <= 2^23,
- *            M*K <= 2^40
+ *   M, K     rows, columns: any M, K >= 1, each <= 2^23, M*K <= 2^40.  M a
+ *            multiple of 16 and K of 8 (every row of every input and output
+ *            16-byte aligned) take the tiled kernel; any other shape takes a
+ *            kernel for arbitrary row alignment (same results, lower
+ *            bandwidth)
  *   axis_mask  MX_ROWWISE, MX_COLWISE or both (one pass over x), optionally
  *            with the format flags MX_ELEM_E5M2 / MX_SCALE_ROUND_UP and the
  *            layout flag MX_SCALE_TILED (scale tensors then have
@@ -225,8 +227,10 @@ size_t mx_scale_size(int64_t rows, int64_t cols, unsigned axis_mask);
  * MXFP8.
  *   x, grad      device, bf16 [M][K], M = sum of group_rows; group g owns rows
  *                r_g .. r_g + group_rows[g] - 1, r_g = sum_{h<g} group_rows[h]
- *   group_rows   HOST array of G row counts, each >= 0 and a multiple of 16
- *                (an empty group is allowed); 1 <= G <= 64, M > 0
+ *   group_rows   HOST array of G row counts, each >= 0 (an empty group is
+ *                allowed); 1 <= G <= 64, 0 < M <= 2^23.  Every count a
+ *                multiple of 16 and K of 8 take the tiled kernel, any other
+ *                stack the any-shape kernel (same results)
  *   axis_mask, fusion  as for mx_quantize (format and layout flags included)
  *   q_row        [M][K]: the groups' row-wise elements (the stacked tensor's)
  *   s_row        the groups' row scales one after the other, group g's
@@ -260,9 +264,10 @@ size_t mx_grouped_scale_size(int64_t K, const int64_t *group_rows, int G, unsign
 /*
  * Gated MXFP8 cast.  x is bf16 [M][2N] holding [gate | linear] (gate =
  * columns 0..N-1); the quantised tensor is y[M][N] = act(gate) * linear,
- * block size 32 (partial at the edges as for mx_quantize), M a positive
- * multiple of 16, N of 8, M <= 2^23, 2N <= 2^23.  axis_mask as for
- * mx_quantize (format flags included).
+ * block size 32 (partial at the edges as for mx_quantize), any M, N >= 1
+ * with M <= 2^23, 2N <= 2^23, M * 2N <= 2^40 (M a multiple of 16 and N of 8
+ * take the tiled kernel).  axis_mask as for mx_quantize (format flags
+ * included).
  *   q_row, s_row  E4M3 [M][N], E8M0 [M][ceil(N/32)]   (iff MX_ROWWISE)
  *   q_col, s_col  E4M3 [N][M], E8M0 [N][ceil(M/32)]   (iff MX_COLWISE)
  */
@@ -278,9 +283,9 @@ mx_status mx_quantize_gated(const void *x, int64_t M, int64_t N, unsigned axis_m
  * tensor is dx[M][2N] = [d_gate | d_linear]:
  *   d_gate   = fl32(fl32(a' * grad) * linear),   d_linear = fl32(a * grad),
  * each rounded once to bf16; block size 32 along 2N (row-wise) and M.
- * M a positive multiple of 16, N of 8, M <= 2^23, 2N <= 2^23 (partial blocks
- * at the edges as for mx_quantize).  axis_mask as for mx_quantize (format
- * flags included).
+ * Any M, N >= 1 with M <= 2^23, 2N <= 2^23, M * 2N <= 2^40 (partial blocks
+ * at the edges as for mx_quantize; M a multiple of 16 and N of 8 take the
+ * tiled kernel).  axis_mask as for mx_quantize (format flags included).
  *   q_row, s_row  E4M3 [M][2N], E8M0 [M][ceil(2N/32)]   (iff MX_ROWWISE)
  *   q_col, s_col  E4M3 [2N][M], E8M0 [2N][ceil(M/32)]   (iff MX_COLWISE)
  * Errors as for mx_quantize_gated.
@@ -292,7 +297,7 @@ mx_status mx_quantize_dgated(const void *grad, const void *x, int64_t M, int64_t
 /*
  * Grouped gated casts (an MoE layer's experts in one launch): x is bf16
  * [M][2N] = [gate | linear] with the groups' rows stacked as for
- * mx_quantize_grouped (HOST group_rows, multiples of 16, empty groups
+ * mx_quantize_grouped (HOST group_rows, any counts >= 0, empty groups
  * allowed, 1 <= G <= 64); each group is cast exactly as mx_quantize_gated
  * (forward: quantised tensor [rows][N], W = N) or mx_quantize_dgated
  * (backward, grad bf16 [M][N]: quantised tensor [rows][2N], W = 2N) casts
@@ -318,8 +323,8 @@ mx_status mx_quantize_dgated_grouped(const void *grad, const void *x, int64_t N,
  * (x is [M][2K], y is [M][K]), or the gated backward for op = 0x200 |
  * MX_GATED_SWIGLU / MX_GATED_GEGLU (x is [M][2K], grad [M][K], y [M][2K]).
  * This is the exact tensor the fused casts quantise; it is exposed so that
- * the pre-op arithmetic can be checked on its own.  M a positive multiple of
- * 16, K of 8, each <= 2^23 (2K <= 2^23 for gated ops).
+ * the pre-op arithmetic can be checked on its own.  Any M, K >= 1, each
+ * <= 2^23 (2K <= 2^23 for gated ops), M * K <= 2^40.
  */
 #define MX_OP_GATED 0x100
 #define MX_OP_DGATED 0x200

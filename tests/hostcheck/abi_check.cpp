@@ -73,24 +73,49 @@ static void check_plan(int64_t M, int64_t K, int tiles_m, int tiles_k, int group
     CHECK((int64_t)groups_m * tiles_k <= INT32_MAX);
 }
 
-static void check_mx(int64_t M, int64_t K, bool tiled)
+// The launch plan of the any-shape kernel for one M x K tensor: 64 x 128
+// steps, walks of at most kAnyMaxWalk steps, one group.
+static void check_any_plan(int64_t M, int64_t K)
+{
+    const mxk::MxArgs &a = g_rec.mx;
+    const mxk::GroupTable &gt = g_rec.gt;
+    CHECK(a.tiles_m == ceil_div(M, mxk::kAnyTileM) && a.tiles_k == ceil_div(K, mxk::kAnyTileK));
+    CHECK(a.group >= 1 && a.group <= mxk::kAnyMaxWalk);
+    CHECK(a.groups_m == ceil_div(a.tiles_m, a.group));
+    CHECK((int64_t)a.groups_m * a.tiles_k <= INT32_MAX);
+    CHECK(gt.count == 1 && gt.len[0] == a.group && gt.walk0[0] == 0 && gt.walk0[1] == a.groups_m);
+    CHECK(gt.row0[0] == 0 && gt.row0[1] == M && gt.srow_off[0] == 0 && gt.scol_off[0] == 0);
+}
+
+// The shapes the tiled kernel takes (M a multiple of 16, K of 8); others go
+// to the any-shape kernel.
+static bool tiled_kernel_shape(int64_t M, int64_t K) { return M % 16 == 0 && K % 8 == 0; }
+
+static void check_mx(int64_t M, int64_t K, bool tiled, bool any = false)
 {
     const mxk::MxArgs &a = g_rec.mx;
     CHECK(a.M == M && a.K == K);
     CHECK((a.tiled != 0) == tiled);
-    check_plan(M, K, a.tiles_m, a.tiles_k, a.group, a.groups_m, tiled);
+    CHECK(g_rec.kind == (any ? mxk::kLaunchMxAny : mxk::kLaunchMx));
+    if (any)
+        check_any_plan(M, K);
+    else
+        check_plan(M, K, a.tiles_m, a.tiles_k, a.group, a.groups_m, tiled);
 }
 
-// A group table over G groups of the given row counts, stacked.
-static void check_groups(const int64_t *rows, int G, int walks_total)
+// A group table over G groups of the given row counts, stacked (walks of the
+// tiled kernel, or with any of the any-shape kernel).
+static void check_groups(const int64_t *rows, int G, int walks_total, bool any = false)
 {
     const mxk::GroupTable &gt = g_rec.gt;
+    const int tile = any ? mxk::kAnyTileM : mxk::kTileM;
+    const int maxlen = any ? mxk::kAnyMaxWalk : mxk::kMaxGroup;
     CHECK(gt.count == G);
     int64_t r = 0;
     for (int g = 0; g < G; g++) {
         CHECK(gt.row0[g] == r);
-        CHECK(gt.len[g] >= 1 && gt.len[g] <= mxk::kMaxGroup);
-        CHECK(gt.walk0[g + 1] - gt.walk0[g] == ceil_div(ceil_div(rows[g], mxk::kTileM), gt.len[g]));
+        CHECK(gt.len[g] >= 1 && gt.len[g] <= maxlen);
+        CHECK(gt.walk0[g + 1] - gt.walk0[g] == ceil_div(ceil_div(rows[g], tile), gt.len[g]));
         r += rows[g];
     }
     CHECK(gt.row0[G] == r);
@@ -107,8 +132,13 @@ static void mx_quantize_cases()
     EXPECT(MX_OK, mx_quantize(P(0), nullptr, 16384, 16384, both, 0, qr, sr, qc, sc, nullptr,
                               nullptr, 0, 0));
     check_mx(16384, 16384, false);
+    // ... and shapes for the any-shape kernel: rows or row lengths that are
+    // not multiples of 16 and 8, down to 1, up to the limits
     const int64_t shapes[][2] = {{kDim, 1 << 17}, {1 << 17, kDim}, {16, kDim}, {kDim, 8},
-                                 {16, 8}, {kDim, kDim >> 6}, {16400, 7176}};
+                                 {16, 8}, {kDim, kDim >> 6}, {16400, 7176},
+                                 {1, 1}, {1, kDim}, {kDim, 1}, {17, 9}, {16383, 16383},
+                                 {kDim - 1, (1 << 17) - 1}, {(1 << 17) - 3, kDim}, {40, 64},
+                                 {kDim, 12}, {kDim >> 6, kDim - 4}};
     for (auto &s : shapes) {
         for (unsigned flags : {0u, (unsigned)MX_SCALE_TILED, MX_ELEM_E5M2 | MX_SCALE_ROUND_UP}) {
             for (int fusion : {0, MX_FUSE_GELU, MX_FUSE_DGELU | MX_FUSE_DBIAS, MX_FUSE_DSILU}) {
@@ -116,7 +146,7 @@ static void mx_quantize_cases()
                 CHECK(((fusion & MX_FUSE_DBIAS) != 0) == (need > 0));
                 EXPECT(MX_OK, mx_quantize(P(0), P(1), s[0], s[1], both | flags, fusion, qr, sr, qc,
                                           sc, db, ws, need, 0));
-                check_mx(s[0], s[1], flags & MX_SCALE_TILED);
+                check_mx(s[0], s[1], flags & MX_SCALE_TILED, !tiled_kernel_shape(s[0], s[1]));
                 if (need) {
                     CHECK(g_rec.segments == g_rec.mx.groups_m);
                     CHECK(need == (size_t)g_rec.mx.groups_m * (size_t)s[1] * 4);
@@ -133,9 +163,10 @@ static void mx_quantize_cases()
     // shapes
     const int64_t bad[][2] = {{kDim + 16, 8},  {16, kDim + 8}, {kDim, (1 << 17) + 8},
                               {0, 8},          {16, 0},        {-16, 8},
-                              {16, -8},        {8, 8},         {16, 4},
+                              {16, -8},        {kDim + 1, 1},  {1, kDim + 1},
                               {kBig, kBig},    {kBig - 15, 8}, {16, kBig - 7},
-                              {INT64_MIN, 8},  {int64_t(1) << 62, int64_t(1) << 62}};
+                              {INT64_MIN, 8},  {int64_t(1) << 62, int64_t(1) << 62},
+                              {kDim, (1 << 17) + 1}, {-1, -1}};
     for (auto &s : bad) {
         EXPECT(MX_ERR_SHAPE, mx_quantize(P(0), nullptr, s[0], s[1], both, 0, qr, sr, qc, sc,
                                          nullptr, nullptr, 0, 0));
@@ -191,26 +222,31 @@ static void gated_cases()
 {
     const unsigned both = MX_ROWWISE | MX_COLWISE;
     uint8_t *qr = P(2), *sr = P(3), *qc = P(4), *sc = P(5);
-    const int64_t ok[][2] = {{128, kDim / 2}, {kDim, 8}, {16, 8}, {kDim, 1 << 16}, {8192, 4096}};
+    const int64_t ok[][2] = {{128, kDim / 2}, {kDim, 8}, {16, 8}, {kDim, 1 << 16}, {8192, 4096},
+                             {1, 1}, {17, 4}, {kDim - 1, 1 << 16}, {128, kDim / 2 - 1}, {40, 12},
+                             {kDim, (1 << 16) - 1}};
     for (auto &s : ok) {
+        // the tiled kernel needs M a multiple of 16 and N of 8 (both halves aligned)
+        const bool any = !(s[0] % 16 == 0 && s[1] % 8 == 0);
         for (int act : {MX_GATED_SWIGLU, MX_GATED_GEGLU}) {
             EXPECT(MX_OK, mx_quantize_gated(P(0), s[0], s[1], both, act, qr, sr, qc, sc, 0));
-            check_mx(s[0], s[1], false);
+            check_mx(s[0], s[1], false, any);
             CHECK(g_rec.mx.ldx == 2 * s[1] && g_rec.mx.lin_off == s[1]);
             EXPECT(MX_OK, mx_quantize_dgated(P(1), P(0), s[0], s[1], both | MX_SCALE_TILED, act, qr,
                                              sr, qc, sc, 0));
-            check_mx(s[0], 2 * s[1], true);
+            check_mx(s[0], 2 * s[1], true, any);
             CHECK(g_rec.mx.ldx == 2 * s[1] && g_rec.mx.ldg == s[1] && g_rec.mx.lin_off == s[1]);
         }
     }
-    const int64_t bad[][2] = {{128, kDim / 2 + 8}, {kDim + 16, 8}, {16, 4}, {16, kBig},
+    const int64_t bad[][2] = {{128, kDim / 2 + 8}, {kDim + 16, 8}, {16, 0}, {16, kBig},
                               {kBig, 8},           {16, kBig / 2 + 1}, {16, INT64_MIN},
-                              {16, -8},            {int64_t(1) << 62, int64_t(1) << 62}};
+                              {16, -8},            {int64_t(1) << 62, int64_t(1) << 62},
+                              {0, 8},              {128, kDim / 2 + 1}};
     for (auto &s : bad) {
         EXPECT(MX_ERR_SHAPE, mx_quantize_gated(P(0), s[0], s[1], both, MX_GATED_SWIGLU, qr, sr, qc, sc, 0));
         EXPECT(MX_ERR_SHAPE, mx_quantize_dgated(P(1), P(0), s[0], s[1], both, MX_GATED_GEGLU, qr, sr,
                                                 qc, sc, 0));
-        if (s[1] > 0 && s[1] <= kDim / 2 && s[1] % 8 == 0)
+        if (s[1] > 0 && s[1] <= kDim / 2)
             continue;   // N itself is valid for the grouped casts below
         const int64_t rows[2] = {16, 16};
         EXPECT(MX_ERR_SHAPE, mx_quantize_gated_grouped(P(0), s[1], rows, 2, both, MX_GATED_SWIGLU, qr,
@@ -227,6 +263,10 @@ static void gated_cases()
     for (int op : {MX_FUSE_GELU, MX_FUSE_DGELU, MX_FUSE_DSILU, MX_OP_GATED | MX_GATED_SWIGLU,
                    MX_OP_DGATED | MX_GATED_GEGLU}) {
         EXPECT(MX_OK, mx_fused_values(P(0), P(1), 16, 8, op, P(2), 0));
+        CHECK(g_rec.kind == mxk::kLaunchValues);
+        EXPECT(MX_OK, mx_fused_values(P(0), P(1), 3, 7, op, P(2), 0));
+        CHECK(g_rec.kind == mxk::kLaunchValuesAny && g_rec.M == 3 && g_rec.K == 7);
+        EXPECT(MX_ERR_SHAPE, mx_fused_values(P(0), P(1), 0, 8, op, P(2), 0));
         EXPECT(MX_ERR_SHAPE, mx_fused_values(P(0), P(1), kBig, kBig, op, P(2), 0));
         EXPECT(MX_ERR_SHAPE, mx_fused_values(P(0), P(1), 16, kBig / 2 + 1, op, P(2), 0));
     }
@@ -246,21 +286,35 @@ static void grouped_cases()
         full[g] = g % 4 == 3 ? 0 : (kDim / 48) & ~int64_t(15);
     const int64_t moe[8] = {1104, 3008, 1072, 6560, 1632, 608, 2256, 144};
     const int64_t one[1] = {kDim};
+    // row counts that are not multiples of 16 (the any-shape kernel)
+    const int64_t ragged[8] = {1101, 3008, 0, 6563, 1, 608, 2255, 17};
+    int64_t full_odd[64];
+    for (int g = 0; g < 64; g++)
+        full_odd[g] = g % 4 == 3 ? 0 : (kDim / 48) - 1;
     struct Case { const int64_t *rows; int G; int64_t K; } cases[] = {
         {full, 64, 1 << 17}, {moe, 8, 7168}, {one, 1, 1 << 17}, {moe, 8, 8}, {one, 1, 1 << 16},
-        {full, 64, 1 << 16}};
+        {full, 64, 1 << 16}, {ragged, 8, 7168}, {moe, 8, 7000}, {ragged, 8, 1}, {full_odd, 64, 1 << 17},
+        {one, 1, (1 << 17) - 1}};
     for (auto &c : cases) {
         int64_t M = 0;
-        for (int g = 0; g < c.G; g++)
+        bool rows16 = true;
+        for (int g = 0; g < c.G; g++) {
             M += c.rows[g];
+            rows16 = rows16 && c.rows[g] % 16 == 0;
+        }
+        const bool any = !(rows16 && c.K % 8 == 0);
         for (unsigned flags : {0u, (unsigned)MX_SCALE_TILED}) {
             for (int fusion : {0, MX_FUSE_DBIAS, MX_FUSE_DGELU | MX_FUSE_DBIAS}) {
                 const size_t need = mx_quantize_grouped_workspace_size(c.K, c.rows, c.G, both | flags,
                                                                       fusion);
                 EXPECT(MX_OK, mx_quantize_grouped(P(0), P(1), c.K, c.rows, c.G, both | flags, fusion,
                                                   qr, sr, qc, sc, db, ws, need, 0));
-                CHECK(g_rec.kind == mxk::kLaunchMxGrouped && g_rec.mx.M == M);
-                check_groups(c.rows, c.G, g_rec.mx.groups_m);
+                CHECK(g_rec.kind == (any ? mxk::kLaunchMxAny : mxk::kLaunchMxGrouped) &&
+                      g_rec.mx.M == M);
+                CHECK(g_rec.mx.tiles_k == ceil_div(c.K, any ? mxk::kAnyTileK : mxk::kTileK));
+                check_groups(c.rows, c.G, g_rec.mx.groups_m, any);
+                if (fusion & MX_FUSE_DBIAS)
+                    CHECK(need == (size_t)g_rec.mx.groups_m * (size_t)c.K * 4);
                 CHECK((int64_t)g_rec.mx.groups_m * g_rec.mx.tiles_k <= INT32_MAX);
                 const size_t srow = mx_grouped_scale_size(c.K, c.rows, c.G, both | flags, 0);
                 const size_t scol = mx_grouped_scale_size(c.K, c.rows, c.G, both | flags, 1);
@@ -278,16 +332,18 @@ static void grouped_cases()
         EXPECT(gated_ok ? MX_OK : MX_ERR_SHAPE,
                mx_quantize_gated_grouped(P(0), c.K, c.rows, c.G, both, MX_GATED_SWIGLU, qr, sr, qc,
                                          sc, 0));
-        if (gated_ok)
-            check_groups(c.rows, c.G, g_rec.mx.groups_m);
+        if (gated_ok) {
+            CHECK(g_rec.kind == (any ? mxk::kLaunchMxAny : mxk::kLaunchMxGrouped));
+            check_groups(c.rows, c.G, g_rec.mx.groups_m, any);
+        }
         EXPECT(gated_ok ? MX_OK : MX_ERR_SHAPE,
                mx_quantize_dgated_grouped(P(1), P(0), c.K, c.rows, c.G, both | MX_SCALE_TILED,
                                           MX_GATED_GEGLU, qr, sr, qc, sc, 0));
         if (gated_ok) {
             CHECK(g_rec.mx.K == 2 * c.K && g_rec.mx.tiled == 1);
-            check_groups(c.rows, c.G, g_rec.mx.groups_m);
+            check_groups(c.rows, c.G, g_rec.mx.groups_m, any);
         }
-        if (c.K % 16 == 0) {
+        if (c.K % 16 == 0 && rows16) {
             for (int two_d : {0, 1}) {
                 EXPECT(MX_OK, nvfp4_quantize_transpose_grouped(P(0), c.K, c.rows, c.G, P<float>(1), two_d,
                                                                both, qr, sr, qc, sc, P<float>(6), 0));
@@ -298,11 +354,12 @@ static void grouped_cases()
         }
     }
     // malformed group lists
-    const int64_t neg[2] = {16, -16}, odd[2] = {16, 8}, huge[2] = {16, kBig}, over[2] = {kDim, 16},
-                  empty[3] = {0, 0, 0}, wrap[3] = {kBig - 15, kBig - 15, 48};
+    const int64_t neg[2] = {16, -16}, huge[2] = {16, kBig}, over[2] = {kDim, 16},
+                  over1[2] = {kDim, 1}, empty[3] = {0, 0, 0}, wrap[3] = {kBig - 15, kBig - 15, 48},
+                  neg1[2] = {17, -1};
     struct Bad { const int64_t *rows; int G; } bads[] = {
-        {neg, 2}, {odd, 2}, {huge, 2}, {over, 2}, {empty, 3}, {wrap, 3}, {full, 65}, {full, 0},
-        {full, -1}, {nullptr, 2}};
+        {neg, 2}, {huge, 2}, {over, 2}, {over1, 2}, {empty, 3}, {wrap, 3}, {full, 65}, {full, 0},
+        {full, -1}, {nullptr, 2}, {neg1, 2}};
     for (auto &b : bads) {
         const mx_status want = b.rows ? MX_ERR_SHAPE : MX_ERR_NULL;
         EXPECT(want, mx_quantize_grouped(P(0), nullptr, 256, b.rows, b.G, both, 0, qr, sr, qc, sc,
@@ -314,6 +371,14 @@ static void grouped_cases()
         CHECK(mx_quantize_grouped_workspace_size(256, b.rows, b.G, both, MX_FUSE_DBIAS) == 0);
         CHECK(mx_grouped_scale_size(256, b.rows, b.G, both, 0) == 0);
     }
+    // NVFP4 keeps whole 16-element blocks: group rows must be multiples of 16
+    const int64_t odd[2] = {16, 8};
+    EXPECT(MX_ERR_SHAPE, nvfp4_quantize_transpose_grouped(P(0), 256, odd, 2, P<float>(1), 0, both,
+                                                          qr, sr, qc, sc, nullptr, 0));
+    EXPECT(MX_ERR_SHAPE, mx_absmax_bf16_grouped(P(0), 256, odd, 2, P<float>(1), 0));
+    EXPECT(MX_OK, mx_quantize_grouped(P(0), nullptr, 256, odd, 2, both, 0, qr, sr, qc, sc, nullptr,
+                                      nullptr, 0, 0));
+    CHECK(g_rec.kind == mxk::kLaunchMxAny);
     for (int64_t K : {kBig, int64_t(0), int64_t(-16), kDim + 16, INT64_MIN}) {
         EXPECT(MX_ERR_SHAPE, mx_quantize_grouped(P(0), nullptr, K, moe, 8, both, 0, qr, sr, qc, sc,
                                                  nullptr, nullptr, 0, 0));

@@ -31,6 +31,14 @@ hipError_t launch_mx_cast_grouped(int op, unsigned axis, unsigned fmt, bool dbia
     return note(kLaunchMxGrouped);
 }
 
+hipError_t launch_mx_cast_any(int op, unsigned axis, unsigned fmt, bool dbias, const MxArgs &a,
+                              const GroupTable &gt, hipStream_t)
+{
+    g_rec.op = op, g_rec.axis = axis, g_rec.fmt = fmt, g_rec.dbias = dbias, g_rec.mx = a;
+    g_rec.gt = gt;
+    return note(kLaunchMxAny);
+}
+
 hipError_t launch_dbias_reduce_grouped(const float *, const GroupTable &gt, int64_t K, float *,
                                        hipStream_t)
 {
@@ -59,6 +67,13 @@ hipError_t launch_fused_values(int op, const uint16_t *, const uint16_t *, int64
 {
     g_rec.op = op, g_rec.M = M, g_rec.K = K;
     return note(kLaunchValues);
+}
+
+hipError_t launch_fused_values_any(int op, const uint16_t *, const uint16_t *, int64_t M,
+                                   int64_t K, uint16_t *, hipStream_t)
+{
+    g_rec.op = op, g_rec.M = M, g_rec.K = K;
+    return note(kLaunchValuesAny);
 }
 
 hipError_t launch_absmax(const uint16_t *, int64_t n, float *, hipStream_t)

@@ -41,7 +41,7 @@ def header_abi_version():
 
 
 def test_version_and_status_strings():
-    assert mx.mx_abi_version() == header_abi_version() == 9
+    assert mx.mx_abi_version() == header_abi_version() == 10
     for code in range(9):
         assert mx.mx_status_str(code).startswith("MX_")
     assert "unknown" in mx.mx_status_str(99)
@@ -70,7 +70,9 @@ def test_workspace_size():
         assert ws(M, K, 3, mx.FUSE_DBIAS) == walks(M, K) * K * 4
         for pre in (mx.FUSE_GELU, mx.FUSE_DGELU, mx.FUSE_DSILU):
             assert ws(M, K, 3, pre | mx.FUSE_DBIAS) == walks(M, K) * K * 4
-    assert ws(40, 64, 3, mx.FUSE_DBIAS) == 0      # invalid shape
+    assert ws(0, 64, 3, mx.FUSE_DBIAS) == 0       # invalid shape
+    assert ws(40, 64, 3, mx.FUSE_DBIAS) == 64 * 4  # any-shape kernel: one walk
+    assert ws(16383, 16383, 3, mx.FUSE_DBIAS) == 32 * 16383 * 4   # walks of 8 x 64 rows
     assert ws(48, 72, 3, mx.FUSE_DBIAS) == 72 * 4  # partial blocks: one walk
     assert ws(64, 64, 0, mx.FUSE_DBIAS) == 0      # invalid axis
     assert ws(64, 64, 3, 0x14) == 0               # invalid pre-op
@@ -153,7 +155,7 @@ NULL = ctypes.c_void_p(0)
     (dict(axis=0x10), mx.MX_ERR_ENUM),
     (dict(axis=3 | mx.SCALE_TILED, x=NULL), mx.MX_ERR_NULL),
     (dict(axis=3 | mx.ELEM_E5M2 | mx.SCALE_ROUND_UP, x=NULL), mx.MX_ERR_NULL),  # flags accepted
-    (dict(axis=1 | mx.ELEM_E5M2, M=40), mx.MX_ERR_SHAPE),
+    (dict(axis=1 | mx.ELEM_E5M2, M=0), mx.MX_ERR_SHAPE),
     (dict(fusion=5), mx.MX_ERR_ENUM),
     (dict(fusion=0x20), mx.MX_ERR_ENUM),
     (dict(fusion=4), mx.MX_ERR_ENUM),
@@ -163,8 +165,8 @@ NULL = ctypes.c_void_p(0)
     (dict(axis=1, s_row=NULL), mx.MX_ERR_NULL),
     (dict(axis=2, q_col=NULL), mx.MX_ERR_NULL),
     (dict(fusion=mx.FUSE_DBIAS, dbias=NULL), mx.MX_ERR_NULL),
-    (dict(M=40), mx.MX_ERR_SHAPE),             # M must be a multiple of 16
-    (dict(K=36), mx.MX_ERR_SHAPE),             # K must be a multiple of 8
+    (dict(M=0), mx.MX_ERR_SHAPE),              # any M, K >= 1 (up to the limits) is a shape
+    (dict(K=-8), mx.MX_ERR_SHAPE),
     (dict(K=0), mx.MX_ERR_SHAPE),
     (dict(M=-32), mx.MX_ERR_SHAPE),
     (dict(M=1 << 31), mx.MX_ERR_SHAPE),
@@ -205,7 +207,7 @@ def test_gated_and_fused_values_reject():
     assert g(axis=0) == mx.MX_ERR_ENUM and g(axis=8) == mx.MX_ERR_ENUM and g(axis=0x23) == mx.MX_ERR_ENUM
     assert g(axis=3 | mx.ELEM_E5M2 | mx.SCALE_ROUND_UP, x=NULL) == mx.MX_ERR_NULL
     assert g(x=NULL) == mx.MX_ERR_NULL
-    assert g(N=44) == mx.MX_ERR_SHAPE and g(M=8) == mx.MX_ERR_SHAPE
+    assert g(N=0) == mx.MX_ERR_SHAPE and g(M=-16) == mx.MX_ERR_SHAPE and g(N=1 << 23) == mx.MX_ERR_SHAPE
     assert g(x=b.p("x", 4)) == mx.MX_ERR_ALIGN
     assert g(q_row=b.p("x", 32)) == mx.MX_ERR_ALIAS
     f = lambda **kw: L.mx_fused_values(kw.get("x", b.p("x")), kw.get("g", b.p("g")), kw.get("M", 64),
@@ -214,7 +216,7 @@ def test_gated_and_fused_values_reject():
     assert f(op=0) == mx.MX_ERR_ENUM and f(op=mx.FUSE_DBIAS) == mx.MX_ERR_ENUM
     assert f(op=mx.OP_GATED | 3) == mx.MX_ERR_ENUM
     assert f(y=NULL) == mx.MX_ERR_NULL and f(op=mx.FUSE_DGELU, g=NULL) == mx.MX_ERR_NULL
-    assert f(K=36) == mx.MX_ERR_SHAPE
+    assert f(K=0) == mx.MX_ERR_SHAPE and f(M=-1) == mx.MX_ERR_SHAPE
     assert f(y=b.p("q_row", 2)) == mx.MX_ERR_ALIGN
     assert f(y=b.p("x", 16)) == mx.MX_ERR_ALIAS
     assert b.untouched()
@@ -232,7 +234,7 @@ def test_dgated_and_backward_values_reject():
     assert d(axis=0x43) == mx.MX_ERR_ENUM and d(axis=2 | mx.ELEM_E5M2, x=NULL) == mx.MX_ERR_NULL
     assert d(g=NULL) == mx.MX_ERR_NULL and d(x=NULL) == mx.MX_ERR_NULL
     assert d(axis=1, s_row=NULL) == mx.MX_ERR_NULL
-    assert d(N=44) == mx.MX_ERR_SHAPE and d(M=0) == mx.MX_ERR_SHAPE
+    assert d(N=0) == mx.MX_ERR_SHAPE and d(M=0) == mx.MX_ERR_SHAPE and d(N=1 << 23) == mx.MX_ERR_SHAPE
     assert d(g=b.p("g", 2)) == mx.MX_ERR_ALIGN and d(s_col=b.p("s_col", 8)) == mx.MX_ERR_ALIGN
     assert d(q_col=b.p("g", 16)) == mx.MX_ERR_ALIAS and d(q_row=b.p("x", 64)) == mx.MX_ERR_ALIAS
     f = lambda **kw: L.mx_fused_values(kw.get("x", b.p("x")), kw.get("g", b.p("g")), 64, 64,
@@ -280,7 +282,8 @@ def test_grouped_sizes():
     assert sz(96, [48, 0, 80], 3, False) == 128 * 3
     assert sz(96, [48, 0, 80], 3, True) == 96 * 2 + 96 * 3
     assert sz(96, [48, 0, 80], 3 | mx.SCALE_TILED, True) == 3 * 1 * 256 + 3 * 1 * 256
-    assert sz(96, [40], 3, False) == 0 and sz(96, [0, 0], 3, False) == 0 and sz(96, [], 3, False) == 0
+    assert sz(96, [40], 3, False) == 40 * 3 and sz(96, [40, 8], 3, True) == 96 * 2 + 96 * 1
+    assert sz(96, [-16], 3, False) == 0 and sz(96, [0, 0], 3, False) == 0 and sz(96, [], 3, False) == 0
 
 
 def test_grouped_rejects():
@@ -299,12 +302,11 @@ def test_grouped_rejects():
     assert gq(axis=0) == mx.MX_ERR_ENUM and gq(fusion=5) == mx.MX_ERR_ENUM
     assert gq(x=NULL) == mx.MX_ERR_NULL and gq(rows_p=NULL) == mx.MX_ERR_NULL
     assert gq(fusion=mx.FUSE_DGELU, g=NULL) == mx.MX_ERR_NULL
-    assert gq(rows=(32, 8)) == mx.MX_ERR_SHAPE          # not a multiple of 16
     assert gq(rows=(32, -16, 48)) == mx.MX_ERR_SHAPE
     assert gq(rows=(0, 0)) == mx.MX_ERR_SHAPE            # no rows at all
     assert gq(rows=(32,), G=0) == mx.MX_ERR_SHAPE
     assert gq(rows=tuple([16] * 65)) == mx.MX_ERR_SHAPE   # more than 64 groups
-    assert gq(K=36) == mx.MX_ERR_SHAPE
+    assert gq(K=0) == mx.MX_ERR_SHAPE and gq(rows=(32, (1 << 23) + 1)) == mx.MX_ERR_SHAPE
     assert gq(x=b.p("x", 8)) == mx.MX_ERR_ALIGN
     assert gq(fusion=mx.FUSE_DBIAS, ws=NULL) == mx.MX_ERR_WORKSPACE
     assert gq(fusion=mx.FUSE_DBIAS, ws_bytes=16) == mx.MX_ERR_WORKSPACE
@@ -329,7 +331,7 @@ def test_grouped_gated_rejects():
     for bwd in (False, True):
         assert gg(bwd=bwd, act=0) == mx.MX_ERR_ENUM and gg(bwd=bwd, axis=0x40 | 3) == mx.MX_ERR_ENUM
         assert gg(bwd=bwd, x=NULL) == mx.MX_ERR_NULL
-        assert gg(bwd=bwd, rows=(32, 8)) == mx.MX_ERR_SHAPE and gg(bwd=bwd, N=12) == mx.MX_ERR_SHAPE
+        assert gg(bwd=bwd, rows=(32, -16)) == mx.MX_ERR_SHAPE and gg(bwd=bwd, N=0) == mx.MX_ERR_SHAPE
         assert gg(bwd=bwd, G=0) == mx.MX_ERR_SHAPE
         assert gg(bwd=bwd, x=b.p("x", 4)) == mx.MX_ERR_ALIGN
         assert gg(bwd=bwd, q_row=b.p("x", 16)) == mx.MX_ERR_ALIAS
@@ -393,7 +395,7 @@ def test_noalloc_rejects_before_any_launch():
     assert qn(axis=0) == mx.MX_ERR_ENUM
     assert qn(x=NULL) == mx.MX_ERR_NULL
     assert qn(fusion=mx.FUSE_DBIAS, dbias=NULL) == mx.MX_ERR_NULL
-    assert qn(M=40) == mx.MX_ERR_SHAPE
+    assert qn(M=0) == mx.MX_ERR_SHAPE
     assert qn(x=b.p("x", 8)) == mx.MX_ERR_ALIGN
     assert qn(q_row=b.p("x", 16)) == mx.MX_ERR_ALIAS
     # 128 x 2^21 with dbias: one walk of 2^21 fp32 partials = 8 MiB > 4 MiB

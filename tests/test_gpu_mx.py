@@ -133,7 +133,7 @@ def test_deterministic_and_guard_bands():
 
 
 def test_error_raises_through_binding():
-    xd = to_dev(np.zeros((40, 64), np.uint16))     # M not a multiple of 16
+    xd = to_dev(np.zeros((40, 64), np.uint16))
     with pytest.raises(mx.MxError) as e:
-        mx.mx_quantize(xd)
-    assert e.value.status == mx.MX_ERR_SHAPE
+        mx.mx_quantize(xd, axis=0x40 | 3)           # an unknown axis flag
+    assert e.value.status == mx.MX_ERR_ENUM

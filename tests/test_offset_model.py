@@ -392,3 +392,230 @@ def test_model_sees_the_linear_half_overrun():
     ox = row * 2 * ldx + 2 * k
     ck.access("old linear", rx, ox + 2 * N + r * 2 * ldx, 16, np.ones_like(ox + r, dtype=bool))
     assert ck.bad and "past the descriptor" in ck.bad[0][1]
+
+
+# ---------------------------------------------------------------------------
+# The any-shape MXFP8 cast (mx_cast_any.hip): 64 x 128 steps, walks of up to
+# 8 steps, one descriptor per row for the loads (scalar: the row is the same
+# for every lane of a wave), staged stores in pieces of W = 16, 4 or 1 bytes.
+# ---------------------------------------------------------------------------
+ANY_M, ANY_K, ANY_WALK, ANY_TARGET = 64, 128, 8, 1024
+
+
+def any_walk_len(rows, K):
+    """any_walk_len (launch.h)."""
+    tk = -(-K // ANY_K)
+    L = ANY_WALK
+    while L > 1:
+        walks = sum(-(-(-(-r // ANY_M)) // L) for r in rows)
+        if walks * tk >= ANY_TARGET:
+            break
+        L >>= 1
+    return L
+
+
+def tile_offset(r, b, RT):
+    return ((b >> 3) * RT + (r >> 5)) * 256 + 4 * (32 * (b & 1) + (r & 31)) + ((b & 7) >> 1)
+
+
+def piece_width(n):
+    return 16 if n % 16 == 0 else 4 if n % 4 == 0 else 1
+
+
+def any_sites(M, K, op, tiled, walk, tk, steps, writes=None):
+    """Every access of workgroup (walk, tk) for the given steps of its walk,
+    as (site, descriptor, offsets, bytes, live, logical address) tuples."""
+    if op == "gated":
+        ldx, lin_off, ldg = 2 * K, K, 0
+    elif op == "dgated":
+        ldx, lin_off, ldg = K, K // 2, K // 2
+    elif op == "grad":
+        ldx, lin_off, ldg = K, 0, K
+    else:
+        ldx, lin_off, ldg = K, 0, 0
+    L = any_walk_len([M], K)
+    tiles_m, tiles_k = -(-M // ANY_M), -(-K // ANY_K)
+    walks = -(-tiles_m // L)
+    t = np.arange(THREADS)
+    c, lane = t & 127, t & 63
+    wv = t >> 6
+    nbK, nbM = (K + 31) >> 5, (M + 31) >> 5
+    t0 = walk * L
+    n = min(L, tiles_m - t0)
+    k0 = tk * ANY_K
+    k = k0 + c
+    col_ok = k < K
+    out = []
+    for s in steps:
+        if s >= n:
+            continue
+        m0 = (t0 + s) * ANY_M
+        # loads: thread (c, h) reads rows m0 + 32 h + i of column k
+        for h in (0, 1):
+            # the threads of half h (128 of them: columns c = 0..127)
+            kh, okh = k[t >> 7 == h], col_ok[t >> 7 == h]
+            for i in (0, 15, 16, 31):
+                row = m0 + 32 * h + i
+                if op == "dgated":
+                    N = lin_off
+                    gate = kh < N
+                    nn = np.where(gate, kh, kh - N)
+                    ox = np.where(okh, 2 * nn, DEAD)
+                    ol = np.where(okh & gate, 2 * nn, DEAD)
+                    live = okh & (row < M)
+                    out.append(("any gate", Desc(2 * row * ldx, 2 * M * ldx), ox, 2, live,
+                                2 * (row * ldx + nn)))
+                    out.append(("any grad", Desc(2 * row * ldg, 2 * M * ldg), ox, 2, live,
+                                2 * (row * ldg + nn)))
+                    out.append(("any linear", Desc(2 * (row * ldx + N), 2 * M * ldx), ol, 2,
+                                live & gate, 2 * (row * ldx + N + nn)))
+                    continue
+                ox = np.where(okh, 2 * kh, DEAD)
+                live = okh & (row < M)
+                out.append(("any x", Desc(2 * row * ldx, 2 * M * ldx), ox, 2, live,
+                            2 * (row * ldx + kh)))
+                if op == "gated":
+                    out.append(("any linear", Desc(2 * (row * ldx + lin_off), 2 * M * ldx), ox, 2,
+                                live, 2 * (row * ldx + lin_off + kh)))
+                elif op == "grad":
+                    out.append(("any grad", Desc(2 * row * ldg, 2 * M * ldg), ox, 2, live,
+                                2 * (row * ldg + kh)))
+        # row scales: thread (r = t / 4, q = t % 4), block b = 4 tk + q
+        r, q = t >> 2, t & 3
+        blocks = [4 * tk + q]
+        if tiled and tk + 1 == tiles_k and tk % 2 == 0:
+            blocks.append(4 * tk + q + 4)
+        for b in blocks:
+            if not tiled:
+                ok = (m0 + r < M) & (b < nbK)
+                out.append(("any s_row", Desc(m0 * nbK, M * nbK), np.where(ok, r * nbK + b, DEAD),
+                            1, ok, (m0 + r) * nbK + b))
+            else:
+                RT, CT = (M + 31) >> 5, (nbK + 7) >> 3
+                base = tile_offset(m0, (4 * tk) & ~7, RT)
+                ok = (m0 + r < 32 * RT) & (b < 8 * CT)
+                to = tile_offset(m0 + r, b, RT)
+                out.append(("any s_row tiled", Desc(base, RT * CT * 256),
+                            np.where(ok, to - base, DEAD), 1, ok, to))
+        # q_row pieces
+        W = piece_width(K)
+        per_row = ANY_K // W
+        iters = ANY_M * per_row // THREADS
+        sub = np.zeros_like(t) if per_row >= 64 else lane // per_row
+        p = 64 * (wv % max(per_row // 64, 1)) + lane if per_row >= 64 else lane % per_row
+        krem = min(K - k0, ANY_K)
+        off = np.where(W * p < krem, sub * K + W * p, DEAD)
+        for i in range(iters):
+            qq = wv + 4 * i
+            r0 = qq // (per_row // 64) if per_row >= 64 else qq * (64 // per_row)
+            for w in range(WAVES):
+                sel = wv == w
+                r0w = int(r0[w * 64]) if isinstance(r0, np.ndarray) else r0
+                live = (W * p < krem) & (m0 + r0w + sub < M)
+                out.append((f"any q_row W={W}", Desc((m0 + r0w) * K + k0, M * K), off[sel], W,
+                            live[sel], ((m0 + r0w + sub) * K + k0 + W * p)[sel]))
+        # q_col pieces
+        W = piece_width(M)
+        per_row = ANY_M // W
+        rpw = 64 // per_row
+        iters = ANY_K // (4 * rpw)
+        sub, p = lane // per_row, lane % per_row
+        mrem = min(M - m0, ANY_M)
+        off = np.where(W * p < mrem, sub * M + W * p, DEAD)
+        for i in range(iters):
+            for w in range(WAVES):
+                sel = wv == w
+                c0 = rpw * (w + 4 * i)
+                live = (W * p < mrem) & (k0 + c0 + sub < K)
+                out.append((f"any q_col W={W}", Desc((k0 + c0) * M + m0, K * M), off[sel], W,
+                            live[sel], ((k0 + c0 + sub) * M + m0 + W * p)[sel]))
+    # column scales at the walk's end
+    jb, cnt = 2 * t0, 2 * n
+    last_walk = walk + 1 == walks
+    if not tiled:
+        idx = np.arange(ANY_K * 2 * ANY_WALK)
+        cc, jj = idx // (2 * ANY_WALK), idx % (2 * ANY_WALK)
+        ok = (jj < cnt) & (k0 + cc < K) & (jb + jj < nbM)
+        out.append(("any s_col", Desc(k0 * nbM + jb, K * nbM), np.where(ok, cc * nbM + jj, DEAD), 1,
+                    ok, (k0 + cc) * nbM + jb + jj))
+    else:
+        RT, CT = (K + 31) >> 5, (nbM + 7) >> 3
+        jend = 8 * CT if last_walk else jb + cnt
+        span = jend - jb
+        base = tile_offset(k0, jb & ~7, RT)
+        idx = np.arange(ANY_K * span)
+        cc, jj = idx // span, idx % span
+        kk, j = k0 + cc, jb + jj
+        ok = (kk < 32 * RT) & (j < 8 * CT)
+        to = tile_offset(kk, j, RT)
+        out.append(("any s_col tiled", Desc(base, RT * CT * 256), np.where(ok, to - base, DEAD), 1,
+                    ok, to))
+    # dbias partials
+    ok = (t < ANY_K) & (k < K)
+    out.append(("any partials", Desc(4 * (walk * K + k0), 4 * walks * K),
+                np.where(ok, 4 * (t & 127), DEAD), 4, ok, 4 * (walk * K + k)))
+    return out
+
+
+def any_model(M, K, op="plain", tiled=False, ck=None):
+    ck = ck or Checker()
+    L = any_walk_len([M], K)
+    tiles_m, tiles_k = -(-M // ANY_M), -(-K // ANY_K)
+    walks = -(-tiles_m // L)
+    for walk in edge(walks):
+        n = min(L, tiles_m - walk * L)
+        for tk in edge(tiles_k):
+            for site, d, off, nbytes, live, addr in any_sites(M, K, op, tiled, walk, tk,
+                                                              sorted({0, n - 1})):
+                ck.access(site, d, off, nbytes, live, addr)
+    return ck
+
+
+ANY_SHAPES = [(MAXD, 1), (1, MAXD), (MAXD - 1, 9), (MAXD, 12), (MAXD, (1 << 17) - 1),
+              ((1 << 17) - 3, MAXD), (17, MAXD - 1), (16383, 16383), (1, 1), (40, 64), (100, 36)]
+
+
+@pytest.mark.parametrize("tiled", [False, True], ids=["compact", "tiled"])
+@pytest.mark.parametrize("M,K", ANY_SHAPES)
+@pytest.mark.parametrize("op", ["plain", "grad"])
+def test_any_shape_offsets(M, K, op, tiled):
+    any_model(M, K, op, tiled).ok()
+
+
+ANY_GATED_N = [(MAXD, 1), (128, (1 << 22) - 1), (17, 1 << 22), (MAXD - 1, 4), (16383, 4093)]
+
+
+@pytest.mark.parametrize("tiled", [False, True], ids=["compact", "tiled"])
+@pytest.mark.parametrize("M,N", ANY_GATED_N)
+def test_any_shape_gated_offsets(M, N, tiled):
+    any_model(M, N, "gated", tiled).ok()
+    any_model(M, 2 * N, "dgated", tiled).ok()
+
+
+@pytest.mark.parametrize("tiled", [False, True], ids=["compact", "tiled"])
+@pytest.mark.parametrize("M,K", [(1, 1), (17, 9), (33, 40), (95, 130), (200, 300), (64, 520),
+                                 (129, 257), (300, 12), (12, 300)])
+def test_any_shape_writes_every_byte_once(M, K, tiled):
+    """Over all workgroups and steps, every byte of q_row, q_col and of both
+    scale tensors (compact, or the tile layout with its padding) is written
+    exactly once, and nothing else is."""
+    L = any_walk_len([M], K)
+    tiles_m, tiles_k = -(-M // ANY_M), -(-K // ANY_K)
+    walks = -(-tiles_m // L)
+    nbK, nbM = (K + 31) >> 5, (M + 31) >> 5
+    size = {"q_row": M * K, "q_col": K * M,
+            "s_row": ((M + 31) >> 5) * ((nbK + 7) >> 3) * 256 if tiled else M * nbK,
+            "s_col": ((K + 31) >> 5) * ((nbM + 7) >> 3) * 256 if tiled else K * nbM}
+    count = {name: np.zeros(n, np.int64) for name, n in size.items()}
+    for walk in range(walks):
+        for tk in range(tiles_k):
+            for site, d, off, nbytes, live, addr in any_sites(M, K, "plain", tiled, walk, tk,
+                                                              range(L)):
+                name = next((nm for nm in count if site.startswith("any " + nm)), None)
+                if name is None:
+                    continue
+                a = np.broadcast_to(addr, live.shape)[live]
+                for b in range(nbytes):
+                    np.add.at(count[name], a + b, 1)
+    for name, cnt in count.items():
+        assert (cnt == 1).all(), (name, int((cnt == 0).sum()), int((cnt > 1).sum()))

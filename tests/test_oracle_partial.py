@@ -30,7 +30,8 @@ def test_hand_worked_partial_block():
 
 
 @pytest.mark.parametrize("mode", [0, O.ELEM_E5M2 | O.SCALE_ROUND_UP])
-@pytest.mark.parametrize("M,K", [(16, 8), (48, 40), (80, 200), (112, 264), (33, 31)])
+@pytest.mark.parametrize("M,K", [(16, 8), (48, 40), (80, 200), (112, 264), (33, 31), (1, 1), (17, 9),
+                                 (3, 70), (70, 3)])
 def test_partial_equals_zero_padded(M, K, mode):
     x = W.loguniform_rows(M, K, seed=4000 + M + K)
     Mp, Kp = -(-M // 32) * 32, -(-K // 32) * 32

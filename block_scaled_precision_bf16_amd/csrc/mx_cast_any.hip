@@ -34,16 +34,44 @@ __device__ __forceinline__ uint32_t buf_load2(rsrc_t r, uint32_t off)
     return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, AUX);
 }
 
-// LDS of one workgroup (38.5 KB: four workgroups per CU).  Row strides are
+// LDS of one workgroup (37.5 KB: four workgroups per CU).  Row strides are
 // multiples of 16 bytes, padded so that the 16-byte accesses of 8
 // consecutive lanes fall into different banks.
 struct alignas(16) AnyStage {
-    uint16_t y[kAnyTileM][kAnyTileK + 8];       // bf16 values of the step (272-byte rows)
-    uint8_t qr[kAnyTileM][kAnyTileK + 16];      // row-wise codes (144-byte rows)
-    uint8_t qt[kAnyTileK][kAnyTileM + 16];      // transposed codes (80-byte rows)
+    // bf16 values of the step (272-byte rows).  Once the row pass has read
+    // row r, the first 128 bytes of that row hold row r's codes: the four
+    // threads of a row are lanes of one wave, whose reads precede its writes.
+    uint16_t y[kAnyTileM][kAnyTileK + 8];
+    // transposed codes, two steps per transposed row: step s at bytes
+    // 64 (s % 2) .. 64 (s % 2) + 63 (144-byte rows), so that the bytes a
+    // step leaves for the next 64-byte-aligned chunk stay next to it
+    uint8_t qt[kAnyTileK][2 * kAnyTileM + 16];
     uint8_t sc[kAnyTileK][2 * kAnyMaxWalk];     // column scales of the walk
     float dsum[kAnyTileK];                      // dbias: column sums of rows 32..63
 };
+
+__device__ __forceinline__ uint8_t *qrow_stage(AnyStage &st, int r)
+{
+    return reinterpret_cast<uint8_t *>(st.y[r]);
+}
+__device__ __forceinline__ const uint8_t *qrow_stage(const AnyStage &st, int r)
+{
+    return reinterpret_cast<const uint8_t *>(st.y[r]);
+}
+
+// Low bits of the absolute byte address p + off.
+__device__ __forceinline__ uint32_t addr_low(const void *p, int64_t off, uint32_t mask)
+{
+    return (uint32_t)((reinterpret_cast<uintptr_t>(p) + (uint64_t)off) & mask);
+}
+
+// The four bytes at staged position i (any alignment) of an LDS row whose
+// dwords at i & ~3 and (i & ~3) + 4 exist.
+__device__ __forceinline__ uint32_t lds_word_at(const uint8_t *row, int i)
+{
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(row + (i & ~3));
+    return __builtin_amdgcn_alignbyte(w[1], w[0], (uint32_t)(i & 3));
+}
 
 // One tensor of the launch (the whole input, or one group of a stack).
 struct AnyView {
@@ -190,83 +218,126 @@ __device__ __forceinline__ void any_store_srow(const MxArgs &a, const AnyView &v
 }
 
 // Staged row-wise codes of a step -> q_row: rows m0 .. m0 + 63, columns
-// k0 .. k0 + 127, in pieces of W bytes (W divides K, so a piece lies wholly
-// inside or outside the tensor).  Each wave instruction writes whole staged
-// rows (W = 4, 16: 2 or 8 of them) or half of one (W = 1), whose first row
-// is the same for all lanes: a scalar descriptor per instruction and one
-// offset register per lane.  Rows past M fall outside the descriptor,
-// pieces past K get the out-of-range offset.
-template <int W>
+// k0 .. k0 + krem - 1.  Rows whose bytes start 16-byte aligned (q_row and K
+// both aligned) leave as 16-byte pieces, 8 rows per wave instruction.
+// Otherwise each row leaves as the aligned dwords inside its segment
+// (16-byte aligned ... 1-byte aligned rows alike), two rows per wave
+// instruction, each dword assembled from two aligned LDS dwords, plus at
+// most 3 head and 3 tail bytes.  Every instruction's rows are the same for
+// all lanes of a half-wave; the descriptor starts at row m0, so rows past M
+// lie outside it.
 __device__ __forceinline__ void any_flush_qrow(const MxArgs &a, const AnyView &v, const AnyStage &st,
                                                int64_t m0, int64_t k0, int krem)
 {
-    constexpr int per_row = kAnyTileK / W;          // pieces per staged row
-    constexpr int iters = kAnyTileM * per_row / kThreads;
     const int lane = (int)threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    // instruction i covers pieces 64 (wv + 4 i) + lane of the staged tile
-    const int sub = per_row >= 64 ? 0 : lane / per_row;
-    const int p = per_row >= 64 ? 64 * (wv % (per_row / 64 > 1 ? per_row / 64 : 1)) + lane
-                                : lane % per_row;
-    const uint32_t off = W * p < krem ? (uint32_t)(sub * a.K + W * p) : kDead;
+    const rsrc_t rq = make_rsrc(v.q_row, m0 * a.K + k0, v.M * a.K);
+    const int mrem = (int)(v.M - m0 < kAnyTileM ? v.M - m0 : kAnyTileM);
+    if ((a.K & 15) == 0 && addr_low(v.q_row, 0, 15) == 0) {
+        const int sub = lane >> 3, p = lane & 7;    // 8 rows x 8 pieces per instruction
 #pragma unroll
-    for (int i = 0; i < iters; i++) {
-        const int q = wv + 4 * i;
-        const int r0 = per_row >= 64 ? q / (per_row / 64) : q * (64 / per_row);
-        const rsrc_t rq = make_rsrc(v.q_row, (m0 + r0) * a.K + k0, v.M * a.K);
-        const uint8_t *src = &st.qr[r0 + sub][W * p];
-        if constexpr (W == 16)
-            buf_store16(rq, off, *reinterpret_cast<const uint4 *>(src));
-        else if constexpr (W == 4)
-            buf_store4(rq, off, *reinterpret_cast<const uint32_t *>(src));
-        else
-            buf_store1(rq, off, *src);
+        for (int i = 0; i < 2; i++) {
+            const int r = 8 * (wv + 4 * i) + sub;
+            const bool ok = r < mrem && 16 * p < krem;
+            buf_store16(rq, ok ? (uint32_t)(r * a.K + 16 * p) : kDead,
+                        *reinterpret_cast<const uint4 *>(qrow_stage(st, r) + 16 * p));
+        }
+        return;
+    }
+    // aligned dwords: lanes 0-31 and 32-63 take dword u = lane % 32 of two rows
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const int r = 2 * (wv + 4 * i) + (lane >> 5), u = lane & 31;
+        const uint32_t al = addr_low(v.q_row, (m0 + r) * a.K + k0, 3);
+        const int head = min(krem, (int)((4 - al) & 3));
+        const int nd = (krem - head) >> 2;
+        const int i0 = head + 4 * u;
+        const bool ok = r < mrem && u < nd;
+        buf_store4(rq, ok ? (uint32_t)(r * a.K + i0) : kDead,
+                   lds_word_at(qrow_stage(st, r), ok ? i0 : 0));
+    }
+    // head bytes (slots 0-2) and tail bytes (slots 3-5) of 8 rows per instruction
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int r = 8 * (wv + 4 * i) + (lane >> 3), slot = lane & 7;
+        const uint32_t al = addr_low(v.q_row, (m0 + r) * a.K + k0, 3);
+        const int head = min(krem, (int)((4 - al) & 3));
+        const int tail0 = head + 4 * ((krem - head) >> 2);
+        const int b = slot < 3 ? slot : tail0 + slot - 3;
+        const bool ok = r < mrem && (slot < 3 ? slot < head : slot < 6 && b < krem);
+        buf_store1(rq, ok ? (uint32_t)(r * a.K + b) : kDead, qrow_stage(st, r)[ok ? b : 0]);
     }
 }
 
-// Staged transposed codes of a step -> q_col: transposed rows k0 .. k0 +
-// 127, bytes m0 .. m0 + 63 of each, in pieces of W bytes (W divides M);
-// organised as any_flush_qrow (transposed rows past K fall outside the
-// descriptor, pieces past M get the out-of-range offset).
-template <int W>
+// Transposed codes of step s -> q_col.  Transposed row c's bytes of this
+// step, codes 0 .. mrem - 1, start at an address whose offset within its
+// 64-byte chunk, sft, is the same at every step (steps are 64 rows apart).
+// The step writes the chunk that starts sft bytes before its first code:
+// bytes 0 .. sft - 1 are the previous step's last codes, still in the
+// other half of the ring, and bytes sft .. 63 this step's first.  Its last
+// sft codes wait for the next step; the walk's last step writes them too.
+// At the walk's first step the chunk's first sft bytes belong to the walk
+// before and are left alone.  Whole 16-byte pieces leave as 16-byte stores
+// (16 rows x 4 pieces per wave instruction), assembled from aligned LDS
+// dwords; pieces with bytes outside the walk leave byte by byte.
 __device__ __forceinline__ void any_flush_qcol(const MxArgs &a, const AnyView &v, const AnyStage &st,
-                                               int64_t m0, int64_t k0, int mrem)
+                                               int64_t m0, int64_t k0, int mrem, int s, bool last)
 {
-    constexpr int per_row = kAnyTileM / W;          // <= 64 pieces per staged row
-    constexpr int rows_per_wave = 64 / per_row;     // rows one wave instruction covers
-    constexpr int iters = kAnyTileK / (4 * rows_per_wave);
-    const int lane = (int)threadIdx.x & 63;
-    const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    const int sub = lane / per_row, p = lane % per_row;
-    const uint32_t off = W * p < mrem ? (uint32_t)(sub * v.M + W * p) : kDead;
+    const int t = (int)threadIdx.x;
+    const rsrc_t rc = make_rsrc(v.q_col, k0 * v.M, a.K * v.M);
+    const int np = last ? 8 : 4;                  // pieces per transposed row
+    const int shift = last ? 3 : 2;
+    for (int i = 0; i < (kAnyTileK * np) / kThreads; i++) {
+        const int idx = t + kThreads * i;
+        const int c = idx >> shift, j = idx & (np - 1);
+        const int sft = (int)addr_low(v.q_col, (k0 + c) * v.M + m0, 63);
+        const int lo = s > 0 ? 0 : sft;           // chunk bytes [lo, hi) exist
+        const int hi = sft + mrem;
+        const int64_t co = (int64_t)c * v.M + m0 - sft;   // chunk start (may be < 0 when lo > 0)
+        const int v0 = (64 * (s & 1) - sft + 16 * j) & 127;   // ring position of byte 16 j
+        const uint8_t *ring = st.qt[c];
+        const bool row_ok = k0 + c < a.K;
+        const bool whole = row_ok && lo <= 16 * j && 16 * j + 16 <= hi;
+        uint4 o;
+        {
+            const uint32_t *w = reinterpret_cast<const uint32_t *>(ring);
+            const int f = v0 >> 2, sh = v0 & 3;
+            uint32_t d[5];
 #pragma unroll
-    for (int i = 0; i < iters; i++) {
-        const int c0 = rows_per_wave * (wv + 4 * i);  // first transposed row of this instruction
-        const rsrc_t rc = make_rsrc(v.q_col, (k0 + c0) * v.M + m0, a.K * v.M);
-        const uint8_t *src = &st.qt[c0 + sub][W * p];
-        if constexpr (W == 16)
-            buf_store16(rc, off, *reinterpret_cast<const uint4 *>(src));
-        else if constexpr (W == 4)
-            buf_store4(rc, off, *reinterpret_cast<const uint32_t *>(src));
-        else
-            buf_store1(rc, off, *src);
+            for (int e = 0; e < 5; e++)
+                d[e] = w[(f + e) & 31];
+            o = make_uint4(__builtin_amdgcn_alignbyte(d[1], d[0], sh),
+                           __builtin_amdgcn_alignbyte(d[2], d[1], sh),
+                           __builtin_amdgcn_alignbyte(d[3], d[2], sh),
+                           __builtin_amdgcn_alignbyte(d[4], d[3], sh));
+        }
+        buf_store16(rc, whole ? (uint32_t)(co + 16 * j) : kDead, o);
+        const bool part = row_ok && !whole && 16 * j < hi && 16 * j + 16 > lo;
+        if (__builtin_amdgcn_ballot_w64(part) != 0) {   // uniform: first and last steps only
+#pragma unroll
+            for (int b = 0; b < 16; b++) {
+                const int pb = 16 * j + b;
+                const bool ok = part && pb >= lo && pb < hi;
+                buf_store1(rc, ok ? (uint32_t)(co + pb) : kDead, ring[(v0 + b) & 127]);
+            }
+        }
     }
 }
 
-// One 64 x 128 step (the s-th of the walk) at rows m0, columns k0.
-template <int OP, int FMT>
+// One 64 x 128 step (the s-th of the walk) at rows m0, columns k0; w: this
+// thread's column values (column k0 + t % 128, rows m0 + 32 (t / 128) + i).
+template <int FMT>
 __device__ __forceinline__ void any_step(const MxArgs &a, const AnyView &v, AnyStage &st,
-                                         int64_t m0, int tk, int s, unsigned axis, bool dbias,
-                                         bool last_tk, float &dacc)
+                                         const uint32_t (&w)[16], int64_t m0, int tk, int s,
+                                         bool last_step, unsigned axis, bool dbias, bool last_tk,
+                                         float &dacc)
 {
     const int t = (int)threadIdx.x;
     const int c = t & (kAnyTileK - 1);
     const int h = __builtin_amdgcn_readfirstlane(t >> 7);   // uniform per wave
-    const int64_t k0 = (int64_t)tk * kAnyTileK, k = k0 + c;
+    const int64_t k0 = (int64_t)tk * kAnyTileK;
     const bool row = axis & 1u, col = (axis & 2u) != 0;
 
-    uint32_t w[16];
-    any_load<OP>(a, v, m0 + 32 * h, k, k < a.K, w);
     if (row) {
 #pragma unroll
         for (int i = 0; i < 16; i++) {
@@ -288,8 +359,9 @@ __device__ __forceinline__ void any_step(const MxArgs &a, const AnyView &v, AnyS
     if (col) {
         uint32_t o[8];
         const uint32_t sb = any_block<FMT>(w, o);
-        *reinterpret_cast<uint4 *>(&st.qt[c][32 * h]) = make_uint4(o[0], o[1], o[2], o[3]);
-        *reinterpret_cast<uint4 *>(&st.qt[c][32 * h + 16]) = make_uint4(o[4], o[5], o[6], o[7]);
+        uint8_t *q = &st.qt[c][64 * (s & 1) + 32 * h];
+        *reinterpret_cast<uint4 *>(q) = make_uint4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<uint4 *>(q + 16) = make_uint4(o[4], o[5], o[6], o[7]);
         st.sc[c][2 * s + h] = (uint8_t)sb;
     }
     __syncthreads();
@@ -305,8 +377,9 @@ __device__ __forceinline__ void any_step(const MxArgs &a, const AnyView &v, AnyS
         }
         uint32_t o[8];
         const uint32_t sb = any_block<FMT>(wr, o);
-        *reinterpret_cast<uint4 *>(&st.qr[r][32 * q]) = make_uint4(o[0], o[1], o[2], o[3]);
-        *reinterpret_cast<uint4 *>(&st.qr[r][32 * q + 16]) = make_uint4(o[4], o[5], o[6], o[7]);
+        uint8_t *qd = qrow_stage(st, r) + 32 * q;   // over row r's bf16 values, already read
+        *reinterpret_cast<uint4 *>(qd) = make_uint4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<uint4 *>(qd + 16) = make_uint4(o[4], o[5], o[6], o[7]);
         const int64_t b = (int64_t)4 * tk + q;
         any_store_srow(a, v, m0, tk, r, b, sb);
         // tile layout: the last strip also writes the padding blocks of its
@@ -315,24 +388,11 @@ __device__ __forceinline__ void any_step(const MxArgs &a, const AnyView &v, AnyS
             any_store_srow(a, v, m0, tk, r, b + 4, 0u);
     }
     __syncthreads();
-    if (row) {
-        const int krem = (int)(a.K - k0 < kAnyTileK ? a.K - k0 : kAnyTileK);
-        if ((a.K & 15) == 0)
-            any_flush_qrow<16>(a, v, st, m0, k0, krem);
-        else if ((a.K & 3) == 0)
-            any_flush_qrow<4>(a, v, st, m0, k0, krem);
-        else
-            any_flush_qrow<1>(a, v, st, m0, k0, krem);
-    }
-    if (col) {
-        const int mrem = (int)(v.M - m0 < kAnyTileM ? v.M - m0 : kAnyTileM);
-        if ((v.M & 15) == 0)
-            any_flush_qcol<16>(a, v, st, m0, k0, mrem);
-        else if ((v.M & 3) == 0)
-            any_flush_qcol<4>(a, v, st, m0, k0, mrem);
-        else
-            any_flush_qcol<1>(a, v, st, m0, k0, mrem);
-    }
+    if (row)
+        any_flush_qrow(a, v, st, m0, k0, (int)(a.K - k0 < kAnyTileK ? a.K - k0 : kAnyTileK));
+    if (col)
+        any_flush_qcol(a, v, st, m0, k0, (int)(v.M - m0 < kAnyTileM ? v.M - m0 : kAnyTileM), s,
+                       last_step);
     __syncthreads();
 }
 
@@ -399,10 +459,16 @@ __global__ __launch_bounds__(kThreads, 4) void mx_cast_any_kernel(MxArgs a, Grou
     const int tiles_m = (int)((v.M + kAnyTileM - 1) / kAnyTileM);
     const int n = tiles_m - t0 < len ? tiles_m - t0 : len;
     const bool last_tk = tk + 1 == a.tiles_k;
+    const int h = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 7);
+    const int64_t k = (int64_t)tk * kAnyTileK + (threadIdx.x & (kAnyTileK - 1));
+    const bool col_ok = k < a.K;
     float dacc = 0.0f;
-    for (int s = 0; s < n; s++)
-        any_step<OP, FMT>(a, v, st, (int64_t)(t0 + s) * kAnyTileM, tk, s, axis, dbias != 0,
-                          last_tk, dacc);
+    for (int s = 0; s < n; s++) {
+        uint32_t w[16];
+        any_load<OP>(a, v, (int64_t)(t0 + s) * kAnyTileM + 32 * h, k, col_ok, w);
+        any_step<FMT>(a, v, st, w, (int64_t)(t0 + s) * kAnyTileM, tk, s, s + 1 == n, axis,
+                      dbias != 0, last_tk, dacc);
+    }
     if (axis & 2u)
         any_flush_scol(a, v, st, t0, n, tk, walk + 1 == gt.walk0[g + 1]);
     if (dbias) {

@@ -422,7 +422,7 @@ def piece_width(n):
     return 16 if n % 16 == 0 else 4 if n % 4 == 0 else 1
 
 
-def any_sites(M, K, op, tiled, walk, tk, steps, writes=None):
+def any_sites(M, K, op, tiled, walk, tk, steps, qrow_base=0, qcol_base=0, L=None):
     """Every access of workgroup (walk, tk) for the given steps of its walk,
     as (site, descriptor, offsets, bytes, live, logical address) tuples."""
     if op == "gated":
@@ -433,7 +433,7 @@ def any_sites(M, K, op, tiled, walk, tk, steps, writes=None):
         ldx, lin_off, ldg = K, 0, K
     else:
         ldx, lin_off, ldg = K, 0, 0
-    L = any_walk_len([M], K)
+    L = L or any_walk_len([M], K)
     tiles_m, tiles_k = -(-M // ANY_M), -(-K // ANY_K)
     walks = -(-tiles_m // L)
     t = np.arange(THREADS)
@@ -497,38 +497,66 @@ def any_sites(M, K, op, tiled, walk, tk, steps, writes=None):
                 to = tile_offset(m0 + r, b, RT)
                 out.append(("any s_row tiled", Desc(base, RT * CT * 256),
                             np.where(ok, to - base, DEAD), 1, ok, to))
-        # q_row pieces
-        W = piece_width(K)
-        per_row = ANY_K // W
-        iters = ANY_M * per_row // THREADS
-        sub = np.zeros_like(t) if per_row >= 64 else lane // per_row
-        p = 64 * (wv % max(per_row // 64, 1)) + lane if per_row >= 64 else lane % per_row
+        # q_row: 16-byte pieces when rows start 16-byte aligned, else the
+        # aligned dwords inside each row's segment plus head and tail bytes
         krem = min(K - k0, ANY_K)
-        off = np.where(W * p < krem, sub * K + W * p, DEAD)
-        for i in range(iters):
-            qq = wv + 4 * i
-            r0 = qq // (per_row // 64) if per_row >= 64 else qq * (64 // per_row)
-            for w in range(WAVES):
-                sel = wv == w
-                r0w = int(r0[w * 64]) if isinstance(r0, np.ndarray) else r0
-                live = (W * p < krem) & (m0 + r0w + sub < M)
-                out.append((f"any q_row W={W}", Desc((m0 + r0w) * K + k0, M * K), off[sel], W,
-                            live[sel], ((m0 + r0w + sub) * K + k0 + W * p)[sel]))
-        # q_col pieces
-        W = piece_width(M)
-        per_row = ANY_M // W
-        rpw = 64 // per_row
-        iters = ANY_K // (4 * rpw)
-        sub, p = lane // per_row, lane % per_row
         mrem = min(M - m0, ANY_M)
-        off = np.where(W * p < mrem, sub * M + W * p, DEAD)
-        for i in range(iters):
-            for w in range(WAVES):
-                sel = wv == w
-                c0 = rpw * (w + 4 * i)
-                live = (W * p < mrem) & (k0 + c0 + sub < K)
-                out.append((f"any q_col W={W}", Desc((k0 + c0) * M + m0, K * M), off[sel], W,
-                            live[sel], ((k0 + c0 + sub) * M + m0 + W * p)[sel]))
+        dq = Desc(m0 * K + k0, M * K)
+        if K % 16 == 0 and qrow_base % 16 == 0:
+            sub, p = lane >> 3, lane & 7
+            for i in range(2):
+                for w in range(WAVES):
+                    sel = wv == w
+                    r = 8 * (w + 4 * i) + sub
+                    ok = (r < mrem) & (16 * p < krem)
+                    out.append(("any q_row W=16", dq, np.where(ok, r * K + 16 * p, DEAD)[sel], 16,
+                                ok[sel], ((m0 + r) * K + k0 + 16 * p)[sel]))
+        else:
+            for i in range(8):
+                for w in range(WAVES):
+                    sel = wv == w
+                    r, u = 2 * (w + 4 * i) + (lane >> 5), lane & 31
+                    al = (qrow_base + (m0 + r) * K + k0) & 3
+                    head = np.minimum(krem, (4 - al) & 3)
+                    nd = (krem - head) >> 2
+                    i0 = head + 4 * u
+                    ok = (r < mrem) & (u < nd)
+                    out.append(("any q_row W=4", dq, np.where(ok, r * K + i0, DEAD)[sel], 4, ok[sel],
+                                ((m0 + r) * K + k0 + i0)[sel]))
+            for i in range(2):
+                for w in range(WAVES):
+                    sel = wv == w
+                    r, slot = 8 * (w + 4 * i) + (lane >> 3), lane & 7
+                    al = (qrow_base + (m0 + r) * K + k0) & 3
+                    head = np.minimum(krem, (4 - al) & 3)
+                    tail0 = head + 4 * ((krem - head) >> 2)
+                    b = np.where(slot < 3, slot, tail0 + slot - 3)
+                    ok = (r < mrem) & np.where(slot < 3, slot < head, (slot < 6) & (b < krem))
+                    out.append(("any q_row W=1", dq, np.where(ok, r * K + b, DEAD)[sel], 1, ok[sel],
+                                ((m0 + r) * K + k0 + b)[sel]))
+        # q_col: the 64-byte chunk that ends sft bytes into this step (16-byte
+        # pieces, or bytes where the chunk reaches outside the walk); the
+        # walk's last step also writes the chunk after it
+        last = s == n - 1
+        npc = 8 if last else 4
+        dc = Desc(k0 * M, K * M)
+        for i in range(ANY_K * npc // THREADS):
+            idx = t + THREADS * i
+            cc, j = idx >> (3 if last else 2), idx & (npc - 1)
+            sft = (qcol_base + (k0 + cc) * M + m0) & 63
+            lo = np.where(s > 0, 0, sft)
+            hi = sft + mrem
+            co = cc * M + m0 - sft
+            row_ok = k0 + cc < K
+            whole = row_ok & (lo <= 16 * j) & (16 * j + 16 <= hi)
+            out.append(("any q_col W=16", dc, np.where(whole, co + 16 * j, DEAD), 16, whole,
+                        (k0 + cc) * M + m0 - sft + 16 * j))
+            part = row_ok & ~whole & (16 * j < hi) & (16 * j + 16 > lo)
+            for b in range(16):
+                pb = 16 * j + b
+                ok = part & (pb >= lo) & (pb < hi)
+                out.append(("any q_col W=1", dc, np.where(ok, co + pb, DEAD), 1, ok,
+                            (k0 + cc) * M + m0 - sft + pb))
     # column scales at the walk's end
     jb, cnt = 2 * t0, 2 * n
     last_walk = walk + 1 == walks
@@ -557,7 +585,9 @@ def any_sites(M, K, op, tiled, walk, tk, steps, writes=None):
     return out
 
 
-def any_model(M, K, op="plain", tiled=False, ck=None):
+def any_model(M, K, op="plain", tiled=False, ck=None, qrow_base=0, qcol_base=0):
+    """qrow_base, qcol_base: the outputs' start addresses modulo 64 (a group
+    of a stack starts anywhere)."""
     ck = ck or Checker()
     L = any_walk_len([M], K)
     tiles_m, tiles_k = -(-M // ANY_M), -(-K // ANY_K)
@@ -566,8 +596,13 @@ def any_model(M, K, op="plain", tiled=False, ck=None):
         n = min(L, tiles_m - walk * L)
         for tk in edge(tiles_k):
             for site, d, off, nbytes, live, addr in any_sites(M, K, op, tiled, walk, tk,
-                                                              sorted({0, n - 1})):
+                                                              sorted({0, min(1, n - 1), n - 1}),
+                                                              qrow_base, qcol_base):
                 ck.access(site, d, off, nbytes, live, addr)
+                base = qrow_base if "q_row" in site else qcol_base if "q_col" in site else 0
+                a = np.broadcast_to(np.asarray(addr, dtype=np.int64), np.shape(live))[live]
+                if nbytes > 1 and ((base + a) % nbytes != 0).any():
+                    ck.bad.append((site, f"{nbytes}-byte store not {nbytes}-byte aligned"))
     return ck
 
 
@@ -580,6 +615,7 @@ ANY_SHAPES = [(MAXD, 1), (1, MAXD), (MAXD - 1, 9), (MAXD, 12), (MAXD, (1 << 17) 
 @pytest.mark.parametrize("op", ["plain", "grad"])
 def test_any_shape_offsets(M, K, op, tiled):
     any_model(M, K, op, tiled).ok()
+    any_model(M, K, op, tiled, qrow_base=13, qcol_base=37).ok()
 
 
 ANY_GATED_N = [(MAXD, 1), (128, (1 << 22) - 1), (17, 1 << 22), (MAXD - 1, 4), (16383, 4093)]
@@ -592,14 +628,17 @@ def test_any_shape_gated_offsets(M, N, tiled):
     any_model(M, 2 * N, "dgated", tiled).ok()
 
 
+@pytest.mark.parametrize("bases", [(0, 0), (5, 22), (16, 48)], ids=["b0", "b5-22", "b16-48"])
 @pytest.mark.parametrize("tiled", [False, True], ids=["compact", "tiled"])
 @pytest.mark.parametrize("M,K", [(1, 1), (17, 9), (33, 40), (95, 130), (200, 300), (64, 520),
-                                 (129, 257), (300, 12), (12, 300)])
-def test_any_shape_writes_every_byte_once(M, K, tiled):
+                                 (129, 257), (300, 12), (12, 300), (600, 64), (1100, 20)])
+@pytest.mark.parametrize("walk", [None, 2, 3, 8], ids=["planned", "L2", "L3", "L8"])
+def test_any_shape_writes_every_byte_once(M, K, tiled, bases, walk):
     """Over all workgroups and steps, every byte of q_row, q_col and of both
     scale tensors (compact, or the tile layout with its padding) is written
-    exactly once, and nothing else is."""
-    L = any_walk_len([M], K)
+    exactly once, and nothing else is -- for the planned walk length and for
+    forced longer walks (whose transposed bytes carry across steps)."""
+    L = walk or any_walk_len([M], K)
     tiles_m, tiles_k = -(-M // ANY_M), -(-K // ANY_K)
     walks = -(-tiles_m // L)
     nbK, nbM = (K + 31) >> 5, (M + 31) >> 5
@@ -607,10 +646,10 @@ def test_any_shape_writes_every_byte_once(M, K, tiled):
             "s_row": ((M + 31) >> 5) * ((nbK + 7) >> 3) * 256 if tiled else M * nbK,
             "s_col": ((K + 31) >> 5) * ((nbM + 7) >> 3) * 256 if tiled else K * nbM}
     count = {name: np.zeros(n, np.int64) for name, n in size.items()}
-    for walk in range(walks):
+    for w in range(walks):
         for tk in range(tiles_k):
-            for site, d, off, nbytes, live, addr in any_sites(M, K, "plain", tiled, walk, tk,
-                                                              range(L)):
+            for site, d, off, nbytes, live, addr in any_sites(M, K, "plain", tiled, w, tk,
+                                                              range(L), *bases, L=L):
                 name = next((nm for nm in count if site.startswith("any " + nm)), None)
                 if name is None:
                     continue

@@ -441,10 +441,10 @@ def nvfp4_quantize_transpose(x, axis=ROWWISE | COLWISE, tensor_amax=None, two_d=
     two_d: one scale per 16 x 16 block (written per row / per column)."""
     x = _c(x, np.uint16)
     M, K = x.shape
-    q_row = np.zeros((M, K // 2), np.uint8) if axis & ROWWISE else None
-    s_row = np.zeros((M, K // 16), np.uint8) if axis & ROWWISE else None
-    q_col = np.zeros((K, M // 2), np.uint8) if axis & COLWISE else None
-    s_col = np.zeros((K, M // 16), np.uint8) if axis & COLWISE else None
+    q_row = np.zeros((M, -(-K // 2)), np.uint8) if axis & ROWWISE else None
+    s_row = np.zeros((M, -(-K // 16)), np.uint8) if axis & ROWWISE else None
+    q_col = np.zeros((K, -(-M // 2)), np.uint8) if axis & COLWISE else None
+    s_col = np.zeros((K, -(-M // 16)), np.uint8) if axis & COLWISE else None
     sg = np.zeros(1, np.float32)
     A = -1.0 if tensor_amax is None else float(tensor_amax)
     fn = lib().orc_nvfp4_quantize_transpose_2d if two_d else lib().orc_nvfp4_quantize_transpose
@@ -463,10 +463,10 @@ def nvfp4_quantize_transpose_grouped(x, group_rows, axis=ROWWISE | COLWISE, amax
     rows = np.ascontiguousarray(group_rows, dtype=np.int64)
     G = rows.size
     assert rows.sum() == M
-    q_row = np.zeros((M, K // 2), np.uint8) if axis & ROWWISE else None
-    s_row = np.zeros((M, K // 16), np.uint8) if axis & ROWWISE else None
-    q_col = np.zeros(K * M // 2, np.uint8) if axis & COLWISE else None
-    s_col = np.zeros(K * M // 16, np.uint8) if axis & COLWISE else None
+    q_row = np.zeros((M, -(-K // 2)), np.uint8) if axis & ROWWISE else None
+    s_row = np.zeros((M, -(-K // 16)), np.uint8) if axis & ROWWISE else None
+    q_col = np.zeros(K * int(sum(-(-int(m) // 2) for m in rows)), np.uint8) if axis & COLWISE else None
+    s_col = np.zeros(K * int(sum(-(-int(m) // 16) for m in rows)), np.uint8) if axis & COLWISE else None
     sg = np.zeros(G, np.float32)
     a = None if amax is None else _c(np.asarray(amax, dtype=np.float32), np.float32)
     rc = lib().orc_nvfp4_quantize_transpose_grouped(

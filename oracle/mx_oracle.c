@@ -58,7 +58,10 @@
  *   R9  a line whose length is not a multiple of 32 ends in a partial block:
  *       its scale and codes come from its own elements alone (the same as
  *       padding the line with zeros, which never change an amax and encode
- *       to zero).
+ *       to zero).  NVFP4 likewise for lines that are not multiples of 16
+ *       (2D: partial 16 x 16 blocks at the edges); a line of n codes packs
+ *       into ceil(n/2) bytes, the high nibble of the last one 0 when n is
+ *       odd -- again the zero-padded tensor's bytes.
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fopenmp -shared
  * -fPIC (see build.py).  OpenMP only splits independent rows / columns /
@@ -838,17 +841,27 @@ float orc_absmax(const uint16_t *x, int64_t n)
 /* A tensor whose amax A is not finite (it holds an Inf or a NaN) has no
  * usable global scale (S_g = fl32(A / 2688) is Inf or NaN): every scale byte
  * is 0x7F, the E4M3 NaN, and every element code 0 (R6). */
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
 static void nvfp4_nonfinite(int64_t M, int64_t K, unsigned axis, uint8_t *q_row, uint8_t *s_row,
                             uint8_t *q_col, uint8_t *s_col)
 {
     if (axis & 1u) {
-        memset(q_row, 0, (size_t)(M * K / 2));
-        memset(s_row, 0x7F, (size_t)(M * K / 16));
+        memset(q_row, 0, (size_t)(M * cdiv(K, 2)));
+        memset(s_row, 0x7F, (size_t)(M * cdiv(K, 16)));
     }
     if (axis & 2u) {
-        memset(q_col, 0, (size_t)(M * K / 2));
-        memset(s_col, 0x7F, (size_t)(M * K / 16));
+        memset(q_col, 0, (size_t)(K * cdiv(M, 2)));
+        memset(s_col, 0x7F, (size_t)(K * cdiv(M, 16)));
     }
+}
+
+/* n codes c[0], c[stride], ... of a line -> ceil(n/2) bytes at q: code 2i in
+ * the low nibble of byte i, code 2i+1 in the high nibble (0 past the end). */
+static void pack_codes(const uint8_t *c, int n, int stride, uint8_t *q)
+{
+    for (int i = 0; 2 * i < n; i++)
+        q[i] = (uint8_t)(c[2 * i * stride] | (2 * i + 1 < n ? c[(2 * i + 1) * stride] << 4 : 0));
 }
 
 /* Tensor scale S_g = fl32(A / (448*6)), or 1 when A = 0. */
@@ -887,17 +900,18 @@ static void nvfp4_block(const double *v, int n, float Sg, uint8_t *nib, int64_t 
     *s = sb;
 }
 
-/* Row-wise NVFP4 of x[M][K] (blocks of 16 along K) into q_row[M][K/2] (code
- * of element 2j in the low nibble of byte j, 2j+1 in the high nibble) and
- * s_row[M][K/16]; and the same for the transpose into q_col[K][M/2],
- * s_col[K][M/16].  tensor_amax < 0 means "compute it from x"; a NaN or
+/* Row-wise NVFP4 of x[M][K] (blocks of 16 along K, the last one partial when
+ * 16 does not divide K) into q_row[M][ceil(K/2)] (code of element 2j in the
+ * low nibble of byte j, 2j+1 in the high nibble) and s_row[M][ceil(K/16)];
+ * and the same for the transpose into q_col[K][ceil(M/2)],
+ * s_col[K][ceil(M/16)].  tensor_amax < 0 means "compute it from x"; a NaN or
  * infinite tensor_amax (the amax of a tensor holding a NaN or an Inf) gives
  * the outputs of nvfp4_nonfinite. */
 int orc_nvfp4_quantize_transpose(const uint16_t *x, int64_t M, int64_t K, unsigned axis,
                                  float tensor_amax, uint8_t *q_row, uint8_t *s_row,
                                  uint8_t *q_col, uint8_t *s_col, float *sg_out)
 {
-    if (M <= 0 || K <= 0 || M % 16 || K % 16)
+    if (M <= 0 || K <= 0)
         return ORC_ERR_SHAPE;
     if (axis & ~3u)
         return ORC_ERR_ENUM;
@@ -911,30 +925,32 @@ int orc_nvfp4_quantize_transpose(const uint16_t *x, int64_t M, int64_t K, unsign
         return ORC_OK;
     }
     if (axis & 1u) {
+        const int64_t nb = cdiv(K, 16), lb = cdiv(K, 2);
 #pragma omp parallel for schedule(static)
         for (int64_t m = 0; m < M; m++) {
             double v[16];
             uint8_t c[16];
-            for (int64_t j = 0; j < K / 16; j++) {
-                for (int i = 0; i < 16; i++)
+            for (int64_t j = 0; j < nb; j++) {
+                const int n = (int)(K - 16 * j < 16 ? K - 16 * j : 16);
+                for (int i = 0; i < n; i++)
                     v[i] = orc_bf16_value(x[m * K + 16 * j + i]);
-                nvfp4_block(v, 16, Sg, c, 1, s_row + m * (K / 16) + j);
-                for (int i = 0; i < 8; i++)
-                    q_row[m * (K / 2) + 8 * j + i] = (uint8_t)(c[2 * i] | (c[2 * i + 1] << 4));
+                nvfp4_block(v, n, Sg, c, 1, s_row + m * nb + j);
+                pack_codes(c, n, 1, q_row + m * lb + 8 * j);
             }
         }
     }
     if (axis & 2u) {
+        const int64_t nb = cdiv(M, 16), lb = cdiv(M, 2);
 #pragma omp parallel for schedule(static)
         for (int64_t k = 0; k < K; k++) {
             double v[16];
             uint8_t c[16];
-            for (int64_t j = 0; j < M / 16; j++) {
-                for (int i = 0; i < 16; i++)
+            for (int64_t j = 0; j < nb; j++) {
+                const int n = (int)(M - 16 * j < 16 ? M - 16 * j : 16);
+                for (int i = 0; i < n; i++)
                     v[i] = orc_bf16_value(x[(16 * j + i) * K + k]);
-                nvfp4_block(v, 16, Sg, c, 1, s_col + k * (M / 16) + j);
-                for (int i = 0; i < 8; i++)
-                    q_col[k * (M / 2) + 8 * j + i] = (uint8_t)(c[2 * i] | (c[2 * i + 1] << 4));
+                nvfp4_block(v, n, Sg, c, 1, s_col + k * nb + j);
+                pack_codes(c, n, 1, q_col + k * lb + 8 * j);
             }
         }
     }
@@ -942,16 +958,17 @@ int orc_nvfp4_quantize_transpose(const uint16_t *x, int64_t M, int64_t K, unsign
 }
 
 /* NVFP4 with 2D scaling ("nvfp42d" in the quantize-transpose table): one
- * E4M3 scale per 16 x 16 block of x, by the same chain as the 1D blocks with
- * b = max |x| over the 256 elements.  Both outputs keep the 1D layouts: the
- * block's scale is written for each of its 16 rows in s_row[M][K/16] and for
- * each of its 16 columns in s_col[K][M/16], and every element is coded with
- * its block's multiplier in q_row and in the transposed q_col. */
+ * E4M3 scale per 16 x 16 block of x (partial blocks at the right and bottom
+ * edges), by the same chain as the 1D blocks with b = max |x| over the
+ * block's elements.  Both outputs keep the 1D layouts: the block's scale is
+ * written for each of its rows in s_row[M][ceil(K/16)] and for each of its
+ * columns in s_col[K][ceil(M/16)], and every element is coded with its
+ * block's multiplier in q_row and in the transposed q_col. */
 int orc_nvfp4_quantize_transpose_2d(const uint16_t *x, int64_t M, int64_t K, unsigned axis,
                                     float tensor_amax, uint8_t *q_row, uint8_t *s_row,
                                     uint8_t *q_col, uint8_t *s_col, float *sg_out)
 {
-    if (M <= 0 || K <= 0 || M % 16 || K % 16)
+    if (M <= 0 || K <= 0)
         return ORC_ERR_SHAPE;
     if (axis & ~3u)
         return ORC_ERR_ENUM;
@@ -964,33 +981,28 @@ int orc_nvfp4_quantize_transpose_2d(const uint16_t *x, int64_t M, int64_t K, uns
         nvfp4_nonfinite(M, K, axis, q_row, s_row, q_col, s_col);
         return ORC_OK;
     }
+    const int64_t nbk = cdiv(K, 16), nbm = cdiv(M, 16), lk = cdiv(K, 2), lm = cdiv(M, 2);
 #pragma omp parallel for schedule(static)
-    for (int64_t bi = 0; bi < M / 16; bi++) {
+    for (int64_t bi = 0; bi < nbm; bi++) {
         double v[256];
         uint8_t c[256];
-        for (int64_t bj = 0; bj < K / 16; bj++) {
-            for (int r = 0; r < 16; r++)
-                for (int q = 0; q < 16; q++)
-                    v[16 * r + q] = orc_bf16_value(x[(16 * bi + r) * K + 16 * bj + q]);
+        const int nr = (int)(M - 16 * bi < 16 ? M - 16 * bi : 16);
+        for (int64_t bj = 0; bj < nbk; bj++) {
+            const int nc = (int)(K - 16 * bj < 16 ? K - 16 * bj : 16);
+            for (int r = 0; r < nr; r++)
+                for (int q = 0; q < nc; q++)
+                    v[nc * r + q] = orc_bf16_value(x[(16 * bi + r) * K + 16 * bj + q]);
             uint8_t sb;
-            nvfp4_block(v, 256, Sg, c, 1, &sb);        /* codes in row-major order */
-            for (int r = 0; r < 16; r++) {
+            nvfp4_block(v, nr * nc, Sg, c, 1, &sb);    /* codes in row-major order */
+            for (int r = 0; r < nr && (axis & 1u); r++) {
                 const int64_t m = 16 * bi + r;
-                if (axis & 1u) {
-                    s_row[m * (K / 16) + bj] = sb;
-                    for (int i = 0; i < 8; i++)
-                        q_row[m * (K / 2) + 8 * bj + i] =
-                            (uint8_t)(c[16 * r + 2 * i] | (c[16 * r + 2 * i + 1] << 4));
-                }
+                s_row[m * nbk + bj] = sb;
+                pack_codes(c + nc * r, nc, 1, q_row + m * lk + 8 * bj);
             }
-            for (int q = 0; q < 16; q++) {
+            for (int q = 0; q < nc && (axis & 2u); q++) {
                 const int64_t k = 16 * bj + q;
-                if (axis & 2u) {
-                    s_col[k * (M / 16) + bi] = sb;
-                    for (int i = 0; i < 8; i++)
-                        q_col[k * (M / 2) + 8 * bi + i] =
-                            (uint8_t)(c[16 * (2 * i) + q] | (c[16 * (2 * i + 1) + q] << 4));
-                }
+                s_col[k * nbm + bi] = sb;
+                pack_codes(c + q, nr, nc, q_col + k * lm + 8 * bi);
             }
         }
     }
@@ -1000,20 +1012,21 @@ int orc_nvfp4_quantize_transpose_2d(const uint16_t *x, int64_t M, int64_t K, uns
 /* Grouped NVFP4 (R10): G tensors stacked along rows, each quantised with its
  * own tensor amax and global scale (amax[g] when amax is given, else the
  * group's own max |x|), 1D or 2D scaling; outputs concatenated group after
- * group: q_row[M][K/2] and s_row[M][K/16] as for the stacked rows, q_col /
- * s_col group g's [K][rows/2] / [K][rows/16] at bytes K*r_g/2 / K*r_g/16,
- * sg_out[g] (1 for an empty group, which owns no output). */
+ * group: q_row[M][ceil(K/2)] and s_row[M][ceil(K/16)] as for the stacked
+ * rows; q_col / s_col group g's [K][ceil(rows/2)] / [K][ceil(rows/16)], one
+ * group after the other; sg_out[g] (1 for an empty group, which owns no
+ * output). */
 int orc_nvfp4_quantize_transpose_grouped(const uint16_t *x, int64_t K, const int64_t *rows, int G,
                                          const float *amax, int two_d, unsigned axis,
                                          uint8_t *q_row, uint8_t *s_row, uint8_t *q_col,
                                          uint8_t *s_col, float *sg_out)
 {
-    if (G <= 0 || K <= 0 || K % 16)
+    if (G <= 0 || K <= 0)
         return ORC_ERR_SHAPE;
-    int64_t r = 0;
+    int64_t r = 0, qc = 0, sc = 0;
     for (int g = 0; g < G; g++) {
         const int64_t m = rows[g];
-        if (m < 0 || m % 16)
+        if (m < 0)
             return ORC_ERR_SHAPE;
         if (m == 0) {
             if (sg_out)
@@ -1022,12 +1035,14 @@ int orc_nvfp4_quantize_transpose_grouped(const uint16_t *x, int64_t K, const int
         }
         const float A = amax ? amax[g] : -1.0f;
         int rc = (two_d ? orc_nvfp4_quantize_transpose_2d : orc_nvfp4_quantize_transpose)(
-            x + r * K, m, K, axis, A, q_row ? q_row + r * K / 2 : NULL,
-            s_row ? s_row + r * K / 16 : NULL, q_col ? q_col + K * r / 2 : NULL,
-            s_col ? s_col + K * r / 16 : NULL, sg_out ? sg_out + g : NULL);
+            x + r * K, m, K, axis, A, q_row ? q_row + r * cdiv(K, 2) : NULL,
+            s_row ? s_row + r * cdiv(K, 16) : NULL, q_col ? q_col + qc : NULL,
+            s_col ? s_col + sc : NULL, sg_out ? sg_out + g : NULL);
         if (rc != ORC_OK)
             return rc;
         r += m;
+        qc += K * cdiv(m, 2);
+        sc += K * cdiv(m, 16);
     }
     return ORC_OK;
 }

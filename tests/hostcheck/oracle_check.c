@@ -142,11 +142,13 @@ static void grouped_call(int which, const int64_t *rows, int G, int64_t K, unsig
     free(x), free(g), free(qr), free(sr), free(qc), free(sc), free(db);
 }
 
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
 static void nvfp4_case(int64_t M, int64_t K, unsigned axis, int two_d, float amax)
 {
     uint16_t *x = input(M * K);
-    uint8_t *qr = buf((axis & ROWS) ? M * K / 2 : 0), *sr = buf((axis & ROWS) ? M * K / 16 : 0);
-    uint8_t *qc = buf((axis & COLS) ? M * K / 2 : 0), *sc = buf((axis & COLS) ? M * K / 16 : 0);
+    uint8_t *qr = buf((axis & ROWS) ? M * cdiv(K, 2) : 0), *sr = buf((axis & ROWS) ? M * cdiv(K, 16) : 0);
+    uint8_t *qc = buf((axis & COLS) ? K * cdiv(M, 2) : 0), *sc = buf((axis & COLS) ? K * cdiv(M, 16) : 0);
     float *sg = (float *)buf(4);
     const float a = amax < 0 ? orc_absmax(x, M * K) : amax;
     expect_ok((two_d ? orc_nvfp4_quantize_transpose_2d : orc_nvfp4_quantize_transpose)(
@@ -157,12 +159,14 @@ static void nvfp4_case(int64_t M, int64_t K, unsigned axis, int two_d, float ama
 
 static void nvfp4_grouped_case(const int64_t *rows, int G, int64_t K, unsigned axis, int two_d)
 {
-    int64_t M = 0;
-    for (int g = 0; g < G; g++)
+    int64_t M = 0, qcb = 0, scb = 0;
+    for (int g = 0; g < G; g++) {
         M += rows[g];
+        qcb += K * cdiv(rows[g], 2), scb += K * cdiv(rows[g], 16);
+    }
     uint16_t *x = input(M * K);
-    uint8_t *qr = buf((axis & ROWS) ? M * K / 2 : 0), *sr = buf((axis & ROWS) ? M * K / 16 : 0);
-    uint8_t *qc = buf((axis & COLS) ? M * K / 2 : 0), *sc = buf((axis & COLS) ? M * K / 16 : 0);
+    uint8_t *qr = buf((axis & ROWS) ? M * cdiv(K, 2) : 0), *sr = buf((axis & ROWS) ? M * cdiv(K, 16) : 0);
+    uint8_t *qc = buf((axis & COLS) ? qcb : 0), *sc = buf((axis & COLS) ? scb : 0);
     float *amax = (float *)buf(G * 4), *sg = (float *)buf(G * 4);
     for (int g = 0, r = 0; g < G; r += (int)rows[g], g++)
         amax[g] = rows[g] ? orc_absmax(x + r * K, rows[g] * K) : 0.0f;
@@ -178,7 +182,8 @@ static void nvfp4_grouped_case(const int64_t *rows, int G, int64_t K, unsigned a
 int main(void)
 {
     orc_set_threads(2);
-    const int64_t shapes[][2] = {{16, 8}, {32, 32}, {48, 40}, {16, 264}, {272, 56}, {64, 520}};
+    const int64_t shapes[][2] = {{16, 8}, {32, 32}, {48, 40}, {16, 264}, {272, 56}, {64, 520},
+                                 {1, 1}, {17, 9}, {3, 70}, {70, 3}};
     const unsigned axes[] = {ROWS, COLS, ROWS | COLS};
     const unsigned variants[] = {0, E5M2, ROUND_UP, E5M2 | ROUND_UP, TILED, TILED | E5M2};
     for (size_t s = 0; s < sizeof shapes / sizeof shapes[0]; s++)
@@ -195,10 +200,10 @@ int main(void)
                     mx_case(2, M, K, axis, act);
                 }
             }
-    const int64_t g1[] = {16, 0, 48, 32}, g2[] = {0, 0, 16}, g3[] = {144};
-    struct { const int64_t *rows; int G; } groups[] = {{g1, 4}, {g2, 3}, {g3, 1}};
+    const int64_t g1[] = {16, 0, 48, 32}, g2[] = {0, 0, 16}, g3[] = {144}, g4[] = {5, 0, 33, 1};
+    struct { const int64_t *rows; int G; } groups[] = {{g1, 4}, {g2, 3}, {g3, 1}, {g4, 4}};
     const unsigned gvariants[] = {0, TILED | ROUND_UP};
-    for (size_t i = 0; i < 3; i++)
+    for (size_t i = 0; i < 4; i++)
         for (size_t a = 0; a < 3; a++)
             for (size_t v = 0; v < 2; v++)
                 for (int64_t K = 8; K <= 296; K += 288) {
@@ -208,18 +213,21 @@ int main(void)
                     grouped_call(1, groups[i].rows, groups[i].G, K, axis, 1);
                     grouped_call(2, groups[i].rows, groups[i].G, K, axis, 2);
                 }
-    const int64_t nshapes[][2] = {{16, 16}, {32, 48}, {48, 272}, {144, 32}};
-    for (size_t s = 0; s < 4; s++)
+    const int64_t nshapes[][2] = {{16, 16}, {32, 48}, {48, 272}, {144, 32},
+                                  {1, 1}, {17, 9}, {5, 31}, {33, 50}};
+    for (size_t s = 0; s < 8; s++)
         for (size_t a = 0; a < 3; a++)
             for (int two_d = 0; two_d <= 1; two_d++) {
                 nvfp4_case(nshapes[s][0], nshapes[s][1], axes[a], two_d, -1.0f);
                 nvfp4_case(nshapes[s][0], nshapes[s][1], axes[a], two_d, 0.0f);
                 nvfp4_case(nshapes[s][0], nshapes[s][1], axes[a], two_d, 1e-38f);
             }
-    for (size_t i = 0; i < 3; i++)
+    for (size_t i = 0; i < 4; i++)
         for (size_t a = 0; a < 3; a++)
-            for (int two_d = 0; two_d <= 1; two_d++)
+            for (int two_d = 0; two_d <= 1; two_d++) {
                 nvfp4_grouped_case(groups[i].rows, groups[i].G, 48, axes[a], two_d);
+                nvfp4_grouped_case(groups[i].rows, groups[i].G, 13, axes[a], two_d);
+            }
     printf("%d oracle calls, %d failed\n", calls, failures);
     return failures ? 1 : 0;
 }

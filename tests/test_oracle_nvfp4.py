@@ -158,7 +158,63 @@ def test_zero_tensor_and_shape_errors():
     out = O.nvfp4_quantize_transpose(z)
     assert out["sg"] == 1.0 and not out["q_row"].any() and not out["s_row"].any()
     with pytest.raises(ValueError):
-        O.nvfp4_quantize_transpose(np.zeros((16, 24), np.uint16))
+        O.nvfp4_quantize_transpose(np.zeros((0, 32), np.uint16))
+
+
+def test_hand_worked_odd_row():
+    """One row [6, -3, 1]: amax 6, S_g = 6/2688; the block's b/6 = 1 over S_g
+    is 448 -> scale byte 0x7E, multiplier 1/(448 S_g) = 1; codes E2M1(6) = 7,
+    E2M1(-3) = 0x8 | 5, E2M1(1) = 2, packed into ceil(3/2) = 2 bytes with the
+    missing fourth code 0.  Transposed, each column is a block of one
+    element: 6 as above; 3: 0.5 / S_g = 224 -> byte 0x76, multiplier 2, -6 ->
+    0x8 | 7; 1: (1/6) / S_g = 74.67 -> nearest E4M3 72 (0x69), multiplier
+    2688 / 432 = 6.22, which saturates to code 7."""
+    x = np.array([[0x40C0, 0xC040, 0x3F80]], np.uint16)
+    o = O.nvfp4_quantize_transpose(x)
+    assert o["q_row"].shape == (1, 2) and o["s_row"].shape == (1, 1)
+    assert list(o["q_row"][0]) == [0xD7, 0x02] and o["s_row"][0, 0] == 0x7E
+    assert o["q_col"].shape == (3, 1) and list(o["q_col"][:, 0]) == [0x07, 0x0F, 0x07]
+    assert list(o["s_col"][:, 0]) == [0x7E, 0x76, 0x69]
+
+
+@pytest.mark.parametrize("two_d", [False, True], ids=["1d", "2d"])
+@pytest.mark.parametrize("M,K", [(1, 1), (17, 9), (5, 31), (33, 50), (40, 7), (16, 24), (3, 16)])
+def test_partial_blocks_equal_zero_padded(M, K, two_d):
+    """Any M, K: every output equals the matching bytes of the cast of the
+    tensor zero-padded to multiples of 16 (zeros change no amax, no block
+    maximum, and code to 0, which also fills the high nibble of an odd row's
+    last byte); the full-block chain is pinned by the tests above."""
+    x = W.student_t_rows(M, K, seed=300 + M + K)
+    Mp, Kp = -(-M // 16) * 16, -(-K // 16) * 16
+    xp = np.zeros((Mp, Kp), np.uint16)
+    xp[:M, :K] = x
+    o = O.nvfp4_quantize_transpose(x, two_d=two_d)
+    p = O.nvfp4_quantize_transpose(xp, two_d=two_d)
+    assert o["sg"] == p["sg"]
+    assert np.array_equal(o["q_row"], p["q_row"][:M, :-(-K // 2)])
+    assert np.array_equal(o["s_row"], p["s_row"][:M, :-(-K // 16)])
+    assert np.array_equal(o["q_col"], p["q_col"][:K, :-(-M // 2)])
+    assert np.array_equal(o["s_col"], p["s_col"][:K, :-(-M // 16)])
+
+
+def test_grouped_any_rows_equal_per_group_casts():
+    rows, K = [5, 0, 33, 16, 1], 19
+    x = W.student_t_rows(sum(rows), K, seed=310)
+    for two_d in (False, True):
+        g = O.nvfp4_quantize_transpose_grouped(x, rows, two_d=two_d)
+        r0 = qc = sc = 0
+        for gi, m in enumerate(rows):
+            if m == 0:
+                assert g["sg"][gi] == 1.0
+                continue
+            o = O.nvfp4_quantize_transpose(np.ascontiguousarray(x[r0:r0 + m]), two_d=two_d)
+            assert g["sg"][gi] == o["sg"]
+            assert np.array_equal(g["q_row"][r0:r0 + m], o["q_row"])
+            assert np.array_equal(g["s_row"][r0:r0 + m], o["s_row"])
+            assert np.array_equal(g["q_col"][qc:qc + o["q_col"].size], o["q_col"].ravel())
+            assert np.array_equal(g["s_col"][sc:sc + o["s_col"].size], o["s_col"].ravel())
+            r0, qc, sc = r0 + m, qc + o["q_col"].size, sc + o["s_col"].size
+        assert qc == g["q_col"].size and sc == g["s_col"].size
 
 
 # --- NVFP4 with 2D (16 x 16 block) scaling ------------------------------------

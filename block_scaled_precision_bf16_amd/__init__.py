@@ -445,13 +445,14 @@ def mx_absmax_bf16(x, out=None, stream=None):
 
 
 def _nv_need(M, K, axis, n_sg):
+    """NVFP4 outputs: codes [rows][ceil(cols/2)], scales [rows][ceil(cols/16)]."""
     need = {}
     if axis & ROWWISE:
-        need["q_row"] = ((M, K // 2), U8)
-        need["s_row"] = ((M, K // 16), U8)
+        need["q_row"] = ((M, -(-K // 2)), U8)
+        need["s_row"] = ((M, -(-K // 16)), U8)
     if axis & COLWISE:
-        need["q_col"] = ((K, M // 2), U8)
-        need["s_col"] = ((K, M // 16), U8)
+        need["q_col"] = ((K, -(-M // 2)), U8)
+        need["s_col"] = ((K, -(-M // 16)), U8)
     need["sg"] = ((n_sg,), F32)
     return need
 
@@ -496,8 +497,8 @@ def mx_absmax_bf16_grouped(x, group_rows, out=None, stream=None):
 def nvfp4_quantize_transpose_grouped(x, group_rows, amax, axis=ROWWISE | COLWISE, two_d=False,
                                      out=None, stream=None):
     """Grouped NVFP4 of x[M][K] = len(group_rows) stacked tensors, each with its
-    own tensor amax (device fp32 [G]).  Returns q_row [M][K/2], s_row
-    [M][K/16], flat q_col / s_col (the groups' transposes one after the
+    own tensor amax (device fp32 [G]).  Returns q_row [M][ceil(K/2)], s_row
+    [M][ceil(K/16)], flat q_col / s_col (the groups' transposes one after the
     other) and the groups' global scales sg [G]."""
     x = _2d(x, "x")
     M, K = x.shape
@@ -505,9 +506,9 @@ def nvfp4_quantize_transpose_grouped(x, group_rows, amax, axis=ROWWISE | COLWISE
     G = len(group_rows)
     dev = x.device
     need = _nv_need(M, K, axis, G)
-    for k in ("q_col", "s_col"):
-        if k in need:
-            need[k] = ((M * K // (2 if k == "q_col" else 16),), U8)
+    if "q_col" in need:   # group g's [K][ceil(rows/2)] and [K][ceil(rows/16)], one after the other
+        need["q_col"] = ((K * sum(-(-int(m) // 2) for m in group_rows),), U8)
+        need["s_col"] = ((K * sum(-(-int(m) // 16) for m in group_rows),), U8)
     o = _outputs(out, need, dev)
     _f32_vec(amax, G, "amax", dev)
     _on_device(dev, *o.values())

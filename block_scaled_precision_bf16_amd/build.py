@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmxcast.so")
-SOURCES = ["api.cpp", "mx_cast.hip", "mx_cast_any.hip", "nvfp4.hip",
+SOURCES = ["api.cpp", "mx_cast.hip", "mx_cast_any.hip", "nvfp4.hip", "nvfp4_any.hip",
            *[f"mx_cast_{kind}_{fmt}.hip" for kind in ("fmt", "grp")
              for fmt in ("e4m3", "e5m2", "e4m3_up", "e5m2_up")]]
 

@@ -47,12 +47,6 @@ bool any_alias(const Span *in, int nin, const Span *out, int nout)
     return false;
 }
 
-bool shape_ok(int64_t M, int64_t K, int64_t block)
-{
-    return M > 0 && K > 0 && M % block == 0 && K % block == 0 && M <= kMaxDim && K <= kMaxDim &&
-           M * K <= kMaxElems;
-}
-
 int tiles(int64_t n, int64_t t) { return (int)((n + t - 1) / t); }
 
 // Kernel op of an mx_quantize pre-op.
@@ -207,43 +201,56 @@ bool build_groups(const int64_t *rows, int G, int64_t K, int op, bool dbias, boo
     return walks > 0;
 }
 
-// Group table of a grouped NVFP4 cast: group sizes multiples of 16 rows
-// (empty groups allowed), K a multiple of 16; walks per group with the walk
-// length of the whole stack.
+// Group table of a grouped NVFP4 cast or absmax: any group sizes (empty
+// groups allowed); walks per group with the walk length of the whole stack.
+// any is set when the stack goes to the any-shape kernel: some group's rows
+// or K are not multiples of 16.  Each group's q_col and s_col start after the
+// previous groups' [K][ceil(rows/2)] and [K][ceil(rows/16)] bytes.
 bool build_nv_groups(const int64_t *rows, int G, int64_t K, mxk::GroupTable &gt, int64_t &M,
-                     int &group)
+                     int &group, bool &any)
 {
     if (!rows || G < 1 || G > mxk::kMaxGroups)
         return false;
     M = 0;
+    bool rows16 = true;
     for (int g = 0; g < G; g++) {
-        if (rows[g] < 0 || rows[g] % 16 != 0 || rows[g] > kMaxDim)
+        if (rows[g] < 0 || rows[g] > kMaxDim)
             return false;
+        rows16 = rows16 && rows[g] % 16 == 0;
         M += rows[g];
     }
-    if (M <= 0 || !shape_ok(M, K, 16))
+    if (M <= 0 || M > kMaxDim || !mx_size_ok(M, K))
         return false;
+    any = !(rows16 && K % 16 == 0);
     int tm[mxk::kMaxGroups];
     for (int g = 0; g < G; g++)
-        tm[g] = tiles(rows[g], mxk::kTileM);
+        tm[g] = tiles(rows[g], any ? mxk::kAnyTileM : mxk::kTileM);
     gt = mxk::GroupTable{};
-    group = mxk::pick_group_rounds(tm, G, tiles(K, mxk::kTileK), 2, 1);
+    group = any ? mxk::any_walk_len(rows, G, K) : mxk::pick_group_rounds(tm, G, tiles(K, mxk::kTileK), 2, 1);
     for (int g = 0; g < G; g++)
         gt.len[g] = group;
     gt.count = G;
-    int64_t walks = 0, r = 0;
+    int64_t walks = 0, r = 0, qc = 0, sc = 0;
     for (int g = 0; g < G; g++) {
         gt.walk0[g] = (int)walks;
         gt.row0[g] = r;
-        gt.srow_off[g] = r * (K / 16);
-        gt.scol_off[g] = K * (r / 16);
+        gt.srow_off[g] = r * ((K + 15) / 16);
+        gt.scol_off[g] = sc;
+        gt.qcol_off[g] = qc;
         walks += (tm[g] + group - 1) / group;
         r += rows[g];
+        qc += K * ((rows[g] + 1) / 2);
+        sc += K * ((rows[g] + 15) / 16);
     }
     gt.walk0[G] = (int)walks;
     gt.row0[G] = M;
     return true;
 }
+
+// Bytes of NVFP4 outputs: codes [rows][ceil(cols/2)], scales
+// [rows][ceil(cols/16)].
+uint64_t nv_code_bytes(int64_t rows, int64_t cols) { return (uint64_t)(rows * ((cols + 1) / 2)); }
+uint64_t nv_scale_bytes(int64_t rows, int64_t cols) { return (uint64_t)(rows * ((cols + 15) / 16)); }
 
 // Total scale bytes of a grouped cast (the groups' scale tensors one after
 // the other).
@@ -295,7 +302,7 @@ static mx_status nvfp4_impl(bool two_d, const void *x, int64_t M, int64_t K, con
     const bool row = axis_mask & MX_ROWWISE, col = axis_mask & MX_COLWISE;
     if (!x || !amax || (row && (!q_row || !s_row)) || (col && (!q_col || !s_col)))
         return MX_ERR_NULL;
-    if (!shape_ok(M, K, 16))
+    if (!mx_size_ok(M, K))
         return MX_ERR_SHAPE;
     if (!aligned(x, 16) || !aligned(amax, 4) ||
         (row && (!aligned(q_row, 16) || !aligned(s_row, 16))) ||
@@ -304,8 +311,10 @@ static mx_status nvfp4_impl(bool two_d, const void *x, int64_t M, int64_t K, con
         return MX_ERR_ALIGN;
     const uint64_t n = (uint64_t)(M * K);
     const Span in[2] = {{x, 2 * n}, {amax, 4}};
-    const Span out[5] = {{row ? q_row : nullptr, n / 2}, {row ? s_row : nullptr, n / 16},
-                         {col ? q_col : nullptr, n / 2}, {col ? s_col : nullptr, n / 16},
+    const Span out[5] = {{row ? q_row : nullptr, nv_code_bytes(M, K)},
+                         {row ? s_row : nullptr, nv_scale_bytes(M, K)},
+                         {col ? q_col : nullptr, nv_code_bytes(K, M)},
+                         {col ? s_col : nullptr, nv_scale_bytes(K, M)},
                          {global_scale_out, 4}};
     if (any_alias(in, 2, out, 5))
         return MX_ERR_ALIAS;
@@ -320,6 +329,14 @@ static mx_status nvfp4_impl(bool two_d, const void *x, int64_t M, int64_t K, con
     a.q_col = q_col;
     a.s_col = s_col;
     a.sg_out = global_scale_out;
+    if (M % 16 != 0 || K % 16 != 0) {
+        const mxk::GroupTable gt = any_table(M, K);   // offsets 0: one tensor
+        a.tiles_k = tiles(K, mxk::kAnyTileK);
+        a.tiles_m = tiles(M, mxk::kAnyTileM);
+        a.group = gt.len[0];
+        a.groups_m = gt.walk0[1];
+        return from_hip(mxk::launch_nvfp4_any(axis_mask, two_d, a, gt, stream));
+    }
     a.tiles_k = tiles(K, mxk::kTileK);
     a.tiles_m = tiles(M, mxk::kTileM);
     mxk::plan_walks(&a.tiles_m, 1, a.tiles_k, mxk::kTargetWorkgroups, false, &a.group);
@@ -799,7 +816,8 @@ mx_status mx_absmax_bf16_grouped(const void *x, int64_t K, const int64_t *group_
     mxk::GroupTable gt;
     int64_t M;
     int group;
-    if (!build_nv_groups(group_rows, G, K, gt, M, group))
+    bool any;
+    if (!build_nv_groups(group_rows, G, K, gt, M, group, any))
         return MX_ERR_SHAPE;
     if (!aligned(x, 16) || !aligned(amax, 4))
         return MX_ERR_ALIGN;
@@ -825,7 +843,8 @@ mx_status nvfp4_quantize_transpose_grouped(const void *x, int64_t K, const int64
     mxk::GroupTable gt;
     int64_t M;
     int group;
-    if (!build_nv_groups(group_rows, G, K, gt, M, group))
+    bool any;
+    if (!build_nv_groups(group_rows, G, K, gt, M, group, any))
         return MX_ERR_SHAPE;
     if (!aligned(x, 16) || !aligned(amax, 4) ||
         (row && (!aligned(q_row, 16) || !aligned(s_row, 16))) ||
@@ -834,8 +853,10 @@ mx_status nvfp4_quantize_transpose_grouped(const void *x, int64_t K, const int64
         return MX_ERR_ALIGN;
     const uint64_t n = (uint64_t)(M * K);
     const Span in[2] = {{x, 2 * n}, {amax, 4 * (uint64_t)G}};
-    const Span out[5] = {{row ? q_row : nullptr, n / 2}, {row ? s_row : nullptr, n / 16},
-                         {col ? q_col : nullptr, n / 2}, {col ? s_col : nullptr, n / 16},
+    const Span out[5] = {{row ? q_row : nullptr, nv_code_bytes(M, K)},
+                         {row ? s_row : nullptr, nv_scale_bytes(M, K)},
+                         {col ? q_col : nullptr, (uint64_t)gt.qcol_off[G - 1] + nv_code_bytes(K, group_rows[G - 1])},
+                         {col ? s_col : nullptr, (uint64_t)gt.scol_off[G - 1] + nv_scale_bytes(K, group_rows[G - 1])},
                          {global_scale_out, 4 * (uint64_t)G}};
     if (any_alias(in, 2, out, 5))
         return MX_ERR_ALIAS;
@@ -850,10 +871,12 @@ mx_status nvfp4_quantize_transpose_grouped(const void *x, int64_t K, const int64
     a.q_col = q_col;
     a.s_col = s_col;
     a.sg_out = global_scale_out;
-    a.tiles_k = tiles(K, mxk::kTileK);
-    a.tiles_m = tiles(M, mxk::kTileM);
+    a.tiles_k = tiles(K, any ? mxk::kAnyTileK : mxk::kTileK);
+    a.tiles_m = tiles(M, any ? mxk::kAnyTileM : mxk::kTileM);
     a.group = group;
     a.groups_m = gt.walk0[G];
+    if (any)
+        return from_hip(mxk::launch_nvfp4_any(axis_mask, scaling_2d != 0, a, gt, stream));
     return from_hip(mxk::launch_nvfp4_grouped(axis_mask, scaling_2d != 0, a, gt, stream));
 }
 

@@ -193,6 +193,7 @@ struct GroupTable {
     int64_t row0[kMaxGroups + 1];     // first row of each group; row0[count] = M
     int64_t srow_off[kMaxGroups];     // byte offset of each group's row scales
     int64_t scol_off[kMaxGroups];     // byte offset of each group's column scales
+    int64_t qcol_off[kMaxGroups];     // NVFP4 of any shape: byte offset of each group's q_col
 };
 
 struct Nv4Args {
@@ -242,5 +243,9 @@ hipError_t launch_nvfp4_grouped(unsigned axis, bool two_d, const Nv4Args &a, con
                                 hipStream_t s);
 hipError_t launch_absmax_grouped(const uint16_t *x, int64_t K, const GroupTable &gt, float *amax,
                                  hipStream_t s);
+// NVFP4 of any shape (nvfp4_any.hip): a.tiles_k = ceil(K / kAnyTileK); gt as
+// for launch_mx_cast_any, with each group's q_col and s_col offsets.
+hipError_t launch_nvfp4_any(unsigned axis, bool two_d, const Nv4Args &a, const GroupTable &gt,
+                            hipStream_t s);
 
 }  // namespace mxk

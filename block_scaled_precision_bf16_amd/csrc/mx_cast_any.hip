@@ -22,17 +22,9 @@
 // through buffer resources (bufio.h); lanes outside the tensor get the
 // out-of-range offset.
 
-#include "bufio.h"
-#include "device_math.h"
-#include "launch.h"
+#include "any_common.h"
 
 namespace mxk {
-
-template <int AUX = 0>
-__device__ __forceinline__ uint32_t buf_load2(rsrc_t r, uint32_t off)
-{
-    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, AUX);
-}
 
 // LDS of one workgroup (37.5 KB: four workgroups per CU).  Row strides are
 // multiples of 16 bytes, padded so that the 16-byte accesses of 8
@@ -59,38 +51,12 @@ __device__ __forceinline__ const uint8_t *qrow_stage(const AnyStage &st, int r)
     return reinterpret_cast<const uint8_t *>(st.y[r]);
 }
 
-// Low bits of the absolute byte address p + off.
-__device__ __forceinline__ uint32_t addr_low(const void *p, int64_t off, uint32_t mask)
-{
-    return (uint32_t)((reinterpret_cast<uintptr_t>(p) + (uint64_t)off) & mask);
-}
-
-// The four bytes at staged position i (any alignment) of an LDS row whose
-// dwords at i & ~3 and (i & ~3) + 4 exist.
-__device__ __forceinline__ uint32_t lds_word_at(const uint8_t *row, int i)
-{
-    const uint32_t *w = reinterpret_cast<const uint32_t *>(row + (i & ~3));
-    return __builtin_amdgcn_alignbyte(w[1], w[0], (uint32_t)(i & 3));
-}
-
 // One tensor of the launch (the whole input, or one group of a stack).
 struct AnyView {
     const uint16_t *x, *aux;
     int64_t M;
     uint8_t *q_row, *s_row, *q_col, *s_col;
 };
-
-__device__ __forceinline__ uint32_t pack2(uint32_t lo, uint32_t hi) { return lo | (hi << 16); }
-
-// Descriptor of row `row` (of `rows`, `ld` elements apart) of a bf16 tensor,
-// from column `col` to the tensor's end; size 0 for a row at or past the
-// last.  The row is the same for every lane of a wave, so the descriptor is
-// scalar and each lane needs a single offset register (its column).
-__device__ __forceinline__ rsrc_t row_rsrc(const uint16_t *p, int64_t row, int64_t ld, int64_t rows,
-                                           int64_t col = 0)
-{
-    return make_rsrc(p, 2 * (row * ld + col), 2 * rows * ld);
-}
 
 // Column k of the quantised tensor, rows m .. m + 31 (those at or past the
 // tensor's M read as 0), after the pre-op: word i holds rows 2i (low half)
@@ -217,113 +183,6 @@ __device__ __forceinline__ void any_store_srow(const MxArgs &a, const AnyView &v
     buf_store1(rs, ok ? (uint32_t)(tile_offset(m0 + r, b, RT) - base) : kDead, (uint8_t)sb);
 }
 
-// Staged row-wise codes of a step -> q_row: rows m0 .. m0 + 63, columns
-// k0 .. k0 + krem - 1.  Rows whose bytes start 16-byte aligned (q_row and K
-// both aligned) leave as 16-byte pieces, 8 rows per wave instruction.
-// Otherwise each row leaves as the aligned dwords inside its segment
-// (16-byte aligned ... 1-byte aligned rows alike), two rows per wave
-// instruction, each dword assembled from two aligned LDS dwords, plus at
-// most 3 head and 3 tail bytes.  Every instruction's rows are the same for
-// all lanes of a half-wave; the descriptor starts at row m0, so rows past M
-// lie outside it.
-__device__ __forceinline__ void any_flush_qrow(const MxArgs &a, const AnyView &v, const AnyStage &st,
-                                               int64_t m0, int64_t k0, int krem)
-{
-    const int lane = (int)threadIdx.x & 63;
-    const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    const rsrc_t rq = make_rsrc(v.q_row, m0 * a.K + k0, v.M * a.K);
-    const int mrem = (int)(v.M - m0 < kAnyTileM ? v.M - m0 : kAnyTileM);
-    if ((a.K & 15) == 0 && addr_low(v.q_row, 0, 15) == 0) {
-        const int sub = lane >> 3, p = lane & 7;    // 8 rows x 8 pieces per instruction
-#pragma unroll
-        for (int i = 0; i < 2; i++) {
-            const int r = 8 * (wv + 4 * i) + sub;
-            const bool ok = r < mrem && 16 * p < krem;
-            buf_store16(rq, ok ? (uint32_t)(r * a.K + 16 * p) : kDead,
-                        *reinterpret_cast<const uint4 *>(qrow_stage(st, r) + 16 * p));
-        }
-        return;
-    }
-    // aligned dwords: lanes 0-31 and 32-63 take dword u = lane % 32 of two rows
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-        const int r = 2 * (wv + 4 * i) + (lane >> 5), u = lane & 31;
-        const uint32_t al = addr_low(v.q_row, (m0 + r) * a.K + k0, 3);
-        const int head = min(krem, (int)((4 - al) & 3));
-        const int nd = (krem - head) >> 2;
-        const int i0 = head + 4 * u;
-        const bool ok = r < mrem && u < nd;
-        buf_store4(rq, ok ? (uint32_t)(r * a.K + i0) : kDead,
-                   lds_word_at(qrow_stage(st, r), ok ? i0 : 0));
-    }
-    // head bytes (slots 0-2) and tail bytes (slots 3-5) of 8 rows per instruction
-#pragma unroll
-    for (int i = 0; i < 2; i++) {
-        const int r = 8 * (wv + 4 * i) + (lane >> 3), slot = lane & 7;
-        const uint32_t al = addr_low(v.q_row, (m0 + r) * a.K + k0, 3);
-        const int head = min(krem, (int)((4 - al) & 3));
-        const int tail0 = head + 4 * ((krem - head) >> 2);
-        const int b = slot < 3 ? slot : tail0 + slot - 3;
-        const bool ok = r < mrem && (slot < 3 ? slot < head : slot < 6 && b < krem);
-        buf_store1(rq, ok ? (uint32_t)(r * a.K + b) : kDead, qrow_stage(st, r)[ok ? b : 0]);
-    }
-}
-
-// Transposed codes of step s -> q_col.  Transposed row c's bytes of this
-// step, codes 0 .. mrem - 1, start at an address whose offset within its
-// 64-byte chunk, sft, is the same at every step (steps are 64 rows apart).
-// The step writes the chunk that starts sft bytes before its first code:
-// bytes 0 .. sft - 1 are the previous step's last codes, still in the
-// other half of the ring, and bytes sft .. 63 this step's first.  Its last
-// sft codes wait for the next step; the walk's last step writes them too.
-// At the walk's first step the chunk's first sft bytes belong to the walk
-// before and are left alone.  Whole 16-byte pieces leave as 16-byte stores
-// (16 rows x 4 pieces per wave instruction), assembled from aligned LDS
-// dwords; pieces with bytes outside the walk leave byte by byte.
-__device__ __forceinline__ void any_flush_qcol(const MxArgs &a, const AnyView &v, const AnyStage &st,
-                                               int64_t m0, int64_t k0, int mrem, int s, bool last)
-{
-    const int t = (int)threadIdx.x;
-    const rsrc_t rc = make_rsrc(v.q_col, k0 * v.M, a.K * v.M);
-    const int np = last ? 8 : 4;                  // pieces per transposed row
-    const int shift = last ? 3 : 2;
-    for (int i = 0; i < (kAnyTileK * np) / kThreads; i++) {
-        const int idx = t + kThreads * i;
-        const int c = idx >> shift, j = idx & (np - 1);
-        const int sft = (int)addr_low(v.q_col, (k0 + c) * v.M + m0, 63);
-        const int lo = s > 0 ? 0 : sft;           // chunk bytes [lo, hi) exist
-        const int hi = sft + mrem;
-        const int64_t co = (int64_t)c * v.M + m0 - sft;   // chunk start (may be < 0 when lo > 0)
-        const int v0 = (64 * (s & 1) - sft + 16 * j) & 127;   // ring position of byte 16 j
-        const uint8_t *ring = st.qt[c];
-        const bool row_ok = k0 + c < a.K;
-        const bool whole = row_ok && lo <= 16 * j && 16 * j + 16 <= hi;
-        uint4 o;
-        {
-            const uint32_t *w = reinterpret_cast<const uint32_t *>(ring);
-            const int f = v0 >> 2, sh = v0 & 3;
-            uint32_t d[5];
-#pragma unroll
-            for (int e = 0; e < 5; e++)
-                d[e] = w[(f + e) & 31];
-            o = make_uint4(__builtin_amdgcn_alignbyte(d[1], d[0], sh),
-                           __builtin_amdgcn_alignbyte(d[2], d[1], sh),
-                           __builtin_amdgcn_alignbyte(d[3], d[2], sh),
-                           __builtin_amdgcn_alignbyte(d[4], d[3], sh));
-        }
-        buf_store16(rc, whole ? (uint32_t)(co + 16 * j) : kDead, o);
-        const bool part = row_ok && !whole && 16 * j < hi && 16 * j + 16 > lo;
-        if (__builtin_amdgcn_ballot_w64(part) != 0) {   // uniform: first and last steps only
-#pragma unroll
-            for (int b = 0; b < 16; b++) {
-                const int pb = 16 * j + b;
-                const bool ok = part && pb >= lo && pb < hi;
-                buf_store1(rc, ok ? (uint32_t)(co + pb) : kDead, ring[(v0 + b) & 127]);
-            }
-        }
-    }
-}
-
 // One 64 x 128 step (the s-th of the walk) at rows m0, columns k0; w: this
 // thread's column values (column k0 + t % 128, rows m0 + 32 (t / 128) + i).
 template <int FMT>
@@ -388,11 +247,14 @@ __device__ __forceinline__ void any_step(const MxArgs &a, const AnyView &v, AnyS
             any_store_srow(a, v, m0, tk, r, b + 4, 0u);
     }
     __syncthreads();
+    const int mrem = (int)(v.M - m0 < kAnyTileM ? v.M - m0 : kAnyTileM);
     if (row)
-        any_flush_qrow(a, v, st, m0, k0, (int)(a.K - k0 < kAnyTileK ? a.K - k0 : kAnyTileK));
+        flush_rows<kAnyTileK>(v.q_row, a.K, m0, k0, v.M * a.K, mrem,
+                              (int)(a.K - k0 < kAnyTileK ? a.K - k0 : kAnyTileK), qrow_stage(st, 0),
+                              (int)sizeof(st.y[0]));
     if (col)
-        any_flush_qcol(a, v, st, m0, k0, (int)(v.M - m0 < kAnyTileM ? v.M - m0 : kAnyTileM), s,
-                       last_step);
+        flush_cols<kAnyTileM>(v.q_col, v.M, k0, a.K, m0, mrem, s, last_step, st.qt[0],
+                              (int)sizeof(st.qt[0]));
     __syncthreads();
 }
 

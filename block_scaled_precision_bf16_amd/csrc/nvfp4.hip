@@ -22,60 +22,10 @@
 #include "bufio.h"
 #include "device_math.h"
 #include "launch.h"
+#include "nv_block.h"
 #include "stage_flush.h"
 
 namespace mxk {
-
-// Scale byte of one NVFP4 block whose largest magnitude has bf16 pattern
-// mag: E4M3(fl32(fl32(b / 6) / S_g)).  The division by S_g gives the IEEE
-// quotient wherever the code can be non-zero (div_by, prepared once per
-// workgroup); the E4M3 rounding is the saturating hardware convert (inputs
-// are finite here).
-__device__ __forceinline__ uint32_t nv_scale(uint32_t mag, const DivBy &sg)
-{
-    const float sq = div_by(div6_bf16(f32_bits(mag << 16)), sg);
-    return e4m3x2<false>(sq, 0.0f, 0u) & 0xFFu;
-}
-
-// Element multiplier of scale byte s: fl32(1 / fl32(dec(s) * S_g)), 0 when
-// the product is 0.  It depends on s alone within a tensor, so a workgroup
-// tabulates the 127 finite codes once.
-__device__ __forceinline__ float nv_inverse(uint32_t s, float sg)
-{
-    const float den = e4m3_value(s) * sg;
-    return den == 0.0f ? 0.0f : 1.0f / den;
-}
-
-// 0xF when bf16 h is +-0 or NaN (its product with an infinite multiplier is
-// NaN), else 0.
-__device__ __forceinline__ uint32_t zero_or_nan_nibble(uint32_t h)
-{
-    const uint32_t a = h & 0x7FFFu;
-    return (a == 0u || a > 0x7F80u) ? 0xFu : 0u;
-}
-
-// Eight bf16 (four words) times inv -> eight E2M1 nibbles, element i in bits
-// 4i..4i+3 (so element 2j is the low nibble of byte j).  The hardware
-// convert gives the nearest E2M1 code on every non-NaN product (e2m1x2); a
-// NaN product (0 * Inf or NaN * Inf, possible only when the multiplier
-// overflowed to Inf, tensor scale below ~2^-120) must encode as +0, so such
-// nibbles are cleared afterwards.
-__device__ __forceinline__ uint32_t encode8_fp4(const uint32_t (&w)[4], float inv)
-{
-    uint32_t o = e2m1x2<0>(bf16_lo(w[0]) * inv, bf16_hi(w[0]) * inv, 0u);
-    o = e2m1x2<1>(bf16_lo(w[1]) * inv, bf16_hi(w[1]) * inv, o);
-    o = e2m1x2<2>(bf16_lo(w[2]) * inv, bf16_hi(w[2]) * inv, o);
-    o = e2m1x2<3>(bf16_lo(w[3]) * inv, bf16_hi(w[3]) * inv, o);
-    const bool inf = __builtin_isinf(inv);
-    if (__builtin_amdgcn_ballot_w64(inf) != 0) {   // uniform: no lane's exec mask changes
-        uint32_t clear = 0;
-#pragma unroll
-        for (int d = 0; d < 4; d++)
-            clear |= (zero_or_nan_nibble(w[d]) << (8 * d)) | (zero_or_nan_nibble(w[d] >> 16) << (8 * d + 4));
-        o &= inf ? ~clear : ~0u;
-    }
-    return o;
-}
 
 // Rows 8q..8q+7 of one column (half HI of word d) times inv -> eight nibbles,
 // row 8q+i in bits 4i..4i+3 (NaN products cleared as above).
@@ -441,8 +391,6 @@ __device__ __forceinline__ void nv_step(const Nv4Args &a, const NvLane &l,
 // with the next sub-tile's loads in flight while one is converted (as in the
 // MXFP8 cast); the transposed output leaves every second sub-tile as whole
 // 128-byte lines.
-// The global scale of a tensor with amax A: A / (448 * 6), 1 for A = 0.
-__device__ __forceinline__ float nv_global_scale(float A) { return A == 0.0f ? 1.0f : A / 2688.0f; }
 
 // A tensor whose amax is not finite (it holds an Inf or a NaN) has no usable
 // global scale: the walk's sub-tiles get scale bytes 0x7F (the E4M3 NaN) and
@@ -653,9 +601,7 @@ __global__ __launch_bounds__(256) void absmax_kernel(const uint16_t *x, int64_t 
     absmax_commit(m, amax_bits);
 }
 
-// Per-group absmax: blockIdx.y is the group, whose rows are x[row0[g] ..
-// row0[g + 1]) of width K (a multiple of 16, so every group starts and ends
-// on whole 16-byte vectors).
+// Per-group absmax: group g's elements are x[row0[g] K .. row0[g + 1] K).
 __global__ void absmax_clear_grouped_kernel(uint32_t *amax_bits, int G)
 {
     if ((int)threadIdx.x < G)
@@ -669,6 +615,10 @@ struct AbsmaxPlan {
     int blk0[kMaxGroups + 1];
 };
 
+// The group's workgroups split the whole 16-byte vectors inside its element
+// range; its first workgroup also takes the elements before the first and
+// after the last of them (fewer than 8 each; all of them when the range
+// holds no whole vector).
 __global__ __launch_bounds__(256) void absmax_grouped_kernel(const uint16_t *x, int64_t K,
                                                              GroupTable gt, AbsmaxPlan plan,
                                                              uint32_t *amax_bits)
@@ -677,11 +627,19 @@ __global__ __launch_bounds__(256) void absmax_grouped_kernel(const uint16_t *x, 
     int g = 0;
     while (g + 1 < gt.count && plan.blk0[g + 1] <= b)
         g++;
-    const int64_t r0 = gt.row0[g];
+    const int64_t e0 = gt.row0[g] * K, e1 = gt.row0[g + 1] * K;
+    const int64_t v0 = (e0 + 7) >> 3, v1 = e1 >> 3;         // whole vectors [v0, v1)
     int64_t b0, b1;
-    chunk_of(((gt.row0[g + 1] - r0) * K) >> 3, b - plan.blk0[g], plan.blk0[g + 1] - plan.blk0[g],
-             b0, b1);
-    const uint32_t m = absmax_chunk(x + r0 * K, b0, b1);
+    chunk_of(v1 > v0 ? v1 - v0 : 0, b - plan.blk0[g], plan.blk0[g + 1] - plan.blk0[g], b0, b1);
+    uint32_t m = absmax_chunk(x + 8 * v0, b0, b1);
+    if (b == plan.blk0[g] && threadIdx.x < 14) {
+        const int64_t head_end = 8 * v0 < e1 ? 8 * v0 : e1;
+        const int64_t tail0 = 8 * v1 > head_end ? 8 * v1 : head_end;
+        const int i = (int)threadIdx.x;
+        const int64_t e = i < 7 ? e0 + i : tail0 + (i - 7);
+        if (i < 7 ? e < head_end : e < e1)
+            m = pk_max_u16(m, x[e] & 0x7FFFu);
+    }
     absmax_commit(m, amax_bits + g);
 }
 

@@ -343,12 +343,19 @@ static void grouped_cases()
             CHECK(g_rec.mx.K == 2 * c.K && g_rec.mx.tiled == 1);
             check_groups(c.rows, c.G, g_rec.mx.groups_m, any);
         }
-        if (c.K % 16 == 0 && rows16) {
+        {
+            const bool nv_any = !(c.K % 16 == 0 && rows16);
             for (int two_d : {0, 1}) {
                 EXPECT(MX_OK, nvfp4_quantize_transpose_grouped(P(0), c.K, c.rows, c.G, P<float>(1), two_d,
                                                                both, qr, sr, qc, sc, P<float>(6), 0));
-                check_groups(c.rows, c.G, g_rec.nv.groups_m);
+                CHECK(g_rec.kind == (nv_any ? mxk::kLaunchNvAny : mxk::kLaunchNvGrouped));
+                check_groups(c.rows, c.G, g_rec.nv.groups_m, nv_any);
                 CHECK((int64_t)g_rec.nv.groups_m * g_rec.nv.tiles_k <= INT32_MAX);
+                int64_t qo = 0, so = 0;
+                for (int g = 0; g < c.G; g++) {
+                    CHECK(g_rec.gt.qcol_off[g] == qo && g_rec.gt.scol_off[g] == so);
+                    qo += c.K * ((c.rows[g] + 1) / 2), so += c.K * ((c.rows[g] + 15) / 16);
+                }
             }
             EXPECT(MX_OK, mx_absmax_bf16_grouped(P(0), c.K, c.rows, c.G, P<float>(1), 0));
         }
@@ -371,11 +378,13 @@ static void grouped_cases()
         CHECK(mx_quantize_grouped_workspace_size(256, b.rows, b.G, both, MX_FUSE_DBIAS) == 0);
         CHECK(mx_grouped_scale_size(256, b.rows, b.G, both, 0) == 0);
     }
-    // NVFP4 keeps whole 16-element blocks: group rows must be multiples of 16
+    // row counts that are not multiples of 16: the any-shape kernels
     const int64_t odd[2] = {16, 8};
-    EXPECT(MX_ERR_SHAPE, nvfp4_quantize_transpose_grouped(P(0), 256, odd, 2, P<float>(1), 0, both,
-                                                          qr, sr, qc, sc, nullptr, 0));
-    EXPECT(MX_ERR_SHAPE, mx_absmax_bf16_grouped(P(0), 256, odd, 2, P<float>(1), 0));
+    EXPECT(MX_OK, nvfp4_quantize_transpose_grouped(P(0), 256, odd, 2, P<float>(1), 0, both, qr, sr,
+                                                   qc, sc, nullptr, 0));
+    CHECK(g_rec.kind == mxk::kLaunchNvAny && g_rec.gt.qcol_off[1] == 256 * 8 &&
+          g_rec.gt.scol_off[1] == 256);
+    EXPECT(MX_OK, mx_absmax_bf16_grouped(P(0), 256, odd, 2, P<float>(1), 0));
     EXPECT(MX_OK, mx_quantize_grouped(P(0), nullptr, 256, odd, 2, both, 0, qr, sr, qc, sc, nullptr,
                                       nullptr, 0, 0));
     CHECK(g_rec.kind == mxk::kLaunchMxAny);
@@ -395,19 +404,42 @@ static void nvfp4_cases()
 {
     const unsigned both = MX_ROWWISE | MX_COLWISE;
     uint8_t *qr = P(2), *sr = P(3), *qc = P(4), *sc = P(5);
-    const int64_t ok[][2] = {{16384, 16384}, {kDim, 1 << 17}, {16, kDim}, {kDim, 16}, {16400, 7168}};
+    // multiples of 16 take the tiled kernel, any other shape the any-shape kernel
+    const int64_t ok[][2] = {{16384, 16384}, {kDim, 1 << 17}, {16, kDim}, {kDim, 16}, {16400, 7168},
+                             {8, 16}, {16, 8}, {1, 1}, {kDim, 1}, {1, kDim}, {16383, 16383},
+                             {kDim - 1, (1 << 17) - 1}};
     for (auto &s : ok) {
+        const bool any = s[0] % 16 != 0 || s[1] % 16 != 0;
         for (int two_d : {0, 1}) {
             EXPECT(MX_OK, (two_d ? nvfp4_quantize_transpose_2d : nvfp4_quantize_transpose)(
                               P(0), s[0], s[1], P<float>(1), both, qr, sr, qc, sc, P<float>(6), 0));
             const mxk::Nv4Args &a = g_rec.nv;
             CHECK(a.M == s[0] && a.K == s[1] && g_rec.two_d == (two_d != 0));
-            check_plan(s[0], s[1], a.tiles_m, a.tiles_k, a.group, a.groups_m, false);
+            CHECK(g_rec.kind == (any ? mxk::kLaunchNvAny : mxk::kLaunchNv));
+            if (any) {
+                const mxk::GroupTable &gt = g_rec.gt;
+                CHECK(a.tiles_m == ceil_div(s[0], mxk::kAnyTileM) &&
+                      a.tiles_k == ceil_div(s[1], mxk::kAnyTileK));
+                CHECK(gt.count == 1 && gt.row0[1] == s[0] && gt.walk0[1] == a.groups_m &&
+                      gt.len[0] == a.group && a.group >= 1 && a.group <= mxk::kAnyMaxWalk);
+                CHECK(gt.qcol_off[0] == 0 && gt.scol_off[0] == 0);
+                CHECK((int64_t)a.groups_m * a.tiles_k <= INT32_MAX);
+            } else {
+                check_plan(s[0], s[1], a.tiles_m, a.tiles_k, a.group, a.groups_m, false);
+            }
         }
         EXPECT(MX_OK, mx_absmax_bf16(P(0), s[0] * s[1], P<float>(1), 0));
     }
-    const int64_t bad[][2] = {{8, 16}, {16, 8}, {kDim + 16, 16}, {kDim, (1 << 17) + 16}, {kBig, kBig},
-                              {-16, 16}, {16, INT64_MIN}, {int64_t(1) << 62, int64_t(1) << 62}};
+    // outputs sized [rows][ceil(cols/2)] and [rows][ceil(cols/16)]: q_col of a
+    // 31 x 9 tensor is 9 * 16 bytes, so an s_col 144 bytes after it is
+    // disjoint and one 128 bytes after it overlaps
+    EXPECT(MX_OK, nvfp4_quantize_transpose(P(0), 31, 9, P<float>(1), both, qr, sr, P(4), P(4, 144),
+                                           nullptr, 0));
+    EXPECT(MX_ERR_ALIAS, nvfp4_quantize_transpose(P(0), 31, 9, P<float>(1), both, qr, sr, P(4),
+                                                  P(4, 128), nullptr, 0));
+    const int64_t bad[][2] = {{0, 16}, {16, 0}, {kDim + 16, 16}, {kDim, (1 << 17) + 16}, {kBig, kBig},
+                              {-16, 16}, {16, INT64_MIN}, {int64_t(1) << 62, int64_t(1) << 62},
+                              {kDim + 1, 1}, {kDim, (1 << 17) + 1}};
     for (auto &s : bad)
         for (int two_d : {0, 1})
             EXPECT(MX_ERR_SHAPE, (two_d ? nvfp4_quantize_transpose_2d : nvfp4_quantize_transpose)(

@@ -88,6 +88,13 @@ hipError_t launch_nvfp4(unsigned axis, bool two_d, const Nv4Args &a, hipStream_t
     return note(kLaunchNv);
 }
 
+hipError_t launch_nvfp4_any(unsigned axis, bool two_d, const Nv4Args &a, const GroupTable &gt,
+                            hipStream_t)
+{
+    g_rec.axis = axis, g_rec.two_d = two_d, g_rec.nv = a, g_rec.gt = gt;
+    return note(kLaunchNvAny);
+}
+
 hipError_t launch_nvfp4_grouped(unsigned axis, bool two_d, const Nv4Args &a,
                                 const GroupTable &gt, hipStream_t)
 {

@@ -5,7 +5,7 @@
 namespace mxk {
 
 enum { kLaunchNone, kLaunchMx, kLaunchMxGrouped, kLaunchValues, kLaunchAbsmax, kLaunchNv,
-       kLaunchNvGrouped, kLaunchAbsmaxGrouped, kLaunchMxAny, kLaunchValuesAny };
+       kLaunchNvGrouped, kLaunchAbsmaxGrouped, kLaunchMxAny, kLaunchValuesAny, kLaunchNvAny };
 
 struct Record {
     int calls = 0, reduces = 0, kind = kLaunchNone;

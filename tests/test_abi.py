@@ -259,7 +259,7 @@ def test_nvfp4_and_absmax_reject():
     assert n(axis=3 | mx.ELEM_E5M2) == mx.MX_ERR_ENUM      # NVFP4 has no format flags
     assert n(axis=1 | mx.SCALE_ROUND_UP) == mx.MX_ERR_ENUM
     assert n(amax=NULL) == mx.MX_ERR_NULL and n(x=NULL) == mx.MX_ERR_NULL
-    assert n(M=24) == mx.MX_ERR_SHAPE and n(K=8) == mx.MX_ERR_SHAPE
+    assert n(M=0) == mx.MX_ERR_SHAPE and n(K=-16) == mx.MX_ERR_SHAPE   # any M, K >= 1 is a shape
     assert n(s_col=b.p("s_col", 1)) == mx.MX_ERR_ALIGN
     assert n(sg=b.p("x", 4)) == mx.MX_ERR_ALIAS
     assert n(amax=b.p("q_row", 0)) == mx.MX_ERR_ALIAS
@@ -361,11 +361,11 @@ def test_grouped_nvfp4_rejects():
     assert nq(two_d=2) == mx.MX_ERR_ENUM
     assert nq(x=NULL) == mx.MX_ERR_NULL and nq(amax=NULL) == mx.MX_ERR_NULL
     assert nq(rows_p=NULL) == mx.MX_ERR_NULL
-    assert nq(rows=(32, 8)) == mx.MX_ERR_SHAPE and nq(K=40) == mx.MX_ERR_SHAPE
+    assert nq(rows=(32, -16)) == mx.MX_ERR_SHAPE and nq(K=0) == mx.MX_ERR_SHAPE
     assert nq(rows=(0,)) == mx.MX_ERR_SHAPE and nq(rows=tuple([16] * 65)) == mx.MX_ERR_SHAPE
     assert nq(s_col=b.p("s_col", 4)) == mx.MX_ERR_ALIGN
     assert nq(sg=b.p("x", 0)) == mx.MX_ERR_ALIAS
-    assert am(x=NULL) == mx.MX_ERR_NULL and am(rows=(24,)) == mx.MX_ERR_SHAPE
+    assert am(x=NULL) == mx.MX_ERR_NULL and am(rows=(-8,)) == mx.MX_ERR_SHAPE
     assert am(amax=b.p("x", 16)) == mx.MX_ERR_ALIAS
     assert b.untouched()
 

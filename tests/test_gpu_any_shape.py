@@ -237,3 +237,115 @@ def test_any_metric_sized():
     r = mx.mx_quantize(to_dev(x), axis=3)
     torch.cuda.synchronize()
     mx_outputs_equal(r, O.mx_quantize(x, axis=3), "16383^2")
+
+
+# --- NVFP4 of any shape ---------------------------------------------------------
+
+def nv_guarded(M, K, axis, n_sg=1, qcol=None, scol=None):
+    """NVFP4 outputs ([rows][ceil(cols/2)] codes, [rows][ceil(cols/16)] scales)
+    in canary-filled buffers with guard bands."""
+    shapes = {}
+    if axis & mx.ROWWISE:
+        shapes["q_row"] = (M, -(-K // 2))
+        shapes["s_row"] = (M, -(-K // 16))
+    if axis & mx.COLWISE:
+        shapes["q_col"] = (qcol,) if qcol is not None else (K, -(-M // 2))
+        shapes["s_col"] = (scol,) if scol is not None else (K, -(-M // 16))
+    g = Guarded.__new__(Guarded)
+    g.bufs, g.out = {}, {}
+    for name, shape in shapes.items():
+        n = int(np.prod(shape))
+        b = torch.full((n + 2 * GUARD,), CANARY, dtype=torch.uint8, device="cuda")
+        g.bufs[name] = b
+        g.out[name] = b[GUARD:GUARD + n].view(shape)
+    g.out["sg"] = torch.empty(n_sg, dtype=torch.float32, device="cuda")
+    return g
+
+
+def nv_both(x, axis=3, two_d=False):
+    M, K = x.shape
+    xd = to_dev(x)
+    amax = mx.mx_absmax_bf16(xd)
+    g = nv_guarded(M, K, axis)
+    r = mx.nvfp4_quantize_transpose(xd, amax, axis=axis, two_d=two_d, out=g.out)
+    torch.cuda.synchronize()
+    o = O.nvfp4_quantize_transpose(x, axis=axis, two_d=two_d)
+    return r, o, g
+
+
+NV_SHAPES = [(1, 1), (1, 40), (40, 1), (3, 7), (17, 9), (16, 24), (24, 16), (48, 36), (100, 129),
+             (129, 300), (65, 1000), (1000, 65), (191, 257), (2049, 1030)]
+
+
+@pytest.mark.parametrize("two_d", [False, True], ids=["1d", "2d"])
+@pytest.mark.parametrize("axis", [1, 2, 3])
+@pytest.mark.parametrize("M,K", NV_SHAPES)
+def test_nv_any(M, K, axis, two_d):
+    x = W.student_t_rows(M, K, seed=9000 + 3 * M + K)
+    r, o, g = nv_both(x, axis, two_d)
+    what = f"nvfp4 {M}x{K} axis {axis} 2d={two_d}"
+    assert r["sg"].item() == o["sg"], what
+    mx_outputs_equal(r, o, what)
+    g.guards_intact(what)
+
+
+@pytest.mark.parametrize("two_d", [False, True], ids=["1d", "2d"])
+def test_nv_any_nonfinite_and_tiny_scale(two_d):
+    x = W.student_t_rows(131, 77, seed=9100)
+    x[70, 76] = 0x7FC0                       # NaN: 0x7F scales, zero codes
+    r, o, g = nv_both(x, 3, two_d)
+    assert np.isnan(r["sg"].item()) and np.isnan(o["sg"])
+    mx_outputs_equal(r, o, "nvfp4 any non-finite")
+    g.guards_intact("nvfp4 any non-finite")
+    x = W.normal(33, 71, seed=9101, sigma=1e-37)   # multipliers that overflow to Inf
+    x[0, :16] = 0
+    x[1, 0] = 0x8000
+    r, o, g = nv_both(x, 3, two_d)
+    assert r["sg"].item() == o["sg"]
+    mx_outputs_equal(r, o, "nvfp4 any tiny S_g")
+
+
+def test_nv_any_every_scale_code():
+    rng = np.random.default_rng(9102)
+    M, K = 63, 2047
+    nb = -(-K // 16)
+    t = np.linspace(0, 1, M * nb).reshape(M, nb)
+    x = rng.standard_normal((M, nb * 16)).astype(np.float32) * np.repeat(2.0 ** (-19 * t), 16, axis=1)
+    x = W.bf16_bits(np.ascontiguousarray(x[:, :K]).astype(np.float32))
+    r, o, g = nv_both(x)
+    assert set(np.unique(o["s_row"]).tolist()) == set(range(127))
+    mx_outputs_equal(r, o, "nvfp4 any scale sweep")
+
+
+@pytest.mark.parametrize("two_d", [False, True], ids=["1d", "2d"])
+@pytest.mark.parametrize("rows,K", [([1101, 0, 17, 640, 3], 517), ([5, 1, 0, 2], 3),
+                                    ([4099, 0, 3001, 17, 9000], 4100), ([48, 16, 0, 32], 40)])
+def test_nv_any_grouped(rows, K, two_d):
+    M = sum(rows)
+    x = W.student_t_rows(M, K, seed=9200 + M + K)
+    xd = to_dev(x)
+    amax = mx.mx_absmax_bf16_grouped(xd, rows)
+    torch.cuda.synchronize()
+    r0 = 0
+    for gi, m in enumerate(rows):     # the grouped absmax over ragged groups
+        want = O.absmax(np.ascontiguousarray(x[r0:r0 + m])) if m else 0.0
+        assert amax[gi].item() == want, (gi, m)
+        r0 += m
+    qcol = K * sum(-(-m // 2) for m in rows)
+    scol = K * sum(-(-m // 16) for m in rows)
+    g = nv_guarded(M, K, 3, len(rows), qcol, scol)
+    r = mx.nvfp4_quantize_transpose_grouped(xd, rows, amax, two_d=two_d, out=g.out)
+    torch.cuda.synchronize()
+    o = O.nvfp4_quantize_transpose_grouped(x, rows, two_d=two_d)
+    assert np.array_equal(r["sg"].cpu().numpy(), o["sg"])
+    mx_outputs_equal(r, o, f"grouped nvfp4 {rows} K={K} 2d={two_d}")
+    g.guards_intact(f"grouped nvfp4 {rows} K={K}")
+
+
+@pytest.mark.parametrize("two_d", [False, True], ids=["1d", "2d"])
+def test_nv_any_large(two_d):
+    x = W.student_t_rows(8191, 8193, seed=9300)
+    r, o, g = nv_both(x, 3, two_d)
+    assert r["sg"].item() == o["sg"]
+    mx_outputs_equal(r, o, f"nvfp4 8191x8193 2d={two_d}")
+    g.guards_intact("nvfp4 8191x8193")

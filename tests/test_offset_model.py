@@ -422,6 +422,81 @@ def piece_width(n):
     return 16 if n % 16 == 0 else 4 if n % 4 == 0 else 1
 
 
+def model_flush_rows(site, base, stride, row0, col0, total, rows_left, seg, SEG):
+    """flush_rows<SEG> (any_common.h): rows row0 .. row0 + rows_left - 1, each
+    a segment of seg bytes at (row0 + r) * stride + col0; base: the output's
+    start address modulo 64."""
+    t = np.arange(THREADS)
+    lane, wv = t & 63, t >> 6
+    d = Desc(row0 * stride + col0, total)
+    out = []
+    if stride % 16 == 0 and base % 16 == 0:
+        per = SEG // 16
+        rows_per = 64 // per
+        sub, p = lane // per, lane % per
+        for i in range(ANY_M // (4 * rows_per)):
+            for w in range(WAVES):
+                sel = wv == w
+                r = rows_per * (w + 4 * i) + sub
+                ok = (r < rows_left) & (16 * p < seg)
+                out.append((f"{site} W=16", d, np.where(ok, r * stride + 16 * p, DEAD)[sel], 16,
+                            ok[sel], ((row0 + r) * stride + col0 + 16 * p)[sel]))
+        return out
+    per = SEG // 4
+    rows_per = 64 // per
+    for i in range(ANY_M // (4 * rows_per)):
+        for w in range(WAVES):
+            sel = wv == w
+            r, u = rows_per * (w + 4 * i) + lane // per, lane % per
+            al = (base + (row0 + r) * stride + col0) & 3
+            head = np.minimum(seg, (4 - al) & 3)
+            nd = (seg - head) >> 2
+            i0 = head + 4 * u
+            ok = (r < rows_left) & (u < nd)
+            out.append((f"{site} W=4", d, np.where(ok, r * stride + i0, DEAD)[sel], 4, ok[sel],
+                        ((row0 + r) * stride + col0 + i0)[sel]))
+    for i in range(2):
+        for w in range(WAVES):
+            sel = wv == w
+            r, slot = 8 * (w + 4 * i) + (lane >> 3), lane & 7
+            al = (base + (row0 + r) * stride + col0) & 3
+            head = np.minimum(seg, (4 - al) & 3)
+            tail0 = head + 4 * ((seg - head) >> 2)
+            b = np.where(slot < 3, slot, tail0 + slot - 3)
+            ok = (r < rows_left) & np.where(slot < 3, slot < head, (slot < 6) & (b < seg))
+            out.append((f"{site} W=1", d, np.where(ok, r * stride + b, DEAD)[sel], 1, ok[sel],
+                        ((row0 + r) * stride + col0 + b)[sel]))
+    return out
+
+
+def model_flush_cols(site, base, tstride, k0, K, pos, rem, s, last, CH):
+    """flush_cols<CH> (any_common.h): transposed rows k0 .. k0 + 127 of K,
+    tstride bytes apart, this step's rem bytes at byte pos of each; base: the
+    output's start address modulo 64."""
+    t = np.arange(THREADS)
+    npc = (CH // 16) * (2 if last else 1)
+    d = Desc(k0 * tstride, K * tstride)
+    out = []
+    for i in range(ANY_K * npc // THREADS):
+        idx = t + THREADS * i
+        cc, j = idx // npc, idx % npc
+        sft = (base + (k0 + cc) * tstride + pos) % CH
+        lo = np.where(s > 0, 0, sft)
+        hi = sft + rem
+        co = cc * tstride + pos - sft
+        row_ok = k0 + cc < K
+        whole = row_ok & (lo <= 16 * j) & (16 * j + 16 <= hi)
+        out.append((f"{site} W=16", d, np.where(whole, co + 16 * j, DEAD), 16, whole,
+                    (k0 + cc) * tstride + pos - sft + 16 * j))
+        part = row_ok & ~whole & (16 * j < hi) & (16 * j + 16 > lo)
+        for b in range(16):
+            pb = 16 * j + b
+            ok = part & (pb >= lo) & (pb < hi)
+            out.append((f"{site} W=1", d, np.where(ok, co + pb, DEAD), 1, ok,
+                        (k0 + cc) * tstride + pos - sft + pb))
+    return out
+
+
 def any_sites(M, K, op, tiled, walk, tk, steps, qrow_base=0, qcol_base=0, L=None):
     """Every access of workgroup (walk, tk) for the given steps of its walk,
     as (site, descriptor, offsets, bytes, live, logical address) tuples."""
@@ -497,66 +572,10 @@ def any_sites(M, K, op, tiled, walk, tk, steps, qrow_base=0, qcol_base=0, L=None
                 to = tile_offset(m0 + r, b, RT)
                 out.append(("any s_row tiled", Desc(base, RT * CT * 256),
                             np.where(ok, to - base, DEAD), 1, ok, to))
-        # q_row: 16-byte pieces when rows start 16-byte aligned, else the
-        # aligned dwords inside each row's segment plus head and tail bytes
         krem = min(K - k0, ANY_K)
         mrem = min(M - m0, ANY_M)
-        dq = Desc(m0 * K + k0, M * K)
-        if K % 16 == 0 and qrow_base % 16 == 0:
-            sub, p = lane >> 3, lane & 7
-            for i in range(2):
-                for w in range(WAVES):
-                    sel = wv == w
-                    r = 8 * (w + 4 * i) + sub
-                    ok = (r < mrem) & (16 * p < krem)
-                    out.append(("any q_row W=16", dq, np.where(ok, r * K + 16 * p, DEAD)[sel], 16,
-                                ok[sel], ((m0 + r) * K + k0 + 16 * p)[sel]))
-        else:
-            for i in range(8):
-                for w in range(WAVES):
-                    sel = wv == w
-                    r, u = 2 * (w + 4 * i) + (lane >> 5), lane & 31
-                    al = (qrow_base + (m0 + r) * K + k0) & 3
-                    head = np.minimum(krem, (4 - al) & 3)
-                    nd = (krem - head) >> 2
-                    i0 = head + 4 * u
-                    ok = (r < mrem) & (u < nd)
-                    out.append(("any q_row W=4", dq, np.where(ok, r * K + i0, DEAD)[sel], 4, ok[sel],
-                                ((m0 + r) * K + k0 + i0)[sel]))
-            for i in range(2):
-                for w in range(WAVES):
-                    sel = wv == w
-                    r, slot = 8 * (w + 4 * i) + (lane >> 3), lane & 7
-                    al = (qrow_base + (m0 + r) * K + k0) & 3
-                    head = np.minimum(krem, (4 - al) & 3)
-                    tail0 = head + 4 * ((krem - head) >> 2)
-                    b = np.where(slot < 3, slot, tail0 + slot - 3)
-                    ok = (r < mrem) & np.where(slot < 3, slot < head, (slot < 6) & (b < krem))
-                    out.append(("any q_row W=1", dq, np.where(ok, r * K + b, DEAD)[sel], 1, ok[sel],
-                                ((m0 + r) * K + k0 + b)[sel]))
-        # q_col: the 64-byte chunk that ends sft bytes into this step (16-byte
-        # pieces, or bytes where the chunk reaches outside the walk); the
-        # walk's last step also writes the chunk after it
-        last = s == n - 1
-        npc = 8 if last else 4
-        dc = Desc(k0 * M, K * M)
-        for i in range(ANY_K * npc // THREADS):
-            idx = t + THREADS * i
-            cc, j = idx >> (3 if last else 2), idx & (npc - 1)
-            sft = (qcol_base + (k0 + cc) * M + m0) & 63
-            lo = np.where(s > 0, 0, sft)
-            hi = sft + mrem
-            co = cc * M + m0 - sft
-            row_ok = k0 + cc < K
-            whole = row_ok & (lo <= 16 * j) & (16 * j + 16 <= hi)
-            out.append(("any q_col W=16", dc, np.where(whole, co + 16 * j, DEAD), 16, whole,
-                        (k0 + cc) * M + m0 - sft + 16 * j))
-            part = row_ok & ~whole & (16 * j < hi) & (16 * j + 16 > lo)
-            for b in range(16):
-                pb = 16 * j + b
-                ok = part & (pb >= lo) & (pb < hi)
-                out.append(("any q_col W=1", dc, np.where(ok, co + pb, DEAD), 1, ok,
-                            (k0 + cc) * M + m0 - sft + pb))
+        out += model_flush_rows("any q_row", qrow_base, K, m0, k0, M * K, mrem, krem, 128)
+        out += model_flush_cols("any q_col", qcol_base, M, k0, K, m0, mrem, s, s == n - 1, 64)
     # column scales at the walk's end
     jb, cnt = 2 * t0, 2 * n
     last_walk = walk + 1 == walks
@@ -651,6 +670,103 @@ def test_any_shape_writes_every_byte_once(M, K, tiled, bases, walk):
             for site, d, off, nbytes, live, addr in any_sites(M, K, "plain", tiled, w, tk,
                                                               range(L), *bases, L=L):
                 name = next((nm for nm in count if site.startswith("any " + nm)), None)
+                if name is None:
+                    continue
+                a = np.broadcast_to(addr, live.shape)[live]
+                for b in range(nbytes):
+                    np.add.at(count[name], a + b, 1)
+    for name, cnt in count.items():
+        assert (cnt == 1).all(), (name, int((cnt == 0).sum()), int((cnt > 1).sum()))
+
+
+# ---------------------------------------------------------------------------
+# NVFP4 of any shape (nvfp4_any.hip): the same walk, 16-element blocks, codes
+# [rows][ceil(cols/2)] (64 bytes per row and 32 per transposed row per step),
+# scales [rows][ceil(cols/16)].
+# ---------------------------------------------------------------------------
+def nv_any_sites(M, K, walk, tk, steps, qrow_base=0, qcol_base=0, L=None):
+    L = L or any_walk_len([M], K)
+    tiles_m = -(-M // ANY_M)
+    t = np.arange(THREADS)
+    c = t & 127
+    t0 = walk * L
+    n = min(L, tiles_m - t0)
+    k0 = tk * ANY_K
+    k = k0 + c
+    lk, lm = -(-K // 2), -(-M // 2)
+    nbk, nbm = -(-K // 16), -(-M // 16)
+    out = []
+    for s in steps:
+        if s >= n:
+            continue
+        m0 = (t0 + s) * ANY_M
+        mrem = min(M - m0, ANY_M)
+        for h in (0, 1):
+            kh = k[t >> 7 == h]
+            for i in (0, 31):
+                row = m0 + 32 * h + i
+                ok = (kh < K) & (row < M)
+                out.append(("nv x", Desc(2 * row * K, 2 * M * K), np.where(kh < K, 2 * kh, DEAD), 2,
+                            ok, 2 * (row * K + kh)))
+        r, qq = t >> 2, t & 3
+        for bq in (0, 1):
+            b = 8 * tk + 2 * qq + bq
+            ok = (m0 + r < M) & (b < nbk)
+            out.append(("nv s_row", Desc(m0 * nbk, M * nbk), np.where(ok, r * nbk + b, DEAD), 1, ok,
+                        (m0 + r) * nbk + b))
+        out += model_flush_rows("nv q_row", qrow_base, lk, m0, 64 * tk, M * lk, mrem,
+                                min(64, lk - 64 * tk), 64)
+        out += model_flush_cols("nv q_col", qcol_base, lm, k0, K, m0 // 2, -(-mrem // 2), s,
+                                s == n - 1, 32)
+    idx = np.arange(ANY_K * 4 * ANY_WALK)
+    cc, jj = idx // (4 * ANY_WALK), idx % (4 * ANY_WALK)
+    jb = 4 * t0
+    ok = (jj < 4 * n) & (k0 + cc < K) & (jb + jj < nbm)
+    out.append(("nv s_col", Desc(k0 * nbm + jb, K * nbm), np.where(ok, cc * nbm + jj, DEAD), 1, ok,
+                (k0 + cc) * nbm + jb + jj))
+    return out
+
+
+NV_ANY_SHAPES = [(MAXD, 1), (1, MAXD), (MAXD - 1, 9), (MAXD, 12), (MAXD, (1 << 17) - 1),
+                 ((1 << 17) - 3, MAXD), (17, MAXD - 1), (16383, 16383), (1, 1), (40, 64)]
+
+
+@pytest.mark.parametrize("M,K", NV_ANY_SHAPES)
+def test_nvfp4_any_shape_offsets(M, K):
+    for bases in ((0, 0), (13, 37)):
+        ck = Checker()
+        L = any_walk_len([M], K)
+        tiles_m, tiles_k = -(-M // ANY_M), -(-K // ANY_K)
+        walks = -(-tiles_m // L)
+        for walk in edge(walks):
+            n = min(L, tiles_m - walk * L)
+            for tk in edge(tiles_k):
+                for site, d, off, nbytes, live, addr in nv_any_sites(M, K, walk, tk,
+                                                                     sorted({0, min(1, n - 1), n - 1}),
+                                                                     *bases):
+                    ck.access(site, d, off, nbytes, live, addr)
+                    base = bases[0] if "q_row" in site else bases[1] if "q_col" in site else 0
+                    a = np.broadcast_to(np.asarray(addr, dtype=np.int64), np.shape(live))[live]
+                    if nbytes > 1 and "nv x" not in site and ((base + a) % nbytes != 0).any():
+                        ck.bad.append((site, f"{nbytes}-byte store not {nbytes}-byte aligned"))
+        ck.ok()
+
+
+@pytest.mark.parametrize("bases", [(0, 0), (5, 22), (16, 48)], ids=["b0", "b5-22", "b16-48"])
+@pytest.mark.parametrize("M,K", [(1, 1), (17, 9), (33, 40), (95, 130), (200, 300), (64, 520),
+                                 (129, 257), (300, 12), (12, 300), (600, 64), (1100, 20)])
+@pytest.mark.parametrize("walk", [None, 2, 3, 8], ids=["planned", "L2", "L3", "L8"])
+def test_nvfp4_any_shape_writes_every_byte_once(M, K, bases, walk):
+    L = walk or any_walk_len([M], K)
+    tiles_m, tiles_k = -(-M // ANY_M), -(-K // ANY_K)
+    walks = -(-tiles_m // L)
+    size = {"q_row": M * -(-K // 2), "s_row": M * -(-K // 16),
+            "q_col": K * -(-M // 2), "s_col": K * -(-M // 16)}
+    count = {name: np.zeros(n, np.int64) for name, n in size.items()}
+    for w in range(walks):
+        for tk in range(tiles_k):
+            for site, d, off, nbytes, live, addr in nv_any_sites(M, K, w, tk, range(L), *bases, L=L):
+                name = next((nm for nm in count if site.startswith("nv " + nm)), None)
                 if name is None:
                     continue
                 a = np.broadcast_to(addr, live.shape)[live]

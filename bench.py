@@ -49,10 +49,14 @@ def mx_bytes(M, K, directions, extra_inputs=0):
 
 
 def nvfp4_bytes(M, K, directions):
-    """2 B per bf16 input, 1/2 B per E2M1 element and 1 B per 16-element E4M3
-    scale for each direction (the absmax pre-pass is timed separately)."""
-    n = M * K
-    return 2 * n + directions * (n // 2 + n // 16)
+    """2 B per bf16 input, 1/2 B per E2M1 element (a line of n codes in
+    ceil(n/2) bytes) and 1 B per E4M3 scale (one per block of up to 16
+    elements of a line) for each direction (directions 2: row-wise and
+    transposed, 1: transposed only; the absmax pre-pass is timed
+    separately)."""
+    row = M * (-(-K // 2) + -(-K // 16))
+    col = K * (-(-M // 2) + -(-M // 16))
+    return 2 * M * K + (row + col if directions == 2 else col)
 
 
 CONFIGS = {
@@ -75,8 +79,9 @@ CONFIGS = {
     "mxfp8_grouped_8x_16384x7168": ("f4_grouped_moe", (16384, 7168), "mx_grouped", 3),
     "nvfp4_grouped_8x_16384x7168": ("f4_grouped_moe", (16384, 7168), "nvfp4_grouped", 3),
     "mxfp8_grouped_swiglu_8x_16384x4096": ("f4_grouped_moe", (16384, 4096), "mx_grouped_swiglu", 3),
-    # the any-shape kernel: rows and row lengths that are not multiples of 16 and 8
+    # the any-shape kernels: rows and row lengths that are not multiples of 16 and 8
     "mxfp8_dim0_dim1_16383": ("c2_dim1_16384", (16383, 16383), "mx", 3),
+    "nvfp4_16383": ("c5_nvfp4_16384", (16383, 16383), "nvfp4", 3),
 }
 
 # Row counts of the 8 experts in the grouped workloads.

@@ -420,7 +420,7 @@ const char *mx_status_str(int s)
     case MX_OK: return "MX_OK";
     case MX_ERR_NULL: return "MX_ERR_NULL: a required pointer is NULL";
     case MX_ERR_ENUM: return "MX_ERR_ENUM: unknown axis mask, fusion or activation";
-    case MX_ERR_SHAPE: return "MX_ERR_SHAPE: size not positive, too large, or (NVFP4) not a multiple of 16";
+    case MX_ERR_SHAPE: return "MX_ERR_SHAPE: size not positive or too large";
     case MX_ERR_ALIGN: return "MX_ERR_ALIGN: pointer not 16-byte aligned";
     case MX_ERR_WORKSPACE: return "MX_ERR_WORKSPACE: workspace missing or too small";
     case MX_ERR_ALIAS: return "MX_ERR_ALIAS: an output overlaps an input or another output";

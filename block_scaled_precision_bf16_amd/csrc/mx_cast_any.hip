@@ -15,12 +15,12 @@
 // column block: its amax, scale byte and 32 codes need no exchange.  The
 // bf16 values also go to LDS, where thread t takes the 32-column row block
 // (t % 4) of row t / 4 for the row-wise output.  Codes of both directions
-// leave through LDS staging in the widest pieces every row's alignment
-// allows (16, 4 or 1 bytes); row scales leave per step, column scales at the
-// end of the walk.  Each scale byte of the GEMM-ready tile layout, padding
-// included, is written by exactly one workgroup.  Loads and stores go
-// through buffer resources (bufio.h); lanes outside the tensor get the
-// out-of-range offset.
+// leave through LDS staging (any_common.h: the aligned dwords of each row,
+// the aligned 64-byte chunks of each transposed row); row scales leave per
+// step, column scales at the end of the walk.  Each scale byte of the
+// GEMM-ready tile layout, padding included, is written by exactly one
+// workgroup.  Loads and stores go through buffer resources (bufio.h); lanes
+// outside the tensor get the out-of-range offset.
 
 #include "any_common.h"
 

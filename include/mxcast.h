@@ -49,8 +49,8 @@
  *   - bf16 tensors are raw 16-bit patterns; E4M3, E8M0 and packed E2M1 are
  *     raw bytes.  Every tensor is row-major and contiguous.
  *   - Column-wise outputs are transposed: for x[M][K], q_col is [K][M] and
- *     s_col is [K][ceil(M/32)] (MXFP8, compact scales) or q_col [K][M/2],
- *     s_col [K][M/16] (NVFP4).
+ *     s_col is [K][ceil(M/32)] (MXFP8, compact scales) or q_col
+ *     [K][ceil(M/2)], s_col [K][ceil(M/16)] (NVFP4).
  *   - Every pointer must be 16-byte aligned (dbias: 4-byte).
  *   - Arguments are validated on the host before anything is enqueued; on a
  *     validation error nothing is written and a non-zero status returns.
@@ -77,8 +77,7 @@ typedef enum mx_status {
     MX_OK = 0,
     MX_ERR_NULL = 1,        /* a required pointer is NULL                     */
     MX_ERR_ENUM = 2,        /* unknown axis mask, fusion or activation        */
-    MX_ERR_SHAPE = 3,       /* non-positive or too large size, or (NVFP4) a   */
-                            /* size that is not a multiple of 16              */
+    MX_ERR_SHAPE = 3,       /* non-positive or too large size                 */
     MX_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned               */
     MX_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required     */
     MX_ERR_ALIAS = 6,       /* an output overlaps an input or another output  */
@@ -341,8 +340,12 @@ mx_status mx_fused_values(const void *x, const void *grad, int64_t M, int64_t K,
 mx_status mx_absmax_bf16(const void *x, int64_t n, float *amax, hipStream_t stream);
 
 /*
- * NVFP4 quantize-transpose of x[M][K] (bf16), block size 16, M and K positive
- * multiples of 16, each <= 2^23, M*K <= 2^40.
+ * NVFP4 quantize-transpose of x[M][K] (bf16), block size 16, any M, K >= 1,
+ * each <= 2^23, M*K <= 2^40.  When 16 does not divide K (M), the last block
+ * of each row (column) is partial: its scale and codes come from its own
+ * elements, and a line of n codes packs into ceil(n/2) bytes, the high nibble
+ * of an odd line's last byte 0.  M and K multiples of 16 take the tiled
+ * kernel, other shapes a kernel for arbitrary row alignment (same results).
  *   amax     device, one fp32: the tensor absmax the global scale is built
  *            from, as mx_absmax_bf16 computes it (on the same stream).  With
  *            a NaN or infinite amax (a tensor holding a NaN or an Inf) there
@@ -350,10 +353,10 @@ mx_status mx_absmax_bf16(const void *x, int64_t n, float *amax, hipStream_t stre
  *            NaN), every element code 0, and S_g = amax / 2688 stays NaN or
  *            Inf.  An amax other than the tensor's absmax is outside the
  *            contract.
- *   q_row, s_row  packed E2M1 [M][K/2] (element 2j in the low nibble of byte
- *            j), E4M3 [M][K/16]                     (iff MX_ROWWISE)
- *   q_col, s_col  the same for the transpose: [K][M/2], [K][M/16]
- *                                                   (iff MX_COLWISE)
+ *   q_row, s_row  packed E2M1 [M][ceil(K/2)] (element 2j in the low nibble
+ *            of byte j), E4M3 [M][ceil(K/16)]        (iff MX_ROWWISE)
+ *   q_col, s_col  the same for the transpose: [K][ceil(M/2)],
+ *            [K][ceil(M/16)]                        (iff MX_COLWISE)
  *   global_scale_out  device, one fp32 receiving S_g; may be NULL
  */
 mx_status nvfp4_quantize_transpose(const void *x, int64_t M, int64_t K, const float *amax,
@@ -363,12 +366,13 @@ mx_status nvfp4_quantize_transpose(const void *x, int64_t M, int64_t K, const fl
 
 /*
  * NVFP4 quantize-transpose with 2D scaling (the "nvfp42d" rows of the
- * quantize-transpose table): one E4M3 scale per 16 x 16 block of x, from the
- * block's amax over its 256 elements by the same chain as above; every
- * element is coded with its block's multiplier.  Arguments, layouts and
- * errors exactly as for nvfp4_quantize_transpose: the block's scale is
- * written for each of its 16 rows in s_row and for each of its 16 columns in
- * s_col, so a consumer of the 1D layouts reads 2D-scaled data unchanged.
+ * quantize-transpose table): one E4M3 scale per 16 x 16 block of x (partial
+ * at the right and bottom edges), from the block's amax over its elements by
+ * the same chain as above; every element is coded with its block's
+ * multiplier.  Arguments, layouts and errors exactly as for
+ * nvfp4_quantize_transpose: the block's scale is written for each of its
+ * rows in s_row and for each of its columns in s_col, so a consumer of the
+ * 1D layouts reads 2D-scaled data unchanged.
  */
 mx_status nvfp4_quantize_transpose_2d(const void *x, int64_t M, int64_t K, const float *amax,
                                       unsigned axis_mask,
@@ -393,13 +397,16 @@ mx_status mx_absmax_bf16_grouped(const void *x, int64_t K, const int64_t *group_
  * with its own tensor amax and global scale.
  *   x            device, bf16 [M][K], M = sum of group_rows; group g owns rows
  *                r_g .. r_g + group_rows[g] - 1
- *   group_rows   HOST array of G row counts, each >= 0 and a multiple of 16;
- *                1 <= G <= 64, M > 0; K a positive multiple of 16
+ *   group_rows   HOST array of G row counts, each >= 0; 1 <= G <= 64,
+ *                0 < M <= 2^23; any K >= 1.  Every count and K multiples of
+ *                16 take the tiled kernel, any other stack the any-shape
+ *                kernel (same results)
  *   amax         device, fp32 [G]: each group's tensor amax (for example from
  *                mx_absmax_bf16_grouped)
- *   q_row, s_row [M][K/2], [M][K/16]: the groups' rows (the stacked layout)
- *   q_col, s_col group g's [K][rows/2] and [K][rows/16] at bytes K * r_g / 2
- *                and K * r_g / 16 (the groups one after the other)
+ *   q_row, s_row [M][ceil(K/2)], [M][ceil(K/16)]: the groups' rows (the
+ *                stacked layout)
+ *   q_col, s_col group g's [K][ceil(rows/2)] and [K][ceil(rows/16)], the
+ *                groups one after the other
  *   global_scale_out  device fp32 [G] or NULL: each group's global scale
  *                (1 for an empty group)
  * Errors as for nvfp4_quantize_transpose; MX_ERR_ENUM also for scaling_2d not

@@ -1,12 +1,14 @@
-"""GPU parity of the MXFP8 casts at shapes the tiled kernel does not take --
-row counts that are not multiples of 16 and row lengths that are not
-multiples of 8, down to a single element -- which go to the any-shape kernel.
-Compared with the oracle byte for byte (both directions, compact and tiled
-scales, every format variant), for the plain cast, the pre-ops with dbias,
-the gated casts and their backward, the grouped casts, the fused values and
-the allocation-free cast.  Outputs are preallocated and filled with a canary
-between guard bands, so a byte the kernel fails to write (tile-layout padding
-included) or writes past its tensor is seen."""
+"""GPU parity of the casts at shapes the tiled kernels do not take -- row
+counts that are not multiples of 16 and row lengths that are not multiples of
+8 (MXFP8) or 16 (NVFP4), down to a single element -- which go to the
+any-shape kernels.  Compared with the oracle byte for byte (both directions;
+MXFP8 with compact and tiled scales and every format variant, for the plain
+cast, the pre-ops with dbias, the gated casts and their backward, the
+grouped casts, the fused values and the allocation-free cast; NVFP4 1D and
+2D, single and grouped, with non-finite and tiny-scale tensors).  Outputs are
+preallocated and filled with a canary between guard bands, so a byte the
+kernel fails to write (tile-layout padding included) or writes past its
+tensor is seen."""
 import os
 
 import numpy as np

@@ -2,8 +2,9 @@
 oracle byte for byte (dbias within its tolerance): shapes with partial edges,
 output selection, element format, scale rule and layout, pre-op and dbias for
 the MXFP8 cast; the gated casts and their backward; NVFP4 1D and 2D; grouped
-casts with random expert sizes.  The cases are drawn from fixed seeds, so the
-set is the same on every run; each case's parameters are in its test id."""
+casts with random expert sizes; and the same at any shape (sizes from 1 up,
+not multiples of 16 or 8).  The cases are drawn from fixed seeds, so the set
+is the same on every run; each case's parameters are in its test id."""
 import os
 
 import numpy as np
@@ -152,3 +153,62 @@ def test_grouped_fuzz(i, rows, K, axis, flags, nv):
         torch.cuda.synchronize()
         o = O.mx_quantize_grouped(x, rows, axis=axis | flags)
     mx_outputs_equal(g, o, f"grouped case {i}")
+
+
+# --- any shape: sizes that need not be multiples of 16 or 8 ---------------------
+
+def any_cases(n=80, seed=20261206):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        M, K = int(rng.integers(1, 600)), int(rng.integers(1, 1200))
+        axis = int(rng.integers(1, 4))
+        flags = FORMATS[int(rng.integers(0, 4))] | (mx.SCALE_TILED if rng.random() < 0.3 else 0)
+        fusion = FUSIONS[int(rng.integers(0, 4))] | (mx.FUSE_DBIAS if rng.random() < 0.4 else 0)
+        out.append(pytest.param(i, M, K, axis, flags, fusion,
+                                id=f"any{i}-{M}x{K}-a{axis}-f{flags}-u{fusion}"))
+    return out
+
+
+@pytest.mark.parametrize("i,M,K,axis,flags,fusion", any_cases())
+def test_any_shape_fuzz(i, M, K, axis, flags, fusion):
+    test_mx_quantize_fuzz(1000 + i, M, K, axis, flags, fusion)
+
+
+def any_nvfp4_cases(n=40, seed=20261207):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        M, K = int(rng.integers(1, 600)), int(rng.integers(1, 1200))
+        axis = int(rng.integers(1, 4))
+        two_d = bool(rng.random() < 0.5)
+        out.append(pytest.param(i, M, K, axis, two_d,
+                                id=f"any{i}-{M}x{K}-a{axis}-{'2d' if two_d else '1d'}"))
+    return out
+
+
+@pytest.mark.parametrize("i,M,K,axis,two_d", any_nvfp4_cases())
+def test_any_shape_nvfp4_fuzz(i, M, K, axis, two_d):
+    test_nvfp4_fuzz(1000 + i, M, K, axis, two_d)
+
+
+def any_grouped_cases(n=20, seed=20261208):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        G = int(rng.integers(1, 9))
+        rows = [int(v) for v in rng.integers(0, 400, G)]
+        if sum(rows) == 0:
+            rows[0] = 1
+        K = int(rng.integers(1, 1100))
+        axis = int(rng.integers(1, 4))
+        flags = FORMATS[int(rng.integers(0, 4))] | (mx.SCALE_TILED if rng.random() < 0.3 else 0)
+        nv = i % 2 == 0
+        out.append(pytest.param(i, rows, K, axis, flags, nv,
+                                id=f"any{i}-{'nvfp4' if nv else 'mxfp8'}-G{G}-K{K}-a{axis}-f{flags}"))
+    return out
+
+
+@pytest.mark.parametrize("i,rows,K,axis,flags,nv", any_grouped_cases())
+def test_any_shape_grouped_fuzz(i, rows, K, axis, flags, nv):
+    test_grouped_fuzz(1000 + i, rows, K, axis, flags, nv)

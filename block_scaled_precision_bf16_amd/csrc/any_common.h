@@ -3,7 +3,7 @@
 //
 // Both kernels walk a 128-column strip in steps of 64 rows.  Each thread
 // loads one column of 32 rows with 2-byte loads through one scalar
-// descriptor per row; the codes of a step leave through LDS:
+// descriptor per 32 rows; the codes of a step leave through LDS:
 //   * row-wise, each row's segment of the step (128 or 64 bytes) as the
 //     aligned dwords inside it plus at most 3 head and 3 tail bytes, or as
 //     16-byte pieces when every row starts 16-byte aligned (flush_rows);
@@ -42,14 +42,44 @@ __device__ __forceinline__ uint32_t lds_word_at(const uint8_t *row, int i)
     return __builtin_amdgcn_alignbyte(w[1], w[0], (uint32_t)(i & 3));
 }
 
-// Descriptor of row `row` (of `rows`, `ld` elements apart) of a bf16 tensor,
-// from column `col` to the tensor's end; size 0 for a row at or past the
-// last.  The row is the same for every lane of a wave, so the descriptor is
-// scalar and each lane needs a single offset register (its column).
+// Descriptor of a bf16 tensor p[rows][ld] from row `row`, column `col` to
+// the tensor's end (size 0 for a row at or past the last).
 __device__ __forceinline__ rsrc_t row_rsrc(const uint16_t *p, int64_t row, int64_t ld, int64_t rows,
                                            int64_t col = 0)
 {
     return make_rsrc(p, 2 * (row * ld + col), 2 * rows * ld);
+}
+
+// Rows m .. m + 31 of a bf16 tensor p[rows][ld] seen from column col: one
+// scalar descriptor from row m, column col to the tensor's end, row i at byte
+// i * pitch of it.  A lane adds its column's offset.  Row i past the last
+// starts at or past the descriptor's end, so only columns need a mask: with
+// ld <= 2^23, every offset of rows 0 .. 31 is below 2^30 and kDead plus any
+// of them stays below 2^32.  (Where 2 (rows - m) ld exceeds the largest
+// descriptor, all 32 rows exist.)
+struct Rows32 {
+    rsrc_t r;
+    uint32_t pitch;
+};
+
+__device__ __forceinline__ Rows32 rows32(const uint16_t *p, int64_t m, int64_t ld, int64_t rows,
+                                         int64_t col = 0)
+{
+    return Rows32{row_rsrc(p, m, ld, rows, col), (uint32_t)(2 * ld)};
+}
+
+__device__ __forceinline__ uint32_t load_row(const Rows32 &v, int i, uint32_t off)
+{
+    return buf_load2(v.r, off + (uint32_t)i * v.pitch);
+}
+
+// A lane's column offset, opaque to the compiler for one step: its 32 row
+// offsets are then formed at each step (one add per load) instead of being
+// held in registers across the whole walk.
+__device__ __forceinline__ uint32_t step_offset(uint32_t off)
+{
+    asm volatile("" : "+v"(off));
+    return off;
 }
 
 // Raw bf16 of column k, rows m .. m + 31 of x[rows][ld] (0 past the last row
@@ -57,11 +87,12 @@ __device__ __forceinline__ rsrc_t row_rsrc(const uint16_t *p, int64_t row, int64
 __device__ __forceinline__ void load_column32(const uint16_t *x, int64_t ld, int64_t rows,
                                               int64_t m, int64_t k, bool col_ok, uint32_t (&w)[16])
 {
-    const uint32_t ox = col_ok ? (uint32_t)(2 * k) : kDead;
+    const Rows32 v = rows32(x, m, ld, rows);
+    const uint32_t ox = step_offset(col_ok ? (uint32_t)(2 * k) : kDead);
     uint32_t e[32];
 #pragma unroll
     for (int i = 0; i < 32; i++)
-        e[i] = buf_load2(row_rsrc(x, m + i, ld, rows), ox);
+        e[i] = load_row(v, i, ox);
 #pragma unroll
     for (int i = 0; i < 16; i++)
         w[i] = pack2(e[2 * i], e[2 * i + 1]);

@@ -73,8 +73,10 @@ __device__ __forceinline__ void any_load(const MxArgs &a, const AnyView &v, int6
         const int64_t N = a.lin_off;
         const bool gate_half = k < N;
         const uint32_t n2 = (uint32_t)(2 * (gate_half ? k : k - N));
-        const uint32_t ox = col_ok ? n2 : kDead;
-        const uint32_t ol = col_ok && gate_half ? n2 : kDead;
+        const uint32_t ox = step_offset(col_ok ? n2 : kDead);
+        const uint32_t ol = step_offset(col_ok && gate_half ? n2 : kDead);
+        const Rows32 vg = rows32(v.x, m, a.ldx, v.M), vd = rows32(v.aux, m, a.ldg, v.M);
+        const Rows32 vl = rows32(v.x, m, a.ldx, v.M, N);
         // two batches of 16 rows: three operands of 32 rows in flight at
         // once would not fit the register budget of four waves per SIMD
 #pragma unroll
@@ -82,9 +84,9 @@ __device__ __forceinline__ void any_load(const MxArgs &a, const AnyView &v, int6
             uint32_t g[16], dy[16], li[16];
 #pragma unroll
             for (int i = 0; i < 16; i++) {
-                g[i] = buf_load2(row_rsrc(v.x, m + r0 + i, a.ldx, v.M), ox);
-                dy[i] = buf_load2(row_rsrc(v.aux, m + r0 + i, a.ldg, v.M), ox);
-                li[i] = buf_load2(row_rsrc(v.x, m + r0 + i, a.ldx, v.M, N), ol);
+                g[i] = load_row(vg, r0 + i, ox);
+                dy[i] = load_row(vd, r0 + i, ox);
+                li[i] = load_row(vl, r0 + i, ol);
             }
 #pragma unroll
             for (int i = 0; i < 8; i++)
@@ -95,11 +97,12 @@ __device__ __forceinline__ void any_load(const MxArgs &a, const AnyView &v, int6
         }
         return;
     }
-    const uint32_t ox = col_ok ? (uint32_t)(2 * k) : kDead;
+    const uint32_t ox = step_offset(col_ok ? (uint32_t)(2 * k) : kDead);
+    const Rows32 vx = rows32(v.x, m, a.ldx, v.M);
     uint32_t e[32];
 #pragma unroll
     for (int i = 0; i < 32; i++)
-        e[i] = buf_load2(row_rsrc(v.x, m + i, a.ldx, v.M), ox);
+        e[i] = load_row(vx, i, ox);
     if constexpr (OP == OP_PLAIN) {
 #pragma unroll
         for (int i = 0; i < 16; i++)
@@ -113,12 +116,11 @@ __device__ __forceinline__ void any_load(const MxArgs &a, const AnyView &v, int6
     } else {
         // second operand: the linear half (gated) or grad (dGELU, dSiLU)
         constexpr bool gated = OP == OP_SWIGLU || OP == OP_GEGLU;
+        const Rows32 vb = gated ? rows32(v.x, m, a.ldx, v.M, a.lin_off) : rows32(v.aux, m, a.ldg, v.M);
         uint32_t b[32];
 #pragma unroll
         for (int i = 0; i < 32; i++)
-            b[i] = buf_load2(gated ? row_rsrc(v.x, m + i, a.ldx, v.M, a.lin_off)
-                                   : row_rsrc(v.aux, m + i, a.ldg, v.M),
-                             ox);
+            b[i] = load_row(vb, i, ox);
 #pragma unroll
         for (int i = 0; i < 16; i++)
             w[i] = fused_pair<OP>(pack2(e[2 * i], e[2 * i + 1]), pack2(b[2 * i], b[2 * i + 1]));

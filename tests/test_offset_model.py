@@ -525,12 +525,15 @@ def any_sites(M, K, op, tiled, walk, tk, steps, qrow_base=0, qcol_base=0, L=None
         if s >= n:
             continue
         m0 = (t0 + s) * ANY_M
-        # loads: thread (c, h) reads rows m0 + 32 h + i of column k
+        # loads: thread (c, h) reads rows m0 + 32 h + i of column k through
+        # one descriptor per operand from row m0 + 32 h (at the operand's
+        # first column) to the tensor's end, row i at byte i * 2 ld of it
         for h in (0, 1):
             # the threads of half h (128 of them: columns c = 0..127)
             kh, okh = k[t >> 7 == h], col_ok[t >> 7 == h]
-            for i in (0, 15, 16, 31):
-                row = m0 + 32 * h + i
+            mh = m0 + 32 * h
+            for i in (0, 1, 15, 16, 30, 31):
+                row = mh + i
                 if op == "dgated":
                     N = lin_off
                     gate = kh < N
@@ -538,23 +541,23 @@ def any_sites(M, K, op, tiled, walk, tk, steps, qrow_base=0, qcol_base=0, L=None
                     ox = np.where(okh, 2 * nn, DEAD)
                     ol = np.where(okh & gate, 2 * nn, DEAD)
                     live = okh & (row < M)
-                    out.append(("any gate", Desc(2 * row * ldx, 2 * M * ldx), ox, 2, live,
-                                2 * (row * ldx + nn)))
-                    out.append(("any grad", Desc(2 * row * ldg, 2 * M * ldg), ox, 2, live,
-                                2 * (row * ldg + nn)))
-                    out.append(("any linear", Desc(2 * (row * ldx + N), 2 * M * ldx), ol, 2,
-                                live & gate, 2 * (row * ldx + N + nn)))
+                    out.append(("any gate", Desc(2 * mh * ldx, 2 * M * ldx), ox + i * 2 * ldx, 2,
+                                live, 2 * (row * ldx + nn)))
+                    out.append(("any grad", Desc(2 * mh * ldg, 2 * M * ldg), ox + i * 2 * ldg, 2,
+                                live, 2 * (row * ldg + nn)))
+                    out.append(("any linear", Desc(2 * (mh * ldx + N), 2 * M * ldx),
+                                ol + i * 2 * ldx, 2, live & gate, 2 * (row * ldx + N + nn)))
                     continue
                 ox = np.where(okh, 2 * kh, DEAD)
                 live = okh & (row < M)
-                out.append(("any x", Desc(2 * row * ldx, 2 * M * ldx), ox, 2, live,
+                out.append(("any x", Desc(2 * mh * ldx, 2 * M * ldx), ox + i * 2 * ldx, 2, live,
                             2 * (row * ldx + kh)))
                 if op == "gated":
-                    out.append(("any linear", Desc(2 * (row * ldx + lin_off), 2 * M * ldx), ox, 2,
-                                live, 2 * (row * ldx + lin_off + kh)))
+                    out.append(("any linear", Desc(2 * (mh * ldx + lin_off), 2 * M * ldx),
+                                ox + i * 2 * ldx, 2, live, 2 * (row * ldx + lin_off + kh)))
                 elif op == "grad":
-                    out.append(("any grad", Desc(2 * row * ldg, 2 * M * ldg), ox, 2, live,
-                                2 * (row * ldg + kh)))
+                    out.append(("any grad", Desc(2 * mh * ldg, 2 * M * ldg), ox + i * 2 * ldg, 2,
+                                live, 2 * (row * ldg + kh)))
         # row scales: thread (r = t / 4, q = t % 4), block b = 4 tk + q
         r, q = t >> 2, t & 3
         blocks = [4 * tk + q]
@@ -703,11 +706,12 @@ def nv_any_sites(M, K, walk, tk, steps, qrow_base=0, qcol_base=0, L=None):
         mrem = min(M - m0, ANY_M)
         for h in (0, 1):
             kh = k[t >> 7 == h]
-            for i in (0, 31):
-                row = m0 + 32 * h + i
+            mh = m0 + 32 * h
+            for i in (0, 1, 30, 31):
+                row = mh + i
                 ok = (kh < K) & (row < M)
-                out.append(("nv x", Desc(2 * row * K, 2 * M * K), np.where(kh < K, 2 * kh, DEAD), 2,
-                            ok, 2 * (row * K + kh)))
+                out.append(("nv x", Desc(2 * mh * K, 2 * M * K),
+                            np.where(kh < K, 2 * kh, DEAD) + i * 2 * K, 2, ok, 2 * (row * K + kh)))
         r, qq = t >> 2, t & 3
         for bq in (0, 1):
             b = 8 * tk + 2 * qq + bq

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmxcast.so")
 SOURCES = ["api.cpp", "mx_cast.hip", "mx_cast_any.hip", "nvfp4.hip", "nvfp4_any.hip",
-           *[f"mx_cast_{kind}_{fmt}.hip" for kind in ("fmt", "grp")
+           *[f"mx_cast_{kind}_{fmt}.hip" for kind in ("fmt", "grp", "rag")
              for fmt in ("e4m3", "e5m2", "e4m3_up", "e5m2_up")]]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -60,37 +60,44 @@ int cast_op(int pre)
 // layout a walk covers at least two sub-tiles, so that it starts on a
 // column-scale tile boundary (8 blocks = 256 rows) and no two workgroups
 // write one scale tile.
-int walk_group(int tm, int tk, int op, bool dbias, bool tiled)
+// rag: the transposed rows start at any byte (the transposed output of a
+// tensor whose M is not a multiple of 16), which caps walks at kMaxRagGroup.
+int walk_group(int tm, int tk, int op, bool dbias, bool tiled, bool rag)
 {
+    const int max_len = rag ? mxk::kMaxRagGroup : mxk::kMaxGroup;
     if (op == mxk::OP_PLAIN && !dbias) {
         // the plain cast: balanced walks on two resident workgroups per CU
         int len;
-        mxk::plan_walks(&tm, 1, tk, mxk::kTargetWorkgroups, tiled, &len);
+        mxk::plan_walks(&tm, 1, tk, mxk::kTargetWorkgroups, tiled, &len, max_len);
         return len;
     }
-    const int g = mxk::pick_group(tm, tk, mxk::target_workgroups(op, dbias));
+    const int g = mxk::pick_group(tm, tk, mxk::target_workgroups(op, dbias), max_len);
     return tiled && g < 2 ? 2 : g;
 }
 
+// Whether the tiled kernel's cast of an M x K tensor with these outputs
+// writes transposed rows that start at any byte.
+bool rag_rows(int64_t M, unsigned axis_mask) { return (axis_mask & MX_COLWISE) && M % 16 != 0; }
+
 // Walks along M of the cast kernel `op` (with or without dbias) for an
 // M x K tensor.
-int walks_m(int64_t M, int64_t K, int op, bool dbias, bool tiled)
+int walks_m(int64_t M, int64_t K, int op, bool dbias, bool tiled, bool rag)
 {
     const int tm = tiles(M, mxk::kTileM), tk = tiles(K, mxk::kTileK);
-    const int g = walk_group(tm, tk, op, dbias, tiled);
+    const int g = walk_group(tm, tk, op, dbias, tiled, rag);
     return (tm + g - 1) / g;
 }
 
-size_t dbias_workspace(int64_t M, int64_t K, int op, bool tiled)
+size_t dbias_workspace(int64_t M, int64_t K, int op, bool tiled, bool rag)
 {
-    return (size_t)walks_m(M, K, op, true, tiled) * (size_t)K * sizeof(float);
+    return (size_t)walks_m(M, K, op, true, tiled, rag) * (size_t)K * sizeof(float);
 }
 
-void set_walk(mxk::MxArgs &a, int op, bool dbias)
+void set_walk(mxk::MxArgs &a, int op, bool dbias, bool rag)
 {
     a.tiles_k = tiles(a.K, mxk::kTileK);
     a.tiles_m = tiles(a.M, mxk::kTileM);
-    a.group = walk_group(a.tiles_m, a.tiles_k, op, dbias, a.tiled != 0);
+    a.group = walk_group(a.tiles_m, a.tiles_k, op, dbias, a.tiled != 0, rag);
     a.groups_m = (a.tiles_m + a.group - 1) / a.group;
 }
 
@@ -112,11 +119,12 @@ bool mx_size_ok(int64_t M, int64_t K)
     return M > 0 && K > 0 && M <= kMaxDim && K <= kMaxDim && M * K <= kMaxElems;
 }
 
-// Shapes the tiled cast kernel takes: every row of every input and output
-// starts on a 16-byte boundary (K a multiple of 8 for the bf16 input and the
-// 8-byte row stores, M a multiple of 16 for the 16-byte stores of the
-// transposed output).  Every other shape goes to the any-shape kernel.
-bool tiled_shape(int64_t M, int64_t K) { return M % 16 == 0 && K % 8 == 0; }
+// Row lengths the tiled cast kernel takes: every row of the bf16 input starts
+// on a 16-byte boundary and every row of q_row on an 8-byte one (K a multiple
+// of 8), for any M.  With the transposed output and M not a multiple of 16,
+// the rows of q_col start at any byte: the grouped kernel's variant for that
+// writes them.  Other row lengths go to the any-shape kernel.
+bool tiled_width(int64_t K) { return K % 8 == 0; }
 
 // Group table of the any-shape kernel for one M x K tensor.
 mxk::GroupTable any_table(int64_t M, int64_t K)
@@ -133,11 +141,11 @@ mxk::GroupTable any_table(int64_t M, int64_t K)
 }
 
 // Bytes of dbias partials for one M x K tensor (either kernel).
-size_t quantize_workspace(int64_t M, int64_t K, int op, bool tiled)
+size_t quantize_workspace(int64_t M, int64_t K, int op, bool tiled, unsigned axis_mask)
 {
-    if (!tiled_shape(M, K))
+    if (!tiled_width(K))
         return (size_t)any_table(M, K).walk0[1] * (size_t)K * sizeof(float);
-    return dbias_workspace(M, K, op, tiled);
+    return dbias_workspace(M, K, op, tiled, rag_rows(M, axis_mask));
 }
 
 mx_status from_hip(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
@@ -145,11 +153,14 @@ mx_status from_hip(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; 
 // Group table of a grouped cast: walks per group (the walk length chosen for
 // the whole stack, at least two sub-tiles with tiled scales), rows, and each
 // group's scale offsets.  False if a group size is invalid.  any is set when
-// the stack goes to the any-shape kernel: some group's rows are not a
-// multiple of 16, or the row length is not aligned for the tiled kernel
-// (width_aligned false); the walks are then that kernel's.
+// the stack goes to the any-shape kernel: the row length is not aligned for
+// the tiled kernel (width_aligned false); the walks are then that kernel's.
+// rag is set when the transposed output (col) is written and some group's
+// rows are not a multiple of 16, so that the groups' transposed rows may
+// start at any byte; walks are then at most kMaxRagGroup sub-tiles.
 bool build_groups(const int64_t *rows, int G, int64_t K, int op, bool dbias, bool tiled,
-                  bool width_aligned, mxk::GroupTable &gt, int64_t &M, int &group, bool &any)
+                  bool width_aligned, bool col, mxk::GroupTable &gt, int64_t &M, int &group,
+                  bool &any, bool &rag)
 {
     if (!rows || G < 1 || G > mxk::kMaxGroups)
         return false;
@@ -163,7 +174,9 @@ bool build_groups(const int64_t *rows, int G, int64_t K, int op, bool dbias, boo
     }
     if (M <= 0 || M > kMaxDim || !mx_size_ok(M, K))
         return false;
-    any = !(rows16 && width_aligned);
+    any = !width_aligned;
+    rag = !rows16 && col;
+    const int max_len = rag ? mxk::kMaxRagGroup : mxk::kMaxGroup;
     int tm[mxk::kMaxGroups];
     for (int g = 0; g < G; g++)
         tm[g] = tiles(rows[g], any ? mxk::kAnyTileM : mxk::kTileM);
@@ -178,7 +191,7 @@ bool build_groups(const int64_t *rows, int G, int64_t K, int op, bool dbias, boo
         // gated backward: dSwiGLU 200 -> 148 us, dGeGLU 191 -> 138 us)
         group = tiled ? 2 : 1;
     } else {
-        group = mxk::pick_group_rounds(tm, G, tiles(K, mxk::kTileK), 2, tiled ? 2 : 1);
+        group = mxk::pick_group_rounds(tm, G, tiles(K, mxk::kTileK), 2, tiled ? 2 : 1, max_len);
     }
     for (int g = 0; g < G; g++)
         gt.len[g] = group;
@@ -293,6 +306,31 @@ static mx_status launch_any(int op, unsigned axis_mask, bool dbias, mxk::MxArgs 
                                             stream));
 }
 
+// One tensor (a.M x a.K, a.K a multiple of 8, everything but the walk set)
+// through the tiled kernel; sets the walk.  With the transposed output and M
+// not a multiple of 16 it goes to the variant whose transposed rows start at
+// any byte, as a stack of one group.
+static mx_status launch_tiled(int op, unsigned axis_mask, bool dbias, mxk::MxArgs &a,
+                              hipStream_t stream)
+{
+    const bool rag = rag_rows(a.M, axis_mask);
+    set_walk(a, op, dbias, rag);
+    if (!rag)
+        return from_hip(mxk::launch_mx_cast(op, axis_mask & 3u, axis_mask & kFmtBits, dbias, a,
+                                            stream));
+    mxk::GroupTable gt{};
+    gt.count = 1;
+    gt.len[0] = a.group;
+    gt.walk0[0] = 0;
+    gt.walk0[1] = a.groups_m;
+    gt.row0[0] = 0;
+    gt.row0[1] = a.M;
+    gt.srow_off[0] = gt.scol_off[0] = 0;
+    a.qcol_nt = 0;
+    return from_hip(mxk::launch_mx_cast_ragged(op, axis_mask & 3u, axis_mask & kFmtBits, dbias, a,
+                                               gt, stream));
+}
+
 static mx_status nvfp4_impl(bool two_d, const void *x, int64_t M, int64_t K, const float *amax,
                             unsigned axis_mask, uint8_t *q_row, uint8_t *s_row, uint8_t *q_col,
                             uint8_t *s_col, float *global_scale_out, hipStream_t stream)
@@ -367,8 +405,8 @@ static mx_status gated_grouped_impl(const void *grad, const void *x, int64_t N,
     mxk::GroupTable gt;
     int64_t M;
     int group;
-    bool any;
-    if (!build_groups(group_rows, G, W, op, false, tiled, N % 8 == 0, gt, M, group, any) ||
+    bool any, rag;
+    if (!build_groups(group_rows, G, W, op, false, tiled, N % 8 == 0, col, gt, M, group, any, rag) ||
         !mx_size_ok(M, 2 * N))
         return MX_ERR_SHAPE;
     if (!aligned(x, 16) || (bwd && !aligned(grad, 16)) ||
@@ -406,8 +444,8 @@ static mx_status gated_grouped_impl(const void *grad, const void *x, int64_t N,
     if (any)
         return from_hip(mxk::launch_mx_cast_any(op, axis_mask & 3u, axis_mask & kFmtBits, false, a,
                                                 gt, stream));
-    return from_hip(mxk::launch_mx_cast_grouped(op, axis_mask & 3u, axis_mask & kFmtBits, false, a,
-                                                gt, stream));
+    return from_hip((rag ? mxk::launch_mx_cast_ragged : mxk::launch_mx_cast_grouped)(
+        op, axis_mask & 3u, axis_mask & kFmtBits, false, a, gt, stream));
 }
 
 extern "C" {
@@ -435,7 +473,8 @@ size_t mx_quantize_workspace_size(int64_t M, int64_t K, unsigned axis_mask, int 
     if (!(fusion & MX_FUSE_DBIAS) || !mx_size_ok(M, K) || !mx_mode_ok(axis_mask) ||
         (fusion & ~0x1F) || (fusion & 0xF) > MX_FUSE_DSILU)
         return 0;
-    return quantize_workspace(M, K, cast_op(fusion & 0xF), (axis_mask & MX_SCALE_TILED) != 0);
+    return quantize_workspace(M, K, cast_op(fusion & 0xF), (axis_mask & MX_SCALE_TILED) != 0,
+                              axis_mask);
 }
 
 size_t mx_scale_size(int64_t rows, int64_t cols, unsigned axis_mask)
@@ -474,7 +513,7 @@ static mx_status quantize_impl(const void *x, const void *grad, int64_t M, int64
         return MX_ERR_ALIGN;
     const int op = cast_op(pre);
     const bool tiled = (axis_mask & MX_SCALE_TILED) != 0;
-    const size_t need = want_dbias ? quantize_workspace(M, K, op, tiled) : 0;
+    const size_t need = want_dbias ? quantize_workspace(M, K, op, tiled, axis_mask) : 0;
     if (noalloc ? need > mxk::kNoAllocScratchBytes
                 : want_dbias && (!workspace || workspace_bytes < need))
         return MX_ERR_WORKSPACE;
@@ -508,14 +547,8 @@ static mx_status quantize_impl(const void *x, const void *grad, int64_t M, int64
     a.partials = want_dbias ? static_cast<float *>(workspace) : nullptr;
     a.tiled = tiled;
     a.qcol_nt = M * K >= mxk::kQcolNtBytes && M % 128 == 0;
-    mx_status st;
-    if (tiled_shape(M, K)) {
-        set_walk(a, op, want_dbias);
-        st = from_hip(mxk::launch_mx_cast(op, axis_mask & 3u, axis_mask & kFmtBits, want_dbias, a,
-                                          stream));
-    } else {
-        st = launch_any(op, axis_mask, want_dbias, a, stream);
-    }
+    const mx_status st = tiled_width(K) ? launch_tiled(op, axis_mask, want_dbias, a, stream)
+                                        : launch_any(op, axis_mask, want_dbias, a, stream);
     if (st != MX_OK || !want_dbias)
         return st;
     return from_hip(mxk::launch_dbias_reduce(a.partials, a.groups_m, K, dbias, stream));
@@ -546,9 +579,10 @@ size_t mx_quantize_grouped_workspace_size(int64_t K, const int64_t *group_rows, 
     mxk::GroupTable gt;
     int64_t M;
     int group;
-    bool any;
+    bool any, rag;
     if (!build_groups(group_rows, G, K, cast_op(fusion & 0xF), true,
-                      (axis_mask & MX_SCALE_TILED) != 0, K % 8 == 0, gt, M, group, any))
+                      (axis_mask & MX_SCALE_TILED) != 0, K % 8 == 0,
+                      (axis_mask & MX_COLWISE) != 0, gt, M, group, any, rag))
         return 0;
     return (size_t)gt.walk0[G] * (size_t)K * sizeof(float);
 }
@@ -559,10 +593,10 @@ size_t mx_grouped_scale_size(int64_t K, const int64_t *group_rows, int G, unsign
     mxk::GroupTable gt;
     int64_t M;
     int group;
-    bool any;
+    bool any, rag;
     if (!mx_mode_ok(axis_mask) ||
         !build_groups(group_rows, G, K, mxk::OP_PLAIN, false, (axis_mask & MX_SCALE_TILED) != 0,
-                      K % 8 == 0, gt, M, group, any))
+                      K % 8 == 0, (axis_mask & MX_COLWISE) != 0, gt, M, group, any, rag))
         return 0;
     return (size_t)grouped_scale_bytes(group_rows, G, K, colwise != 0,
                                        (axis_mask & MX_SCALE_TILED) != 0);
@@ -587,8 +621,9 @@ mx_status mx_quantize_grouped(const void *x, const void *grad, int64_t K, const 
     mxk::GroupTable gt;
     int64_t M;
     int group;
-    bool any;
-    if (!build_groups(group_rows, G, K, op, want_dbias, tiled, K % 8 == 0, gt, M, group, any))
+    bool any, rag;
+    if (!build_groups(group_rows, G, K, op, want_dbias, tiled, K % 8 == 0, col, gt, M, group, any,
+                      rag))
         return MX_ERR_SHAPE;
     if (!aligned(x, 16) || (has_grad && !aligned(grad, 16)) ||
         (row && (!aligned(q_row, 16) || !aligned(s_row, 16))) ||
@@ -628,11 +663,10 @@ mx_status mx_quantize_grouped(const void *x, const void *grad, int64_t K, const 
     a.tiles_m = tiles(M, mxk::kTileM);
     a.group = group;
     a.groups_m = gt.walk0[G];
+    const auto launch = any ? mxk::launch_mx_cast_any
+                            : rag ? mxk::launch_mx_cast_ragged : mxk::launch_mx_cast_grouped;
     mx_status st = from_hip(
-        any ? mxk::launch_mx_cast_any(op, axis_mask & 3u, axis_mask & kFmtBits, want_dbias, a, gt,
-                                      stream)
-            : mxk::launch_mx_cast_grouped(op, axis_mask & 3u, axis_mask & kFmtBits, want_dbias, a,
-                                          gt, stream));
+        launch(op, axis_mask & 3u, axis_mask & kFmtBits, want_dbias, a, gt, stream));
     if (st != MX_OK || !want_dbias)
         return st;
     return from_hip(mxk::launch_dbias_reduce_grouped(a.partials, gt, K, dbias, stream));
@@ -695,11 +729,8 @@ mx_status mx_quantize_gated(const void *x, int64_t M, int64_t N, unsigned axis_m
     a.tiled = tiled;
     a.qcol_nt = 0;
     const int op = act == MX_GATED_SWIGLU ? mxk::OP_SWIGLU : mxk::OP_GEGLU;
-    if (!tiled_shape(M, N))
-        return launch_any(op, axis_mask, false, a, stream);
-    set_walk(a, op, false);
-    return from_hip(
-        mxk::launch_mx_cast(op, axis_mask & 3u, axis_mask & kFmtBits, false, a, stream));
+    return tiled_width(N) ? launch_tiled(op, axis_mask, false, a, stream)
+                          : launch_any(op, axis_mask, false, a, stream);
 }
 
 mx_status mx_quantize_dgated(const void *grad, const void *x, int64_t M, int64_t N,
@@ -743,11 +774,9 @@ mx_status mx_quantize_dgated(const void *grad, const void *x, int64_t M, int64_t
     a.tiled = tiled;
     a.qcol_nt = 0;
     const int op = act == MX_GATED_SWIGLU ? mxk::OP_DSWIGLU : mxk::OP_DGEGLU;
-    if (!tiled_shape(M, N))   // the tiled kernel needs both halves 8-column aligned
-        return launch_any(op, axis_mask, false, a, stream);
-    set_walk(a, op, false);
-    return from_hip(
-        mxk::launch_mx_cast(op, axis_mask & 3u, axis_mask & kFmtBits, false, a, stream));
+    // the tiled kernel needs both halves 8-column aligned
+    return tiled_width(N) ? launch_tiled(op, axis_mask, false, a, stream)
+                          : launch_any(op, axis_mask, false, a, stream);
 }
 
 mx_status mx_fused_values(const void *x, const void *grad, int64_t M, int64_t K, int op, void *y,

@@ -30,8 +30,12 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTileM = 2 * kRowsPerLane * kWaves;  // 128
 constexpr int kTileK = kColsPerLane * 32;          // 256
-// A cast workgroup walks down up to kMaxGroup sub-tiles of a 256-column strip.
+// A cast workgroup walks down up to kMaxGroup sub-tiles of a 256-column strip;
+// up to kMaxRagGroup when its transposed rows start at any byte (its stage
+// then holds two sub-tiles, and the walk's column scales must still fit two
+// workgroups' LDS into a CU's 160 KB).
 constexpr int kMaxGroup = 16;
+constexpr int kMaxRagGroup = 14;
 // Workgroups the host aims to launch at least: two per MI355X compute unit
 // for the plain cast (bound by memory, two resident per CU) and for the casts
 // with dbias; four for the other fused casts (bound by their arithmetic,
@@ -46,10 +50,12 @@ inline int target_workgroups(int op, bool dbias)
 }
 
 // Sub-tiles per workgroup for a tiles_m x tiles_k grid of sub-tiles: the
-// deepest power of two <= kMaxGroup that still yields `target` workgroups.
-inline int pick_group(int tiles_m, int tiles_k, int target)
+// deepest power of two <= max_len that still yields `target` workgroups.
+inline int pick_group(int tiles_m, int tiles_k, int target, int max_len = kMaxGroup)
 {
-    int g = kMaxGroup;
+    int g = 1;
+    while (2 * g <= max_len)
+        g *= 2;
     while (g > 1 && (int64_t)((tiles_m + g - 1) / g) * tiles_k < target)
         g >>= 1;
     return g;
@@ -65,12 +71,15 @@ inline int pick_group(int tiles_m, int tiles_k, int target)
 // longer walk.  Reproduces pick_group's choice on the one-group workloads it
 // was tuned on.
 inline int pick_group_rounds(const int *tiles_m, int groups, int tiles_k, int slots_per_cu,
-                             int min_group)
+                             int min_group, int max_len = kMaxGroup)
 {
     const int64_t slots = 256 * (int64_t)slots_per_cu;
     int best = 0;
     int64_t best_cost = 0;
-    for (int g = kMaxGroup; g >= min_group; g >>= 1) {
+    int top = 1;
+    while (2 * top <= max_len)
+        top *= 2;
+    for (int g = top; g >= min_group; g >>= 1) {
         int64_t walks = 0;
         for (int i = 0; i < groups; i++)
             walks += (tiles_m[i] + g - 1) / g;
@@ -101,11 +110,11 @@ inline int pick_group_rounds(const int *tiles_m, int groups, int tiles_k, int sl
 // (one group of 128 sub-tile rows, 64 strips, 512 slots) this is 16, the
 // deepest walk that fills every slot once.
 inline void plan_walks(const int *tiles_m, int groups, int tiles_k, int slots, bool even,
-                       int *len)
+                       int *len, int max_len = kMaxGroup)
 {
     int best_L = 0, best_long = 0;
     int64_t best_cost = 0;
-    for (int L = even ? 2 : 1; L <= kMaxGroup; L += even ? 2 : 1) {
+    for (int L = even ? 2 : 1; L <= max_len; L += even ? 2 : 1) {
         int64_t walks = 0;
         int longest = 0;
         for (int g = 0; g < groups; g++) {
@@ -213,6 +222,12 @@ hipError_t launch_mx_cast(int op, unsigned axis, unsigned fmt, bool dbias, const
 // pointers describe the whole stack.
 hipError_t launch_mx_cast_grouped(int op, unsigned axis, unsigned fmt, bool dbias, const MxArgs &a,
                                   const GroupTable &gt, hipStream_t s);
+// launch_mx_cast_grouped for stacks whose transposed rows may start at any
+// byte (a group's rows, or the rows before it, not multiples of 16; K, the
+// row length, a multiple of 8); axis must include the column-wise output.
+// A single tensor is a stack of one group.
+hipError_t launch_mx_cast_ragged(int op, unsigned axis, unsigned fmt, bool dbias, const MxArgs &a,
+                                 const GroupTable &gt, hipStream_t s);
 // The same operations for any shape (mx_cast_any.hip): a.tiles_k =
 // ceil(K / kAnyTileK); gt gives each group's rows, walks (gt.len steps each)
 // and scale offsets (one group for a single tensor); a.partials holds

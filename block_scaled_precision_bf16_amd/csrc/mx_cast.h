@@ -267,19 +267,25 @@ __device__ __forceinline__ void row_pass(const MxArgs &a, const uint32_t (&w)[kR
 // per lane), the 8 threads that read a row back read its 8 chunks, and both
 // patterns then cover all banks.  s: the column-block scales of the whole
 // strip segment the workgroup walks (4 per sub-tile), transposed (block-major,
-// stage_flush.h) and written out once.
-struct ColStage {
-    uint4 q[kTileK][kTileM / 16];            // 32 KB
-    uint8_t s[4 * kMaxGroup][kTileK];        // 16 KB
+// stage_flush.h) and written out once.  RAG (transposed rows at any byte):
+// two q tiles, the current sub-tile's and the previous one's, whose last
+// bytes complete the first line the current one writes; walks of at most
+// kMaxRagGroup sub-tiles keep the stage within two workgroups per CU.
+template <bool RAG>
+struct ColStageT {
+    uint4 q[RAG ? 2 : 1][kTileK][kTileM / 16];                 // 32 KB each
+    uint8_t s[4 * (RAG ? kMaxRagGroup : kMaxGroup)][kTileK];  // 16 KB, 14 KB
 };
+using ColStage = ColStageT<false>;
+using StageTile = uint4[kTileK][kTileM / 16];
 
 __device__ __forceinline__ int stage_chunk(int kl, int j) { return j ^ ((kl >> 3) & 7); }
 
 // Column-wise blocks of sub-tile g: the 32 rows of a column block are this
 // lane's 16 and those of lane l ^ 32; each lane converts its own 16 bytes of
 // each column and puts them into the staging tile.
-template <int FMT>
-__device__ __forceinline__ void col_pass(ColStage &st, const uint32_t (&w)[kRowsPerLane][4],
+template <int FMT, bool RAG>
+__device__ __forceinline__ void col_pass(ColStageT<RAG> &st, const uint32_t (&w)[kRowsPerLane][4],
                                          int wave, int half, int cl, int g, uint32_t (&cmax)[4])
 {
 #pragma unroll
@@ -295,7 +301,7 @@ __device__ __forceinline__ void col_pass(ColStage &st, const uint32_t (&w)[kRows
         if (sb == 0xFFu)
             o = make_uint4(0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu);
         const int kl = cl * kColsPerLane + c;
-        st.q[kl][stage_chunk(kl, 2 * wave + half)] = o;
+        st.q[RAG ? (g & 1) : 0][kl][stage_chunk(kl, 2 * wave + half)] = o;
         sbs[c] = sb;
     }
     // both halves hold the same column scales; one writes them
@@ -319,7 +325,132 @@ __device__ __forceinline__ void col_flush_q(const MxArgs &a, const ColStage &st,
     for (int i = 0; i < kTileK / 32; i++) {
         const int kr = (t >> 3) + 32 * i;
         const uint32_t off = chunk_live && k0 + kr < a.K ? (uint32_t)(kr * a.M) + 16 * jr : kDead;
-        buf_store16<AUX>(rc, off, st.q[kr][stage_chunk(kr, jr)]);
+        buf_store16<AUX>(rc, off, st.q[0][kr][stage_chunk(kr, jr)]);
+    }
+}
+
+// Bytes s .. s + 15 (0 <= s < 16) of the 32 bytes p (bytes 0-15) and c
+// (bytes 16-31): the dword shift in two rounds of selects, then the byte
+// shift.  Written on named words, not an array: the compiler turns selects
+// among an array's elements into an indexed load from scratch memory.
+__device__ __forceinline__ uint4 window16(uint4 p, uint4 c, uint32_t s)
+{
+    const bool d1 = (s & 4u) != 0, d2 = (s & 8u) != 0;
+    const uint32_t y0 = d1 ? p.y : p.x, y1 = d1 ? p.z : p.y, y2 = d1 ? p.w : p.z;
+    const uint32_t y3 = d1 ? c.x : p.w, y4 = d1 ? c.y : c.x, y5 = d1 ? c.z : c.y;
+    const uint32_t y6 = d1 ? c.w : c.z;
+    const uint32_t x0 = d2 ? y2 : y0, x1 = d2 ? y3 : y1, x2 = d2 ? y4 : y2;
+    const uint32_t x3 = d2 ? y5 : y3, x4 = d2 ? y6 : y4;
+    const uint32_t sh = s & 3u;
+    return make_uint4(__builtin_amdgcn_alignbyte(x1, x0, sh), __builtin_amdgcn_alignbyte(x2, x1, sh),
+                      __builtin_amdgcn_alignbyte(x3, x2, sh), __builtin_amdgcn_alignbyte(x4, x3, sh));
+}
+
+// Byte b (a constant once unrolled) of v.
+__device__ __forceinline__ uint8_t byte_of(uint4 v, int b)
+{
+    const uint32_t d = b < 4 ? v.x : b < 8 ? v.y : b < 12 ? v.z : v.w;
+    return (uint8_t)(d >> (8 * (b & 3)));
+}
+
+// The staged transposed tile of sub-tile g of a walk when transposed rows
+// start at any byte (the tensor's M, or the rows before its group, not a
+// multiple of 16).  Row kr's bytes of a sub-tile start at an address whose
+// offset sft within its 128-byte line is the same at every sub-tile of the
+// walk (they lie 128 bytes apart), so the sub-tile writes the whole line that
+// starts sft bytes before its first byte: the previous sub-tile's last sft
+// bytes (still in the other stage tile) and its own first 128 - sft, as 8
+// aligned 16-byte pieces.  Its own last sft bytes go out with the next
+// sub-tile.  Only bytes of the walk are written: at its first sub-tile the
+// sft bytes before it belong to the walk or group before, and its last
+// sub-tile also writes the line after, up to the row's end (rem bytes of the
+// sub-tile); the pieces holding other bytes as well -- at most one at each
+// end of a row -- leave byte by byte, at those two sub-tiles only.  Thread t
+// writes piece t % 8 of rows t / 8 + 32 i, and the ends of row t.
+
+// The 16 bytes at position u (0 <= u < 384) of row kr in the sequence: the
+// previous sub-tile's 128 bytes, the current one's 128, then 128 unstaged
+// bytes (any value).
+__device__ __forceinline__ uint4 rag_bytes(const StageTile &prev, const StageTile &cur, int kr,
+                                           int u)
+{
+    const int qa = u >> 4, qb = qa + 1;
+    const uint4 *pa = qa < 8 ? &prev[kr][stage_chunk(kr, qa)] : &cur[kr][stage_chunk(kr, (qa - 8) & 7)];
+    const uint4 *pb = qb < 8 ? &prev[kr][stage_chunk(kr, qb)] : &cur[kr][stage_chunk(kr, (qb - 8) & 7)];
+    return window16(*pa, *pb, (uint32_t)(u & 15));
+}
+
+template <int AUX>
+__device__ __forceinline__ void col_flush_q_rag(const MxArgs &a, const ColStageT<true> &st, int tm,
+                                                int tk, int g, bool first, bool last)
+{
+    const int t = (int)threadIdx.x;
+    const int j = t & 7;
+    const int64_t mt = (int64_t)tm * kTileM;
+    const int64_t k0 = (int64_t)tk * kTileK;
+    const int rem = a.M - mt < kTileM ? (int)(a.M - mt) : kTileM;   // the sub-tile's bytes per row
+    const StageTile &cur = st.q[g & 1], &prev = st.q[(g & 1) ^ 1];
+    // descriptor from the line boundary at or below this sub-tile's first byte
+    // of row k0; a row's offset d0 + kr M is below 255 * 2^23 + 128
+    const uint8_t *row0 = a.q_col + k0 * a.M;
+    const uint32_t d0 = (uint32_t)(reinterpret_cast<uintptr_t>(row0) & 127u);
+    const rsrc_t rc = make_rsrc(row0 - d0, mt, (a.K - k0) * a.M + d0);
+    const uint32_t M = (uint32_t)a.M;
+    // the rows' offsets are the same at every sub-tile; kept opaque here, they
+    // are formed again each time instead of being held across the walk
+    uint32_t base = d0;
+    asm volatile("" : "+v"(base));
+    // bytes lo .. rem - 1 of the sub-tile's row segment are its to write
+    // (negative: the previous sub-tile's)
+    const int lo = first ? 0 : -kTileM;
+#pragma unroll
+    for (int i = 0; i < kTileK / 32; i++) {
+        const int kr = (t >> 3) + 32 * i;
+        const uint32_t at = base + (uint32_t)kr * M;      // the row's first byte of the sub-tile
+        const int sft = (int)(at & 127u);
+        const int p0 = 16 * j - sft;                       // the piece's first byte in the segment
+        const uint4 v = rag_bytes(prev, cur, kr, p0 + kTileM);
+        const bool whole = k0 + kr < a.K && p0 >= lo && p0 + 16 <= rem;
+        buf_store16<AUX>(rc, whole ? at - (uint32_t)sft + 16u * j : kDead, v);
+    }
+    if (!(first || last))
+        return;
+    // the walk's ends, one row per thread: at the first sub-tile the piece
+    // that holds the row's first byte (if it starts before it), at the last
+    // one the piece that holds its last byte (if it ends after it), byte by
+    // byte, and the whole pieces of the line after
+    const int kr = t;
+    const bool row_ok = k0 + kr < a.K;
+    const uint32_t at = base + (uint32_t)kr * M;
+    const int sft = (int)(at & 127u);
+    const uint32_t line = at - (uint32_t)sft;
+    const int qa = sft >> 4;                                   // piece of the first byte
+    const int qb = (rem - 1 + sft) >> 4;                       // piece of the last byte
+    const bool head = first && row_ok && (sft & 15) != 0;
+    const bool tail = last && row_ok && ((rem + sft) & 15) != 0 && !(head && qb == qa);
+#pragma unroll
+    for (int e = 0; e < 2; e++) {
+        const bool on = e == 0 ? head : tail;
+        if (__builtin_amdgcn_ballot_w64(on) == 0)
+            continue;
+        const int q = e == 0 ? qa : qb;
+        const int p0 = 16 * q - sft;
+        const uint4 v = rag_bytes(prev, cur, kr, p0 + kTileM);
+#pragma unroll
+        for (int b = 0; b < 16; b++) {
+            const bool ok = on && p0 + b >= lo && p0 + b < rem;
+            buf_store1(rc, ok ? line + 16u * q + b : kDead, byte_of(v, b));
+        }
+    }
+    if (!last)
+        return;
+#pragma unroll 1
+    for (int q = 8; q < 16; q++) {
+        const int p0 = 16 * q - sft;
+        const bool whole = row_ok && p0 + 16 <= rem;
+        if (__builtin_amdgcn_ballot_w64(whole) == 0)
+            continue;
+        buf_store16<AUX>(rc, whole ? line + 16u * q : kDead, rag_bytes(prev, cur, kr, p0 + kTileM));
     }
 }
 
@@ -337,8 +468,8 @@ __device__ __forceinline__ uint32_t tile_word(uint2 v, int lane)
 // whole tiles except, for odd n, the upper half of the last one, which holds
 // no block of the tensor and is written as zeros.  The strip's 256
 // transposed rows are 8 row tiles, contiguous for each block tile.
-template <int AUX>
-__device__ __forceinline__ void col_flush_s_tiled(const MxArgs &a, const ColStage &st, int rg,
+template <int AUX, class Stage>
+__device__ __forceinline__ void col_flush_s_tiled(const MxArgs &a, const Stage &st, int rg,
                                                   int tk, int n)
 {
     const int t = (int)threadIdx.x;
@@ -365,8 +496,8 @@ __device__ __forceinline__ void col_flush_s_tiled(const MxArgs &a, const ColStag
 // Write the strip segment's column scales: 4 n bytes per column for a walk
 // of n sub-tiles (the tile layout, or compact rows in the widest pieces the
 // row length of s_col, the segment's start and its length allow).
-template <int AUX>
-__device__ __forceinline__ void col_flush_s(const MxArgs &a, const ColStage &st, int rg, int tk,
+template <int AUX, class Stage>
+__device__ __forceinline__ void col_flush_s(const MxArgs &a, const Stage &st, int rg, int tk,
                                             int n)
 {
     if (a.tiled) {
@@ -423,17 +554,18 @@ __device__ __forceinline__ void srow_flush(const MxArgs &a, const uint8_t (&srow
 // One sub-tile of the walk: row pass (direct row stores, row scales to LDS),
 // column pass into LDS, then the staged output leaves as whole lines.  Lanes
 // outside the tensor hold zeros and their stores are out of range.
-template <int OP, int FMT, bool ROW, bool COL, bool DBIAS>
+template <int OP, int FMT, bool ROW, bool COL, bool DBIAS, bool RAG>
 __device__ __forceinline__ void tile_step(const MxArgs &a, const LaneAt &l,
                                           const uint32_t (&w)[kRowsPerLane][4],
-                                          uint8_t (&srow)[kTileM][kTileK / 32], ColStage *st,
-                                          int tm, int tk, int g, float (&dsum)[kColsPerLane])
+                                          uint8_t (&srow)[kTileM][kTileK / 32],
+                                          ColStageT<RAG> *st, int tm, int tk, int g, int n,
+                                          float (&dsum)[kColsPerLane])
 {
     const bool live = lane_live(a, l, tm, tk);
     uint32_t cmax[4] = {0u, 0u, 0u, 0u};
     row_pass<OP, FMT, ROW, COL>(a, w, l, tm, tk, live, &srow[l.row][l.cl >> 2], cmax);
     if constexpr (COL)
-        col_pass<FMT>(*st, w, l.wave, l.half, l.cl, g, cmax);
+        col_pass<FMT, RAG>(*st, w, l.wave, l.half, l.cl, g, cmax);
     if constexpr (DBIAS) {
 #pragma unroll
         for (int c = 0; c < kColsPerLane; c++) {
@@ -445,7 +577,9 @@ __device__ __forceinline__ void tile_step(const MxArgs &a, const LaneAt &l,
         }
     }
     __syncthreads();
-    if constexpr (COL) {
+    if constexpr (COL && RAG) {
+        col_flush_q_rag<Policy<OP, ROW, COL>::q_col>(a, *st, tm, tk, g, g == 0, g + 1 == n);
+    } else if constexpr (COL) {
         // the non-temporal transposed stores pay off only for outputs too
         // large to be absorbed by the caches (the host decides: qcol_nt)
         if (Policy<OP, ROW, COL>::q_col == kNT && !a.qcol_nt)
@@ -467,14 +601,19 @@ __device__ __forceinline__ void tile_step(const MxArgs &a, const LaneAt &l,
 // workgroup (at most 168 VGPRs); the plain cast keeps its double register set
 // for the prefetch, and the dbias sums and the gated backward need their
 // registers (capping them spills and measured slower).
-template <int OP, bool DBIAS>
+template <int OP, bool DBIAS, bool RAG = false>
 constexpr int min_blocks()
 {
-    return OP == OP_PLAIN || OP == OP_DSWIGLU || OP == OP_DGEGLU || DBIAS ? 1 : 3;
+    const int n = OP == OP_PLAIN || OP == OP_DSWIGLU || OP == OP_DGEGLU || DBIAS ? 1 : 3;
+    // RAG: the double stage fits two workgroups per CU, and the plain cast
+    // (without its prefetch there) takes two as well
+    if (RAG)
+        return n == 3 || (OP == OP_PLAIN && !DBIAS) ? 2 : n;
+    return n;
 }
 
 // Walk rg of strip tk: the whole of a workgroup's work.
-template <int OP, int FMT, bool ROW, bool COL, bool DBIAS>
+template <int OP, int FMT, bool ROW, bool COL, bool DBIAS, bool RAG = false>
 __device__ __forceinline__ void mx_cast_walk(const MxArgs &a, int rg, int tk)
 {
     const int tm0 = rg * a.group;
@@ -482,14 +621,14 @@ __device__ __forceinline__ void mx_cast_walk(const MxArgs &a, int rg, int tk)
     const LaneAt l = lane_at();
 
     __shared__ __align__(16) uint8_t srow[kTileM][kTileK / 32];
-    ColStage *st = nullptr;
+    ColStageT<RAG> *st = nullptr;
     if constexpr (COL) {
-        __shared__ ColStage stage;
+        __shared__ ColStageT<RAG> stage;
         st = &stage;
     }
     float dsum[kColsPerLane] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
-    if constexpr (OP == OP_PLAIN) {
+    if constexpr (OP == OP_PLAIN && !RAG) {
         // Software pipeline over two register sets.  Every pass through the
         // loop body issues the same memory instructions (the load past the
         // walk's end reads a sub-tile outside the tensor, which costs no
@@ -503,13 +642,14 @@ __device__ __forceinline__ void mx_cast_walk(const MxArgs &a, int rg, int tk)
         for (; g + 1 < n; g += 2) {
             load_tile<OP, Policy<OP, ROW, COL>::x>(a, l, tm0 + g + 1, tk, wb);
             __builtin_amdgcn_sched_barrier(0);
-            tile_step<OP, FMT, ROW, COL, DBIAS>(a, l, wa, srow, st, tm0 + g, tk, g, dsum);
+            tile_step<OP, FMT, ROW, COL, DBIAS, RAG>(a, l, wa, srow, st, tm0 + g, tk, g, n, dsum);
             load_tile<OP, Policy<OP, ROW, COL>::x>(a, l, g + 2 < n ? tm0 + g + 2 : past, tk, wa);
             __builtin_amdgcn_sched_barrier(0);
-            tile_step<OP, FMT, ROW, COL, DBIAS>(a, l, wb, srow, st, tm0 + g + 1, tk, g + 1, dsum);
+            tile_step<OP, FMT, ROW, COL, DBIAS, RAG>(a, l, wb, srow, st, tm0 + g + 1, tk, g + 1, n,
+                                                    dsum);
         }
         if (g < n)
-            tile_step<OP, FMT, ROW, COL, DBIAS>(a, l, wa, srow, st, tm0 + g, tk, g, dsum);
+            tile_step<OP, FMT, ROW, COL, DBIAS, RAG>(a, l, wa, srow, st, tm0 + g, tk, g, n, dsum);
     } else {
         uint32_t w[kRowsPerLane][4];
         for (int g = 0; g < n; g++) {
@@ -526,7 +666,7 @@ __device__ __forceinline__ void mx_cast_walk(const MxArgs &a, int rg, int tk)
             } else {
                 load_tile<OP, Policy<OP, ROW, COL>::x>(a, l, tm0 + g, tk, w);
             }
-            tile_step<OP, FMT, ROW, COL, DBIAS>(a, l, w, srow, st, tm0 + g, tk, g, dsum);
+            tile_step<OP, FMT, ROW, COL, DBIAS, RAG>(a, l, w, srow, st, tm0 + g, tk, g, n, dsum);
         }
     }
     if constexpr (COL)
@@ -541,7 +681,7 @@ __device__ __forceinline__ void mx_cast_walk(const MxArgs &a, int rg, int tk)
         // workgroup small enough for three per CU
         float4 (*red)[kTileK / 4];
         if constexpr (COL) {
-            red = reinterpret_cast<float4 (*)[kTileK / 4]>(&st->q[0][0]);
+            red = reinterpret_cast<float4 (*)[kTileK / 4]>(&st->q[0][0][0]);
         } else {
             __shared__ float4 red_own[2 * kWaves][kTileK / 4];
             red = red_own;
@@ -600,8 +740,8 @@ __global__ __launch_bounds__(kThreads, (min_blocks<OP, DBIAS>())) void mx_cast_k
 // Grouped: walk rg (numbered across all groups) belongs to the group g with
 // walk0[g] <= rg < walk0[g + 1]; that group is cast as a tensor of its own,
 // its inputs and outputs found at the group's offsets.
-template <int OP, int FMT, bool ROW, bool COL, bool DBIAS>
-__global__ __launch_bounds__(kThreads, (min_blocks<OP, DBIAS>())) void mx_cast_grouped_kernel(
+template <int OP, int FMT, bool ROW, bool COL, bool DBIAS, bool RAG>
+__global__ __launch_bounds__(kThreads, (min_blocks<OP, DBIAS, RAG>())) void mx_cast_grouped_kernel(
     MxArgs a, GroupTable gt)
 {
     int rg, tk;
@@ -622,15 +762,16 @@ __global__ __launch_bounds__(kThreads, (min_blocks<OP, DBIAS>())) void mx_cast_g
     b.tiles_m = (int)((b.M + kTileM - 1) / kTileM);
     b.group = gt.len[g];
     b.groups_m = gt.walk0[g + 1] - gt.walk0[g];
-    mx_cast_walk<OP, FMT, ROW, COL, DBIAS>(b, rg - gt.walk0[g], tk);
+    mx_cast_walk<OP, FMT, ROW, COL, DBIAS, RAG>(b, rg - gt.walk0[g], tk);
 }
 
-template <int OP, int FMT, bool ROW, bool COL, bool DBIAS, bool GROUPED>
+template <int OP, int FMT, bool ROW, bool COL, bool DBIAS, bool GROUPED, bool RAG>
 hipError_t launch_one(const MxArgs &a, const GroupTable *gt, hipStream_t s)
 {
+    static_assert(GROUPED || !RAG, "transposed rows at any byte: the grouped kernel only");
     const int blocks = a.groups_m * a.tiles_k;
     if constexpr (GROUPED)
-        hipLaunchKernelGGL((mx_cast_grouped_kernel<OP, FMT, ROW, COL, DBIAS>), dim3(blocks),
+        hipLaunchKernelGGL((mx_cast_grouped_kernel<OP, FMT, ROW, COL, DBIAS, RAG>), dim3(blocks),
                            dim3(kThreads), 0, s, a, *gt);
     else
         hipLaunchKernelGGL((mx_cast_kernel<OP, FMT, ROW, COL, DBIAS>), dim3(blocks),
@@ -638,62 +779,71 @@ hipError_t launch_one(const MxArgs &a, const GroupTable *gt, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int OP, int FMT, bool DBIAS, bool GROUPED>
+template <int OP, int FMT, bool DBIAS, bool GROUPED, bool RAG>
 hipError_t launch_axis(unsigned axis, const MxArgs &a, const GroupTable *gt, hipStream_t s)
 {
     switch (axis) {
-    case 1u: return launch_one<OP, FMT, true, false, DBIAS, GROUPED>(a, gt, s);
-    case 2u: return launch_one<OP, FMT, false, true, DBIAS, GROUPED>(a, gt, s);
-    case 3u: return launch_one<OP, FMT, true, true, DBIAS, GROUPED>(a, gt, s);
+    case 1u:
+        // row-wise alone has no transposed rows to align: never the RAG variant
+        if constexpr (RAG)
+            return hipErrorInvalidValue;
+        else
+            return launch_one<OP, FMT, true, false, DBIAS, GROUPED, false>(a, gt, s);
+    case 2u: return launch_one<OP, FMT, false, true, DBIAS, GROUPED, RAG>(a, gt, s);
+    case 3u: return launch_one<OP, FMT, true, true, DBIAS, GROUPED, RAG>(a, gt, s);
     default: return hipErrorInvalidValue;
     }
 }
 
 // Every pre-op, output set and dbias choice of one format, plain (gt null)
 // or grouped.
-template <int FMT, bool GROUPED>
+template <int FMT, bool GROUPED, bool RAG>
 hipError_t launch_mx_cast_fmt(int op, unsigned axis, bool dbias, const MxArgs &a,
                               const GroupTable *gt, hipStream_t s)
 {
     switch (op) {
     case OP_PLAIN:
-        return dbias ? launch_axis<OP_PLAIN, FMT, true, GROUPED>(axis, a, gt, s)
-                     : launch_axis<OP_PLAIN, FMT, false, GROUPED>(axis, a, gt, s);
+        return dbias ? launch_axis<OP_PLAIN, FMT, true, GROUPED, RAG>(axis, a, gt, s)
+                     : launch_axis<OP_PLAIN, FMT, false, GROUPED, RAG>(axis, a, gt, s);
     case OP_GELU:
-        return dbias ? launch_axis<OP_GELU, FMT, true, GROUPED>(axis, a, gt, s)
-                     : launch_axis<OP_GELU, FMT, false, GROUPED>(axis, a, gt, s);
+        return dbias ? launch_axis<OP_GELU, FMT, true, GROUPED, RAG>(axis, a, gt, s)
+                     : launch_axis<OP_GELU, FMT, false, GROUPED, RAG>(axis, a, gt, s);
     case OP_DGELU:
-        return dbias ? launch_axis<OP_DGELU, FMT, true, GROUPED>(axis, a, gt, s)
-                     : launch_axis<OP_DGELU, FMT, false, GROUPED>(axis, a, gt, s);
+        return dbias ? launch_axis<OP_DGELU, FMT, true, GROUPED, RAG>(axis, a, gt, s)
+                     : launch_axis<OP_DGELU, FMT, false, GROUPED, RAG>(axis, a, gt, s);
     case OP_SWIGLU:
-        return launch_axis<OP_SWIGLU, FMT, false, GROUPED>(axis, a, gt, s);
+        return launch_axis<OP_SWIGLU, FMT, false, GROUPED, RAG>(axis, a, gt, s);
     case OP_GEGLU:
-        return launch_axis<OP_GEGLU, FMT, false, GROUPED>(axis, a, gt, s);
+        return launch_axis<OP_GEGLU, FMT, false, GROUPED, RAG>(axis, a, gt, s);
     case OP_DSILU:
-        return dbias ? launch_axis<OP_DSILU, FMT, true, GROUPED>(axis, a, gt, s)
-                     : launch_axis<OP_DSILU, FMT, false, GROUPED>(axis, a, gt, s);
+        return dbias ? launch_axis<OP_DSILU, FMT, true, GROUPED, RAG>(axis, a, gt, s)
+                     : launch_axis<OP_DSILU, FMT, false, GROUPED, RAG>(axis, a, gt, s);
     case OP_DSWIGLU:
-        return launch_axis<OP_DSWIGLU, FMT, false, GROUPED>(axis, a, gt, s);
+        return launch_axis<OP_DSWIGLU, FMT, false, GROUPED, RAG>(axis, a, gt, s);
     case OP_DGEGLU:
-        return launch_axis<OP_DGEGLU, FMT, false, GROUPED>(axis, a, gt, s);
+        return launch_axis<OP_DGEGLU, FMT, false, GROUPED, RAG>(axis, a, gt, s);
     default:
         return hipErrorInvalidValue;
     }
 }
 
-// Instantiated once each, in mx_cast_fmt_*.hip (plain) and mx_cast_grp_*.hip
-// (grouped).
-#define MXK_DECLARE_FMT(F, G)                                                                   \
-    extern template hipError_t launch_mx_cast_fmt<F, G>(int, unsigned, bool, const MxArgs &,   \
-                                                        const GroupTable *, hipStream_t);
-MXK_DECLARE_FMT(0, false)
-MXK_DECLARE_FMT(kFmtE5M2, false)
-MXK_DECLARE_FMT(kFmtRoundUp, false)
-MXK_DECLARE_FMT(kFmtE5M2 | kFmtRoundUp, false)
-MXK_DECLARE_FMT(0, true)
-MXK_DECLARE_FMT(kFmtE5M2, true)
-MXK_DECLARE_FMT(kFmtRoundUp, true)
-MXK_DECLARE_FMT(kFmtE5M2 | kFmtRoundUp, true)
+// Instantiated once each, in mx_cast_fmt_*.hip (plain), mx_cast_grp_*.hip
+// (grouped) and mx_cast_rag_*.hip (grouped, transposed rows at any byte).
+#define MXK_DECLARE_FMT(F, G, R)                                                               \
+    extern template hipError_t launch_mx_cast_fmt<F, G, R>(int, unsigned, bool, const MxArgs &, \
+                                                           const GroupTable *, hipStream_t);
+MXK_DECLARE_FMT(0, false, false)
+MXK_DECLARE_FMT(kFmtE5M2, false, false)
+MXK_DECLARE_FMT(kFmtRoundUp, false, false)
+MXK_DECLARE_FMT(kFmtE5M2 | kFmtRoundUp, false, false)
+MXK_DECLARE_FMT(0, true, false)
+MXK_DECLARE_FMT(kFmtE5M2, true, false)
+MXK_DECLARE_FMT(kFmtRoundUp, true, false)
+MXK_DECLARE_FMT(kFmtE5M2 | kFmtRoundUp, true, false)
+MXK_DECLARE_FMT(0, true, true)
+MXK_DECLARE_FMT(kFmtE5M2, true, true)
+MXK_DECLARE_FMT(kFmtRoundUp, true, true)
+MXK_DECLARE_FMT(kFmtE5M2 | kFmtRoundUp, true, true)
 #undef MXK_DECLARE_FMT
 
 }  // namespace mxk

@@ -117,16 +117,16 @@ __global__ __launch_bounds__(256) void fused_values_kernel(const uint16_t *x, co
     *reinterpret_cast<uint4 *>(y + i) = o;
 }
 
-template <bool GROUPED>
+template <bool GROUPED, bool RAG>
 static hipError_t dispatch_fmt(int op, unsigned axis, unsigned fmt, bool dbias, const MxArgs &a,
                                const GroupTable *gt, hipStream_t s)
 {
     switch (fmt) {
-    case 0u: return launch_mx_cast_fmt<0, GROUPED>(op, axis, dbias, a, gt, s);
-    case kFmtE5M2: return launch_mx_cast_fmt<kFmtE5M2, GROUPED>(op, axis, dbias, a, gt, s);
-    case kFmtRoundUp: return launch_mx_cast_fmt<kFmtRoundUp, GROUPED>(op, axis, dbias, a, gt, s);
+    case 0u: return launch_mx_cast_fmt<0, GROUPED, RAG>(op, axis, dbias, a, gt, s);
+    case kFmtE5M2: return launch_mx_cast_fmt<kFmtE5M2, GROUPED, RAG>(op, axis, dbias, a, gt, s);
+    case kFmtRoundUp: return launch_mx_cast_fmt<kFmtRoundUp, GROUPED, RAG>(op, axis, dbias, a, gt, s);
     case kFmtE5M2 | kFmtRoundUp:
-        return launch_mx_cast_fmt<kFmtE5M2 | kFmtRoundUp, GROUPED>(op, axis, dbias, a, gt, s);
+        return launch_mx_cast_fmt<kFmtE5M2 | kFmtRoundUp, GROUPED, RAG>(op, axis, dbias, a, gt, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -134,13 +134,19 @@ static hipError_t dispatch_fmt(int op, unsigned axis, unsigned fmt, bool dbias, 
 hipError_t launch_mx_cast(int op, unsigned axis, unsigned fmt, bool dbias, const MxArgs &a,
                           hipStream_t s)
 {
-    return dispatch_fmt<false>(op, axis, fmt, dbias, a, nullptr, s);
+    return dispatch_fmt<false, false>(op, axis, fmt, dbias, a, nullptr, s);
 }
 
 hipError_t launch_mx_cast_grouped(int op, unsigned axis, unsigned fmt, bool dbias, const MxArgs &a,
                                   const GroupTable &gt, hipStream_t s)
 {
-    return dispatch_fmt<true>(op, axis, fmt, dbias, a, &gt, s);
+    return dispatch_fmt<true, false>(op, axis, fmt, dbias, a, &gt, s);
+}
+
+hipError_t launch_mx_cast_ragged(int op, unsigned axis, unsigned fmt, bool dbias, const MxArgs &a,
+                                 const GroupTable &gt, hipStream_t s)
+{
+    return dispatch_fmt<true, true>(op, axis, fmt, dbias, a, &gt, s);
 }
 
 hipError_t launch_dbias_reduce(const float *partials, int segments, int64_t K, float *dbias,

@@ -2,6 +2,6 @@
 #include "mx_cast.h"
 
 namespace mxk {
-template hipError_t launch_mx_cast_fmt<kFmtE5M2 | kFmtRoundUp, false>(int, unsigned, bool, const MxArgs &,
+template hipError_t launch_mx_cast_fmt<kFmtE5M2 | kFmtRoundUp, false, false>(int, unsigned, bool, const MxArgs &,
                                                     const GroupTable *, hipStream_t);
 }  // namespace mxk

@@ -3,6 +3,6 @@
 #include "mx_cast.h"
 
 namespace mxk {
-template hipError_t launch_mx_cast_fmt<0, true>(int, unsigned, bool, const MxArgs &,
+template hipError_t launch_mx_cast_fmt<0, true, false>(int, unsigned, bool, const MxArgs &,
                                                    const GroupTable *, hipStream_t);
 }  // namespace mxk

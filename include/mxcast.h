@@ -150,11 +150,12 @@ typedef enum mx_status {
  *   x        device, bf16 [M][K]
  *   grad     device, bf16 [M][K]; required for MX_FUSE_DGELU / DSILU, else
  *            ignored
- *   M, K     rows, columns: any M, K >= 1, each <= 2^23, M*K <= 2^40.  M a
- *            multiple of 16 and K of 8 (every row of every input and output
- *            16-byte aligned) take the tiled kernel; any other shape takes a
- *            kernel for arbitrary row alignment (same results, lower
- *            bandwidth)
+ *   M, K     rows, columns: any M, K >= 1, each <= 2^23, M*K <= 2^40.  K a
+ *            multiple of 8 (every row of x 16-byte aligned) takes the tiled
+ *            kernel, for any M (with M not a multiple of 16 the rows of q_col
+ *            start at any byte and it writes them through a two-tile stage,
+ *            at a lower bandwidth); any other K takes a kernel for arbitrary
+ *            row alignment (same results, lower bandwidth still)
  *   axis_mask  MX_ROWWISE, MX_COLWISE or both (one pass over x), optionally
  *            with the format flags MX_ELEM_E5M2 / MX_SCALE_ROUND_UP and the
  *            layout flag MX_SCALE_TILED (scale tensors then have
@@ -227,9 +228,10 @@ size_t mx_scale_size(int64_t rows, int64_t cols, unsigned axis_mask);
  *   x, grad      device, bf16 [M][K], M = sum of group_rows; group g owns rows
  *                r_g .. r_g + group_rows[g] - 1, r_g = sum_{h<g} group_rows[h]
  *   group_rows   HOST array of G row counts, each >= 0 (an empty group is
- *                allowed); 1 <= G <= 64, 0 < M <= 2^23.  Every count a
- *                multiple of 16 and K of 8 take the tiled kernel, any other
- *                stack the any-shape kernel (same results)
+ *                allowed); 1 <= G <= 64, 0 < M <= 2^23.  K a multiple of 8
+ *                takes the tiled kernel, for any counts (counts that are not
+ *                multiples of 16: as for an M that is not, in mx_quantize),
+ *                any other K the any-shape kernel (same results)
  *   axis_mask, fusion  as for mx_quantize (format and layout flags included)
  *   q_row        [M][K]: the groups' row-wise elements (the stacked tensor's)
  *   s_row        the groups' row scales one after the other, group g's
@@ -264,9 +266,9 @@ size_t mx_grouped_scale_size(int64_t K, const int64_t *group_rows, int G, unsign
  * Gated MXFP8 cast.  x is bf16 [M][2N] holding [gate | linear] (gate =
  * columns 0..N-1); the quantised tensor is y[M][N] = act(gate) * linear,
  * block size 32 (partial at the edges as for mx_quantize), any M, N >= 1
- * with M <= 2^23, 2N <= 2^23, M * 2N <= 2^40 (M a multiple of 16 and N of 8
- * take the tiled kernel).  axis_mask as for mx_quantize (format flags
- * included).
+ * with M <= 2^23, 2N <= 2^23, M * 2N <= 2^40 (N a multiple of 8 takes the
+ * tiled kernel, for any M, as in mx_quantize).  axis_mask as for mx_quantize
+ * (format flags included).
  *   q_row, s_row  E4M3 [M][N], E8M0 [M][ceil(N/32)]   (iff MX_ROWWISE)
  *   q_col, s_col  E4M3 [N][M], E8M0 [N][ceil(M/32)]   (iff MX_COLWISE)
  */
@@ -283,8 +285,8 @@ mx_status mx_quantize_gated(const void *x, int64_t M, int64_t N, unsigned axis_m
  *   d_gate   = fl32(fl32(a' * grad) * linear),   d_linear = fl32(a * grad),
  * each rounded once to bf16; block size 32 along 2N (row-wise) and M.
  * Any M, N >= 1 with M <= 2^23, 2N <= 2^23, M * 2N <= 2^40 (partial blocks
- * at the edges as for mx_quantize; M a multiple of 16 and N of 8 take the
- * tiled kernel).  axis_mask as for mx_quantize (format flags included).
+ * at the edges as for mx_quantize; N a multiple of 8 takes the tiled kernel,
+ * for any M).  axis_mask as for mx_quantize (format flags included).
  *   q_row, s_row  E4M3 [M][2N], E8M0 [M][ceil(2N/32)]   (iff MX_ROWWISE)
  *   q_col, s_col  E4M3 [2N][M], E8M0 [2N][ceil(M/32)]   (iff MX_COLWISE)
  * Errors as for mx_quantize_gated.

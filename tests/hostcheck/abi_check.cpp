@@ -87,20 +87,37 @@ static void check_any_plan(int64_t M, int64_t K)
     CHECK(gt.row0[0] == 0 && gt.row0[1] == M && gt.srow_off[0] == 0 && gt.scol_off[0] == 0);
 }
 
-// The shapes the tiled kernel takes (M a multiple of 16, K of 8); others go
-// to the any-shape kernel.
-static bool tiled_kernel_shape(int64_t M, int64_t K) { return M % 16 == 0 && K % 8 == 0; }
+// The kernel an M x K cast goes to: the tiled kernel for row lengths that
+// are multiples of 8, its variant for transposed rows at any byte when the
+// transposed output is asked for and M is not a multiple of 16, the
+// any-shape kernel for other row lengths.
+static int mx_route(int64_t M, int64_t K, bool col = true)
+{
+    if (K % 8 != 0)
+        return mxk::kLaunchMxAny;
+    return col && M % 16 != 0 ? mxk::kLaunchMxRagged : mxk::kLaunchMx;
+}
 
-static void check_mx(int64_t M, int64_t K, bool tiled, bool any = false)
+static void check_mx(int64_t M, int64_t K, bool tiled, int kind = mxk::kLaunchMx)
 {
     const mxk::MxArgs &a = g_rec.mx;
     CHECK(a.M == M && a.K == K);
     CHECK((a.tiled != 0) == tiled);
-    CHECK(g_rec.kind == (any ? mxk::kLaunchMxAny : mxk::kLaunchMx));
-    if (any)
+    CHECK(g_rec.kind == kind);
+    if (kind == mxk::kLaunchMxAny) {
         check_any_plan(M, K);
-    else
-        check_plan(M, K, a.tiles_m, a.tiles_k, a.group, a.groups_m, tiled);
+        return;
+    }
+    check_plan(M, K, a.tiles_m, a.tiles_k, a.group, a.groups_m, tiled);
+    if (kind == mxk::kLaunchMxRagged) {
+        // the tensor as a stack of one group, with the tiled kernel's walks,
+        // at most kMaxRagGroup sub-tiles long (the double stage's budget)
+        CHECK(a.group <= mxk::kMaxRagGroup);
+        const mxk::GroupTable &gt = g_rec.gt;
+        CHECK(gt.count == 1 && gt.len[0] == a.group && gt.walk0[0] == 0 && gt.walk0[1] == a.groups_m);
+        CHECK(gt.row0[0] == 0 && gt.row0[1] == M && gt.srow_off[0] == 0 && gt.scol_off[0] == 0);
+        CHECK(a.qcol_nt == 0);
+    }
 }
 
 // A group table over G groups of the given row counts, stacked (walks of the
@@ -138,7 +155,8 @@ static void mx_quantize_cases()
                                  {16, 8}, {kDim, kDim >> 6}, {16400, 7176},
                                  {1, 1}, {1, kDim}, {kDim, 1}, {17, 9}, {16383, 16383},
                                  {kDim - 1, (1 << 17) - 1}, {(1 << 17) - 3, kDim}, {40, 64},
-                                 {kDim, 12}, {kDim >> 6, kDim - 4}};
+                                 {kDim, 12}, {kDim >> 6, kDim - 4}, {16383, 16384}, {1, 8},
+                                 {kDim - 1, 8}, {(1 << 17) - 1, kDim}, {100, 7168}};
     for (auto &s : shapes) {
         for (unsigned flags : {0u, (unsigned)MX_SCALE_TILED, MX_ELEM_E5M2 | MX_SCALE_ROUND_UP}) {
             for (int fusion : {0, MX_FUSE_GELU, MX_FUSE_DGELU | MX_FUSE_DBIAS, MX_FUSE_DSILU}) {
@@ -146,7 +164,7 @@ static void mx_quantize_cases()
                 CHECK(((fusion & MX_FUSE_DBIAS) != 0) == (need > 0));
                 EXPECT(MX_OK, mx_quantize(P(0), P(1), s[0], s[1], both | flags, fusion, qr, sr, qc,
                                           sc, db, ws, need, 0));
-                check_mx(s[0], s[1], flags & MX_SCALE_TILED, !tiled_kernel_shape(s[0], s[1]));
+                check_mx(s[0], s[1], flags & MX_SCALE_TILED, mx_route(s[0], s[1]));
                 if (need) {
                     CHECK(g_rec.segments == g_rec.mx.groups_m);
                     CHECK(need == (size_t)g_rec.mx.groups_m * (size_t)s[1] * 4);
@@ -157,8 +175,10 @@ static void mx_quantize_cases()
         }
         EXPECT(MX_OK, mx_quantize(P(0), nullptr, s[0], s[1], MX_ROWWISE, 0, qr, sr, nullptr,
                                   nullptr, nullptr, nullptr, 0, 0));
+        check_mx(s[0], s[1], false, mx_route(s[0], s[1], false));
         EXPECT(MX_OK, mx_quantize(P(0), nullptr, s[0], s[1], MX_COLWISE, 0, nullptr, nullptr, qc,
                                   sc, nullptr, nullptr, 0, 0));
+        check_mx(s[0], s[1], false, mx_route(s[0], s[1]));
     }
     // shapes
     const int64_t bad[][2] = {{kDim + 16, 8},  {16, kDim + 8}, {kDim, (1 << 17) + 8},
@@ -226,15 +246,18 @@ static void gated_cases()
                              {1, 1}, {17, 4}, {kDim - 1, 1 << 16}, {128, kDim / 2 - 1}, {40, 12},
                              {kDim, (1 << 16) - 1}};
     for (auto &s : ok) {
-        // the tiled kernel needs M a multiple of 16 and N of 8 (both halves aligned)
-        const bool any = !(s[0] % 16 == 0 && s[1] % 8 == 0);
+        // the tiled kernel needs N a multiple of 8 (both halves aligned)
+        const int kind = mx_route(s[0], s[1]);
         for (int act : {MX_GATED_SWIGLU, MX_GATED_GEGLU}) {
             EXPECT(MX_OK, mx_quantize_gated(P(0), s[0], s[1], both, act, qr, sr, qc, sc, 0));
-            check_mx(s[0], s[1], false, any);
+            check_mx(s[0], s[1], false, kind);
             CHECK(g_rec.mx.ldx == 2 * s[1] && g_rec.mx.lin_off == s[1]);
+            EXPECT(MX_OK, mx_quantize_gated(P(0), s[0], s[1], MX_ROWWISE, act, qr, sr, nullptr,
+                                            nullptr, 0));
+            check_mx(s[0], s[1], false, mx_route(s[0], s[1], false));
             EXPECT(MX_OK, mx_quantize_dgated(P(1), P(0), s[0], s[1], both | MX_SCALE_TILED, act, qr,
                                              sr, qc, sc, 0));
-            check_mx(s[0], 2 * s[1], true, any);
+            check_mx(s[0], 2 * s[1], true, kind);
             CHECK(g_rec.mx.ldx == 2 * s[1] && g_rec.mx.ldg == s[1] && g_rec.mx.lin_off == s[1]);
         }
     }
@@ -302,15 +325,18 @@ static void grouped_cases()
             M += c.rows[g];
             rows16 = rows16 && c.rows[g] % 16 == 0;
         }
-        const bool any = !(rows16 && c.K % 8 == 0);
+        const bool any = c.K % 8 != 0;
+        const int kind = any ? mxk::kLaunchMxAny : rows16 ? mxk::kLaunchMxGrouped : mxk::kLaunchMxRagged;
         for (unsigned flags : {0u, (unsigned)MX_SCALE_TILED}) {
             for (int fusion : {0, MX_FUSE_DBIAS, MX_FUSE_DGELU | MX_FUSE_DBIAS}) {
                 const size_t need = mx_quantize_grouped_workspace_size(c.K, c.rows, c.G, both | flags,
                                                                       fusion);
                 EXPECT(MX_OK, mx_quantize_grouped(P(0), P(1), c.K, c.rows, c.G, both | flags, fusion,
                                                   qr, sr, qc, sc, db, ws, need, 0));
-                CHECK(g_rec.kind == (any ? mxk::kLaunchMxAny : mxk::kLaunchMxGrouped) &&
-                      g_rec.mx.M == M);
+                CHECK(g_rec.kind == kind && g_rec.mx.M == M);
+                if (kind == mxk::kLaunchMxRagged)
+                    for (int g = 0; g < c.G; g++)
+                        CHECK(g_rec.gt.len[g] <= mxk::kMaxRagGroup);
                 CHECK(g_rec.mx.tiles_k == ceil_div(c.K, any ? mxk::kAnyTileK : mxk::kTileK));
                 check_groups(c.rows, c.G, g_rec.mx.groups_m, any);
                 if (fusion & MX_FUSE_DBIAS)
@@ -333,7 +359,7 @@ static void grouped_cases()
                mx_quantize_gated_grouped(P(0), c.K, c.rows, c.G, both, MX_GATED_SWIGLU, qr, sr, qc,
                                          sc, 0));
         if (gated_ok) {
-            CHECK(g_rec.kind == (any ? mxk::kLaunchMxAny : mxk::kLaunchMxGrouped));
+            CHECK(g_rec.kind == kind);
             check_groups(c.rows, c.G, g_rec.mx.groups_m, any);
         }
         EXPECT(gated_ok ? MX_OK : MX_ERR_SHAPE,
@@ -378,7 +404,9 @@ static void grouped_cases()
         CHECK(mx_quantize_grouped_workspace_size(256, b.rows, b.G, both, MX_FUSE_DBIAS) == 0);
         CHECK(mx_grouped_scale_size(256, b.rows, b.G, both, 0) == 0);
     }
-    // row counts that are not multiples of 16: the any-shape kernels
+    // row counts that are not multiples of 16: the any-shape NVFP4 kernel, and
+    // the MXFP8 kernel variant whose transposed rows start at any byte (the
+    // plain grouped kernel for the row-wise output alone)
     const int64_t odd[2] = {16, 8};
     EXPECT(MX_OK, nvfp4_quantize_transpose_grouped(P(0), 256, odd, 2, P<float>(1), 0, both, qr, sr,
                                                    qc, sc, nullptr, 0));
@@ -386,6 +414,12 @@ static void grouped_cases()
           g_rec.gt.scol_off[1] == 256);
     EXPECT(MX_OK, mx_absmax_bf16_grouped(P(0), 256, odd, 2, P<float>(1), 0));
     EXPECT(MX_OK, mx_quantize_grouped(P(0), nullptr, 256, odd, 2, both, 0, qr, sr, qc, sc, nullptr,
+                                      nullptr, 0, 0));
+    CHECK(g_rec.kind == mxk::kLaunchMxRagged);
+    EXPECT(MX_OK, mx_quantize_grouped(P(0), nullptr, 256, odd, 2, MX_ROWWISE, 0, qr, sr, nullptr,
+                                      nullptr, nullptr, nullptr, 0, 0));
+    CHECK(g_rec.kind == mxk::kLaunchMxGrouped);
+    EXPECT(MX_OK, mx_quantize_grouped(P(0), nullptr, 252, odd, 2, both, 0, qr, sr, qc, sc, nullptr,
                                       nullptr, 0, 0));
     CHECK(g_rec.kind == mxk::kLaunchMxAny);
     for (int64_t K : {kBig, int64_t(0), int64_t(-16), kDim + 16, INT64_MIN}) {

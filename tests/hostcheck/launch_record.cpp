@@ -31,6 +31,14 @@ hipError_t launch_mx_cast_grouped(int op, unsigned axis, unsigned fmt, bool dbia
     return note(kLaunchMxGrouped);
 }
 
+hipError_t launch_mx_cast_ragged(int op, unsigned axis, unsigned fmt, bool dbias,
+                                 const MxArgs &a, const GroupTable &gt, hipStream_t)
+{
+    g_rec.op = op, g_rec.axis = axis, g_rec.fmt = fmt, g_rec.dbias = dbias, g_rec.mx = a;
+    g_rec.gt = gt;
+    return note(kLaunchMxRagged);
+}
+
 hipError_t launch_mx_cast_any(int op, unsigned axis, unsigned fmt, bool dbias, const MxArgs &a,
                               const GroupTable &gt, hipStream_t)
 {

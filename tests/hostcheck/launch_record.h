@@ -5,7 +5,8 @@
 namespace mxk {
 
 enum { kLaunchNone, kLaunchMx, kLaunchMxGrouped, kLaunchValues, kLaunchAbsmax, kLaunchNv,
-       kLaunchNvGrouped, kLaunchAbsmaxGrouped, kLaunchMxAny, kLaunchValuesAny, kLaunchNvAny };
+       kLaunchNvGrouped, kLaunchAbsmaxGrouped, kLaunchMxAny, kLaunchValuesAny, kLaunchNvAny,
+       kLaunchMxRagged };
 
 struct Record {
     int calls = 0, reduces = 0, kind = kLaunchNone;

@@ -31,22 +31,25 @@ ROWS_PER_LANE, COLS_PER_LANE, WAVES = 16, 8, 4
 THREADS = 64 * WAVES
 TILE_M, TILE_K = 128, 256
 MAX_GROUP = 16
+MAX_RAG_GROUP = 14
 MAX_RECORDS = 0x7FFFFFFF
 DEAD = 0x80000000
 U32 = 1 << 32
 
 
-def pick_group(tiles_m, tiles_k, target=512):
-    g = MAX_GROUP
+def pick_group(tiles_m, tiles_k, target=512, max_len=16):
+    g = 1
+    while 2 * g <= max_len:
+        g *= 2
     while g > 1 and ((tiles_m + g - 1) // g) * tiles_k < target:
         g >>= 1
     return g
 
 
-def plan_walk(t, tiles_k, slots=512, even=False):
+def plan_walk(t, tiles_k, slots=512, even=False, max_len=16):
     """plan_walks (launch.h) for one tensor of t sub-tile rows."""
     best = None
-    for L in range(2 if even else 1, MAX_GROUP + 1, 2 if even else 1):
+    for L in range(2 if even else 1, max_len + 1, 2 if even else 1):
         lg = -(-t // -(-t // L))
         lg += lg & 1 if even else 0
         cost = -(-(-(-t // lg) * tiles_k) // slots) * (lg + 1)
@@ -131,10 +134,12 @@ def mx_model(M, K, op="plain", tiled=False, ck=None):
     else:
         ldx, lin_off, ldg = K, 0, K
     tiles_m, tiles_k = -(-M // TILE_M), -(-K // TILE_K)
+    # walks of the variant for transposed rows at any byte: at most 14
+    max_len = MAX_RAG_GROUP if M % 16 else MAX_GROUP
     if op == "plain":
-        group = plan_walk(tiles_m, tiles_k, even=tiled)
+        group = plan_walk(tiles_m, tiles_k, even=tiled, max_len=max_len)
     else:
-        group = pick_group(tiles_m, tiles_k)
+        group = pick_group(tiles_m, tiles_k, max_len=max_len)
         if tiled and group < 2:
             group = 2
     groups_m = -(-tiles_m // group)
@@ -198,12 +203,20 @@ def mx_model(M, K, op="plain", tiled=False, ck=None):
         # ---- col_flush_q: thread t writes chunk t % 8 of transposed rows t / 8 + 32 i
         jr = t & 7
         mt, k0 = tm * TILE_M, tk * TILE_K
-        rc = Desc(k0 * M + mt, K * M)
-        chunk_live = mt + 16 * jr < M
-        kr = (t >> 3)[None, :] + 32 * np.arange(TILE_K // 32)[:, None]
-        ok = chunk_live & (k0 + kr < K)
-        ck.access("q_col", rc, np.where(ok, kr * M + 16 * jr, DEAD), 16, ok,
-                  (k0 + kr) * M + mt + 16 * jr)
+        if M % 16:
+            # col_flush_q_rag, at the sub-tile's place in its walk
+            g = tm % group
+            n = min(tiles_m - (tm - g), group)
+            for site, d, off, nb_, lv, addr in model_col_flush_q_rag(0, M, K, tm, tk, g == 0,
+                                                                     g == n - 1):
+                ck.access(site, d, off, nb_, lv, addr)
+        else:
+            rc = Desc(k0 * M + mt, K * M)
+            chunk_live = mt + 16 * jr < M
+            kr = (t >> 3)[None, :] + 32 * np.arange(TILE_K // 32)[:, None]
+            ok = chunk_live & (k0 + kr < K)
+            ck.access("q_col", rc, np.where(ok, kr * M + 16 * jr, DEAD), 16, ok,
+                      (k0 + kr) * M + mt + 16 * jr)
         # ---- srow_flush
         nb = -(-K // 32)
         if tiled:
@@ -248,6 +261,101 @@ def mx_model(M, K, op="plain", tiled=False, ck=None):
             rs_ = Desc(k0 * nblk + first, K * nblk)
             scale_rows(ck, "s_col", rs_, k0, K, nblk, first, count)
     return ck
+
+
+def model_col_flush_q_rag(base, M, K, tm, tk, first, last):
+    """col_flush_q_rag (mx_cast.h): the transposed tile of sub-tile tm of
+    strip tk when transposed rows start at any byte -- each row's whole
+    128-byte line around the sub-tile's first byte, 16-byte pieces, bytes
+    outside the walk left alone -- as (site, descriptor, offsets, bytes, live,
+    address) with addresses counted from the start of the tensor's (or
+    group's) q_col, which lies at `base` modulo 128."""
+    t = np.arange(THREADS)
+    j = t & 7
+    mt, k0 = tm * TILE_M, tk * TILE_K
+    rem = min(M - mt, TILE_M)
+    d0 = (base + k0 * M) % 128
+    # make_rsrc(row0 - d0, mt, (K - k0) * M + d0), row0 = q_col + k0 M
+    d = Desc(k0 * M - d0 + mt, K * M)
+    lo = 0 if first else -TILE_M
+    out = []
+    for i in range(TILE_K // 32):
+        kr = (t >> 3) + 32 * i
+        at = d0 + kr * M
+        sft = at % 128
+        p0 = 16 * j - sft
+        whole = (k0 + kr < K) & (p0 >= lo) & (p0 + 16 <= rem)
+        out.append(("q_col rag W=16", d, np.where(whole, at - sft + 16 * j, DEAD), 16, whole,
+                    (k0 + kr) * M + mt + p0))
+    if not (first or last):
+        return out
+    # the walk's ends, row t per thread
+    kr = t
+    row_ok = k0 + kr < K
+    at = d0 + kr * M
+    sft = at % 128
+    line = at - sft
+    qa, qb = sft >> 4, (rem - 1 + sft) >> 4
+    head = first & row_ok & (sft % 16 != 0)
+    tail = last & row_ok & ((rem + sft) % 16 != 0) & ~(head & (qb == qa))
+    for on, q in ((head, qa), (tail, qb)):
+        p0 = 16 * q - sft
+        for b in range(16):
+            ok = on & (p0 + b >= lo) & (p0 + b < rem)
+            out.append(("q_col rag W=1", d, np.where(ok, line + 16 * q + b, DEAD), 1, ok,
+                        (k0 + kr) * M + mt + p0 + b))
+    if last:
+        for q in range(8, 16):
+            p0 = 16 * q - sft
+            whole = row_ok & (p0 + 16 <= rem)
+            out.append(("q_col rag W=16", d, np.where(whole, line + 16 * q, DEAD), 16, whole,
+                        (k0 + kr) * M + mt + p0))
+    return out
+
+
+RAG_STACKS = [([1], 8), ([17], 24), ([129], 256), ([300], 264), ([255, 1], 8), ([16, 8], 256),
+              ([1, 17, 0, 300, 129, 5], 40), ([1104, 3008, 1072, 6563, 1], 8),
+              ([250, 131, 9], 520)]
+
+
+@pytest.mark.parametrize("base", [0, 5, 16, 127])
+@pytest.mark.parametrize("L", [1, 2, 3, 14])
+@pytest.mark.parametrize("rows,K", RAG_STACKS)
+def test_ragged_transposed_writes_every_byte_once(rows, K, L, base):
+    """col_flush_q_rag over every walk of walk length L of every group of a
+    stack (the groups' [K][rows] transposes one after the other, the stack's
+    q_col at `base` modulo 128): every byte written exactly once, 16-byte
+    stores aligned, away from walk ends only in whole lines, every access
+    inside its descriptor."""
+    total = K * sum(rows)
+    count = np.zeros(total, np.int64)
+    ck = Checker()
+    r0 = 0
+    for M in rows:
+        if M == 0:
+            continue
+        gbase = (base + K * r0) % 128
+        tiles_m, tiles_k = -(-M // TILE_M), -(-K // TILE_K)
+        for w in range(-(-tiles_m // L)):
+            n = min(L, tiles_m - w * L)
+            for tk in range(tiles_k):
+                for g in range(n):
+                    for site, d, off, nb_, live, addr in model_col_flush_q_rag(
+                            gbase, M, K, w * L + g, tk, g == 0, g == n - 1):
+                        ck.access(site, d, off, nb_, live, addr)
+                        a = np.broadcast_to(addr, live.shape)[live]
+                        assert (a >= 0).all()
+                        if nb_ == 16:
+                            assert ((gbase + a) % 16 == 0).all(), "16-byte store not aligned"
+                            if 0 < g < n - 1 and a.size:
+                                # a sub-tile inside the walk writes each row's line whole
+                                lines = (gbase + a) // 128
+                                assert (np.bincount(lines - lines.min()) % 8 == 0).all()
+                        for b in range(nb_):
+                            np.add.at(count, K * r0 + a + b, 1)
+        r0 += M
+    ck.ok()
+    assert (count == 1).all(), (int((count == 0).sum()), int((count > 1).sum()))
 
 
 def scale_rows(ck, site, rs, k0, K, pitch, first, count, base_align=0):
@@ -339,7 +447,10 @@ def nv_model(M, K, ck=None):
 MAXD = 1 << 23
 
 MX_SHAPES = [(MAXD, 32), (MAXD, 8), (MAXD - 16, 40), (32, MAXD), (16, MAXD), (128, MAXD),
-             (144, MAXD - 8), (1 << 17, MAXD), (MAXD, 1 << 17), (16400, 7176), (16384, 16384)]
+             (144, MAXD - 8), (1 << 17, MAXD), (MAXD, 1 << 17), (16400, 7176), (16384, 16384),
+             # rows that are not multiples of 16: transposed rows at any byte
+             (MAXD - 1, 8), (MAXD - 1, 1 << 17), ((1 << 17) - 1, MAXD), (1, MAXD), (17, MAXD - 8),
+             (16383, 16384), (129, 7168)]
 
 
 @pytest.mark.parametrize("tiled", [False, True], ids=["compact", "tiled"])
@@ -352,7 +463,8 @@ def test_mx_quantize_offsets(M, K, op, tiled):
 # gated: the quantised tensor is [M][N] with N <= 2^22 (full row 2N <= 2^23);
 # gated backward: [M][2N].
 GATED_N = [(MAXD, 8), (128, 1 << 22), (144, (1 << 22) - 8), (1 << 17, 1 << 22),
-           (16, 1 << 22), (8192, 4096), (16400, 3592)]
+           (16, 1 << 22), (8192, 4096), (16400, 3592), (MAXD - 1, 8), (129, 1 << 22),
+           (8191, 4096)]
 
 
 @pytest.mark.parametrize("tiled", [False, True], ids=["compact", "tiled"])

@@ -82,10 +82,23 @@ CONFIGS = {
     # the any-shape kernels: rows and row lengths that are not multiples of 16 and 8
     "mxfp8_dim0_dim1_16383": ("c2_dim1_16384", (16383, 16383), "mx", 3),
     "nvfp4_16383": ("c5_nvfp4_16384", (16383, 16383), "nvfp4", 3),
+    # rows that are not multiples of 16, row lengths that are multiples of 8
+    # (MXFP8: the tiled kernel, transposed rows at any byte)
+    "mxfp8_dim0_dim1_16383x16384": ("c2_dim1_16384", (16383, 16384), "mx", 3),
+    "mxfp8_grouped_ragged_8x_16384x7168": ("f4_grouped_moe", (16384, 7168), "mx_grouped", 3),
+    "nvfp4_grouped_ragged_8x_16384x7168": ("f4_grouped_moe", (16384, 7168), "nvfp4_grouped", 3),
 }
 
-# Row counts of the 8 experts in the grouped workloads.
+# Row counts of the 8 experts in the grouped workloads: shares of a seeded
+# Dirichlet draw, rounded down to multiples of 16 -- or, for the ragged
+# workloads, not rounded (the token counts of a real MoE layer).
 MOE_GROUPS = dict(groups=8, seed=8)
+MOE_RAGGED = ("mxfp8_grouped_ragged_8x_16384x7168", "nvfp4_grouped_ragged_8x_16384x7168")
+
+
+def group_rows(config, M):
+    import workloads as W
+    return W.moe_group_rows(M, **MOE_GROUPS, step=1 if config in MOE_RAGGED else 16)
 
 # MXFP8 flags OR-ed into the axis mask (E5M2 elements = 4, round-up E8M0
 # rule = 8, GEMM-ready tiled scales = 16), and the format each plain MXFP8
@@ -215,7 +228,7 @@ def main():
 
     # outputs and workspace allocated once, outside the timed region
     if kind == "mx_grouped":
-        grp_rows = W.moe_group_rows(M, **MOE_GROUPS)
+        grp_rows = group_rows(args.config, M)
         out = mx.mx_quantize_grouped(x, grp_rows)
         step = lambda: mx.mx_quantize_grouped(x, grp_rows, out=out)
         nbk = -(-K // 32)
@@ -224,7 +237,7 @@ def main():
                     directions="row+col per group", format="mxfp8 e4m3 + e8m0")
     elif kind == "mx_grouped_swiglu":
         # an MoE layer's expert FFN input [gate | linear] (N = K / 2 per half)
-        grp_rows = W.moe_group_rows(M, **MOE_GROUPS)
+        grp_rows = group_rows(args.config, M)
         out = mx.mx_quantize_gated_grouped(x, grp_rows, mx.GATED_SWIGLU)
         step = lambda: mx.mx_quantize_gated_grouped(x, grp_rows, mx.GATED_SWIGLU, out=out)
         N = K // 2
@@ -234,13 +247,15 @@ def main():
                     directions="row+col per group", format="mxfp8 e4m3 + e8m0",
                     activation="swiglu")
     elif kind == "nvfp4_grouped":
-        grp_rows = W.moe_group_rows(M, **MOE_GROUPS)
+        grp_rows = group_rows(args.config, M)
         amax = mx.mx_absmax_bf16_grouped(x, grp_rows)
         pre_pass = ("absmax (per group)", lambda: mx.mx_absmax_bf16_grouped(x, grp_rows, out=amax),
                     2 * M * K)
         out = mx.nvfp4_quantize_transpose_grouped(x, grp_rows, amax)
         step = lambda: mx.nvfp4_quantize_transpose_grouped(x, grp_rows, amax, out=out)
-        alg_bytes = nvfp4_bytes(M, K, 2)
+        # each group's transpose: [K][ceil(m/2)] codes, [K][ceil(m/16)] scales
+        alg_bytes = nvfp4_bytes(M, K, 2) - K * (-(-M // 2) + -(-M // 16)) + \
+            K * sum(-(-m // 2) + -(-m // 16) for m in grp_rows)
         desc = dict(workload=args.config, M=M, K=K, groups=grp_rows, block=16,
                     directions="row+transpose per group",
                     format="nvfp4 (e2m1 + e4m3 scales + fp32 scale per group)")
@@ -420,13 +435,13 @@ def main():
         c0 = time.process_time()
         t0 = time.perf_counter()
         if kind == "mx_grouped":
-            O.mx_quantize_grouped(xs, W.moe_group_rows(M, **MOE_GROUPS))
+            O.mx_quantize_grouped(xs, group_rows(args.config, M))
             sb = alg_bytes
         elif kind == "nvfp4_grouped":
-            O.nvfp4_quantize_transpose_grouped(xs, W.moe_group_rows(M, **MOE_GROUPS))
+            O.nvfp4_quantize_transpose_grouped(xs, group_rows(args.config, M))
             sb = alg_bytes
         elif kind == "mx_grouped_swiglu":
-            O.mx_quantize_gated_grouped(xs, W.moe_group_rows(M, **MOE_GROUPS), mx.GATED_SWIGLU)
+            O.mx_quantize_gated_grouped(xs, group_rows(args.config, M), mx.GATED_SWIGLU)
             sb = alg_bytes
         elif kind.startswith("nvfp4"):
             O.nvfp4_quantize_transpose(xs, tensor_amax=O.absmax(x_h), two_d=kind == "nvfp4_2d")

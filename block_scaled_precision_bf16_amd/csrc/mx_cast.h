@@ -366,7 +366,8 @@ __device__ __forceinline__ uint8_t byte_of(uint4 v, int b)
 // sub-tile also writes the line after, up to the row's end (rem bytes of the
 // sub-tile); the pieces holding other bytes as well -- at most one at each
 // end of a row -- leave byte by byte, at those two sub-tiles only.  Thread t
-// writes piece t % 8 of rows t / 8 + 32 i, and the ends of row t.
+// writes piece t % 8 of rows t / 8 + 32 i (and of the line after), and byte
+// t % 16 of the end pieces of rows t / 16 + 16 i.
 
 // The 16 bytes at position u (0 <= u < 384) of row kr in the sequence: the
 // previous sub-tile's 128 bytes, the current one's 128, then 128 unstaged
@@ -413,44 +414,46 @@ __device__ __forceinline__ void col_flush_q_rag(const MxArgs &a, const ColStageT
         const bool whole = k0 + kr < a.K && p0 >= lo && p0 + 16 <= rem;
         buf_store16<AUX>(rc, whole ? at - (uint32_t)sft + 16u * j : kDead, v);
     }
-    if (!(first || last))
-        return;
-    // the walk's ends, one row per thread: at the first sub-tile the piece
-    // that holds the row's first byte (if it starts before it), at the last
-    // one the piece that holds its last byte (if it ends after it), byte by
-    // byte, and the whole pieces of the line after
-    const int kr = t;
-    const bool row_ok = k0 + kr < a.K;
-    const uint32_t at = base + (uint32_t)kr * M;
-    const int sft = (int)(at & 127u);
-    const uint32_t line = at - (uint32_t)sft;
-    const int qa = sft >> 4;                                   // piece of the first byte
-    const int qb = (rem - 1 + sft) >> 4;                       // piece of the last byte
-    const bool head = first && row_ok && (sft & 15) != 0;
-    const bool tail = last && row_ok && ((rem + sft) & 15) != 0 && !(head && qb == qa);
+    if (last) {
+        // the line after, whole pieces (the same lanes per row)
 #pragma unroll
-    for (int e = 0; e < 2; e++) {
-        const bool on = e == 0 ? head : tail;
-        if (__builtin_amdgcn_ballot_w64(on) == 0)
-            continue;
-        const int q = e == 0 ? qa : qb;
-        const int p0 = 16 * q - sft;
-        const uint4 v = rag_bytes(prev, cur, kr, p0 + kTileM);
-#pragma unroll
-        for (int b = 0; b < 16; b++) {
-            const bool ok = on && p0 + b >= lo && p0 + b < rem;
-            buf_store1(rc, ok ? line + 16u * q + b : kDead, byte_of(v, b));
+        for (int i = 0; i < kTileK / 32; i++) {
+            const int kr = (t >> 3) + 32 * i;
+            const uint32_t at = base + (uint32_t)kr * M;
+            const int sft = (int)(at & 127u);
+            const int p0 = kTileM + 16 * j - sft;
+            const bool whole = k0 + kr < a.K && p0 + 16 <= rem;
+            buf_store16<AUX>(rc, whole ? at - (uint32_t)sft + (uint32_t)(kTileM + 16 * j) : kDead,
+                             rag_bytes(prev, cur, kr, p0 + kTileM));
         }
     }
-    if (!last)
+    if (!(first || last))
         return;
-#pragma unroll 1
-    for (int q = 8; q < 16; q++) {
-        const int p0 = 16 * q - sft;
-        const bool whole = row_ok && p0 + 16 <= rem;
-        if (__builtin_amdgcn_ballot_w64(whole) == 0)
+    // the walk's ends byte by byte: at the first sub-tile the piece that holds
+    // a row's first byte (if it starts before it), at the last the piece that
+    // holds its last byte (if it ends after it); 16 lanes per row, one byte
+    // each, so that a store touches 4 lines
+    const int b = t & 15;
+    for (int e = 0; e < 2; e++) {
+        if (e == 0 ? !first : !last)
             continue;
-        buf_store16<AUX>(rc, whole ? line + 16u * q : kDead, rag_bytes(prev, cur, kr, p0 + kTileM));
+#pragma unroll 4
+        for (int i = 0; i < kTileK / 16; i++) {
+            const int kr = (t >> 4) + 16 * i;
+            const uint32_t at = base + (uint32_t)kr * M;
+            const int sft = (int)(at & 127u);
+            const int q = e == 0 ? sft >> 4 : (rem - 1 + sft) >> 4;
+            const bool edge = e == 0 ? (sft & 15) != 0
+                                     : ((rem + sft) & 15) != 0 && !(first && q == (sft >> 4) && (sft & 15));
+            const int p = 16 * q - sft + b;                        // the byte's place in the segment
+            const bool ok = k0 + kr < a.K && edge && p >= lo && p < rem;
+            if (__builtin_amdgcn_ballot_w64(ok) == 0)
+                continue;
+            const int u = ok ? p + kTileM : 0, c = u >> 4;   // 0 <= u < 256 where ok
+            const uint8_t *src = reinterpret_cast<const uint8_t *>(
+                c < 8 ? &prev[kr][stage_chunk(kr, c)] : &cur[kr][stage_chunk(kr, (c - 8) & 7)]);
+            buf_store1(rc, ok ? at - (uint32_t)sft + (uint32_t)(16 * q + b) : kDead, src[u & 15]);
+        }
     }
 }
 

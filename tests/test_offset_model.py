@@ -287,29 +287,38 @@ def model_col_flush_q_rag(base, M, K, tm, tk, first, last):
         whole = (k0 + kr < K) & (p0 >= lo) & (p0 + 16 <= rem)
         out.append(("q_col rag W=16", d, np.where(whole, at - sft + 16 * j, DEAD), 16, whole,
                     (k0 + kr) * M + mt + p0))
+    if last:
+        # the line after, whole pieces, the same lanes
+        for i in range(TILE_K // 32):
+            kr = (t >> 3) + 32 * i
+            at = d0 + kr * M
+            sft = at % 128
+            p0 = TILE_M + 16 * j - sft
+            whole = (k0 + kr < K) & (p0 + 16 <= rem)
+            out.append(("q_col rag W=16", d, np.where(whole, at - sft + TILE_M + 16 * j, DEAD), 16,
+                        whole, (k0 + kr) * M + mt + p0))
     if not (first or last):
         return out
-    # the walk's ends, row t per thread
-    kr = t
-    row_ok = k0 + kr < K
-    at = d0 + kr * M
-    sft = at % 128
-    line = at - sft
-    qa, qb = sft >> 4, (rem - 1 + sft) >> 4
-    head = first & row_ok & (sft % 16 != 0)
-    tail = last & row_ok & ((rem + sft) % 16 != 0) & ~(head & (qb == qa))
-    for on, q in ((head, qa), (tail, qb)):
-        p0 = 16 * q - sft
-        for b in range(16):
-            ok = on & (p0 + b >= lo) & (p0 + b < rem)
-            out.append(("q_col rag W=1", d, np.where(ok, line + 16 * q + b, DEAD), 1, ok,
-                        (k0 + kr) * M + mt + p0 + b))
-    if last:
-        for q in range(8, 16):
-            p0 = 16 * q - sft
-            whole = row_ok & (p0 + 16 <= rem)
-            out.append(("q_col rag W=16", d, np.where(whole, line + 16 * q, DEAD), 16, whole,
-                        (k0 + kr) * M + mt + p0))
+    # the end pieces byte by byte: 16 lanes per row
+    b = t & 15
+    for e in (0, 1):
+        if (e == 0 and not first) or (e == 1 and not last):
+            continue
+        for i in range(TILE_K // 16):
+            kr = (t >> 4) + 16 * i
+            at = d0 + kr * M
+            sft = at % 128
+            qa = sft >> 4
+            if e == 0:
+                q = qa
+                edge = sft % 16 != 0
+            else:
+                q = (rem - 1 + sft) >> 4
+                edge = ((rem + sft) % 16 != 0) & ~(first & (q == qa) & (sft % 16 != 0))
+            p = 16 * q - sft + b
+            ok = (k0 + kr < K) & edge & (p >= lo) & (p < rem)
+            out.append(("q_col rag W=1", d, np.where(ok, at - sft + 16 * q + b, DEAD), 1, ok,
+                        (k0 + kr) * M + mt + p))
     return out
 
 

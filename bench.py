@@ -83,10 +83,11 @@ CONFIGS = {
     "mxfp8_dim0_dim1_16383": ("c2_dim1_16384", (16383, 16383), "mx", 3),
     "nvfp4_16383": ("c5_nvfp4_16384", (16383, 16383), "nvfp4", 3),
     # rows that are not multiples of 16, row lengths that are multiples of 8
-    # (MXFP8: the tiled kernel, transposed rows at any byte)
+    # (MXFP8) or 16 (NVFP4): the tiled kernels, transposed rows at any byte
     "mxfp8_dim0_dim1_16383x16384": ("c2_dim1_16384", (16383, 16384), "mx", 3),
     "mxfp8_grouped_ragged_8x_16384x7168": ("f4_grouped_moe", (16384, 7168), "mx_grouped", 3),
     "nvfp4_grouped_ragged_8x_16384x7168": ("f4_grouped_moe", (16384, 7168), "nvfp4_grouped", 3),
+    "nvfp4_16383x16384": ("c5_nvfp4_16384", (16383, 16384), "nvfp4", 3),
 }
 
 # Row counts of the 8 experts in the grouped workloads: shares of a seeded

@@ -216,11 +216,14 @@ bool build_groups(const int64_t *rows, int G, int64_t K, int op, bool dbias, boo
 
 // Group table of a grouped NVFP4 cast or absmax: any group sizes (empty
 // groups allowed); walks per group with the walk length of the whole stack.
-// any is set when the stack goes to the any-shape kernel: some group's rows
-// or K are not multiples of 16.  Each group's q_col and s_col start after the
-// previous groups' [K][ceil(rows/2)] and [K][ceil(rows/16)] bytes.
-bool build_nv_groups(const int64_t *rows, int G, int64_t K, mxk::GroupTable &gt, int64_t &M,
-                     int &group, bool &any)
+// any is set when the stack goes to the any-shape kernel: K is not a
+// multiple of 16.  rag is set when the transposed output (col) is written and
+// some group's rows are not multiples of 16, so that the groups' transposed
+// rows may start at any byte; walks are then even, at most kMaxNvRagGroup
+// sub-tiles.  Each group's q_col and s_col start after the previous groups'
+// [K][ceil(rows/2)] and [K][ceil(rows/16)] bytes.
+bool build_nv_groups(const int64_t *rows, int G, int64_t K, bool col, mxk::GroupTable &gt,
+                     int64_t &M, int &group, bool &any, bool &rag)
 {
     if (!rows || G < 1 || G > mxk::kMaxGroups)
         return false;
@@ -234,12 +237,16 @@ bool build_nv_groups(const int64_t *rows, int G, int64_t K, mxk::GroupTable &gt,
     }
     if (M <= 0 || M > kMaxDim || !mx_size_ok(M, K))
         return false;
-    any = !(rows16 && K % 16 == 0);
+    any = K % 16 != 0;
+    rag = !any && !rows16 && col;
     int tm[mxk::kMaxGroups];
     for (int g = 0; g < G; g++)
         tm[g] = tiles(rows[g], any ? mxk::kAnyTileM : mxk::kTileM);
     gt = mxk::GroupTable{};
-    group = any ? mxk::any_walk_len(rows, G, K) : mxk::pick_group_rounds(tm, G, tiles(K, mxk::kTileK), 2, 1);
+    const int tk = tiles(K, mxk::kTileK);
+    group = any ? mxk::any_walk_len(rows, G, K)
+                : rag ? mxk::pick_group_rounds(tm, G, tk, 2, 2, mxk::kMaxNvRagGroup)
+                      : mxk::pick_group_rounds(tm, G, tk, 2, 1);
     for (int g = 0; g < G; g++)
         gt.len[g] = group;
     gt.count = G;
@@ -367,7 +374,23 @@ static mx_status nvfp4_impl(bool two_d, const void *x, int64_t M, int64_t K, con
     a.q_col = q_col;
     a.s_col = s_col;
     a.sg_out = global_scale_out;
-    if (M % 16 != 0 || K % 16 != 0) {
+    if (K % 16 == 0 && M % 16 != 0 && col) {
+        // transposed rows at any byte: the tiled kernel's variant for them,
+        // the tensor as a stack of one group (even walks of at most
+        // kMaxNvRagGroup sub-tiles)
+        a.tiles_k = tiles(K, mxk::kTileK);
+        a.tiles_m = tiles(M, mxk::kTileM);
+        mxk::plan_walks(&a.tiles_m, 1, a.tiles_k, mxk::kTargetWorkgroups, true, &a.group,
+                        mxk::kMaxNvRagGroup);
+        a.groups_m = (a.tiles_m + a.group - 1) / a.group;
+        mxk::GroupTable gt{};
+        gt.count = 1;
+        gt.len[0] = a.group;
+        gt.walk0[1] = a.groups_m;
+        gt.row0[1] = M;
+        return from_hip(mxk::launch_nvfp4_ragged(axis_mask, two_d, a, gt, stream));
+    }
+    if (K % 16 != 0) {
         const mxk::GroupTable gt = any_table(M, K);   // offsets 0: one tensor
         a.tiles_k = tiles(K, mxk::kAnyTileK);
         a.tiles_m = tiles(M, mxk::kAnyTileM);
@@ -845,8 +868,8 @@ mx_status mx_absmax_bf16_grouped(const void *x, int64_t K, const int64_t *group_
     mxk::GroupTable gt;
     int64_t M;
     int group;
-    bool any;
-    if (!build_nv_groups(group_rows, G, K, gt, M, group, any))
+    bool any, rag;
+    if (!build_nv_groups(group_rows, G, K, false, gt, M, group, any, rag))
         return MX_ERR_SHAPE;
     if (!aligned(x, 16) || !aligned(amax, 4))
         return MX_ERR_ALIGN;
@@ -872,8 +895,8 @@ mx_status nvfp4_quantize_transpose_grouped(const void *x, int64_t K, const int64
     mxk::GroupTable gt;
     int64_t M;
     int group;
-    bool any;
-    if (!build_nv_groups(group_rows, G, K, gt, M, group, any))
+    bool any, rag;
+    if (!build_nv_groups(group_rows, G, K, col, gt, M, group, any, rag))
         return MX_ERR_SHAPE;
     if (!aligned(x, 16) || !aligned(amax, 4) ||
         (row && (!aligned(q_row, 16) || !aligned(s_row, 16))) ||
@@ -906,7 +929,8 @@ mx_status nvfp4_quantize_transpose_grouped(const void *x, int64_t K, const int64
     a.groups_m = gt.walk0[G];
     if (any)
         return from_hip(mxk::launch_nvfp4_any(axis_mask, scaling_2d != 0, a, gt, stream));
-    return from_hip(mxk::launch_nvfp4_grouped(axis_mask, scaling_2d != 0, a, gt, stream));
+    return from_hip((rag ? mxk::launch_nvfp4_ragged : mxk::launch_nvfp4_grouped)(
+        axis_mask, scaling_2d != 0, a, gt, stream));
 }
 
 mx_status nvfp4_quantize_transpose_2d(const void *x, int64_t M, int64_t K, const float *amax,

@@ -36,6 +36,9 @@ constexpr int kTileK = kColsPerLane * 32;          // 256
 // workgroups' LDS into a CU's 160 KB).
 constexpr int kMaxGroup = 16;
 constexpr int kMaxRagGroup = 14;
+// The same for the NVFP4 cast (its stage holds two pairs of sub-tiles, and
+// walks are even there so that each pair lies in one walk).
+constexpr int kMaxNvRagGroup = 4;
 // Workgroups the host aims to launch at least: two per MI355X compute unit
 // for the plain cast (bound by memory, two resident per CU) and for the casts
 // with dbias; four for the other fused casts (bound by their arithmetic,
@@ -256,6 +259,12 @@ hipError_t launch_absmax(const uint16_t *x, int64_t n, float *amax, hipStream_t 
 hipError_t launch_nvfp4(unsigned axis, bool two_d, const Nv4Args &a, hipStream_t s);
 hipError_t launch_nvfp4_grouped(unsigned axis, bool two_d, const Nv4Args &a, const GroupTable &gt,
                                 hipStream_t s);
+// launch_nvfp4_grouped for stacks whose transposed rows may start at any
+// byte (a group's rows, or the rows before it, not multiples of 16; K a
+// multiple of 16); axis must include the transposed output; gt holds each
+// group's q_col and s_col offsets.  A single tensor is a stack of one group.
+hipError_t launch_nvfp4_ragged(unsigned axis, bool two_d, const Nv4Args &a, const GroupTable &gt,
+                               hipStream_t s);
 hipError_t launch_absmax_grouped(const uint16_t *x, int64_t K, const GroupTable &gt, float *amax,
                                  hipStream_t s);
 // NVFP4 of any shape (nvfp4_any.hip): a.tiles_k = ceil(K / kAnyTileK); gt as

@@ -41,6 +41,7 @@
 #include "bufio.h"
 #include "device_math.h"
 #include "launch.h"
+#include "rag_flush.h"
 #include "stage_flush.h"
 
 namespace mxk {
@@ -329,132 +330,39 @@ __device__ __forceinline__ void col_flush_q(const MxArgs &a, const ColStage &st,
     }
 }
 
-// Bytes s .. s + 15 (0 <= s < 16) of the 32 bytes p (bytes 0-15) and c
-// (bytes 16-31): the dword shift in two rounds of selects, then the byte
-// shift.  Written on named words, not an array: the compiler turns selects
-// among an array's elements into an indexed load from scratch memory.
-__device__ __forceinline__ uint4 window16(uint4 p, uint4 c, uint32_t s)
-{
-    const bool d1 = (s & 4u) != 0, d2 = (s & 8u) != 0;
-    const uint32_t y0 = d1 ? p.y : p.x, y1 = d1 ? p.z : p.y, y2 = d1 ? p.w : p.z;
-    const uint32_t y3 = d1 ? c.x : p.w, y4 = d1 ? c.y : c.x, y5 = d1 ? c.z : c.y;
-    const uint32_t y6 = d1 ? c.w : c.z;
-    const uint32_t x0 = d2 ? y2 : y0, x1 = d2 ? y3 : y1, x2 = d2 ? y4 : y2;
-    const uint32_t x3 = d2 ? y5 : y3, x4 = d2 ? y6 : y4;
-    const uint32_t sh = s & 3u;
-    return make_uint4(__builtin_amdgcn_alignbyte(x1, x0, sh), __builtin_amdgcn_alignbyte(x2, x1, sh),
-                      __builtin_amdgcn_alignbyte(x3, x2, sh), __builtin_amdgcn_alignbyte(x4, x3, sh));
-}
+// The staged transposed tiles of a ragged MXFP8 walk, as rag_flush.h reads
+// them: prev (the previous sub-tile's) and cur.
+struct MxRagView {
+    const StageTile &prev, &cur;
+    __device__ __forceinline__ uint4 chunk(int kr, int c) const
+    {
+        return c < 8 ? prev[kr][stage_chunk(kr, c)] : cur[kr][stage_chunk(kr, (c - 8) & 7)];
+    }
+    __device__ __forceinline__ uint8_t byte(int kr, int u) const
+    {
+        const int c = u >> 4;
+        const uint4 *p = c < 8 ? &prev[kr][stage_chunk(kr, c)] : &cur[kr][stage_chunk(kr, (c - 8) & 7)];
+        return reinterpret_cast<const uint8_t *>(p)[u & 15];
+    }
+};
 
-// Byte b (a constant once unrolled) of v.
-__device__ __forceinline__ uint8_t byte_of(uint4 v, int b)
-{
-    const uint32_t d = b < 4 ? v.x : b < 8 ? v.y : b < 12 ? v.z : v.w;
-    return (uint8_t)(d >> (8 * (b & 3)));
-}
-
-// The staged transposed tile of sub-tile g of a walk when transposed rows
+// The staged transposed tile of sub-tile g of a walk whose transposed rows
 // start at any byte (the tensor's M, or the rows before its group, not a
-// multiple of 16).  Row kr's bytes of a sub-tile start at an address whose
-// offset sft within its 128-byte line is the same at every sub-tile of the
-// walk (they lie 128 bytes apart), so the sub-tile writes the whole line that
-// starts sft bytes before its first byte: the previous sub-tile's last sft
-// bytes (still in the other stage tile) and its own first 128 - sft, as 8
-// aligned 16-byte pieces.  Its own last sft bytes go out with the next
-// sub-tile.  Only bytes of the walk are written: at its first sub-tile the
-// sft bytes before it belong to the walk or group before, and its last
-// sub-tile also writes the line after, up to the row's end (rem bytes of the
-// sub-tile); the pieces holding other bytes as well -- at most one at each
-// end of a row -- leave byte by byte, at those two sub-tiles only.  Thread t
-// writes piece t % 8 of rows t / 8 + 32 i (and of the line after), and byte
-// t % 16 of the end pieces of rows t / 16 + 16 i.
-
-// The 16 bytes at position u (0 <= u < 384) of row kr in the sequence: the
-// previous sub-tile's 128 bytes, the current one's 128, then 128 unstaged
-// bytes (any value).
-__device__ __forceinline__ uint4 rag_bytes(const StageTile &prev, const StageTile &cur, int kr,
-                                           int u)
-{
-    const int qa = u >> 4, qb = qa + 1;
-    const uint4 *pa = qa < 8 ? &prev[kr][stage_chunk(kr, qa)] : &cur[kr][stage_chunk(kr, (qa - 8) & 7)];
-    const uint4 *pb = qb < 8 ? &prev[kr][stage_chunk(kr, qb)] : &cur[kr][stage_chunk(kr, (qb - 8) & 7)];
-    return window16(*pa, *pb, (uint32_t)(u & 15));
-}
-
+// multiple of 16): sub-tiles are the steps of rag_flush_lines.
 template <int AUX>
 __device__ __forceinline__ void col_flush_q_rag(const MxArgs &a, const ColStageT<true> &st, int tm,
                                                 int tk, int g, bool first, bool last)
 {
-    const int t = (int)threadIdx.x;
-    const int j = t & 7;
     const int64_t mt = (int64_t)tm * kTileM;
     const int64_t k0 = (int64_t)tk * kTileK;
     const int rem = a.M - mt < kTileM ? (int)(a.M - mt) : kTileM;   // the sub-tile's bytes per row
-    const StageTile &cur = st.q[g & 1], &prev = st.q[(g & 1) ^ 1];
     // descriptor from the line boundary at or below this sub-tile's first byte
     // of row k0; a row's offset d0 + kr M is below 255 * 2^23 + 128
     const uint8_t *row0 = a.q_col + k0 * a.M;
     const uint32_t d0 = (uint32_t)(reinterpret_cast<uintptr_t>(row0) & 127u);
     const rsrc_t rc = make_rsrc(row0 - d0, mt, (a.K - k0) * a.M + d0);
-    const uint32_t M = (uint32_t)a.M;
-    // the rows' offsets are the same at every sub-tile; kept opaque here, they
-    // are formed again each time instead of being held across the walk
-    uint32_t base = d0;
-    asm volatile("" : "+v"(base));
-    // bytes lo .. rem - 1 of the sub-tile's row segment are its to write
-    // (negative: the previous sub-tile's)
-    const int lo = first ? 0 : -kTileM;
-#pragma unroll
-    for (int i = 0; i < kTileK / 32; i++) {
-        const int kr = (t >> 3) + 32 * i;
-        const uint32_t at = base + (uint32_t)kr * M;      // the row's first byte of the sub-tile
-        const int sft = (int)(at & 127u);
-        const int p0 = 16 * j - sft;                       // the piece's first byte in the segment
-        const uint4 v = rag_bytes(prev, cur, kr, p0 + kTileM);
-        const bool whole = k0 + kr < a.K && p0 >= lo && p0 + 16 <= rem;
-        buf_store16<AUX>(rc, whole ? at - (uint32_t)sft + 16u * j : kDead, v);
-    }
-    if (last) {
-        // the line after, whole pieces (the same lanes per row)
-#pragma unroll
-        for (int i = 0; i < kTileK / 32; i++) {
-            const int kr = (t >> 3) + 32 * i;
-            const uint32_t at = base + (uint32_t)kr * M;
-            const int sft = (int)(at & 127u);
-            const int p0 = kTileM + 16 * j - sft;
-            const bool whole = k0 + kr < a.K && p0 + 16 <= rem;
-            buf_store16<AUX>(rc, whole ? at - (uint32_t)sft + (uint32_t)(kTileM + 16 * j) : kDead,
-                             rag_bytes(prev, cur, kr, p0 + kTileM));
-        }
-    }
-    if (!(first || last))
-        return;
-    // the walk's ends byte by byte: at the first sub-tile the piece that holds
-    // a row's first byte (if it starts before it), at the last the piece that
-    // holds its last byte (if it ends after it); 16 lanes per row, one byte
-    // each, so that a store touches 4 lines
-    const int b = t & 15;
-    for (int e = 0; e < 2; e++) {
-        if (e == 0 ? !first : !last)
-            continue;
-#pragma unroll 4
-        for (int i = 0; i < kTileK / 16; i++) {
-            const int kr = (t >> 4) + 16 * i;
-            const uint32_t at = base + (uint32_t)kr * M;
-            const int sft = (int)(at & 127u);
-            const int q = e == 0 ? sft >> 4 : (rem - 1 + sft) >> 4;
-            const bool edge = e == 0 ? (sft & 15) != 0
-                                     : ((rem + sft) & 15) != 0 && !(first && q == (sft >> 4) && (sft & 15));
-            const int p = 16 * q - sft + b;                        // the byte's place in the segment
-            const bool ok = k0 + kr < a.K && edge && p >= lo && p < rem;
-            if (__builtin_amdgcn_ballot_w64(ok) == 0)
-                continue;
-            const int u = ok ? p + kTileM : 0, c = u >> 4;   // 0 <= u < 256 where ok
-            const uint8_t *src = reinterpret_cast<const uint8_t *>(
-                c < 8 ? &prev[kr][stage_chunk(kr, c)] : &cur[kr][stage_chunk(kr, (c - 8) & 7)]);
-            buf_store1(rc, ok ? at - (uint32_t)sft + (uint32_t)(16 * q + b) : kDead, src[u & 15]);
-        }
-    }
+    const MxRagView v{st.q[(g & 1) ^ 1], st.q[g & 1]};
+    rag_flush_lines<AUX>(v, rc, d0, (uint32_t)a.M, a.K - k0, rem, first, last);
 }
 
 // The 4-byte word lane L of a GEMM-ready scale tile holds: bytes j = 0..3 are

@@ -23,6 +23,7 @@
 #include "device_math.h"
 #include "launch.h"
 #include "nv_block.h"
+#include "rag_flush.h"
 #include "stage_flush.h"
 
 namespace mxk {
@@ -91,12 +92,17 @@ __device__ __forceinline__ bool nv_live(const Nv4Args &a, const NvLane &l, int t
 // writes bytes 8 nv_half(kl, h & 1) of chunk 4p + h / 2.  s: the 8 column-block scales
 // per sub-tile of the whole walk, transposed (block-major, stage_flush.h).
 // srow: the 16 row-block scales per row of the current sub-tile.
-struct NvStage {
-    uint8_t q[kTileK][128];                      // 32 KB
-    uint8_t s[8 * kMaxGroup][kTileK];            // 32 KB, block-major (stage_flush.h)
-    uint8_t srow[kTileM][kTileK / 16];           // 2 KB
-    float inv[128];                              // multiplier of each scale byte
+// RAG (transposed rows at any byte, rag_flush.h): two pair tiles, the
+// current pair's and the previous one's; walks of at most kMaxNvRagGroup
+// sub-tiles keep the stage within two workgroups per CU.
+template <bool RAG>
+struct NvStageT {
+    uint8_t q[RAG ? 2 : 1][kTileK][128];                        // 32 KB each
+    uint8_t s[8 * (RAG ? kMaxNvRagGroup : kMaxGroup)][kTileK];  // 32 KB, 8 KB
+    uint8_t srow[kTileM][kTileK / 16];                          // 2 KB
+    float inv[128];                                             // multiplier of each scale byte
 };
+using NvStage = NvStageT<false>;
 
 __device__ __forceinline__ int nv_chunk(int kl, int j) { return j ^ ((kl >> 3) & 7); }
 
@@ -106,6 +112,24 @@ __device__ __forceinline__ int nv_chunk(int kl, int j) { return j ^ ((kl >> 3) &
 // and any 16 consecutive lanes write 16 different 8-byte slots of a 128-byte
 // span (no LDS bank conflict); the flush swaps them back.
 __device__ __forceinline__ int nv_half(int kl, int half) { return half ^ ((kl >> 6) & 1); }
+
+// The staged pair tiles of a ragged walk as rag_flush.h reads them, each
+// chunk's 8-byte halves back in order.
+struct NvRagView {
+    const uint8_t (*prev)[128], (*cur)[128];
+    __device__ __forceinline__ uint4 chunk(int kr, int c) const
+    {
+        const uint8_t *row = c < 8 ? prev[kr] : cur[kr];
+        const uint4 v = *reinterpret_cast<const uint4 *>(row + 16 * nv_chunk(kr, c & 7));
+        return nv_half(kr, 0) ? make_uint4(v.z, v.w, v.x, v.y) : v;
+    }
+    __device__ __forceinline__ uint8_t byte(int kr, int u) const
+    {
+        const int c = u >> 4;
+        const uint8_t *row = c < 8 ? prev[kr] : cur[kr];
+        return row[16 * nv_chunk(kr, c & 7) + ((u & 15) ^ (8 * nv_half(kr, 0)))];
+    }
+};
 
 template <int XA>
 __device__ __forceinline__ void nv_load(const Nv4Args &a, const NvLane &l, int tm, int tk,
@@ -146,7 +170,7 @@ __device__ __forceinline__ void nv_flush_q(const Nv4Args &a, const NvStage &st, 
     for (int i = 0; i < kTileK / 32; i++) {
         const int kr = (t >> 3) + 32 * i;
         const bool col_ok = in_pair && k0 + kr < a.K;
-        uint4 v = *reinterpret_cast<const uint4 *>(&st.q[kr][16 * nv_chunk(kr, jr)]);
+        uint4 v = *reinterpret_cast<const uint4 *>(&st.q[0][kr][16 * nv_chunk(kr, jr)]);
         if (nv_half(kr, 0))
             v = make_uint4(v.z, v.w, v.x, v.y);
         const uint32_t off = (uint32_t)(kr * ld) + 16 * jr;
@@ -162,14 +186,36 @@ __device__ __forceinline__ void nv_flush_q(const Nv4Args &a, const NvStage &st, 
     }
 }
 
+// Transposed output of pair pp of a walk whose transposed rows start at any
+// byte (the tensor's M, or the rows before its group, not a multiple of 16):
+// pairs are the steps of rag_flush_lines, rows of ceil(M/2) bytes.  tm: the
+// pair's first sub-tile; parts 1: the pair holds that sub-tile only.
+template <int AUX>
+__device__ __forceinline__ void nv_flush_q_rag(const Nv4Args &a, const NvStageT<true> &st, int tm,
+                                               int tk, int pp, int parts, bool first, bool last)
+{
+    const int64_t k0 = (int64_t)tk * kTileK;
+    const int64_t ld = (a.M + 1) >> 1;                        // bytes per transposed row
+    const int64_t b0 = (int64_t)tm * (kTileM / 2);             // the pair's first byte of a row
+    const int64_t cap = 64 * parts;
+    const int rem = (int)(ld - b0 < cap ? ld - b0 : cap);
+    // descriptor from the line boundary at or below the pair's first byte of
+    // row k0; a row's offset d0 + kr ld is below 255 * 2^22 + 128
+    const uint8_t *row0 = a.q_col + k0 * ld;
+    const uint32_t d0 = (uint32_t)(reinterpret_cast<uintptr_t>(row0) & 127u);
+    const rsrc_t rc = make_rsrc(row0 - d0, b0, (a.K - k0) * ld + d0);
+    const NvRagView v{st.q[(pp & 1) ^ 1], st.q[pp & 1]};
+    rag_flush_lines<AUX>(v, rc, d0, (uint32_t)ld, a.K - k0, rem, first, last);
+}
+
 // Column-block scales of the walk: 8 n bytes per column for n sub-tiles,
 // 16-byte chunks from neighbouring threads when s_col's rows allow it.
-template <int AUX>
-__device__ __forceinline__ void nv_flush_s(const Nv4Args &a, const NvStage &st, int tm0, int tk,
+template <int AUX, class Stage>
+__device__ __forceinline__ void nv_flush_s(const Nv4Args &a, const Stage &st, int tm0, int tk,
                                            int n)
 {
     const int64_t k0 = (int64_t)tk * kTileK;
-    const int64_t nblk = a.M >> 4;                             // scales per column
+    const int64_t nblk = (a.M + 15) >> 4;                      // scales per column
     const int64_t first = (int64_t)tm0 * (kTileM / 16);
     const int64_t left = nblk - first;
     const int count = (int)(left < 8 * n ? left : 8 * n);
@@ -178,8 +224,8 @@ __device__ __forceinline__ void nv_flush_s(const Nv4Args &a, const NvStage &st, 
 }
 
 // Row-block scales of sub-tile tm: thread t < 128 writes row t's 16 bytes.
-template <int AUX>
-__device__ __forceinline__ void nv_flush_srow(const Nv4Args &a, const NvStage &st, int tm, int tk)
+template <int AUX, class Stage>
+__device__ __forceinline__ void nv_flush_srow(const Nv4Args &a, const Stage &st, int tm, int tk)
 {
     const int t = (int)threadIdx.x;
     const int64_t row = (int64_t)tm * kTileM + t;
@@ -204,9 +250,9 @@ __device__ __forceinline__ void nv_flush_srow(const Nv4Args &a, const NvStage &s
 // 2D scaling: the lane's 16 rows x 8 columns and its pair lane's form one
 // 16 x 16 block; one scale and multiplier serve all its elements, in both
 // outputs.
-template <bool ROW, bool COL>
+template <bool ROW, bool COL, bool RAG>
 __device__ __forceinline__ void nv_step_2d(const Nv4Args &a, const NvLane &l,
-                                           const uint32_t (&w)[kRowsPerLane][4], NvStage &st,
+                                           const uint32_t (&w)[kRowsPerLane][4], NvStageT<RAG> &st,
                                            const DivBy &sg, rsrc_t rq, uint32_t qoff, int g)
 {
     using P = NvPolicy<ROW, COL>;
@@ -248,7 +294,8 @@ __device__ __forceinline__ void nv_step_2d(const Nv4Args &a, const NvLane &l,
             for (int q = 0; q < 2; q++)
                 o[q] = (c & 1) ? encode8_fp4_col<1>(wc, q, d, inv) : encode8_fp4_col<0>(wc, q, d, inv);
             const int kl = l.cl * kColsPerLane + c;
-            *reinterpret_cast<uint2 *>(&st.q[kl][16 * nv_chunk(kl, jr) + 8 * nv_half(kl, l.half)]) =
+            *reinterpret_cast<uint2 *>(
+                &st.q[RAG ? (g >> 1) & 1 : 0][kl][16 * nv_chunk(kl, jr) + 8 * nv_half(kl, l.half)]) =
                 make_uint2(o[0], o[1]);
         }
         // the 16 x 16 block's scale, for each of the lane's 8 columns
@@ -257,10 +304,10 @@ __device__ __forceinline__ void nv_step_2d(const Nv4Args &a, const NvLane &l,
     }
 }
 
-template <bool ROW, bool COL, bool TWO_D, int FLUSH>
+template <bool ROW, bool COL, bool TWO_D, int FLUSH, bool RAG>
 __device__ __forceinline__ void nv_step(const Nv4Args &a, const NvLane &l,
-                                        const uint32_t (&w)[kRowsPerLane][4], NvStage &st,
-                                        const DivBy &sg, int tm, int tk, int g)
+                                        const uint32_t (&w)[kRowsPerLane][4], NvStageT<RAG> &st,
+                                        const DivBy &sg, int tm, int tk, int g, int n)
 {
     using P = NvPolicy<ROW, COL>;
     const bool live = nv_live(a, l, tm, tk);
@@ -274,7 +321,7 @@ __device__ __forceinline__ void nv_step(const Nv4Args &a, const NvLane &l,
             qoff = (uint32_t)(l.row * ld) + 4 * l.cl;
     }
     if constexpr (TWO_D) {
-        nv_step_2d<ROW, COL>(a, l, w, st, sg, rq, qoff, g);
+        nv_step_2d<ROW, COL, RAG>(a, l, w, st, sg, rq, qoff, g);
     } else {
     // Rows go in pairs: both lanes of a row block know the block maxima of
     // rows r and r + 1; the even lane derives the scale of row r, the odd
@@ -371,8 +418,9 @@ __device__ __forceinline__ void nv_step(const Nv4Args &a, const NvLane &l,
                 for (int q = 0; q < 2; q++)
                     o[q] = hi ? encode8_fp4_col<1>(wc, q, d, v) : encode8_fp4_col<0>(wc, q, d, v);
                 const int kl = l.cl * kColsPerLane + c;
-                *reinterpret_cast<uint2 *>(
-                    &st.q[kl][16 * nv_chunk(kl, jr) + 8 * nv_half(kl, l.half)]) = make_uint2(o[0], o[1]);
+                *reinterpret_cast<uint2 *>(&st.q[RAG ? (g >> 1) & 1 : 0][kl][16 * nv_chunk(kl, jr) +
+                                                                  8 * nv_half(kl, l.half)]) =
+                    make_uint2(o[0], o[1]);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -382,7 +430,10 @@ __device__ __forceinline__ void nv_step(const Nv4Args &a, const NvLane &l,
     __syncthreads();
     if constexpr (ROW)
         nv_flush_srow<P::s_row>(a, st, tm, tk);
-    if constexpr (COL && FLUSH != 0)
+    if constexpr (COL && FLUSH != 0 && RAG)
+        nv_flush_q_rag<P::q_col>(a, st, FLUSH == 2 ? tm - 1 : tm, tk, g >> 1, FLUSH, g < 2,
+                                 FLUSH == 1 || g + 1 == n);
+    else if constexpr (COL && FLUSH != 0)
         nv_flush_q<P::q_col>(a, st, FLUSH == 2 ? tm - 1 : tm, tk, FLUSH, (a.M & 31) != 0);
     __syncthreads();
 }
@@ -396,7 +447,7 @@ __device__ __forceinline__ void nv_step(const Nv4Args &a, const NvLane &l,
 // global scale: the walk's sub-tiles get scale bytes 0x7F (the E4M3 NaN) and
 // element codes 0, in 8-byte pieces of element rows and single scale bytes,
 // every piece outside the tensor dropped by its descriptor.
-template <bool ROW, bool COL>
+template <bool ROW, bool COL, bool RAG>
 __device__ void nv_fill_nonfinite(const Nv4Args &a, int tm0, int n, int tk)
 {
     const int t = (int)threadIdx.x;
@@ -419,15 +470,25 @@ __device__ void nv_fill_nonfinite(const Nv4Args &a, int tm0, int n, int tk)
             }
         }
         if constexpr (COL) {
-            // 256 transposed rows x (64 element bytes, 8 scale bytes)
-            const int64_t lq = a.M >> 1, ls = a.M >> 4;
+            // 256 transposed rows x (64 element bytes, 8 scale bytes); rows
+            // that start at any byte (RAG) take the element bytes one by one
+            const int64_t lq = (a.M + 1) >> 1, ls = (a.M + 15) >> 4;
             const rsrc_t rq = make_rsrc(a.q_col, k0 * lq + (m0 >> 1), a.K * lq);
             const rsrc_t rs = make_rsrc(a.s_col, k0 * ls + (m0 >> 4), a.K * ls);
             for (int i = t; i < kTileK * 8; i += kThreads) {
                 const int kr = i >> 3, p = i & 7;
                 const bool row_ok = k0 + kr < a.K;
-                buf_store8<0>(rq, row_ok && (m0 >> 1) + 8 * p < lq ? (uint32_t)(kr * lq + 8 * p) : kDead,
-                              zero);
+                if constexpr (RAG) {
+#pragma unroll
+                    for (int e = 0; e < 8; e++)
+                        buf_store1<0>(rq, row_ok && (m0 >> 1) + 8 * p + e < lq
+                                              ? (uint32_t)(kr * lq + 8 * p + e) : kDead,
+                                      (uint8_t)0);
+                } else {
+                    buf_store8<0>(rq, row_ok && (m0 >> 1) + 8 * p < lq ? (uint32_t)(kr * lq + 8 * p)
+                                                                     : kDead,
+                                  zero);
+                }
                 buf_store1<0>(rs, row_ok && (m0 >> 4) + p < ls ? (uint32_t)(kr * ls + p) : kDead,
                               (uint8_t)0x7F);
             }
@@ -435,7 +496,7 @@ __device__ void nv_fill_nonfinite(const Nv4Args &a, int tm0, int n, int tk)
     }
 }
 
-template <bool ROW, bool COL, bool TWO_D>
+template <bool ROW, bool COL, bool TWO_D, bool RAG = false>
 __device__ __forceinline__ void nv_walk(const Nv4Args &a, int rg, int tk)
 {
     using P = NvPolicy<ROW, COL>;
@@ -445,15 +506,32 @@ __device__ __forceinline__ void nv_walk(const Nv4Args &a, int rg, int tk)
 
     const float sgf = nv_global_scale(*a.amax);
     if (!__builtin_isfinite(sgf)) {   // uniform: every thread of the workgroup returns
-        nv_fill_nonfinite<ROW, COL>(a, tm0, n, tk);
+        nv_fill_nonfinite<ROW, COL, RAG>(a, tm0, n, tk);
         return;
     }
     const DivBy sg = div_by_prepare(sgf);
 
-    __shared__ NvStage st;
+    __shared__ NvStageT<RAG> st;
     if (threadIdx.x < 128)
         st.inv[threadIdx.x] = nv_inverse(threadIdx.x, sgf);
     __syncthreads();
+    if constexpr (RAG) {
+        // without the prefetch: its second register set would not fit
+        // beside the two-pair flush at two workgroups per CU
+        uint32_t w[kRowsPerLane][4];
+        for (int g = 0; g < n; g++) {
+            nv_load<P::x>(a, l, tm0 + g, tk, w);
+            if (g & 1)
+                nv_step<ROW, COL, TWO_D, 2, RAG>(a, l, w, st, sg, tm0 + g, tk, g, n);
+            else if (g + 1 == n)
+                nv_step<ROW, COL, TWO_D, 1, RAG>(a, l, w, st, sg, tm0 + g, tk, g, n);
+            else
+                nv_step<ROW, COL, TWO_D, 0, RAG>(a, l, w, st, sg, tm0 + g, tk, g, n);
+        }
+        if constexpr (COL)
+            nv_flush_s<P::s_col>(a, st, tm0, tk, n);
+        return;
+    }
     uint32_t wa[kRowsPerLane][4], wb[kRowsPerLane][4];
     const int past = a.tiles_m;   // a sub-tile row outside the tensor: reads as zeros
     nv_load<P::x>(a, l, tm0, tk, wa);
@@ -461,13 +539,13 @@ __device__ __forceinline__ void nv_walk(const Nv4Args &a, int rg, int tk)
     for (; g + 1 < n; g += 2) {
         nv_load<P::x>(a, l, tm0 + g + 1, tk, wb);
         __builtin_amdgcn_sched_barrier(0);
-        nv_step<ROW, COL, TWO_D, 0>(a, l, wa, st, sg, tm0 + g, tk, g);
+        nv_step<ROW, COL, TWO_D, 0, RAG>(a, l, wa, st, sg, tm0 + g, tk, g, n);
         nv_load<P::x>(a, l, g + 2 < n ? tm0 + g + 2 : past, tk, wa);
         __builtin_amdgcn_sched_barrier(0);
-        nv_step<ROW, COL, TWO_D, 2>(a, l, wb, st, sg, tm0 + g + 1, tk, g + 1);
+        nv_step<ROW, COL, TWO_D, 2, RAG>(a, l, wb, st, sg, tm0 + g + 1, tk, g + 1, n);
     }
     if (g < n)
-        nv_step<ROW, COL, TWO_D, 1>(a, l, wa, st, sg, tm0 + g, tk, g);
+        nv_step<ROW, COL, TWO_D, 1, RAG>(a, l, wa, st, sg, tm0 + g, tk, g, n);
     if constexpr (COL)
         nv_flush_s<P::s_col>(a, st, tm0, tk, n);
 }
@@ -486,7 +564,7 @@ __global__ __launch_bounds__(kThreads, 2) void nvfp4_kernel(Nv4Args a)
 // walk0[g] <= rg < walk0[g + 1], quantised as a tensor of its own with its
 // own amax (amax[g]) and global scale.  Workgroup 0 writes every group's
 // global scale (1 for an empty group).
-template <bool ROW, bool COL, bool TWO_D>
+template <bool ROW, bool COL, bool TWO_D, bool RAG>
 __global__ __launch_bounds__(kThreads, 2) void nvfp4_grouped_kernel(Nv4Args a, GroupTable gt)
 {
     const int job = xcd_tile((int)blockIdx.x, (int)gridDim.x);
@@ -506,12 +584,15 @@ __global__ __launch_bounds__(kThreads, 2) void nvfp4_grouped_kernel(Nv4Args a, G
     b.amax = a.amax + g;
     b.q_row = a.q_row ? a.q_row + r0 * (a.K >> 1) : nullptr;
     b.s_row = a.s_row ? a.s_row + r0 * (a.K >> 4) : nullptr;
-    b.q_col = a.q_col ? a.q_col + a.K * (r0 >> 1) : nullptr;
-    b.s_col = a.s_col ? a.s_col + a.K * (r0 >> 4) : nullptr;
+    // a group's transpose after the previous groups' [K][ceil(rows/2)] and
+    // [K][ceil(rows/16)] bytes (the same as K r0 / 2 and K r0 / 16 when every
+    // group's rows are a multiple of 16)
+    b.q_col = a.q_col ? a.q_col + (RAG ? gt.qcol_off[g] : a.K * (r0 >> 1)) : nullptr;
+    b.s_col = a.s_col ? a.s_col + (RAG ? gt.scol_off[g] : a.K * (r0 >> 4)) : nullptr;
     b.tiles_m = (int)((b.M + kTileM - 1) / kTileM);
     b.group = gt.len[g];
     b.groups_m = gt.walk0[g + 1] - gt.walk0[g];
-    nv_walk<ROW, COL, TWO_D>(b, rg - gt.walk0[g], tk);
+    nv_walk<ROW, COL, TWO_D, RAG>(b, rg - gt.walk0[g], tk);
 }
 
 // ---------------------------------------------------------------------------
@@ -683,26 +764,31 @@ hipError_t launch_absmax_grouped(const uint16_t *x, int64_t K, const GroupTable 
     return hipGetLastError();
 }
 
-template <bool ROW, bool COL, bool TWO_D>
+template <bool ROW, bool COL, bool TWO_D, bool RAG>
 static hipError_t launch_nv(const Nv4Args &a, const GroupTable *gt, hipStream_t s)
 {
     const dim3 grid((unsigned)(a.groups_m * a.tiles_k));
-    if (gt)
-        hipLaunchKernelGGL((nvfp4_grouped_kernel<ROW, COL, TWO_D>), grid, dim3(kThreads), 0, s, a,
-                           *gt);
+    if (RAG || gt)
+        hipLaunchKernelGGL((nvfp4_grouped_kernel<ROW, COL, TWO_D, RAG>), grid, dim3(kThreads), 0, s,
+                           a, *gt);
     else
         hipLaunchKernelGGL((nvfp4_kernel<ROW, COL, TWO_D>), grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
-template <bool TWO_D>
+template <bool TWO_D, bool RAG = false>
 static hipError_t launch_nv_axis(unsigned axis, const Nv4Args &a, const GroupTable *gt,
                                  hipStream_t s)
 {
     switch (axis) {
-    case 1u: return launch_nv<true, false, TWO_D>(a, gt, s);
-    case 2u: return launch_nv<false, true, TWO_D>(a, gt, s);
-    case 3u: return launch_nv<true, true, TWO_D>(a, gt, s);
+    case 1u:
+        // row-wise alone has no transposed rows to align: never the RAG variant
+        if constexpr (RAG)
+            return hipErrorInvalidValue;
+        else
+            return launch_nv<true, false, TWO_D, false>(a, gt, s);
+    case 2u: return launch_nv<false, true, TWO_D, RAG>(a, gt, s);
+    case 3u: return launch_nv<true, true, TWO_D, RAG>(a, gt, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -717,6 +803,13 @@ hipError_t launch_nvfp4_grouped(unsigned axis, bool two_d, const Nv4Args &a, con
                                 hipStream_t s)
 {
     return two_d ? launch_nv_axis<true>(axis, a, &gt, s) : launch_nv_axis<false>(axis, a, &gt, s);
+}
+
+hipError_t launch_nvfp4_ragged(unsigned axis, bool two_d, const Nv4Args &a, const GroupTable &gt,
+                               hipStream_t s)
+{
+    return two_d ? launch_nv_axis<true, true>(axis, a, &gt, s)
+                 : launch_nv_axis<false, true>(axis, a, &gt, s);
 }
 
 }  // namespace mxk

@@ -370,11 +370,16 @@ static void grouped_cases()
             check_groups(c.rows, c.G, g_rec.mx.groups_m, any);
         }
         {
-            const bool nv_any = !(c.K % 16 == 0 && rows16);
+            const bool nv_any = c.K % 16 != 0;
+            const bool nv_rag = !nv_any && !rows16;
             for (int two_d : {0, 1}) {
                 EXPECT(MX_OK, nvfp4_quantize_transpose_grouped(P(0), c.K, c.rows, c.G, P<float>(1), two_d,
                                                                both, qr, sr, qc, sc, P<float>(6), 0));
-                CHECK(g_rec.kind == (nv_any ? mxk::kLaunchNvAny : mxk::kLaunchNvGrouped));
+                CHECK(g_rec.kind == (nv_any ? mxk::kLaunchNvAny
+                                            : nv_rag ? mxk::kLaunchNvRagged : mxk::kLaunchNvGrouped));
+                if (nv_rag)
+                    for (int g = 0; g < c.G; g++)
+                        CHECK(g_rec.gt.len[g] % 2 == 0 && g_rec.gt.len[g] <= mxk::kMaxNvRagGroup);
                 check_groups(c.rows, c.G, g_rec.nv.groups_m, nv_any);
                 CHECK((int64_t)g_rec.nv.groups_m * g_rec.nv.tiles_k <= INT32_MAX);
                 int64_t qo = 0, so = 0;
@@ -404,13 +409,13 @@ static void grouped_cases()
         CHECK(mx_quantize_grouped_workspace_size(256, b.rows, b.G, both, MX_FUSE_DBIAS) == 0);
         CHECK(mx_grouped_scale_size(256, b.rows, b.G, both, 0) == 0);
     }
-    // row counts that are not multiples of 16: the any-shape NVFP4 kernel, and
-    // the MXFP8 kernel variant whose transposed rows start at any byte (the
-    // plain grouped kernel for the row-wise output alone)
+    // row counts that are not multiples of 16: the tiled kernels' variants
+    // whose transposed rows start at any byte (the plain grouped kernel for
+    // the row-wise output alone)
     const int64_t odd[2] = {16, 8};
     EXPECT(MX_OK, nvfp4_quantize_transpose_grouped(P(0), 256, odd, 2, P<float>(1), 0, both, qr, sr,
                                                    qc, sc, nullptr, 0));
-    CHECK(g_rec.kind == mxk::kLaunchNvAny && g_rec.gt.qcol_off[1] == 256 * 8 &&
+    CHECK(g_rec.kind == mxk::kLaunchNvRagged && g_rec.gt.qcol_off[1] == 256 * 8 &&
           g_rec.gt.scol_off[1] == 256);
     EXPECT(MX_OK, mx_absmax_bf16_grouped(P(0), 256, odd, 2, P<float>(1), 0));
     EXPECT(MX_OK, mx_quantize_grouped(P(0), nullptr, 256, odd, 2, both, 0, qr, sr, qc, sc, nullptr,
@@ -443,13 +448,28 @@ static void nvfp4_cases()
                              {8, 16}, {16, 8}, {1, 1}, {kDim, 1}, {1, kDim}, {16383, 16383},
                              {kDim - 1, (1 << 17) - 1}};
     for (auto &s : ok) {
-        const bool any = s[0] % 16 != 0 || s[1] % 16 != 0;
+        // K not a multiple of 16: the any-shape kernel; M not a multiple of
+        // 16 (with the transposed output): the tiled kernel's ragged variant
+        const bool any = s[1] % 16 != 0;
+        const bool rag = !any && s[0] % 16 != 0;
         for (int two_d : {0, 1}) {
             EXPECT(MX_OK, (two_d ? nvfp4_quantize_transpose_2d : nvfp4_quantize_transpose)(
                               P(0), s[0], s[1], P<float>(1), both, qr, sr, qc, sc, P<float>(6), 0));
             const mxk::Nv4Args &a = g_rec.nv;
             CHECK(a.M == s[0] && a.K == s[1] && g_rec.two_d == (two_d != 0));
-            CHECK(g_rec.kind == (any ? mxk::kLaunchNvAny : mxk::kLaunchNv));
+            CHECK(g_rec.kind == (any ? mxk::kLaunchNvAny : rag ? mxk::kLaunchNvRagged : mxk::kLaunchNv));
+            if (rag) {
+                const mxk::GroupTable &gt = g_rec.gt;
+                CHECK(a.tiles_m == ceil_div(s[0], mxk::kTileM) && a.tiles_k == ceil_div(s[1], mxk::kTileK));
+                CHECK(a.group % 2 == 0 && a.group <= mxk::kMaxNvRagGroup || a.group >= a.tiles_m);
+                CHECK(gt.count == 1 && gt.row0[1] == s[0] && gt.walk0[1] == a.groups_m &&
+                      gt.len[0] == a.group && a.groups_m == ceil_div(a.tiles_m, a.group));
+                CHECK(gt.qcol_off[0] == 0 && gt.scol_off[0] == 0);
+                CHECK((int64_t)a.groups_m * a.tiles_k <= INT32_MAX);
+                EXPECT(MX_OK, nvfp4_quantize_transpose(P(0), s[0], s[1], P<float>(1), MX_ROWWISE, qr, sr,
+                                                       nullptr, nullptr, nullptr, 0));
+                CHECK(g_rec.kind == mxk::kLaunchNv);
+            }
             if (any) {
                 const mxk::GroupTable &gt = g_rec.gt;
                 CHECK(a.tiles_m == ceil_div(s[0], mxk::kAnyTileM) &&

@@ -110,6 +110,13 @@ hipError_t launch_nvfp4_grouped(unsigned axis, bool two_d, const Nv4Args &a,
     return note(kLaunchNvGrouped);
 }
 
+hipError_t launch_nvfp4_ragged(unsigned axis, bool two_d, const Nv4Args &a,
+                                const GroupTable &gt, hipStream_t)
+{
+    g_rec.axis = axis, g_rec.two_d = two_d, g_rec.nv = a, g_rec.gt = gt;
+    return note(kLaunchNvRagged);
+}
+
 hipError_t launch_absmax_grouped(const uint16_t *, int64_t K, const GroupTable &gt, float *,
                                  hipStream_t)
 {

@@ -6,7 +6,7 @@ namespace mxk {
 
 enum { kLaunchNone, kLaunchMx, kLaunchMxGrouped, kLaunchValues, kLaunchAbsmax, kLaunchNv,
        kLaunchNvGrouped, kLaunchAbsmaxGrouped, kLaunchMxAny, kLaunchValuesAny, kLaunchNvAny,
-       kLaunchMxRagged };
+       kLaunchMxRagged, kLaunchNvRagged };
 
 struct Record {
     int calls = 0, reduces = 0, kind = kLaunchNone;

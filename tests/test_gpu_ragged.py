@@ -1,13 +1,15 @@
-"""GPU parity of the MXFP8 casts whose row length is a multiple of 8 but whose
-row count (or a group's) is not a multiple of 16: the tiled kernel takes them,
-and the variant of its transposed flush for transposed rows that start at any
-byte writes q_col (each sub-tile's 8 aligned 16-byte pieces per row, the
-previous sub-tile's last bytes carried in LDS).  MoE stacks with ragged expert
+"""GPU parity of the casts whose row length is a multiple of 8 (MXFP8) or 16
+(NVFP4) but whose row count (or a group's) is not a multiple of 16: the tiled
+kernels take them, and the variant of their transposed flush for transposed
+rows that start at any byte writes q_col (whole 128-byte lines from two staged
+tiles, bytes at a walk's ends one by one).  MoE stacks with unrounded expert
 sizes are the common case.  Compared with the oracle byte for byte in canary-
-filled buffers with guard bands: plain casts in both output sets and every
+filled buffers with guard bands.  MXFP8: plain casts in every output set,
 format and scale layout, the pre-ops with dbias, the gated casts and their
 backward, grouped stacks (one launch over groups of any size, empty ones
-included), the allocation-free cast, and a 16383 x 16384 tensor."""
+included), the allocation-free cast and a 16383 x 16384 tensor.  NVFP4: 1D
+and 2D blocks, single and grouped, non-finite and tiny-scale tensors, and
+16383 x 16384."""
 import os
 
 import numpy as np
@@ -18,7 +20,7 @@ import block_scaled_precision_bf16_amd as mx
 import oracle as O
 import workloads as W
 from gpu_util import assert_dbias_close, mx_outputs_equal, to_dev
-from test_gpu_any_shape import FLAG_IDS, FLAGS, Guarded
+from test_gpu_any_shape import FLAG_IDS, FLAGS, Guarded, nv_both, nv_guarded
 
 pytestmark = pytest.mark.gpu
 
@@ -175,3 +177,72 @@ def test_ragged_metric_sized():
     torch.cuda.synchronize()
     mx_outputs_equal(r, O.mx_quantize(x, axis=3), "16383x16384")
     g.guards_intact("16383x16384")
+
+
+# --- NVFP4: K a multiple of 16, rows (or a group's) not ---------------------
+
+NV_SHAPES = [(1, 16), (17, 32), (40, 64), (129, 256), (255, 272), (1000, 528), (4097, 256),
+             (33, 7168), (2049, 1040)]
+
+
+@pytest.mark.parametrize("two_d", [False, True], ids=["1d", "2d"])
+@pytest.mark.parametrize("axis", [1, 2, 3])
+@pytest.mark.parametrize("M,K", NV_SHAPES)
+def test_ragged_nvfp4(M, K, axis, two_d):
+    x = W.student_t_rows(M, K, seed=9400 + 3 * M + K)
+    r, o, g = nv_both(x, axis, two_d)
+    what = f"nvfp4 {M}x{K} axis {axis} 2d={two_d}"
+    assert r["sg"].item() == o["sg"], what
+    mx_outputs_equal(r, o, what)
+    g.guards_intact(what)
+
+
+@pytest.mark.parametrize("two_d", [False, True], ids=["1d", "2d"])
+def test_ragged_nvfp4_nonfinite_and_tiny_scale(two_d):
+    x = W.student_t_rows(131, 80, seed=9500)
+    x[70, 76] = 0x7FC0                       # NaN: 0x7F scales, zero codes
+    r, o, g = nv_both(x, 3, two_d)
+    assert np.isnan(r["sg"].item()) and np.isnan(o["sg"])
+    mx_outputs_equal(r, o, "nvfp4 ragged non-finite")
+    g.guards_intact("nvfp4 ragged non-finite")
+    x = W.normal(33, 64, seed=9501, sigma=1e-37)   # multipliers that overflow to Inf
+    x[0, :16] = 0
+    x[1, 0] = 0x8000
+    r, o, g = nv_both(x, 3, two_d)
+    assert r["sg"].item() == o["sg"]
+    mx_outputs_equal(r, o, "nvfp4 ragged tiny S_g")
+    g.guards_intact("nvfp4 ragged tiny S_g")
+
+
+NV_GROUPS = [([1101, 0, 17, 640, 3], 528), ([5, 1, 0, 2], 16), ([4099, 0, 3001, 17, 9000], 272),
+             (W.moe_group_rows(16384, 8, seed=8, step=1), 7168)]
+
+
+@pytest.mark.parametrize("two_d", [False, True], ids=["1d", "2d"])
+@pytest.mark.parametrize("axis", [2, 3])
+@pytest.mark.parametrize("rows,K", NV_GROUPS, ids=["mixed", "tiny", "large", "moe"])
+def test_ragged_nvfp4_grouped(rows, K, axis, two_d):
+    M = sum(rows)
+    x = W.student_t_rows(M, K, seed=9600 + M + K)
+    xd = to_dev(x)
+    amax = mx.mx_absmax_bf16_grouped(xd, rows)
+    qcol = K * sum(-(-m // 2) for m in rows)
+    scol = K * sum(-(-m // 16) for m in rows)
+    g = nv_guarded(M, K, axis, len(rows), qcol, scol)
+    r = mx.nvfp4_quantize_transpose_grouped(xd, rows, amax, axis=axis, two_d=two_d, out=g.out)
+    torch.cuda.synchronize()
+    o = O.nvfp4_quantize_transpose_grouped(x, rows, axis=axis, two_d=two_d)
+    what = f"grouped nvfp4 {rows} K={K} axis {axis} 2d={two_d}"
+    assert np.array_equal(r["sg"].cpu().numpy(), o["sg"]), what
+    mx_outputs_equal(r, o, what)
+    g.guards_intact(what)
+
+
+@pytest.mark.parametrize("two_d", [False, True], ids=["1d", "2d"])
+def test_ragged_nvfp4_large(two_d):
+    """16383 x 16384: the NVFP4 metric-sized tensor less one row."""
+    x = W.student_t_rows(16383, 16384, seed=9700)
+    r, o, g = nv_both(x, 3, two_d)
+    assert r["sg"].item() == o["sg"]
+    mx_outputs_equal(r, o, f"nvfp4 16383x16384 2d={two_d}")
+    g.guards_intact("nvfp4 16383x16384")

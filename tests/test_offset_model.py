@@ -32,6 +32,7 @@ THREADS = 64 * WAVES
 TILE_M, TILE_K = 128, 256
 MAX_GROUP = 16
 MAX_RAG_GROUP = 14
+MAX_NV_RAG_GROUP = 4
 MAX_RECORDS = 0x7FFFFFFF
 DEAD = 0x80000000
 U32 = 1 << 32
@@ -263,40 +264,26 @@ def mx_model(M, K, op="plain", tiled=False, ck=None):
     return ck
 
 
-def model_col_flush_q_rag(base, M, K, tm, tk, first, last):
-    """col_flush_q_rag (mx_cast.h): the transposed tile of sub-tile tm of
-    strip tk when transposed rows start at any byte -- each row's whole
-    128-byte line around the sub-tile's first byte, 16-byte pieces, bytes
-    outside the walk left alone -- as (site, descriptor, offsets, bytes, live,
-    address) with addresses counted from the start of the tensor's (or
-    group's) q_col, which lies at `base` modulo 128."""
+def model_rag_lines(d, base, pitch, rows, addr0, rem, first, last):
+    """rag_flush_lines (rag_flush.h): one step of a walk over transposed rows
+    pitch bytes apart, `rows` of them from the strip's first, as (site,
+    descriptor, offsets, bytes, live, address) -- d the descriptor from the
+    line boundary at or below the step's first byte of the strip's first row
+    (base bytes before it), addr0(kr) the address of row kr's first byte of
+    the step."""
     t = np.arange(THREADS)
     j = t & 7
-    mt, k0 = tm * TILE_M, tk * TILE_K
-    rem = min(M - mt, TILE_M)
-    d0 = (base + k0 * M) % 128
-    # make_rsrc(row0 - d0, mt, (K - k0) * M + d0), row0 = q_col + k0 M
-    d = Desc(k0 * M - d0 + mt, K * M)
-    lo = 0 if first else -TILE_M
+    lo = 0 if first else -128
     out = []
-    for i in range(TILE_K // 32):
+    for i in range(256 // 32):
         kr = (t >> 3) + 32 * i
-        at = d0 + kr * M
+        at = base + kr * pitch
         sft = at % 128
-        p0 = 16 * j - sft
-        whole = (k0 + kr < K) & (p0 >= lo) & (p0 + 16 <= rem)
-        out.append(("q_col rag W=16", d, np.where(whole, at - sft + 16 * j, DEAD), 16, whole,
-                    (k0 + kr) * M + mt + p0))
-    if last:
-        # the line after, whole pieces, the same lanes
-        for i in range(TILE_K // 32):
-            kr = (t >> 3) + 32 * i
-            at = d0 + kr * M
-            sft = at % 128
-            p0 = TILE_M + 16 * j - sft
-            whole = (k0 + kr < K) & (p0 + 16 <= rem)
-            out.append(("q_col rag W=16", d, np.where(whole, at - sft + TILE_M + 16 * j, DEAD), 16,
-                        whole, (k0 + kr) * M + mt + p0))
+        for p in (0, 128) if last else (0,):
+            p0 = p + 16 * j - sft
+            whole = (kr < rows) & (p0 >= lo) & (p0 + 16 <= rem)
+            out.append(("rag W=16", d, np.where(whole, at - sft + p + 16 * j, DEAD), 16, whole,
+                        addr0(kr) + p0))
     if not (first or last):
         return out
     # the end pieces byte by byte: 16 lanes per row
@@ -304,9 +291,9 @@ def model_col_flush_q_rag(base, M, K, tm, tk, first, last):
     for e in (0, 1):
         if (e == 0 and not first) or (e == 1 and not last):
             continue
-        for i in range(TILE_K // 16):
+        for i in range(256 // 16):
             kr = (t >> 4) + 16 * i
-            at = d0 + kr * M
+            at = base + kr * pitch
             sft = at % 128
             qa = sft >> 4
             if e == 0:
@@ -316,10 +303,34 @@ def model_col_flush_q_rag(base, M, K, tm, tk, first, last):
                 q = (rem - 1 + sft) >> 4
                 edge = ((rem + sft) % 16 != 0) & ~(first & (q == qa) & (sft % 16 != 0))
             p = 16 * q - sft + b
-            ok = (k0 + kr < K) & edge & (p >= lo) & (p < rem)
-            out.append(("q_col rag W=1", d, np.where(ok, at - sft + 16 * q + b, DEAD), 1, ok,
-                        (k0 + kr) * M + mt + p))
+            ok = (kr < rows) & edge & (p >= lo) & (p < rem)
+            out.append(("rag W=1", d, np.where(ok, at - sft + 16 * q + b, DEAD), 1, ok,
+                        addr0(kr) + p))
     return out
+
+
+def model_col_flush_q_rag(base, M, K, tm, tk, first, last):
+    """col_flush_q_rag (mx_cast.h): sub-tile tm of strip tk, addresses from
+    the start of the tensor's (or group's) q_col, which lies at `base` modulo
+    128."""
+    mt, k0 = tm * TILE_M, tk * TILE_K
+    rem = min(M - mt, TILE_M)
+    d0 = (base + k0 * M) % 128
+    # make_rsrc(row0 - d0, mt, (K - k0) * M + d0), row0 = q_col + k0 M
+    d = Desc(k0 * M - d0 + mt, K * M)
+    return model_rag_lines(d, d0, M, K - k0, lambda kr: (k0 + kr) * M + mt, rem, first, last)
+
+
+def model_nv_flush_q_rag(base, M, K, tm, tk, parts, first, last):
+    """nv_flush_q_rag (nvfp4.hip): the pair of sub-tiles starting at tm
+    (parts 1: that sub-tile only), rows of ceil(M/2) bytes."""
+    k0 = tk * TILE_K
+    ld = (M + 1) >> 1
+    b0 = tm * (TILE_M // 2)
+    rem = min(ld - b0, 64 * parts)
+    d0 = (base + k0 * ld) % 128
+    d = Desc(k0 * ld - d0 + b0, K * ld)
+    return model_rag_lines(d, d0, ld, K - k0, lambda kr: (k0 + kr) * ld + b0, rem, first, last)
 
 
 RAG_STACKS = [([1], 8), ([17], 24), ([129], 256), ([300], 264), ([255, 1], 8), ([16, 8], 256),
@@ -367,6 +378,43 @@ def test_ragged_transposed_writes_every_byte_once(rows, K, L, base):
     assert (count == 1).all(), (int((count == 0).sum()), int((count > 1).sum()))
 
 
+@pytest.mark.parametrize("base", [0, 5, 64, 127])
+@pytest.mark.parametrize("L", [2, 4])
+@pytest.mark.parametrize("rows,K", [([1], 16), ([17], 32), ([257], 256), ([300], 272),
+                                    ([255, 1], 16), ([16, 8], 256), ([1, 17, 0, 300, 129, 5], 48),
+                                    ([1104, 3008, 1072, 6563, 1], 16), ([250, 131, 9], 528)])
+def test_nvfp4_ragged_transposed_writes_every_byte_once(rows, K, L, base):
+    """nv_flush_q_rag over every pair of every walk (even length L) of every
+    group of a stack (the groups' [K][ceil(rows/2)] transposes one after the
+    other, at `base` modulo 128): every byte written exactly once, every
+    access inside its descriptor."""
+    total = K * sum(-(-m // 2) for m in rows)
+    count = np.zeros(total, np.int64)
+    ck = Checker()
+    off = 0
+    for M in rows:
+        if M == 0:
+            continue
+        gbase = (base + off) % 128
+        tiles_m, tiles_k = -(-M // TILE_M), -(-K // TILE_K)
+        for w in range(-(-tiles_m // L)):
+            n = min(L, tiles_m - w * L)
+            for tk in range(tiles_k):
+                for g in range(1, n + 1, 2):       # the flushes: g odd, or a walk's lone last
+                    parts = 2 if g < n else 1
+                    tm = w * L + (g - 1)
+                    for site, d, o, nb_, live, addr in model_nv_flush_q_rag(
+                            gbase, M, K, tm, tk, parts, g < 2, g + 1 >= n):
+                        ck.access(site, d, o, nb_, live, addr)
+                        a = np.broadcast_to(addr, live.shape)[live]
+                        assert (a >= 0).all()
+                        for b in range(nb_):
+                            np.add.at(count, off + a + b, 1)
+        off += K * -(-M // 2)
+    ck.ok()
+    assert (count == 1).all(), (int((count == 0).sum()), int((count > 1).sum()))
+
+
 def scale_rows(ck, site, rs, k0, K, pitch, first, count, base_align=0):
     """flush_scale_rows (stage_flush.h): row c's `count` bytes in pieces of
     the widest size CH that pitch, first, count and the base allow."""
@@ -389,24 +437,27 @@ def scale_rows(ck, site, rs, k0, K, pitch, first, count, base_align=0):
 def nv_model(M, K, ck=None):
     ck = ck or Checker()
     tiles_m, tiles_k = -(-M // TILE_M), -(-K // TILE_K)
-    group = plan_walk(tiles_m, tiles_k)
+    rag = M % 16 != 0
+    group = plan_walk(tiles_m, tiles_k, even=rag, max_len=MAX_NV_RAG_GROUP if rag else 16)
     groups_m = -(-tiles_m // group)
     t, wave, half, cl, row = lanes()
     r = np.arange(ROWS_PER_LANE)[:, None]
     for tm, tk in itertools.product(edge(tiles_m) + [tiles_m], edge(tiles_k)):
         live = (tm * TILE_M + row < M) & (tk * TILE_K + cl * COLS_PER_LANE < K)
+        # a live lane's rows past M (M not a multiple of 16) fall outside
+        in_rows = tm * TILE_M + row + r < M
         tile = tm * TILE_M * K + tk * TILE_K
         rx = Desc(2 * tile, 2 * M * K)
         rs = 2 * K
         off = np.where(live, row * rs + 2 * COLS_PER_LANE * cl, DEAD)
-        ck.access("nv x", rx, off + r * rs, 16, live,
+        ck.access("nv x", rx, off + r * rs, 16, live & in_rows,
                   2 * ((tm * TILE_M + row + r) * K + tk * TILE_K + COLS_PER_LANE * cl))
         if tm == tiles_m:
             continue
         ld = K >> 1
         rq = Desc(tm * TILE_M * ld + tk * (TILE_K // 2), M * ld)
         qoff = np.where(live, row * ld + 4 * cl, DEAD)
-        ck.access("nv q_row", rq, qoff + r * ld, 4, live,
+        ck.access("nv q_row", rq, qoff + r * ld, 4, live & in_rows,
                   (tm * TILE_M + row + r) * ld + tk * (TILE_K // 2) + 4 * cl)
         nb = K >> 4
         rrow = tm * TILE_M + t
@@ -423,6 +474,12 @@ def nv_model(M, K, ck=None):
                       rrow * nb + (k0 >> 4) + b)
     # nv_flush_q for the pair starting at each edge sub-tile (parts 1 and 2)
     for tm, tk, parts in itertools.product(edge(tiles_m), edge(tiles_k), (1, 2)):
+        if rag:
+            for first, last in ((True, False), (False, True), (True, True)):
+                for site, d, off, nb_, lv, addr in model_nv_flush_q_rag(0, M, K, tm, tk, parts,
+                                                                        first, last):
+                    ck.access("nv q_col " + site, d, off, nb_, lv, addr)
+            continue
         jr = t & 7
         m0, k0 = tm * TILE_M, tk * TILE_K
         ld = M >> 1
@@ -441,7 +498,7 @@ def nv_model(M, K, ck=None):
             ck.access("nv q_col lo", rc, np.where(lv, off, DEAD), 8, lv, addr)
             lv = col_ok & (row0 + 16 < M)
             ck.access("nv q_col hi", rc, np.where(lv, off + 8, DEAD), 8, lv, addr + 8)
-    nblk = M >> 4
+    nblk = (M + 15) >> 4
     for rg, tk in itertools.product(edge(groups_m), edge(tiles_k)):
         n = min(tiles_m - rg * group, group)
         tm0 = rg * group
@@ -489,7 +546,10 @@ def test_dgated_offsets(M, N, tiled):
 
 
 NV_SHAPES = [(MAXD, 16), (16, MAXD), (128, MAXD), (144, MAXD - 16), (1 << 17, MAXD),
-             (MAXD, 1 << 17), (16400, 7168), (16384, 16384)]
+             (MAXD, 1 << 17), (16400, 7168), (16384, 16384),
+             # rows that are not multiples of 16: transposed rows at any byte
+             (MAXD - 1, 16), (MAXD - 1, 1 << 17), (1, MAXD), (17, MAXD - 16), ((1 << 17) - 1, MAXD),
+             (16383, 16384), (129, 7168)]
 
 
 @pytest.mark.parametrize("M,K", NV_SHAPES)

@@ -346,8 +346,10 @@ mx_status mx_absmax_bf16(const void *x, int64_t n, float *amax, hipStream_t stre
  * each <= 2^23, M*K <= 2^40.  When 16 does not divide K (M), the last block
  * of each row (column) is partial: its scale and codes come from its own
  * elements, and a line of n codes packs into ceil(n/2) bytes, the high nibble
- * of an odd line's last byte 0.  M and K multiples of 16 take the tiled
- * kernel, other shapes a kernel for arbitrary row alignment (same results).
+ * of an odd line's last byte 0.  K a multiple of 16 takes the tiled kernel,
+ * for any M (with the transpose and M not a multiple of 16, its rows start
+ * at any byte and a variant of the kernel writes them through a two-pair
+ * stage); other K a kernel for arbitrary row alignment (same results).
  *   amax     device, one fp32: the tensor absmax the global scale is built
  *            from, as mx_absmax_bf16 computes it (on the same stream).  With
  *            a NaN or infinite amax (a tensor holding a NaN or an Inf) there
@@ -400,8 +402,10 @@ mx_status mx_absmax_bf16_grouped(const void *x, int64_t K, const int64_t *group_
  *   x            device, bf16 [M][K], M = sum of group_rows; group g owns rows
  *                r_g .. r_g + group_rows[g] - 1
  *   group_rows   HOST array of G row counts, each >= 0; 1 <= G <= 64,
- *                0 < M <= 2^23; any K >= 1.  Every count and K multiples of
- *                16 take the tiled kernel, any other stack the any-shape
+ *                0 < M <= 2^23; any K >= 1.  K a multiple of 16 takes the
+ *                tiled kernel, for any counts (counts that are not multiples
+ *                of 16: through its variant for transposed rows at any byte,
+ *                as for nvfp4_quantize_transpose), any other K the any-shape
  *                kernel (same results)
  *   amax         device, fp32 [G]: each group's tensor amax (for example from
  *                mx_absmax_bf16_grouped)

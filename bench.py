@@ -31,6 +31,7 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
 KERNEL_SOURCES = ["block_scaled_precision_bf16_amd/csrc/mx_cast_fmt_e4m3.hip",
                   "block_scaled_precision_bf16_amd/csrc/mx_cast.h",
                   "block_scaled_precision_bf16_amd/csrc/stage_flush.h",
+                  "block_scaled_precision_bf16_amd/csrc/rag_flush.h",
                   "block_scaled_precision_bf16_amd/csrc/device_math.h",
                   "block_scaled_precision_bf16_amd/csrc/launch.h",
                   "block_scaled_precision_bf16_amd/csrc/bufio.h",

@@ -540,7 +540,9 @@ __device__ __forceinline__ void mx_cast_walk(const MxArgs &a, int rg, int tk)
     float dsum[kColsPerLane] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
     if constexpr (OP == OP_PLAIN && !RAG) {
-        // Software pipeline over two register sets.  Every pass through the
+        // Software pipeline over two register sets (not with RAG: its second
+        // register set beside the two-tile flush left one workgroup per CU,
+        // slower than two without it).  Every pass through the
         // loop body issues the same memory instructions (the load past the
         // walk's end reads a sub-tile outside the tensor, which costs no
         // traffic), so the loads of the next sub-tile are never waited for

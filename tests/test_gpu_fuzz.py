@@ -2,8 +2,10 @@
 oracle byte for byte (dbias within its tolerance): shapes with partial edges,
 output selection, element format, scale rule and layout, pre-op and dbias for
 the MXFP8 cast; the gated casts and their backward; NVFP4 1D and 2D; grouped
-casts with random expert sizes; and the same at any shape (sizes from 1 up,
-not multiples of 16 or 8).  The cases are drawn from fixed seeds, so the set
+casts with random expert sizes; the same at any shape (sizes from 1 up, not
+multiples of 16 or 8); and at row counts that are not multiples of 16 with
+aligned rows (the tiled kernels' ragged variants, up to several sub-tiles per
+walk).  The cases are drawn from fixed seeds, so the set
 is the same on every run; each case's parameters are in its test id."""
 import os
 
@@ -212,3 +214,68 @@ def any_grouped_cases(n=20, seed=20261208):
 @pytest.mark.parametrize("i,rows,K,axis,flags,nv", any_grouped_cases())
 def test_any_shape_grouped_fuzz(i, rows, K, axis, flags, nv):
     test_grouped_fuzz(1000 + i, rows, K, axis, flags, nv)
+
+
+# --- ragged row counts: row lengths multiples of 8 (MXFP8) or 16 (NVFP4), row
+# counts (or a group's) not multiples of 16 -- the tiled kernels with
+# transposed rows at any byte; sizes up to several sub-tiles per walk
+
+def ragged_cases(n=80, seed=20261209):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        M = int(rng.integers(1, 3000))
+        M += 1 if M % 16 == 0 else 0
+        K = 8 * int(rng.integers(1, 200))
+        axis = int(rng.integers(1, 4))
+        flags = FORMATS[int(rng.integers(0, 4))] | (mx.SCALE_TILED if rng.random() < 0.3 else 0)
+        fusion = FUSIONS[int(rng.integers(0, 4))] | (mx.FUSE_DBIAS if rng.random() < 0.4 else 0)
+        out.append(pytest.param(i, M, K, axis, flags, fusion,
+                                id=f"rag{i}-{M}x{K}-a{axis}-f{flags}-u{fusion}"))
+    return out
+
+
+@pytest.mark.parametrize("i,M,K,axis,flags,fusion", ragged_cases())
+def test_ragged_fuzz(i, M, K, axis, flags, fusion):
+    test_mx_quantize_fuzz(2000 + i, M, K, axis, flags, fusion)
+
+
+def ragged_nvfp4_cases(n=40, seed=20261210):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        M = int(rng.integers(1, 3000))
+        M += 1 if M % 16 == 0 else 0
+        K = 16 * int(rng.integers(1, 100))
+        axis = int(rng.integers(1, 4))
+        two_d = bool(rng.random() < 0.5)
+        out.append(pytest.param(i, M, K, axis, two_d,
+                                id=f"rag{i}-{M}x{K}-a{axis}-{'2d' if two_d else '1d'}"))
+    return out
+
+
+@pytest.mark.parametrize("i,M,K,axis,two_d", ragged_nvfp4_cases())
+def test_ragged_nvfp4_fuzz(i, M, K, axis, two_d):
+    test_nvfp4_fuzz(2000 + i, M, K, axis, two_d)
+
+
+def ragged_grouped_cases(n=30, seed=20261211):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        G = int(rng.integers(1, 9))
+        rows = [int(v) for v in rng.integers(0, 1500, G)]
+        if all(r % 16 == 0 for r in rows):
+            rows[0] += 1
+        nv = i % 2 == 0
+        K = (16 if nv else 8) * int(rng.integers(1, 80))
+        axis = int(rng.integers(1, 4))
+        flags = FORMATS[int(rng.integers(0, 4))] | (mx.SCALE_TILED if rng.random() < 0.3 else 0)
+        out.append(pytest.param(i, rows, K, axis, flags, nv,
+                                id=f"rag{i}-{'nvfp4' if nv else 'mxfp8'}-G{G}-K{K}-a{axis}-f{flags}"))
+    return out
+
+
+@pytest.mark.parametrize("i,rows,K,axis,flags,nv", ragged_grouped_cases())
+def test_ragged_grouped_fuzz(i, rows, K, axis, flags, nv):
+    test_grouped_fuzz(2000 + i, rows, K, axis, flags, nv)

@@ -113,7 +113,10 @@ def test_c1_special_256x512():
     mx_outputs_equal(g, O.mx_quantize(x), "C1")
 
 
-@pytest.mark.parametrize("M,K", [(1 << 23, 32), (32, 1 << 23), ((1 << 23) - 16, 40)])
+@pytest.mark.parametrize("M,K", [(1 << 23, 32), (32, 1 << 23), ((1 << 23) - 16, 40),
+                                 # ragged row counts: the tiled kernel's variant for
+                                 # transposed rows at any byte
+                                 ((1 << 23) - 1, 8), (17, 1 << 23)])
 @pytest.mark.parametrize("layout", [0, mx.SCALE_TILED], ids=["compact", "tiled"])
 def test_mxfp8_maximum_dimensions(M, K, layout):
     """The largest row count (2^23 rows of 32 or 40 columns: the most
@@ -128,7 +131,7 @@ def test_mxfp8_maximum_dimensions(M, K, layout):
     mx_outputs_equal(g, o, f"max dims {M}x{K} {layout}")
 
 
-@pytest.mark.parametrize("M,K", [(1 << 23, 16), (16, 1 << 23)])
+@pytest.mark.parametrize("M,K", [(1 << 23, 16), (16, 1 << 23), ((1 << 23) - 1, 16), (17, 1 << 23)])
 def test_nvfp4_maximum_dimensions(M, K):
     x = W.student_t_rows(M, K, seed=91)
     xd = to_dev(x)

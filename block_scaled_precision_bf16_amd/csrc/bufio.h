@@ -71,6 +71,12 @@ __device__ __forceinline__ void buf_store4(rsrc_t r, uint32_t off, uint32_t v)
 }
 
 template <int AUX = 0>
+__device__ __forceinline__ void buf_store2(rsrc_t r, uint32_t off, uint16_t v)
+{
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)off, 0, AUX);
+}
+
+template <int AUX = 0>
 __device__ __forceinline__ void buf_store1(rsrc_t r, uint32_t off, uint8_t v)
 {
     __builtin_amdgcn_raw_buffer_store_b8(v, r, (int)off, 0, AUX);

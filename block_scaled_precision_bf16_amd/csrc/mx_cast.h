@@ -338,12 +338,6 @@ struct MxRagView {
     {
         return c < 8 ? prev[kr][stage_chunk(kr, c)] : cur[kr][stage_chunk(kr, (c - 8) & 7)];
     }
-    __device__ __forceinline__ uint8_t byte(int kr, int u) const
-    {
-        const int c = u >> 4;
-        const uint4 *p = c < 8 ? &prev[kr][stage_chunk(kr, c)] : &cur[kr][stage_chunk(kr, (c - 8) & 7)];
-        return reinterpret_cast<const uint8_t *>(p)[u & 15];
-    }
 };
 
 // The staged transposed tile of sub-tile g of a walk whose transposed rows

@@ -123,12 +123,6 @@ struct NvRagView {
         const uint4 v = *reinterpret_cast<const uint4 *>(row + 16 * nv_chunk(kr, c & 7));
         return nv_half(kr, 0) ? make_uint4(v.z, v.w, v.x, v.y) : v;
     }
-    __device__ __forceinline__ uint8_t byte(int kr, int u) const
-    {
-        const int c = u >> 4;
-        const uint8_t *row = c < 8 ? prev[kr] : cur[kr];
-        return row[16 * nv_chunk(kr, c & 7) + ((u & 15) ^ (8 * nv_half(kr, 0)))];
-    }
 };
 
 template <int XA>

@@ -14,15 +14,16 @@
 // sft bytes before it belong to the walk or group before, and its last step
 // also writes the line after, up to the row's end (rem bytes of the step);
 // the pieces holding other bytes as well -- at most one at each end of a row
-// -- leave byte by byte, at those two steps only.  Thread t writes piece
-// t % 8 of rows t / 8 + 32 i (and of the line after), and byte t % 16 of the
-// end pieces of rows t / 16 + 16 i.
+// -- leave in naturally aligned stores of 1, 2, 4 and 8 bytes, at those two
+// steps only.  Thread t writes piece t % 8 of rows t / 8 + 32 i (and of the
+// line after), and the end pieces of row t.
 //
 // A staged view V gives, for transposed row kr, V::chunk(kr, c): the
 // previous step's 16-byte chunk c (c < 8), the current step's chunk c - 8
-// (8 <= c < 16), any value beyond; and V::byte(kr, u): byte u of that
-// sequence (0 <= u < 256).
+// (8 <= c < 16), any value beyond.
 #pragma once
+
+#include <type_traits>
 
 #include "bufio.h"
 #include "launch.h"
@@ -52,6 +53,53 @@ __device__ __forceinline__ uint4 rag_bytes(const V &v, int kr, int u)
 {
     const int c = u >> 4;
     return window16(v.chunk(kr, c), v.chunk(kr, c + 1), (uint32_t)(u & 15));
+}
+
+// Bytes b .. b + S - 1 of the 16 bytes w (b a multiple of S) to offset off.
+template <int S>
+__device__ __forceinline__ void rag_store_at(rsrc_t rc, uint32_t off, uint4 w, int b)
+{
+    if constexpr (S == 8) {
+        const bool hi = (b & 8) != 0;
+        buf_store8(rc, off, make_uint2(hi ? w.z : w.x, hi ? w.w : w.y));
+    } else {
+        const uint32_t lo = (b & 4) ? w.y : w.x, up = (b & 4) ? w.w : w.z;
+        const uint32_t d = (b & 8) ? up : lo;
+        if constexpr (S == 4)
+            buf_store4(rc, off, d);
+        else if constexpr (S == 2)
+            buf_store2(rc, off, (uint16_t)(d >> (8 * (b & 2))));
+        else
+            buf_store1(rc, off, (uint8_t)(d >> (8 * (b & 3))));
+    }
+}
+
+// Bytes b0 .. b1 - 1 (0 <= b0 < b1 <= 16, less than the whole piece: the
+// end pieces are partial) of the 16 bytes w to the 16-byte aligned offset pa (lanes with `on` false store nothing), in naturally
+// aligned stores: upwards by size while b0's low bits are set (UP; b0 = 0
+// needs none of them), then downwards by size.  Once a size does not fit
+// upwards, no larger one does, so the downward stores start at a multiple of
+// that size and stay aligned.
+template <bool UP>
+__device__ __forceinline__ void rag_store_range(rsrc_t rc, bool on, uint32_t pa, uint4 w, int b0, int b1)
+{
+    int b = b0;
+    const auto put = [&](auto size, bool go) {
+        constexpr int S = decltype(size)::value;
+        go = go && on && b + S <= b1;
+        rag_store_at<S>(rc, go ? pa + (uint32_t)b : kDead, w, b);
+        b += go ? S : 0;
+    };
+    if (UP) {
+        put(std::integral_constant<int, 1>{}, (b & 1) != 0);
+        put(std::integral_constant<int, 2>{}, (b & 2) != 0);
+        put(std::integral_constant<int, 4>{}, (b & 4) != 0);
+        put(std::integral_constant<int, 8>{}, (b & 8) != 0);
+    }
+    put(std::integral_constant<int, 8>{}, true);
+    put(std::integral_constant<int, 4>{}, true);
+    put(std::integral_constant<int, 2>{}, true);
+    put(std::integral_constant<int, 1>{}, true);
 }
 
 // One step of the walk: rc covers the transposed output from the line
@@ -98,30 +146,24 @@ __device__ __forceinline__ void rag_flush_lines(const V &v, rsrc_t rc, uint32_t 
     }
     if (!(first || last))
         return;
-    // the end pieces byte by byte: at the first step the piece that holds a
-    // row's first byte (if it starts before it), at the last the piece that
-    // holds its last byte (if it ends after it); 16 lanes per row, one byte
-    // each, so that a store touches 4 lines
-    const int b = t & 15;
-    for (int e = 0; e < 2; e++) {
-        if (e == 0 ? !first : !last)
-            continue;
-#pragma unroll 4
-        for (int i = 0; i < 256 / 16; i++) {
-            const int kr = (t >> 4) + 16 * i;
-            const uint32_t at = base + (uint32_t)kr * pitch;
-            const int sft = (int)(at & 127u);
-            const int q = e == 0 ? sft >> 4 : (rem - 1 + sft) >> 4;
-            const bool edge = e == 0 ? (sft & 15) != 0
-                                     : ((rem + sft) & 15) != 0 && !(first && q == (sft >> 4) && (sft & 15));
-            const int p = 16 * q - sft + b;                        // the byte's place in the segment
-            const bool ok = kr < rows && edge && p >= lo && p < rem;
-            if (__builtin_amdgcn_ballot_w64(ok) == 0)
-                continue;
-            buf_store1(rc, ok ? at - (uint32_t)sft + (uint32_t)(16 * q + b) : kDead,
-                       v.byte(kr, ok ? p + 128 : 0));          // 0 <= p + 128 < 256 where ok
-        }
-    }
+    // the end pieces, one row per thread: at the first step the walk's bytes
+    // of the piece that holds the row's first byte (if the piece starts
+    // before it), at the last those of the piece that holds its last byte (if
+    // it ends after it)
+    const int kr = t;
+    const uint32_t at = base + (uint32_t)kr * pitch;
+    const int sft = (int)(at & 127u);
+    const int o = sft & 15, et = (rem + sft) & 15;
+    const int qh = sft >> 4, qt = (rem - 1 + sft) >> 4;
+    const bool head = kr < rows && first && o != 0;
+    // a walk of one step whose bytes all lie in the head piece has no tail
+    const bool tail = kr < rows && last && et != 0 && !(head && qt == qh);
+    if (__builtin_amdgcn_ballot_w64(head) != 0)
+        rag_store_range<true>(rc, head, at - (uint32_t)sft + 16u * qh,
+                              rag_bytes(v, kr, 128 - o), o, min(16, o + rem));
+    if (__builtin_amdgcn_ballot_w64(tail) != 0)
+        rag_store_range<false>(rc, tail, at - (uint32_t)sft + 16u * qt,
+                               rag_bytes(v, kr, 16 * qt - sft + 128), 0, et);
 }
 
 }  // namespace mxk

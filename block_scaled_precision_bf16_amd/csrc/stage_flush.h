@@ -16,12 +16,6 @@
 
 namespace mxk {
 
-template <int AUX = 0>
-__device__ __forceinline__ void buf_store2(rsrc_t r, uint32_t off, uint16_t v)
-{
-    __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)off, 0, AUX);
-}
-
 // Column-block scales are staged transposed: s[b][pos] holds the scale of
 // block b of the walk (a 32-row block of MXFP8, a 16-row block of NVFP4) of
 // transposed row kl, at byte pos = kl ^ scol_swz(b).  A lane's 8 columns

@@ -286,27 +286,59 @@ def model_rag_lines(d, base, pitch, rows, addr0, rem, first, last):
                         addr0(kr) + p0))
     if not (first or last):
         return out
-    # the end pieces byte by byte: 16 lanes per row
-    b = t & 15
-    for e in (0, 1):
-        if (e == 0 and not first) or (e == 1 and not last):
+    # the end pieces, one row per thread, in naturally aligned stores:
+    # upwards from the head range's first byte while its low bits are set,
+    # then downwards by size
+    kr = t
+    at = base + kr * pitch
+    sft = at % 128
+    o, et = sft % 16, (rem + sft) % 16
+    qh, qt = sft >> 4, (rem - 1 + sft) >> 4
+    head = (kr < rows) & first & (o != 0)
+    tail = (kr < rows) & last & (et != 0) & ~(head & (qt == qh))
+    for on, q, b, b1, up in ((head, qh, o, np.minimum(16, o + rem), True),
+                             (tail, qt, np.zeros_like(t), et, False)):
+        if not on.any():
             continue
-        for i in range(256 // 16):
-            kr = (t >> 4) + 16 * i
-            at = base + kr * pitch
-            sft = at % 128
-            qa = sft >> 4
-            if e == 0:
-                q = qa
-                edge = sft % 16 != 0
-            else:
-                q = (rem - 1 + sft) >> 4
-                edge = ((rem + sft) % 16 != 0) & ~(first & (q == qa) & (sft % 16 != 0))
-            p = 16 * q - sft + b
-            ok = (kr < rows) & edge & (p >= lo) & (p < rem)
-            out.append(("rag W=1", d, np.where(ok, at - sft + 16 * q + b, DEAD), 1, ok,
-                        addr0(kr) + p))
+        for size, go, bs in range_stores(on, b, b1, up):
+            out.append((f"rag end W={size}", d, np.where(go, at - sft + 16 * q + bs, DEAD), size, go,
+                        addr0(kr) + 16 * q - sft + bs))
     return out
+
+
+def range_stores(on, b0, b1, up):
+    """rag_store_range (rag_flush.h): the stores (size, lanes that store,
+    first byte) of bytes b0 .. b1 - 1 of a 16-byte piece."""
+    steps = ([(1, True), (2, True), (4, True), (8, True)] if up else []) + \
+            [(8, False), (4, False), (2, False), (1, False)]
+    b = b0
+    out = []
+    for size, by_bit in steps:
+        go = on & (b + size <= b1) & (((b & size) != 0) if by_bit else True)
+        out.append((size, go, b))
+        b = np.where(go, b + size, b)
+    return out
+
+
+def test_range_stores_cover_any_range_once_aligned():
+    """Every partial byte range of a 16-byte piece (from byte 0 without the
+    upward pass): each byte stored exactly once, every store naturally
+    aligned and inside the range."""
+    b0, b1 = np.meshgrid(np.arange(16), np.arange(17), indexing="ij")
+    b0, b1 = b0.ravel(), b1.ravel()
+    keep = (b0 < b1) & (b1 - b0 < 16)
+    b0, b1 = b0[keep], b1[keep]
+    for up in (True, False):
+        sel = np.ones_like(b0, bool) if up else b0 == 0
+        lo, hi = b0[sel], b1[sel]
+        cover = np.zeros((lo.size, 16), np.int64)
+        for size, go, b in range_stores(np.ones(lo.size, bool), lo, hi, up):
+            assert (b[go] % size == 0).all()
+            assert ((b[go] >= lo[go]) & (b[go] + size <= hi[go])).all()
+            for k in range(size):
+                np.add.at(cover, (np.nonzero(go)[0], b[go] + k), 1)
+        want = (np.arange(16) >= lo[:, None]) & (np.arange(16) < hi[:, None])
+        assert (cover == want).all()
 
 
 def model_col_flush_q_rag(base, M, K, tm, tk, first, last):
@@ -365,8 +397,8 @@ def test_ragged_transposed_writes_every_byte_once(rows, K, L, base):
                         ck.access(site, d, off, nb_, live, addr)
                         a = np.broadcast_to(addr, live.shape)[live]
                         assert (a >= 0).all()
+                        assert ((gbase + a) % nb_ == 0).all(), f"{nb_}-byte store not aligned"
                         if nb_ == 16:
-                            assert ((gbase + a) % 16 == 0).all(), "16-byte store not aligned"
                             if 0 < g < n - 1 and a.size:
                                 # a sub-tile inside the walk writes each row's line whole
                                 lines = (gbase + a) // 128
@@ -408,6 +440,7 @@ def test_nvfp4_ragged_transposed_writes_every_byte_once(rows, K, L, base):
                         ck.access(site, d, o, nb_, live, addr)
                         a = np.broadcast_to(addr, live.shape)[live]
                         assert (a >= 0).all()
+                        assert ((gbase + a) % nb_ == 0).all(), f"{nb_}-byte store not aligned"
                         for b in range(nb_):
                             np.add.at(count, off + a + b, 1)
         off += K * -(-M // 2)

@@ -119,6 +119,7 @@ __device__ __forceinline__ void rag_flush_lines(const V &v, rsrc_t rc, uint32_t 
     // bytes lo .. rem - 1 of the step's row segment are its to write
     // (negative: the previous step's)
     const int lo = first ? 0 : -128;
+    const int nr = rows < 256 ? (int)rows : 256;   // rows of the strip that exist
     // two rows' pieces in flight at a time: enough to overlap the reads, and
     // the registers stay within what the casts around it leave
 #pragma unroll 2
@@ -128,7 +129,7 @@ __device__ __forceinline__ void rag_flush_lines(const V &v, rsrc_t rc, uint32_t 
         const int sft = (int)(at & 127u);
         const int p0 = 16 * j - sft;                       // the piece's first byte in the segment
         const uint4 w = rag_bytes(v, kr, p0 + 128);
-        const bool whole = kr < rows && p0 >= lo && p0 + 16 <= rem;
+        const bool whole = kr < nr && p0 >= lo && p0 + 16 <= rem;
         buf_store16<AUX>(rc, whole ? at - (uint32_t)sft + 16u * j : kDead, w);
     }
     if (last) {
@@ -139,7 +140,7 @@ __device__ __forceinline__ void rag_flush_lines(const V &v, rsrc_t rc, uint32_t 
             const uint32_t at = base + (uint32_t)kr * pitch;
             const int sft = (int)(at & 127u);
             const int p0 = 128 + 16 * j - sft;
-            const bool whole = kr < rows && p0 + 16 <= rem;
+            const bool whole = kr < nr && p0 + 16 <= rem;
             buf_store16<AUX>(rc, whole ? at - (uint32_t)sft + (uint32_t)(128 + 16 * j) : kDead,
                              rag_bytes(v, kr, p0 + 128));
         }
@@ -155,9 +156,9 @@ __device__ __forceinline__ void rag_flush_lines(const V &v, rsrc_t rc, uint32_t 
     const int sft = (int)(at & 127u);
     const int o = sft & 15, et = (rem + sft) & 15;
     const int qh = sft >> 4, qt = (rem - 1 + sft) >> 4;
-    const bool head = kr < rows && first && o != 0;
+    const bool head = kr < nr && first && o != 0;
     // a walk of one step whose bytes all lie in the head piece has no tail
-    const bool tail = kr < rows && last && et != 0 && !(head && qt == qh);
+    const bool tail = kr < nr && last && et != 0 && !(head && qt == qh);
     if (__builtin_amdgcn_ballot_w64(head) != 0)
         rag_store_range<true>(rc, head, at - (uint32_t)sft + 16u * qh,
                               rag_bytes(v, kr, 128 - o), o, min(16, o + rem));

@@ -10,13 +10,14 @@
 //   * transposed, each transposed row's bytes of the step (64 or 32) start
 //     at the same offset within a chunk of that size at every step, so a
 //     two-step ring in LDS lets every step write whole aligned chunks as
-//     16-byte pieces; only a walk's first and last chunks leave byte by byte
-//     (flush_cols).
+//     16-byte pieces; only a walk's first and last chunks leave in narrower
+//     stores (flush_cols).
 #pragma once
 
 #include "bufio.h"
 #include "device_math.h"
 #include "launch.h"
+#include "rag_flush.h"
 
 namespace mxk {
 
@@ -167,8 +168,9 @@ __device__ __forceinline__ void flush_rows(uint8_t *out, int64_t stride, int64_t
 // step's first.  Its last sft bytes wait for the next step; the walk's last
 // step writes them too.  At the walk's first step the chunk's first sft
 // bytes belong to the walk before and are left alone.  Whole 16-byte pieces
-// leave as 16-byte stores assembled from aligned LDS dwords; pieces with
-// bytes outside the walk leave byte by byte.
+// leave as 16-byte stores assembled from aligned LDS dwords; of the pieces
+// with bytes outside the walk, the walk's bytes leave in naturally aligned
+// stores of 1, 2, 4 and 8 bytes.
 template <int CH>
 __device__ __forceinline__ void flush_cols(uint8_t *out, int64_t tstride, int64_t k0, int64_t K,
                                            int64_t pos, int rem, int s, bool last,
@@ -206,14 +208,9 @@ __device__ __forceinline__ void flush_cols(uint8_t *out, int64_t tstride, int64_
         }
         buf_store16(rc, whole ? (uint32_t)(co + 16 * j) : kDead, o);
         const bool part = row_ok && !whole && 16 * j < hi && 16 * j + 16 > lo;
-        if (__builtin_amdgcn_ballot_w64(part) != 0) {   // uniform: first and last steps only
-#pragma unroll
-            for (int b = 0; b < 16; b++) {
-                const int pb = 16 * j + b;
-                const bool ok = part && pb >= lo && pb < hi;
-                buf_store1(rc, ok ? (uint32_t)(co + pb) : kDead, rr[(v0 + b) & (2 * CH - 1)]);
-            }
-        }
+        if (__builtin_amdgcn_ballot_w64(part) != 0)   // uniform: first and last steps only
+            rag_store_range<true>(rc, part, (uint32_t)(co + 16 * j), o,
+                                  lo > 16 * j ? lo - 16 * j : 0, hi < 16 * j + 16 ? hi - 16 * j : 16);
     }
 }
 

@@ -703,11 +703,12 @@ def model_flush_cols(site, base, tstride, k0, K, pos, rem, s, last, CH):
         out.append((f"{site} W=16", d, np.where(whole, co + 16 * j, DEAD), 16, whole,
                     (k0 + cc) * tstride + pos - sft + 16 * j))
         part = row_ok & ~whole & (16 * j < hi) & (16 * j + 16 > lo)
-        for b in range(16):
-            pb = 16 * j + b
-            ok = part & (pb >= lo) & (pb < hi)
-            out.append((f"{site} W=1", d, np.where(ok, co + pb, DEAD), 1, ok,
-                        (k0 + cc) * tstride + pos - sft + pb))
+        if part.any():
+            b0 = np.where(lo > 16 * j, lo - 16 * j, 0)
+            b1 = np.where(hi < 16 * j + 16, hi - 16 * j, 16)
+            for size, go, b in range_stores(part, b0, b1, True):
+                out.append((f"{site} W={size}", d, np.where(go, co + 16 * j + b, DEAD), size, go,
+                            (k0 + cc) * tstride + pos - sft + 16 * j + b))
     return out
 
 

@@ -336,7 +336,9 @@ struct MxRagView {
     const StageTile &prev, &cur;
     __device__ __forceinline__ uint4 chunk(int kr, int c) const
     {
-        return c < 8 ? prev[kr][stage_chunk(kr, c)] : cur[kr][stage_chunk(kr, (c - 8) & 7)];
+        // chunk c & 7 of the previous tile (c < 8) or of the current one
+        const StageTile &tile = c < 8 ? prev : cur;
+        return tile[kr][stage_chunk(kr, c & 7)];
     }
 };
 

@@ -119,9 +119,13 @@ struct NvRagView {
     const uint8_t (*prev)[128], (*cur)[128];
     __device__ __forceinline__ uint4 chunk(int kr, int c) const
     {
-        const uint8_t *row = c < 8 ? prev[kr] : cur[kr];
-        const uint4 v = *reinterpret_cast<const uint4 *>(row + 16 * nv_chunk(kr, c & 7));
-        return nv_half(kr, 0) ? make_uint4(v.z, v.w, v.x, v.y) : v;
+        // the chunk's first 8 bytes lie in its second half where the halves
+        // are swapped: two 8-byte reads in logical order, no selects
+        const uint8_t *p = (c < 8 ? prev[kr] : cur[kr]) + 16 * nv_chunk(kr, c & 7);
+        const int h = nv_half(kr, 0) ? 8 : 0;
+        const uint2 lo = *reinterpret_cast<const uint2 *>(p + h);
+        const uint2 hi = *reinterpret_cast<const uint2 *>(p + (8 - h));
+        return make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
 };
 

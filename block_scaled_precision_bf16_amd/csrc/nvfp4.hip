@@ -113,19 +113,25 @@ __device__ __forceinline__ int nv_chunk(int kl, int j) { return j ^ ((kl >> 3) &
 // span (no LDS bank conflict); the flush swaps them back.
 __device__ __forceinline__ int nv_half(int kl, int half) { return half ^ ((kl >> 6) & 1); }
 
+// Chunk j (0-7) of staged transposed row kr, its 8-byte halves in logical
+// order: where the halves are swapped, the chunk's first 8 bytes lie in its
+// second half, so the two 8-byte reads take them in that order (no selects).
+__device__ __forceinline__ uint4 nv_read_chunk(const uint8_t *row, int kr, int j)
+{
+    const uint8_t *p = row + 16 * nv_chunk(kr, j);
+    const int h = nv_half(kr, 0) ? 8 : 0;
+    const uint2 lo = *reinterpret_cast<const uint2 *>(p + h);
+    const uint2 hi = *reinterpret_cast<const uint2 *>(p + (8 - h));
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
 // The staged pair tiles of a ragged walk as rag_flush.h reads them, each
 // chunk's 8-byte halves back in order.
 struct NvRagView {
     const uint8_t (*prev)[128], (*cur)[128];
     __device__ __forceinline__ uint4 chunk(int kr, int c) const
     {
-        // the chunk's first 8 bytes lie in its second half where the halves
-        // are swapped: two 8-byte reads in logical order, no selects
-        const uint8_t *p = (c < 8 ? prev[kr] : cur[kr]) + 16 * nv_chunk(kr, c & 7);
-        const int h = nv_half(kr, 0) ? 8 : 0;
-        const uint2 lo = *reinterpret_cast<const uint2 *>(p + h);
-        const uint2 hi = *reinterpret_cast<const uint2 *>(p + (8 - h));
-        return make_uint4(lo.x, lo.y, hi.x, hi.y);
+        return nv_read_chunk(c < 8 ? prev[kr] : cur[kr], kr, c & 7);
     }
 };
 
@@ -152,7 +158,7 @@ __device__ __forceinline__ void nv_load(const Nv4Args &a, const NvLane &l, int t
 // so a 16-byte chunk may hold 16 rows inside M and 16 outside; then each
 // chunk leaves as two 8-byte halves (a run-time choice, so that the groups of
 // a grouped cast each take their own).
-template <int AUX>
+template <int AUX, bool TWO_D>
 __device__ __forceinline__ void nv_flush_q(const Nv4Args &a, const NvStage &st, int tm, int tk,
                                            int parts, bool half)
 {
@@ -168,9 +174,17 @@ __device__ __forceinline__ void nv_flush_q(const Nv4Args &a, const NvStage &st, 
     for (int i = 0; i < kTileK / 32; i++) {
         const int kr = (t >> 3) + 32 * i;
         const bool col_ok = in_pair && k0 + kr < a.K;
-        uint4 v = *reinterpret_cast<const uint4 *>(&st.q[0][kr][16 * nv_chunk(kr, jr)]);
-        if (nv_half(kr, 0))
-            v = make_uint4(v.z, v.w, v.x, v.y);
+        // the 2D casts read the halves in order; the 1D casts, short of
+        // registers, read the chunk whole and swap its halves with selects
+        // (4 more spilled registers and 2 % slower the other way round)
+        uint4 v;
+        if constexpr (TWO_D) {
+            v = nv_read_chunk(st.q[0][kr], kr, jr);
+        } else {
+            v = *reinterpret_cast<const uint4 *>(&st.q[0][kr][16 * nv_chunk(kr, jr)]);
+            if (nv_half(kr, 0))
+                v = make_uint4(v.z, v.w, v.x, v.y);
+        }
         const uint32_t off = (uint32_t)(kr * ld) + 16 * jr;
         if (!half) {
             buf_store16<AUX>(rc, col_ok && row0 < a.M ? off : kDead, v);
@@ -432,7 +446,7 @@ __device__ __forceinline__ void nv_step(const Nv4Args &a, const NvLane &l,
         nv_flush_q_rag<P::q_col>(a, st, FLUSH == 2 ? tm - 1 : tm, tk, g >> 1, FLUSH, g < 2,
                                  FLUSH == 1 || g + 1 == n);
     else if constexpr (COL && FLUSH != 0)
-        nv_flush_q<P::q_col>(a, st, FLUSH == 2 ? tm - 1 : tm, tk, FLUSH, (a.M & 31) != 0);
+        nv_flush_q<P::q_col, TWO_D>(a, st, FLUSH == 2 ? tm - 1 : tm, tk, FLUSH, (a.M & 31) != 0);
     __syncthreads();
 }
 
